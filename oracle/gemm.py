@@ -1,0 +1,142 @@
+"""Block-scaled FP8 GEMMs and the masked BF16 GEMM, in float64 (oracle side).
+
+TEST INFRASTRUCTURE ONLY (see ``oracle/__init__.py``).
+
+Definition followed ("DeepInside DeepGEMM", section 2 NT layout and section 4
+example; "DeepGEMM tested by Novita AI", section "Technological Innovations",
+per-block promotion): with A [M, K] and B [N, K] holding E4M3 codes, sfa
+[M, ceil(K/128)] one scale per row per 128-wide K-block and sfb
+[ceil(N/128), ceil(K/128)] one scale per 128x128 block of B,
+
+    P_kb[m, n] = sum_{k in block kb} dec(A[m, k]) * dec(B[n, k])
+    D[m, n]    = sum_kb P_kb[m, n] * (sfa[m, kb] * sfb[n // 128, kb])
+
+and D is returned as float64 (no bf16 rounding: the comparison allows for
+the device's bf16 output).
+
+Exactness: every E4M3 value is an integer multiple of 2^-9 below 2^9, so a
+product is an integer multiple of 2^-18 below 2^18 and a 128-term block sum
+is an integer multiple of 2^-18 below 2^25; P_kb is therefore exact in
+float64 whatever order the matmul library sums in.  sfa*sfb (two binary32
+values) is exact in float64.  Only the final multiply and the sum over
+blocks round, at float64 precision.
+
+Pins: tests/test_oracle_gemm.py (pure-Python brute force on tiny shapes,
+the closed form for one-hot B with power-of-two scales, numpy float64
+matmul when every scale is 1, and the masked/contiguous invariants).
+"""
+
+import numpy as np
+
+from .formats import e4m3_decode, bf16_decode, ue8m0_decode
+
+BLOCK = 128
+
+
+def _scaled_block_gemm(a, b, sfa, sfb):
+    """D = sum_kb (A_kb B_kb^T) * (sfa[:, kb] outer sfb-per-column[:, kb])."""
+    A = e4m3_decode(a)
+    B = e4m3_decode(b)
+    M, K = A.shape
+    N = B.shape[0]
+    sfa = np.asarray(sfa, dtype=np.float64)
+    sfb = np.asarray(sfb, dtype=np.float64)
+    nkb = -(-K // BLOCK)
+    col_block = np.arange(N) // BLOCK  # which row-block of B each output column uses
+    D = np.zeros((M, N), dtype=np.float64)
+    for kb in range(nkb):
+        ks = slice(kb * BLOCK, (kb + 1) * BLOCK)
+        P = A[:, ks] @ B[:, ks].T
+        D += P * (sfa[:, kb][:, None] * sfb[col_block, kb][None, :])
+    return D
+
+
+def fp8_gemm_nt(a, b, sfa, sfb, c=None):
+    """Dense D = C + A . B^T with block scales.
+
+    a uint8 [M, K], b uint8 [N, K] (E4M3 codes), sfa float [M, ceil(K/128)],
+    sfb float [ceil(N/128), ceil(K/128)], optional c [M, N] (float64).
+    Returns float64 [M, N].
+    """
+    D = _scaled_block_gemm(np.asarray(a), np.asarray(b), sfa, sfb)
+    if c is not None:
+        D = D + np.asarray(c, dtype=np.float64)
+    return D
+
+
+def m_grouped_fp8_gemm_nt_contiguous(a, b, sfa, sfb, grouped_layout):
+    """Groups concatenated along M ("DeepGEMM tested by Novita AI", contiguous
+    layout section).  Row m uses group g = grouped_layout[m // 128]; a block
+    with g < 0 is skipped.
+
+    a [Msum, K], b [G, N, K], sfa [Msum, nkb], sfb [G, nnb, nkb].
+    Returns (D float64 [Msum, N], written bool [Msum]); rows with
+    written=False are left to the caller's contents.
+    """
+    a = np.asarray(a)
+    layout = np.asarray(grouped_layout, dtype=np.int64)
+    Msum = a.shape[0]
+    N = b.shape[1]
+    D = np.zeros((Msum, N), dtype=np.float64)
+    written = np.zeros(Msum, dtype=bool)
+    for blk, g in enumerate(layout):
+        if g < 0:
+            continue
+        rows = slice(blk * BLOCK, min((blk + 1) * BLOCK, Msum))
+        D[rows] = _scaled_block_gemm(a[rows], b[g], sfa[rows], sfb[g])
+        written[rows] = True
+    return D, written
+
+
+def _valid_rows(masked_m, max_m):
+    """Rows computed for each group: masked_m clamped to [0, max_m]."""
+    return [int(min(max(int(v), 0), max_m)) for v in np.asarray(masked_m).reshape(-1)]
+
+
+def m_grouped_fp8_gemm_nt_masked(a, b, sfa, sfb, masked_m, max_m):
+    """Masked grouped GEMM ("DeepGEMM CUDA Graph Compatibility for Masked
+    Grouped GEMMs", section "Tensor-Based Metadata Arguments"): group g
+    computes only its first masked_m[g] rows of a padded [max_m, K] buffer.
+
+    a [G, max_m, K], b [G, N, K], sfa [G, max_m, nkb], sfb [G, nnb, nkb].
+    Returns (D float64 [G, max_m, N], written bool [G, max_m]).
+    """
+    G = b.shape[0]
+    N = b.shape[1]
+    D = np.zeros((G, max_m, N), dtype=np.float64)
+    written = np.zeros((G, max_m), dtype=bool)
+    for g, v in enumerate(_valid_rows(masked_m, max_m)):
+        if v == 0:
+            continue
+        D[g, :v] = _scaled_block_gemm(a[g, :v], b[g], sfa[g, :v], sfb[g])
+        written[g, :v] = True
+    return D, written
+
+
+def m_grouped_bf16_gemm_nt_masked(a_bits, b_bits, masked_m, max_m):
+    """Masked grouped BF16 GEMM: D[g, m] = A[g, m] . B[g]^T for m < masked_m[g]
+    (same page and section; signature of its capture example).
+
+    a_bits uint16 [G, max_m, K], b_bits uint16 [G, N, K] (bfloat16 patterns).
+    Returns (D float64 [G, max_m, N], written bool [G, max_m]).
+    """
+    G = b_bits.shape[0]
+    N = b_bits.shape[1]
+    D = np.zeros((G, max_m, N), dtype=np.float64)
+    written = np.zeros((G, max_m), dtype=bool)
+    for g, v in enumerate(_valid_rows(masked_m, max_m)):
+        if v == 0:
+            continue
+        D[g, :v] = bf16_decode(a_bits[g, :v]) @ bf16_decode(b_bits[g]).T
+        written[g, :v] = True
+    return D, written
+
+
+def scales_from_packed_ue8m0(packed, n):
+    """Unpack int32 words of four UE8M0 bytes back to float64 scales [..., n]
+    (byte j of word i is the exponent of element 4i + j)."""
+    words = np.asarray(packed, dtype=np.int32).view(np.uint32)
+    out = np.empty(words.shape[:-1] + (n,), dtype=np.float64)
+    for j in range(n):
+        out[..., j] = ue8m0_decode((words[..., j // 4] >> np.uint32(8 * (j % 4))) & np.uint32(0xFF))
+    return out

@@ -1,0 +1,207 @@
+"""Pins of the oracle's GEMMs: pure-Python brute force on tiny shapes (with
+torch's own e4m3/bf16 decoding, sharing no code with the oracle), the
+closed form for one-hot B with power-of-two scales, numpy float64 matmul
+when every scale is 1, and the masked / contiguous invariants."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from moe_grouped_gemm_x128_amd import synth
+
+
+def _torch_e4m3(codes):
+    return torch.from_numpy(np.ascontiguousarray(codes, dtype=np.uint8)).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+
+
+def _torch_bf16(bits):
+    return torch.from_numpy(np.ascontiguousarray(bits, dtype=np.uint16).view(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
+
+
+def _brute(a, b, sfa, sfb):
+    """D[m][n] = sum_k (A[m,k] * sfa[m, k//128]) * (B[n,k] * sfb[n//128, k//128]),
+    element by element in Python floats."""
+    A = _torch_e4m3(a).tolist()
+    B = _torch_e4m3(b).tolist()
+    sa = np.asarray(sfa, dtype=np.float64).tolist()
+    sb = np.asarray(sfb, dtype=np.float64).tolist()
+    M, K = len(A), len(A[0])
+    N = len(B)
+    D = [[0.0] * N for _ in range(M)]
+    for m in range(M):
+        for n in range(N):
+            acc = 0.0
+            for k in range(K):
+                acc += (A[m][k] * sa[m][k // 128]) * (B[n][k] * sb[n // 128][k // 128])
+            D[m][n] = acc
+    return np.array(D)
+
+
+def _random_operands(seed, M, N, K, ue8m0=False):
+    xa = synth.normal_f32(seed, (M, K))
+    xb = synth.normal_f32(seed + 1, (N, K))
+    a, sfa = oracle.per_token_cast_to_fp8(xa, ue8m0)
+    b, sfb = oracle.per_block_cast_to_fp8(xb, ue8m0)
+    return a, b, sfa, sfb
+
+
+def _close(x, ref, rtol=1e-12):
+    scale = max(np.sqrt(np.mean(ref ** 2)), 1e-300)
+    return np.max(np.abs(x - ref)) <= rtol * scale
+
+
+@pytest.mark.parametrize("M,N,K", [(3, 260, 384), (2, 129, 300), (5, 7, 128)])
+def test_dense_matches_brute_force(M, N, K):
+    a, b, sfa, sfb = _random_operands(21, M, N, K)
+    got = oracle.fp8_gemm_nt(a, b, sfa, sfb)
+    assert got.shape == (M, N)
+    assert _close(got, _brute(a, b, sfa, sfb))
+
+
+def test_dense_brute_force_rejects_transposed_scales():
+    # the pin is sensitive to the scale indexing: a B-scale grid read
+    # transposed (square 2x2 grid here) gives a different product
+    a, b, sfa, sfb = _random_operands(22, 2, 256, 256)
+    sfb = sfb * np.array([[1.0, 2.0], [4.0, 8.0]], dtype=np.float32)
+    good = oracle.fp8_gemm_nt(a, b, sfa, sfb)
+    bad = oracle.fp8_gemm_nt(a, b, sfa, np.ascontiguousarray(sfb.T))
+    ref = _brute(a, b, sfa, sfb)
+    assert _close(good, ref) and not _close(bad, ref, rtol=1e-3)
+
+
+def test_dense_one_hot_closed_form():
+    rng = np.random.default_rng(23)
+    M, N, K = 6, 256, 512
+    a = rng.integers(0, 0x7E, size=(M, K)).astype(np.uint8) | (rng.integers(0, 2, size=(M, K)).astype(np.uint8) << 7)
+    kn = rng.permutation(K)[:N]  # column n picks K index kn[n]
+    b = np.zeros((N, K), dtype=np.uint8)
+    b[np.arange(N), kn] = 0x38  # 1.0
+    sfa = np.exp2(rng.integers(-8, 8, size=(M, K // 128))).astype(np.float32)
+    sfb = np.exp2(rng.integers(-8, 8, size=(N // 128, K // 128))).astype(np.float32)
+    got = oracle.fp8_gemm_nt(a, b, sfa, sfb)
+    A = _torch_e4m3(a)
+    want = np.empty((M, N))
+    for n in range(N):
+        k = kn[n]
+        want[:, n] = A[:, k] * sfa[:, k // 128] * sfb[n // 128, k // 128]
+    assert np.array_equal(got, want)
+
+
+def test_dense_unit_scales_is_matmul():
+    a, b, _, _ = _random_operands(24, 64, 200, 384)
+    ones_a = np.ones((64, 3), np.float32)
+    ones_b = np.ones((2, 3), np.float32)
+    got = oracle.fp8_gemm_nt(a, b, ones_a, ones_b)
+    want = _torch_e4m3(a) @ _torch_e4m3(b).T
+    assert np.array_equal(got, want)  # all partial sums are exact in float64
+
+
+def test_dense_accumulate_c():
+    a, b, sfa, sfb = _random_operands(25, 4, 130, 256)
+    c = np.random.default_rng(0).standard_normal((4, 130))
+    assert np.array_equal(oracle.fp8_gemm_nt(a, b, sfa, sfb, c), oracle.fp8_gemm_nt(a, b, sfa, sfb) + c)
+
+
+def test_dense_ue8m0_scales_from_packed():
+    a, b, sfa, sfb = _random_operands(26, 3, 130, 512, ue8m0=True)
+    pa, bad_a = oracle.pack_ue8m0_to_int(sfa)
+    pb, bad_b = oracle.pack_ue8m0_to_int(sfb)
+    assert bad_a == 0 and bad_b == 0
+    ua = oracle.scales_from_packed_ue8m0(pa, 4)
+    ub = oracle.scales_from_packed_ue8m0(pb, 4)
+    assert np.array_equal(ua, sfa) and np.array_equal(ub, sfb)
+    assert _close(oracle.fp8_gemm_nt(a, b, ua, ub), _brute(a, b, sfa, sfb))
+
+
+def _masked_case(seed, G, max_m, N, K):
+    xa = synth.normal_f32(seed, (G, max_m, K))
+    xb = synth.normal_f32(seed + 1, (G, N, K))
+    a, sfa = oracle.per_token_cast_to_fp8(xa)
+    b, sfb = oracle.per_block_cast_to_fp8(xb)
+    return a, b, sfa, sfb
+
+
+def test_masked_brute_force_and_untouched_rows():
+    G, max_m, N, K = 3, 5, 130, 256
+    a, b, sfa, sfb = _masked_case(31, G, max_m, N, K)
+    mm = np.array([2, 0, 5], dtype=np.int32)
+    D, written = oracle.m_grouped_fp8_gemm_nt_masked(a, b, sfa, sfb, mm, max_m)
+    assert D.shape == (G, max_m, N)
+    for g in range(G):
+        assert np.array_equal(written[g], np.arange(max_m) < mm[g])
+        if mm[g]:
+            v = mm[g]
+            assert _close(D[g, :v], _brute(a[g, :v], b[g], sfa[g, :v], sfb[g]))
+        assert np.all(D[g, mm[g]:] == 0.0)
+
+
+def test_masked_full_equals_dense_per_group_and_clamps():
+    G, max_m, N, K = 2, 6, 200, 384
+    a, b, sfa, sfb = _masked_case(32, G, max_m, N, K)
+    full, w = oracle.m_grouped_fp8_gemm_nt_masked(a, b, sfa, sfb, np.array([max_m, 99]), max_m)
+    assert w.all()
+    for g in range(G):
+        assert np.array_equal(full[g], oracle.fp8_gemm_nt(a[g], b[g], sfa[g], sfb[g]))
+    none, w0 = oracle.m_grouped_fp8_gemm_nt_masked(a, b, sfa, sfb, np.array([0, -7]), max_m)
+    assert not w0.any() and np.all(none == 0.0)
+
+
+def test_contiguous_brute_force_skip_and_permutation():
+    G, N, K = 3, 130, 256
+    nblk = 4
+    xa = synth.normal_f32(41, (nblk * 128, K))
+    xb = synth.normal_f32(42, (G, N, K))
+    a, sfa = oracle.per_token_cast_to_fp8(xa)
+    b, sfb = oracle.per_block_cast_to_fp8(xb)
+    layout = np.array([2, -1, 0, 2], dtype=np.int32)
+    D, written = oracle.m_grouped_fp8_gemm_nt_contiguous(a, b, sfa, sfb, layout)
+    assert np.array_equal(written, np.repeat(layout >= 0, 128))
+    assert np.all(D[128:256] == 0.0)
+    # brute force on two sampled rows of each computed block
+    for blk, g in enumerate(layout):
+        if g < 0:
+            continue
+        rows = [blk * 128, blk * 128 + 77]
+        assert _close(D[rows], _brute(a[rows], b[g], sfa[rows], sfb[g]))
+    # permuting the group ids of the blocks permutes which B each block uses
+    perm = np.array([1, 2, 0])  # new id of old group g is perm[g]
+    b2 = np.empty_like(b)
+    sfb2 = np.empty_like(sfb)
+    b2[perm] = b
+    sfb2[perm] = sfb
+    layout2 = np.where(layout >= 0, perm[np.maximum(layout, 0)], -1).astype(np.int32)
+    D2, _ = oracle.m_grouped_fp8_gemm_nt_contiguous(a, b2, sfa, sfb2, layout2)
+    assert np.array_equal(D, D2)
+
+
+def test_bf16_masked_brute_force():
+    G, max_m, N, K = 2, 4, 9, 40
+    ab = synth.bf16_bits_from_f32(synth.normal_f32(51, (G, max_m, K)))
+    bb = synth.bf16_bits_from_f32(synth.normal_f32(52, (G, N, K)))
+    mm = np.array([3, 4], dtype=np.int32)
+    D, written = oracle.m_grouped_bf16_gemm_nt_masked(ab, bb, mm, max_m)
+    A = _torch_bf16(ab)
+    B = _torch_bf16(bb)
+    for g in range(G):
+        for m in range(max_m):
+            for n in range(N):
+                want = sum(A[g, m, k] * B[g, n, k] for k in range(K)) if m < mm[g] else 0.0
+                assert abs(D[g, m, n] - want) <= 1e-12 * (1 + abs(want))
+    assert np.array_equal(written, np.arange(max_m)[None, :] < mm[:, None])
+
+
+def test_bf16_masked_is_matmul():
+    G, max_m, N, K = 2, 16, 64, 256
+    ab = synth.bf16_bits_from_f32(synth.normal_f32(53, (G, max_m, K)))
+    bb = synth.bf16_bits_from_f32(synth.normal_f32(54, (G, N, K)))
+    D, _ = oracle.m_grouped_bf16_gemm_nt_masked(ab, bb, np.array([16, 16]), max_m)
+    for g in range(G):
+        want = _torch_bf16(ab[g]) @ _torch_bf16(bb[g]).T
+        assert np.allclose(D[g], want, rtol=0, atol=1e-12)
+
+
+def test_synth_chunked_draw_matches_whole():
+    whole = synth.normal_f32(9, (3, 5, 7))
+    parts = np.stack(list(synth.normal_f32_chunks(9, (3, 5, 7))))
+    assert np.array_equal(whole, parts)
