@@ -1,0 +1,345 @@
+"""Benchmark of the block-scaled FP8 GEMM path on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload dense|contiguous|masked|masked_graph]
+
+Default workload ("dense"): the five DeepSeek-V3-shaped dense GEMMs,
+M = 4096 with (N, K) in {(2112, 7168), (24576, 1536), (7168, 16384),
+(4096, 7168), (7168, 2048)}, N(0, 1) float32 inputs already resident in HBM.
+One step = for every shape: per-token FP8 cast of A (1x128 scales),
+per-block FP8 cast of B (128x128 scales), and the block-scaled FP8 GEMM
+with BF16 output -- the whole hot path, no work skipped.
+
+Prints ONE JSON line.  `value` is GEMM FLOPs (2*M*N*K summed over the
+shapes) per second of whole-step time; `roofline` describes the dominant
+kernel (the FP8 GEMM) from HIP events recorded around each GEMM launch on
+the launch stream; `cpu_baseline` times the CPU oracle on a bounded sample
+of the same workload.
+
+Other workloads (for the measurements in the design notes):
+  contiguous   -- MoE prefill: 4 groups x 8192 rows, (N, K) = (4096, 7168) and (7168, 2048)
+  masked       -- MoE decode: 32 experts, max_m 256, masked_m ~ floor(192 U(0.7, 1.3)),
+                  (N, K) = (4096, 7168) and (7168, 2048); metric GB/s
+  masked_graph -- 64 experts, max_m 128, N 7168, K 2048, UE8M0 scales packed by
+                  pack_ue8m0_to_int, FP8 and BF16 masked GEMMs replayed as one hipGraph
+"""
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+FP8_PEAK_TFLOPS = 5000.0   # MI355X dense FP8 MFMA
+BF16_PEAK_TFLOPS = 2500.0  # MI355X dense BF16 MFMA
+HBM_PEAK_GBS = 8000.0      # MI355X HBM3E
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+# ---------------------------------------------------------------------------
+# workloads
+# ---------------------------------------------------------------------------
+
+class DenseWorkload:
+    name = "dense_fp8_v3_shapes"
+
+    def __init__(self, torch, mg, synth):
+        self.torch, self.mg = torch, mg
+        dev = torch.device("cuda")
+        self.M = synth.DENSE_V3_M
+        self.shapes = list(synth.DENSE_V3_SHAPES)
+        self.bufs = []
+        for i, (N, K) in enumerate(self.shapes):
+            sa, sb = synth.dense_v3_seeds(i)
+            xa = torch.from_numpy(synth.normal_f32(sa, (self.M, K))).to(dev)
+            xb = torch.from_numpy(synth.normal_f32(sb, (N, K))).to(dev)
+            buf = dict(
+                xa=xa, xb=xb,
+                a=torch.empty((self.M, K), dtype=torch.uint8, device=dev),
+                sfa=torch.empty((K // 128, self.M), dtype=torch.float32, device=dev).t(),
+                b=torch.empty((N, K), dtype=torch.uint8, device=dev),
+                sfb=torch.empty(((N + 127) // 128, K // 128), dtype=torch.float32, device=dev),
+                d=torch.empty((self.M, N), dtype=torch.bfloat16, device=dev),
+            )
+            self.bufs.append(buf)
+        self.flops = [2.0 * self.M * N * K for N, K in self.shapes]
+        # algorithmic bytes of one GEMM launch: A, B, both scales once, D once
+        self.gemm_bytes = [self.M * K + N * K + 4 * (self.M * K // 128 + ((N + 127) // 128) * (K // 128)) + 2 * self.M * N
+                           for N, K in self.shapes]
+
+    def step(self, events=None):
+        mg = self.mg
+        for i, b in enumerate(self.bufs):
+            mg.per_token_cast_to_fp8(b["xa"], b["a"], b["sfa"])
+            mg.per_block_cast_to_fp8(b["xb"], b["b"], b["sfb"])
+            if events is not None:
+                events[i][0].record()
+            mg.fp8_gemm_nt(b["a"], b["b"], b["sfa"], b["sfb"], None, b["d"])
+            if events is not None:
+                events[i][1].record()
+
+    def config(self):
+        return {"workload": self.name, "M": self.M, "shapes_NK": self.shapes,
+                "scales": "fp32 1x128 (A) / 128x128 (B)", "out": "bf16"}
+
+
+class ContiguousWorkload:
+    name = "contiguous_fp8_moe_prefill"
+
+    def __init__(self, torch, mg, synth):
+        self.torch, self.mg = torch, mg
+        dev = torch.device("cuda")
+        c = synth.CONTIG
+        self.G, per = c["G"], c["rows_per_group"]
+        self.Msum = self.G * per
+        self.shapes = list(c["shapes"])
+        self.layout = torch.from_numpy(synth.contiguous_layout(self.G, per)).to(dev)
+        self.bufs = []
+        for si, (N, K) in enumerate(self.shapes):
+            xa = torch.from_numpy(synth.normal_f32(c["seed_a"] + 10 * si, (self.Msum, K))).to(dev)
+            xb = torch.empty((self.G, N, K), dtype=torch.float32, device=dev)
+            for g, chunk in enumerate(synth.normal_f32_chunks(c["seed_b"] + 10 * si, (self.G, N, K))):
+                xb[g].copy_(torch.from_numpy(chunk))
+            self.bufs.append(dict(
+                xa=xa, xb=xb,
+                a=torch.empty((self.Msum, K), dtype=torch.uint8, device=dev),
+                sfa=torch.empty((K // 128, self.Msum), dtype=torch.float32, device=dev).t(),
+                b=torch.empty((self.G, N, K), dtype=torch.uint8, device=dev),
+                sfb=torch.empty((self.G, (N + 127) // 128, K // 128), dtype=torch.float32, device=dev),
+                d=torch.empty((self.Msum, N), dtype=torch.bfloat16, device=dev)))
+        self.flops = [2.0 * self.Msum * N * K for N, K in self.shapes]
+        self.gemm_bytes = [self.Msum * K + self.G * N * K + 2 * self.Msum * N for N, K in self.shapes]
+
+    def step(self, events=None):
+        mg = self.mg
+        for i, b in enumerate(self.bufs):
+            mg.per_token_cast_to_fp8(b["xa"], b["a"], b["sfa"])
+            mg.per_block_cast_to_fp8(b["xb"], b["b"], b["sfb"])
+            if events is not None:
+                events[i][0].record()
+            mg.m_grouped_fp8_gemm_nt_contiguous(b["a"], b["b"], b["sfa"], b["sfb"], b["d"], self.layout)
+            if events is not None:
+                events[i][1].record()
+
+    def config(self):
+        return {"workload": self.name, "groups": self.G, "rows": self.Msum, "shapes_NK": self.shapes}
+
+
+class MaskedWorkload:
+    name = "masked_fp8_moe_decode"
+
+    def __init__(self, torch, mg, synth):
+        self.torch, self.mg = torch, mg
+        dev = torch.device("cuda")
+        c = synth.MASKED
+        self.G, self.max_m = c["G"], c["max_m"]
+        self.shapes = list(c["shapes"])
+        mm = synth.masked_m_decode(c["seed_m"], self.G)
+        self.mm_host = mm
+        self.masked_m = torch.from_numpy(mm).to(dev)
+        self.bufs = []
+        for si, (N, K) in enumerate(self.shapes):
+            xa = torch.from_numpy(synth.normal_f32(c["seed_a"] + 10 * si, (self.G, self.max_m, K))).to(dev)
+            b = torch.empty((self.G, N, K), dtype=torch.uint8, device=dev)
+            sfb = torch.empty((self.G, (N + 127) // 128, K // 128), dtype=torch.float32, device=dev)
+            xb = torch.empty((N, K), dtype=torch.float32, device=dev)
+            for g, chunk in enumerate(synth.normal_f32_chunks(c["seed_b"] + 10 * si, (self.G, N, K))):
+                xb.copy_(torch.from_numpy(chunk))
+                mg.per_block_cast_to_fp8(xb, b[g], sfb[g])  # expert weights: quantized once
+            del xb
+            self.bufs.append(dict(
+                xa=xa, b=b, sfb=sfb,
+                a=torch.empty((self.G, self.max_m, K), dtype=torch.uint8, device=dev),
+                sfa=torch.empty((self.G, self.max_m, K // 128), dtype=torch.float32, device=dev),
+                d=torch.empty((self.G, self.max_m, N), dtype=torch.bfloat16, device=dev)))
+        rows = int(mm.sum())
+        active = int((mm > 0).sum())
+        self.flops = [2.0 * rows * N * K for N, K in self.shapes]
+        self.gemm_bytes = [active * (N * K + 4 * ((N + 127) // 128) * (K // 128)) + rows * (K + 4 * (K // 128) + 2 * N) + 4 * self.G
+                           for N, K in self.shapes]
+
+    def step(self, events=None):
+        mg = self.mg
+        for i, b in enumerate(self.bufs):
+            mg.per_token_cast_to_fp8(b["xa"], b["a"], b["sfa"])
+            if events is not None:
+                events[i][0].record()
+            mg.m_grouped_fp8_gemm_nt_masked(b["a"], b["b"], b["sfa"], b["sfb"], b["d"], self.masked_m, self.max_m)
+            if events is not None:
+                events[i][1].record()
+
+    def config(self):
+        return {"workload": self.name, "experts": self.G, "max_m": self.max_m,
+                "sum_masked_m": int(self.mm_host.sum()), "shapes_NK": self.shapes}
+
+
+# ---------------------------------------------------------------------------
+# CPU baseline: the oracle on a bounded sample of the dense workload
+# ---------------------------------------------------------------------------
+
+def time_cpu_baseline(rows_a=256, rows_b=2048):
+    import oracle
+    from moe_grouped_gemm_x128_amd import synth
+
+    try:
+        from threadpoolctl import threadpool_info
+
+        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        blas_threads = 1
+    flops = 0.0
+    spent = 0.0
+    for i, (N, K) in enumerate(synth.DENSE_V3_SHAPES):
+        sa, sb = synth.dense_v3_seeds(i)
+        rng_a = synth.normal_f32(sa, (synth.DENSE_V3_M, K))[:rows_a]
+        rng_b = synth.normal_f32(sb, (N, K))[:rows_b]
+        t = time.perf_counter()
+        a, sfa = oracle.per_token_cast_to_fp8(rng_a)
+        b, sfb = oracle.per_block_cast_to_fp8(rng_b)
+        oracle.fp8_gemm_nt(a, b, sfa, sfb)
+        spent += time.perf_counter() - t
+        flops += 2.0 * rows_a * min(rows_b, N) * K
+    return {
+        "value": flops / spent / 1e12,
+        "unit": "TFLOPS",
+        "cores": blas_threads,
+        "kind": "oracle",
+        "sample": (f"per shape: first {rows_a} rows of A x first {rows_b} rows of B, per-token + per-block quantize "
+                   f"+ block-scaled GEMM in float64 (numpy; elementwise work single-threaded, matmul on "
+                   f"{blas_threads} BLAS threads); {spent:.1f} s of oracle time"),
+        "seconds": spent,
+    }
+
+
+# ---------------------------------------------------------------------------
+# main
+# ---------------------------------------------------------------------------
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="dense", choices=["dense", "contiguous", "masked"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="also run one 1 GiB device copy (calibrates rocprofv3 FETCH/WRITE_SIZE counters)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this library has no multi-GPU path "
+              "(expert/column sharding across GPUs is a design note only); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import moe_grouped_gemm_x128_amd as mg
+    from moe_grouped_gemm_x128_amd import synth
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    torch.cuda.set_device(0)
+    mg.dgmi_init()
+
+    log(f"setting up workload {args.workload}")
+    W = {"dense": DenseWorkload, "contiguous": ContiguousWorkload, "masked": MaskedWorkload}[args.workload](torch, mg, synth)
+    torch.cuda.synchronize()
+
+    for _ in range(args.warmup):
+        W.step()
+    torch.cuda.synchronize()
+    log(f"warmup done ({args.warmup} steps); timing {args.steps} steps")
+
+    nshape = len(W.flops)
+    events = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(nshape)]
+              for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        W.step(events[s])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    log("timed region done")
+
+    if args.copy_probe:
+        src = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    # per-shape average GEMM launch duration (ms)
+    gemm_ms = [float(np.mean([events[s][i][0].elapsed_time(events[s][i][1]) for s in range(args.steps)]))
+               for i in range(nshape)]
+    ms_per_step = wall * 1e3 / args.steps
+    total_flops = float(sum(W.flops))
+    value = total_flops / (ms_per_step * 1e-3) / 1e12
+    mean_launch_ms = float(np.mean(gemm_ms))
+    mean_flops = total_flops / nshape
+    is_masked = args.workload == "masked"
+    if is_masked:
+        mean_bytes = float(np.mean(W.gemm_bytes))
+        achieved = mean_bytes / (mean_launch_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": achieved / HBM_PEAK_GBS, "traffic": None}
+    else:
+        achieved = mean_flops / (mean_launch_ms * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": achieved, "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": achieved / FP8_PEAK_TFLOPS, "traffic": None}
+    roof["kernel"] = "fp8_gemm_kernel"
+    roof["avg_launch_us"] = mean_launch_ms * 1e3
+    roof["per_launch"] = "mean over the workload's GEMM launches of one step (algorithmic work / HIP-event duration)"
+
+    per_shape = []
+    for i in range(nshape):
+        N, K = W.shapes[i]
+        per_shape.append({"N": N, "K": K, "gemm_us": gemm_ms[i] * 1e3,
+                          "tflops": W.flops[i] / (gemm_ms[i] * 1e-3) / 1e12,
+                          "gbs": W.gemm_bytes[i] / (gemm_ms[i] * 1e-3) / 1e9})
+
+    if is_masked:
+        metric = "masked grouped FP8 GEMM GB/s (% HBM)"
+        unit = "GB/s"
+        step_bytes = float(sum(W.gemm_bytes))
+        value = step_bytes / (ms_per_step * 1e-3) / 1e9
+    else:
+        metric = "FP8 block-scaled GEMM TFLOPS (% FP8 MFMA peak)"
+        unit = "TFLOPS"
+
+    out = {
+        "metric": metric,
+        "value": value,
+        "unit": unit,
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8_e4m3",
+        "data": "synthetic N(0,1) float32 inputs, seeded (numpy PCG64); no real activations or weights",
+        "config": W.config(),
+        "roofline": roof,
+        "gemm_per_shape": per_shape,
+        "gemm_only_value": mean_flops / (mean_launch_ms * 1e-3) / 1e12 if not is_masked else achieved,
+    }
+    if not args.no_cpu_baseline and args.workload == "dense":
+        log("timing the CPU oracle on a bounded sample")
+        out["cpu_baseline"] = time_cpu_baseline()
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,189 @@
+/*
+ * dgmi.h -- C ABI of the block-scaled FP8 (grouped) GEMM library for MI355X.
+ *
+ * The library (libdgmi.so) computes DeepGEMM-style FP8 GEMMs with
+ * fine-grained scaling on gfx950: E4M3 operands, one FP32 scale per 1x128
+ * K-block of each activation row and one per 128x128 block of the weights
+ * (or the same scales as power-of-two UE8M0 exponents packed four to an
+ * int32), each 128-wide K-block contracted on the matrix cores and promoted
+ * into an FP32 accumulator multiplied by both scales, BF16 out.
+ *   "DeepInside DeepGEMM: Unpacking DeepSeek's Unified Tensor Core Library
+ *    for SM90 and SM100", section 2 (NT layout, FP32 or packed UE8M0 scale
+ *    factors) and section 4 (fp8_gemm_nt(a, b, a_sf, b_sf, c, bf16)).
+ *
+ * Conventions shared by every entry point
+ *   - Every buffer is device memory allocated and owned by the caller,
+ *     outputs included.  The library never allocates, frees, synchronises,
+ *     reads device memory on the host, or keeps a pointer after returning
+ *     ("DeepGEMM CUDA Graph Compatibility for Masked Grouped GEMMs",
+ *     sections "Eliminating Host-Side Allocation" and "Tensor-Based
+ *     Metadata Arguments").
+ *   - Each call validates shapes/dtypes/strides on the host, then enqueues
+ *     its kernels on `stream` (NULL = the null stream) and returns.  The
+ *     launch configuration depends only on the shapes, never on device
+ *     data, so every entry point except dgmi_init may be captured into a
+ *     hipGraph and replayed (same page, section "Stateless Kernel
+ *     Architecture").  Device faults surface at the caller's next sync.
+ *   - Tensors are described by dg_tensor: shape and strides in ELEMENTS.
+ *     The innermost (last) stride of every data operand must be 1.
+ *   - On error nothing is launched, the call returns a non-zero status and
+ *     dg_last_error() describes it.  Calls are reentrant and thread-safe.
+ */
+#ifndef DGMI_H
+#define DGMI_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* element types */
+enum {
+  DG_F32 = 0,  /* IEEE binary32 */
+  DG_BF16 = 1, /* bfloat16 */
+  DG_E4M3 = 2, /* OCP FP8 E4M3 ("fn": max 448, no inf), one byte */
+  DG_I32 = 3   /* int32: masked_m, grouped_layout, packed UE8M0 scales */
+};
+
+/* status codes */
+enum {
+  DG_OK = 0,
+  DG_INVALID_ARG = 1,   /* null / dtype / ndim / shape / stride / alignment / aliasing */
+  DG_UNSUPPORTED = 2,   /* legal but not implemented (K % 128 != 0, c != NULL) */
+  DG_LAUNCH_FAILED = 3  /* the HIP runtime rejected a launch */
+};
+
+typedef struct dg_tensor {
+  void* data;        /* device pointer, caller-owned */
+  int32_t dtype;     /* DG_* element type */
+  int32_t ndim;      /* 1..4 */
+  int64_t shape[4];
+  int64_t stride[4]; /* in elements */
+} dg_tensor;
+
+/* Message for the last non-zero status returned on this thread. */
+const char* dg_last_error(void);
+
+/* Optional eager set-up (checks that a gfx950 device is current).  Not
+ * capture-safe; every other entry point works without calling it. */
+int dgmi_init(void);
+
+/*
+ * D = A . B^T, block-scaled FP8, BF16 out ("DeepInside DeepGEMM", section 4:
+ * the NT GEMM fp8_gemm_nt with D = C + A @ B.T).
+ *   a   E4M3 [M, K]          row stride lda (elements = bytes), 16-B aligned
+ *   b   E4M3 [N, K]          weights in NT layout (K contiguous)
+ *   sfa F32  [M, K/128]      any strides (K-major or M-major), or
+ *       I32  [M, ceil(K/512)] packed UE8M0 (byte j of word i: K-block 4i+j)
+ *   sfb F32  [ceil(N/128), K/128] or I32 [ceil(N/128), ceil(K/512)]
+ *       sfa and sfb must use the same format.
+ *   c   must be NULL (accumulate form not built: DG_UNSUPPORTED otherwise)
+ *   d   BF16 [M, N], any row stride (innermost stride 1)
+ * D[m,n] = sum_kb (sum_{k in kb} A[m,k] B[n,k]) * sfa[m,kb] * sfb[n/128,kb].
+ * K must be a multiple of 128; M and N are arbitrary.
+ */
+int fp8_gemm_nt(const dg_tensor* a, const dg_tensor* b, const dg_tensor* sfa,
+                const dg_tensor* sfb, const dg_tensor* c, const dg_tensor* d,
+                hipStream_t stream);
+
+/*
+ * Contiguous grouped FP8 GEMM: groups concatenated along M ("DeepGEMM tested
+ * by Novita AI", section on the contiguous layout for prefill / training).
+ *   a   E4M3 [Msum, K], Msum % 128 == 0
+ *   b   E4M3 [G, N, K]
+ *   sfa as fp8_gemm_nt with M = Msum;  sfb [G, ceil(N/128), ...]
+ *   d   BF16 [Msum, N]
+ *   grouped_layout I32 [Msum/128] on the device: group id of each 128-row
+ *       block; a negative id marks a block to skip (its rows of d are not
+ *       written).  Ids >= G are treated as skipped as well.
+ */
+int m_grouped_fp8_gemm_nt_contiguous(const dg_tensor* a, const dg_tensor* b,
+                                     const dg_tensor* sfa, const dg_tensor* sfb,
+                                     const dg_tensor* d, const dg_tensor* grouped_layout,
+                                     hipStream_t stream);
+
+/*
+ * Masked grouped FP8 GEMM for MoE decode ("DeepGEMM CUDA Graph Compatibility
+ * for Masked Grouped GEMMs", section "Tensor-Based Metadata Arguments").
+ *   a   E4M3 [G, max_m, K] (or [G*max_m, K])
+ *   b   E4M3 [G, N, K]
+ *   sfa F32 [G, max_m, K/128] (or [G*max_m, K/128]) or packed I32
+ *   sfb F32 [G, ceil(N/128), K/128] or packed I32
+ *   d   BF16 [G, max_m, N] (or [G*max_m, N])
+ *   masked_m I32 [G] on the device: group g computes its first
+ *       clamp(masked_m[g], 0, max_m) rows; every other row of d is left
+ *       untouched.  Read only by the kernels, never by the host.
+ *   max_m_per_group  rows per group of the padded buffers (fixes the grid).
+ */
+int m_grouped_fp8_gemm_nt_masked(const dg_tensor* a, const dg_tensor* b,
+                                 const dg_tensor* sfa, const dg_tensor* sfb,
+                                 const dg_tensor* d, const dg_tensor* masked_m,
+                                 int64_t max_m_per_group, hipStream_t stream);
+
+/*
+ * Masked grouped BF16 GEMM, argument order of the pages' capture example
+ * (a, b, d, masked_m, max_m_per_group): D[g,m,:] = A[g,m,:] . B[g]^T for
+ * m < clamp(masked_m[g], 0, max_m), FP32 accumulation, BF16 out.
+ *   a BF16 [G, max_m, K] or [G*max_m, K]; b BF16 [G, N, K]; d like a with N.
+ *   K must be a multiple of 64.
+ */
+int m_grouped_bf16_gemm_nt_masked(const dg_tensor* a, const dg_tensor* b,
+                                  const dg_tensor* d, const dg_tensor* masked_m,
+                                  int64_t max_m_per_group, hipStream_t stream);
+
+/*
+ * Per-token FP8 cast: each row of x cut into 1x128 blocks along K; block
+ * scale s = amax/448 (amax floored at 1e-4; with use_ue8m0 rounded up to a
+ * power of two), q = e4m3(x/s) rounded to nearest even after clamping to
+ * +-448 ("DeepInside DeepGEMM", section 5: the FP8 casting helpers).
+ *   x  F32 or BF16 [R, K] or [G, R, K]
+ *   q  E4M3 same shape
+ *   sf F32 [R, ceil(K/128)] (or [G, R, ...]) with any strides
+ */
+int per_token_cast_to_fp8(const dg_tensor* x, const dg_tensor* q, const dg_tensor* sf,
+                          int use_ue8m0, hipStream_t stream);
+
+/*
+ * Per-block FP8 cast over 128x128 blocks (weights): as per_token_cast_to_fp8
+ * with one scale per block.
+ *   x  F32 or BF16 [N, K] or [G, N, K];  q E4M3 same shape
+ *   sf F32 [ceil(N/128), ceil(K/128)] or [G, ...] with any strides
+ */
+int per_block_cast_to_fp8(const dg_tensor* x, const dg_tensor* q, const dg_tensor* sf,
+                          int use_ue8m0, hipStream_t stream);
+
+/*
+ * Pack FP32 power-of-two scales into UE8M0 bytes, four per int32 ("[GH-ISSUE
+ * #414] pack_ue8m0_to_int is not CUDA Graph capture safe", section "Expected
+ * behavior"): byte j of out[..., i] = bits 30..23 of x[..., 4i+j]; missing
+ * tail elements give zero bytes.  Shape and dtype checks stay on the host;
+ * the value check of the issue's Summary (x >= 0 with a zero mantissa) is
+ * done on the device without any host synchronisation: when invalid_count
+ * is not NULL, the number of offending elements is ADDED to the int32 it
+ * points to (device memory; the caller zeroes it).
+ *   x   F32 [..., n] (1 to 3 dims, innermost stride 1)
+ *   out I32 [..., ceil(n/4)] same leading shape
+ */
+int pack_ue8m0_to_int(const dg_tensor* x, const dg_tensor* out, int32_t* invalid_count,
+                      hipStream_t stream);
+
+/* Launch configuration chosen for a GEMM (a pure function of the shapes). */
+typedef struct dg_config {
+  int32_t block_m, block_n;   /* output tile of one workgroup */
+  int32_t threads;            /* workgroup size */
+  int64_t grid;               /* workgroups launched */
+  int32_t lds_bytes;          /* static LDS per workgroup */
+} dg_config;
+
+enum { DG_KIND_DENSE = 0, DG_KIND_CONTIGUOUS = 1, DG_KIND_MASKED = 2, DG_KIND_BF16_MASKED = 3 };
+
+/* Fill *out with the configuration `kind` would launch for these sizes
+ * (M = rows: M, Msum or max_m; G = groups, 1 for dense). */
+int dg_query_config(int32_t kind, int64_t G, int64_t M, int64_t N, int64_t K, dg_config* out);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* DGMI_H */

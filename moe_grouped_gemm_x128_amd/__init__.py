@@ -1,7 +1,23 @@
 """Block-scaled FP8 (grouped) GEMM library for MI355X (gfx950).
 
-The compute path is the HIP library ``libdgmi.so`` built from ``csrc/``;
-this package holds its thin ctypes binding and the seeded synthetic input
-generators.  Importing the package loads nothing; the library is opened on
-first use of the binding.
+The compute path is the HIP library ``libdgmi.so`` built from ``csrc/``
+(``python -m moe_grouped_gemm_x128_amd.build``); this package holds its thin
+ctypes binding (same names and argument order as ``include/dgmi.h``) and the
+seeded synthetic input generators.  Importing the package loads nothing; the
+library is opened on first use and a missing library raises.
 """
+
+from .binding import (  # noqa: F401
+    DgmiError,
+    load_library,
+    last_error,
+    dgmi_init,
+    fp8_gemm_nt,
+    m_grouped_fp8_gemm_nt_contiguous,
+    m_grouped_fp8_gemm_nt_masked,
+    m_grouped_bf16_gemm_nt_masked,
+    per_token_cast_to_fp8,
+    per_block_cast_to_fp8,
+    pack_ue8m0_to_int,
+    query_config,
+)

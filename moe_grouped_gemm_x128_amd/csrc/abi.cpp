@@ -1,0 +1,484 @@
+// Host side of libdgmi: the extern "C" entry points declared in dgmi.h.
+//
+// Every entry point validates its descriptors on the host (dtype, rank,
+// shape consistency, unit innermost stride, alignment, aliasing of the
+// output), then enqueues the kernels on the caller's stream and returns.
+// Nothing here allocates, synchronises or reads device memory, so each call
+// can be captured into a hipGraph ("DeepGEMM CUDA Graph Compatibility for
+// Masked Grouped GEMMs", sections "Eliminating Host-Side Allocation" and
+// "Tensor-Based Metadata Arguments"; "[GH-ISSUE #414] pack_ue8m0_to_int is
+// not CUDA Graph capture safe", section "Expected behavior": shape and dtype
+// checks stay on the host, value checks never synchronise).
+
+#include <stdarg.h>
+#include <stdio.h>
+
+#include <string>
+
+#include "../../include/dgmi.h"
+#include "launch.hpp"
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+int ok() {
+  g_err.clear();
+  return DG_OK;
+}
+
+int elem_size(int32_t dtype) {
+  switch (dtype) {
+    case DG_F32: return 4;
+    case DG_BF16: return 2;
+    case DG_E4M3: return 1;
+    case DG_I32: return 4;
+    default: return 0;
+  }
+}
+
+const char* dtype_name(int32_t dtype) {
+  switch (dtype) {
+    case DG_F32: return "F32";
+    case DG_BF16: return "BF16";
+    case DG_E4M3: return "E4M3";
+    case DG_I32: return "I32";
+    default: return "?";
+  }
+}
+
+// Basic well-formedness: non-null, known dtype, 1..4 dims, non-negative
+// shape, non-negative strides, innermost stride 1 when `unit_inner`.
+int check_basic(const dg_tensor* t, const char* name, bool unit_inner) {
+  if (t == nullptr) return fail(DG_INVALID_ARG, "%s: descriptor is NULL", name);
+  if (elem_size(t->dtype) == 0) return fail(DG_INVALID_ARG, "%s: unknown dtype %d", name, t->dtype);
+  if (t->ndim < 1 || t->ndim > 4) return fail(DG_INVALID_ARG, "%s: ndim %d not in 1..4", name, t->ndim);
+  int64_t numel = 1;
+  for (int i = 0; i < t->ndim; ++i) {
+    if (t->shape[i] < 0) return fail(DG_INVALID_ARG, "%s: negative extent in dim %d", name, i);
+    if (t->stride[i] < 0) return fail(DG_INVALID_ARG, "%s: negative stride in dim %d", name, i);
+    if (t->shape[i] > INT32_MAX) return fail(DG_INVALID_ARG, "%s: extent of dim %d exceeds 2^31-1", name, i);
+    numel *= t->shape[i];
+  }
+  if (numel > 0 && t->data == nullptr) return fail(DG_INVALID_ARG, "%s: data pointer is NULL", name);
+  if (unit_inner && t->shape[t->ndim - 1] > 1 && t->stride[t->ndim - 1] != 1)
+    return fail(DG_INVALID_ARG, "%s: innermost stride must be 1 (got %lld)", name, (long long)t->stride[t->ndim - 1]);
+  return DG_OK;
+}
+
+int check_dtype(const dg_tensor* t, const char* name, int32_t want) {
+  if (t->dtype != want)
+    return fail(DG_INVALID_ARG, "%s: dtype %s, expected %s", name, dtype_name(t->dtype), dtype_name(want));
+  return DG_OK;
+}
+
+// Byte span [lo, hi) touched by a strided tensor (empty => lo == hi).
+void span(const dg_tensor* t, uintptr_t* lo, uintptr_t* hi) {
+  int64_t last = 0;
+  for (int i = 0; i < t->ndim; ++i) {
+    if (t->shape[i] == 0) {
+      *lo = *hi = reinterpret_cast<uintptr_t>(t->data);
+      return;
+    }
+    last += (t->shape[i] - 1) * t->stride[i];
+  }
+  *lo = reinterpret_cast<uintptr_t>(t->data);
+  *hi = *lo + (uintptr_t)((last + 1) * elem_size(t->dtype));
+}
+
+int check_no_alias(const dg_tensor* out, const char* oname, const dg_tensor* in, const char* iname) {
+  if (in == nullptr) return DG_OK;
+  uintptr_t a0, a1, b0, b1;
+  span(out, &a0, &a1);
+  span(in, &b0, &b1);
+  if (a0 < a1 && b0 < b1 && a0 < b1 && b0 < a1)
+    return fail(DG_INVALID_ARG, "%s overlaps %s in memory", oname, iname);
+  return DG_OK;
+}
+
+bool aligned(const void* p, int bytes) { return (reinterpret_cast<uintptr_t>(p) % bytes) == 0; }
+
+#define DG_TRY(expr)             \
+  do {                           \
+    int rc_ = (expr);            \
+    if (rc_ != DG_OK) return rc_; \
+  } while (0)
+
+// A matrix-like operand viewed as [G, R, C]: either 3-D, or 2-D with R = G*rows
+// split by `rows_per_group` (rows_per_group <= 0: 2-D means a single group).
+struct View3 {
+  int64_t G, R, C;
+  int64_t sg, sr;
+};
+
+int view3(const dg_tensor* t, const char* name, int64_t G_expect, int64_t rows_per_group, View3* v) {
+  if (t->ndim == 3) {
+    v->G = t->shape[0];
+    v->R = t->shape[1];
+    v->C = t->shape[2];
+    v->sg = t->stride[0];
+    v->sr = t->stride[1];
+  } else if (t->ndim == 2) {
+    if (rows_per_group > 0) {
+      if (t->shape[0] != G_expect * rows_per_group)
+        return fail(DG_INVALID_ARG, "%s: 2-D leading extent %lld != groups*rows %lld", name,
+                    (long long)t->shape[0], (long long)(G_expect * rows_per_group));
+      v->G = G_expect;
+      v->R = rows_per_group;
+      v->sg = rows_per_group * t->stride[0];
+    } else {
+      v->G = 1;
+      v->R = t->shape[0];
+      v->sg = 0;
+    }
+    v->C = t->shape[1];
+    v->sr = t->stride[0];
+  } else {
+    return fail(DG_INVALID_ARG, "%s: expected 2 or 3 dims, got %d", name, t->ndim);
+  }
+  if (G_expect >= 0 && v->G != G_expect)
+    return fail(DG_INVALID_ARG, "%s: %lld groups, expected %lld", name, (long long)v->G, (long long)G_expect);
+  return DG_OK;
+}
+
+// Scale-factor operand of the FP8 GEMMs: F32 [.., rows, nkb] or packed I32
+// [.., rows, ceil(nkb/4)]; any strides.
+int check_scales(const dg_tensor* t, const char* name, int sf_fmt, int64_t G_expect, int64_t rows_per_group,
+                 int64_t rows, int64_t nkb, View3* v) {
+  DG_TRY(check_basic(t, name, false));
+  DG_TRY(check_dtype(t, name, sf_fmt == dgmi::SF_F32 ? DG_F32 : DG_I32));
+  DG_TRY(view3(t, name, G_expect, rows_per_group, v));
+  const int64_t cols = sf_fmt == dgmi::SF_F32 ? nkb : (nkb + 3) / 4;
+  if (v->R != rows || v->C != cols)
+    return fail(DG_INVALID_ARG, "%s: shape [..,%lld,%lld], expected [..,%lld,%lld]", name, (long long)v->R,
+                (long long)v->C, (long long)rows, (long long)cols);
+  return DG_OK;
+}
+
+int check_launch(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(DG_LAUNCH_FAILED, "%s: launch failed: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+// Common FP8 GEMM validation.  mode: dense / contig / masked.
+int fp8_gemm_common(int mode, const dg_tensor* a, const dg_tensor* b, const dg_tensor* sfa, const dg_tensor* sfb,
+                    const dg_tensor* c, const dg_tensor* d, const dg_tensor* meta, int64_t max_m, hipStream_t stream,
+                    const char* fname) {
+  DG_TRY(check_basic(a, "a", true));
+  DG_TRY(check_basic(b, "b", true));
+  DG_TRY(check_basic(d, "d", true));
+  DG_TRY(check_dtype(a, "a", DG_E4M3));
+  DG_TRY(check_dtype(b, "b", DG_E4M3));
+  DG_TRY(check_dtype(d, "d", DG_BF16));
+  if (c != nullptr) return fail(DG_UNSUPPORTED, "%s: the accumulate input c is not supported (pass NULL)", fname);
+  if (sfa == nullptr || sfb == nullptr) return fail(DG_INVALID_ARG, "%s: scale descriptors must not be NULL", fname);
+  if (sfa->dtype != sfb->dtype) return fail(DG_INVALID_ARG, "%s: sfa and sfb must have the same dtype", fname);
+  const int sf_fmt = sfa->dtype == DG_I32 ? dgmi::SF_UE8M0 : dgmi::SF_F32;
+
+  View3 va, vb, vd, vsa, vsb;
+  int64_t G = 1, rows_pg = 0;
+  if (mode == dgmi::MODE_DENSE) {
+    if (a->ndim != 2 || b->ndim != 2 || d->ndim != 2) return fail(DG_INVALID_ARG, "%s: a, b, d must be 2-D", fname);
+    DG_TRY(view3(b, "b", 1, 0, &vb));
+  } else {
+    if (b->ndim != 3) return fail(DG_INVALID_ARG, "%s: b must be [G, N, K]", fname);
+    G = b->shape[0];
+    DG_TRY(view3(b, "b", G, 0, &vb));
+  }
+  if (mode == dgmi::MODE_MASKED) {
+    if (max_m < 0) return fail(DG_INVALID_ARG, "%s: max_m_per_group must be >= 0", fname);
+    rows_pg = max_m;
+    DG_TRY(view3(a, "a", G, rows_pg, &va));
+    DG_TRY(view3(d, "d", G, rows_pg, &vd));
+  } else {
+    if (a->ndim != 2 || d->ndim != 2) return fail(DG_INVALID_ARG, "%s: a and d must be 2-D", fname);
+    DG_TRY(view3(a, "a", 1, 0, &va));
+    DG_TRY(view3(d, "d", 1, 0, &vd));
+  }
+  const int64_t M = va.R, K = va.C, N = vb.R;
+  if (vb.C != K) return fail(DG_INVALID_ARG, "%s: K mismatch: a has %lld, b has %lld", fname, (long long)K, (long long)vb.C);
+  if (vd.R != M || vd.C != N)
+    return fail(DG_INVALID_ARG, "%s: d is [..,%lld,%lld], expected [..,%lld,%lld]", fname, (long long)vd.R,
+                (long long)vd.C, (long long)M, (long long)N);
+  if (mode == dgmi::MODE_MASKED && M != max_m)
+    return fail(DG_INVALID_ARG, "%s: a has %lld rows per group, max_m_per_group is %lld", fname, (long long)M,
+                (long long)max_m);
+  if (K % 128 != 0) return fail(DG_UNSUPPORTED, "%s: K = %lld is not a multiple of 128", fname, (long long)K);
+  const int64_t nkb = K / 128, nnb = (N + 127) / 128;
+  DG_TRY(check_scales(sfa, "sfa", sf_fmt, mode == dgmi::MODE_MASKED ? G : 1, rows_pg, M, nkb, &vsa));
+  DG_TRY(check_scales(sfb, "sfb", sf_fmt, mode == dgmi::MODE_DENSE ? 1 : G, 0, nnb, nkb, &vsb));
+  if (mode == dgmi::MODE_DENSE && (sfb->ndim != 2 || sfa->ndim != 2))
+    return fail(DG_INVALID_ARG, "%s: sfa and sfb must be 2-D", fname);
+  if (mode == dgmi::MODE_CONTIG && sfb->ndim != 3) return fail(DG_INVALID_ARG, "%s: sfb must be [G, ceil(N/128), ..]", fname);
+
+  // alignment: 16-B operand rows (the kernels load 16-B chunks), 16-B output rows
+  if (!aligned(a->data, 16) || !aligned(b->data, 16) || va.sr % 16 || vb.sr % 16 || va.sg % 16 || vb.sg % 16)
+    return fail(DG_INVALID_ARG, "%s: a and b need 16-byte aligned bases and row/group strides", fname);
+  if (!aligned(d->data, 2)) return fail(DG_INVALID_ARG, "%s: d must be 2-byte aligned", fname);
+  if (!aligned(sfa->data, 4) || !aligned(sfb->data, 4)) return fail(DG_INVALID_ARG, "%s: scales must be 4-byte aligned", fname);
+
+  if (mode == dgmi::MODE_CONTIG) {
+    if (M % 128 != 0) return fail(DG_INVALID_ARG, "%s: Msum = %lld is not a multiple of 128", fname, (long long)M);
+    DG_TRY(check_basic(meta, "grouped_layout", true));
+    DG_TRY(check_dtype(meta, "grouped_layout", DG_I32));
+    if (meta->ndim != 1 || meta->shape[0] != M / 128)
+      return fail(DG_INVALID_ARG, "%s: grouped_layout must be I32 [Msum/128 = %lld]", fname, (long long)(M / 128));
+  } else if (mode == dgmi::MODE_MASKED) {
+    DG_TRY(check_basic(meta, "masked_m", true));
+    DG_TRY(check_dtype(meta, "masked_m", DG_I32));
+    if (meta->ndim != 1 || meta->shape[0] != G)
+      return fail(DG_INVALID_ARG, "%s: masked_m must be I32 [G = %lld]", fname, (long long)G);
+  }
+  DG_TRY(check_no_alias(d, "d", a, "a"));
+  DG_TRY(check_no_alias(d, "d", b, "b"));
+  DG_TRY(check_no_alias(d, "d", sfa, "sfa"));
+  DG_TRY(check_no_alias(d, "d", sfb, "sfb"));
+  if (meta != nullptr) DG_TRY(check_no_alias(d, "d", meta, "metadata"));
+
+  dgmi::Fp8GemmParams p = {};
+  p.a = static_cast<const uint8_t*>(a->data);
+  p.b = static_cast<const uint8_t*>(b->data);
+  p.sfa = sfa->data;
+  p.sfb = sfb->data;
+  p.d = static_cast<uint16_t*>(d->data);
+  p.meta = meta ? static_cast<const int32_t*>(meta->data) : nullptr;
+  p.lda = va.sr;
+  p.a_gs = va.sg;
+  p.ldb = vb.sr;
+  p.b_gs = vb.sg;
+  p.sfa_sm = vsa.sr;
+  p.sfa_sk = sfa->stride[sfa->ndim - 1];
+  p.sfa_gs = vsa.sg;
+  p.sfb_sn = vsb.sr;
+  p.sfb_sk = sfb->stride[sfb->ndim - 1];
+  p.sfb_gs = vsb.sg;
+  p.ldd = vd.sr;
+  p.d_gs = vd.sg;
+  p.M = (int32_t)M;
+  p.N = (int32_t)N;
+  p.K = (int32_t)K;
+  p.G = (int32_t)G;
+  if (M == 0 || N == 0 || G == 0) return ok();
+  if (K == 0) return fail(DG_UNSUPPORTED, "%s: K = 0 is not supported", fname);
+  return check_launch(dgmi::launch_fp8_gemm(p, mode, sf_fmt, stream), fname);
+}
+
+// Quantizer validation: x [R, K] or [G, R, K]; q same shape; sf [.., R', KB].
+int quant_common(const dg_tensor* x, const dg_tensor* q, const dg_tensor* sf, int use_ue8m0, hipStream_t stream,
+                 bool per_block, const char* fname) {
+  DG_TRY(check_basic(x, "x", true));
+  DG_TRY(check_basic(q, "q", true));
+  DG_TRY(check_basic(sf, "sf", false));
+  if (x->dtype != DG_F32 && x->dtype != DG_BF16) return fail(DG_INVALID_ARG, "%s: x must be F32 or BF16", fname);
+  DG_TRY(check_dtype(q, "q", DG_E4M3));
+  DG_TRY(check_dtype(sf, "sf", DG_F32));
+  if (x->ndim != q->ndim || x->ndim != sf->ndim || (x->ndim != 2 && x->ndim != 3))
+    return fail(DG_INVALID_ARG, "%s: x, q and sf must all be 2-D or all 3-D", fname);
+  for (int i = 0; i < x->ndim; ++i)
+    if (x->shape[i] != q->shape[i]) return fail(DG_INVALID_ARG, "%s: q must have the shape of x", fname);
+  View3 vx, vq, vs;
+  DG_TRY(view3(x, "x", -1, 0, &vx));
+  DG_TRY(view3(q, "q", vx.G, 0, &vq));
+  DG_TRY(view3(sf, "sf", vx.G, 0, &vs));
+  const int64_t R = vx.R, K = vx.C;
+  const int64_t srows = per_block ? (R + 127) / 128 : R;
+  if (vs.R != srows || vs.C != (K + 127) / 128)
+    return fail(DG_INVALID_ARG, "%s: sf is [..,%lld,%lld], expected [..,%lld,%lld]", fname, (long long)vs.R,
+                (long long)vs.C, (long long)srows, (long long)((K + 127) / 128));
+  const int xe = elem_size(x->dtype);
+  if (!aligned(x->data, 16) || (vx.sr * xe) % 16 || (vx.sg * xe) % 16)
+    return fail(DG_INVALID_ARG, "%s: x needs a 16-byte aligned base and row/group strides", fname);
+  if (!aligned(q->data, 4) || vq.sr % 4 || vq.sg % 4)
+    return fail(DG_INVALID_ARG, "%s: q needs a 4-byte aligned base and row/group strides", fname);
+  if (!aligned(sf->data, 4)) return fail(DG_INVALID_ARG, "%s: sf must be 4-byte aligned", fname);
+  DG_TRY(check_no_alias(q, "q", x, "x"));
+  DG_TRY(check_no_alias(sf, "sf", x, "x"));
+  DG_TRY(check_no_alias(sf, "sf", q, "q"));
+  dgmi::QuantArgs p = {};
+  p.x = x->data;
+  p.x_bf16 = x->dtype == DG_BF16;
+  p.sx_g = vx.sg;
+  p.sx_r = vx.sr;
+  p.q = static_cast<uint8_t*>(q->data);
+  p.sq_g = vq.sg;
+  p.sq_r = vq.sr;
+  p.sf = static_cast<float*>(sf->data);
+  p.ssf_g = vs.sg;
+  p.ssf_r = vs.sr;
+  p.ssf_k = sf->stride[sf->ndim - 1];
+  p.G = (int32_t)vx.G;
+  p.R = (int32_t)R;
+  p.K = (int32_t)K;
+  p.ue8m0 = use_ue8m0 ? 1 : 0;
+  if (vx.G == 0 || R == 0 || K == 0) return ok();
+  return check_launch(per_block ? dgmi::launch_per_block(p, stream) : dgmi::launch_per_token(p, stream), fname);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* dg_last_error(void) { return g_err.c_str(); }
+
+int dgmi_init(void) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(DG_LAUNCH_FAILED, "dgmi_init: no HIP device: %s", hipGetErrorString(e));
+  hipDeviceProp_t prop;
+  e = hipGetDeviceProperties(&prop, dev);
+  if (e != hipSuccess) return fail(DG_LAUNCH_FAILED, "dgmi_init: %s", hipGetErrorString(e));
+  if (std::string(prop.gcnArchName).rfind("gfx950", 0) != 0)
+    return fail(DG_UNSUPPORTED, "dgmi_init: device %d is %s, this library is built for gfx950", dev, prop.gcnArchName);
+  return ok();
+}
+
+int fp8_gemm_nt(const dg_tensor* a, const dg_tensor* b, const dg_tensor* sfa, const dg_tensor* sfb,
+                const dg_tensor* c, const dg_tensor* d, hipStream_t stream) {
+  return fp8_gemm_common(dgmi::MODE_DENSE, a, b, sfa, sfb, c, d, nullptr, 0, stream, "fp8_gemm_nt");
+}
+
+int m_grouped_fp8_gemm_nt_contiguous(const dg_tensor* a, const dg_tensor* b, const dg_tensor* sfa,
+                                     const dg_tensor* sfb, const dg_tensor* d, const dg_tensor* grouped_layout,
+                                     hipStream_t stream) {
+  if (grouped_layout == nullptr) return fail(DG_INVALID_ARG, "m_grouped_fp8_gemm_nt_contiguous: grouped_layout is NULL");
+  return fp8_gemm_common(dgmi::MODE_CONTIG, a, b, sfa, sfb, nullptr, d, grouped_layout, 0, stream,
+                         "m_grouped_fp8_gemm_nt_contiguous");
+}
+
+int m_grouped_fp8_gemm_nt_masked(const dg_tensor* a, const dg_tensor* b, const dg_tensor* sfa, const dg_tensor* sfb,
+                                 const dg_tensor* d, const dg_tensor* masked_m, int64_t max_m_per_group,
+                                 hipStream_t stream) {
+  if (masked_m == nullptr) return fail(DG_INVALID_ARG, "m_grouped_fp8_gemm_nt_masked: masked_m is NULL");
+  return fp8_gemm_common(dgmi::MODE_MASKED, a, b, sfa, sfb, nullptr, d, masked_m, max_m_per_group, stream,
+                         "m_grouped_fp8_gemm_nt_masked");
+}
+
+int m_grouped_bf16_gemm_nt_masked(const dg_tensor* a, const dg_tensor* b, const dg_tensor* d,
+                                  const dg_tensor* masked_m, int64_t max_m_per_group, hipStream_t stream) {
+  const char* fname = "m_grouped_bf16_gemm_nt_masked";
+  DG_TRY(check_basic(a, "a", true));
+  DG_TRY(check_basic(b, "b", true));
+  DG_TRY(check_basic(d, "d", true));
+  DG_TRY(check_dtype(a, "a", DG_BF16));
+  DG_TRY(check_dtype(b, "b", DG_BF16));
+  DG_TRY(check_dtype(d, "d", DG_BF16));
+  if (masked_m == nullptr) return fail(DG_INVALID_ARG, "%s: masked_m is NULL", fname);
+  DG_TRY(check_basic(masked_m, "masked_m", true));
+  DG_TRY(check_dtype(masked_m, "masked_m", DG_I32));
+  if (b->ndim != 3) return fail(DG_INVALID_ARG, "%s: b must be [G, N, K]", fname);
+  if (max_m_per_group < 0) return fail(DG_INVALID_ARG, "%s: max_m_per_group must be >= 0", fname);
+  const int64_t G = b->shape[0];
+  View3 va, vb, vd;
+  DG_TRY(view3(b, "b", G, 0, &vb));
+  DG_TRY(view3(a, "a", G, max_m_per_group, &va));
+  DG_TRY(view3(d, "d", G, max_m_per_group, &vd));
+  const int64_t M = va.R, K = va.C, N = vb.R;
+  if (M != max_m_per_group) return fail(DG_INVALID_ARG, "%s: a has %lld rows per group, max_m_per_group is %lld", fname, (long long)M, (long long)max_m_per_group);
+  if (vb.C != K) return fail(DG_INVALID_ARG, "%s: K mismatch", fname);
+  if (vd.R != M || vd.C != N) return fail(DG_INVALID_ARG, "%s: d must be [G, max_m, N]", fname);
+  if (masked_m->ndim != 1 || masked_m->shape[0] != G) return fail(DG_INVALID_ARG, "%s: masked_m must be I32 [G]", fname);
+  if (K % 64 != 0) return fail(DG_UNSUPPORTED, "%s: K = %lld is not a multiple of 64", fname, (long long)K);
+  if (!aligned(a->data, 16) || !aligned(b->data, 16) || va.sr % 8 || vb.sr % 8 || va.sg % 8 || vb.sg % 8)
+    return fail(DG_INVALID_ARG, "%s: a and b need 16-byte aligned bases and row/group strides", fname);
+  if (!aligned(d->data, 2)) return fail(DG_INVALID_ARG, "%s: d must be 2-byte aligned", fname);
+  DG_TRY(check_no_alias(d, "d", a, "a"));
+  DG_TRY(check_no_alias(d, "d", b, "b"));
+  DG_TRY(check_no_alias(d, "d", masked_m, "masked_m"));
+  dgmi::Bf16GemmParams p = {};
+  p.a = static_cast<const uint16_t*>(a->data);
+  p.b = static_cast<const uint16_t*>(b->data);
+  p.d = static_cast<uint16_t*>(d->data);
+  p.masked_m = static_cast<const int32_t*>(masked_m->data);
+  p.lda = va.sr;
+  p.a_gs = va.sg;
+  p.ldb = vb.sr;
+  p.b_gs = vb.sg;
+  p.ldd = vd.sr;
+  p.d_gs = vd.sg;
+  p.max_m = (int32_t)M;
+  p.N = (int32_t)N;
+  p.K = (int32_t)K;
+  p.G = (int32_t)G;
+  if (G == 0 || M == 0 || N == 0) return ok();
+  if (K == 0) return fail(DG_UNSUPPORTED, "%s: K = 0 is not supported", fname);
+  return check_launch(dgmi::launch_bf16_masked(p, stream), fname);
+}
+
+int per_token_cast_to_fp8(const dg_tensor* x, const dg_tensor* q, const dg_tensor* sf, int use_ue8m0,
+                          hipStream_t stream) {
+  return quant_common(x, q, sf, use_ue8m0, stream, false, "per_token_cast_to_fp8");
+}
+
+int per_block_cast_to_fp8(const dg_tensor* x, const dg_tensor* q, const dg_tensor* sf, int use_ue8m0,
+                          hipStream_t stream) {
+  return quant_common(x, q, sf, use_ue8m0, stream, true, "per_block_cast_to_fp8");
+}
+
+int pack_ue8m0_to_int(const dg_tensor* x, const dg_tensor* out, int32_t* invalid_count, hipStream_t stream) {
+  const char* fname = "pack_ue8m0_to_int";
+  DG_TRY(check_basic(x, "x", true));
+  DG_TRY(check_basic(out, "out", true));
+  DG_TRY(check_dtype(x, "x", DG_F32));
+  DG_TRY(check_dtype(out, "out", DG_I32));
+  if (x->ndim != out->ndim || x->ndim > 3) return fail(DG_INVALID_ARG, "%s: x and out must have the same rank (1..3)", fname);
+  for (int i = 0; i + 1 < x->ndim; ++i)
+    if (x->shape[i] != out->shape[i]) return fail(DG_INVALID_ARG, "%s: leading shapes of x and out differ", fname);
+  const int64_t n = x->shape[x->ndim - 1];
+  const int64_t nw = (n + 3) / 4;
+  if (out->shape[out->ndim - 1] != nw)
+    return fail(DG_INVALID_ARG, "%s: out has %lld words per row, expected ceil(%lld/4) = %lld", fname,
+                (long long)out->shape[out->ndim - 1], (long long)n, (long long)nw);
+  if (!aligned(x->data, 4) || !aligned(out->data, 4)) return fail(DG_INVALID_ARG, "%s: x and out must be 4-byte aligned", fname);
+  DG_TRY(check_no_alias(out, "out", x, "x"));
+  dgmi::PackArgs p = {};
+  p.x = static_cast<const float*>(x->data);
+  p.out = static_cast<int32_t*>(out->data);
+  p.n = (int32_t)n;
+  p.nw = (int32_t)nw;
+  p.invalid = invalid_count;
+  if (x->ndim == 1) {
+    p.G = 1; p.R = 1; p.sx_g = p.sx_r = 0; p.so_g = p.so_r = 0;
+  } else if (x->ndim == 2) {
+    p.G = 1; p.R = (int32_t)x->shape[0]; p.sx_g = 0; p.sx_r = x->stride[0]; p.so_g = 0; p.so_r = out->stride[0];
+  } else {
+    p.G = (int32_t)x->shape[0]; p.R = (int32_t)x->shape[1];
+    p.sx_g = x->stride[0]; p.sx_r = x->stride[1]; p.so_g = out->stride[0]; p.so_r = out->stride[1];
+  }
+  if (p.G == 0 || p.R == 0 || nw == 0) return ok();
+  return check_launch(dgmi::launch_pack_ue8m0(p, stream), fname);
+}
+
+int dg_query_config(int32_t kind, int64_t G, int64_t M, int64_t N, int64_t K, dg_config* out) {
+  if (out == nullptr) return fail(DG_INVALID_ARG, "dg_query_config: out is NULL");
+  if (G < 0 || M < 0 || N < 0 || K < 0) return fail(DG_INVALID_ARG, "dg_query_config: negative size");
+  dgmi::TileCfg c;
+  int64_t grid;
+  if (kind == DG_KIND_BF16_MASKED) {
+    c = dgmi::bf16_masked_config(G, M, N, K);
+    grid = dgmi::bf16_masked_grid(c, G, M, N);
+  } else if (kind >= DG_KIND_DENSE && kind <= DG_KIND_MASKED) {
+    const int mode = kind == DG_KIND_DENSE ? dgmi::MODE_DENSE : (kind == DG_KIND_CONTIGUOUS ? dgmi::MODE_CONTIG : dgmi::MODE_MASKED);
+    c = dgmi::fp8_gemm_config(mode, G, M, N, K);
+    grid = dgmi::fp8_gemm_grid(c, mode, G, M, N);
+  } else {
+    return fail(DG_INVALID_ARG, "dg_query_config: unknown kind %d", kind);
+  }
+  out->block_m = c.bm;
+  out->block_n = c.bn;
+  out->threads = c.threads;
+  out->grid = grid;
+  out->lds_bytes = c.lds_bytes;
+  return ok();
+}
+
+}  // extern "C"

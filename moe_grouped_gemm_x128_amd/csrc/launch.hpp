@@ -1,0 +1,54 @@
+// Kernel launchers of libdgmi, called by the host-side ABI (abi.cpp) after
+// it has validated every argument.  Internal interface.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "common.hpp"
+
+namespace dgmi {
+
+// Quantizer arguments.  x is viewed as [G, R, K] (R = rows, or N for the
+// per-block cast); strides in elements.  sf is [G, R or ceil(R/128), ceil(K/128)].
+struct QuantArgs {
+  const void* x;
+  int32_t x_bf16;
+  int64_t sx_g, sx_r;
+  uint8_t* q;
+  int64_t sq_g, sq_r;
+  float* sf;
+  int64_t ssf_g, ssf_r, ssf_k;
+  int32_t G, R, K;
+  int32_t ue8m0;
+};
+
+struct PackArgs {
+  const float* x;
+  int64_t sx_g, sx_r;
+  int32_t* out;
+  int64_t so_g, so_r;
+  int32_t G, R, n, nw;
+  int32_t* invalid;
+};
+
+// Tile configuration of a GEMM launch (a pure function of the shapes).
+struct TileCfg {
+  int bm, bn, threads, lds_bytes;
+  int variant;  // index of the kernel instance
+};
+
+hipError_t launch_per_token(const QuantArgs& p, hipStream_t stream);
+hipError_t launch_per_block(const QuantArgs& p, hipStream_t stream);
+hipError_t launch_pack_ue8m0(const PackArgs& p, hipStream_t stream);
+
+// FP8 GEMM: choose the tile for (mode, G, M, N, K) and launch.
+TileCfg fp8_gemm_config(int mode, int64_t G, int64_t M, int64_t N, int64_t K);
+int64_t fp8_gemm_grid(const TileCfg& cfg, int mode, int64_t G, int64_t M, int64_t N);
+hipError_t launch_fp8_gemm(Fp8GemmParams p, int mode, int sf_fmt, hipStream_t stream);
+
+TileCfg bf16_masked_config(int64_t G, int64_t max_m, int64_t N, int64_t K);
+int64_t bf16_masked_grid(const TileCfg& cfg, int64_t G, int64_t max_m, int64_t N);
+hipError_t launch_bf16_masked(Bf16GemmParams p, hipStream_t stream);
+
+}  // namespace dgmi

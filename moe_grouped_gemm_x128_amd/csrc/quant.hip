@@ -1,0 +1,229 @@
+// FP8 quantizers (per-token 1x128 and per-block 128x128) and the UE8M0
+// packing kernel, gfx950.
+//
+// What they compute ("DeepInside DeepGEMM", sections 2 and 5: FP32 scaling
+// factors per block, packed UE8M0 scales four to an int, and the FP8
+// casting helpers that feed fp8_gemm_nt):
+//   amax = max |x| over the block, floored at 1e-4
+//   s    = amax / 448                      (correctly rounded binary32 division)
+//   s    = smallest power of two >= s      (UE8M0 scales only)
+//   q    = e4m3(clamp(x / s, -448, 448))   (round to nearest even)
+// Packing ("[GH-ISSUE #414] pack_ue8m0_to_int is not CUDA Graph capture
+// safe", section "Expected behavior"): the exponent byte of four
+// consecutive scales per int32; the value check of the issue's Summary is a
+// device-side count, never a host synchronisation.
+//
+// All three are HBM-bound streaming kernels: one read of x and one write of
+// q per element, with the block reduction held in registers.
+
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace dgmi {
+
+namespace {
+
+__device__ __forceinline__ float load_elem(const float* p) { return *p; }
+__device__ __forceinline__ float load_elem(const uint16_t* p) { return bf16_to_f32(*p); }
+
+// Four consecutive elements starting at p (16-B aligned for f32, 8-B for bf16).
+__device__ __forceinline__ void load4(const float* p, float v[4]) {
+  float4 t = *reinterpret_cast<const float4*>(p);
+  v[0] = t.x; v[1] = t.y; v[2] = t.z; v[3] = t.w;
+}
+__device__ __forceinline__ void load4(const uint16_t* p, float v[4]) {
+  uint2 t = *reinterpret_cast<const uint2*>(p);
+  v[0] = __uint_as_float(t.x << 16);
+  v[1] = __uint_as_float(t.x & 0xffff0000u);
+  v[2] = __uint_as_float(t.y << 16);
+  v[3] = __uint_as_float(t.y & 0xffff0000u);
+}
+
+// Block scale from the block maximum.
+__device__ __forceinline__ float block_scale(float amax, int ue8m0) {
+  amax = fmaxf(amax, 1e-4f);
+  float s = __fdiv_rn(amax, 448.0f);
+  if (ue8m0) {
+    uint32_t u = __float_as_uint(s);  // s is a positive normal number
+    if (u & 0x007fffffu) u = (u & 0x7f800000u) + 0x00800000u;
+    s = __uint_as_float(u);
+  }
+  return s;
+}
+
+// Four values -> four E4M3 bytes (little-endian in one word), x / s rounded
+// to nearest even by the hardware conversion after clamping to +-448.
+__device__ __forceinline__ uint32_t encode4(const float v[4], float s) {
+  float t[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) t[j] = fminf(fmaxf(__fdiv_rn(v[j], s), -448.0f), 448.0f);
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(t[0], t[1], 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(t[2], t[3], w, true);
+  return (uint32_t)w;
+}
+
+__device__ __forceinline__ uint32_t encode1(float v, float s) {
+  float t = fminf(fmaxf(__fdiv_rn(v, s), -448.0f), 448.0f);
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(t, 0.0f, 0, false) & 0xffu;
+}
+
+// ---------------------------------------------------------------------------
+// per-token: one half-wave (32 lanes x 4 elements) per 1x128 block
+// ---------------------------------------------------------------------------
+template <typename TIn>
+__global__ __launch_bounds__(256) void per_token_kernel(QuantArgs p) {
+  const TIn* __restrict__ x = static_cast<const TIn*>(p.x);
+  const int lane32 = threadIdx.x & 31;
+  const int64_t KB = (p.K + 127) / 128;
+  const int64_t total = (int64_t)p.G * p.R * KB;
+  const int64_t blk = (int64_t)blockIdx.x * 8 + (threadIdx.x >> 5);
+  if (blk >= total) return;  // whole half-waves only; the shuffles below stay within a half
+  const int kb = (int)(blk % KB);
+  const int64_t rr = blk / KB;
+  const int r = (int)(rr % p.R);
+  const int g = (int)(rr / p.R);
+  const TIn* xr = x + g * p.sx_g + r * p.sx_r;
+  const int k0 = kb * 128 + lane32 * 4;
+
+  float v[4];
+  if (k0 + 3 < p.K) {
+    load4(xr + k0, v);
+  } else {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) v[j] = (k0 + j < p.K) ? load_elem(xr + k0 + j) : 0.0f;
+  }
+  float amax = fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3])));
+#pragma unroll
+  for (int off = 16; off > 0; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 32));
+  const float s = block_scale(amax, p.ue8m0);
+
+  uint8_t* qr = p.q + g * p.sq_g + r * p.sq_r;
+  if (k0 + 3 < p.K) {
+    *reinterpret_cast<uint32_t*>(qr + k0) = encode4(v, s);
+  } else {
+    for (int j = 0; j < 4; ++j)
+      if (k0 + j < p.K) qr[k0 + j] = (uint8_t)encode1(v[j], s);
+  }
+  if (lane32 == 0) p.sf[g * p.ssf_g + r * p.ssf_r + kb * p.ssf_k] = s;
+}
+
+// ---------------------------------------------------------------------------
+// per-block: one workgroup (256 threads) per 128x128 block; thread t owns
+// columns 4*(t%32)..+3 of rows t/32 + 8j, j = 0..15 (64 values in registers)
+// ---------------------------------------------------------------------------
+template <typename TIn>
+__global__ __launch_bounds__(256) void per_block_kernel(QuantArgs p) {
+  __shared__ float red[4];
+  const TIn* __restrict__ x = static_cast<const TIn*>(p.x);
+  const int NB = (p.R + 127) / 128, KB = (p.K + 127) / 128;
+  int blk = blockIdx.x;
+  const int kb = blk % KB;
+  blk /= KB;
+  const int nb = blk % NB;
+  const int g = blk / NB;
+  const int tid = threadIdx.x;
+  const int c0 = kb * 128 + (tid & 31) * 4;
+  const int rbase = nb * 128 + (tid >> 5);
+  const TIn* xg = x + g * p.sx_g;
+  const bool full_cols = c0 + 3 < p.K;
+
+  float v[16][4];
+  float amax = 0.0f;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    const int r = rbase + 8 * j;
+    if (r < p.R && full_cols) {
+      load4(xg + (int64_t)r * p.sx_r + c0, v[j]);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        v[j][e] = (r < p.R && c0 + e < p.K) ? load_elem(xg + (int64_t)r * p.sx_r + c0 + e) : 0.0f;
+    }
+    amax = fmaxf(amax, fmaxf(fmaxf(fabsf(v[j][0]), fabsf(v[j][1])), fmaxf(fabsf(v[j][2]), fabsf(v[j][3]))));
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 64));
+  if ((tid & 63) == 0) red[tid >> 6] = amax;
+  __syncthreads();
+  amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  const float s = block_scale(amax, p.ue8m0);
+
+  uint8_t* qg = p.q + g * p.sq_g;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    const int r = rbase + 8 * j;
+    if (r >= p.R) continue;
+    uint8_t* qr = qg + (int64_t)r * p.sq_r;
+    if (full_cols) {
+      *reinterpret_cast<uint32_t*>(qr + c0) = encode4(v[j], s);
+    } else {
+      for (int e = 0; e < 4; ++e)
+        if (c0 + e < p.K) qr[c0 + e] = (uint8_t)encode1(v[j][e], s);
+    }
+  }
+  if (tid == 0) p.sf[g * p.ssf_g + nb * p.ssf_r + kb * p.ssf_k] = s;
+}
+
+// ---------------------------------------------------------------------------
+// UE8M0 pack: one thread per output int32
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void pack_ue8m0_kernel(PackArgs p) {
+  const int64_t total = (int64_t)p.G * p.R * p.nw;
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  int bad = 0;
+  if (i < total) {
+    const int w = (int)(i % p.nw);
+    const int64_t rr = i / p.nw;
+    const int r = (int)(rr % p.R);
+    const int g = (int)(rr / p.R);
+    const float* xr = p.x + g * p.sx_g + r * p.sx_r;
+    uint32_t word = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int k = 4 * w + j;
+      if (k < p.n) {
+        const uint32_t bits = __float_as_uint(xr[k]);
+        word |= ((bits >> 23) & 0xffu) << (8 * j);
+        bad += ((bits >> 31) != 0u || (bits & 0x007fffffu) != 0u) ? 1 : 0;
+      }
+    }
+    p.out[g * p.so_g + r * p.so_r + w] = (int32_t)word;
+  }
+  if (p.invalid != nullptr) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) bad += __shfl_xor(bad, off, 64);
+    if ((threadIdx.x & 63) == 0 && bad != 0) atomicAdd(p.invalid, bad);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_per_token(const QuantArgs& p, hipStream_t stream) {
+  const int64_t KB = (p.K + 127) / 128;
+  const int64_t blocks = ((int64_t)p.G * p.R * KB + 7) / 8;
+  if (blocks == 0) return hipSuccess;
+  if (p.x_bf16)
+    per_token_kernel<uint16_t><<<dim3((unsigned)blocks), dim3(256), 0, stream>>>(p);
+  else
+    per_token_kernel<float><<<dim3((unsigned)blocks), dim3(256), 0, stream>>>(p);
+  return hipGetLastError();
+}
+
+hipError_t launch_per_block(const QuantArgs& p, hipStream_t stream) {
+  const int64_t blocks = (int64_t)p.G * ((p.R + 127) / 128) * ((p.K + 127) / 128);
+  if (blocks == 0) return hipSuccess;
+  if (p.x_bf16)
+    per_block_kernel<uint16_t><<<dim3((unsigned)blocks), dim3(256), 0, stream>>>(p);
+  else
+    per_block_kernel<float><<<dim3((unsigned)blocks), dim3(256), 0, stream>>>(p);
+  return hipGetLastError();
+}
+
+hipError_t launch_pack_ue8m0(const PackArgs& p, hipStream_t stream) {
+  const int64_t total = (int64_t)p.G * p.R * p.nw;
+  if (total == 0) return hipSuccess;
+  pack_ue8m0_kernel<<<dim3((unsigned)((total + 255) / 256)), dim3(256), 0, stream>>>(p);
+  return hipGetLastError();
+}
+
+}  // namespace dgmi

@@ -1,0 +1,73 @@
+"""Shared helpers of the parity tests: device transfers, the BF16 output
+comparison at the stated tolerance, and sentinel handling."""
+
+import sys
+
+import numpy as np
+
+import oracle
+
+# Tolerance of a BF16 GEMM output against the float64 oracle:
+#   normalised difference 1 - 2 sum(xy) / (sum(x^2) + sum(y^2)) <= 1e-3, and
+#   per element |x - y| <= 1e-2 * rms(y) + 2^-8 * |y|
+# (2^-8 is the bf16 rounding bound; 1e-2 rms covers FP32 accumulation).
+DIFF_TOL = 1e-3
+ABS_RMS_TOL = 1e-2
+REL_TOL = 2.0 ** -8
+
+SENTINEL_BF16 = 0x7FA5  # a NaN pattern: any write over it is visible
+
+
+def say(msg):
+    """Print a progress line naming the case before a GPU step."""
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def to_dev(arr, dtype=None):
+    import torch
+
+    t = torch.from_numpy(np.ascontiguousarray(arr))
+    if dtype is not None:
+        t = t.view(dtype)
+    return t.cuda()
+
+
+def to_host(t):
+    import torch
+
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).cpu().numpy().view(np.uint16)
+    return t.cpu().numpy()
+
+
+def bf16_bits_to_f64(bits):
+    return oracle.bf16_decode(bits)
+
+
+def norm_diff(x, y):
+    x = np.asarray(x, dtype=np.float64).ravel()
+    y = np.asarray(y, dtype=np.float64).ravel()
+    den = float((x * x).sum() + (y * y).sum())
+    if den == 0.0:
+        return 0.0
+    return 1.0 - 2.0 * float((x * y).sum()) / den
+
+
+def assert_bf16_close(got_bits, ref, what=""):
+    """got_bits: uint16 bf16 patterns; ref: float64 oracle values (same shape)."""
+    got = bf16_bits_to_f64(got_bits)
+    assert got.shape == ref.shape, (what, got.shape, ref.shape)
+    assert np.all(np.isfinite(got)), f"{what}: non-finite output"
+    d = norm_diff(got, ref)
+    assert d <= DIFF_TOL, f"{what}: normalised diff {d:.3e} > {DIFF_TOL}"
+    if ref.size == 0:
+        return
+    rms = float(np.sqrt(np.mean(ref * ref)))
+    err = np.abs(got - ref)
+    bound = ABS_RMS_TOL * rms + REL_TOL * np.abs(ref)
+    bad = err > bound
+    if bad.any():
+        idx = np.argwhere(bad)[:5]
+        details = ", ".join(f"{tuple(i)}: got {got[tuple(i)]:.6g} ref {ref[tuple(i)]:.6g}" for i in idx)
+        raise AssertionError(f"{what}: {int(bad.sum())} elements outside tolerance (rms {rms:.4g}); {details}")

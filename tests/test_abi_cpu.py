@@ -1,0 +1,160 @@
+"""The C-ABI library loads, exports every entry point include/dgmi.h
+declares, and rejects malformed descriptors on the host before any launch.
+No compute call is made here (no GPU needed): every call below fails
+validation, which returns before touching the device."""
+
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+import torch
+
+from moe_grouped_gemm_x128_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dgmi.h")
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", src, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(binding.LIB_PATH):
+        pytest.fail("libdgmi.so is not built (python -m moe_grouped_gemm_x128_amd.build)")
+    return binding.load_library()
+
+
+def test_header_declares_expected_entry_points():
+    assert _declared() == sorted(binding.ENTRY_POINTS)
+
+
+def test_every_declared_symbol_is_exported(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", binding.LIB_PATH], capture_output=True, text=True, check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
+    for name in _declared():
+        assert name in exported, name
+        assert getattr(lib, name) is not None
+
+
+def test_query_config_is_a_pure_function_of_shapes(lib):
+    c = binding.query_config(binding.DG_KIND_DENSE, 1, 4096, 2112, 7168)
+    assert c == binding.query_config(binding.DG_KIND_DENSE, 1, 4096, 2112, 7168)
+    assert c["grid"] == -(-4096 // c["block_m"]) * -(-2112 // c["block_n"])
+    m = binding.query_config(binding.DG_KIND_MASKED, 32, 256, 4096, 7168)
+    assert m["grid"] == 32 * -(-256 // m["block_m"]) * -(-4096 // m["block_n"])
+    b = binding.query_config(binding.DG_KIND_BF16_MASKED, 64, 128, 7168, 2048)
+    assert b["grid"] == 64 * -(-128 // b["block_m"]) * -(-7168 // b["block_n"])
+    with pytest.raises(binding.DgmiError):
+        binding.query_config(9, 1, 1, 1, 1)
+
+
+def _t(shape, dtype, stride=None):
+    t = torch.empty(shape, dtype=dtype)
+    if stride is not None:
+        t = torch.empty_strided(shape, stride, dtype=dtype)
+    return t
+
+
+def _call_dense(lib, a, b, sfa, sfb, d, c=None):
+    D = binding.describe
+    return lib.fp8_gemm_nt(ctypes.byref(D(a)), ctypes.byref(D(b)), ctypes.byref(D(sfa)), ctypes.byref(D(sfb)),
+                           ctypes.byref(D(c)) if c is not None else None, ctypes.byref(D(d)), None)
+
+
+def test_dense_validation_errors(lib):
+    M, N, K = 128, 256, 512
+    a = _t((M, K), torch.uint8)
+    b = _t((N, K), torch.uint8)
+    sfa = _t((M, K // 128), torch.float32)
+    sfb = _t((N // 128, K // 128), torch.float32)
+    d = _t((M, N), torch.bfloat16)
+    # wrong dtype of d
+    assert _call_dense(lib, a, b, sfa, sfb, d.float()) == binding.DG_INVALID_ARG
+    assert "dtype" in binding.last_error()
+    # K mismatch
+    assert _call_dense(lib, a, _t((N, K + 128), torch.uint8), sfa, sfb, d) == binding.DG_INVALID_ARG
+    # wrong scale shape (per-row B scales are not the 128x128 format)
+    assert _call_dense(lib, a, b, sfa, _t((N, K // 128), torch.float32), d) == binding.DG_INVALID_ARG
+    # mixed scale formats
+    assert _call_dense(lib, a, b, sfa, _t((2, 1), torch.int32), d) == binding.DG_INVALID_ARG
+    # non-unit inner stride
+    assert _call_dense(lib, a.t(), b, sfa, sfb, d) == binding.DG_INVALID_ARG
+    # K not a multiple of 128 -> unsupported
+    a2, b2 = _t((M, 200), torch.uint8), _t((N, 200), torch.uint8)
+    assert _call_dense(lib, a2, b2, _t((M, 2), torch.float32), _t((2, 2), torch.float32), d) == binding.DG_UNSUPPORTED
+    # accumulate input not built
+    assert _call_dense(lib, a, b, sfa, sfb, d, c=_t((M, N), torch.bfloat16)) == binding.DG_UNSUPPORTED
+    # output aliasing an input
+    alias = torch.empty(M * K, dtype=torch.uint8)
+    a3 = alias.view(M, K)
+    d3 = alias.view(torch.bfloat16)[: M * N].view(M, N) if M * K * 1 >= M * N * 2 else None
+    if d3 is not None:
+        assert _call_dense(lib, a3, b, sfa, sfb, d3) == binding.DG_INVALID_ARG
+    # misaligned operand rows
+    ab = _t((M, K + 8), torch.uint8)[:, :K]
+    assert _call_dense(lib, ab, b, sfa, sfb, d) == binding.DG_INVALID_ARG
+    assert "aligned" in binding.last_error()
+
+
+def test_masked_validation_errors(lib):
+    G, max_m, N, K = 4, 64, 256, 256
+    D = binding.describe
+    a = _t((G, max_m, K), torch.uint8)
+    b = _t((G, N, K), torch.uint8)
+    sfa = _t((G, max_m, K // 128), torch.float32)
+    sfb = _t((G, N // 128, K // 128), torch.float32)
+    d = _t((G, max_m, N), torch.bfloat16)
+    mm = _t((G,), torch.int32)
+
+    def call(a=a, b=b, sfa=sfa, sfb=sfb, d=d, mm=mm, max_m=max_m):
+        return lib.m_grouped_fp8_gemm_nt_masked(ctypes.byref(D(a)), ctypes.byref(D(b)), ctypes.byref(D(sfa)),
+                                                ctypes.byref(D(sfb)), ctypes.byref(D(d)),
+                                                ctypes.byref(D(mm)) if mm is not None else None, max_m, None)
+
+    assert call(mm=None) == binding.DG_INVALID_ARG
+    assert call(mm=_t((G + 1,), torch.int32)) == binding.DG_INVALID_ARG
+    assert call(mm=_t((G,), torch.float32)) == binding.DG_INVALID_ARG
+    assert call(max_m=max_m + 1) == binding.DG_INVALID_ARG
+    assert call(d=_t((G, max_m, N + 8), torch.bfloat16)) == binding.DG_INVALID_ARG
+    assert call(max_m=-1) == binding.DG_INVALID_ARG
+
+
+def test_contiguous_validation_errors(lib):
+    G, Msum, N, K = 2, 384, 256, 256
+    D = binding.describe
+    a = _t((Msum, K), torch.uint8)
+    b = _t((G, N, K), torch.uint8)
+    sfa = _t((Msum, 2), torch.float32)
+    sfb = _t((G, 2, 2), torch.float32)
+    d = _t((Msum, N), torch.bfloat16)
+
+    def call(layout, a=a, sfa=sfa, d=d):
+        return lib.m_grouped_fp8_gemm_nt_contiguous(ctypes.byref(D(a)), ctypes.byref(D(b)), ctypes.byref(D(sfa)),
+                                                    ctypes.byref(D(sfb)), ctypes.byref(D(d)),
+                                                    ctypes.byref(D(layout)) if layout is not None else None, None)
+
+    assert call(None) == binding.DG_INVALID_ARG
+    assert call(_t((Msum // 128 + 1,), torch.int32)) == binding.DG_INVALID_ARG
+    a2, sfa2, d2 = _t((200, K), torch.uint8), _t((200, 2), torch.float32), _t((200, N), torch.bfloat16)
+    assert call(_t((1,), torch.int32), a=a2, sfa=sfa2, d=d2) == binding.DG_INVALID_ARG
+
+
+def test_quantizer_and_pack_validation_errors(lib):
+    D = binding.describe
+    x = _t((4, 256), torch.float32)
+    q = _t((4, 256), torch.uint8)
+    sf = _t((4, 2), torch.float32)
+    assert lib.per_token_cast_to_fp8(ctypes.byref(D(x)), ctypes.byref(D(q)), ctypes.byref(D(_t((4, 3), torch.float32))), 0, None) == binding.DG_INVALID_ARG
+    assert lib.per_token_cast_to_fp8(ctypes.byref(D(x)), ctypes.byref(D(_t((4, 255), torch.uint8))), ctypes.byref(D(sf)), 0, None) == binding.DG_INVALID_ARG
+    assert lib.per_block_cast_to_fp8(ctypes.byref(D(x)), ctypes.byref(D(q)), ctypes.byref(D(sf)), 0, None) == binding.DG_INVALID_ARG
+    assert lib.per_token_cast_to_fp8(ctypes.byref(D(x.to(torch.int32))), ctypes.byref(D(q)), ctypes.byref(D(sf)), 0, None) == binding.DG_INVALID_ARG
+    s = _t((3, 10), torch.float32)
+    assert lib.pack_ue8m0_to_int(ctypes.byref(D(s)), ctypes.byref(D(_t((3, 2), torch.int32))), None, None) == binding.DG_INVALID_ARG
+    assert lib.pack_ue8m0_to_int(ctypes.byref(D(s)), ctypes.byref(D(_t((3, 3), torch.float32))), None, None) == binding.DG_INVALID_ARG
+    assert lib.pack_ue8m0_to_int(None, ctypes.byref(D(_t((3, 3), torch.int32))), None, None) == binding.DG_INVALID_ARG

@@ -1,0 +1,332 @@
+"""GPU parity of the block-scaled FP8 GEMMs (dense, contiguous-grouped,
+masked-grouped) against the float64 oracle.
+
+Operands are quantized on the GPU by the library and independently by the
+oracle (the two must agree bit for bit); the oracle GEMM consumes its own
+quantized values.  Small shapes are compared in full; the full-size
+DeepSeek-V3 shapes are compared on sampled rows x sampled 128-column blocks,
+which the oracle computes from the corresponding slices of the inputs."""
+
+import numpy as np
+import pytest
+
+import oracle
+from moe_grouped_gemm_x128_amd import synth
+
+from helpers import SENTINEL_BF16, assert_bf16_close, say, to_dev, to_host
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+def _mg():
+    import moe_grouped_gemm_x128_amd as mg
+
+    return mg
+
+
+def q_tok(xt, ue8m0=False):
+    """Per-token quantize a device tensor [..., K]; scales M-major for 2-D."""
+    mg = _mg()
+    K = xt.shape[-1]
+    q = torch.empty(xt.shape, dtype=torch.uint8, device="cuda")
+    if xt.dim() == 2:
+        sf = torch.empty((K // 128, xt.shape[0]), dtype=torch.float32, device="cuda").t()
+    else:
+        sf = torch.empty(xt.shape[:-1] + (K // 128,), dtype=torch.float32, device="cuda")
+    mg.per_token_cast_to_fp8(xt, q, sf, ue8m0)
+    return q, sf
+
+
+def q_blk(xt, ue8m0=False):
+    mg = _mg()
+    N, K = xt.shape[-2], xt.shape[-1]
+    q = torch.empty(xt.shape, dtype=torch.uint8, device="cuda")
+    sf = torch.empty(xt.shape[:-2] + (-(-N // 128), K // 128), dtype=torch.float32, device="cuda")
+    mg.per_block_cast_to_fp8(xt, q, sf, ue8m0)
+    return q, sf
+
+
+def sentinel_like(shape):
+    return torch.full(shape, SENTINEL_BF16, dtype=torch.int16, device="cuda").view(torch.bfloat16)
+
+
+# ---------------------------------------------------------------------------
+# dense
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("M,N,K", [(128, 256, 512), (200, 300, 384), (1, 130, 128), (257, 64, 256), (64, 2112, 1024)])
+def test_dense_full_compare(M, N, K):
+    say(f"fp8_gemm_nt M={M} N={N} K={K}")
+    mg = _mg()
+    xa = synth.normal_f32(101, (M, K))
+    xb = synth.normal_f32(102, (N, K))
+    a, sfa = q_tok(to_dev(xa))
+    b, sfb = q_blk(to_dev(xb))
+    d = sentinel_like((M, N))
+    mg.fp8_gemm_nt(a, b, sfa, sfb, None, d)
+    torch.cuda.synchronize()
+    ra, rsfa = oracle.per_token_cast_to_fp8(xa)
+    rb, rsfb = oracle.per_block_cast_to_fp8(xb)
+    assert np.array_equal(to_host(a), ra) and np.array_equal(to_host(b), rb)
+    ref = oracle.fp8_gemm_nt(ra, rb, rsfa, rsfb)
+    assert_bf16_close(to_host(d), ref, f"dense {M}x{N}x{K}")
+
+
+def test_dense_ue8m0_packed_scales():
+    say("fp8_gemm_nt UE8M0 packed scales")
+    mg = _mg()
+    M, N, K = 192, 384, 1024
+    xa = synth.normal_f32(111, (M, K))
+    xb = synth.normal_f32(112, (N, K))
+    a, sfa = q_tok(to_dev(xa), ue8m0=True)
+    b, sfb = q_blk(to_dev(xb), ue8m0=True)
+    pa = torch.empty((M, K // 512), dtype=torch.int32, device="cuda")
+    pb = torch.empty((N // 128, K // 512), dtype=torch.int32, device="cuda")
+    mg.pack_ue8m0_to_int(sfa.contiguous(), pa)
+    mg.pack_ue8m0_to_int(sfb, pb)
+    d = sentinel_like((M, N))
+    mg.fp8_gemm_nt(a, b, pa, pb, None, d)
+    torch.cuda.synchronize()
+    ra, rsfa = oracle.per_token_cast_to_fp8(xa, True)
+    rb, rsfb = oracle.per_block_cast_to_fp8(xb, True)
+    rpa, _ = oracle.pack_ue8m0_to_int(rsfa)
+    rpb, _ = oracle.pack_ue8m0_to_int(rsfb)
+    assert np.array_equal(to_host(pa), rpa) and np.array_equal(to_host(pb), rpb)
+    ref = oracle.fp8_gemm_nt(ra, rb, oracle.scales_from_packed_ue8m0(rpa, K // 128),
+                             oracle.scales_from_packed_ue8m0(rpb, K // 128))
+    assert_bf16_close(to_host(d), ref, "dense ue8m0")
+
+
+def test_dense_one_hot_closed_form_bit_exact():
+    """B one-hot (column n reads K index kn[n]) and power-of-two scales: every
+    output is sfa*sfb*A[m, kn[n]] exactly, representable in bf16, so the
+    device result must match bit for bit; this pins the A/B/scale indexing
+    and the MFMA fragment layout."""
+    say("fp8_gemm_nt one-hot closed form")
+    mg = _mg()
+    rng = np.random.default_rng(23)
+    M, N, K = 160, 272, 768
+    a = (rng.integers(0, 0x7E, size=(M, K)) | (rng.integers(0, 2, size=(M, K)) << 7)).astype(np.uint8)
+    kn = rng.permutation(K)[:N]
+    b = np.zeros((N, K), dtype=np.uint8)
+    b[np.arange(N), kn] = 0x38
+    sfa = np.exp2(rng.integers(-6, 6, size=(M, K // 128))).astype(np.float32)
+    sfb = np.exp2(rng.integers(-6, 6, size=(-(-N // 128), K // 128))).astype(np.float32)
+    d = sentinel_like((M, N))
+    mg.fp8_gemm_nt(to_dev(a), to_dev(b), to_dev(sfa), to_dev(sfb), None, d)
+    torch.cuda.synchronize()
+    ref = oracle.fp8_gemm_nt(a, b, sfa, sfb)
+    ref_bits = to_host(torch.from_numpy(ref.astype(np.float32)).to(torch.bfloat16))
+    assert np.array_equal(torch.from_numpy(ref_bits.view(np.int16)).view(torch.bfloat16).double().numpy(), ref)
+    got = to_host(d)
+    bad = np.argwhere(got != ref_bits)
+    assert bad.size == 0, f"{len(bad)} mismatches, first {bad[:5].tolist()}"
+
+
+def _sample_rows(M, n, seed):
+    rows = np.random.default_rng(seed).choice(M, size=min(n, M), replace=False)
+    return np.unique(np.concatenate([rows, [0, M - 1]]))
+
+
+def _sample_col_blocks(N):
+    nnb = -(-N // 128)
+    return sorted({0, nnb // 2, nnb - 1})
+
+
+@pytest.mark.parametrize("i", range(len(synth.DENSE_V3_SHAPES)))
+def test_dense_v3_shapes_sampled(i):
+    N, K = synth.DENSE_V3_SHAPES[i]
+    M = synth.DENSE_V3_M
+    say(f"fp8_gemm_nt full size M={M} N={N} K={K}")
+    mg = _mg()
+    sa, sb = synth.dense_v3_seeds(i)
+    xa = synth.normal_f32(sa, (M, K))
+    xb = synth.normal_f32(sb, (N, K))
+    a, sfa = q_tok(to_dev(xa))
+    b, sfb = q_blk(to_dev(xb))
+    d = sentinel_like((M, N))
+    mg.fp8_gemm_nt(a, b, sfa, sfb, None, d)
+    torch.cuda.synchronize()
+    rows = _sample_rows(M, 40, 7 + i)
+    ra, rsfa = oracle.per_token_cast_to_fp8(xa[rows])
+    assert np.array_equal(to_host(a)[rows], ra)
+    dh = to_host(d)
+    for nb in _sample_col_blocks(N):
+        cols = slice(nb * 128, min(N, nb * 128 + 128))
+        rb, rsfb = oracle.per_block_cast_to_fp8(xb[cols])
+        ref = oracle.fp8_gemm_nt(ra, rb, rsfa, rsfb)
+        assert_bf16_close(dh[rows][:, cols], ref, f"dense {M}x{N}x{K} col block {nb}")
+
+
+# ---------------------------------------------------------------------------
+# contiguous grouped
+# ---------------------------------------------------------------------------
+
+def test_contiguous_small_with_skips():
+    say("contiguous small, shuffled layout with -1 blocks")
+    mg = _mg()
+    G, N, K = 3, 300, 256
+    layout = np.array([2, -1, 0, 2, 1, -1, 5], dtype=np.int32)  # 5 >= G: skipped too
+    Msum = layout.size * 128
+    xa = synth.normal_f32(121, (Msum, K))
+    xb = synth.normal_f32(122, (G, N, K))
+    a, sfa = q_tok(to_dev(xa))
+    b, sfb = q_blk(to_dev(xb))
+    d = sentinel_like((Msum, N))
+    mg.m_grouped_fp8_gemm_nt_contiguous(a, b, sfa, sfb, d, to_dev(layout))
+    torch.cuda.synchronize()
+    ra, rsfa = oracle.per_token_cast_to_fp8(xa)
+    rb, rsfb = oracle.per_block_cast_to_fp8(xb)
+    ref_layout = np.where(layout < G, layout, -1)
+    ref, written = oracle.m_grouped_fp8_gemm_nt_contiguous(ra, rb, rsfa, rsfb, ref_layout)
+    got = to_host(d)
+    assert np.all(got[~written] == SENTINEL_BF16)
+    assert_bf16_close(got[written], ref[written], "contiguous small")
+
+
+def test_contiguous_mixed_groups_in_one_tile():
+    """Adjacent 128-row blocks of different groups (and a skipped one next
+    to a computed one) in every position."""
+    say("contiguous alternating groups")
+    mg = _mg()
+    G, N, K = 2, 256, 384
+    layout = np.array([0, 1, 1, 0, -1, 1, 0, -1, -1, 1], dtype=np.int32)
+    Msum = layout.size * 128
+    xa = synth.normal_f32(123, (Msum, K))
+    xb = synth.normal_f32(124, (G, N, K))
+    a, sfa = q_tok(to_dev(xa))
+    b, sfb = q_blk(to_dev(xb))
+    d = sentinel_like((Msum, N))
+    mg.m_grouped_fp8_gemm_nt_contiguous(a, b, sfa, sfb, d, to_dev(layout))
+    torch.cuda.synchronize()
+    ra, rsfa = oracle.per_token_cast_to_fp8(xa)
+    rb, rsfb = oracle.per_block_cast_to_fp8(xb)
+    ref, written = oracle.m_grouped_fp8_gemm_nt_contiguous(ra, rb, rsfa, rsfb, layout)
+    got = to_host(d)
+    assert np.all(got[~written] == SENTINEL_BF16)
+    assert_bf16_close(got[written], ref[written], "contiguous alternating")
+
+
+@pytest.mark.parametrize("si", [0, 1])
+def test_contiguous_prefill_full_size_sampled(si):
+    N, K = synth.CONTIG["shapes"][si]
+    G, per = synth.CONTIG["G"], synth.CONTIG["rows_per_group"]
+    Msum = G * per
+    say(f"contiguous full size G={G} Msum={Msum} N={N} K={K}")
+    mg = _mg()
+    xa = synth.normal_f32(synth.CONTIG["seed_a"] + 10 * si, (Msum, K))
+    xb_dev = torch.empty((G, N, K), dtype=torch.float32, device="cuda")
+    xb_host = []
+    for g, chunk in enumerate(synth.normal_f32_chunks(synth.CONTIG["seed_b"] + 10 * si, (G, N, K))):
+        xb_dev[g].copy_(torch.from_numpy(chunk))
+        xb_host.append(chunk)
+    layout = synth.contiguous_layout(G, per)
+    a, sfa = q_tok(to_dev(xa))
+    b, sfb = q_blk(xb_dev)
+    del xb_dev
+    d = sentinel_like((Msum, N))
+    mg.m_grouped_fp8_gemm_nt_contiguous(a, b, sfa, sfb, d, to_dev(layout))
+    torch.cuda.synchronize()
+    dh = to_host(d)
+    rows = _sample_rows(Msum, 48, 31 + si)
+    ra, rsfa = oracle.per_token_cast_to_fp8(xa[rows])
+    for nb in _sample_col_blocks(N):
+        cols = slice(nb * 128, min(N, nb * 128 + 128))
+        for g in range(G):
+            sel = (rows // per) == g
+            if not sel.any():
+                continue
+            rb, rsfb = oracle.per_block_cast_to_fp8(xb_host[g][cols])
+            ref = oracle.fp8_gemm_nt(ra[sel], rb, rsfa[sel], rsfb)
+            assert_bf16_close(dh[rows[sel]][:, cols], ref, f"contiguous g={g} col block {nb}")
+
+
+# ---------------------------------------------------------------------------
+# masked grouped
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("ue8m0", [False, True])
+def test_masked_small_sentinel_and_clamp(ue8m0):
+    say(f"masked small ue8m0={ue8m0}")
+    mg = _mg()
+    G, max_m, N, K = 6, 160, 200, 256
+    mm = np.array([0, 17, 160, 999, -3, 129], dtype=np.int32)
+    xa = synth.normal_f32(131, (G, max_m, K))
+    xb = synth.normal_f32(132, (G, N, K))
+    a, sfa = q_tok(to_dev(xa), ue8m0)
+    b, sfb = q_blk(to_dev(xb), ue8m0)
+    if ue8m0:
+        pa = torch.empty((G, max_m, 1), dtype=torch.int32, device="cuda")
+        pb = torch.empty((G, 2, 1), dtype=torch.int32, device="cuda")
+        mg.pack_ue8m0_to_int(sfa, pa)
+        mg.pack_ue8m0_to_int(sfb, pb)
+        sfa, sfb = pa, pb
+    d = sentinel_like((G, max_m, N))
+    mg.m_grouped_fp8_gemm_nt_masked(a, b, sfa, sfb, d, to_dev(mm), max_m)
+    torch.cuda.synchronize()
+    ra, rsfa = oracle.per_token_cast_to_fp8(xa, ue8m0)
+    rb, rsfb = oracle.per_block_cast_to_fp8(xb, ue8m0)
+    ref, written = oracle.m_grouped_fp8_gemm_nt_masked(ra, rb, rsfa, rsfb, mm, max_m)
+    got = to_host(d)
+    assert np.all(got[~written] == SENTINEL_BF16)
+    assert_bf16_close(got[written], ref[written], "masked small")
+
+
+def test_masked_2d_views_and_all_zero():
+    say("masked 2-D views, masked_m all zero then all max")
+    mg = _mg()
+    G, max_m, N, K = 3, 64, 128, 128
+    xa = synth.normal_f32(141, (G * max_m, K))
+    xb = synth.normal_f32(142, (G, N, K))
+    a, sfa = q_tok(to_dev(xa))
+    b, sfb = q_blk(to_dev(xb))
+    d = sentinel_like((G * max_m, N))
+    mg.m_grouped_fp8_gemm_nt_masked(a, b, sfa.contiguous(), sfb, d, to_dev(np.zeros(G, np.int32)), max_m)
+    torch.cuda.synchronize()
+    assert np.all(to_host(d) == SENTINEL_BF16)
+    mg.m_grouped_fp8_gemm_nt_masked(a, b, sfa.contiguous(), sfb, d, to_dev(np.full(G, max_m, np.int32)), max_m)
+    torch.cuda.synchronize()
+    ra, rsfa = oracle.per_token_cast_to_fp8(xa)
+    rb, rsfb = oracle.per_block_cast_to_fp8(xb)
+    got = to_host(d).reshape(G, max_m, N)
+    for g in range(G):
+        ref = oracle.fp8_gemm_nt(ra[g * max_m:(g + 1) * max_m], rb[g], rsfa[g * max_m:(g + 1) * max_m], rsfb[g])
+        assert_bf16_close(got[g], ref, f"masked full group {g}")
+
+
+@pytest.mark.parametrize("si", [0, 1])
+def test_masked_decode_full_size_sampled(si):
+    N, K = synth.MASKED["shapes"][si]
+    G, max_m = synth.MASKED["G"], synth.MASKED["max_m"]
+    say(f"masked full size G={G} max_m={max_m} N={N} K={K}")
+    mg = _mg()
+    mm = synth.masked_m_decode(synth.MASKED["seed_m"], G)
+    xa = synth.normal_f32(synth.MASKED["seed_a"] + 10 * si, (G, max_m, K))
+    xb_dev = torch.empty((G, N, K), dtype=torch.float32, device="cuda")
+    sample_groups = [0, 7, G - 1]
+    xb_keep = {}
+    for g, chunk in enumerate(synth.normal_f32_chunks(synth.MASKED["seed_b"] + 10 * si, (G, N, K))):
+        xb_dev[g].copy_(torch.from_numpy(chunk))
+        if g in sample_groups:
+            xb_keep[g] = chunk
+    a, sfa = q_tok(to_dev(xa))
+    b, sfb = q_blk(xb_dev)
+    del xb_dev
+    d = sentinel_like((G, max_m, N))
+    mg.m_grouped_fp8_gemm_nt_masked(a, b, sfa, sfb, d, to_dev(mm), max_m)
+    torch.cuda.synchronize()
+    dh = to_host(d)
+    # rows at and beyond masked_m stay untouched in every group
+    for g in range(G):
+        assert np.all(dh[g, mm[g]:] == SENTINEL_BF16), g
+    for g in sample_groups:
+        v = int(mm[g])
+        rows = _sample_rows(v, 24, 50 + g)
+        ra, rsfa = oracle.per_token_cast_to_fp8(xa[g, rows])
+        for nb in _sample_col_blocks(N):
+            cols = slice(nb * 128, min(N, nb * 128 + 128))
+            rb, rsfb = oracle.per_block_cast_to_fp8(xb_keep[g][cols])
+            ref = oracle.fp8_gemm_nt(ra, rb, rsfa, rsfb)
+            assert_bf16_close(dh[g, rows][:, cols], ref, f"masked g={g} col block {nb}")

@@ -1,0 +1,137 @@
+"""Masked grouped GEMMs captured once in a hipGraph and replayed with new
+masked_m contents written between replays (64 experts, max_m 128,
+N 7168, K 2048).
+
+The captured graph holds, per replay: the per-token UE8M0 cast of the
+activations, pack_ue8m0_to_int of both scale tensors, the masked FP8 GEMM
+on the packed scales, and the masked BF16 GEMM on the same shapes.  Replay
+0 has every masked_m = 0, replay 1 every masked_m = 128, the rest are
+seeded uniform draws.  Every replay is checked against the oracle on
+sampled experts, rows and column blocks, every untouched row is checked
+against the sentinel, and the replayed outputs are compared bit for bit
+with an eager run of the same calls."""
+
+import numpy as np
+import pytest
+
+import oracle
+from moe_grouped_gemm_x128_amd import synth
+
+from helpers import SENTINEL_BF16, assert_bf16_close, say, to_dev, to_host
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+CHECK_GROUPS = (0, 1, 21, 42, 63)
+
+
+def _mg():
+    import moe_grouped_gemm_x128_amd as mg
+
+    return mg
+
+
+def test_masked_graph_replay_with_new_masked_m():
+    cfg = synth.MASKED_GRAPH
+    G, max_m, N, K = cfg["G"], cfg["max_m"], cfg["N"], cfg["K"]
+    KB = K // 128
+    say(f"graph setup G={G} max_m={max_m} N={N} K={K}")
+    mg = _mg()
+
+    xa = synth.normal_f32(cfg["seed_a"], (G, max_m, K))
+    xa_dev = to_dev(xa)
+    xb_dev = torch.empty((G, N, K), dtype=torch.float32, device="cuda")
+    xb_keep = {}
+    for g, chunk in enumerate(synth.normal_f32_chunks(cfg["seed_b"], (G, N, K))):
+        xb_dev[g].copy_(torch.from_numpy(chunk))
+        if g in CHECK_GROUPS:
+            xb_keep[g] = chunk
+    # weights: quantized once, outside the graph (static across replays)
+    qb = torch.empty((G, N, K), dtype=torch.uint8, device="cuda")
+    sfb = torch.empty((G, N // 128, KB), dtype=torch.float32, device="cuda")
+    mg.per_block_cast_to_fp8(xb_dev, qb, sfb, True)
+    b16 = xb_dev.to(torch.bfloat16)
+    a16 = xa_dev.to(torch.bfloat16)
+    del xb_dev
+    torch.cuda.synchronize()
+
+    qa = torch.empty((G, max_m, K), dtype=torch.uint8, device="cuda")
+    sfa = torch.empty((G, max_m, KB), dtype=torch.float32, device="cuda")
+    pa = torch.empty((G, max_m, KB // 4), dtype=torch.int32, device="cuda")
+    pb = torch.empty((G, N // 128, KB // 4), dtype=torch.int32, device="cuda")
+    d8 = torch.empty((G, max_m, N), dtype=torch.bfloat16, device="cuda")
+    d16 = torch.empty((G, max_m, N), dtype=torch.bfloat16, device="cuda")
+    masked_m = torch.zeros(G, dtype=torch.int32, device="cuda")
+
+    def step():
+        mg.per_token_cast_to_fp8(xa_dev, qa, sfa, True)
+        mg.pack_ue8m0_to_int(sfa, pa)
+        mg.pack_ue8m0_to_int(sfb, pb)
+        mg.m_grouped_fp8_gemm_nt_masked(qa, qb, pa, pb, d8, masked_m, max_m)
+        mg.m_grouped_bf16_gemm_nt_masked(a16, b16, d16, masked_m, max_m)
+
+    def fill_sentinel():
+        d8.view(torch.int16).fill_(SENTINEL_BF16)
+        d16.view(torch.int16).fill_(SENTINEL_BF16)
+
+    # warm-up, then capture on a side stream
+    fill_sentinel()
+    step()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        graph.capture_begin()
+        step()
+        graph.capture_end()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+
+    # oracle quantization of the checked experts (A rows are sampled per replay)
+    rq_b, rsf_b = {}, {}
+    for g in CHECK_GROUPS:
+        rq_b[g], rsf_b[g] = oracle.per_block_cast_to_fp8(xb_keep[g], True)
+    a16_bits = to_host(a16)
+    b16_bits = {g: synth.bf16_bits_from_f32(xb_keep[g]) for g in CHECK_GROUPS}
+    ref_pb = {g: oracle.pack_ue8m0_to_int(rsf_b[g])[0] for g in CHECK_GROUPS}
+    pb_host = None
+
+    draws = [np.zeros(G, np.int32), np.full(G, max_m, np.int32)]
+    draws += [synth.masked_m_uniform(cfg["seed_m"] + r, G, max_m) for r in range(2, 6)]
+    for r, mm in enumerate(draws):
+        say(f"graph replay {r}: sum(masked_m)={int(mm.sum())}")
+        masked_m.copy_(torch.from_numpy(mm))
+        fill_sentinel()
+        graph.replay()
+        torch.cuda.synchronize()
+        g8, g16 = to_host(d8), to_host(d16)
+        # eager run of the same calls: identical bits
+        fill_sentinel()
+        step()
+        torch.cuda.synchronize()
+        assert np.array_equal(to_host(d8), g8), f"replay {r}: FP8 replay differs from eager"
+        assert np.array_equal(to_host(d16), g16), f"replay {r}: BF16 replay differs from eager"
+        if pb_host is None:
+            pb_host = to_host(pb)
+            for g in CHECK_GROUPS:
+                assert np.array_equal(pb_host[g], ref_pb[g])
+        for g in range(G):
+            v = int(mm[g])
+            assert np.all(g8[g, v:] == SENTINEL_BF16) and np.all(g16[g, v:] == SENTINEL_BF16), (r, g)
+        for g in CHECK_GROUPS:
+            v = int(mm[g])
+            if v == 0:
+                continue
+            rows = np.unique(np.concatenate([np.random.default_rng(100 * r + g).choice(v, size=min(12, v), replace=False), [v - 1]]))
+            ra, rsfa = oracle.per_token_cast_to_fp8(xa[g, rows], True)
+            rpa, _ = oracle.pack_ue8m0_to_int(rsfa)
+            ua = oracle.scales_from_packed_ue8m0(rpa, KB)
+            ub = oracle.scales_from_packed_ue8m0(ref_pb[g], KB)
+            for nb in (0, 27, 55):
+                cols = slice(nb * 128, nb * 128 + 128)
+                ref8 = oracle.fp8_gemm_nt(ra, rq_b[g][cols], ua, ub[nb:nb + 1])
+                assert_bf16_close(g8[g, rows][:, cols], ref8, f"replay {r} fp8 g={g} nb={nb}")
+                ref16 = oracle.bf16_decode(a16_bits[g, rows]) @ oracle.bf16_decode(b16_bits[g][cols]).T
+                assert_bf16_close(g16[g, rows][:, cols], ref16, f"replay {r} bf16 g={g} nb={nb}")
