@@ -185,7 +185,7 @@ class MaskedWorkload:
 # CPU baseline: the oracle on a bounded sample of the dense workload
 # ---------------------------------------------------------------------------
 
-def time_cpu_baseline(rows_a=256, rows_b=2048):
+def time_cpu_baseline(rows_a=512, rows_b=6144):
     import oracle
     from moe_grouped_gemm_x128_amd import synth
 

@@ -15,7 +15,7 @@
 
 #include <string>
 
-#include "../../include/dgmi.h"
+#include "dgmi.h"
 #include "launch.hpp"
 
 namespace {

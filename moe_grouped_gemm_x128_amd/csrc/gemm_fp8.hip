@@ -21,12 +21,25 @@
 //                 beyond masked_m[g] exits at once, rows beyond masked_m[g]
 //                 are never stored
 //
-// Data path per workgroup (BM x BN tile, WM x WN waves of 64 lanes):
-//   HBM -> registers (16-B loads, coalesced along K) -> LDS (double
-//   buffered, 128-B rows with the 16-B chunk index XOR-swizzled by the row)
-//   -> MFMA operand fragments (two ds_read_b128 per 16x128 fragment).
-// A row scales are staged through LDS with the tiles; the B block scale of
-// a wave is one uniform value per K-block.
+// Data path per workgroup (BM x BN tile, WM x WN waves of 64 lanes, K-step
+// 128 = one scale block):
+//   * HBM -> LDS with global_load_lds_dwordx4 (no register staging): each
+//     wave instruction fills 8 tile rows of 128 bytes; the 16-byte chunk
+//     index of row r is stored at slot (chunk ^ (r & 7)), so the 16 rows of
+//     an MFMA fragment read at one chunk hit distinct banks.  Two static LDS
+//     stages; the loads of K-block kb+1 are issued right after the barrier
+//     that opens K-block kb, so they overlap its MFMAs.
+//   * The MFMA takes the B fragment as its first operand: the 16x16 partial
+//     then holds, per lane, one output row (m = lane % 16) and four output
+//     columns.  The B fragment rows are permuted so that the four fragments
+//     of a wave give every lane 16 consecutive columns: one row scale per
+//     lane per fragment row, and the BF16 epilogue stores 2 x 16 bytes per
+//     lane per fragment row, straight from registers.
+//   * Tile order is XCD-aware: workgroups are dealt to the 8 XCDs round
+//     robin, so the block index is remapped to give each XCD a contiguous
+//     band of tiles (its L2 then holds the shared A rows / B columns).
+
+#include <type_traits>
 
 #include "common.hpp"
 #include "launch.hpp"
@@ -36,22 +49,43 @@ namespace dgmi {
 namespace {
 
 constexpr int BK = 128;  // K-block = scale block = K of one MFMA
+constexpr int NUM_XCD = 8;
 
-// Byte offset in a tile of 16-byte chunk c (0..7) of row r.
-__device__ __forceinline__ int lds_off(int r, int c) { return r * 128 + ((c ^ (r & 7)) << 4); }
+typedef __attribute__((address_space(3))) void lds_void;
 
-template <int BM, int BN, int WM, int WN>
+// s_waitcnt immediate that waits for vmcnt <= n only (gfx9 encoding: vmcnt
+// bits [3:0] and [15:14], expcnt [6:4] and lgkmcnt [11:8] left at "no wait").
+constexpr int vmcnt_only(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+
+// LDS swizzle: 16-byte chunk c of tile row r is stored at slot c ^ h(r),
+// with h linear over GF(2) in the row bits:
+//   h(r) = (b0 ^ b3 ^ b5) | b1 << 1 | (b2 ^ b4) << 2.
+// The MFMA fragment reads touch 16 rows at one chunk: A fragments rows
+// r0 + 0..15 (bits 0-3 vary), B fragments the permuted rows of the epilogue
+// layout (bits 0, 1, 4, 5 vary).  h is a bijection on the varying bits in
+// both cases, for every group of 8 lanes and for every 16 lanes split by
+// row parity, so the reads are free of bank conflicts with 32 or with 64
+// four-byte banks.
+__device__ __host__ constexpr int swz(int r) { return ((r ^ (r >> 3) ^ (r >> 5)) & 1) | (r & 2) | ((((r >> 2) ^ (r >> 4)) & 1) << 2); }
+// Byte offset in a tile of 16-byte chunk c (0..7) of tile row r.
+__device__ __forceinline__ int lds_off(int r, int c) { return r * 128 + ((c ^ swz(r)) << 4); }
+
+template <int BM_, int BN_, int WM_, int WN_, int STAGES_>
 struct TileShape {
-  static constexpr int NT = WM * WN * 64;
+  static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, STAGES = STAGES_;
+  static constexpr int NW = WM * WN;
+  static constexpr int NT = NW * 64;
   static constexpr int TM = BM / WM, TN = BN / WN;  // wave tile
   static constexpr int FM = TM / 16, FN = TN / 16;  // 16x16 fragments per wave
-  static constexpr int ACH = BM * 8 / NT;           // 16-B chunks per thread per stage
-  static constexpr int BCH = BN * 8 / NT;
-  static constexpr int STAGE = (BM + BN) * BK;      // bytes of one LDS stage
-  static_assert((BM * 8) % NT == 0 && (BN * 8) % NT == 0, "tile rows must split evenly over threads");
-  static_assert(TM % 16 == 0 && TN % 16 == 0, "wave tile must be whole fragments");
-  static_assert(TN <= 128 && 128 % TN == 0, "a wave's columns must lie in one 128-column scale block");
-  static_assert(BM <= NT, "one thread per tile row stages the A scales");
+  static constexpr int A_LOADS = BM / (8 * NW);     // LDS-DMA instructions per wave per stage
+  static constexpr int B_LOADS = BN / (8 * NW);
+  static constexpr int A_BYTES = BM * BK, STAGE = (BM + BN) * BK;
+  static_assert(BM % (8 * NW) == 0 && BN % (8 * NW) == 0, "tile rows must split into 8-row wave loads");
+  static_assert(FN == 4, "the epilogue packs four fragments into 16 consecutive columns");
+  static_assert(TN == 64 && 128 % TN == 0, "a wave's columns must lie in one 128-column scale block");
+  static constexpr int NBT = (BN + 127) / 128;      // 128-column scale blocks per tile
+  static_assert(BM + NBT <= NT, "one thread per tile row stages the A scales, one per column block the B scale");
+  static_assert(STAGES == 2 || STAGES == 3, "two or three LDS stages");
 };
 
 template <int SF>
@@ -64,44 +98,71 @@ __device__ __forceinline__ float load_scale(const void* base, int64_t idx_row, i
   }
 }
 
-template <int BM, int BN, int WM, int WN, int MODE, int SF>
-__global__ __launch_bounds__(WM* WN * 64) void fp8_gemm_kernel(const Fp8GemmParams p) {
-  using T = TileShape<BM, BN, WM, WN>;
-  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * T::STAGE];
-  __shared__ __attribute__((aligned(16))) float ssa[2][BM];
+// Tile index of this workgroup after the XCD remap: the hardware deals
+// block b to XCD b % 8; XCD x receives the contiguous tile range starting at
+// x*q + min(x, r) (q = total / 8, r = total % 8).
+__device__ __forceinline__ int xcd_remap(int b, int total) {
+  const int q = total / NUM_XCD, r = total % NUM_XCD;
+  const int x = b % NUM_XCD, local = b / NUM_XCD;
+  return x * q + min(x, r) + local;
+}
+
+// Linear tile t -> (tm, tn), walking bands of `gm` tile rows column by column
+// so that consecutive tiles share B columns and nearby A rows.
+__device__ __forceinline__ void band_order(int t, int tiles_m, int tiles_n, int gm, int& tm, int& tn) {
+  const int band = t / (gm * tiles_n);
+  const int first = band * gm;
+  const int rows = min(gm, tiles_m - first);
+  const int in_band = t - band * gm * tiles_n;
+  tm = first + in_band % rows;
+  tn = in_band / rows;
+}
+
+template <class T, int SF, int MODE>
+__global__ __launch_bounds__(T::NT) void fp8_gemm_kernel(const Fp8GemmParams p) {
+  __shared__ __attribute__((aligned(16))) uint8_t smem0[T::STAGE];
+  __shared__ __attribute__((aligned(16))) uint8_t smem1[T::STAGE];
+  __shared__ __attribute__((aligned(16))) uint8_t smem2[T::STAGES == 3 ? T::STAGE : 16];
+  // per stage: A row scales in slots [0, BM), B block scales in [BM, BM + NBT);
+  // one slot per thread so the stores need no branch
+  __shared__ __attribute__((aligned(16))) float ssc[T::STAGES][T::NT];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int wm = wave / WN, wn = wave % WN;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / T::WN, wn = wave % T::WN;
 
-  // ---- tile decode (depends on device metadata only through early exits)
-  int bid = blockIdx.x;
+  // ---- tile decode (device metadata only gates early exits, never the grid)
+  const int per_group = p.tiles_m * p.tiles_n;
+  const int total = (MODE == MODE_MASKED ? p.G : 1) * per_group;
+  int t = xcd_remap(blockIdx.x, total);
   int g = 0;
   if (MODE == MODE_MASKED) {
-    const int per = p.tiles_m * p.tiles_n;
-    g = bid / per;
-    bid -= g * per;
+    g = t / per_group;
+    t -= g * per_group;
   }
-  const int tm = bid / p.tiles_n, tn = bid - (bid / p.tiles_n) * p.tiles_n;
-  const int m0 = tm * BM, n0 = tn * BN;
+  int tm, tn;
+  band_order(t, p.tiles_m, p.tiles_n, MODE == MODE_MASKED ? p.tiles_m : 8, tm, tn);
+  const int m0 = __builtin_amdgcn_readfirstlane(tm * T::BM), n0 = __builtin_amdgcn_readfirstlane(tn * T::BN);
+  g = __builtin_amdgcn_readfirstlane(g);
 
   int row_lim = p.M;  // rows [0, row_lim) may be read and written
   int npass = 1;
-  int pg[2] = {0, 0}, plo[2] = {0, 0}, phi[2] = {BM, BM};
+  int pg[2] = {0, 0}, plo[2] = {0, 0}, phi[2] = {T::BM, T::BM};
   if (MODE == MODE_MASKED) {
-    int v = p.meta[g];
+    int v = __builtin_amdgcn_readfirstlane(p.meta[g]);
     v = v < 0 ? 0 : (v > p.M ? p.M : v);
     if (m0 >= v) return;
     row_lim = v;
+    pg[0] = g;
   } else if (MODE == MODE_CONTIG) {
     const int nblk = p.M / 128;
     const int b0 = m0 / 128;
-    int g0 = p.meta[b0];
+    int g0 = __builtin_amdgcn_readfirstlane(p.meta[b0]);
     if (g0 >= p.G) g0 = -1;
     int g1 = g0;
-    if (BM == 256) {
-      g1 = (b0 + 1 < nblk) ? p.meta[b0 + 1] : -1;
+    if (T::BM == 256) {
+      g1 = (b0 + 1 < nblk) ? __builtin_amdgcn_readfirstlane(p.meta[b0 + 1]) : -1;
       if (g1 >= p.G) g1 = -1;
     }
     if (g0 == g1) {
@@ -119,33 +180,55 @@ __global__ __launch_bounds__(WM* WN * 64) void fp8_gemm_kernel(const Fp8GemmPara
   const int NB = (p.N + 127) / 128;
   const int nb_wave = __builtin_amdgcn_readfirstlane(min((n0 + wn * T::TN) / 128, NB - 1));
   const uint8_t* A = p.a + (MODE == MODE_MASKED ? (int64_t)g * p.a_gs : 0);
-  const int64_t sfa_g = (MODE == MODE_MASKED) ? (int64_t)g * p.sfa_gs : 0;
+  const int64_t sfa_goff = (MODE == MODE_MASKED) ? (int64_t)g * p.sfa_gs : 0;
   uint16_t* D = p.d + (MODE == MODE_MASKED ? (int64_t)g * p.d_gs : 0);
 
-  // per-thread global sources and LDS destinations of the tile loads
-  const uint8_t* asrc[T::ACH];
-  int aoff[T::ACH];
-#pragma unroll
-  for (int j = 0; j < T::ACH; ++j) {
-    const int q = tid + j * T::NT, r = q >> 3, c = q & 7;
-    asrc[j] = A + (int64_t)min(m0 + r, row_lim - 1) * p.lda + c * 16;
-    aoff[j] = lds_off(r, c);
-  }
-  int boff[T::BCH];
-  int brow[T::BCH];
-#pragma unroll
-  for (int j = 0; j < T::BCH; ++j) {
-    const int q = tid + j * T::NT, r = q >> 3, c = q & 7;
-    brow[j] = min(n0 + r, p.N - 1);
-    boff[j] = BM * BK + lds_off(r, c);
-  }
-  const int64_t sa_row = min(m0 + (tid < BM ? tid : 0), row_lim - 1);
+  // LDS-DMA sources.  Instruction j of this wave fills tile rows
+  // [8(j*NW+wave), +8); lane l writes slot l%8 of row l/8 and so reads chunk
+  // (slot ^ (row & 7)) = (slot ^ l/8).  The buffer resources start at the
+  // tile's first row and cover only the rows that exist (rows < row_lim for
+  // A, < N for B): the hardware range check on the per-lane offset returns
+  // zeros past them, so no clamping and no memory traffic for those rows.
+  // Row (g8*8 + lrow) has h = lrow ^ h(g8*8) by linearity, so lane l reads
+  // chunk (l%8) ^ (l/8) ^ h(g8*8), the last term uniform per instruction.
+  const int lrow = lane >> 3, lslot = lane & 7;
+  const int a_rows = __builtin_amdgcn_readfirstlane(max(0, min(row_lim - m0, T::BM)));
+  const int b_rows = __builtin_amdgcn_readfirstlane(max(0, min(p.N - n0, T::BN)));
+  const uint32_t a_vrow = (uint32_t)((wave * 8 + lrow) * p.lda), b_vrow = (uint32_t)((wave * 8 + lrow) * p.ldb);
+  const uint32_t vchunk = (uint32_t)(lslot ^ lrow);
+  const uint32_t a_jstep = (uint32_t)(T::NW * 8 * p.lda), b_jstep = (uint32_t)(T::NW * 8 * p.ldb);
+  const __amdgpu_buffer_rsrc_t a_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(A + (int64_t)m0 * p.lda), (short)0, a_rows * (int)p.lda, 0x00020000);
+  // Scale staged by this thread: A row m0 + tid (tid < BM), B column block
+  // n0/128 + (tid - BM) (BM <= tid < BM + NBT), else a harmless duplicate of row 0.
+  const bool sc_is_b = tid >= T::BM && tid < T::BM + T::NBT;
+  const int64_t sc_row = sc_is_b ? (int64_t)min(n0 / 128 + (tid - T::BM), NB - 1)
+                                 : (int64_t)max(0, min(m0 + (tid < T::BM ? tid : 0), row_lim - 1));
+
+  // fragment-read geometry: MFMA row j of B fragment f is tile column
+  // (j/4)*16 + f*4 + j%4, so lane group q = lane/16 ends up with columns
+  // 16q .. 16q+15 of the wave tile (4 per fragment).
+  // With h linear, lds_off(r0 + x, c) = (lds_off(x, c) ^ (h(r0) << 4)) + r0*128
+  // whenever r0 has no bits below 4 in common with x; fragment offsets are
+  // therefore a per-lane base XOR a compile-time constant, plus an immediate.
+  const int fr = lane & 15;
+  const int kc = (lane >> 4) * 2;  // first of the lane's two 16-B K chunks
+  const int a_base = lds_off(wm * T::TM + fr, kc);                                  // fragment 0, chunk kc
+  const int b_base = T::A_BYTES + lds_off(wn * T::TN + (fr >> 2) * 16 + (fr & 3), kc);  // fragment 0, chunk kc
+
+  // a wave whose rows all lie past masked_m skips its MFMAs (masked decode)
+  const int fm_live = (MODE == MODE_MASKED) ? (row_lim > m0 + wm * T::TM ? 1 : 0) : 1;
 
   for (int pass = 0; pass < npass; ++pass) {
-    const int gg = (MODE == MODE_MASKED) ? g : pg[pass];
+    const int gg = __builtin_amdgcn_readfirstlane((MODE == MODE_MASKED) ? g : pg[pass]);
     const uint8_t* B = p.b + (int64_t)gg * p.b_gs;
-    const void* sfa = static_cast<const char*>(p.sfa) + sfa_g * (SF == SF_F32 ? 4 : 4);
-    const void* sfb = static_cast<const char*>(p.sfb) + (int64_t)gg * p.sfb_gs * 4;
+    const __amdgpu_buffer_rsrc_t b_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(B + (int64_t)n0 * p.ldb), (short)0, b_rows * (int)p.ldb, 0x00020000);
+    const void* sfa = static_cast<const float*>(p.sfa) + sfa_goff;
+    const void* sfb = static_cast<const float*>(p.sfb) + (int64_t)gg * p.sfb_gs;
+    const void* sc_base = sc_is_b ? sfb : sfa;
+    const int64_t sc_srow = sc_is_b ? p.sfb_sn : p.sfa_sm, sc_sk = sc_is_b ? p.sfb_sk : p.sfa_sk;
+    auto load_sc = [&](int kb) { return load_scale<SF>(sc_base, sc_row, kb, sc_srow, sc_sk); };
 
     f32x4 acc[T::FM][T::FN];
 #pragma unroll
@@ -153,91 +236,184 @@ __global__ __launch_bounds__(WM* WN * 64) void fp8_gemm_kernel(const Fp8GemmPara
 #pragma unroll
       for (int j = 0; j < T::FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    i32x4 ra[T::ACH], rb[T::BCH];
-    float rsa = 0.f, rsb = 0.f;
-    auto gload = [&](int kb) {
+    auto issue_loads = [&](uint8_t* stage, int kb) {
+      const int koff = kb * BK;
 #pragma unroll
-      for (int j = 0; j < T::ACH; ++j) ra[j] = *reinterpret_cast<const i32x4*>(asrc[j] + (int64_t)kb * BK);
-#pragma unroll
-      for (int j = 0; j < T::BCH; ++j)
-        rb[j] = *reinterpret_cast<const i32x4*>(B + (int64_t)brow[j] * p.ldb + (int64_t)kb * BK + ((tid + j * T::NT) & 7) * 16);
-      if (tid < BM) rsa = load_scale<SF>(sfa, sa_row, kb, p.sfa_sm, p.sfa_sk);
-      rsb = load_scale<SF>(sfb, nb_wave, kb, p.sfb_sn, p.sfb_sk);
-    };
-    auto lstore = [&](int st) {
-      uint8_t* base = smem + st * T::STAGE;
-#pragma unroll
-      for (int j = 0; j < T::ACH; ++j) *reinterpret_cast<i32x4*>(base + aoff[j]) = ra[j];
-#pragma unroll
-      for (int j = 0; j < T::BCH; ++j) *reinterpret_cast<i32x4*>(base + boff[j]) = rb[j];
-      if (tid < BM) ssa[st][tid] = rsa;
-    };
-
-    gload(0);
-    lstore(0);
-    float sb_cur = rsb;
-    __syncthreads();
-
-    const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
-    for (int kb = 0; kb < KB; ++kb) {
-      const int st = kb & 1;
-      const bool more = kb + 1 < KB;
-      if (more) gload(kb + 1);
-
-      const uint8_t* As = smem + st * T::STAGE;
-      const uint8_t* Bs = As + BM * BK;
-      const int fr = lane & 15;          // fragment row (A) / column (B)
-      const int fc = (lane >> 4) * 2;    // first of the lane's two 16-B K chunks
-      i32x8 bf[T::FN];
-#pragma unroll
-      for (int j = 0; j < T::FN; ++j) {
-        const int r = wn * T::TN + j * 16 + fr;
-        const i32x4 lo = *reinterpret_cast<const i32x4*>(Bs + lds_off(r, fc));
-        const i32x4 hi = *reinterpret_cast<const i32x4*>(Bs + lds_off(r, fc + 1));
-        bf[j] = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      for (int j = 0; j < T::A_LOADS; ++j) {
+        const uint32_t hu = (uint32_t)swz((j * T::NW + wave) * 8);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(a_rsrc, (lds_void*)(stage + (j * T::NW + wave) * 1024), 16,
+                                                 a_vrow + j * a_jstep + ((vchunk ^ hu) << 4), koff, 0, 0);
       }
 #pragma unroll
-      for (int i = 0; i < T::FM; ++i) {
-        const int r = wm * T::TM + i * 16 + fr;
-        const i32x4 lo = *reinterpret_cast<const i32x4*>(As + lds_off(r, fc));
-        const i32x4 hi = *reinterpret_cast<const i32x4*>(As + lds_off(r, fc + 1));
-        const i32x8 af = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        const f32x4 s = *reinterpret_cast<const f32x4*>(&ssa[st][wm * T::TM + i * 16 + (lane >> 4) * 4]) * sb_cur;
+      for (int j = 0; j < T::B_LOADS; ++j) {
+        const uint32_t hu = (uint32_t)swz((j * T::NW + wave) * 8);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(b_rsrc, (lds_void*)(stage + T::A_BYTES + (j * T::NW + wave) * 1024), 16,
+                                                 b_vrow + j * b_jstep + ((vchunk ^ hu) << 4), koff, 0, 0);
+      }
+    };
+
+    // One K-block of the wave tile, software-pipelined by hand: the FN
+    // MFMAs of A fragment i are interleaved with the promote FMAs of
+    // fragment i-1, whose partials were produced a full fragment earlier, so
+    // no FMA waits on an MFMA in flight; the LDS reads of fragment i+1 are
+    // in flight meanwhile.  Scheduling fences keep exactly this order (the
+    // compiler would otherwise pair each MFMA with its own FMAs).
+    auto compute = [&](const uint8_t* stage, const float* sa_lds) {
+      const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+      const float sb = sa_lds[T::BM + (wn * T::TN) / 128];
+      auto b_frag = [&](int f) {
+        const int off = (b_base ^ (swz(f * 4) << 4)) + f * 4 * 128;  // rows +4f
+        const i32x4 lo = *reinterpret_cast<const i32x4*>(stage + off);
+        const i32x4 hi = *reinterpret_cast<const i32x4*>(stage + (off ^ 16));
+        return i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      };
+      auto a_frag = [&](int i) {
+        const int off = (a_base ^ (swz(i * 16) << 4)) + i * 16 * 128;  // rows +16i
+        const i32x4 lo = *reinterpret_cast<const i32x4*>(stage + off);
+        const i32x4 hi = *reinterpret_cast<const i32x4*>(stage + (off ^ 16));
+        return i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      };
+      // fragment group 0 streams the B fragments in: each MFMA waits only for
+      // its own operands, so the first MFMAs start after four LDS reads
+      // instead of after the whole B set (all waves read at once here).
+      f32x4 P[2][T::FN];
+      i32x8 bf[T::FN];
+      float s_prev;
+      float sa_next;
+      i32x8 af_next;
+      {
+        const i32x8 af = a_frag(0);
+        bf[0] = b_frag(0);
+        s_prev = sa_lds[wm * T::TM + fr] * sb;
 #pragma unroll
-        for (int j = 0; j < T::FN; ++j) {
-          const f32x4 part = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af, bf[j], zero, 0, 0, 0, 0, 0, 0);
-          acc[i][j] += part * s;
+        for (int f = 0; f < T::FN; ++f) {
+          __builtin_amdgcn_sched_barrier(0);
+          if (f + 1 < T::FN) bf[f + 1] = b_frag(f + 1);
+          if (f + 1 == T::FN) {
+            sa_next = sa_lds[wm * T::TM + 16 + fr];
+            af_next = a_frag(1);
+          }
+          P[0][f] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf[f], af, zero, 0, 0, 0, 0, 0, 0);
         }
       }
-      if (more) {
-        lstore(st ^ 1);
-        sb_cur = rsb;
+#pragma unroll
+      for (int i = 1; i < T::FM; ++i) {
+        const i32x8 af = af_next;
+        const float s_i = sa_next * sb;
+        __builtin_amdgcn_sched_barrier(0);
+        if (i + 1 < T::FM) {  // LDS reads of the next fragment, in flight during this one
+          sa_next = sa_lds[wm * T::TM + (i + 1) * 16 + fr];
+          af_next = a_frag(i + 1);
+        }
+#pragma unroll
+        for (int f = 0; f < T::FN; ++f) {
+          __builtin_amdgcn_sched_barrier(0);
+          P[i & 1][f] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf[f], af, zero, 0, 0, 0, 0, 0, 0);
+          __builtin_amdgcn_sched_barrier(0);
+          acc[i - 1][f] += P[(i - 1) & 1][f] * s_prev;
+        }
+        s_prev = s_i;
       }
-      __syncthreads();
-    }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int f = 0; f < T::FN; ++f) acc[T::FM - 1][f] += P[(T::FM - 1) & 1][f] * s_prev;
+    };
 
-    // ---- epilogue: BF16 out, rows < row_lim of this pass, columns < N
+    // One K-block per call, S = T::STAGES static stages.  Top: store the
+    // scale loaded by the previous call into its stage slot, wait until this
+    // stage's loads have landed (S = 3 leaves the next stage's loads in
+    // flight), barrier.  Then start the loads of K-block kb + S - 1 into the
+    // stage computed S - 1 calls ago (clamped at the end: the last calls
+    // re-load the final K-block into dead stages, harmlessly), and compute.
+    // The scale for kb + S - 1 is consumed only at the top of the next call:
+    // vmcnt is in order, so consuming it earlier would also wait for the
+    // previous call's tile loads.  No branches inside a call, so the MFMA /
+    // promote interleave stays one scheduling region.
+    uint8_t* stages[3] = {smem0, smem1, smem2};
+    float rs;  // scale loaded by the previous call
+    auto kblock = [&](auto st_tag, int kb) {
+      constexpr int ST = decltype(st_tag)::value;
+      constexpr int S = T::STAGES;
+      ssc[(ST + S - 2) % S][tid] = rs;
+      // this wave's loads into the current stage have landed (with S = 3 the
+      // next stage's stay in flight) and its scale store is done; then the
+      // barrier makes every wave's data visible.  A plain s_barrier: a
+      // __syncthreads() would also drain every outstanding load.
+      if (S == 2) __builtin_amdgcn_s_waitcnt(0);
+      else __builtin_amdgcn_s_waitcnt(vmcnt_only(T::A_LOADS + T::B_LOADS) & ~(15 << 8));
+      __builtin_amdgcn_s_barrier();
+      const int kn = min(kb + S - 1, KB - 1);
+      rs = load_sc(kn);
+      __builtin_amdgcn_sched_barrier(0);  // keep the scale load ahead of the tile loads (vmcnt is in order)
+      issue_loads(stages[(ST + S - 1) % S], kn);
+      if (MODE != MODE_MASKED || fm_live > 0) compute(stages[ST], ssc[ST]);
+    };
+
+    // prologue: K-blocks 0 .. S-2 in flight, their scales staged (the last one pending in rs)
+#pragma unroll
+    for (int s = 0; s + 1 < T::STAGES; ++s) issue_loads(stages[s], min(s, KB - 1));
+#pragma unroll
+    for (int s = 0; s + 2 < T::STAGES; ++s) ssc[s][tid] = load_sc(min(s, KB - 1));
+    rs = load_sc(min(T::STAGES - 2, KB - 1));
+    int kb = 0;
+    if constexpr (T::STAGES == 2) {
+      for (; kb + 1 < KB; kb += 2) {
+        kblock(std::integral_constant<int, 0>{}, kb);
+        kblock(std::integral_constant<int, 1>{}, kb + 1);
+      }
+      if (kb < KB) kblock(std::integral_constant<int, 0>{}, kb);
+    } else {
+      for (; kb + 2 < KB; kb += 3) {
+        kblock(std::integral_constant<int, 0>{}, kb);
+        kblock(std::integral_constant<int, 1>{}, kb + 1);
+        kblock(std::integral_constant<int, 2>{}, kb + 2);
+      }
+      if (kb < KB) kblock(std::integral_constant<int, 0>{}, kb);
+      if (kb + 1 < KB) kblock(std::integral_constant<int, 1>{}, kb + 1);
+    }
+    __builtin_amdgcn_s_waitcnt(0);  // drain the redundant last loads before LDS is reused or freed
+
+    // ---- epilogue: BF16, row m = lane%16 of each fragment row, 16 consecutive columns per lane
+    const int col0 = n0 + wn * T::TN + (lane >> 4) * 16;
+    const bool vec_ok = ((p.ldd & 7) == 0) && ((reinterpret_cast<uintptr_t>(D) & 15) == 0);
 #pragma unroll
     for (int i = 0; i < T::FM; ++i) {
+      const int rl = wm * T::TM + i * 16 + fr;
+      const int row = m0 + rl;
+      if (rl < plo[pass] || rl >= phi[pass] || row >= row_lim) continue;
+      uint32_t packed[8];
 #pragma unroll
-      for (int j = 0; j < T::FN; ++j) {
-        const int col = n0 + wn * T::TN + j * 16 + (lane & 15);
+      for (int f = 0; f < T::FN; ++f) {
+        packed[2 * f] = (uint32_t)f32_to_bf16_rne(acc[i][f][0]) | ((uint32_t)f32_to_bf16_rne(acc[i][f][1]) << 16);
+        packed[2 * f + 1] = (uint32_t)f32_to_bf16_rne(acc[i][f][2]) | ((uint32_t)f32_to_bf16_rne(acc[i][f][3]) << 16);
+      }
+      uint16_t* drow = D + (int64_t)row * p.ldd;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int rl = wm * T::TM + i * 16 + (lane >> 4) * 4 + e;
-          const int row = m0 + rl;
-          if (rl >= plo[pass] && rl < phi[pass] && row < row_lim && col < p.N)
-            D[(int64_t)row * p.ldd + col] = f32_to_bf16_rne(acc[i][j][e]);
+      for (int h = 0; h < 2; ++h) {
+        const int c = col0 + 8 * h;
+        if (vec_ok && c + 8 <= p.N) {
+          *reinterpret_cast<i32x4*>(drow + c) =
+              i32x4{(int)packed[4 * h], (int)packed[4 * h + 1], (int)packed[4 * h + 2], (int)packed[4 * h + 3]};
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            if (c + e < p.N) drow[c + e] = (uint16_t)(packed[4 * h + e / 2] >> (16 * (e & 1)));
         }
       }
     }
+    if (pass + 1 < npass) __syncthreads();  // the next pass reuses the LDS stages
   }
 }
 
-template <int BM, int BN, int WM, int WN>
+using TileL = TileShape<256, 256, 2, 4, 2>;  // 512 threads, wave tile 128 x 64, 2 x 64 KB stages
+using TileT = TileShape<256, 128, 4, 2, 3>;  // 512 threads, wave tile  64 x 64, 3 x 48 KB stages
+using TileW = TileShape<128, 256, 2, 4, 3>;  // 512 threads, wave tile  64 x 64, 3 x 48 KB stages
+using TileS = TileShape<128, 128, 2, 2, 3>;  // 256 threads, wave tile  64 x 64, 3 x 32 KB stages
+
+template <class T>
 hipError_t launch_tile(const Fp8GemmParams& p, int mode, int sf_fmt, int64_t grid, hipStream_t stream) {
-  const dim3 g((unsigned)grid), b(WM * WN * 64);
-#define DGMI_LAUNCH(MODE_, SF_) fp8_gemm_kernel<BM, BN, WM, WN, MODE_, SF_><<<g, b, 0, stream>>>(p)
+  const dim3 g((unsigned)grid), b(T::NT);
+#define DGMI_LAUNCH(MODE_, SF_) fp8_gemm_kernel<T, SF_, MODE_><<<g, b, 0, stream>>>(p)
   if (sf_fmt == SF_F32) {
     if (mode == MODE_DENSE) DGMI_LAUNCH(MODE_DENSE, SF_F32);
     else if (mode == MODE_CONTIG) DGMI_LAUNCH(MODE_CONTIG, SF_F32);
@@ -251,17 +427,29 @@ hipError_t launch_tile(const Fp8GemmParams& p, int mode, int sf_fmt, int64_t gri
   return hipGetLastError();
 }
 
+template <class T>
+TileCfg make_cfg(int variant) {
+  TileCfg c;
+  c.bm = T::BM;
+  c.bn = T::BN;
+  c.threads = T::NT;
+  c.lds_bytes = T::STAGES * T::STAGE + T::STAGES * T::NT * 4 + (T::STAGES == 3 ? 0 : 16);
+  c.variant = variant;
+  return c;
+}
+
 }  // namespace
 
+// Tile choice, a pure function of the shapes.  Rows <= 128 (small dense M,
+// decode buffers of up to 128 rows per expert) use 128-row tiles with three
+// stages; everything else the 256 x 256 tile, which measured fastest on all
+// the large dense and grouped shapes (its 2-stage pipeline hides the loads;
+// the 3-stage 256 x 128 tile re-reads more from L2 and issues more LDS reads
+// per MFMA).
 TileCfg fp8_gemm_config(int mode, int64_t G, int64_t M, int64_t N, int64_t K) {
-  (void)mode; (void)G; (void)M; (void)N; (void)K;
-  TileCfg c;
-  c.bm = 128;
-  c.bn = 128;
-  c.threads = 256;
-  c.lds_bytes = 2 * (128 + 128) * BK + 2 * 128 * 4;
-  c.variant = 0;
-  return c;
+  (void)mode; (void)G; (void)K;
+  if (M <= 128) return N <= 128 ? make_cfg<TileS>(2) : make_cfg<TileW>(1);
+  return make_cfg<TileL>(0);
 }
 
 int64_t fp8_gemm_grid(const TileCfg& cfg, int mode, int64_t G, int64_t M, int64_t N) {
@@ -275,7 +463,12 @@ hipError_t launch_fp8_gemm(Fp8GemmParams p, int mode, int sf_fmt, hipStream_t st
   p.tiles_n = (p.N + cfg.bn - 1) / cfg.bn;
   const int64_t grid = fp8_gemm_grid(cfg, mode, p.G, p.M, p.N);
   if (grid == 0) return hipSuccess;
-  return launch_tile<128, 128, 2, 2>(p, mode, sf_fmt, grid, stream);
+  switch (cfg.variant) {
+    case 0: return launch_tile<TileL>(p, mode, sf_fmt, grid, stream);
+    case 1: return launch_tile<TileW>(p, mode, sf_fmt, grid, stream);
+    case 2: return launch_tile<TileS>(p, mode, sf_fmt, grid, stream);
+    default: return launch_tile<TileT>(p, mode, sf_fmt, grid, stream);
+  }
 }
 
 }  // namespace dgmi
