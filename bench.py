@@ -182,10 +182,39 @@ class MaskedWorkload:
 
 
 # ---------------------------------------------------------------------------
+# recorded HBM traffic of the GEMM kernel (rocprofv3 PMC), valid for one source
+# ---------------------------------------------------------------------------
+
+def recorded_traffic(workload):
+    """Bytes per GEMM launch (FETCH + WRITE, calibrated against a 1 GiB copy)
+    from profiles/fp8_gemm_traffic.txt, or None when the record is missing or
+    was taken on a different version of the kernel source."""
+    import hashlib
+
+    rec_path = os.path.join(ROOT, "profiles", "fp8_gemm_traffic.txt")
+    src_path = os.path.join(ROOT, "moe_grouped_gemm_x128_amd", "csrc", "gemm_fp8.hip")
+    if not os.path.exists(rec_path):
+        return None
+    rec = {}
+    for line in open(rec_path):
+        if line.startswith("#") or ":" not in line:
+            continue
+        k, v = line.split(":", 1)
+        rec[k.strip()] = v.strip()
+    cur = hashlib.sha256(open(src_path, "rb").read()).hexdigest()[:16]
+    if rec.get("gemm_fp8_source_sha256_16") != cur:
+        return None
+    try:
+        return float(rec[f"{workload}_fetch_bytes_per_launch"]) + float(rec[f"{workload}_write_bytes_per_launch"])
+    except KeyError:
+        return None
+
+
+# ---------------------------------------------------------------------------
 # CPU baseline: the oracle on a bounded sample of the dense workload
 # ---------------------------------------------------------------------------
 
-def time_cpu_baseline(rows_a=512, rows_b=6144):
+def time_cpu_baseline(rows_a=512, rows_b=8192):
     import oracle
     from moe_grouped_gemm_x128_amd import synth
 
@@ -295,6 +324,9 @@ def main():
         achieved = mean_flops / (mean_launch_ms * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": achieved, "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": achieved / FP8_PEAK_TFLOPS, "traffic": None}
+    roof["traffic"] = recorded_traffic(args.workload)
+    roof["traffic_unit"] = "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)"
+    roof["algorithmic_bytes_per_launch"] = float(np.mean(W.gemm_bytes))
     roof["kernel"] = "fp8_gemm_kernel"
     roof["avg_launch_us"] = mean_launch_ms * 1e3
     roof["per_launch"] = "mean over the workload's GEMM launches of one step (algorithmic work / HIP-event duration)"
