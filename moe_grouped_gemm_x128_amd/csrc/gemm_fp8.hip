@@ -85,7 +85,7 @@ struct TileShape {
   static_assert(TN == 64 && 128 % TN == 0, "a wave's columns must lie in one 128-column scale block");
   static constexpr int NBT = (BN + 127) / 128;      // 128-column scale blocks per tile
   static_assert(BM + NBT <= NT, "one thread per tile row stages the A scales, one per column block the B scale");
-  static_assert(STAGES == 2 || STAGES == 3, "two or three LDS stages");
+  static_assert(STAGES == 2, "the K loop double-buffers the LDS tiles");
 };
 
 template <int SF>
@@ -122,7 +122,6 @@ template <class T, int SF, int MODE>
 __global__ __launch_bounds__(T::NT) void fp8_gemm_kernel(const Fp8GemmParams p) {
   __shared__ __attribute__((aligned(16))) uint8_t smem0[T::STAGE];
   __shared__ __attribute__((aligned(16))) uint8_t smem1[T::STAGE];
-  __shared__ __attribute__((aligned(16))) uint8_t smem2[T::STAGES == 3 ? T::STAGE : 16];
   // per stage: A row scales in slots [0, BM), B block scales in [BM, BM + NBT);
   // one slot per thread so the stores need no branch
   __shared__ __attribute__((aligned(16))) float ssc[T::STAGES][T::NT];
@@ -252,124 +251,134 @@ __global__ __launch_bounds__(T::NT) void fp8_gemm_kernel(const Fp8GemmParams p) 
       }
     };
 
-    // One K-block of the wave tile, software-pipelined by hand: the FN
-    // MFMAs of A fragment i are interleaved with the promote FMAs of
-    // fragment i-1, whose partials were produced a full fragment earlier, so
-    // no FMA waits on an MFMA in flight; the LDS reads of fragment i+1 are
-    // in flight meanwhile.  Scheduling fences keep exactly this order (the
-    // compiler would otherwise pair each MFMA with its own FMAs).
-    auto compute = [&](const uint8_t* stage, const float* sa_lds) {
-      const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
-      const float sb = sa_lds[T::BM + (wn * T::TN) / 128];
-      auto b_frag = [&](int f) {
-        const int off = (b_base ^ (swz(f * 4) << 4)) + f * 4 * 128;  // rows +4f
-        const i32x4 lo = *reinterpret_cast<const i32x4*>(stage + off);
-        const i32x4 hi = *reinterpret_cast<const i32x4*>(stage + (off ^ 16));
-        return i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-      };
-      auto a_frag = [&](int i) {
-        const int off = (a_base ^ (swz(i * 16) << 4)) + i * 16 * 128;  // rows +16i
-        const i32x4 lo = *reinterpret_cast<const i32x4*>(stage + off);
-        const i32x4 hi = *reinterpret_cast<const i32x4*>(stage + (off ^ 16));
-        return i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-      };
-      // fragment group 0 streams the B fragments in: each MFMA waits only for
-      // its own operands, so the first MFMAs start after four LDS reads
-      // instead of after the whole B set (all waves read at once here).
-      f32x4 P[2][T::FN];
-      i32x8 bf[T::FN];
-      float s_prev;
-      float sa_next;
-      i32x8 af_next;
-      {
-        const i32x8 af = a_frag(0);
-        bf[0] = b_frag(0);
-        s_prev = sa_lds[wm * T::TM + fr] * sb;
+    // ---- K loop: one continuous software pipeline over fragment groups.
+    // Group (kb, i) issues the FN MFMAs of A fragment i of K-block kb and,
+    // interleaved, the promote FMAs of the previous group (its partials are
+    // a whole group old, so no FMA waits on an MFMA in flight), while the LDS
+    // reads for the next group are in flight.  Two LDS stages.  The barrier
+    // sits at a late point of each K-block, before its last group: by then
+    // every wave has read all it needs of the current stage (the last A
+    // fragment is already in registers), so after the barrier that stage is
+    // free for the loads of K-block kb+2, and the other stage -- whose loads
+    // were issued one K-block earlier -- is complete and visible.  The last
+    // group therefore streams in the next K-block's B fragments, first A
+    // fragment and scales, and the next K-block starts with no bubble.
+    // Scheduling fences keep exactly this order (the compiler would otherwise
+    // pair each MFMA with its own FMAs and serialise on the MFMA latency).
+    const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+    auto b_frag = [&](const uint8_t* stage, int f) {
+      const int off = (b_base ^ (swz(f * 4) << 4)) + f * 4 * 128;  // rows +4f
+      const i32x4 lo = *reinterpret_cast<const i32x4*>(stage + off);
+      const i32x4 hi = *reinterpret_cast<const i32x4*>(stage + (off ^ 16));
+      return i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    };
+    auto a_frag = [&](const uint8_t* stage, int i) {
+      const int off = (a_base ^ (swz(i * 16) << 4)) + i * 16 * 128;  // rows +16i
+      const i32x4 lo = *reinterpret_cast<const i32x4*>(stage + off);
+      const i32x4 hi = *reinterpret_cast<const i32x4*>(stage + (off ^ 16));
+      return i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    };
+    const int sa_row0 = wm * T::TM + fr;           // this lane's scale slot for fragment row 0
+    const int sb_slot = T::BM + (wn * T::TN) / 128;  // this wave's B block scale slot
+
+    // carried across groups / K-blocks
+    i32x8 bf[T::FN];
+    i32x8 af;            // A fragment of the current group
+    float sa, sb;        // raw scales of the current group's rows / the current K-block
+    f32x4 P[2][T::FN];   // partials of the current and the previous group
+    float s_prev = 0.f;  // combined scale of the previous group (the first promote adds 0 * 0)
 #pragma unroll
-        for (int f = 0; f < T::FN; ++f) {
-          __builtin_amdgcn_sched_barrier(0);
-          if (f + 1 < T::FN) bf[f + 1] = b_frag(f + 1);
-          if (f + 1 == T::FN) {
-            sa_next = sa_lds[wm * T::TM + 16 + fr];
-            af_next = a_frag(1);
-          }
-          P[0][f] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf[f], af, zero, 0, 0, 0, 0, 0, 0);
-        }
-      }
+    for (int f = 0; f < T::FN; ++f) P[(T::FM - 1) & 1][f] = zero;
+    float rs;            // scale value staged by this thread for a later K-block
+
+    // prologue: K-blocks 0 and 1 in flight, K-block 0 landed, its first operands in registers
+    // The wait before the barrier counts the loads issued after the stage-0
+    // tiles (one scale + the stage-1 tiles); the fences keep the issue order
+    // that count assumes (the compiler would otherwise hoist the scale loads
+    // above the tile loads and leave the last stage-0 tile load in flight).
+    issue_loads(smem0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    const float rs0 = load_sc(0);
+    rs = load_sc(min(1, KB - 1));
+    __builtin_amdgcn_sched_barrier(0);
+    issue_loads(smem1, min(1, KB - 1));
+    __builtin_amdgcn_sched_barrier(0);
+    ssc[0][tid] = rs0;
+    __builtin_amdgcn_s_waitcnt(vmcnt_only(T::A_LOADS + T::B_LOADS + 1) & ~(15 << 8));
+    __builtin_amdgcn_s_barrier();
 #pragma unroll
-      for (int i = 1; i < T::FM; ++i) {
-        const i32x8 af = af_next;
-        const float s_i = sa_next * sb;
+    for (int f = 0; f < T::FN; ++f) bf[f] = b_frag(smem0, f);
+    af = a_frag(smem0, 0);
+    sa = ssc[0][sa_row0];
+    sb = ssc[0][sb_slot];
+
+    auto kblock = [&](auto st_tag, int kb) {
+      constexpr int ST = decltype(st_tag)::value;
+      uint8_t* cur = ST == 0 ? smem0 : smem1;
+      uint8_t* nxt = ST == 0 ? smem1 : smem0;
+      float* sc_cur = ssc[ST];
+      float* sc_nxt = ssc[ST ^ 1];
+#pragma unroll
+      for (int i = 0; i < T::FM; ++i) {
         __builtin_amdgcn_sched_barrier(0);
-        if (i + 1 < T::FM) {  // LDS reads of the next fragment, in flight during this one
-          sa_next = sa_lds[wm * T::TM + (i + 1) * 16 + fr];
-          af_next = a_frag(i + 1);
+        const float s_cur = sa * sb;
+        i32x8 af_next;
+        float sa_next, sb_next = sb;
+        if (i + 1 < T::FM) {
+          sa_next = sc_cur[sa_row0 + (i + 1) * 16];
+          af_next = a_frag(cur, i + 1);
+        } else {
+          // late point: stage the scales of K-block kb+1, wait for its tiles
+          // (loaded one K-block ago), barrier; `cur` is now free for kb+2
+          sc_nxt[tid] = rs;
+          __builtin_amdgcn_s_waitcnt(vmcnt_only(0) & ~(15 << 8));
+          __builtin_amdgcn_s_barrier();
+          const int kn2 = min(kb + 2, KB - 1);
+          rs = load_sc(kn2);
+          __builtin_amdgcn_sched_barrier(0);  // scale load ahead of the tile loads (vmcnt is in order)
+          issue_loads(cur, kn2);
+          __builtin_amdgcn_sched_barrier(0);
+          sa_next = sc_nxt[sa_row0];
+          sb_next = sc_nxt[sb_slot];
+          af_next = a_frag(nxt, 0);
         }
 #pragma unroll
         for (int f = 0; f < T::FN; ++f) {
           __builtin_amdgcn_sched_barrier(0);
           P[i & 1][f] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf[f], af, zero, 0, 0, 0, 0, 0, 0);
           __builtin_amdgcn_sched_barrier(0);
-          acc[i - 1][f] += P[(i - 1) & 1][f] * s_prev;
+          if (i > 0) acc[i - 1][f] += P[(i - 1) & 1][f] * s_prev;
+          else acc[T::FM - 1][f] += P[(T::FM - 1) & 1][f] * s_prev;
+          if (i + 1 == T::FM) bf[f] = b_frag(nxt, f);  // last use of bf[f] in this K-block
         }
-        s_prev = s_i;
+        s_prev = s_cur;
+        af = af_next;
+        sa = sa_next;
+        sb = sb_next;
       }
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int f = 0; f < T::FN; ++f) acc[T::FM - 1][f] += P[(T::FM - 1) & 1][f] * s_prev;
     };
 
-    // One K-block per call, S = T::STAGES static stages.  Top: store the
-    // scale loaded by the previous call into its stage slot, wait until this
-    // stage's loads have landed (S = 3 leaves the next stage's loads in
-    // flight), barrier.  Then start the loads of K-block kb + S - 1 into the
-    // stage computed S - 1 calls ago (clamped at the end: the last calls
-    // re-load the final K-block into dead stages, harmlessly), and compute.
-    // The scale for kb + S - 1 is consumed only at the top of the next call:
-    // vmcnt is in order, so consuming it earlier would also wait for the
-    // previous call's tile loads.  No branches inside a call, so the MFMA /
-    // promote interleave stays one scheduling region.
-    uint8_t* stages[3] = {smem0, smem1, smem2};
-    float rs;  // scale loaded by the previous call
-    auto kblock = [&](auto st_tag, int kb) {
-      constexpr int ST = decltype(st_tag)::value;
-      constexpr int S = T::STAGES;
-      ssc[(ST + S - 2) % S][tid] = rs;
-      // this wave's loads into the current stage have landed (with S = 3 the
-      // next stage's stay in flight) and its scale store is done; then the
-      // barrier makes every wave's data visible.  A plain s_barrier: a
-      // __syncthreads() would also drain every outstanding load.
-      if (S == 2) __builtin_amdgcn_s_waitcnt(0);
-      else __builtin_amdgcn_s_waitcnt(vmcnt_only(T::A_LOADS + T::B_LOADS) & ~(15 << 8));
-      __builtin_amdgcn_s_barrier();
-      const int kn = min(kb + S - 1, KB - 1);
-      rs = load_sc(kn);
-      __builtin_amdgcn_sched_barrier(0);  // keep the scale load ahead of the tile loads (vmcnt is in order)
-      issue_loads(stages[(ST + S - 1) % S], kn);
-      if (MODE != MODE_MASKED || fm_live > 0) compute(stages[ST], ssc[ST]);
-    };
-
-    // prologue: K-blocks 0 .. S-2 in flight, their scales staged (the last one pending in rs)
-#pragma unroll
-    for (int s = 0; s + 1 < T::STAGES; ++s) issue_loads(stages[s], min(s, KB - 1));
-#pragma unroll
-    for (int s = 0; s + 2 < T::STAGES; ++s) ssc[s][tid] = load_sc(min(s, KB - 1));
-    rs = load_sc(min(T::STAGES - 2, KB - 1));
     int kb = 0;
-    if constexpr (T::STAGES == 2) {
+    if (MODE != MODE_MASKED || fm_live > 0) {
       for (; kb + 1 < KB; kb += 2) {
         kblock(std::integral_constant<int, 0>{}, kb);
         kblock(std::integral_constant<int, 1>{}, kb + 1);
       }
       if (kb < KB) kblock(std::integral_constant<int, 0>{}, kb);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int f = 0; f < T::FN; ++f) acc[T::FM - 1][f] += P[(T::FM - 1) & 1][f] * s_prev;
     } else {
-      for (; kb + 2 < KB; kb += 3) {
-        kblock(std::integral_constant<int, 0>{}, kb);
-        kblock(std::integral_constant<int, 1>{}, kb + 1);
-        kblock(std::integral_constant<int, 2>{}, kb + 2);
+      // this wave's rows all lie past masked_m: it still takes part in the
+      // loads and barriers of every K-block, without MFMAs
+      for (; kb < KB; ++kb) {
+        ((kb & 1) ? ssc[0] : ssc[1])[tid] = rs;
+        __builtin_amdgcn_s_waitcnt(vmcnt_only(0) & ~(15 << 8));
+        __builtin_amdgcn_s_barrier();
+        const int kn2 = min(kb + 2, KB - 1);
+        rs = load_sc(kn2);
+        issue_loads((kb & 1) ? smem1 : smem0, kn2);
       }
-      if (kb < KB) kblock(std::integral_constant<int, 0>{}, kb);
-      if (kb + 1 < KB) kblock(std::integral_constant<int, 1>{}, kb + 1);
     }
     __builtin_amdgcn_s_waitcnt(0);  // drain the redundant last loads before LDS is reused or freed
 
@@ -406,9 +415,9 @@ __global__ __launch_bounds__(T::NT) void fp8_gemm_kernel(const Fp8GemmParams p) 
 }
 
 using TileL = TileShape<256, 256, 2, 4, 2>;  // 512 threads, wave tile 128 x 64, 2 x 64 KB stages
-using TileT = TileShape<256, 128, 4, 2, 3>;  // 512 threads, wave tile  64 x 64, 3 x 48 KB stages
-using TileW = TileShape<128, 256, 2, 4, 3>;  // 512 threads, wave tile  64 x 64, 3 x 48 KB stages
-using TileS = TileShape<128, 128, 2, 2, 3>;  // 256 threads, wave tile  64 x 64, 3 x 32 KB stages
+using TileT = TileShape<256, 128, 4, 2, 2>;  // 512 threads, wave tile  64 x 64, 2 x 48 KB stages
+using TileW = TileShape<128, 256, 2, 4, 2>;  // 512 threads, wave tile  64 x 64, 2 x 48 KB stages
+using TileS = TileShape<128, 128, 2, 2, 2>;  // 256 threads, wave tile  64 x 64, 2 x 32 KB stages
 
 template <class T>
 hipError_t launch_tile(const Fp8GemmParams& p, int mode, int sf_fmt, int64_t grid, hipStream_t stream) {
@@ -433,7 +442,7 @@ TileCfg make_cfg(int variant) {
   c.bm = T::BM;
   c.bn = T::BN;
   c.threads = T::NT;
-  c.lds_bytes = T::STAGES * T::STAGE + T::STAGES * T::NT * 4 + (T::STAGES == 3 ? 0 : 16);
+  c.lds_bytes = T::STAGES * T::STAGE + T::STAGES * T::NT * 4;
   c.variant = variant;
   return c;
 }
@@ -441,11 +450,10 @@ TileCfg make_cfg(int variant) {
 }  // namespace
 
 // Tile choice, a pure function of the shapes.  Rows <= 128 (small dense M,
-// decode buffers of up to 128 rows per expert) use 128-row tiles with three
-// stages; everything else the 256 x 256 tile, which measured fastest on all
-// the large dense and grouped shapes (its 2-stage pipeline hides the loads;
-// the 3-stage 256 x 128 tile re-reads more from L2 and issues more LDS reads
-// per MFMA).
+// decode buffers of up to 128 rows per expert) use 128-row tiles;
+// everything else the 256 x 256 tile, which measured fastest on all the
+// large dense and grouped shapes (the 256 x 128 tile re-reads more from L2
+// and issues more LDS reads per MFMA).
 TileCfg fp8_gemm_config(int mode, int64_t G, int64_t M, int64_t N, int64_t K) {
   (void)mode; (void)G; (void)K;
   if (M <= 128) return N <= 128 ? make_cfg<TileS>(2) : make_cfg<TileW>(1);
