@@ -181,6 +181,124 @@ class MaskedWorkload:
                 "sum_masked_m": int(self.mm_host.sum()), "shapes_NK": self.shapes}
 
 
+class MaskedGraphWorkload:
+    """64 experts x 128 rows, N 7168, K 2048: per-token UE8M0 cast of the
+    activations, pack_ue8m0_to_int of both scale tensors, the masked FP8 GEMM
+    on the packed scales and the masked BF16 GEMM on the same shapes, captured
+    once as one hipGraph and replayed with a new masked_m (uniform integers in
+    [0, 128]) written into the device tensor before each replay."""
+    name = "masked_graph_ue8m0_fp8_and_bf16"
+
+    def __init__(self, torch, mg, synth):
+        self.torch, self.mg, self.synth = torch, mg, synth
+        dev = torch.device("cuda")
+        c = synth.MASKED_GRAPH
+        G, max_m, N, K = c["G"], c["max_m"], c["N"], c["K"]
+        KB = K // 128
+        self.G, self.max_m, self.N, self.K = G, max_m, N, K
+        self.shapes = [(N, K), (N, K)]  # FP8 masked, BF16 masked
+        self.seed_m = c["seed_m"]
+        self.xa = torch.from_numpy(synth.normal_f32(c["seed_a"], (G, max_m, K))).to(dev)
+        self.qb = torch.empty((G, N, K), dtype=torch.uint8, device=dev)
+        self.sfb = torch.empty((G, N // 128, KB), dtype=torch.float32, device=dev)
+        self.b16 = torch.empty((G, N, K), dtype=torch.bfloat16, device=dev)
+        xb = torch.empty((N, K), dtype=torch.float32, device=dev)
+        for g, chunk in enumerate(synth.normal_f32_chunks(c["seed_b"], (G, N, K))):
+            xb.copy_(torch.from_numpy(chunk))
+            mg.per_block_cast_to_fp8(xb, self.qb[g], self.sfb[g], True)  # expert weights: quantized once
+            self.b16[g].copy_(xb)
+        del xb
+        self.a16 = self.xa.to(torch.bfloat16)
+        self.qa = torch.empty((G, max_m, K), dtype=torch.uint8, device=dev)
+        self.sfa = torch.empty((G, max_m, KB), dtype=torch.float32, device=dev)
+        self.pa = torch.empty((G, max_m, (KB + 3) // 4), dtype=torch.int32, device=dev)
+        self.pb = torch.empty((G, N // 128, (KB + 3) // 4), dtype=torch.int32, device=dev)
+        self.d8 = torch.empty((G, max_m, N), dtype=torch.bfloat16, device=dev)
+        self.d16 = torch.empty((G, max_m, N), dtype=torch.bfloat16, device=dev)
+        self.masked_m = torch.zeros(G, dtype=torch.int32, device=dev)
+        self.draw = 0
+        self.mm_host = []
+        self.flops, self.gemm_bytes = [0.0, 0.0], [0.0, 0.0]
+        self.nsteps = 0
+
+        self._calls()  # eager warm-up before capture
+        torch.cuda.synchronize()
+        self.graph = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            self.graph.capture_begin()
+            self._calls()
+            self.graph.capture_end()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+
+    def _calls(self, events=None):
+        mg = self.mg
+        mg.per_token_cast_to_fp8(self.xa, self.qa, self.sfa, True)
+        mg.pack_ue8m0_to_int(self.sfa, self.pa)
+        mg.pack_ue8m0_to_int(self.sfb, self.pb)
+        if events is not None:
+            events[0][0].record()
+        mg.m_grouped_fp8_gemm_nt_masked(self.qa, self.qb, self.pa, self.pb, self.d8, self.masked_m, self.max_m)
+        if events is not None:
+            events[0][1].record()
+            events[1][0].record()
+        mg.m_grouped_bf16_gemm_nt_masked(self.a16, self.b16, self.d16, self.masked_m, self.max_m)
+        if events is not None:
+            events[1][1].record()
+
+    def _next_masked_m(self):
+        mm = self.synth.masked_m_uniform(self.seed_m + 2 + self.draw, self.G, self.max_m)
+        self.draw += 1
+        return mm
+
+    def step(self, events=None):
+        """One replay of the captured graph with a fresh masked_m."""
+        mm = self._next_masked_m()
+        self.masked_m.copy_(self.torch.from_numpy(mm))
+        self.graph.replay()
+        self.mm_host.append(mm)
+
+    def _bytes(self, mm):
+        rows, active = int(mm.sum()), int((mm > 0).sum())
+        N, K = self.N, self.K
+        KB = K // 128
+        nb = (N + 127) // 128
+        fp8 = active * (N * K + 4 * nb * ((KB + 3) // 4)) + rows * (K + 4 * ((KB + 3) // 4) + 2 * N) + 4 * self.G
+        bf16 = active * (2 * N * K) + rows * (2 * K + 2 * N) + 4 * self.G
+        return 2.0 * rows * N * K, fp8, bf16
+
+    def step_bytes(self):
+        """Mean algorithmic GEMM bytes (FP8 + BF16) per replayed step."""
+        return float(np.mean([sum(self._bytes(m)[1:]) for m in self.mm_host]))
+
+    def timing_pass(self, events):
+        """Eager pass over the same calls with HIP events around each GEMM
+        (events cannot be recorded inside a replay); per-kernel figures come
+        from these passes, the step time from the replays."""
+        mm = self._next_masked_m()
+        self.masked_m.copy_(self.torch.from_numpy(mm))
+        self._calls(events)
+        f, b8, b16 = self._bytes(mm)
+        self.flops[0] += f
+        self.flops[1] += f
+        self.gemm_bytes[0] += b8
+        self.gemm_bytes[1] += b16
+        self.nsteps += 1
+
+    def finish(self):
+        n = max(self.nsteps, 1)
+        self.flops = [f / n for f in self.flops]
+        self.gemm_bytes = [b / n for b in self.gemm_bytes]
+
+    def config(self):
+        return {"workload": self.name, "experts": self.G, "max_m": self.max_m, "N": self.N, "K": self.K,
+                "mean_sum_masked_m": float(np.mean([m.sum() for m in self.mm_host])) if self.mm_host else 0.0,
+                "kernels": ["gemm_kernel FP8 kind (UE8M0 packed scales)", "gemm_kernel BF16 kind"],
+                "step": "one hipGraph replay: UE8M0 cast of A, 2 packs, FP8 masked GEMM, BF16 masked GEMM"}
+
+
 # ---------------------------------------------------------------------------
 # recorded HBM traffic of the GEMM kernel (rocprofv3 PMC), valid for one source
 # ---------------------------------------------------------------------------
@@ -192,7 +310,7 @@ def recorded_traffic(workload):
     import hashlib
 
     rec_path = os.path.join(ROOT, "profiles", "fp8_gemm_traffic.txt")
-    src_path = os.path.join(ROOT, "moe_grouped_gemm_x128_amd", "csrc", "gemm_fp8.hip")
+    src_path = os.path.join(ROOT, "moe_grouped_gemm_x128_amd", "csrc", "gemm.hip")
     if not os.path.exists(rec_path):
         return None
     rec = {}
@@ -257,7 +375,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="dense", choices=["dense", "contiguous", "masked"])
+    ap.add_argument("--workload", default="dense", choices=["dense", "contiguous", "masked", "masked_graph"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run one 1 GiB device copy (calibrates rocprofv3 FETCH/WRITE_SIZE counters)")
@@ -280,24 +398,33 @@ def main():
     mg.dgmi_init()
 
     log(f"setting up workload {args.workload}")
-    W = {"dense": DenseWorkload, "contiguous": ContiguousWorkload, "masked": MaskedWorkload}[args.workload](torch, mg, synth)
+    W = {"dense": DenseWorkload, "contiguous": ContiguousWorkload, "masked": MaskedWorkload,
+         "masked_graph": MaskedGraphWorkload}[args.workload](torch, mg, synth)
     torch.cuda.synchronize()
 
     for _ in range(args.warmup):
         W.step()
     torch.cuda.synchronize()
+    if hasattr(W, "timing_pass"):
+        W.mm_host = []  # count the timed replays only
     log(f"warmup done ({args.warmup} steps); timing {args.steps} steps")
 
     nshape = len(W.flops)
     events = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(nshape)]
               for _ in range(args.steps)]
     torch.cuda.synchronize()
+    graph_wl = hasattr(W, "timing_pass")
     t0 = time.perf_counter()
     for s in range(args.steps):
-        W.step(events[s])
+        W.step(None if graph_wl else events[s])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     log("timed region done")
+    if graph_wl:
+        for s in range(args.steps):
+            W.timing_pass(events[s])
+        torch.cuda.synchronize()
+        W.finish()
 
     if args.copy_probe:
         src = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
@@ -314,8 +441,14 @@ def main():
     value = total_flops / (ms_per_step * 1e-3) / 1e12
     mean_launch_ms = float(np.mean(gemm_ms))
     mean_flops = total_flops / nshape
-    is_masked = args.workload == "masked"
-    if is_masked:
+    is_masked = args.workload in ("masked", "masked_graph")
+    if graph_wl:
+        # dominant kernel: the GEMM with the longest launches
+        dom = int(np.argmax(gemm_ms))
+        achieved = W.gemm_bytes[dom] / (gemm_ms[dom] * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": achieved / HBM_PEAK_GBS, "traffic": None}
+    elif is_masked:
         mean_bytes = float(np.mean(W.gemm_bytes))
         achieved = mean_bytes / (mean_launch_ms * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -327,9 +460,14 @@ def main():
     roof["traffic"] = recorded_traffic(args.workload)
     roof["traffic_unit"] = "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)"
     roof["algorithmic_bytes_per_launch"] = float(np.mean(W.gemm_bytes))
-    roof["kernel"] = "fp8_gemm_kernel"
+    roof["kernel"] = "gemm_kernel (FP8 kind)"
     roof["avg_launch_us"] = mean_launch_ms * 1e3
     roof["per_launch"] = "mean over the workload's GEMM launches of one step (algorithmic work / HIP-event duration)"
+    if graph_wl:
+        roof["algorithmic_bytes_per_launch"] = float(W.gemm_bytes[dom])
+        roof["kernel"] = ["gemm_kernel (FP8 kind, UE8M0)", "gemm_kernel (BF16 kind)"][dom]
+        roof["avg_launch_us"] = gemm_ms[dom] * 1e3
+        roof["per_launch"] = "the longer of the two GEMM kernels (algorithmic bytes / HIP-event duration of eager launches)"
 
     per_shape = []
     for i in range(nshape):
@@ -338,7 +476,13 @@ def main():
                           "tflops": W.flops[i] / (gemm_ms[i] * 1e-3) / 1e12,
                           "gbs": W.gemm_bytes[i] / (gemm_ms[i] * 1e-3) / 1e9})
 
-    if is_masked:
+    if graph_wl:
+        metric = "masked grouped FP8 (UE8M0) + BF16 GEMM GB/s under graph replay (% HBM)"
+        unit = "GB/s"
+        value = W.step_bytes() / (ms_per_step * 1e-3) / 1e9
+        per_shape[0]["kernel"] = "fp8 masked, UE8M0 packed scales"
+        per_shape[1]["kernel"] = "bf16 masked"
+    elif is_masked:
         metric = "masked grouped FP8 GEMM GB/s (% HBM)"
         unit = "GB/s"
         step_bytes = float(sum(W.gemm_bytes))
@@ -358,7 +502,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp8_e4m3",
+        "dtype": "fp8_e4m3+bf16" if graph_wl else "fp8_e4m3",
         "data": "synthetic N(0,1) float32 inputs, seeded (numpy PCG64); no real activations or weights",
         "config": W.config(),
         "roofline": roof,

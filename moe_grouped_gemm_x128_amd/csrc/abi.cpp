@@ -245,7 +245,7 @@ int fp8_gemm_common(int mode, const dg_tensor* a, const dg_tensor* b, const dg_t
   DG_TRY(check_no_alias(d, "d", sfb, "sfb"));
   if (meta != nullptr) DG_TRY(check_no_alias(d, "d", meta, "metadata"));
 
-  dgmi::Fp8GemmParams p = {};
+  dgmi::GemmParams p = {};
   p.a = static_cast<const uint8_t*>(a->data);
   p.b = static_cast<const uint8_t*>(b->data);
   p.sfa = sfa->data;
@@ -266,7 +266,7 @@ int fp8_gemm_common(int mode, const dg_tensor* a, const dg_tensor* b, const dg_t
   p.d_gs = vd.sg;
   p.M = (int32_t)M;
   p.N = (int32_t)N;
-  p.K = (int32_t)K;
+  p.k_bytes = (int32_t)K;
   p.G = (int32_t)G;
   if (M == 0 || N == 0 || G == 0) return ok();
   if (K == 0) return fail(DG_UNSUPPORTED, "%s: K = 0 is not supported", fname);
@@ -394,20 +394,21 @@ int m_grouped_bf16_gemm_nt_masked(const dg_tensor* a, const dg_tensor* b, const 
   DG_TRY(check_no_alias(d, "d", a, "a"));
   DG_TRY(check_no_alias(d, "d", b, "b"));
   DG_TRY(check_no_alias(d, "d", masked_m, "masked_m"));
-  dgmi::Bf16GemmParams p = {};
-  p.a = static_cast<const uint16_t*>(a->data);
-  p.b = static_cast<const uint16_t*>(b->data);
+  // the kernel addresses A and B in bytes
+  dgmi::GemmParams p = {};
+  p.a = static_cast<const uint8_t*>(a->data);
+  p.b = static_cast<const uint8_t*>(b->data);
   p.d = static_cast<uint16_t*>(d->data);
-  p.masked_m = static_cast<const int32_t*>(masked_m->data);
-  p.lda = va.sr;
-  p.a_gs = va.sg;
-  p.ldb = vb.sr;
-  p.b_gs = vb.sg;
+  p.meta = static_cast<const int32_t*>(masked_m->data);
+  p.lda = 2 * va.sr;
+  p.a_gs = 2 * va.sg;
+  p.ldb = 2 * vb.sr;
+  p.b_gs = 2 * vb.sg;
   p.ldd = vd.sr;
   p.d_gs = vd.sg;
-  p.max_m = (int32_t)M;
+  p.M = (int32_t)M;
   p.N = (int32_t)N;
-  p.K = (int32_t)K;
+  p.k_bytes = (int32_t)(2 * K);
   p.G = (int32_t)G;
   if (G == 0 || M == 0 || N == 0) return ok();
   if (K == 0) return fail(DG_UNSUPPORTED, "%s: K = 0 is not supported", fname);

@@ -15,16 +15,20 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 // Scale-factor storage of the FP8 GEMMs.
 enum ScaleFmt : int { SF_F32 = 0, SF_UE8M0 = 1 };
 
-// Tile scheduling of the FP8 GEMM kernel.
+// Tile scheduling of the GEMM kernel.
 enum GemmMode : int { MODE_DENSE = 0, MODE_CONTIG = 1, MODE_MASKED = 2 };
 
-// Arguments of one FP8 GEMM launch.  Strides are in elements; "gs" is the
-// stride between groups (masked: per expert buffer; contiguous: per B).
-struct Fp8GemmParams {
+// Arguments of one GEMM launch (block-scaled FP8, or BF16 without scales).
+// The A and B operands are addressed in BYTES: lda, ldb and their group
+// strides are byte strides and k_bytes is the row length in bytes (K for
+// FP8, 2K for BF16).  Scale strides are in elements (32-bit words); d
+// strides in BF16 elements.  "gs" is the stride between groups (masked: per
+// expert buffer; contiguous: per B).
+struct GemmParams {
   const uint8_t* a;
   const uint8_t* b;
-  const void* sfa;
-  const void* sfb;
+  const void* sfa;  // FP8 only
+  const void* sfb;  // FP8 only
   uint16_t* d;
   const int32_t* meta;  // masked_m [G] or grouped_layout [M/128]; unused for dense
   int64_t lda, a_gs;
@@ -33,19 +37,7 @@ struct Fp8GemmParams {
   int64_t sfb_sn, sfb_sk, sfb_gs;
   int64_t ldd, d_gs;
   int32_t M;       // dense: M; contiguous: Msum; masked: max_m
-  int32_t N, K, G;
-  int32_t tiles_m, tiles_n;
-};
-
-struct Bf16GemmParams {
-  const uint16_t* a;
-  const uint16_t* b;
-  uint16_t* d;
-  const int32_t* masked_m;
-  int64_t lda, a_gs;
-  int64_t ldb, b_gs;
-  int64_t ldd, d_gs;
-  int32_t max_m, N, K, G;
+  int32_t N, k_bytes, G;
   int32_t tiles_m, tiles_n;
 };
 

@@ -27,6 +27,7 @@ def _dev_bf16(bits):
     (4, 128, 300, 256, [0, 5, 128, 77]),
     (3, 200, 128, 64, [200, 199, 1000]),
     (2, 16, 1000, 512, [-4, 16]),
+    (2, 256, 384, 320, [256, 130]),
 ])
 def test_bf16_masked_full_compare(G, max_m, N, K, mm):
     say(f"bf16 masked G={G} max_m={max_m} N={N} K={K} masked_m={mm}")

@@ -56,7 +56,8 @@ def sentinel_like(shape):
 # dense
 # ---------------------------------------------------------------------------
 
-@pytest.mark.parametrize("M,N,K", [(128, 256, 512), (200, 300, 384), (1, 130, 128), (257, 64, 256), (64, 2112, 1024)])
+@pytest.mark.parametrize("M,N,K", [(128, 256, 512), (200, 300, 384), (1, 130, 128), (257, 64, 256), (64, 2112, 1024),
+                                   (96, 100, 640), (128, 128, 384)])
 def test_dense_full_compare(M, N, K):
     say(f"fp8_gemm_nt M={M} N={N} K={K}")
     mg = _mg()
