@@ -38,10 +38,11 @@
 //     staging): each wave instruction fills 8 tile rows of 128 bytes; the
 //     16-byte chunk c of row r is stored at slot c ^ h(r), so the 16 rows of
 //     an MFMA fragment read at one chunk hit distinct banks.
-//   * One continuous software pipeline over fragment groups (below): one
-//     barrier per K-slice, placed before the slice's last fragment group;
-//     the loads of slice kb+S are issued right after it into the stage just
-//     freed, so S-1 slices are always in flight.
+//   * One continuous software pipeline over fragment groups (below): two
+//     barriers per K-slice.  After the first (second fragment group) the B
+//     tile of slice kb+S is loaded into the B part of the slice's stage;
+//     after the second (before the last group) its A tile, so S-1 slices of
+//     A and nearly S of B are always in flight.
 //   * The MFMA takes the B fragment as its first operand: the 16x16 result
 //     then holds, per lane, one output row (m = lane % 16) and four output
 //     columns.  The B fragment rows are permuted so that the four fragments
@@ -97,14 +98,14 @@ struct TileShape {
   static constexpr int A_LOADS = BM / (8 * NW);     // LDS-DMA instructions per wave per stage
   static constexpr int B_LOADS = BN / (8 * NW);
   static constexpr int LOADS = A_LOADS + B_LOADS;
-  static constexpr int A_BYTES = BM * BK, STAGE = (BM + BN) * BK;
+  static constexpr int A_BYTES = BM * BK, B_BYTES = BN * BK, STAGE = (BM + BN) * BK;
   static_assert(BM % (8 * NW) == 0 && BN % (8 * NW) == 0, "tile rows must split into 8-row wave loads");
   static_assert(FN == 4, "the epilogue packs four fragments into 16 consecutive columns");
   static_assert(TN == 64 && 128 % TN == 0, "a wave's columns must lie in one 128-column scale block");
   static constexpr int NBT = (BN + 127) / 128;      // 128-column scale blocks per tile
   static_assert(BM + NBT <= NT, "one thread per tile row stages the A scales, one per column block the B scale");
   static_assert(STAGES >= 2 && STAGES <= 3, "two or three LDS stages");
-  static_assert(FM >= 2, "the last fragment group of a K-slice is the one after the barrier");
+  static_assert(FM >= 3, "a K-slice has an early point (group 1) before its late point (last group)");
   template <int KIND>
   static constexpr int lds_bytes() { return STAGES * STAGE + (KIND == KIND_FP8 ? STAGES * NT * 4 : 0); }
 };
@@ -148,15 +149,20 @@ template <class T, int KIND, int SF, int MODE>
 __global__ __launch_bounds__(T::NT) void gemm_kernel(const GemmParams p) {
   constexpr int S = T::STAGES;
   constexpr bool FP8 = KIND == KIND_FP8;
-  // one array per stage, so that the compiler can tell the LDS-DMA target
-  // of one stage from the fragment reads of another (no false waits)
-  __shared__ __attribute__((aligned(16))) uint8_t smem0[T::STAGE];
-  __shared__ __attribute__((aligned(16))) uint8_t smem1[T::STAGE];
-  __shared__ __attribute__((aligned(16))) uint8_t smem2[S > 2 ? T::STAGE : 16];
+  // one array per stage and operand, so that the compiler can tell the
+  // LDS-DMA target of one from the fragment reads of another (it would
+  // otherwise drain every load in flight before those reads)
+  __shared__ __attribute__((aligned(16))) uint8_t lds_a0[T::A_BYTES];
+  __shared__ __attribute__((aligned(16))) uint8_t lds_a1[T::A_BYTES];
+  __shared__ __attribute__((aligned(16))) uint8_t lds_a2[S > 2 ? T::A_BYTES : 16];
+  __shared__ __attribute__((aligned(16))) uint8_t lds_b0[T::B_BYTES];
+  __shared__ __attribute__((aligned(16))) uint8_t lds_b1[T::B_BYTES];
+  __shared__ __attribute__((aligned(16))) uint8_t lds_b2[S > 2 ? T::B_BYTES : 16];
   // FP8: per stage, A row scales in slots [0, BM), B block scales in
   // [BM, BM + NBT); one slot per thread so the stores need no branch
   __shared__ __attribute__((aligned(16))) float ssc[FP8 ? S : 1][FP8 ? T::NT : 1];
-  auto stage_of = [&](int s) -> uint8_t* { return s == 0 ? smem0 : (s == 1 ? smem1 : smem2); };
+  auto stage_a = [&](int s) -> uint8_t* { return s == 0 ? lds_a0 : (s == 1 ? lds_a1 : lds_a2); };
+  auto stage_b = [&](int s) -> uint8_t* { return s == 0 ? lds_b0 : (s == 1 ? lds_b1 : lds_b2); };
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -238,20 +244,25 @@ __global__ __launch_bounds__(T::NT) void gemm_kernel(const GemmParams p) {
   const __amdgpu_buffer_rsrc_t b_rsrc = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(B + (int64_t)n0 * p.ldb), (short)0, b_rows * (int)p.ldb, 0x00020000);
 
-  auto issue_loads = [&](uint8_t* stage, int kb) {
-    const int koff = kb * BK;
+  auto issue_a = [&](uint8_t* stage, int kb) {
 #pragma unroll
     for (int j = 0; j < T::A_LOADS; ++j) {
       const uint32_t hu = (uint32_t)swz((j * T::NW + wave) * 8);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(a_rsrc, (lds_void*)(stage + (j * T::NW + wave) * 1024), 16,
-                                               a_vrow + j * a_jstep + ((vchunk ^ hu) << 4), koff, 0, 0);
+                                               a_vrow + j * a_jstep + ((vchunk ^ hu) << 4), kb * BK, 0, 0);
     }
+  };
+  auto issue_b = [&](uint8_t* stage, int kb) {
 #pragma unroll
     for (int j = 0; j < T::B_LOADS; ++j) {
       const uint32_t hu = (uint32_t)swz((j * T::NW + wave) * 8);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(b_rsrc, (lds_void*)(stage + T::A_BYTES + (j * T::NW + wave) * 1024), 16,
-                                               b_vrow + j * b_jstep + ((vchunk ^ hu) << 4), koff, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(b_rsrc, (lds_void*)(stage + (j * T::NW + wave) * 1024), 16,
+                                               b_vrow + j * b_jstep + ((vchunk ^ hu) << 4), kb * BK, 0, 0);
     }
+  };
+  auto issue_loads = [&](int st, int kb) {
+    issue_a(stage_a(st), kb);
+    issue_b(stage_b(st), kb);
   };
 
   // Scale staged by this thread (FP8): A row m0 + tid (tid < BM), B column
@@ -268,8 +279,18 @@ __global__ __launch_bounds__(T::NT) void gemm_kernel(const GemmParams p) {
     if constexpr (FP8) return load_scale_raw<SF>(sc_base, sc_row, kb, sc_srow, sc_sk);
     else return 0u;
   };
+  // The scale goes to LDS through an opaque ds_write: the compiler's own
+  // wait for it would otherwise also drain every LDS-DMA tile load in
+  // flight (it cannot tell this array from the stages).  The asm waits for
+  // nothing itself; its register input makes the compiler wait for the
+  // scale load, and the s_waitcnt lgkmcnt(0) before the next barrier
+  // completes the write.
   auto store_sc = [&](int slot, uint32_t raw, int kb) {
-    if constexpr (FP8) ssc[slot][tid] = scale_value<SF>(raw, kb);
+    if constexpr (FP8) {
+      const float v = scale_value<SF>(raw, kb);
+      const uint32_t off = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) float*)&ssc[slot][tid];
+      asm volatile("ds_write_b32 %0, %1" ::"v"(off), "v"(v) : "memory");
+    }
   };
 
   // fragment-read geometry: MFMA row j of B fragment f is tile column
@@ -281,13 +302,12 @@ __global__ __launch_bounds__(T::NT) void gemm_kernel(const GemmParams p) {
   const int fr = lane & 15;
   const int kc = (lane >> 4) * 2;  // first of the lane's two 16-B K chunks
   const int a_base = lds_off(wm * T::TM + fr, kc);                                  // fragment 0, chunk kc
-  const int b_base = T::A_BYTES + lds_off(wn * T::TN + (fr >> 2) * 16 + (fr & 3), kc);  // fragment 0, chunk kc
+  const int b_base = lds_off(wn * T::TN + (fr >> 2) * 16 + (fr & 3), kc);  // fragment 0, chunk kc
 
   // a wave whose rows all lie outside the rows to compute skips its MFMAs
   // (masked decode past masked_m; the unused half of a contiguous tile)
   const int wrow0 = wm * T::TM;
   const bool live = wrow0 < hi && wrow0 + T::TM > lo && m0 + wrow0 < row_lim;
-
   f32x4 acc[T::FM][T::FN];
 #pragma unroll
   for (int i = 0; i < T::FM; ++i)
@@ -300,33 +320,46 @@ __global__ __launch_bounds__(T::NT) void gemm_kernel(const GemmParams p) {
   // the fences keep the issue order that count assumes (the compiler would
   // otherwise hoist the scale loads above the tile loads and leave the last
   // slice-0 tile load in flight at the barrier).
-  issue_loads(smem0, 0);
+  issue_loads(0, 0);
   __builtin_amdgcn_sched_barrier(0);
   const uint32_t rs0 = load_sc(0);
   uint32_t rs = load_sc(min(1, KB - 1));  // scale of the next slice to stage
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int s = 1; s < S; ++s) {
-    issue_loads(stage_of(s), min(s, KB - 1));
+    issue_loads(s, min(s, KB - 1));
     __builtin_amdgcn_sched_barrier(0);
   }
   store_sc(0, rs0, 0);
   __builtin_amdgcn_s_waitcnt(vmcnt_lgkm0((FP8 ? 1 : 0) + (S - 1) * T::LOADS));
   __builtin_amdgcn_s_barrier();
 
+  // Early point of K-slice kb (start of its second fragment group): every
+  // wave has its B fragments of the slice in registers, so after a barrier
+  // the B part of stage kb % S is free and the B tile of slice kb+S is
+  // loaded into it, most of a slice before the A tile (B is the operand that
+  // streams from HBM in the grouped decode shapes; A is shared and cached).
+  auto early_point = [&](uint8_t* cur_b, int kb) {
+    __builtin_amdgcn_s_waitcnt(vmcnt_lgkm0(63));  // this wave's LDS reads are done
+    __builtin_amdgcn_s_barrier();
+    issue_b(cur_b, min(kb + S, KB - 1));
+    __builtin_amdgcn_sched_barrier(0);
+  };
   // Late point of K-slice kb (before its last fragment group): stage the
-  // scales of slice kb+1, wait for its tiles (issued S-1 slices ago: only
-  // the S-2 newer slices may stay in flight), barrier -- after it every wave
-  // is done with stage kb % S and slice kb+1 is visible -- then load slice
-  // kb+S into stage kb % S.  The scale load goes first (vmcnt counts in
-  // issue order).
-  auto late_point = [&](uint8_t* cur, int kb) {
-    store_sc((kb + 1) % S, rs, kb + 1);
-    __builtin_amdgcn_s_waitcnt(vmcnt_lgkm0((S - 2) * T::LOADS));
+  // scales of slice kb+1, wait for its tiles, barrier -- after it every wave
+  // is done with stage kb % S and slice kb+1 is visible -- then load the A
+  // tile of slice kb+S into stage kb % S.  The scale load goes first (vmcnt
+  // counts in issue order).  Loads issued after the tiles of slice kb+1 that
+  // may stay in flight: the B tile of slice kb+2 for two stages; the A tile
+  // of slice kb+2 and the B tile of slice kb+3 for three.
+  constexpr int LATE_VM = S == 2 ? T::B_LOADS : (S - 2) * T::LOADS;
+  auto late_point = [&](uint8_t* cur_a, int kb, int slot) {
+    store_sc(slot, rs, kb + 1);
+    __builtin_amdgcn_s_waitcnt(vmcnt_lgkm0(LATE_VM));
     __builtin_amdgcn_s_barrier();
     rs = load_sc(min(kb + 2, KB - 1));
     __builtin_amdgcn_sched_barrier(0);
-    issue_loads(cur, min(kb + S, KB - 1));
+    issue_a(cur_a, min(kb + S, KB - 1));
     __builtin_amdgcn_sched_barrier(0);
   };
 
@@ -346,29 +379,28 @@ __global__ __launch_bounds__(T::NT) void gemm_kernel(const GemmParams p) {
   const int sa_row0 = wm * T::TM + fr;             // this lane's scale slot for fragment row 0
   const int sb_slot = T::BM + (wn * T::TN) / 128;  // this wave's B block scale slot
 
-  if (live) {
-    // ---- K loop: one continuous software pipeline over fragment groups.
-    // Group (kb, i) issues the FN MFMAs of A fragment i of slice kb and (FP8)
-    // interleaved, the promote FMAs of the previous group (its partials are
-    // a whole group old, so no FMA waits on an MFMA in flight), while the
-    // LDS reads for the next group are in flight.  The barrier sits before
-    // the last group of each slice: by then every wave has read all it needs
-    // of the current stage (the last A fragment is already in registers), so
-    // the last group streams in the next slice's B fragments, first A
-    // fragment and scales, and the next slice starts with no bubble.
-    // Scheduling fences keep exactly this order (the compiler would otherwise
-    // pair each MFMA with its own FMAs and serialise on the MFMA latency).
+  // ---- K loop: one continuous software pipeline over fragment groups.
+  // Group (kb, i) issues the FN MFMAs of A fragment i of slice kb and (FP8)
+  // interleaved, the promote FMAs of the previous group (its partials are a
+  // whole group old, so no FMA waits on an MFMA in flight), while the LDS
+  // reads for the next group are in flight.  The barrier sits before the
+  // last group of each slice: by then every wave has read all it needs of
+  // the current stage (the last A fragment is already in registers), so the
+  // last group streams in the next slice's B fragments, first A fragment and
+  // scales, and the next slice starts with no bubble.  Scheduling fences
+  // keep exactly this order (the compiler would otherwise pair each MFMA
+  // with its own FMAs and serialise on the MFMA latency).
+  auto kloop = [&]() {
     i32x8 bf[T::FN];
-    i32x8 af;            // A fragment of the current group
+    i32x8 af;                  // A fragment of the current group
     float sa = 0.f, sb = 0.f;  // raw scales of the current group's rows / the current slice
-    f32x4 P[2][T::FN];   // partials of the current and the previous group
-    float s_prev = 0.f;  // combined scale of the previous group (the first promote adds 0 * 0)
+    f32x4 P[2][T::FN];         // partials of the current and the previous group
+    float s_prev = 0.f;        // combined scale of the previous group (the first promote adds 0 * 0)
 #pragma unroll
     for (int f = 0; f < T::FN; ++f) P[(T::FM - 1) & 1][f] = zero;
-
 #pragma unroll
-    for (int f = 0; f < T::FN; ++f) bf[f] = b_frag(smem0, f);
-    af = a_frag(smem0, 0);
+    for (int f = 0; f < T::FN; ++f) bf[f] = b_frag(lds_b0, f);
+    af = a_frag(lds_a0, 0);
     if constexpr (FP8) {
       sa = ssc[0][sa_row0];
       sb = ssc[0][sb_slot];
@@ -376,26 +408,32 @@ __global__ __launch_bounds__(T::NT) void gemm_kernel(const GemmParams p) {
 
     auto kblock = [&](auto st_tag, int kb) {
       constexpr int ST = decltype(st_tag)::value;
-      uint8_t* cur = ST == 0 ? smem0 : (ST == 1 ? smem1 : smem2);
-      uint8_t* nxt = (ST + 1) % S == 0 ? smem0 : ((ST + 1) % S == 1 ? smem1 : smem2);
+      constexpr int NX = (ST + 1) % S;
+      uint8_t* cur_a = ST == 0 ? lds_a0 : (ST == 1 ? lds_a1 : lds_a2);
+      uint8_t* cur_b = ST == 0 ? lds_b0 : (ST == 1 ? lds_b1 : lds_b2);
+      uint8_t* nxt_a = NX == 0 ? lds_a0 : (NX == 1 ? lds_a1 : lds_a2);
+      uint8_t* nxt_b = NX == 0 ? lds_b0 : (NX == 1 ? lds_b1 : lds_b2);
 #pragma unroll
       for (int i = 0; i < T::FM; ++i) {
         __builtin_amdgcn_sched_barrier(0);
+        if (i == 1) early_point(cur_b, kb);
         const float s_cur = sa * sb;
-        i32x8 af_next;
+        i32x8 af_next = af;
         float sa_next = sa, sb_next = sb;
         if (i + 1 < T::FM) {
           if constexpr (FP8) sa_next = ssc[ST][sa_row0 + (i + 1) * 16];
-          af_next = a_frag(cur, i + 1);
+          af_next = a_frag(cur_a, i + 1);
         } else {
-          late_point(cur, kb);
+          late_point(cur_a, kb, NX);
           if constexpr (FP8) {
-            sa_next = ssc[(ST + 1) % S][sa_row0];
-            sb_next = ssc[(ST + 1) % S][sb_slot];
+            sa_next = ssc[NX][sa_row0];
+            sb_next = ssc[NX][sb_slot];
           }
-          af_next = a_frag(nxt, 0);
+          af_next = a_frag(nxt_a, 0);
         }
         if constexpr (FP8) {
+          // the promote of the previous group: i-1 of this slice, or the
+          // last group of the previous slice
 #pragma unroll
           for (int f = 0; f < T::FN; ++f) {
             __builtin_amdgcn_sched_barrier(0);
@@ -403,7 +441,7 @@ __global__ __launch_bounds__(T::NT) void gemm_kernel(const GemmParams p) {
             __builtin_amdgcn_sched_barrier(0);
             if (i > 0) acc[i - 1][f] += P[(i - 1) & 1][f] * s_prev;
             else acc[T::FM - 1][f] += P[(T::FM - 1) & 1][f] * s_prev;
-            if (i + 1 == T::FM) bf[f] = b_frag(nxt, f);  // last use of bf[f] in this slice
+            if (i + 1 == T::FM) bf[f] = b_frag(nxt_b, f);  // last use of bf[f] in this slice
           }
         } else {
           // two K=32 halves per 128-byte slice; the four fragments between
@@ -417,7 +455,10 @@ __global__ __launch_bounds__(T::NT) void gemm_kernel(const GemmParams p) {
           for (int f = 0; f < T::FN; ++f) {
             __builtin_amdgcn_sched_barrier(0);
             acc[i][f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(hi_bf16(bf[f]), hi_bf16(af), acc[i][f], 0, 0, 0);
-            if (i + 1 == T::FM) bf[f] = b_frag(nxt, f);
+          }
+          if (i + 1 == T::FM) {
+#pragma unroll
+            for (int f = 0; f < T::FN; ++f) bf[f] = b_frag(nxt_b, f);
           }
         }
         s_prev = s_cur;
@@ -442,10 +483,17 @@ __global__ __launch_bounds__(T::NT) void gemm_kernel(const GemmParams p) {
 #pragma unroll
       for (int f = 0; f < T::FN; ++f) acc[T::FM - 1][f] += P[(T::FM - 1) & 1][f] * s_prev;
     }
+  };
+
+  if (live) {
+    kloop();
   } else {
     // this wave computes nothing: it still takes part in the scale staging,
     // loads and barriers of every K-slice, without MFMAs
-    for (int kb = 0; kb < KB; ++kb) late_point(stage_of(kb % S), kb);
+    for (int kb = 0; kb < KB; ++kb) {
+      early_point(stage_b(kb % S), kb);
+      late_point(stage_a(kb % S), kb, (kb + 1) % S);
+    }
   }
   __builtin_amdgcn_s_waitcnt(0);  // drain the redundant last loads before LDS is reused or freed
   if (!live) return;
@@ -483,8 +531,9 @@ __global__ __launch_bounds__(T::NT) void gemm_kernel(const GemmParams p) {
 using TileL = TileShape<256, 256, 2, 4, 2>;  // 512 threads, wave tile 128 x 64, 2 x 64 KB stages
 using TileW = TileShape<128, 256, 2, 4, 3>;  // 512 threads, wave tile  64 x 64, 3 x 48 KB stages
 using TileS = TileShape<128, 128, 2, 2, 3>;  // 256 threads, wave tile  64 x 64, 3 x 32 KB stages
+using TileT = TileShape<256, 128, 4, 2, 3>;  // 512 threads, wave tile  64 x 64, 3 x 48 KB stages
 
-enum Variant : int { VAR_L = 0, VAR_W = 1, VAR_S = 2 };
+enum Variant : int { VAR_L = 0, VAR_W = 1, VAR_S = 2, VAR_T = 3 };
 
 template <class T, int KIND>
 hipError_t launch_tile(const GemmParams& p, int mode, int sf_fmt, int64_t grid, hipStream_t stream) {
@@ -524,6 +573,7 @@ hipError_t launch_variant(const TileCfg& cfg, const GemmParams& p, int mode, int
   switch (cfg.variant) {
     case VAR_L: return launch_tile<TileL, KIND>(p, mode, sf_fmt, grid, stream);
     case VAR_W: return launch_tile<TileW, KIND>(p, mode, sf_fmt, grid, stream);
+    case VAR_T: return launch_tile<TileT, KIND>(p, mode, sf_fmt, grid, stream);
     default: return launch_tile<TileS, KIND>(p, mode, sf_fmt, grid, stream);
   }
 }
