@@ -304,12 +304,13 @@ class MaskedGraphWorkload:
 # ---------------------------------------------------------------------------
 
 def recorded_traffic(workload):
-    """Bytes per GEMM launch (FETCH + WRITE, calibrated against a 1 GiB copy)
-    from profiles/fp8_gemm_traffic.txt, or None when the record is missing or
-    was taken on a different version of the kernel source."""
+    """Bytes per launch of the dominant GEMM kernel (FETCH + WRITE, calibrated
+    against a 1 GiB copy) from profiles/gemm_traffic.txt, or None when the
+    record is missing or was taken on a different version of the kernel
+    source."""
     import hashlib
 
-    rec_path = os.path.join(ROOT, "profiles", "fp8_gemm_traffic.txt")
+    rec_path = os.path.join(ROOT, "profiles", "gemm_traffic.txt")
     src_path = os.path.join(ROOT, "moe_grouped_gemm_x128_amd", "csrc", "gemm.hip")
     if not os.path.exists(rec_path):
         return None
@@ -320,7 +321,7 @@ def recorded_traffic(workload):
         k, v = line.split(":", 1)
         rec[k.strip()] = v.strip()
     cur = hashlib.sha256(open(src_path, "rb").read()).hexdigest()[:16]
-    if rec.get("gemm_fp8_source_sha256_16") != cur:
+    if rec.get("gemm_source_sha256_16") != cur:
         return None
     try:
         return float(rec[f"{workload}_fetch_bytes_per_launch"]) + float(rec[f"{workload}_write_bytes_per_launch"])

@@ -227,10 +227,12 @@ __global__ __launch_bounds__(T::NT) void gemm_kernel(const GemmParams p) {
 
   // LDS-DMA sources.  Instruction j of this wave fills tile rows
   // [8(j*NW+wave), +8); lane l writes slot l%8 of row l/8 and so reads chunk
-  // (slot ^ h(row)).  The buffer resources start at the tile's first row and
-  // cover only the rows that exist (rows < min(row_lim, m0 + hi) for A, < N
-  // for B): the hardware range check on the per-lane offset returns zeros
-  // past them, so no clamping and no memory traffic for those rows.
+  // (slot ^ h(row)).  Instruction j uses its own buffer resource, starting
+  // j*8*NW rows into the tile and covering only the rows that exist (rows <
+  // min(row_lim, m0 + hi) for A, < N for B): the hardware range check on the
+  // per-lane offset returns zeros past them, so no clamping and no memory
+  // traffic for those rows, and the per-lane offset is the same for every j
+  // whose h term matches (one register per operand on 8-wave tiles).
   // Row (g8*8 + lrow) has h = lrow ^ h(g8*8) by linearity, so lane l reads
   // chunk (l%8) ^ (l/8) ^ h(g8*8), the last term uniform per instruction.
   const int lrow = lane >> 3, lslot = lane & 7;
@@ -238,26 +240,29 @@ __global__ __launch_bounds__(T::NT) void gemm_kernel(const GemmParams p) {
   const int b_rows = __builtin_amdgcn_readfirstlane(max(0, min(p.N - n0, T::BN)));
   const uint32_t a_vrow = (uint32_t)((wave * 8 + lrow) * p.lda), b_vrow = (uint32_t)((wave * 8 + lrow) * p.ldb);
   const uint32_t vchunk = (uint32_t)(lslot ^ lrow);
-  const uint32_t a_jstep = (uint32_t)(T::NW * 8 * p.lda), b_jstep = (uint32_t)(T::NW * 8 * p.ldb);
-  const __amdgpu_buffer_rsrc_t a_rsrc = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(A + (int64_t)m0 * p.lda), (short)0, a_rows * (int)p.lda, 0x00020000);
-  const __amdgpu_buffer_rsrc_t b_rsrc = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(B + (int64_t)n0 * p.ldb), (short)0, b_rows * (int)p.ldb, 0x00020000);
+  const int a_jstep = T::NW * 8 * (int)p.lda, b_jstep = T::NW * 8 * (int)p.ldb;
+  const uint8_t* const a_tile = A + (int64_t)m0 * p.lda;
+  const uint8_t* const b_tile = B + (int64_t)n0 * p.ldb;
+  const int a_bytes = a_rows * (int)p.lda, b_bytes = b_rows * (int)p.ldb;
 
   auto issue_a = [&](uint8_t* stage, int kb) {
 #pragma unroll
     for (int j = 0; j < T::A_LOADS; ++j) {
       const uint32_t hu = (uint32_t)swz((j * T::NW + wave) * 8);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(a_rsrc, (lds_void*)(stage + (j * T::NW + wave) * 1024), 16,
-                                               a_vrow + j * a_jstep + ((vchunk ^ hu) << 4), kb * BK, 0, 0);
+      const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+          (void*)(a_tile + (int64_t)j * a_jstep), (short)0, max(0, a_bytes - j * a_jstep), 0x00020000);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)(stage + (j * T::NW + wave) * 1024), 16,
+                                               a_vrow + ((vchunk ^ hu) << 4), kb * BK, 0, 0);
     }
   };
   auto issue_b = [&](uint8_t* stage, int kb) {
 #pragma unroll
     for (int j = 0; j < T::B_LOADS; ++j) {
       const uint32_t hu = (uint32_t)swz((j * T::NW + wave) * 8);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(b_rsrc, (lds_void*)(stage + (j * T::NW + wave) * 1024), 16,
-                                               b_vrow + j * b_jstep + ((vchunk ^ hu) << 4), kb * BK, 0, 0);
+      const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+          (void*)(b_tile + (int64_t)j * b_jstep), (short)0, max(0, b_bytes - j * b_jstep), 0x00020000);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)(stage + (j * T::NW + wave) * 1024), 16,
+                                               b_vrow + ((vchunk ^ hu) << 4), kb * BK, 0, 0);
     }
   };
   auto issue_loads = [&](int st, int kb) {
@@ -279,18 +284,8 @@ __global__ __launch_bounds__(T::NT) void gemm_kernel(const GemmParams p) {
     if constexpr (FP8) return load_scale_raw<SF>(sc_base, sc_row, kb, sc_srow, sc_sk);
     else return 0u;
   };
-  // The scale goes to LDS through an opaque ds_write: the compiler's own
-  // wait for it would otherwise also drain every LDS-DMA tile load in
-  // flight (it cannot tell this array from the stages).  The asm waits for
-  // nothing itself; its register input makes the compiler wait for the
-  // scale load, and the s_waitcnt lgkmcnt(0) before the next barrier
-  // completes the write.
   auto store_sc = [&](int slot, uint32_t raw, int kb) {
-    if constexpr (FP8) {
-      const float v = scale_value<SF>(raw, kb);
-      const uint32_t off = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) float*)&ssc[slot][tid];
-      asm volatile("ds_write_b32 %0, %1" ::"v"(off), "v"(v) : "memory");
-    }
+    if constexpr (FP8) ssc[slot][tid] = scale_value<SF>(raw, kb);
   };
 
   // fragment-read geometry: MFMA row j of B fragment f is tile column
@@ -390,10 +385,15 @@ __global__ __launch_bounds__(T::NT) void gemm_kernel(const GemmParams p) {
   // scales, and the next slice starts with no bubble.  Scheduling fences
   // keep exactly this order (the compiler would otherwise pair each MFMA
   // with its own FMAs and serialise on the MFMA latency).
+  // A fragments (and their row scales) are read PF fragment groups ahead
+  // of their MFMAs; the next slice's first PF are read right after the late
+  // barrier.
+  constexpr int PF = 1;
+  static_assert(PF == 1 || PF == 2, "prefetch depth");
   auto kloop = [&]() {
     i32x8 bf[T::FN];
-    i32x8 af;                  // A fragment of the current group
-    float sa = 0.f, sb = 0.f;  // raw scales of the current group's rows / the current slice
+    i32x8 af, af1;             // A fragments of the current and (PF = 2) the next group
+    float sa = 0.f, sa1 = 0.f, sb = 0.f;  // raw row scales of those groups / block scale of the slice
     f32x4 P[2][T::FN];         // partials of the current and the previous group
     float s_prev = 0.f;        // combined scale of the previous group (the first promote adds 0 * 0)
 #pragma unroll
@@ -401,8 +401,10 @@ __global__ __launch_bounds__(T::NT) void gemm_kernel(const GemmParams p) {
 #pragma unroll
     for (int f = 0; f < T::FN; ++f) bf[f] = b_frag(lds_b0, f);
     af = a_frag(lds_a0, 0);
+    af1 = PF == 2 ? a_frag(lds_a0, 1) : af;
     if constexpr (FP8) {
       sa = ssc[0][sa_row0];
+      sa1 = PF == 2 ? ssc[0][sa_row0 + 16] : sa;
       sb = ssc[0][sb_slot];
     }
 
@@ -418,18 +420,26 @@ __global__ __launch_bounds__(T::NT) void gemm_kernel(const GemmParams p) {
         __builtin_amdgcn_sched_barrier(0);
         if (i == 1) early_point(cur_b, kb);
         const float s_cur = sa * sb;
-        i32x8 af_next = af;
-        float sa_next = sa, sb_next = sb;
+        // the A fragment / row scale that become current after this group
+        // (n0) and, for PF = 2, the one after (n1)
+        i32x8 n0 = af1, n1 = af1;
+        float ns0 = sa1, ns1 = sa1, nsb = sb;
         if (i + 1 < T::FM) {
-          if constexpr (FP8) sa_next = ssc[ST][sa_row0 + (i + 1) * 16];
-          af_next = a_frag(cur_a, i + 1);
+          if (PF == 1) {
+            if constexpr (FP8) ns0 = ssc[ST][sa_row0 + (i + 1) * 16];
+            n0 = a_frag(cur_a, i + 1);
+          } else if (i + 2 < T::FM) {
+            if constexpr (FP8) ns1 = ssc[ST][sa_row0 + (i + 2) * 16];
+            n1 = a_frag(cur_a, i + 2);
+          }
         } else {
           late_point(cur_a, kb, NX);
           if constexpr (FP8) {
-            sa_next = ssc[NX][sa_row0];
-            sb_next = ssc[NX][sb_slot];
+            ns0 = ssc[NX][sa_row0];
+            if (PF == 2) ns1 = ssc[NX][sa_row0 + 16];
+            nsb = ssc[NX][sb_slot];
           }
-          af_next = a_frag(nxt_a, 0);
+          n0 = a_frag(nxt_a, 0);
         }
         if constexpr (FP8) {
           // the promote of the previous group: i-1 of this slice, or the
@@ -461,10 +471,21 @@ __global__ __launch_bounds__(T::NT) void gemm_kernel(const GemmParams p) {
             for (int f = 0; f < T::FN; ++f) bf[f] = b_frag(nxt_b, f);
           }
         }
+        if (PF == 2 && i + 1 == T::FM) {
+          __builtin_amdgcn_sched_barrier(0);
+          n1 = a_frag(nxt_a, 1);  // after the B fragments the next group 0 waits for
+        }
         s_prev = s_cur;
-        af = af_next;
-        sa = sa_next;
-        sb = sb_next;
+        if (PF == 1) {
+          af = n0;
+          sa = ns0;
+        } else {
+          af = i + 1 < T::FM ? af1 : n0;
+          sa = i + 1 < T::FM ? sa1 : ns0;
+          af1 = n1;
+          sa1 = ns1;
+        }
+        sb = nsb;
       }
     };
 

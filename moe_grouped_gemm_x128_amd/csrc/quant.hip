@@ -51,60 +51,98 @@ __device__ __forceinline__ float block_scale(float amax, int ue8m0) {
   return s;
 }
 
+// The correctly rounded binary32 quotient x / s, given r = RN(1 / s) (one
+// correctly rounded division per block): y = RN(x r) is within one ulp of
+// x / s, the residual x - y s is exact with an FMA, and RN(y + r (x - y s))
+// is the correctly rounded quotient (Markstein's correction step) whenever
+// it is a normal number.  Smaller quotients (below 2^-126) encode to E4M3
+// zero whichever way they round, so the FP8 bytes are those of x / s.  The
+// sign is copied from x (s > 0): the correction would turn -0 into +0.
+struct Recip {
+  float s, r;
+};
+__device__ __forceinline__ Recip recip_of(float s) { return Recip{s, __fdiv_rn(1.0f, s)}; }
+__device__ __forceinline__ float quot(float x, Recip d) {
+  const float y = x * d.r;
+  const float e = __builtin_fmaf(-y, d.s, x);
+  return __builtin_copysignf(__builtin_fmaf(e, d.r, y), x);
+}
+
 // Four values -> four E4M3 bytes (little-endian in one word), x / s rounded
 // to nearest even by the hardware conversion after clamping to +-448.
-__device__ __forceinline__ uint32_t encode4(const float v[4], float s) {
+__device__ __forceinline__ uint32_t encode4(const float v[4], Recip d) {
   float t[4];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) t[j] = fminf(fmaxf(__fdiv_rn(v[j], s), -448.0f), 448.0f);
+  for (int j = 0; j < 4; ++j) t[j] = fminf(fmaxf(quot(v[j], d), -448.0f), 448.0f);
   int w = __builtin_amdgcn_cvt_pk_fp8_f32(t[0], t[1], 0, false);
   w = __builtin_amdgcn_cvt_pk_fp8_f32(t[2], t[3], w, true);
   return (uint32_t)w;
 }
 
-__device__ __forceinline__ uint32_t encode1(float v, float s) {
-  float t = fminf(fmaxf(__fdiv_rn(v, s), -448.0f), 448.0f);
+__device__ __forceinline__ uint32_t encode1(float v, Recip d) {
+  float t = fminf(fmaxf(quot(v, d), -448.0f), 448.0f);
   return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(t, 0.0f, 0, false) & 0xffu;
 }
 
 // ---------------------------------------------------------------------------
-// per-token: one half-wave (32 lanes x 4 elements) per 1x128 block
+// per-token: one half-wave (32 lanes x 4 elements) per 1x128 block, four
+// consecutive blocks of a row per half-wave with all their loads issued
+// before the first reduction (four 16-byte loads in flight per lane)
 // ---------------------------------------------------------------------------
+constexpr int TOKEN_BLOCKS = 4;
+
 template <typename TIn>
 __global__ __launch_bounds__(256) void per_token_kernel(QuantArgs p) {
   const TIn* __restrict__ x = static_cast<const TIn*>(p.x);
   const int lane32 = threadIdx.x & 31;
-  const int64_t KB = (p.K + 127) / 128;
-  const int64_t total = (int64_t)p.G * p.R * KB;
-  const int64_t blk = (int64_t)blockIdx.x * 8 + (threadIdx.x >> 5);
-  if (blk >= total) return;  // whole half-waves only; the shuffles below stay within a half
-  const int kb = (int)(blk % KB);
-  const int64_t rr = blk / KB;
+  const int KB = (p.K + 127) / 128;
+  const int KQ = (KB + TOKEN_BLOCKS - 1) / TOKEN_BLOCKS;  // block groups per row
+  const int64_t total = (int64_t)p.G * p.R * KQ;
+  const int64_t grp = (int64_t)blockIdx.x * 8 + (threadIdx.x >> 5);
+  if (grp >= total) return;  // whole half-waves only; the shuffles below stay within a half
+  const int kq = (int)(grp % KQ);
+  const int64_t rr = grp / KQ;
   const int r = (int)(rr % p.R);
   const int g = (int)(rr / p.R);
   const TIn* xr = x + g * p.sx_g + r * p.sx_r;
-  const int k0 = kb * 128 + lane32 * 4;
-
-  float v[4];
-  if (k0 + 3 < p.K) {
-    load4(xr + k0, v);
-  } else {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) v[j] = (k0 + j < p.K) ? load_elem(xr + k0 + j) : 0.0f;
-  }
-  float amax = fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3])));
-#pragma unroll
-  for (int off = 16; off > 0; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 32));
-  const float s = block_scale(amax, p.ue8m0);
-
   uint8_t* qr = p.q + g * p.sq_g + r * p.sq_r;
-  if (k0 + 3 < p.K) {
-    *reinterpret_cast<uint32_t*>(qr + k0) = encode4(v, s);
-  } else {
-    for (int j = 0; j < 4; ++j)
-      if (k0 + j < p.K) qr[k0 + j] = (uint8_t)encode1(v[j], s);
+  const int kb0 = kq * TOKEN_BLOCKS;
+
+  float v[TOKEN_BLOCKS][4];
+#pragma unroll
+  for (int b = 0; b < TOKEN_BLOCKS; ++b) {
+    const int k0 = (kb0 + b) * 128 + lane32 * 4;
+    if (k0 + 3 < p.K) {
+      load4(xr + k0, v[b]);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) v[b][j] = (k0 + j < p.K) ? load_elem(xr + k0 + j) : 0.0f;
+    }
   }
-  if (lane32 == 0) p.sf[g * p.ssf_g + r * p.ssf_r + kb * p.ssf_k] = s;
+  float amax[TOKEN_BLOCKS];
+#pragma unroll
+  for (int b = 0; b < TOKEN_BLOCKS; ++b)
+    amax[b] = fmaxf(fmaxf(fabsf(v[b][0]), fabsf(v[b][1])), fmaxf(fabsf(v[b][2]), fabsf(v[b][3])));
+#pragma unroll
+  for (int off = 16; off > 0; off >>= 1)
+#pragma unroll
+    for (int b = 0; b < TOKEN_BLOCKS; ++b) amax[b] = fmaxf(amax[b], __shfl_xor(amax[b], off, 32));
+
+#pragma unroll
+  for (int b = 0; b < TOKEN_BLOCKS; ++b) {
+    const int kb = kb0 + b;
+    if (kb >= KB) break;
+    const float s = block_scale(amax[b], p.ue8m0);
+    const Recip d = recip_of(s);
+    const int k0 = kb * 128 + lane32 * 4;
+    if (k0 + 3 < p.K) {
+      *reinterpret_cast<uint32_t*>(qr + k0) = encode4(v[b], d);
+    } else {
+      for (int j = 0; j < 4; ++j)
+        if (k0 + j < p.K) qr[k0 + j] = (uint8_t)encode1(v[b][j], d);
+    }
+    if (lane32 == 0) p.sf[g * p.ssf_g + r * p.ssf_r + kb * p.ssf_k] = s;
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -147,6 +185,7 @@ __global__ __launch_bounds__(256) void per_block_kernel(QuantArgs p) {
   __syncthreads();
   amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
   const float s = block_scale(amax, p.ue8m0);
+  const Recip d = recip_of(s);
 
   uint8_t* qg = p.q + g * p.sq_g;
 #pragma unroll
@@ -155,10 +194,10 @@ __global__ __launch_bounds__(256) void per_block_kernel(QuantArgs p) {
     if (r >= p.R) continue;
     uint8_t* qr = qg + (int64_t)r * p.sq_r;
     if (full_cols) {
-      *reinterpret_cast<uint32_t*>(qr + c0) = encode4(v[j], s);
+      *reinterpret_cast<uint32_t*>(qr + c0) = encode4(v[j], d);
     } else {
       for (int e = 0; e < 4; ++e)
-        if (c0 + e < p.K) qr[c0 + e] = (uint8_t)encode1(v[j][e], s);
+        if (c0 + e < p.K) qr[c0 + e] = (uint8_t)encode1(v[j][e], d);
     }
   }
   if (tid == 0) p.sf[g * p.ssf_g + nb * p.ssf_r + kb * p.ssf_k] = s;
@@ -200,7 +239,8 @@ __global__ __launch_bounds__(256) void pack_ue8m0_kernel(PackArgs p) {
 
 hipError_t launch_per_token(const QuantArgs& p, hipStream_t stream) {
   const int64_t KB = (p.K + 127) / 128;
-  const int64_t blocks = ((int64_t)p.G * p.R * KB + 7) / 8;
+  const int64_t KQ = (KB + TOKEN_BLOCKS - 1) / TOKEN_BLOCKS;
+  const int64_t blocks = ((int64_t)p.G * p.R * KQ + 7) / 8;
   if (blocks == 0) return hipSuccess;
   if (p.x_bf16)
     per_token_kernel<uint16_t><<<dim3((unsigned)blocks), dim3(256), 0, stream>>>(p);
