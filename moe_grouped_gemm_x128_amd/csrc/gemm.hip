@@ -9,8 +9,11 @@
 // Each 128-wide K-block is exactly one v_mfma_f32_16x16x128_f8f6f4 per
 // 16x16 output fragment, computed into a fresh FP32 partial; the partial is
 // then promoted into the FP32 accumulator with one FMA per element using the
-// product of the row scale and the 128x128 block scale.  Output is BF16
-// (round to nearest even).
+// product of the row scale and the 128x128 block scale.  With power-of-two
+// UE8M0 scales the promote is the MFMA's own: v_mfma_scale_f32_16x16x128_
+// f8f6f4 multiplies by 2^(e-127) per A row and per B row and accumulates in
+// place (the SM100 recipe of "DeepInside DeepGEMM", section 2, on CDNA4).
+// Output is BF16 (round to nearest even).
 //
 // The BF16 kind ("DeepGEMM CUDA Graph Compatibility for Masked Grouped
 // GEMMs", the masked BF16 call of its capture example) computes
@@ -441,7 +444,18 @@ __global__ __launch_bounds__(T::NT) void gemm_kernel(const GemmParams p) {
           }
           n0 = a_frag(nxt_a, 0);
         }
-        if constexpr (FP8) {
+        if constexpr (FP8 && SF == SF_UE8M0) {
+          // power-of-two scales go into the MFMA itself: its scale operands
+          // multiply by 2^(e-127) per A row (the lane's row) and per B row
+          // (one 128-column block per wave), and it accumulates in place
+          const int ea = (int)(__float_as_uint(sa) >> 23), eb = (int)(__float_as_uint(sb) >> 23);
+#pragma unroll
+          for (int f = 0; f < T::FN; ++f) {
+            __builtin_amdgcn_sched_barrier(0);
+            acc[i][f] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf[f], af, acc[i][f], 0, 0, 0, eb, 0, ea);
+            if (i + 1 == T::FM) bf[f] = b_frag(nxt_b, f);  // last use of bf[f] in this slice
+          }
+        } else if constexpr (FP8) {
           // the promote of the previous group: i-1 of this slice, or the
           // last group of the previous slice
 #pragma unroll
@@ -499,7 +513,7 @@ __global__ __launch_bounds__(T::NT) void gemm_kernel(const GemmParams p) {
     if constexpr (S > 2) {
       if (kb + 1 < KB) kblock(std::integral_constant<int, 1>{}, kb + 1);
     }
-    if constexpr (FP8) {
+    if constexpr (FP8 && SF == SF_F32) {
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int f = 0; f < T::FN; ++f) acc[T::FM - 1][f] += P[(T::FM - 1) & 1][f] * s_prev;
