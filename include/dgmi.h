@@ -51,7 +51,7 @@ enum {
 enum {
   DG_OK = 0,
   DG_INVALID_ARG = 1,   /* null / dtype / ndim / shape / stride / alignment / aliasing */
-  DG_UNSUPPORTED = 2,   /* legal but not implemented (K % 128 != 0, c != NULL) */
+  DG_UNSUPPORTED = 2,   /* legal but not implemented (K % 128 != 0) */
   DG_LAUNCH_FAILED = 3  /* the HIP runtime rejected a launch */
 };
 
@@ -79,9 +79,13 @@ int dgmi_init(void);
  *       I32  [M, ceil(K/512)] packed UE8M0 (byte j of word i: K-block 4i+j)
  *   sfb F32  [ceil(N/128), K/128] or I32 [ceil(N/128), ceil(K/512)]
  *       sfa and sfb must use the same format.
- *   c   must be NULL (accumulate form not built: DG_UNSUPPORTED otherwise)
+ *   c   NULL, or the accumulate input C: BF16 or F32 [M, N], any row stride
+ *       (innermost stride 1), element-aligned; it may be d itself (same base,
+ *       dtype and strides: an in-place D += A . B^T), any other overlap with d
+ *       is rejected.  Each element of C is added to the FP32 accumulator
+ *       before the BF16 rounding (same section: D = C + A @ B.T).
  *   d   BF16 [M, N], any row stride (innermost stride 1)
- * D[m,n] = sum_kb (sum_{k in kb} A[m,k] B[n,k]) * sfa[m,kb] * sfb[n/128,kb].
+ * D[m,n] = C[m,n] + sum_kb (sum_{k in kb} A[m,k] B[n,k]) * sfa[m,kb] * sfb[n/128,kb].
  * K must be a multiple of 128; M and N are arbitrary.
  */
 int fp8_gemm_nt(const dg_tensor* a, const dg_tensor* b, const dg_tensor* sfa,

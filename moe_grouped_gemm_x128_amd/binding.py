@@ -151,7 +151,7 @@ def dgmi_init():
 
 
 def fp8_gemm_nt(a, b, sfa, sfb, c, d, stream=None):
-    """d = a . b^T with block scales (c must be None)."""
+    """d = c + a . b^T with block scales; c is None or a BF16/F32 [M, N] tensor (may be d)."""
     lib = load_library()
     _check(lib.fp8_gemm_nt(_ref(describe(a)), _ref(describe(b)), _ref(describe(sfa)), _ref(describe(sfb)),
                            _ref(describe(c)), _ref(describe(d)), _stream(stream)))

@@ -180,7 +180,6 @@ int fp8_gemm_common(int mode, const dg_tensor* a, const dg_tensor* b, const dg_t
   DG_TRY(check_dtype(a, "a", DG_E4M3));
   DG_TRY(check_dtype(b, "b", DG_E4M3));
   DG_TRY(check_dtype(d, "d", DG_BF16));
-  if (c != nullptr) return fail(DG_UNSUPPORTED, "%s: the accumulate input c is not supported (pass NULL)", fname);
   if (sfa == nullptr || sfb == nullptr) return fail(DG_INVALID_ARG, "%s: scale descriptors must not be NULL", fname);
   if (sfa->dtype != sfb->dtype) return fail(DG_INVALID_ARG, "%s: sfa and sfb must have the same dtype", fname);
   const int sf_fmt = sfa->dtype == DG_I32 ? dgmi::SF_UE8M0 : dgmi::SF_F32;
@@ -244,6 +243,22 @@ int fp8_gemm_common(int mode, const dg_tensor* a, const dg_tensor* b, const dg_t
   DG_TRY(check_no_alias(d, "d", sfa, "sfa"));
   DG_TRY(check_no_alias(d, "d", sfb, "sfb"));
   if (meta != nullptr) DG_TRY(check_no_alias(d, "d", meta, "metadata"));
+  // accumulate input (dense form only): D = C + A . B^T, C BF16 or F32 [M, N];
+  // c may be d itself (same base and strides), any other overlap is rejected
+  bool c_f32 = false;
+  int64_t ldc = 0;
+  if (c != nullptr) {
+    if (mode != dgmi::MODE_DENSE) return fail(DG_INVALID_ARG, "%s: c is only taken by the dense GEMM", fname);
+    DG_TRY(check_basic(c, "c", true));
+    if (c->dtype != DG_BF16 && c->dtype != DG_F32) return fail(DG_INVALID_ARG, "%s: c must be BF16 or F32", fname);
+    if (c->ndim != 2 || c->shape[0] != M || c->shape[1] != N)
+      return fail(DG_INVALID_ARG, "%s: c must be [M, N] = [%lld, %lld]", fname, (long long)M, (long long)N);
+    c_f32 = c->dtype == DG_F32;
+    if (!aligned(c->data, c_f32 ? 4 : 2)) return fail(DG_INVALID_ARG, "%s: c must be element-aligned", fname);
+    ldc = c->stride[0];
+    const bool same_as_d = c->data == d->data && c->dtype == d->dtype && ldc == d->stride[0];
+    if (!same_as_d) DG_TRY(check_no_alias(d, "d", c, "c"));
+  }
 
   dgmi::GemmParams p = {};
   p.a = static_cast<const uint8_t*>(a->data);
@@ -251,6 +266,9 @@ int fp8_gemm_common(int mode, const dg_tensor* a, const dg_tensor* b, const dg_t
   p.sfa = sfa->data;
   p.sfb = sfb->data;
   p.d = static_cast<uint16_t*>(d->data);
+  p.c = c != nullptr ? c->data : nullptr;
+  p.ldc = ldc;
+  p.c_f32 = c_f32 ? 1 : 0;
   p.meta = meta ? static_cast<const int32_t*>(meta->data) : nullptr;
   p.lda = va.sr;
   p.a_gs = va.sg;

@@ -30,6 +30,9 @@ struct GemmParams {
   const void* sfa;  // FP8 only
   const void* sfb;  // FP8 only
   uint16_t* d;
+  const void* c;        // dense only: optional accumulate input C [M, N] (BF16 or F32), may be d
+  int64_t ldc;          // row stride of c in elements
+  int32_t c_f32;        // c holds F32 (else BF16)
   const int32_t* meta;  // masked_m [G] or grouped_layout [M/128]; unused for dense
   int64_t lda, a_gs;
   int64_t ldb, b_gs;

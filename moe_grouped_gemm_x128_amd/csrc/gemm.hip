@@ -541,6 +541,45 @@ __global__ __launch_bounds__(T::NT) void gemm_kernel(const GemmParams p) {
     const int rl = wm * T::TM + i * 16 + fr;
     const int row = m0 + rl;
     if (rl < lo || rl >= hi || row >= row_lim) continue;
+    if (MODE == MODE_DENSE && p.c != nullptr) {
+      // D = C + A . B^T ("DeepInside DeepGEMM", section 4): C is added to the
+      // FP32 accumulator before the BF16 rounding (read before d is written,
+      // so c may be d itself)
+      const int cc = col0;
+      if (p.c_f32) {
+        const float* crow = static_cast<const float*>(p.c) + (int64_t)row * p.ldc;
+        const bool cvec = ((p.ldc & 3) == 0) && ((reinterpret_cast<uintptr_t>(p.c) & 15) == 0) && cc + 16 <= p.N;
+#pragma unroll
+        for (int f = 0; f < T::FN; ++f) {
+          if (cvec) {
+            const f32x4 cv = *reinterpret_cast<const f32x4*>(crow + cc + 4 * f);
+            acc[i][f] += cv;
+          } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              if (cc + 4 * f + e < p.N) acc[i][f][e] += crow[cc + 4 * f + e];
+          }
+        }
+      } else {
+        const uint16_t* crow = static_cast<const uint16_t*>(p.c) + (int64_t)row * p.ldc;
+        const bool cvec = ((p.ldc & 7) == 0) && ((reinterpret_cast<uintptr_t>(p.c) & 15) == 0) && cc + 16 <= p.N;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          if (cvec) {
+            const i32x4 cv = *reinterpret_cast<const i32x4*>(crow + cc + 8 * h);
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+              acc[i][2 * h + w / 2][2 * (w & 1)] += __uint_as_float((uint32_t)cv[w] << 16);
+              acc[i][2 * h + w / 2][2 * (w & 1) + 1] += __uint_as_float((uint32_t)cv[w] & 0xffff0000u);
+            }
+          } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+              if (cc + 8 * h + e < p.N) acc[i][2 * h + e / 4][e & 3] += bf16_to_f32(crow[cc + 8 * h + e]);
+          }
+        }
+      }
+    }
     uint32_t packed[8];
 #pragma unroll
     for (int f = 0; f < T::FN; ++f) {

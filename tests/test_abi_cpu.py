@@ -88,8 +88,11 @@ def test_dense_validation_errors(lib):
     # K not a multiple of 128 -> unsupported
     a2, b2 = _t((M, 200), torch.uint8), _t((N, 200), torch.uint8)
     assert _call_dense(lib, a2, b2, _t((M, 2), torch.float32), _t((2, 2), torch.float32), d) == binding.DG_UNSUPPORTED
-    # accumulate input not built
-    assert _call_dense(lib, a, b, sfa, sfb, d, c=_t((M, N), torch.bfloat16)) == binding.DG_UNSUPPORTED
+    # accumulate input: wrong shape, wrong dtype, partial overlap with d
+    assert _call_dense(lib, a, b, sfa, sfb, d, c=_t((M, N + 1), torch.bfloat16)) == binding.DG_INVALID_ARG
+    assert _call_dense(lib, a, b, sfa, sfb, d, c=_t((M, N), torch.int32)) == binding.DG_INVALID_ARG
+    big = _t((M + 1, N), torch.bfloat16)
+    assert _call_dense(lib, a, b, sfa, sfb, big[1:], c=big[:-1]) == binding.DG_INVALID_ARG
     # output aliasing an input
     alias = torch.empty(M * K, dtype=torch.uint8)
     a3 = alias.view(M, K)

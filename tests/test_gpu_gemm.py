@@ -161,6 +161,41 @@ def test_dense_v3_shapes_sampled(i):
         assert_bf16_close(dh[rows][:, cols], ref, f"dense {M}x{N}x{K} col block {nb}")
 
 
+@pytest.mark.parametrize("M,N,K", [(200, 300, 384), (64, 2112, 1024), (130, 130, 256)])
+@pytest.mark.parametrize("c_kind", ["bf16", "f32", "inplace"])
+def test_dense_accumulate_c(M, N, K, c_kind):
+    """D = C + A . B^T ("DeepInside DeepGEMM", section 4): C in BF16 or FP32,
+    with a padded row stride, or C being d itself."""
+    say(f"fp8_gemm_nt accumulate M={M} N={N} K={K} c={c_kind}")
+    mg = _mg()
+    xa = synth.normal_f32(171, (M, K))
+    xb = synth.normal_f32(172, (N, K))
+    xc = synth.normal_f32(173, (M, N)) * np.float32(8.0)
+    a, sfa = q_tok(to_dev(xa))
+    b, sfb = q_blk(to_dev(xb))
+    if c_kind == "f32":
+        cbuf = torch.zeros((M, N + 4), dtype=torch.float32, device="cuda")
+        cbuf[:, :N] = to_dev(xc)
+        c = cbuf[:, :N]
+        cref = xc.astype(np.float64)
+        d = sentinel_like((M, N))
+    else:
+        cbits = synth.bf16_bits_from_f32(xc)
+        cref = oracle.bf16_decode(cbits)
+        cbuf = torch.zeros((M, N + 8), dtype=torch.int16, device="cuda")
+        cbuf[:, :N] = to_dev(cbits.view(np.int16))
+        c = cbuf[:, :N].view(torch.bfloat16)
+        d = c if c_kind == "inplace" else sentinel_like((M, N))
+    mg.fp8_gemm_nt(a, b, sfa, sfb, c, d)
+    torch.cuda.synchronize()
+    ra, rsfa = oracle.per_token_cast_to_fp8(xa)
+    rb, rsfb = oracle.per_block_cast_to_fp8(xb)
+    ref = oracle.fp8_gemm_nt(ra, rb, rsfa, rsfb, c=cref)
+    assert_bf16_close(to_host(d), ref, f"accumulate {c_kind} {M}x{N}x{K}")
+    if c_kind == "inplace":
+        assert np.all(to_host(cbuf)[:, N:] == 0), "the row padding of c/d was written"
+
+
 # ---------------------------------------------------------------------------
 # contiguous grouped
 # ---------------------------------------------------------------------------
