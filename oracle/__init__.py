@@ -12,7 +12,8 @@ Modules
   quant    -- per-token (1x128) and per-block (128x128) FP8 quantizers and
               the UE8M0 packing of four scales into one int32.
   gemm     -- dense, contiguous-grouped and masked-grouped FP8 GEMMs with
-              fine-grained scales, and the masked BF16 GEMM.
+              fine-grained scales, and the dense, contiguous-grouped and
+              masked-grouped BF16 GEMMs.
 
 Sources (the pages this follows):
   * "DeepInside DeepGEMM: Unpacking DeepSeek's Unified Tensor Core Library
@@ -43,7 +44,9 @@ from .formats import (
 )
 from .quant import per_token_cast_to_fp8, per_block_cast_to_fp8, pack_ue8m0_to_int, AMAX_FLOOR
 from .gemm import (
+    bf16_gemm_nt,
     fp8_gemm_nt,
+    m_grouped_bf16_gemm_nt_contiguous,
     m_grouped_fp8_gemm_nt_contiguous,
     m_grouped_fp8_gemm_nt_masked,
     m_grouped_bf16_gemm_nt_masked,
@@ -60,6 +63,8 @@ __all__ = [
     "per_token_cast_to_fp8",
     "per_block_cast_to_fp8",
     "pack_ue8m0_to_int",
+    "bf16_gemm_nt",
+    "m_grouped_bf16_gemm_nt_contiguous",
     "fp8_gemm_nt",
     "m_grouped_fp8_gemm_nt_contiguous",
     "m_grouped_fp8_gemm_nt_masked",

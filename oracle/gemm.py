@@ -132,6 +132,42 @@ def m_grouped_bf16_gemm_nt_masked(a_bits, b_bits, masked_m, max_m):
     return D, written
 
 
+def bf16_gemm_nt(a_bits, b_bits, c=None):
+    """Dense BF16 GEMM D = C + A . B^T ("DeepGEMM: Why DeepSeek Built Its Own
+    BLAS Kernels", its table of primitives: the BF16 GEMM next to FP8; NT
+    layout and accumulate form as for fp8_gemm_nt).
+
+    a_bits uint16 [M, K], b_bits uint16 [N, K] (bfloat16 patterns), optional
+    c [M, N] (float64).  Returns float64 [M, N].
+    """
+    D = bf16_decode(a_bits) @ bf16_decode(b_bits).T
+    if c is not None:
+        D = D + np.asarray(c, dtype=np.float64)
+    return D
+
+
+def m_grouped_bf16_gemm_nt_contiguous(a_bits, b_bits, grouped_layout):
+    """Contiguous grouped BF16 GEMM: row m uses B[g] with g =
+    grouped_layout[m // 128]; a block with g < 0 is skipped (same layout as
+    m_grouped_fp8_gemm_nt_contiguous, without scales).
+
+    a_bits uint16 [Msum, K], b_bits uint16 [G, N, K].
+    Returns (D float64 [Msum, N], written bool [Msum]).
+    """
+    layout = np.asarray(grouped_layout, dtype=np.int64)
+    Msum = a_bits.shape[0]
+    N = b_bits.shape[1]
+    D = np.zeros((Msum, N), dtype=np.float64)
+    written = np.zeros(Msum, dtype=bool)
+    for blk, g in enumerate(layout):
+        if g < 0:
+            continue
+        rows = slice(blk * 128, min((blk + 1) * 128, Msum))
+        D[rows] = bf16_decode(a_bits[rows]) @ bf16_decode(b_bits[g]).T
+        written[rows] = True
+    return D, written
+
+
 def scales_from_packed_ue8m0(packed, n):
     """Unpack int32 words of four UE8M0 bytes back to float64 scales [..., n]
     (byte j of word i is the exponent of element 4i + j)."""

@@ -201,6 +201,55 @@ def test_bf16_masked_is_matmul():
         assert np.allclose(D[g], want, rtol=0, atol=1e-12)
 
 
+def test_bf16_dense_brute_force_and_accumulate():
+    M, N, K = 5, 7, 33
+    ab = synth.bf16_bits_from_f32(synth.normal_f32(55, (M, K)))
+    bb = synth.bf16_bits_from_f32(synth.normal_f32(56, (N, K)))
+    c = synth.normal_f32(57, (M, N)).astype(np.float64)
+    A, B = _torch_bf16(ab), _torch_bf16(bb)
+    D = oracle.bf16_gemm_nt(ab, bb)
+    Dc = oracle.bf16_gemm_nt(ab, bb, c=c)
+    for m in range(M):
+        for n in range(N):
+            want = sum(A[m, k] * B[n, k] for k in range(K))
+            assert abs(D[m, n] - want) <= 1e-12 * (1 + abs(want))
+            assert abs(Dc[m, n] - (want + c[m, n])) <= 1e-12 * (1 + abs(want) + abs(c[m, n]))
+
+
+def test_bf16_dense_exact_on_small_integers():
+    # integers below 2^8 are exact in bfloat16; their products sum exactly
+    rng = np.random.default_rng(58)
+    A = rng.integers(-20, 21, size=(6, 64)).astype(np.float32)
+    B = rng.integers(-20, 21, size=(9, 64)).astype(np.float32)
+    D = oracle.bf16_gemm_nt(synth.bf16_bits_from_f32(A), synth.bf16_bits_from_f32(B))
+    want = A.astype(np.int64) @ B.astype(np.int64).T
+    assert np.array_equal(D, want.astype(np.float64))
+
+
+def test_bf16_contiguous_blocks_skips_and_permutation():
+    G, N, K = 3, 20, 48
+    layout = np.array([1, -1, 0, 2, 1], dtype=np.int32)
+    Msum = layout.size * 128
+    ab = synth.bf16_bits_from_f32(synth.normal_f32(59, (Msum, K)))
+    bb = synth.bf16_bits_from_f32(synth.normal_f32(60, (G, N, K)))
+    D, written = oracle.m_grouped_bf16_gemm_nt_contiguous(ab, bb, layout)
+    assert np.array_equal(written, np.repeat(layout >= 0, 128))
+    for blk, g in enumerate(layout):
+        rows = slice(blk * 128, (blk + 1) * 128)
+        if g < 0:
+            assert np.all(D[rows] == 0)
+        else:
+            want = _torch_bf16(ab[rows]) @ _torch_bf16(bb[g]).T
+            assert np.allclose(D[rows], want, rtol=0, atol=1e-12)
+    # relabelling the groups together with B leaves D unchanged
+    perm = np.array([2, 0, 1])
+    b2 = np.empty_like(bb)
+    b2[perm] = bb
+    layout2 = np.where(layout >= 0, perm[np.maximum(layout, 0)], -1).astype(np.int32)
+    D2, _ = oracle.m_grouped_bf16_gemm_nt_contiguous(ab, b2, layout2)
+    assert np.array_equal(D, D2)
+
+
 def test_synth_chunked_draw_matches_whole():
     whole = synth.normal_f32(9, (3, 5, 7))
     parts = np.stack(list(synth.normal_f32_chunks(9, (3, 5, 7))))
