@@ -138,6 +138,28 @@ int m_grouped_bf16_gemm_nt_masked(const dg_tensor* a, const dg_tensor* b,
                                   int64_t max_m_per_group, hipStream_t stream);
 
 /*
+ * Dense BF16 GEMM D = C + A . B^T: the BF16 GEMM primitive ("DeepGEMM: Why
+ * DeepSeek Built Its Own BLAS Kernels", its table of primitives) in the NT
+ * layout and accumulate form of fp8_gemm_nt, FP32 accumulation, BF16 out.
+ *   a BF16 [M, K], b BF16 [N, K] (row strides multiples of 8 elements,
+ *   16-B aligned bases); c NULL or BF16/F32 [M, N] as for fp8_gemm_nt (may be
+ *   d itself); d BF16 [M, N], any row stride.  K must be a multiple of 64.
+ */
+int bf16_gemm_nt(const dg_tensor* a, const dg_tensor* b, const dg_tensor* c, const dg_tensor* d,
+                 hipStream_t stream);
+
+/*
+ * Contiguous grouped BF16 GEMM: the layout of m_grouped_fp8_gemm_nt_contiguous
+ * without scales.
+ *   a BF16 [Msum, K] (Msum % 128 == 0), b BF16 [G, N, K], d BF16 [Msum, N]
+ *   grouped_layout I32 [Msum/128]: group id per 128-row block; negative ids
+ *   (and ids >= G) skip the block, its rows of d are not written.
+ *   K must be a multiple of 64.
+ */
+int m_grouped_bf16_gemm_nt_contiguous(const dg_tensor* a, const dg_tensor* b, const dg_tensor* d,
+                                      const dg_tensor* grouped_layout, hipStream_t stream);
+
+/*
  * Per-token FP8 cast: each row of x cut into 1x128 blocks along K; block
  * scale s = amax/448 (amax floored at 1e-4; with use_ue8m0 rounded up to a
  * power of two), q = e4m3(x/s) rounded to nearest even after clamping to
@@ -181,7 +203,10 @@ typedef struct dg_config {
   int32_t lds_bytes;          /* static LDS per workgroup */
 } dg_config;
 
-enum { DG_KIND_DENSE = 0, DG_KIND_CONTIGUOUS = 1, DG_KIND_MASKED = 2, DG_KIND_BF16_MASKED = 3 };
+enum {
+  DG_KIND_DENSE = 0, DG_KIND_CONTIGUOUS = 1, DG_KIND_MASKED = 2,            /* FP8 GEMMs */
+  DG_KIND_BF16_MASKED = 3, DG_KIND_BF16_DENSE = 4, DG_KIND_BF16_CONTIGUOUS = 5  /* BF16 GEMMs */
+};
 
 /* Fill *out with the configuration `kind` would launch for these sizes
  * (M = rows: M, Msum or max_m; G = groups, 1 for dense). */

@@ -16,6 +16,8 @@ from .binding import (  # noqa: F401
     m_grouped_fp8_gemm_nt_contiguous,
     m_grouped_fp8_gemm_nt_masked,
     m_grouped_bf16_gemm_nt_masked,
+    bf16_gemm_nt,
+    m_grouped_bf16_gemm_nt_contiguous,
     per_token_cast_to_fp8,
     per_block_cast_to_fp8,
     pack_ue8m0_to_int,

@@ -15,7 +15,8 @@ LIB_PATH = os.path.join(HERE, "libdgmi.so")
 
 DG_F32, DG_BF16, DG_E4M3, DG_I32 = 0, 1, 2, 3
 DG_OK, DG_INVALID_ARG, DG_UNSUPPORTED, DG_LAUNCH_FAILED = 0, 1, 2, 3
-DG_KIND_DENSE, DG_KIND_CONTIGUOUS, DG_KIND_MASKED, DG_KIND_BF16_MASKED = 0, 1, 2, 3
+DG_KIND_DENSE, DG_KIND_CONTIGUOUS, DG_KIND_MASKED = 0, 1, 2
+DG_KIND_BF16_MASKED, DG_KIND_BF16_DENSE, DG_KIND_BF16_CONTIGUOUS = 3, 4, 5
 
 ENTRY_POINTS = (
     "dg_last_error",
@@ -24,6 +25,8 @@ ENTRY_POINTS = (
     "m_grouped_fp8_gemm_nt_contiguous",
     "m_grouped_fp8_gemm_nt_masked",
     "m_grouped_bf16_gemm_nt_masked",
+    "bf16_gemm_nt",
+    "m_grouped_bf16_gemm_nt_contiguous",
     "per_token_cast_to_fp8",
     "per_block_cast_to_fp8",
     "pack_ue8m0_to_int",
@@ -78,6 +81,8 @@ def load_library(path=None):
         "m_grouped_fp8_gemm_nt_contiguous": ([T, T, T, T, T, T, vp], ctypes.c_int),
         "m_grouped_fp8_gemm_nt_masked": ([T, T, T, T, T, T, i64, vp], ctypes.c_int),
         "m_grouped_bf16_gemm_nt_masked": ([T, T, T, T, i64, vp], ctypes.c_int),
+        "bf16_gemm_nt": ([T, T, T, T, vp], ctypes.c_int),
+        "m_grouped_bf16_gemm_nt_contiguous": ([T, T, T, T, vp], ctypes.c_int),
         "per_token_cast_to_fp8": ([T, T, T, ctypes.c_int, vp], ctypes.c_int),
         "per_block_cast_to_fp8": ([T, T, T, ctypes.c_int, vp], ctypes.c_int),
         "pack_ue8m0_to_int": ([T, T, vp, vp], ctypes.c_int),
@@ -178,6 +183,21 @@ def m_grouped_bf16_gemm_nt_masked(a, b, d, masked_m, max_m_per_group, stream=Non
     lib = load_library()
     _check(lib.m_grouped_bf16_gemm_nt_masked(_ref(describe(a)), _ref(describe(b)), _ref(describe(d)),
                                              _ref(describe(masked_m)), int(max_m_per_group), _stream(stream)))
+    return d
+
+
+def bf16_gemm_nt(a, b, c, d, stream=None):
+    """d = c + a . b^T in BF16 (FP32 accumulation); c is None or a BF16/F32 [M, N] tensor (may be d)."""
+    lib = load_library()
+    _check(lib.bf16_gemm_nt(_ref(describe(a)), _ref(describe(b)), _ref(describe(c)), _ref(describe(d)),
+                            _stream(stream)))
+    return d
+
+
+def m_grouped_bf16_gemm_nt_contiguous(a, b, d, grouped_layout, stream=None):
+    lib = load_library()
+    _check(lib.m_grouped_bf16_gemm_nt_contiguous(_ref(describe(a)), _ref(describe(b)), _ref(describe(d)),
+                                                 _ref(describe(grouped_layout)), _stream(stream)))
     return d
 
 

@@ -342,6 +342,95 @@ int quant_common(const dg_tensor* x, const dg_tensor* q, const dg_tensor* sf, in
   return check_launch(per_block ? dgmi::launch_per_block(p, stream) : dgmi::launch_per_token(p, stream), fname);
 }
 
+// The BF16 GEMMs (dense with optional C, contiguous, masked): the same
+// kernel body as the FP8 GEMM with BF16 operands and no scales.
+int bf16_gemm_common(int mode, const dg_tensor* a, const dg_tensor* b, const dg_tensor* c, const dg_tensor* d,
+                     const dg_tensor* meta, int64_t max_m, hipStream_t stream, const char* fname) {
+  DG_TRY(check_basic(a, "a", true));
+  DG_TRY(check_basic(b, "b", true));
+  DG_TRY(check_basic(d, "d", true));
+  DG_TRY(check_dtype(a, "a", DG_BF16));
+  DG_TRY(check_dtype(b, "b", DG_BF16));
+  DG_TRY(check_dtype(d, "d", DG_BF16));
+  View3 va, vb, vd;
+  int64_t G = 1;
+  if (mode == dgmi::MODE_DENSE) {
+    if (a->ndim != 2 || b->ndim != 2 || d->ndim != 2) return fail(DG_INVALID_ARG, "%s: a, b, d must be 2-D", fname);
+    DG_TRY(view3(b, "b", 1, 0, &vb));
+  } else {
+    if (b->ndim != 3) return fail(DG_INVALID_ARG, "%s: b must be [G, N, K]", fname);
+    G = b->shape[0];
+    DG_TRY(view3(b, "b", G, 0, &vb));
+  }
+  if (mode == dgmi::MODE_MASKED) {
+    if (max_m < 0) return fail(DG_INVALID_ARG, "%s: max_m_per_group must be >= 0", fname);
+    DG_TRY(view3(a, "a", G, max_m, &va));
+    DG_TRY(view3(d, "d", G, max_m, &vd));
+  } else {
+    if (a->ndim != 2 || d->ndim != 2) return fail(DG_INVALID_ARG, "%s: a and d must be 2-D", fname);
+    DG_TRY(view3(a, "a", 1, 0, &va));
+    DG_TRY(view3(d, "d", 1, 0, &vd));
+  }
+  const int64_t M = va.R, K = va.C, N = vb.R;
+  if (mode == dgmi::MODE_MASKED && M != max_m)
+    return fail(DG_INVALID_ARG, "%s: a has %lld rows per group, max_m_per_group is %lld", fname, (long long)M, (long long)max_m);
+  if (vb.C != K) return fail(DG_INVALID_ARG, "%s: K mismatch", fname);
+  if (vd.R != M || vd.C != N) return fail(DG_INVALID_ARG, "%s: d must be [.., %lld, %lld]", fname, (long long)M, (long long)N);
+  if (K % 64 != 0) return fail(DG_UNSUPPORTED, "%s: K = %lld is not a multiple of 64", fname, (long long)K);
+  if (!aligned(a->data, 16) || !aligned(b->data, 16) || va.sr % 8 || vb.sr % 8 || va.sg % 8 || vb.sg % 8)
+    return fail(DG_INVALID_ARG, "%s: a and b need 16-byte aligned bases and row/group strides", fname);
+  if (!aligned(d->data, 2)) return fail(DG_INVALID_ARG, "%s: d must be 2-byte aligned", fname);
+  if (mode == dgmi::MODE_CONTIG) {
+    if (M % 128 != 0) return fail(DG_INVALID_ARG, "%s: Msum = %lld is not a multiple of 128", fname, (long long)M);
+    DG_TRY(check_basic(meta, "grouped_layout", true));
+    DG_TRY(check_dtype(meta, "grouped_layout", DG_I32));
+    if (meta->ndim != 1 || meta->shape[0] != M / 128)
+      return fail(DG_INVALID_ARG, "%s: grouped_layout must be I32 [Msum/128 = %lld]", fname, (long long)(M / 128));
+  } else if (mode == dgmi::MODE_MASKED) {
+    DG_TRY(check_basic(meta, "masked_m", true));
+    DG_TRY(check_dtype(meta, "masked_m", DG_I32));
+    if (meta->ndim != 1 || meta->shape[0] != G) return fail(DG_INVALID_ARG, "%s: masked_m must be I32 [G]", fname);
+  }
+  DG_TRY(check_no_alias(d, "d", a, "a"));
+  DG_TRY(check_no_alias(d, "d", b, "b"));
+  if (meta != nullptr) DG_TRY(check_no_alias(d, "d", meta, "metadata"));
+  bool c_f32 = false;
+  int64_t ldc = 0;
+  if (c != nullptr) {
+    DG_TRY(check_basic(c, "c", true));
+    if (c->dtype != DG_BF16 && c->dtype != DG_F32) return fail(DG_INVALID_ARG, "%s: c must be BF16 or F32", fname);
+    if (c->ndim != 2 || c->shape[0] != M || c->shape[1] != N)
+      return fail(DG_INVALID_ARG, "%s: c must be [M, N] = [%lld, %lld]", fname, (long long)M, (long long)N);
+    c_f32 = c->dtype == DG_F32;
+    if (!aligned(c->data, c_f32 ? 4 : 2)) return fail(DG_INVALID_ARG, "%s: c must be element-aligned", fname);
+    ldc = c->stride[0];
+    const bool same_as_d = c->data == d->data && c->dtype == d->dtype && ldc == d->stride[0];
+    if (!same_as_d) DG_TRY(check_no_alias(d, "d", c, "c"));
+  }
+  // the kernel addresses A and B in bytes
+  dgmi::GemmParams p = {};
+  p.a = static_cast<const uint8_t*>(a->data);
+  p.b = static_cast<const uint8_t*>(b->data);
+  p.d = static_cast<uint16_t*>(d->data);
+  p.c = c != nullptr ? c->data : nullptr;
+  p.ldc = ldc;
+  p.c_f32 = c_f32 ? 1 : 0;
+  p.meta = meta ? static_cast<const int32_t*>(meta->data) : nullptr;
+  p.lda = 2 * va.sr;
+  p.a_gs = 2 * va.sg;
+  p.ldb = 2 * vb.sr;
+  p.b_gs = 2 * vb.sg;
+  p.ldd = vd.sr;
+  p.d_gs = vd.sg;
+  p.M = (int32_t)M;
+  p.N = (int32_t)N;
+  p.k_bytes = (int32_t)(2 * K);
+  p.G = (int32_t)G;
+  if (G == 0 || M == 0 || N == 0) return ok();
+  if (K == 0) return fail(DG_UNSUPPORTED, "%s: K = 0 is not supported", fname);
+  return check_launch(dgmi::launch_bf16_gemm(p, mode, stream), fname);
+}
+
 }  // namespace
 
 extern "C" {
@@ -381,56 +470,22 @@ int m_grouped_fp8_gemm_nt_masked(const dg_tensor* a, const dg_tensor* b, const d
                          "m_grouped_fp8_gemm_nt_masked");
 }
 
+int bf16_gemm_nt(const dg_tensor* a, const dg_tensor* b, const dg_tensor* c, const dg_tensor* d, hipStream_t stream) {
+  return bf16_gemm_common(dgmi::MODE_DENSE, a, b, c, d, nullptr, 0, stream, "bf16_gemm_nt");
+}
+
+int m_grouped_bf16_gemm_nt_contiguous(const dg_tensor* a, const dg_tensor* b, const dg_tensor* d,
+                                      const dg_tensor* grouped_layout, hipStream_t stream) {
+  if (grouped_layout == nullptr) return fail(DG_INVALID_ARG, "m_grouped_bf16_gemm_nt_contiguous: grouped_layout is NULL");
+  return bf16_gemm_common(dgmi::MODE_CONTIG, a, b, nullptr, d, grouped_layout, 0, stream,
+                          "m_grouped_bf16_gemm_nt_contiguous");
+}
+
 int m_grouped_bf16_gemm_nt_masked(const dg_tensor* a, const dg_tensor* b, const dg_tensor* d,
                                   const dg_tensor* masked_m, int64_t max_m_per_group, hipStream_t stream) {
-  const char* fname = "m_grouped_bf16_gemm_nt_masked";
-  DG_TRY(check_basic(a, "a", true));
-  DG_TRY(check_basic(b, "b", true));
-  DG_TRY(check_basic(d, "d", true));
-  DG_TRY(check_dtype(a, "a", DG_BF16));
-  DG_TRY(check_dtype(b, "b", DG_BF16));
-  DG_TRY(check_dtype(d, "d", DG_BF16));
-  if (masked_m == nullptr) return fail(DG_INVALID_ARG, "%s: masked_m is NULL", fname);
-  DG_TRY(check_basic(masked_m, "masked_m", true));
-  DG_TRY(check_dtype(masked_m, "masked_m", DG_I32));
-  if (b->ndim != 3) return fail(DG_INVALID_ARG, "%s: b must be [G, N, K]", fname);
-  if (max_m_per_group < 0) return fail(DG_INVALID_ARG, "%s: max_m_per_group must be >= 0", fname);
-  const int64_t G = b->shape[0];
-  View3 va, vb, vd;
-  DG_TRY(view3(b, "b", G, 0, &vb));
-  DG_TRY(view3(a, "a", G, max_m_per_group, &va));
-  DG_TRY(view3(d, "d", G, max_m_per_group, &vd));
-  const int64_t M = va.R, K = va.C, N = vb.R;
-  if (M != max_m_per_group) return fail(DG_INVALID_ARG, "%s: a has %lld rows per group, max_m_per_group is %lld", fname, (long long)M, (long long)max_m_per_group);
-  if (vb.C != K) return fail(DG_INVALID_ARG, "%s: K mismatch", fname);
-  if (vd.R != M || vd.C != N) return fail(DG_INVALID_ARG, "%s: d must be [G, max_m, N]", fname);
-  if (masked_m->ndim != 1 || masked_m->shape[0] != G) return fail(DG_INVALID_ARG, "%s: masked_m must be I32 [G]", fname);
-  if (K % 64 != 0) return fail(DG_UNSUPPORTED, "%s: K = %lld is not a multiple of 64", fname, (long long)K);
-  if (!aligned(a->data, 16) || !aligned(b->data, 16) || va.sr % 8 || vb.sr % 8 || va.sg % 8 || vb.sg % 8)
-    return fail(DG_INVALID_ARG, "%s: a and b need 16-byte aligned bases and row/group strides", fname);
-  if (!aligned(d->data, 2)) return fail(DG_INVALID_ARG, "%s: d must be 2-byte aligned", fname);
-  DG_TRY(check_no_alias(d, "d", a, "a"));
-  DG_TRY(check_no_alias(d, "d", b, "b"));
-  DG_TRY(check_no_alias(d, "d", masked_m, "masked_m"));
-  // the kernel addresses A and B in bytes
-  dgmi::GemmParams p = {};
-  p.a = static_cast<const uint8_t*>(a->data);
-  p.b = static_cast<const uint8_t*>(b->data);
-  p.d = static_cast<uint16_t*>(d->data);
-  p.meta = static_cast<const int32_t*>(masked_m->data);
-  p.lda = 2 * va.sr;
-  p.a_gs = 2 * va.sg;
-  p.ldb = 2 * vb.sr;
-  p.b_gs = 2 * vb.sg;
-  p.ldd = vd.sr;
-  p.d_gs = vd.sg;
-  p.M = (int32_t)M;
-  p.N = (int32_t)N;
-  p.k_bytes = (int32_t)(2 * K);
-  p.G = (int32_t)G;
-  if (G == 0 || M == 0 || N == 0) return ok();
-  if (K == 0) return fail(DG_UNSUPPORTED, "%s: K = 0 is not supported", fname);
-  return check_launch(dgmi::launch_bf16_masked(p, stream), fname);
+  if (masked_m == nullptr) return fail(DG_INVALID_ARG, "m_grouped_bf16_gemm_nt_masked: masked_m is NULL");
+  return bf16_gemm_common(dgmi::MODE_MASKED, a, b, nullptr, d, masked_m, max_m_per_group, stream,
+                          "m_grouped_bf16_gemm_nt_masked");
 }
 
 int per_token_cast_to_fp8(const dg_tensor* x, const dg_tensor* q, const dg_tensor* sf, int use_ue8m0,
@@ -482,13 +537,15 @@ int dg_query_config(int32_t kind, int64_t G, int64_t M, int64_t N, int64_t K, dg
   if (G < 0 || M < 0 || N < 0 || K < 0) return fail(DG_INVALID_ARG, "dg_query_config: negative size");
   dgmi::TileCfg c;
   int64_t grid;
-  if (kind == DG_KIND_BF16_MASKED) {
-    c = dgmi::bf16_masked_config(G, M, N, K);
-    grid = dgmi::bf16_masked_grid(c, G, M, N);
+  if (kind == DG_KIND_BF16_MASKED || kind == DG_KIND_BF16_DENSE || kind == DG_KIND_BF16_CONTIGUOUS) {
+    const int mode = kind == DG_KIND_BF16_DENSE ? dgmi::MODE_DENSE
+                                                : (kind == DG_KIND_BF16_CONTIGUOUS ? dgmi::MODE_CONTIG : dgmi::MODE_MASKED);
+    c = dgmi::bf16_gemm_config(mode, G, M, N, K);
+    grid = dgmi::gemm_grid(c, mode, G, M, N);
   } else if (kind >= DG_KIND_DENSE && kind <= DG_KIND_MASKED) {
     const int mode = kind == DG_KIND_DENSE ? dgmi::MODE_DENSE : (kind == DG_KIND_CONTIGUOUS ? dgmi::MODE_CONTIG : dgmi::MODE_MASKED);
     c = dgmi::fp8_gemm_config(mode, G, M, N, K);
-    grid = dgmi::fp8_gemm_grid(c, mode, G, M, N);
+    grid = dgmi::gemm_grid(c, mode, G, M, N);
   } else {
     return fail(DG_INVALID_ARG, "dg_query_config: unknown kind %d", kind);
   }

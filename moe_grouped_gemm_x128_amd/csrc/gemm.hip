@@ -613,7 +613,9 @@ template <class T, int KIND>
 hipError_t launch_tile(const GemmParams& p, int mode, int sf_fmt, int64_t grid, hipStream_t stream) {
   const dim3 g((unsigned)grid), b(T::NT);
   if constexpr (KIND == KIND_BF16) {
-    gemm_kernel<T, KIND_BF16, SF_F32, MODE_MASKED><<<g, b, 0, stream>>>(p);
+    if (mode == MODE_DENSE) gemm_kernel<T, KIND_BF16, SF_F32, MODE_DENSE><<<g, b, 0, stream>>>(p);
+    else if (mode == MODE_CONTIG) gemm_kernel<T, KIND_BF16, SF_F32, MODE_CONTIG><<<g, b, 0, stream>>>(p);
+    else gemm_kernel<T, KIND_BF16, SF_F32, MODE_MASKED><<<g, b, 0, stream>>>(p);
     return hipGetLastError();
   }
 #define DGMI_LAUNCH(MODE_, SF_) gemm_kernel<T, KIND_FP8, SF_, MODE_><<<g, b, 0, stream>>>(p)
@@ -665,7 +667,7 @@ TileCfg fp8_gemm_config(int mode, int64_t G, int64_t M, int64_t N, int64_t K) {
   return make_cfg<TileL, KIND_FP8>(VAR_L);
 }
 
-int64_t fp8_gemm_grid(const TileCfg& cfg, int mode, int64_t G, int64_t M, int64_t N) {
+int64_t gemm_grid(const TileCfg& cfg, int mode, int64_t G, int64_t M, int64_t N) {
   const int64_t tm = (M + cfg.bm - 1) / cfg.bm, tn = (N + cfg.bn - 1) / cfg.bn;
   const int64_t tiles = (mode == MODE_MASKED ? G : 1) * tm * tn;
   // contiguous 256-row tiles: a second copy for tiles split between two groups
@@ -676,30 +678,26 @@ hipError_t launch_fp8_gemm(GemmParams p, int mode, int sf_fmt, hipStream_t strea
   const TileCfg cfg = fp8_gemm_config(mode, p.G, p.M, p.N, p.k_bytes);
   p.tiles_m = (p.M + cfg.bm - 1) / cfg.bm;
   p.tiles_n = (p.N + cfg.bn - 1) / cfg.bn;
-  const int64_t grid = fp8_gemm_grid(cfg, mode, p.G, p.M, p.N);
+  const int64_t grid = gemm_grid(cfg, mode, p.G, p.M, p.N);
   if (grid == 0) return hipSuccess;
   return launch_variant<KIND_FP8>(cfg, p, mode, sf_fmt, grid, stream);
 }
 
-// Masked BF16 GEMM: the decode buffers hold at most max_m rows per expert;
-// 128-row tiles with three stages up to 128 rows, the 256 x 256 tile above.
-TileCfg bf16_masked_config(int64_t G, int64_t max_m, int64_t N, int64_t K) {
-  (void)G; (void)K;
-  if (max_m <= 128) return N <= 128 ? make_cfg<TileS, KIND_BF16>(VAR_S) : make_cfg<TileW, KIND_BF16>(VAR_W);
+// BF16 GEMMs: the same tile choice as the FP8 GEMM (a K-slice is 64 BF16
+// elements instead of 128 FP8 ones, the bytes per tile are the same).
+TileCfg bf16_gemm_config(int mode, int64_t G, int64_t M, int64_t N, int64_t K) {
+  (void)mode; (void)G; (void)K;
+  if (M <= 128) return N <= 128 ? make_cfg<TileS, KIND_BF16>(VAR_S) : make_cfg<TileW, KIND_BF16>(VAR_W);
   return make_cfg<TileL, KIND_BF16>(VAR_L);
 }
 
-int64_t bf16_masked_grid(const TileCfg& cfg, int64_t G, int64_t max_m, int64_t N) {
-  return G * ((max_m + cfg.bm - 1) / cfg.bm) * ((N + cfg.bn - 1) / cfg.bn);
-}
-
-hipError_t launch_bf16_masked(GemmParams p, hipStream_t stream) {
-  const TileCfg cfg = bf16_masked_config(p.G, p.M, p.N, p.k_bytes / 2);
+hipError_t launch_bf16_gemm(GemmParams p, int mode, hipStream_t stream) {
+  const TileCfg cfg = bf16_gemm_config(mode, p.G, p.M, p.N, p.k_bytes / 2);
   p.tiles_m = (p.M + cfg.bm - 1) / cfg.bm;
   p.tiles_n = (p.N + cfg.bn - 1) / cfg.bn;
-  const int64_t grid = bf16_masked_grid(cfg, p.G, p.M, p.N);
+  const int64_t grid = gemm_grid(cfg, mode, p.G, p.M, p.N);
   if (grid == 0) return hipSuccess;
-  return launch_variant<KIND_BF16>(cfg, p, MODE_MASKED, SF_F32, grid, stream);
+  return launch_variant<KIND_BF16>(cfg, p, mode, SF_F32, grid, stream);
 }
 
 }  // namespace dgmi

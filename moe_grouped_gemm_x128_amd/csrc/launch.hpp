@@ -42,14 +42,13 @@ hipError_t launch_per_token(const QuantArgs& p, hipStream_t stream);
 hipError_t launch_per_block(const QuantArgs& p, hipStream_t stream);
 hipError_t launch_pack_ue8m0(const PackArgs& p, hipStream_t stream);
 
-// FP8 GEMM: choose the tile for (mode, G, M, N, K) and launch.
+// GEMMs: the tile for (mode, G, M, N, K) and the grid it launches (pure
+// functions of the shapes), and the launchers.
 TileCfg fp8_gemm_config(int mode, int64_t G, int64_t M, int64_t N, int64_t K);
-int64_t fp8_gemm_grid(const TileCfg& cfg, int mode, int64_t G, int64_t M, int64_t N);
+TileCfg bf16_gemm_config(int mode, int64_t G, int64_t M, int64_t N, int64_t K);
+int64_t gemm_grid(const TileCfg& cfg, int mode, int64_t G, int64_t M, int64_t N);
 hipError_t launch_fp8_gemm(GemmParams p, int mode, int sf_fmt, hipStream_t stream);
-
-// Masked BF16 GEMM (same kernel body; byte strides in p, no scales).
-TileCfg bf16_masked_config(int64_t G, int64_t max_m, int64_t N, int64_t K);
-int64_t bf16_masked_grid(const TileCfg& cfg, int64_t G, int64_t max_m, int64_t N);
-hipError_t launch_bf16_masked(GemmParams p, hipStream_t stream);
+// BF16 GEMMs: same kernel body; byte strides in p, no scales
+hipError_t launch_bf16_gemm(GemmParams p, int mode, hipStream_t stream);
 
 }  // namespace dgmi

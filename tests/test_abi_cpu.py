@@ -42,6 +42,34 @@ def test_every_declared_symbol_is_exported(lib):
         assert getattr(lib, name) is not None
 
 
+def test_bf16_gemm_validation_errors(lib):
+    D = binding.describe
+    M, N, K = 128, 64, 128
+    a, b, d = _t((M, K), torch.bfloat16), _t((N, K), torch.bfloat16), _t((M, N), torch.bfloat16)
+
+    def dense(a, b, c, d):
+        return lib.bf16_gemm_nt(ctypes.byref(D(a)), ctypes.byref(D(b)), ctypes.byref(D(c)) if c is not None else None,
+                                ctypes.byref(D(d)), None)
+
+    assert dense(a.float(), b, None, d) == binding.DG_INVALID_ARG          # dtype
+    assert dense(a, _t((N, K + 64), torch.bfloat16), None, d) == binding.DG_INVALID_ARG  # K mismatch
+    assert dense(a, b, None, _t((M, N + 1), torch.bfloat16)) == binding.DG_INVALID_ARG  # d shape
+    assert dense(_t((M, 96), torch.bfloat16), _t((N, 96), torch.bfloat16), None, d) == binding.DG_UNSUPPORTED  # K % 64
+    assert dense(a, b, _t((M, N), torch.int32), d) == binding.DG_INVALID_ARG  # c dtype
+    lay = _t((2,), torch.int32)
+    bg = _t((3, N, K), torch.bfloat16)
+    dg = _t((256, N), torch.bfloat16)
+
+    def contig(a, b, d, layout):
+        return lib.m_grouped_bf16_gemm_nt_contiguous(ctypes.byref(D(a)), ctypes.byref(D(b)), ctypes.byref(D(d)),
+                                                     ctypes.byref(D(layout)) if layout is not None else None, None)
+
+    assert contig(_t((256, K), torch.bfloat16), bg, dg, None) == binding.DG_INVALID_ARG  # no layout
+    assert contig(_t((200, K), torch.bfloat16), bg, _t((200, N), torch.bfloat16), lay) == binding.DG_INVALID_ARG  # Msum % 128
+    assert contig(_t((256, K), torch.bfloat16), bg, dg, _t((3,), torch.int32)) == binding.DG_INVALID_ARG  # layout length
+    assert contig(_t((256, K), torch.bfloat16), _t((N, K), torch.bfloat16), dg, lay) == binding.DG_INVALID_ARG  # b rank
+
+
 def test_query_config_is_a_pure_function_of_shapes(lib):
     c = binding.query_config(binding.DG_KIND_DENSE, 1, 4096, 2112, 7168)
     assert c == binding.query_config(binding.DG_KIND_DENSE, 1, 4096, 2112, 7168)
@@ -50,6 +78,13 @@ def test_query_config_is_a_pure_function_of_shapes(lib):
     assert m["grid"] == 32 * -(-256 // m["block_m"]) * -(-4096 // m["block_n"])
     b = binding.query_config(binding.DG_KIND_BF16_MASKED, 64, 128, 7168, 2048)
     assert b["grid"] == 64 * -(-128 // b["block_m"]) * -(-7168 // b["block_n"])
+    bd = binding.query_config(binding.DG_KIND_BF16_DENSE, 1, 4096, 7168, 2048)
+    assert bd["grid"] == -(-4096 // bd["block_m"]) * -(-7168 // bd["block_n"])
+    c = binding.query_config(binding.DG_KIND_CONTIGUOUS, 4, 32768, 4096, 7168)
+    bc = binding.query_config(binding.DG_KIND_BF16_CONTIGUOUS, 4, 32768, 4096, 7168)
+    tiles = -(-32768 // c["block_m"]) * -(-4096 // c["block_n"])
+    # 256-row contiguous tiles launch a second grid copy for tiles split between two groups
+    assert c["grid"] == (2 * tiles if c["block_m"] == 256 else tiles) and bc["grid"] == c["grid"]
     with pytest.raises(binding.DgmiError):
         binding.query_config(9, 1, 1, 1, 1)
 

@@ -1,0 +1,104 @@
+"""BF16 dense and contiguous-grouped GEMMs on the GPU against the oracle
+(BF16 operands, FP32 accumulation, BF16 out; tolerance of tests/helpers.py).
+Shapes span the 256-row tile (two stages) and the 128-row tiles (three
+stages), ragged M and N, K slices 1..many, the accumulate input C, and
+contiguous layouts with skipped blocks and tiles split between groups."""
+
+import numpy as np
+import pytest
+
+import oracle
+from moe_grouped_gemm_x128_amd import synth
+
+from helpers import SENTINEL_BF16, assert_bf16_close, say, to_dev, to_host
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+def _mg():
+    import moe_grouped_gemm_x128_amd as mg
+
+    return mg
+
+
+def _dev_bf16(bits):
+    return to_dev(bits.view(np.int16)).view(torch.bfloat16)
+
+
+def _sentinel(shape):
+    return torch.full(shape, SENTINEL_BF16, dtype=torch.int16, device="cuda").view(torch.bfloat16)
+
+
+@pytest.mark.parametrize("M,N,K", [(128, 256, 512), (200, 300, 384), (1, 130, 64), (257, 64, 256),
+                                   (64, 2112, 1024), (96, 100, 640), (300, 520, 192)])
+def test_bf16_dense_full_compare(M, N, K):
+    say(f"bf16_gemm_nt M={M} N={N} K={K}")
+    mg = _mg()
+    ab = synth.bf16_bits_from_f32(synth.normal_f32(181, (M, K)))
+    bb = synth.bf16_bits_from_f32(synth.normal_f32(182, (N, K)))
+    d = _sentinel((M, N))
+    mg.bf16_gemm_nt(_dev_bf16(ab), _dev_bf16(bb), None, d)
+    torch.cuda.synchronize()
+    assert_bf16_close(to_host(d), oracle.bf16_gemm_nt(ab, bb), f"bf16 dense {M}x{N}x{K}")
+
+
+@pytest.mark.parametrize("c_kind", ["bf16", "f32", "inplace"])
+def test_bf16_dense_accumulate_c(c_kind):
+    M, N, K = 200, 300, 256
+    say(f"bf16_gemm_nt accumulate c={c_kind}")
+    mg = _mg()
+    ab = synth.bf16_bits_from_f32(synth.normal_f32(183, (M, K)))
+    bb = synth.bf16_bits_from_f32(synth.normal_f32(184, (N, K)))
+    xc = synth.normal_f32(185, (M, N)) * np.float32(4.0)
+    if c_kind == "f32":
+        c = to_dev(xc)
+        cref = xc.astype(np.float64)
+        d = _sentinel((M, N))
+    else:
+        cbits = synth.bf16_bits_from_f32(xc)
+        cref = oracle.bf16_decode(cbits)
+        c = _dev_bf16(cbits)
+        d = c if c_kind == "inplace" else _sentinel((M, N))
+    mg.bf16_gemm_nt(_dev_bf16(ab), _dev_bf16(bb), c, d)
+    torch.cuda.synchronize()
+    assert_bf16_close(to_host(d), oracle.bf16_gemm_nt(ab, bb, c=cref), f"bf16 accumulate {c_kind}")
+
+
+def test_bf16_dense_large_sampled():
+    """A DeepSeek-V3-sized dense shape (4096 x 4096 x 7168), checked on
+    sampled rows against the oracle."""
+    M, N, K = 4096, 4096, 7168
+    say(f"bf16_gemm_nt {M}x{N}x{K} sampled")
+    mg = _mg()
+    xa = synth.normal_f32(186, (M, K))
+    xb = synth.normal_f32(187, (N, K))
+    a = to_dev(xa).to(torch.bfloat16)
+    b = to_dev(xb).to(torch.bfloat16)
+    d = _sentinel((M, N))
+    mg.bf16_gemm_nt(a, b, None, d)
+    torch.cuda.synchronize()
+    ab, bb = to_host(a), to_host(b)
+    assert np.array_equal(ab, synth.bf16_bits_from_f32(xa)), "device bf16 cast differs from the host RNE cast"
+    rows = np.unique(np.concatenate([np.random.default_rng(188).choice(M, 24, replace=False), [0, M - 1]]))
+    ref = oracle.bf16_gemm_nt(ab[rows], bb)
+    assert_bf16_close(to_host(d)[rows], ref, "bf16 dense large sampled")
+
+
+@pytest.mark.parametrize("layout", [[2, -1, 0, 2, 1, -1, 5], [0, 1, 1, 0, -1, 1, 0, -1, -1, 1]])
+def test_bf16_contiguous_skips_and_mixed_tiles(layout):
+    say(f"m_grouped_bf16_gemm_nt_contiguous layout={layout}")
+    mg = _mg()
+    layout = np.array(layout, dtype=np.int32)
+    G, N, K = 3, 300, 192
+    Msum = layout.size * 128
+    ab = synth.bf16_bits_from_f32(synth.normal_f32(189, (Msum, K)))
+    bb = synth.bf16_bits_from_f32(synth.normal_f32(190, (G, N, K)))
+    d = _sentinel((Msum, N))
+    mg.m_grouped_bf16_gemm_nt_contiguous(_dev_bf16(ab), _dev_bf16(bb), d, to_dev(layout))
+    torch.cuda.synchronize()
+    ref, written = oracle.m_grouped_bf16_gemm_nt_contiguous(ab, bb, np.where(layout < G, layout, -1))
+    got = to_host(d)
+    assert np.all(got[~written] == SENTINEL_BF16)
+    assert_bf16_close(got[written], ref[written], "bf16 contiguous")
