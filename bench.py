@@ -21,6 +21,8 @@ Other workloads (for the measurements in the design notes):
                   (N, K) = (4096, 7168) and (7168, 2048); metric GB/s
   masked_graph -- 64 experts, max_m 128, N 7168, K 2048, UE8M0 scales packed by
                   pack_ue8m0_to_int, FP8 and BF16 masked GEMMs replayed as one hipGraph
+  bf16_dense   -- the five dense shapes with BF16 operands through bf16_gemm_nt
+                  (metric against the 2.5 PFLOP/s BF16 MFMA peak)
 """
 
 import argparse
@@ -89,6 +91,38 @@ class DenseWorkload:
     def config(self):
         return {"workload": self.name, "M": self.M, "shapes_NK": self.shapes,
                 "scales": "fp32 1x128 (A) / 128x128 (B)", "out": "bf16"}
+
+
+class Bf16DenseWorkload:
+    """The five dense shapes with BF16 operands (converted once, outside the
+    step) through bf16_gemm_nt; one step = the five GEMMs."""
+    name = "dense_bf16_v3_shapes"
+
+    def __init__(self, torch, mg, synth):
+        self.torch, self.mg = torch, mg
+        dev = torch.device("cuda")
+        self.M = synth.DENSE_V3_M
+        self.shapes = list(synth.DENSE_V3_SHAPES)
+        self.bufs = []
+        for i, (N, K) in enumerate(self.shapes):
+            sa, sb = synth.dense_v3_seeds(i)
+            a = torch.from_numpy(synth.normal_f32(sa, (self.M, K))).to(dev).to(torch.bfloat16)
+            b = torch.from_numpy(synth.normal_f32(sb, (N, K))).to(dev).to(torch.bfloat16)
+            d = torch.empty((self.M, N), dtype=torch.bfloat16, device=dev)
+            self.bufs.append((a, b, d))
+        self.flops = [2.0 * self.M * N * K for N, K in self.shapes]
+        self.gemm_bytes = [2 * (self.M * K + N * K + self.M * N) for N, K in self.shapes]
+
+    def step(self, events=None):
+        for i, (a, b, d) in enumerate(self.bufs):
+            if events is not None:
+                events[i][0].record()
+            self.mg.bf16_gemm_nt(a, b, None, d)
+            if events is not None:
+                events[i][1].record()
+
+    def config(self):
+        return {"workload": self.name, "M": self.M, "shapes_NK": self.shapes, "out": "bf16"}
 
 
 class ContiguousWorkload:
@@ -376,7 +410,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="dense", choices=["dense", "contiguous", "masked", "masked_graph"])
+    ap.add_argument("--workload", default="dense", choices=["dense", "contiguous", "masked", "masked_graph", "bf16_dense"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run one 1 GiB device copy (calibrates rocprofv3 FETCH/WRITE_SIZE counters)")
@@ -400,7 +434,7 @@ def main():
 
     log(f"setting up workload {args.workload}")
     W = {"dense": DenseWorkload, "contiguous": ContiguousWorkload, "masked": MaskedWorkload,
-         "masked_graph": MaskedGraphWorkload}[args.workload](torch, mg, synth)
+         "masked_graph": MaskedGraphWorkload, "bf16_dense": Bf16DenseWorkload}[args.workload](torch, mg, synth)
     torch.cuda.synchronize()
 
     for _ in range(args.warmup):
@@ -455,9 +489,10 @@ def main():
         roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": achieved / HBM_PEAK_GBS, "traffic": None}
     else:
+        peak = BF16_PEAK_TFLOPS if args.workload == "bf16_dense" else FP8_PEAK_TFLOPS
         achieved = mean_flops / (mean_launch_ms * 1e-3) / 1e12
-        roof = {"bound": "mfma", "achieved": achieved, "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
-                "frac": achieved / FP8_PEAK_TFLOPS, "traffic": None}
+        roof = {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
+                "frac": achieved / peak, "traffic": None}
     roof["traffic"] = recorded_traffic(args.workload)
     roof["traffic_unit"] = "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)"
     roof["algorithmic_bytes_per_launch"] = float(np.mean(W.gemm_bytes))
@@ -488,6 +523,10 @@ def main():
         unit = "GB/s"
         step_bytes = float(sum(W.gemm_bytes))
         value = step_bytes / (ms_per_step * 1e-3) / 1e9
+    elif args.workload == "bf16_dense":
+        metric = "BF16 GEMM TFLOPS (% BF16 MFMA peak)"
+        unit = "TFLOPS"
+        roof["kernel"] = "gemm_kernel (BF16 kind)"
     else:
         metric = "FP8 block-scaled GEMM TFLOPS (% FP8 MFMA peak)"
         unit = "TFLOPS"
@@ -503,7 +542,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp8_e4m3+bf16" if graph_wl else "fp8_e4m3",
+        "dtype": "fp8_e4m3+bf16" if graph_wl else ("bf16" if args.workload == "bf16_dense" else "fp8_e4m3"),
         "data": "synthetic N(0,1) float32 inputs, seeded (numpy PCG64); no real activations or weights",
         "config": W.config(),
         "roofline": roof,
