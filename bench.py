@@ -1,6 +1,12 @@
 """Benchmark of the block-scaled FP8 GEMM path on one MI355X.
 
-    python bench.py [--steps K] [--warmup W] [--workload dense|contiguous|masked|masked_graph]
+    python bench.py [--steps K] [--warmup W] [--settle-seconds S]
+                    [--workload dense|contiguous|masked|masked_graph|bf16_dense]
+
+Before the W warmup steps, untimed steps run for S seconds (default 1): under
+sustained GEMM load the GPU clock dips for the first few milliseconds and
+settles within a few tens of milliseconds, and the K timed steps measure the
+settled, sustained rate.
 
 Default workload ("dense"): the five DeepSeek-V3-shaped dense GEMMs,
 M = 4096 with (N, K) in {(2112, 7168), (24576, 1536), (7168, 16384),
@@ -408,9 +414,12 @@ def time_cpu_baseline(rows_a=512, rows_b=8192):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="dense", choices=["dense", "contiguous", "masked", "masked_graph", "bf16_dense"])
+    ap.add_argument("--settle-seconds", type=float, default=1.0,
+                    help="untimed steps run for this long before the warmup steps, so that the timed steps see "
+                         "the GPU's steady sustained clock rather than the dip of its first milliseconds under load")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run one 1 GiB device copy (calibrates rocprofv3 FETCH/WRITE_SIZE counters)")
@@ -437,6 +446,18 @@ def main():
          "masked_graph": MaskedGraphWorkload, "bf16_dense": Bf16DenseWorkload}[args.workload](torch, mg, synth)
     torch.cuda.synchronize()
 
+    # Power-state settle: under sustained GEMM load the clock dips for the first
+    # few milliseconds (to ~1.4 GHz) and recovers to its steady level within a
+    # few tens of milliseconds; steps run here are not timed and not counted.
+    settle_steps = 0
+    t_settle = time.perf_counter() + args.settle_seconds
+    while time.perf_counter() < t_settle:
+        W.step()
+        settle_steps += 1
+        if settle_steps % 16 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    log(f"settle done ({settle_steps} steps in {args.settle_seconds:.2f} s)")
     for _ in range(args.warmup):
         W.step()
     torch.cuda.synchronize()
@@ -538,6 +559,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "settle": {"seconds": args.settle_seconds, "steps": settle_steps},
         "ms_per_step": ms_per_step,
         "higher_is_better": True,
         "scaling": "weak",
