@@ -17,9 +17,10 @@ with BF16 output -- the whole hot path, no work skipped.
 
 Prints ONE JSON line.  `value` is GEMM FLOPs (2*M*N*K summed over the
 shapes) per second of whole-step time; `roofline` describes the dominant
-kernel (the FP8 GEMM) from HIP events recorded around each GEMM launch on
-the launch stream; `cpu_baseline` times the CPU oracle on a bounded sample
-of the same workload.
+kernel (the FP8 GEMM) from HIP events recorded around each GEMM call on the
+launch stream (a call is one kernel launch, or two in stream order where the
+launch plan splits the columns); `cpu_baseline` times the CPU oracle on a
+bounded sample of the same workload.
 
 Other workloads (for the measurements in the design notes):
   contiguous   -- MoE prefill: 4 groups x 8192 rows, (N, K) = (4096, 7168) and (7168, 2048)
@@ -94,6 +95,10 @@ class DenseWorkload:
             if events is not None:
                 events[i][1].record()
 
+    def plan_args(self, i):
+        N, K = self.shapes[i]
+        return ("DG_KIND_DENSE", 1, self.M, N, K)
+
     def config(self):
         return {"workload": self.name, "M": self.M, "shapes_NK": self.shapes,
                 "scales": "fp32 1x128 (A) / 128x128 (B)", "out": "bf16"}
@@ -126,6 +131,10 @@ class Bf16DenseWorkload:
             self.mg.bf16_gemm_nt(a, b, None, d)
             if events is not None:
                 events[i][1].record()
+
+    def plan_args(self, i):
+        N, K = self.shapes[i]
+        return ("DG_KIND_BF16_DENSE", 1, self.M, N, K)
 
     def config(self):
         return {"workload": self.name, "M": self.M, "shapes_NK": self.shapes, "out": "bf16"}
@@ -168,6 +177,10 @@ class ContiguousWorkload:
             mg.m_grouped_fp8_gemm_nt_contiguous(b["a"], b["b"], b["sfa"], b["sfb"], b["d"], self.layout)
             if events is not None:
                 events[i][1].record()
+
+    def plan_args(self, i):
+        N, K = self.shapes[i]
+        return ("DG_KIND_CONTIGUOUS", self.G, self.Msum, N, K)
 
     def config(self):
         return {"workload": self.name, "groups": self.G, "rows": self.Msum, "shapes_NK": self.shapes}
@@ -215,6 +228,10 @@ class MaskedWorkload:
             mg.m_grouped_fp8_gemm_nt_masked(b["a"], b["b"], b["sfa"], b["sfb"], b["d"], self.masked_m, self.max_m)
             if events is not None:
                 events[i][1].record()
+
+    def plan_args(self, i):
+        N, K = self.shapes[i]
+        return ("DG_KIND_MASKED", self.G, self.max_m, N, K)
 
     def config(self):
         return {"workload": self.name, "experts": self.G, "max_m": self.max_m,
@@ -332,6 +349,9 @@ class MaskedGraphWorkload:
         self.flops = [f / n for f in self.flops]
         self.gemm_bytes = [b / n for b in self.gemm_bytes]
 
+    def plan_args(self, i):
+        return ("DG_KIND_MASKED" if i == 0 else "DG_KIND_BF16_MASKED", self.G, self.max_m, self.N, self.K)
+
     def config(self):
         return {"workload": self.name, "experts": self.G, "max_m": self.max_m, "N": self.N, "K": self.K,
                 "mean_sum_masked_m": float(np.mean([m.sum() for m in self.mm_host])) if self.mm_host else 0.0,
@@ -433,7 +453,7 @@ def main():
     import torch
 
     import moe_grouped_gemm_x128_amd as mg
-    from moe_grouped_gemm_x128_amd import synth
+    from moe_grouped_gemm_x128_amd import binding, synth
 
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
@@ -515,11 +535,13 @@ def main():
         roof = {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
                 "frac": achieved / peak, "traffic": None}
     roof["traffic"] = recorded_traffic(args.workload)
-    roof["traffic_unit"] = "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)"
+    roof["traffic_unit"] = "HBM bytes per GEMM call (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)"
     roof["algorithmic_bytes_per_launch"] = float(np.mean(W.gemm_bytes))
     roof["kernel"] = "gemm_kernel (FP8 kind)"
     roof["avg_launch_us"] = mean_launch_ms * 1e3
-    roof["per_launch"] = "mean over the workload's GEMM launches of one step (algorithmic work / HIP-event duration)"
+    roof["per_launch"] = ("mean over the workload's GEMM calls of one step (algorithmic work / HIP-event duration "
+                          "around the call; a call is one kernel launch, or two in stream order where the launch "
+                          "plan splits the columns, see gemm_per_shape)")
     if graph_wl:
         roof["algorithmic_bytes_per_launch"] = float(W.gemm_bytes[dom])
         roof["kernel"] = ["gemm_kernel (FP8 kind, UE8M0)", "gemm_kernel (BF16 kind)"][dom]
@@ -529,9 +551,15 @@ def main():
     per_shape = []
     for i in range(nshape):
         N, K = W.shapes[i]
+        kind, G, Mq, Nq, Kq = W.plan_args(i)
+        plan = binding.query_config(getattr(binding, kind), G, Mq, Nq, Kq)
+        tiles = f"{plan['block_m']}x{plan['block_n']}"
+        if plan["block_n2"]:
+            tiles += f" on columns [0, {plan['n_split']}), {plan['block_m']}x{plan['block_n2']} on the rest"
         per_shape.append({"N": N, "K": K, "gemm_us": gemm_ms[i] * 1e3,
                           "tflops": W.flops[i] / (gemm_ms[i] * 1e-3) / 1e12,
-                          "gbs": W.gemm_bytes[i] / (gemm_ms[i] * 1e-3) / 1e9})
+                          "gbs": W.gemm_bytes[i] / (gemm_ms[i] * 1e-3) / 1e9,
+                          "launches": 2 if plan["block_n2"] else 1, "tiles": tiles})
 
     if graph_wl:
         metric = "masked grouped FP8 (UE8M0) + BF16 GEMM GB/s under graph replay (% HBM)"

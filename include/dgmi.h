@@ -195,12 +195,22 @@ int per_block_cast_to_fp8(const dg_tensor* x, const dg_tensor* q, const dg_tenso
 int pack_ue8m0_to_int(const dg_tensor* x, const dg_tensor* out, int32_t* invalid_count,
                       hipStream_t stream);
 
-/* Launch configuration chosen for a GEMM (a pure function of the shapes). */
+/* Launch configuration chosen for a GEMM (a pure function of the shapes).
+ * A GEMM is one launch over all N columns, or two launches in stream order:
+ * the first over columns [0, n_split), the second (block_n2 > 0) over
+ * [n_split, N) with a narrower tile, when that fills the last round of
+ * workgroups over the compute units better (block sizes that are not powers
+ * of two: "DeepGEMM tested by Novita AI", section "Technological Innovations
+ * of DeepGEMM", item "Support for Arbitrary Matrix Sizes"). */
 typedef struct dg_config {
-  int32_t block_m, block_n;   /* output tile of one workgroup */
+  int32_t block_m, block_n;   /* output tile of one workgroup (first launch) */
   int32_t threads;            /* workgroup size */
-  int64_t grid;               /* workgroups launched */
-  int32_t lds_bytes;          /* static LDS per workgroup */
+  int64_t grid;               /* workgroups of the first launch */
+  int32_t lds_bytes;          /* static LDS per workgroup of the first launch */
+  int64_t n_split;            /* columns of the first launch (N when there is one launch) */
+  int32_t block_n2;           /* tile width of the second launch, 0 if none (block_m, threads as above) */
+  int64_t grid2;              /* workgroups of the second launch, 0 if none */
+  int32_t lds_bytes2;         /* static LDS per workgroup of the second launch */
 } dg_config;
 
 enum {

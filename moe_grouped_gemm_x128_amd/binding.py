@@ -51,6 +51,10 @@ class DgConfig(ctypes.Structure):
         ("threads", ctypes.c_int32),
         ("grid", ctypes.c_int64),
         ("lds_bytes", ctypes.c_int32),
+        ("n_split", ctypes.c_int64),
+        ("block_n2", ctypes.c_int32),
+        ("grid2", ctypes.c_int64),
+        ("lds_bytes2", ctypes.c_int32),
     ]
 
 
@@ -228,4 +232,5 @@ def pack_ue8m0_to_int(x, out, invalid_count=None, stream=None):
 def query_config(kind, G, M, N, K):
     cfg = DgConfig()
     _check(load_library().dg_query_config(int(kind), int(G), int(M), int(N), int(K), ctypes.byref(cfg)))
-    return dict(block_m=cfg.block_m, block_n=cfg.block_n, threads=cfg.threads, grid=cfg.grid, lds_bytes=cfg.lds_bytes)
+    return dict(block_m=cfg.block_m, block_n=cfg.block_n, threads=cfg.threads, grid=cfg.grid, lds_bytes=cfg.lds_bytes,
+                n_split=cfg.n_split, block_n2=cfg.block_n2, grid2=cfg.grid2, lds_bytes2=cfg.lds_bytes2)

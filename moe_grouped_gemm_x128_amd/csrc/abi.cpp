@@ -535,25 +535,27 @@ int pack_ue8m0_to_int(const dg_tensor* x, const dg_tensor* out, int32_t* invalid
 int dg_query_config(int32_t kind, int64_t G, int64_t M, int64_t N, int64_t K, dg_config* out) {
   if (out == nullptr) return fail(DG_INVALID_ARG, "dg_query_config: out is NULL");
   if (G < 0 || M < 0 || N < 0 || K < 0) return fail(DG_INVALID_ARG, "dg_query_config: negative size");
-  dgmi::TileCfg c;
-  int64_t grid;
+  dgmi::GemmPlan c;
+  int mode;
   if (kind == DG_KIND_BF16_MASKED || kind == DG_KIND_BF16_DENSE || kind == DG_KIND_BF16_CONTIGUOUS) {
-    const int mode = kind == DG_KIND_BF16_DENSE ? dgmi::MODE_DENSE
-                                                : (kind == DG_KIND_BF16_CONTIGUOUS ? dgmi::MODE_CONTIG : dgmi::MODE_MASKED);
-    c = dgmi::bf16_gemm_config(mode, G, M, N, K);
-    grid = dgmi::gemm_grid(c, mode, G, M, N);
+    mode = kind == DG_KIND_BF16_DENSE ? dgmi::MODE_DENSE
+                                      : (kind == DG_KIND_BF16_CONTIGUOUS ? dgmi::MODE_CONTIG : dgmi::MODE_MASKED);
+    c = dgmi::bf16_gemm_plan(mode, G, M, N, K);
   } else if (kind >= DG_KIND_DENSE && kind <= DG_KIND_MASKED) {
-    const int mode = kind == DG_KIND_DENSE ? dgmi::MODE_DENSE : (kind == DG_KIND_CONTIGUOUS ? dgmi::MODE_CONTIG : dgmi::MODE_MASKED);
-    c = dgmi::fp8_gemm_config(mode, G, M, N, K);
-    grid = dgmi::gemm_grid(c, mode, G, M, N);
+    mode = kind == DG_KIND_DENSE ? dgmi::MODE_DENSE : (kind == DG_KIND_CONTIGUOUS ? dgmi::MODE_CONTIG : dgmi::MODE_MASKED);
+    c = dgmi::fp8_gemm_plan(mode, G, M, N, K);
   } else {
     return fail(DG_INVALID_ARG, "dg_query_config: unknown kind %d", kind);
   }
-  out->block_m = c.bm;
-  out->block_n = c.bn;
-  out->threads = c.threads;
-  out->grid = grid;
-  out->lds_bytes = c.lds_bytes;
+  out->block_m = c.cfg[0].bm;
+  out->block_n = c.cfg[0].bn;
+  out->threads = c.cfg[0].threads;
+  out->grid = dgmi::plan_grid(c, 0, mode, G, M, N);
+  out->lds_bytes = c.cfg[0].lds_bytes;
+  out->n_split = c.parts == 2 ? c.n_split : N;
+  out->block_n2 = c.parts == 2 ? c.cfg[1].bn : 0;
+  out->grid2 = dgmi::plan_grid(c, 1, mode, G, M, N);
+  out->lds_bytes2 = c.parts == 2 ? c.cfg[1].lds_bytes : 0;
   return ok();
 }
 

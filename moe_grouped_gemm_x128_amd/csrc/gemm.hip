@@ -48,10 +48,18 @@
 //     A and nearly S of B are always in flight.
 //   * The MFMA takes the B fragment as its first operand: the 16x16 result
 //     then holds, per lane, one output row (m = lane % 16) and four output
-//     columns.  The B fragment rows are permuted so that the four fragments
-//     of a wave give every lane 16 consecutive columns: one row scale per
-//     lane per fragment row, and the BF16 epilogue stores 2 x 16 bytes per
-//     lane per fragment row, straight from registers.
+//     columns.  On 64-column wave tiles the B fragment rows are permuted so
+//     that the four fragments of a wave give every lane 16 consecutive
+//     columns: one row scale per lane per fragment row, one block scale per
+//     wave, and the BF16 epilogue stores 2 x 16 bytes per lane per fragment
+//     row, straight from registers.  The 48-column wave tiles of the
+//     256 x 192 tile keep MFMA order (4 columns per lane and fragment, one
+//     block scale per fragment, 8-byte stores).
+//   * Block sizes per shape ("DeepGEMM tested by Novita AI", section
+//     "Technological Innovations of DeepGEMM", item "Support for Arbitrary
+//     Matrix Sizes"): a 256 x 192 tile, alone or (BF16) beside the
+//     256 x 256 one in a second launch over the last columns, when that
+//     fills the last round of workgroups better (plan_large).
 //   * Tile order is XCD-aware: workgroups are dealt to the 8 XCDs round
 //     robin, so the block index is remapped to give each XCD a contiguous
 //     band of tiles (its L2 then holds the shared A rows / B columns).
@@ -83,7 +91,8 @@ constexpr int vmcnt_lgkm0(int n) { return vmcnt_only(n) & ~(15 << 8); }
 //   h(r) = (b0 ^ b3 ^ b5) | b1 << 1 | (b2 ^ b4) << 2.
 // The MFMA fragment reads touch 16 rows at one chunk: A fragments rows
 // r0 + 0..15 (bits 0-3 vary), B fragments the permuted rows of the epilogue
-// layout (bits 0, 1, 4, 5 vary).  h is a bijection on the varying bits in
+// layout (bits 0, 1, 4, 5 vary) or, on 48-column wave tiles, rows r0 + 0..15
+// like A (r0 a multiple of 16).  h is a bijection on the varying bits in
 // both cases, for every group of 8 lanes and for every 16 lanes split by
 // row parity, so the reads are free of bank conflicts with 32 or with 64
 // four-byte banks.
@@ -103,9 +112,17 @@ struct TileShape {
   static constexpr int LOADS = A_LOADS + B_LOADS;
   static constexpr int A_BYTES = BM * BK, B_BYTES = BN * BK, STAGE = (BM + BN) * BK;
   static_assert(BM % (8 * NW) == 0 && BN % (8 * NW) == 0, "tile rows must split into 8-row wave loads");
-  static_assert(FN == 4, "the epilogue packs four fragments into 16 consecutive columns");
-  static_assert(TN == 64 && 128 % TN == 0, "a wave's columns must lie in one 128-column scale block");
-  static constexpr int NBT = (BN + 127) / 128;      // 128-column scale blocks per tile
+  // Column layouts.  PERM (64-column wave tiles, tile starts at multiples of
+  // 128): the B rows are permuted so that a lane holds 16 consecutive
+  // columns, and a wave's columns lie in one 128-column scale block.
+  // Otherwise fragment f holds columns 16f..16f+15 of the wave tile in MFMA
+  // order (4 consecutive columns per lane), and each fragment takes the scale
+  // of its own 128-column block (a 16-column fragment never straddles one
+  // when the tile starts at a multiple of 16).
+  static constexpr bool PERM = TN == 64;
+  static_assert(PERM ? FN == 4 : TN % 16 == 0, "wave tile columns");
+  static constexpr int NSB = PERM ? 1 : FN;         // B block scales a wave uses per K-slice
+  static constexpr int NBT = (BN + 127) / 128 + (PERM ? 0 : 1);  // 128-column scale blocks a tile touches
   static_assert(BM + NBT <= NT, "one thread per tile row stages the A scales, one per column block the B scale");
   static_assert(STAGES >= 2 && STAGES <= 3, "two or three LDS stages");
   static_assert(FM >= 3, "a K-slice has an early point (group 1) before its late point (last group)");
@@ -145,8 +162,71 @@ __device__ __forceinline__ void band_order(int t, int tiles_m, int tiles_n, int 
   tn = in_band / rows;
 }
 
+typedef int32_t i32x2 __attribute__((ext_vector_type(2)));
+
 __device__ __forceinline__ bf16x8 lo_bf16(const i32x8& v) { return __builtin_bit_cast(bf16x8, i32x4{v[0], v[1], v[2], v[3]}); }
 __device__ __forceinline__ bf16x8 hi_bf16(const i32x8& v) { return __builtin_bit_cast(bf16x8, i32x4{v[4], v[5], v[6], v[7]}); }
+
+// Epilogue of the unpermuted column layout: fragment f of wave column wn
+// holds tile columns wn*TN + 16f + 4q .. +3 in lane group q = lane/16, row
+// m = lane%16 of each fragment row.  Optional C (dense only) is added to the
+// FP32 accumulator before the BF16 rounding; c may alias d (each element of
+// C is read before the same thread writes it).  8-byte stores of four BF16.
+template <class T>
+__device__ __forceinline__ void epilogue_cols4(const GemmParams& p, uint16_t* D, f32x4 (&acc)[T::FM][T::FN], int m0,
+                                               int n0, int wm, int wn, int lane, int lo, int hi, int row_lim,
+                                               bool dense) {
+  const int fr = lane & 15;
+  const int colq = n0 + wn * T::TN + (lane >> 4) * 4;
+  const bool vec_ok = ((p.ldd & 3) == 0) && ((reinterpret_cast<uintptr_t>(D) & 7) == 0);
+  const bool has_c = dense && p.c != nullptr;
+#pragma unroll
+  for (int i = 0; i < T::FM; ++i) {
+    const int rl = wm * T::TM + i * 16 + fr;
+    const int row = m0 + rl;
+    if (rl < lo || rl >= hi || row >= row_lim) continue;
+    uint16_t* drow = D + (int64_t)row * p.ldd;
+#pragma unroll
+    for (int f = 0; f < T::FN; ++f) {
+      const int c = colq + 16 * f;
+      f32x4 v = acc[i][f];
+      if (has_c) {
+        if (p.c_f32) {
+          const float* crow = static_cast<const float*>(p.c) + (int64_t)row * p.ldc;
+          if (((p.ldc & 3) == 0) && ((reinterpret_cast<uintptr_t>(p.c) & 15) == 0) && c + 4 <= p.N) {
+            v += *reinterpret_cast<const f32x4*>(crow + c);
+          } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              if (c + e < p.N) v[e] += crow[c + e];
+          }
+        } else {
+          const uint16_t* crow = static_cast<const uint16_t*>(p.c) + (int64_t)row * p.ldc;
+          if (((p.ldc & 3) == 0) && ((reinterpret_cast<uintptr_t>(p.c) & 7) == 0) && c + 4 <= p.N) {
+            const i32x2 cv = *reinterpret_cast<const i32x2*>(crow + c);
+            v[0] += __uint_as_float((uint32_t)cv[0] << 16);
+            v[1] += __uint_as_float((uint32_t)cv[0] & 0xffff0000u);
+            v[2] += __uint_as_float((uint32_t)cv[1] << 16);
+            v[3] += __uint_as_float((uint32_t)cv[1] & 0xffff0000u);
+          } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              if (c + e < p.N) v[e] += bf16_to_f32(crow[c + e]);
+          }
+        }
+      }
+      const uint32_t w0 = (uint32_t)f32_to_bf16_rne(v[0]) | ((uint32_t)f32_to_bf16_rne(v[1]) << 16);
+      const uint32_t w1 = (uint32_t)f32_to_bf16_rne(v[2]) | ((uint32_t)f32_to_bf16_rne(v[3]) << 16);
+      if (vec_ok && c + 4 <= p.N) {
+        *reinterpret_cast<i32x2*>(drow + c) = i32x2{(int)w0, (int)w1};
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (c + e < p.N) drow[c + e] = (uint16_t)((e < 2 ? w0 : w1) >> (16 * (e & 1)));
+      }
+    }
+  }
+}
 
 template <class T, int KIND, int SF, int MODE>
 __global__ __launch_bounds__(T::NT) void gemm_kernel(const GemmParams p) {
@@ -299,10 +379,16 @@ __global__ __launch_bounds__(T::NT) void gemm_kernel(const GemmParams p) {
   // With h linear, lds_off(r0 + x, c) = (lds_off(x, c) ^ (h(r0) << 4)) + r0*128
   // whenever r0 has no bits below 4 in common with x; fragment offsets are
   // therefore a per-lane base XOR a compile-time constant, plus an immediate.
+  // Without the permutation (PERM false) fragment f reads tile rows
+  // wn*TN + 16f + 0..15; its offsets are kept per fragment (the row base is
+  // a multiple of 16 but its bits can overlap those of 16f).
   const int fr = lane & 15;
   const int kc = (lane >> 4) * 2;  // first of the lane's two 16-B K chunks
   const int a_base = lds_off(wm * T::TM + fr, kc);                                  // fragment 0, chunk kc
-  const int b_base = lds_off(wn * T::TN + (fr >> 2) * 16 + (fr & 3), kc);  // fragment 0, chunk kc
+  const int b_base = lds_off(wn * T::TN + (fr >> 2) * 16 + (fr & 3), kc);  // fragment 0, chunk kc (PERM)
+  int b_offs[T::PERM ? 1 : T::FN];
+#pragma unroll
+  for (int f = 0; f < (T::PERM ? 1 : T::FN); ++f) b_offs[f] = lds_off(wn * T::TN + 16 * f + fr, kc);
 
   // a wave whose rows all lie outside the rows to compute skips its MFMAs
   // (masked decode past masked_m; the unused half of a contiguous tile)
@@ -388,7 +474,8 @@ __global__ __launch_bounds__(T::NT) void gemm_kernel(const GemmParams p) {
 
   const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
   auto b_frag = [&](const uint8_t* stage, int f) {
-    const int off = (b_base ^ (swz(f * 4) << 4)) + f * 4 * 128;  // rows +4f
+    const int off = T::PERM ? (b_base ^ (swz(f * 4) << 4)) + f * 4 * 128  // rows +4f
+                            : b_offs[T::PERM ? 0 : f];
     const i32x4 l = *reinterpret_cast<const i32x4*>(stage + off);
     const i32x4 h = *reinterpret_cast<const i32x4*>(stage + (off ^ 16));
     return i32x8{l[0], l[1], l[2], l[3], h[0], h[1], h[2], h[3]};
@@ -399,8 +486,13 @@ __global__ __launch_bounds__(T::NT) void gemm_kernel(const GemmParams p) {
     const i32x4 h = *reinterpret_cast<const i32x4*>(stage + (off ^ 16));
     return i32x8{l[0], l[1], l[2], l[3], h[0], h[1], h[2], h[3]};
   };
-  const int sa_row0 = wm * T::TM + fr;             // this lane's scale slot for fragment row 0
-  const int sb_slot = T::BM + (wn * T::TN) / 128;  // this wave's B block scale slot
+  const int sa_row0 = wm * T::TM + fr;  // this lane's scale slot for fragment row 0
+  // B block scale slots of this wave (one, or one per fragment); slot BM + x
+  // holds column block n0/128 + x
+  int sb_slot[T::NSB];
+#pragma unroll
+  for (int f = 0; f < T::NSB; ++f)
+    sb_slot[f] = T::BM + (T::PERM ? (wn * T::TN) / 128 : ((n0 & 127) + wn * T::TN + 16 * f) / 128);
 
   // ---- K loop: one continuous software pipeline over fragment groups.
   // Group (kb, i) issues the FN MFMAs of A fragment i of slice kb and (FP8)
@@ -415,15 +507,19 @@ __global__ __launch_bounds__(T::NT) void gemm_kernel(const GemmParams p) {
   // with its own FMAs and serialise on the MFMA latency).
   // A fragments (and their row scales) are read PF fragment groups ahead
   // of their MFMAs; the next slice's first PF are read right after the late
-  // barrier.
-  constexpr int PF = 1;
+  // barrier.  Two groups ahead where a group has fewer than four MFMAs, so
+  // that the LDS read latency still has as many MFMAs to hide behind.
+  constexpr int PF = T::FN < 4 ? 2 : 1;
   static_assert(PF == 1 || PF == 2, "prefetch depth");
   auto kloop = [&]() {
     i32x8 bf[T::FN];
     i32x8 af, af1;             // A fragments of the current and (PF = 2) the next group
-    float sa = 0.f, sa1 = 0.f, sb = 0.f;  // raw row scales of those groups / block scale of the slice
-    f32x4 P[2][T::FN];         // partials of the current and the previous group
-    float s_prev = 0.f;        // combined scale of the previous group (the first promote adds 0 * 0)
+    float sa = 0.f, sa1 = 0.f;  // row scales of those groups
+    float sb[T::NSB];           // block scale(s) of the slice
+    f32x4 P[2][T::FN];          // partials of the current and the previous group
+    float s_prev[T::NSB];       // combined scale(s) of the previous group (the first promote adds 0 * 0)
+#pragma unroll
+    for (int f = 0; f < T::NSB; ++f) sb[f] = s_prev[f] = 0.f;
 #pragma unroll
     for (int f = 0; f < T::FN; ++f) P[(T::FM - 1) & 1][f] = zero;
 #pragma unroll
@@ -433,7 +529,8 @@ __global__ __launch_bounds__(T::NT) void gemm_kernel(const GemmParams p) {
     if constexpr (FP8) {
       sa = ssc[0][sa_row0];
       sa1 = PF == 2 ? ssc[0][sa_row0 + 16] : sa;
-      sb = ssc[0][sb_slot];
+#pragma unroll
+      for (int f = 0; f < T::NSB; ++f) sb[f] = ssc[0][sb_slot[f]];
     }
 
     auto kblock = [&](auto st_tag, int kb) {
@@ -447,11 +544,15 @@ __global__ __launch_bounds__(T::NT) void gemm_kernel(const GemmParams p) {
       for (int i = 0; i < T::FM; ++i) {
         __builtin_amdgcn_sched_barrier(0);
         if (i == 1) early_sync();
-        const float s_cur = sa * sb;
+        float s_cur[T::NSB];
+#pragma unroll
+        for (int f = 0; f < T::NSB; ++f) s_cur[f] = sa * sb[f];
         // the A fragment / row scale that become current after this group
         // (n0) and, for PF = 2, the one after (n1)
         i32x8 n0 = af1, n1 = af1;
-        float ns0 = sa1, ns1 = sa1, nsb = sb;
+        float ns0 = sa1, ns1 = sa1, nsb[T::NSB];
+#pragma unroll
+        for (int f = 0; f < T::NSB; ++f) nsb[f] = sb[f];
         if (i + 1 < T::FM) {
           if (PF == 1) {
             if constexpr (FP8) ns0 = ssc[ST][sa_row0 + (i + 1) * 16];
@@ -465,18 +566,20 @@ __global__ __launch_bounds__(T::NT) void gemm_kernel(const GemmParams p) {
           if constexpr (FP8) {
             ns0 = ssc[NX][sa_row0];
             if (PF == 2) ns1 = ssc[NX][sa_row0 + 16];
-            nsb = ssc[NX][sb_slot];
+#pragma unroll
+            for (int f = 0; f < T::NSB; ++f) nsb[f] = ssc[NX][sb_slot[f]];
           }
           n0 = a_frag(nxt_a, 0);
         }
         if constexpr (FP8 && SF == SF_UE8M0) {
           // power-of-two scales go into the MFMA itself: its scale operands
           // multiply by 2^(e-127) per A row (the lane's row) and per B row
-          // (one 128-column block per wave), and it accumulates in place
-          const int ea = (int)(__float_as_uint(sa) >> 23), eb = (int)(__float_as_uint(sb) >> 23);
+          // (the fragment's 128-column block), and it accumulates in place
+          const int ea = (int)(__float_as_uint(sa) >> 23);
 #pragma unroll
           for (int f = 0; f < T::FN; ++f) {
             __builtin_amdgcn_sched_barrier(0);
+            const int eb = (int)(__float_as_uint(sb[T::NSB == 1 ? 0 : f]) >> 23);
             acc[i][f] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf[f], af, acc[i][f], 0, 0, 0, eb, 0, ea);
             spread_loads(i, f, cur_a, cur_b, kb);
             if (i + 1 == T::FM) bf[f] = b_frag(nxt_b, f);  // last use of bf[f] in this slice
@@ -490,8 +593,9 @@ __global__ __launch_bounds__(T::NT) void gemm_kernel(const GemmParams p) {
             P[i & 1][f] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf[f], af, zero, 0, 0, 0, 0, 0, 0);
             spread_loads(i, f, cur_a, cur_b, kb);
             __builtin_amdgcn_sched_barrier(0);
-            if (i > 0) acc[i - 1][f] += P[(i - 1) & 1][f] * s_prev;
-            else acc[T::FM - 1][f] += P[(T::FM - 1) & 1][f] * s_prev;
+            const float sp = s_prev[T::NSB == 1 ? 0 : f];
+            if (i > 0) acc[i - 1][f] += P[(i - 1) & 1][f] * sp;
+            else acc[T::FM - 1][f] += P[(T::FM - 1) & 1][f] * sp;
             if (i + 1 == T::FM) bf[f] = b_frag(nxt_b, f);  // last use of bf[f] in this slice
           }
         } else {
@@ -517,7 +621,8 @@ __global__ __launch_bounds__(T::NT) void gemm_kernel(const GemmParams p) {
           __builtin_amdgcn_sched_barrier(0);
           n1 = a_frag(nxt_a, 1);  // after the B fragments the next group 0 waits for
         }
-        s_prev = s_cur;
+#pragma unroll
+        for (int f = 0; f < T::NSB; ++f) s_prev[f] = s_cur[f];
         if (PF == 1) {
           af = n0;
           sa = ns0;
@@ -527,7 +632,8 @@ __global__ __launch_bounds__(T::NT) void gemm_kernel(const GemmParams p) {
           af1 = n1;
           sa1 = ns1;
         }
-        sb = nsb;
+#pragma unroll
+        for (int f = 0; f < T::NSB; ++f) sb[f] = nsb[f];
       }
     };
 
@@ -544,7 +650,7 @@ __global__ __launch_bounds__(T::NT) void gemm_kernel(const GemmParams p) {
     if constexpr (FP8 && SF == SF_F32) {
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int f = 0; f < T::FN; ++f) acc[T::FM - 1][f] += P[(T::FM - 1) & 1][f] * s_prev;
+      for (int f = 0; f < T::FN; ++f) acc[T::FM - 1][f] += P[(T::FM - 1) & 1][f] * s_prev[T::NSB == 1 ? 0 : f];
     }
   };
 
@@ -561,70 +667,74 @@ __global__ __launch_bounds__(T::NT) void gemm_kernel(const GemmParams p) {
   __builtin_amdgcn_s_waitcnt(0);  // drain the redundant last loads before LDS is reused or freed
   if (!live) return;
 
-  // ---- epilogue: BF16, row m = lane%16 of each fragment row, 16 consecutive columns per lane
-  const int col0 = n0 + wn * T::TN + (lane >> 4) * 16;
-  const bool vec_ok = ((p.ldd & 7) == 0) && ((reinterpret_cast<uintptr_t>(D) & 15) == 0);
+  if constexpr (!T::PERM) {
+    epilogue_cols4<T>(p, D, acc, m0, n0, wm, wn, lane, lo, hi, row_lim, MODE == MODE_DENSE);
+  } else {
+    // ---- epilogue: BF16, row m = lane%16 of each fragment row, 16 consecutive columns per lane
+    const int col0 = n0 + wn * T::TN + (lane >> 4) * 16;
+    const bool vec_ok = ((p.ldd & 7) == 0) && ((reinterpret_cast<uintptr_t>(D) & 15) == 0);
 #pragma unroll
-  for (int i = 0; i < T::FM; ++i) {
-    const int rl = wm * T::TM + i * 16 + fr;
-    const int row = m0 + rl;
-    if (rl < lo || rl >= hi || row >= row_lim) continue;
-    if (MODE == MODE_DENSE && p.c != nullptr) {
-      // D = C + A . B^T ("DeepInside DeepGEMM", section 4): C is added to the
-      // FP32 accumulator before the BF16 rounding (read before d is written,
-      // so c may be d itself)
-      const int cc = col0;
-      if (p.c_f32) {
-        const float* crow = static_cast<const float*>(p.c) + (int64_t)row * p.ldc;
-        const bool cvec = ((p.ldc & 3) == 0) && ((reinterpret_cast<uintptr_t>(p.c) & 15) == 0) && cc + 16 <= p.N;
+    for (int i = 0; i < T::FM; ++i) {
+      const int rl = wm * T::TM + i * 16 + fr;
+      const int row = m0 + rl;
+      if (rl < lo || rl >= hi || row >= row_lim) continue;
+      if (MODE == MODE_DENSE && p.c != nullptr) {
+        // D = C + A . B^T ("DeepInside DeepGEMM", section 4): C is added to the
+        // FP32 accumulator before the BF16 rounding (read before d is written,
+        // so c may be d itself)
+        const int cc = col0;
+        if (p.c_f32) {
+          const float* crow = static_cast<const float*>(p.c) + (int64_t)row * p.ldc;
+          const bool cvec = ((p.ldc & 3) == 0) && ((reinterpret_cast<uintptr_t>(p.c) & 15) == 0) && cc + 16 <= p.N;
 #pragma unroll
-        for (int f = 0; f < T::FN; ++f) {
-          if (cvec) {
-            const f32x4 cv = *reinterpret_cast<const f32x4*>(crow + cc + 4 * f);
-            acc[i][f] += cv;
-          } else {
+          for (int f = 0; f < T::FN; ++f) {
+            if (cvec) {
+              const f32x4 cv = *reinterpret_cast<const f32x4*>(crow + cc + 4 * f);
+              acc[i][f] += cv;
+            } else {
 #pragma unroll
-            for (int e = 0; e < 4; ++e)
-              if (cc + 4 * f + e < p.N) acc[i][f][e] += crow[cc + 4 * f + e];
-          }
-        }
-      } else {
-        const uint16_t* crow = static_cast<const uint16_t*>(p.c) + (int64_t)row * p.ldc;
-        const bool cvec = ((p.ldc & 7) == 0) && ((reinterpret_cast<uintptr_t>(p.c) & 15) == 0) && cc + 16 <= p.N;
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          if (cvec) {
-            const i32x4 cv = *reinterpret_cast<const i32x4*>(crow + cc + 8 * h);
-#pragma unroll
-            for (int w = 0; w < 4; ++w) {
-              acc[i][2 * h + w / 2][2 * (w & 1)] += __uint_as_float((uint32_t)cv[w] << 16);
-              acc[i][2 * h + w / 2][2 * (w & 1) + 1] += __uint_as_float((uint32_t)cv[w] & 0xffff0000u);
+              for (int e = 0; e < 4; ++e)
+                if (cc + 4 * f + e < p.N) acc[i][f][e] += crow[cc + 4 * f + e];
             }
-          } else {
+          }
+        } else {
+          const uint16_t* crow = static_cast<const uint16_t*>(p.c) + (int64_t)row * p.ldc;
+          const bool cvec = ((p.ldc & 7) == 0) && ((reinterpret_cast<uintptr_t>(p.c) & 15) == 0) && cc + 16 <= p.N;
 #pragma unroll
-            for (int e = 0; e < 8; ++e)
-              if (cc + 8 * h + e < p.N) acc[i][2 * h + e / 4][e & 3] += bf16_to_f32(crow[cc + 8 * h + e]);
+          for (int h = 0; h < 2; ++h) {
+            if (cvec) {
+              const i32x4 cv = *reinterpret_cast<const i32x4*>(crow + cc + 8 * h);
+#pragma unroll
+              for (int w = 0; w < 4; ++w) {
+                acc[i][2 * h + w / 2][2 * (w & 1)] += __uint_as_float((uint32_t)cv[w] << 16);
+                acc[i][2 * h + w / 2][2 * (w & 1) + 1] += __uint_as_float((uint32_t)cv[w] & 0xffff0000u);
+              }
+            } else {
+#pragma unroll
+              for (int e = 0; e < 8; ++e)
+                if (cc + 8 * h + e < p.N) acc[i][2 * h + e / 4][e & 3] += bf16_to_f32(crow[cc + 8 * h + e]);
+            }
           }
         }
       }
-    }
-    uint32_t packed[8];
+      uint32_t packed[8];
 #pragma unroll
-    for (int f = 0; f < T::FN; ++f) {
-      packed[2 * f] = (uint32_t)f32_to_bf16_rne(acc[i][f][0]) | ((uint32_t)f32_to_bf16_rne(acc[i][f][1]) << 16);
-      packed[2 * f + 1] = (uint32_t)f32_to_bf16_rne(acc[i][f][2]) | ((uint32_t)f32_to_bf16_rne(acc[i][f][3]) << 16);
-    }
-    uint16_t* drow = D + (int64_t)row * p.ldd;
+      for (int f = 0; f < T::FN; ++f) {
+        packed[2 * f] = (uint32_t)f32_to_bf16_rne(acc[i][f][0]) | ((uint32_t)f32_to_bf16_rne(acc[i][f][1]) << 16);
+        packed[2 * f + 1] = (uint32_t)f32_to_bf16_rne(acc[i][f][2]) | ((uint32_t)f32_to_bf16_rne(acc[i][f][3]) << 16);
+      }
+      uint16_t* drow = D + (int64_t)row * p.ldd;
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int c = col0 + 8 * h;
-      if (vec_ok && c + 8 <= p.N) {
-        *reinterpret_cast<i32x4*>(drow + c) =
-            i32x4{(int)packed[4 * h], (int)packed[4 * h + 1], (int)packed[4 * h + 2], (int)packed[4 * h + 3]};
-      } else {
+      for (int h = 0; h < 2; ++h) {
+        const int c = col0 + 8 * h;
+        if (vec_ok && c + 8 <= p.N) {
+          *reinterpret_cast<i32x4*>(drow + c) =
+              i32x4{(int)packed[4 * h], (int)packed[4 * h + 1], (int)packed[4 * h + 2], (int)packed[4 * h + 3]};
+        } else {
 #pragma unroll
-        for (int e = 0; e < 8; ++e)
-          if (c + e < p.N) drow[c + e] = (uint16_t)(packed[4 * h + e / 2] >> (16 * (e & 1)));
+          for (int e = 0; e < 8; ++e)
+            if (c + e < p.N) drow[c + e] = (uint16_t)(packed[4 * h + e / 2] >> (16 * (e & 1)));
+        }
       }
     }
   }
@@ -634,8 +744,9 @@ using TileL = TileShape<256, 256, 2, 4, 2>;  // 512 threads, wave tile 128 x 64,
 using TileW = TileShape<128, 256, 2, 4, 3>;  // 512 threads, wave tile  64 x 64, 3 x 48 KB stages
 using TileS = TileShape<128, 128, 2, 2, 3>;  // 256 threads, wave tile  64 x 64, 3 x 32 KB stages
 using TileT = TileShape<256, 128, 4, 2, 3>;  // 512 threads, wave tile  64 x 64, 3 x 48 KB stages
+using TileN = TileShape<256, 192, 2, 4, 2>;  // 512 threads, wave tile 128 x 48, 2 x 56 KB stages
 
-enum Variant : int { VAR_L = 0, VAR_W = 1, VAR_S = 2, VAR_T = 3 };
+enum Variant : int { VAR_L = 0, VAR_W = 1, VAR_S = 2, VAR_T = 3, VAR_N = 4 };
 
 template <class T, int KIND>
 hipError_t launch_tile(const GemmParams& p, int mode, int sf_fmt, int64_t grid, hipStream_t stream) {
@@ -678,21 +789,107 @@ hipError_t launch_variant(const TileCfg& cfg, const GemmParams& p, int mode, int
     case VAR_L: return launch_tile<TileL, KIND>(p, mode, sf_fmt, grid, stream);
     case VAR_W: return launch_tile<TileW, KIND>(p, mode, sf_fmt, grid, stream);
     case VAR_T: return launch_tile<TileT, KIND>(p, mode, sf_fmt, grid, stream);
+    case VAR_N: return launch_tile<TileN, KIND>(p, mode, sf_fmt, grid, stream);
     default: return launch_tile<TileS, KIND>(p, mode, sf_fmt, grid, stream);
   }
+}
+
+// Launch plan for problems above 128 rows, a pure function of the shapes.
+// The 256 x 256 tile computes whole rounds of one tile per CU; when its tile
+// count leaves the last round partly idle, the 256 x 192 tile may take all
+// columns, or columns [n_split, N) in a second launch after the 256 x 256
+// tile's [0, n_split).  Cost model, in K-loop slices of the 256 x 256 tile
+// (both kinds move 128 bytes of K per slice), from per-wave cycle stamps of
+// the FP8 kernel on 4096 x {4096, 3072, 2112} x {7168, 2048}: a 256 x 192
+// slice costs 0.88 of one (2320 against 2640 cycles); every round adds 7
+// (prologue and epilogue, about 18.6K cycles); a second launch adds 5.7 (the
+// first launch's tail and the launch gap, about 15K cycles).  A round costs
+// rounds(tiles) * (KB * slice + 7).  E.g. M = 4096: N = 2112, K = 7168 goes
+// to 176 tiles of 256 x 192 (63 -> 56.3); BF16 N = 7168, K = 16384 (256
+// slices) splits at 4096 (526 -> 501); N = 7168, K = 2048 stays on 256 x 256.
+// Only the BF16 kind splits: the FP8 kernel runs at the power limit, and in
+// a partly idle last round its busy CUs clock higher (2.03 GHz with 176 of
+// 256 busy, 1.86 with all), which recovers what the second launch would
+// save.  Measured on 4096 x 7168 x 16384, one box, builds alternated: FP8
+// split 390.7 against 391.6 us back to back and 387.6 against 380.4 us in
+// the benchmark's step; BF16 split 3% faster in both.
+constexpr int NUM_CU = 256;
+
+template <int KIND>
+GemmPlan plan_large(int mode, int64_t G, int64_t M, int64_t N, int64_t KB) {
+  const int64_t units = (mode == MODE_MASKED ? G : 1) * ((M + 255) / 256);
+  const double slice_n = 0.88, per_round = 7.0, per_launch = 5.7;
+  auto cost = [&](int64_t cols, int64_t bn, double slice) {
+    const int64_t rounds = (units * ((cols + bn - 1) / bn) + NUM_CU - 1) / NUM_CU;
+    return (double)rounds * ((double)KB * slice + per_round);
+  };
+  GemmPlan best;
+  best.parts = 1;
+  best.n_split = N;
+  best.cfg[0] = make_cfg<TileL, KIND>(VAR_L);
+  double best_cost = cost(N, 256, 1.0);
+  const double only_n = cost(N, 192, slice_n);
+  if (only_n < best_cost) {
+    best_cost = only_n;
+    best.cfg[0] = make_cfg<TileN, KIND>(VAR_N);
+  }
+  for (int64_t n1 = 256; KIND == KIND_BF16 && n1 < N; n1 += 256) {
+    const double c = cost(n1, 256, 1.0) + cost(N - n1, 192, slice_n) + per_launch;
+    if (c < best_cost) {
+      best_cost = c;
+      best.parts = 2;
+      best.n_split = n1;
+      best.cfg[0] = make_cfg<TileL, KIND>(VAR_L);
+      best.cfg[1] = make_cfg<TileN, KIND>(VAR_N);
+    }
+  }
+  return best;
+}
+
+template <int KIND>
+hipError_t launch_plan(const GemmPlan& plan, GemmParams p, int mode, int sf_fmt, hipStream_t stream) {
+  for (int part = 0; part < plan.parts; ++part) {
+    GemmParams q = p;
+    const int64_t n_off = part == 0 ? 0 : plan.n_split;
+    const int64_t n_len = plan.parts == 1 ? p.N : (part == 0 ? plan.n_split : p.N - plan.n_split);
+    if (n_off > 0) {
+      // columns [n_off, N): B rows, the B scale rows of their 128-column
+      // blocks (n_off is a multiple of 256), D and C columns
+      q.b = p.b + n_off * p.ldb;
+      if (KIND == KIND_FP8) q.sfb = static_cast<const uint32_t*>(p.sfb) + (n_off / 128) * p.sfb_sn;
+      q.d = p.d + n_off;
+      if (p.c != nullptr) q.c = static_cast<const uint8_t*>(p.c) + n_off * (p.c_f32 ? 4 : 2);
+    }
+    q.N = (int32_t)n_len;
+    const TileCfg& cfg = plan.cfg[part];
+    q.tiles_m = (q.M + cfg.bm - 1) / cfg.bm;
+    q.tiles_n = (q.N + cfg.bn - 1) / cfg.bn;
+    const int64_t grid = gemm_grid(cfg, mode, q.G, q.M, q.N);
+    if (grid == 0) continue;
+    const hipError_t e = launch_variant<KIND>(cfg, q, mode, sf_fmt, grid, stream);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 }  // namespace
 
 // Tile choice, a pure function of the shapes.  Rows <= 128 (small dense M,
 // decode buffers of up to 128 rows per expert) use 128-row tiles with three
-// stages; everything else the 256 x 256 tile with two stages (three do not
-// fit in LDS), which measured fastest on all the large dense and grouped
-// shapes.
-TileCfg fp8_gemm_config(int mode, int64_t G, int64_t M, int64_t N, int64_t K) {
-  (void)mode; (void)G; (void)K;
-  if (M <= 128) return N <= 128 ? make_cfg<TileS, KIND_FP8>(VAR_S) : make_cfg<TileW, KIND_FP8>(VAR_W);
-  return make_cfg<TileL, KIND_FP8>(VAR_L);
+// stages (one launch); everything else 256-row tiles with two stages (three
+// do not fit in LDS): the 256 x 256 tile, which measured fastest on all the
+// large dense and grouped shapes whose tiles fill whole rounds of the CUs,
+// with the 256 x 192 tile taking all or part of the columns when that fills
+// the last round better (plan_large).
+GemmPlan fp8_gemm_plan(int mode, int64_t G, int64_t M, int64_t N, int64_t K) {
+  if (M <= 128) {
+    GemmPlan p;
+    p.parts = 1;
+    p.n_split = N;
+    p.cfg[0] = N <= 128 ? make_cfg<TileS, KIND_FP8>(VAR_S) : make_cfg<TileW, KIND_FP8>(VAR_W);
+    return p;
+  }
+  return plan_large<KIND_FP8>(mode, G, M, N, (K + BK - 1) / BK);
 }
 
 int64_t gemm_grid(const TileCfg& cfg, int mode, int64_t G, int64_t M, int64_t N) {
@@ -702,30 +899,31 @@ int64_t gemm_grid(const TileCfg& cfg, int mode, int64_t G, int64_t M, int64_t N)
   return (mode == MODE_CONTIG && cfg.bm == 256) ? 2 * tiles : tiles;
 }
 
+int64_t plan_grid(const GemmPlan& plan, int part, int mode, int64_t G, int64_t M, int64_t N) {
+  if (part >= plan.parts) return 0;
+  const int64_t n_len = plan.parts == 1 ? N : (part == 0 ? plan.n_split : N - plan.n_split);
+  return gemm_grid(plan.cfg[part], mode, G, M, n_len);
+}
+
 hipError_t launch_fp8_gemm(GemmParams p, int mode, int sf_fmt, hipStream_t stream) {
-  const TileCfg cfg = fp8_gemm_config(mode, p.G, p.M, p.N, p.k_bytes);
-  p.tiles_m = (p.M + cfg.bm - 1) / cfg.bm;
-  p.tiles_n = (p.N + cfg.bn - 1) / cfg.bn;
-  const int64_t grid = gemm_grid(cfg, mode, p.G, p.M, p.N);
-  if (grid == 0) return hipSuccess;
-  return launch_variant<KIND_FP8>(cfg, p, mode, sf_fmt, grid, stream);
+  return launch_plan<KIND_FP8>(fp8_gemm_plan(mode, p.G, p.M, p.N, p.k_bytes), p, mode, sf_fmt, stream);
 }
 
 // BF16 GEMMs: the same tile choice as the FP8 GEMM (a K-slice is 64 BF16
 // elements instead of 128 FP8 ones, the bytes per tile are the same).
-TileCfg bf16_gemm_config(int mode, int64_t G, int64_t M, int64_t N, int64_t K) {
-  (void)mode; (void)G; (void)K;
-  if (M <= 128) return N <= 128 ? make_cfg<TileS, KIND_BF16>(VAR_S) : make_cfg<TileW, KIND_BF16>(VAR_W);
-  return make_cfg<TileL, KIND_BF16>(VAR_L);
+GemmPlan bf16_gemm_plan(int mode, int64_t G, int64_t M, int64_t N, int64_t K) {
+  if (M <= 128) {
+    GemmPlan p;
+    p.parts = 1;
+    p.n_split = N;
+    p.cfg[0] = N <= 128 ? make_cfg<TileS, KIND_BF16>(VAR_S) : make_cfg<TileW, KIND_BF16>(VAR_W);
+    return p;
+  }
+  return plan_large<KIND_BF16>(mode, G, M, N, (2 * K + BK - 1) / BK);
 }
 
 hipError_t launch_bf16_gemm(GemmParams p, int mode, hipStream_t stream) {
-  const TileCfg cfg = bf16_gemm_config(mode, p.G, p.M, p.N, p.k_bytes / 2);
-  p.tiles_m = (p.M + cfg.bm - 1) / cfg.bm;
-  p.tiles_n = (p.N + cfg.bn - 1) / cfg.bn;
-  const int64_t grid = gemm_grid(cfg, mode, p.G, p.M, p.N);
-  if (grid == 0) return hipSuccess;
-  return launch_variant<KIND_BF16>(cfg, p, mode, SF_F32, grid, stream);
+  return launch_plan<KIND_BF16>(bf16_gemm_plan(mode, p.G, p.M, p.N, p.k_bytes / 2), p, mode, SF_F32, stream);
 }
 
 }  // namespace dgmi

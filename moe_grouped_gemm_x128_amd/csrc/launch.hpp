@@ -42,11 +42,21 @@ hipError_t launch_per_token(const QuantArgs& p, hipStream_t stream);
 hipError_t launch_per_block(const QuantArgs& p, hipStream_t stream);
 hipError_t launch_pack_ue8m0(const PackArgs& p, hipStream_t stream);
 
-// GEMMs: the tile for (mode, G, M, N, K) and the grid it launches (pure
+// Launch plan of a GEMM: one launch over all N columns, or two launches on
+// the same stream, cfg[0] over columns [0, n_split) and cfg[1] over
+// [n_split, N) (n_split a multiple of 256).
+struct GemmPlan {
+  TileCfg cfg[2];
+  int64_t n_split;
+  int parts;
+};
+
+// GEMMs: the plan for (mode, G, M, N, K) and the grid of each launch (pure
 // functions of the shapes), and the launchers.
-TileCfg fp8_gemm_config(int mode, int64_t G, int64_t M, int64_t N, int64_t K);
-TileCfg bf16_gemm_config(int mode, int64_t G, int64_t M, int64_t N, int64_t K);
+GemmPlan fp8_gemm_plan(int mode, int64_t G, int64_t M, int64_t N, int64_t K);
+GemmPlan bf16_gemm_plan(int mode, int64_t G, int64_t M, int64_t N, int64_t K);
 int64_t gemm_grid(const TileCfg& cfg, int mode, int64_t G, int64_t M, int64_t N);
+int64_t plan_grid(const GemmPlan& plan, int part, int mode, int64_t G, int64_t M, int64_t N);
 hipError_t launch_fp8_gemm(GemmParams p, int mode, int sf_fmt, hipStream_t stream);
 // BF16 GEMMs: same kernel body; byte strides in p, no scales
 hipError_t launch_bf16_gemm(GemmParams p, int mode, hipStream_t stream);

@@ -73,13 +73,14 @@ def test_bf16_gemm_validation_errors(lib):
 def test_query_config_is_a_pure_function_of_shapes(lib):
     c = binding.query_config(binding.DG_KIND_DENSE, 1, 4096, 2112, 7168)
     assert c == binding.query_config(binding.DG_KIND_DENSE, 1, 4096, 2112, 7168)
-    assert c["grid"] == -(-4096 // c["block_m"]) * -(-2112 // c["block_n"])
+    assert c["grid"] == -(-4096 // c["block_m"]) * -(-c["n_split"] // c["block_n"])
     m = binding.query_config(binding.DG_KIND_MASKED, 32, 256, 4096, 7168)
-    assert m["grid"] == 32 * -(-256 // m["block_m"]) * -(-4096 // m["block_n"])
+    assert m["grid"] == 32 * -(-256 // m["block_m"]) * -(-m["n_split"] // m["block_n"])
     b = binding.query_config(binding.DG_KIND_BF16_MASKED, 64, 128, 7168, 2048)
-    assert b["grid"] == 64 * -(-128 // b["block_m"]) * -(-7168 // b["block_n"])
+    assert b["grid"] == 64 * -(-128 // b["block_m"]) * -(-b["n_split"] // b["block_n"])
     bd = binding.query_config(binding.DG_KIND_BF16_DENSE, 1, 4096, 7168, 2048)
-    assert bd["grid"] == -(-4096 // bd["block_m"]) * -(-7168 // bd["block_n"])
+    assert bd["grid"] == -(-4096 // bd["block_m"]) * -(-bd["n_split"] // bd["block_n"])
+    assert bd["grid2"] == (-(-4096 // bd["block_m"]) * -(-(7168 - bd["n_split"]) // bd["block_n2"]) if bd["block_n2"] else 0)
     c = binding.query_config(binding.DG_KIND_CONTIGUOUS, 4, 32768, 4096, 7168)
     bc = binding.query_config(binding.DG_KIND_BF16_CONTIGUOUS, 4, 32768, 4096, 7168)
     tiles = -(-32768 // c["block_m"]) * -(-4096 // c["block_n"])
@@ -87,6 +88,45 @@ def test_query_config_is_a_pure_function_of_shapes(lib):
     assert c["grid"] == (2 * tiles if c["block_m"] == 256 else tiles) and bc["grid"] == c["grid"]
     with pytest.raises(binding.DgmiError):
         binding.query_config(9, 1, 1, 1, 1)
+
+
+@pytest.mark.parametrize("N,K,fp8_plan,bf16_plan", [
+    # 144 tiles of 256 x 256 fill 56% of one round: 176 of 256 x 192
+    (2112, 7168, (192, 2112, 0), (192, 2112, 0)),
+    (24576, 1536, (256, 24576, 0), (256, 24576, 0)),    # 6 whole rounds
+    # 1.75 rounds: BF16 splits into 256 tiles of 256 x 256, then 256 of
+    # 256 x 192; the FP8 kernel gains nothing from it (power-limited clock)
+    (7168, 16384, (256, 7168, 0), (256, 4096, 192)),
+    (4096, 7168, (256, 4096, 0), (256, 4096, 0)),        # one whole round
+    (7168, 2048, (256, 7168, 0), (256, 7168, 0)),        # too few K-slices to pay for a second launch
+])
+def test_launch_plan_of_the_dense_v3_shapes(lib, N, K, fp8_plan, bf16_plan):
+    """The launch plan fills whole rounds of one workgroup per compute unit
+    (256): one launch of the 256 x 256 or of the 256 x 192 tile, or (BF16)
+    columns [0, n_split) on the first and [n_split, N) on the second."""
+    for kind, plan in ((binding.DG_KIND_DENSE, fp8_plan), (binding.DG_KIND_BF16_DENSE, bf16_plan)):
+        block_n, n_split, block_n2 = plan
+        c = binding.query_config(kind, 1, 4096, N, K)
+        assert (c["block_m"], c["block_n"], c["n_split"], c["block_n2"]) == (256, block_n, n_split, block_n2)
+        assert c["grid"] == 16 * -(-n_split // block_n)
+        assert c["grid2"] == (16 * -(-(N - n_split) // block_n2) if block_n2 else 0)
+        assert c["lds_bytes"] <= 160 * 1024 and c["lds_bytes2"] <= 160 * 1024
+
+
+def test_launch_plan_of_the_grouped_shapes(lib):
+    # masked decode, 32 experts x 256 rows: whole rounds of 256 x 256 at
+    # N = 4096; at N = 7168 (3.5 rounds, 16 K-slices) a split does not pay
+    m = binding.query_config(binding.DG_KIND_MASKED, 32, 256, 4096, 7168)
+    assert (m["block_n"], m["n_split"], m["block_n2"], m["grid"]) == (256, 4096, 0, 512)
+    m = binding.query_config(binding.DG_KIND_MASKED, 32, 256, 7168, 2048)
+    assert (m["block_n"], m["n_split"], m["block_n2"], m["grid"], m["grid2"]) == (256, 7168, 0, 896, 0)
+    # contiguous prefill: whole rounds of 256 x 256 (plus the second grid copy)
+    for N in (4096, 7168):
+        c = binding.query_config(binding.DG_KIND_CONTIGUOUS, 4, 32768, N, 7168)
+        assert (c["block_n"], c["n_split"], c["block_n2"], c["grid"]) == (256, N, 0, 2 * 128 * N // 256)
+    # rows <= 128: one launch of a 128-row tile
+    s = binding.query_config(binding.DG_KIND_MASKED, 64, 128, 7168, 2048)
+    assert (s["block_m"], s["n_split"], s["block_n2"], s["grid2"]) == (128, 7168, 0, 0)
 
 
 def _t(shape, dtype, stride=None):

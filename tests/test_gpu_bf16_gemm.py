@@ -31,11 +31,28 @@ def _sentinel(shape):
     return torch.full(shape, SENTINEL_BF16, dtype=torch.int16, device="cuda").view(torch.bfloat16)
 
 
+# one whole round of 256 x 256 tiles, and the split plan (256 x 256 tiles on
+# columns [0, 4096), 256 x 192 on [4096, 7100), last tile 124 columns)
+PLAN_L = (4000, 4000, 128)
+PLAN_SPLIT = (4000, 7100, 4096)  # 64 K-slices of 64 BF16 elements
+
+
+def _expect_plan(M, N, K):
+    from moe_grouped_gemm_x128_amd import binding
+
+    c = binding.query_config(binding.DG_KIND_BF16_DENSE, 1, M, N, K)
+    if (M, N) == PLAN_L[:2]:
+        assert (c["block_m"], c["block_n"], c["block_n2"]) == (256, 256, 0)
+    elif (M, N) == PLAN_SPLIT[:2]:
+        assert (c["block_n"], c["n_split"], c["block_n2"]) == (256, 4096, 192)
+
+
 @pytest.mark.parametrize("M,N,K", [(128, 256, 512), (200, 300, 384), (1, 130, 64), (257, 64, 256),
-                                   (64, 2112, 1024), (96, 100, 640), (300, 520, 192)])
+                                   (64, 2112, 1024), (96, 100, 640), (300, 520, 192), PLAN_L])
 def test_bf16_dense_full_compare(M, N, K):
     say(f"bf16_gemm_nt M={M} N={N} K={K}")
     mg = _mg()
+    _expect_plan(M, N, K)
     ab = synth.bf16_bits_from_f32(synth.normal_f32(181, (M, K)))
     bb = synth.bf16_bits_from_f32(synth.normal_f32(182, (N, K)))
     d = _sentinel((M, N))
@@ -44,10 +61,11 @@ def test_bf16_dense_full_compare(M, N, K):
     assert_bf16_close(to_host(d), oracle.bf16_gemm_nt(ab, bb), f"bf16 dense {M}x{N}x{K}")
 
 
+@pytest.mark.parametrize("M,N,K", [(200, 300, 256), PLAN_L])
 @pytest.mark.parametrize("c_kind", ["bf16", "f32", "inplace"])
-def test_bf16_dense_accumulate_c(c_kind):
-    M, N, K = 200, 300, 256
-    say(f"bf16_gemm_nt accumulate c={c_kind}")
+def test_bf16_dense_accumulate_c(M, N, K, c_kind):
+    say(f"bf16_gemm_nt accumulate M={M} N={N} K={K} c={c_kind}")
+    _expect_plan(M, N, K)
     mg = _mg()
     ab = synth.bf16_bits_from_f32(synth.normal_f32(183, (M, K)))
     bb = synth.bf16_bits_from_f32(synth.normal_f32(184, (N, K)))
@@ -64,6 +82,35 @@ def test_bf16_dense_accumulate_c(c_kind):
     mg.bf16_gemm_nt(_dev_bf16(ab), _dev_bf16(bb), c, d)
     torch.cuda.synchronize()
     assert_bf16_close(to_host(d), oracle.bf16_gemm_nt(ab, bb, c=cref), f"bf16 accumulate {c_kind}")
+
+
+@pytest.mark.parametrize("c_kind", [None, "bf16", "f32", "inplace"])
+def test_bf16_dense_split_plan_sampled_rows(c_kind):
+    """The two-launch plan (256 x 256 tiles on columns [0, 4096), 256 x 192
+    on [4096, 7100), the second launch's B rows, D and C columns offset on
+    the host); every column compared on sampled rows."""
+    M, N, K = PLAN_SPLIT
+    say(f"bf16_gemm_nt split plan {M}x{N}x{K} c={c_kind}")
+    _expect_plan(M, N, K)
+    mg = _mg()
+    ab = synth.bf16_bits_from_f32(synth.normal_f32(191, (M, K)))
+    bb = synth.bf16_bits_from_f32(synth.normal_f32(192, (N, K)))
+    c, cref = None, None
+    if c_kind is not None:
+        xc = synth.normal_f32(193, (M, N)) * np.float32(16.0)
+        if c_kind == "f32":
+            c = to_dev(xc)
+            cref = xc.astype(np.float64)
+        else:
+            cbits = synth.bf16_bits_from_f32(xc)
+            cref = oracle.bf16_decode(cbits)
+            c = _dev_bf16(cbits)
+    d = c if c_kind == "inplace" else _sentinel((M, N))
+    mg.bf16_gemm_nt(_dev_bf16(ab), _dev_bf16(bb), c, d)
+    torch.cuda.synchronize()
+    rows = np.unique(np.concatenate([np.random.default_rng(194).choice(M, 32, replace=False), [0, M - 1]]))
+    ref = oracle.bf16_gemm_nt(ab[rows], bb, c=None if cref is None else cref[rows])
+    assert_bf16_close(to_host(d)[rows], ref, f"bf16 split plan c={c_kind}")
 
 
 def test_bf16_dense_large_sampled():
@@ -86,13 +133,20 @@ def test_bf16_dense_large_sampled():
     assert_bf16_close(to_host(d)[rows], ref, "bf16 dense large sampled")
 
 
-@pytest.mark.parametrize("layout", [[2, -1, 0, 2, 1, -1, 5], [0, 1, 1, 0, -1, 1, 0, -1, -1, 1]])
-def test_bf16_contiguous_skips_and_mixed_tiles(layout):
-    say(f"m_grouped_bf16_gemm_nt_contiguous layout={layout}")
+@pytest.mark.parametrize("layout,N", [([2, -1, 0, 2, 1, -1, 5], 300), ([0, 1, 1, 0, -1, 1, 0, -1, -1, 1], 300),
+                                      # 256 x 256 tile: 32 blocks x 4096 columns, one whole round
+                                      ([0, 1, 1, 0, -1, 1, 0, -1, -1, 1, 2, 2, 5, 2, 0, 0] * 2, 4096)])
+def test_bf16_contiguous_skips_and_mixed_tiles(layout, N):
+    say(f"m_grouped_bf16_gemm_nt_contiguous N={N} layout={layout}")
     mg = _mg()
     layout = np.array(layout, dtype=np.int32)
-    G, N, K = 3, 300, 192
+    G, K = 3, 192 if N < 4096 else 64
     Msum = layout.size * 128
+    if N == 4096:
+        from moe_grouped_gemm_x128_amd import binding
+
+        c = binding.query_config(binding.DG_KIND_BF16_CONTIGUOUS, G, Msum, N, K)
+        assert (c["block_m"], c["block_n"], c["block_n2"]) == (256, 256, 0)
     ab = synth.bf16_bits_from_f32(synth.normal_f32(189, (Msum, K)))
     bb = synth.bf16_bits_from_f32(synth.normal_f32(190, (G, N, K)))
     d = _sentinel((Msum, N))

@@ -28,10 +28,17 @@ def _dev_bf16(bits):
     (3, 200, 128, 64, [200, 199, 1000]),
     (2, 16, 1000, 512, [-4, 16]),
     (2, 256, 384, 320, [256, 130]),
+    # 256 x 256 tile (one whole round: 16 experts x 4096 columns)
+    (16, 256, 4096, 64, [0, 17, 256, 999, -3, 129, 128, 200, 1, 255, 64, 130, 250, 16, 0, 192]),
 ])
 def test_bf16_masked_full_compare(G, max_m, N, K, mm):
     say(f"bf16 masked G={G} max_m={max_m} N={N} K={K} masked_m={mm}")
     mg = _mg()
+    if G == 16:
+        from moe_grouped_gemm_x128_amd import binding
+
+        c = binding.query_config(binding.DG_KIND_BF16_MASKED, G, max_m, N, K)
+        assert (c["block_m"], c["block_n"], c["block_n2"]) == (256, 256, 0)
     mm = np.array(mm, dtype=np.int32)
     ab = synth.bf16_bits_from_f32(synth.normal_f32(151, (G, max_m, K)))
     bb = synth.bf16_bits_from_f32(synth.normal_f32(152, (G, N, K)))

@@ -56,11 +56,29 @@ def sentinel_like(shape):
 # dense
 # ---------------------------------------------------------------------------
 
+# Shapes of every launch plan of the FP8 GEMM, with ragged M and N: rows
+# <= 128 (128-row tiles), one launch of the 256 x 192 tile (below one round
+# of tiles) and one whole round of 256 x 256 tiles (4000 x 4000).
+PLAN_L = (4000, 4000, 256)
+
+
+def _expect_plan(kind, M, N, K):
+    from moe_grouped_gemm_x128_amd import binding
+
+    c = binding.query_config(getattr(binding, kind), 1, M, N, K)
+    if (M, N) == PLAN_L[:2]:
+        assert (c["block_m"], c["block_n"], c["block_n2"]) == (256, 256, 0)
+    elif M > 128:
+        assert (c["block_m"], c["block_n"], c["block_n2"]) == (256, 192, 0)
+    return c
+
+
 @pytest.mark.parametrize("M,N,K", [(128, 256, 512), (200, 300, 384), (1, 130, 128), (257, 64, 256), (64, 2112, 1024),
-                                   (96, 100, 640), (128, 128, 384)])
+                                   (96, 100, 640), (128, 128, 384), PLAN_L])
 def test_dense_full_compare(M, N, K):
     say(f"fp8_gemm_nt M={M} N={N} K={K}")
     mg = _mg()
+    _expect_plan("DG_KIND_DENSE", M, N, K)
     xa = synth.normal_f32(101, (M, K))
     xb = synth.normal_f32(102, (N, K))
     a, sfa = q_tok(to_dev(xa))
@@ -75,16 +93,17 @@ def test_dense_full_compare(M, N, K):
     assert_bf16_close(to_host(d), ref, f"dense {M}x{N}x{K}")
 
 
-def test_dense_ue8m0_packed_scales():
-    say("fp8_gemm_nt UE8M0 packed scales")
+@pytest.mark.parametrize("M,N,K", [(192, 384, 1024), (PLAN_L[0], PLAN_L[1], 512)])
+def test_dense_ue8m0_packed_scales(M, N, K):
+    say(f"fp8_gemm_nt UE8M0 packed scales M={M} N={N} K={K}")
     mg = _mg()
-    M, N, K = 192, 384, 1024
+    _expect_plan("DG_KIND_DENSE", M, N, K)
     xa = synth.normal_f32(111, (M, K))
     xb = synth.normal_f32(112, (N, K))
     a, sfa = q_tok(to_dev(xa), ue8m0=True)
     b, sfb = q_blk(to_dev(xb), ue8m0=True)
     pa = torch.empty((M, K // 512), dtype=torch.int32, device="cuda")
-    pb = torch.empty((N // 128, K // 512), dtype=torch.int32, device="cuda")
+    pb = torch.empty((-(-N // 128), K // 512), dtype=torch.int32, device="cuda")
     mg.pack_ue8m0_to_int(sfa.contiguous(), pa)
     mg.pack_ue8m0_to_int(sfb, pb)
     d = sentinel_like((M, N))
@@ -100,17 +119,18 @@ def test_dense_ue8m0_packed_scales():
     assert_bf16_close(to_host(d), ref, "dense ue8m0")
 
 
-def test_dense_one_hot_closed_form_bit_exact():
+@pytest.mark.parametrize("M,N,K", [(160, 272, 768), PLAN_L])
+def test_dense_one_hot_closed_form_bit_exact(M, N, K):
     """B one-hot (column n reads K index kn[n]) and power-of-two scales: every
     output is sfa*sfb*A[m, kn[n]] exactly, representable in bf16, so the
     device result must match bit for bit; this pins the A/B/scale indexing
-    and the MFMA fragment layout."""
-    say("fp8_gemm_nt one-hot closed form")
+    and the MFMA fragment layout of each launch plan."""
+    say(f"fp8_gemm_nt one-hot closed form M={M} N={N} K={K}")
     mg = _mg()
+    _expect_plan("DG_KIND_DENSE", M, N, K)
     rng = np.random.default_rng(23)
-    M, N, K = 160, 272, 768
     a = (rng.integers(0, 0x7E, size=(M, K)) | (rng.integers(0, 2, size=(M, K)) << 7)).astype(np.uint8)
-    kn = rng.permutation(K)[:N]
+    kn = rng.integers(0, K, size=N) if N > K else rng.permutation(K)[:N]
     b = np.zeros((N, K), dtype=np.uint8)
     b[np.arange(N), kn] = 0x38
     sfa = np.exp2(rng.integers(-6, 6, size=(M, K // 128))).astype(np.float32)
@@ -161,7 +181,7 @@ def test_dense_v3_shapes_sampled(i):
         assert_bf16_close(dh[rows][:, cols], ref, f"dense {M}x{N}x{K} col block {nb}")
 
 
-@pytest.mark.parametrize("M,N,K", [(200, 300, 384), (64, 2112, 1024), (130, 130, 256)])
+@pytest.mark.parametrize("M,N,K", [(200, 300, 384), (64, 2112, 1024), (130, 130, 256), PLAN_L])
 @pytest.mark.parametrize("c_kind", ["bf16", "f32", "inplace"])
 def test_dense_accumulate_c(M, N, K, c_kind):
     """D = C + A . B^T ("DeepInside DeepGEMM", section 4): C in BF16 or FP32,
@@ -245,6 +265,35 @@ def test_contiguous_mixed_groups_in_one_tile():
     assert_bf16_close(got[written], ref[written], "contiguous alternating")
 
 
+def test_contiguous_mixed_groups_256x256_tile():
+    """Skipped blocks, out-of-range ids and tiles split between two groups on
+    the 256 x 256 tile (32 blocks x 4096 columns: one whole round of tiles),
+    compared in full."""
+    say("contiguous mixed groups, 256 x 256 tile")
+    mg = _mg()
+    from moe_grouped_gemm_x128_amd import binding
+
+    G, N, K = 3, 4096, 128
+    layout = np.array([0, 1, 1, 0, -1, 1, 0, -1, -1, 1, 2, 2, 5, 2, 0, 0] * 2, dtype=np.int32)
+    Msum = layout.size * 128
+    c = binding.query_config(binding.DG_KIND_CONTIGUOUS, G, Msum, N, K)
+    assert (c["block_m"], c["block_n"], c["block_n2"]) == (256, 256, 0)
+    xa = synth.normal_f32(125, (Msum, K))
+    xb = synth.normal_f32(126, (G, N, K))
+    a, sfa = q_tok(to_dev(xa))
+    b, sfb = q_blk(to_dev(xb))
+    d = sentinel_like((Msum, N))
+    mg.m_grouped_fp8_gemm_nt_contiguous(a, b, sfa, sfb, d, to_dev(layout))
+    torch.cuda.synchronize()
+    ra, rsfa = oracle.per_token_cast_to_fp8(xa)
+    rb, rsfb = oracle.per_block_cast_to_fp8(xb)
+    ref_layout = np.where(layout < G, layout, -1)
+    ref, written = oracle.m_grouped_fp8_gemm_nt_contiguous(ra, rb, rsfa, rsfb, ref_layout)
+    got = to_host(d)
+    assert np.all(got[~written] == SENTINEL_BF16)
+    assert_bf16_close(got[written], ref[written], "contiguous 256 x 256 tile")
+
+
 @pytest.mark.parametrize("si", [0, 1])
 def test_contiguous_prefill_full_size_sampled(si):
     N, K = synth.CONTIG["shapes"][si]
@@ -308,6 +357,40 @@ def test_masked_small_sentinel_and_clamp(ue8m0):
     got = to_host(d)
     assert np.all(got[~written] == SENTINEL_BF16)
     assert_bf16_close(got[written], ref[written], "masked small")
+
+
+@pytest.mark.parametrize("ue8m0", [False, True])
+def test_masked_sentinel_and_clamp_256x256_tile(ue8m0):
+    """masked_m of 0, within the first 128 rows (the waves of rows 128..255
+    compute nothing), exactly 128, full, beyond max_m and negative, on the
+    256 x 256 tile (16 experts x 4096 columns: one whole round)."""
+    say(f"masked 256 x 256 tile ue8m0={ue8m0}")
+    mg = _mg()
+    from moe_grouped_gemm_x128_amd import binding
+
+    G, max_m, N, K = 16, 256, 4096, 128
+    mm = np.array([0, 17, 256, 999, -3, 129, 128, 200, 1, 255, 64, 130, 250, 16, 0, 192], dtype=np.int32)
+    c = binding.query_config(binding.DG_KIND_MASKED, G, max_m, N, K)
+    assert (c["block_m"], c["block_n"], c["block_n2"]) == (256, 256, 0)
+    xa = synth.normal_f32(133, (G, max_m, K))
+    xb = synth.normal_f32(134, (G, N, K))
+    a, sfa = q_tok(to_dev(xa), ue8m0)
+    b, sfb = q_blk(to_dev(xb), ue8m0)
+    if ue8m0:
+        pa = torch.empty((G, max_m, 1), dtype=torch.int32, device="cuda")
+        pb = torch.empty((G, N // 128, 1), dtype=torch.int32, device="cuda")
+        mg.pack_ue8m0_to_int(sfa, pa)
+        mg.pack_ue8m0_to_int(sfb, pb)
+        sfa, sfb = pa, pb
+    d = sentinel_like((G, max_m, N))
+    mg.m_grouped_fp8_gemm_nt_masked(a, b, sfa, sfb, d, to_dev(mm), max_m)
+    torch.cuda.synchronize()
+    ra, rsfa = oracle.per_token_cast_to_fp8(xa, ue8m0)
+    rb, rsfb = oracle.per_block_cast_to_fp8(xb, ue8m0)
+    ref, written = oracle.m_grouped_fp8_gemm_nt_masked(ra, rb, rsfa, rsfb, mm, max_m)
+    got = to_host(d)
+    assert np.all(got[~written] == SENTINEL_BF16)
+    assert_bf16_close(got[written], ref[written], "masked 256 x 256 tile")
 
 
 def test_masked_2d_views_and_all_zero():
