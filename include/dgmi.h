@@ -51,7 +51,7 @@ enum {
 enum {
   DG_OK = 0,
   DG_INVALID_ARG = 1,   /* null / dtype / ndim / shape / stride / alignment / aliasing */
-  DG_UNSUPPORTED = 2,   /* legal but not implemented (K % 128 != 0) */
+  DG_UNSUPPORTED = 2,   /* legal but not implemented (K % 128 != 0; GEMM operand row strides of 8 MiB or more) */
   DG_LAUNCH_FAILED = 3  /* the HIP runtime rejected a launch */
 };
 

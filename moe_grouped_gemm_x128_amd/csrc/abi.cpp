@@ -165,6 +165,17 @@ int check_scales(const dg_tensor* t, const char* name, int sf_fmt, int64_t G_exp
   return DG_OK;
 }
 
+// The kernels address a tile of up to 256 rows of A or B with 32-bit buffer
+// offsets (row * row stride + K offset): row strides (bytes) must stay below
+// 2^31 / 256, i.e. 8 MiB.
+int check_row_strides(int64_t lda_bytes, int64_t ldb_bytes, const char* fname) {
+  constexpr int64_t kMax = INT32_MAX / 256;
+  if (lda_bytes > kMax || ldb_bytes > kMax)
+    return fail(DG_UNSUPPORTED, "%s: row strides of a and b must be below %lld bytes (got %lld, %lld)", fname,
+                (long long)kMax, (long long)lda_bytes, (long long)ldb_bytes);
+  return DG_OK;
+}
+
 int check_launch(hipError_t e, const char* what) {
   if (e != hipSuccess) return fail(DG_LAUNCH_FAILED, "%s: launch failed: %s", what, hipGetErrorString(e));
   return ok();
@@ -223,6 +234,7 @@ int fp8_gemm_common(int mode, const dg_tensor* a, const dg_tensor* b, const dg_t
   // alignment: 16-B operand rows (the kernels load 16-B chunks), 16-B output rows
   if (!aligned(a->data, 16) || !aligned(b->data, 16) || va.sr % 16 || vb.sr % 16 || va.sg % 16 || vb.sg % 16)
     return fail(DG_INVALID_ARG, "%s: a and b need 16-byte aligned bases and row/group strides", fname);
+  DG_TRY(check_row_strides(va.sr, vb.sr, fname));
   if (!aligned(d->data, 2)) return fail(DG_INVALID_ARG, "%s: d must be 2-byte aligned", fname);
   if (!aligned(sfa->data, 4) || !aligned(sfb->data, 4)) return fail(DG_INVALID_ARG, "%s: scales must be 4-byte aligned", fname);
 
@@ -379,6 +391,7 @@ int bf16_gemm_common(int mode, const dg_tensor* a, const dg_tensor* b, const dg_
   if (K % 64 != 0) return fail(DG_UNSUPPORTED, "%s: K = %lld is not a multiple of 64", fname, (long long)K);
   if (!aligned(a->data, 16) || !aligned(b->data, 16) || va.sr % 8 || vb.sr % 8 || va.sg % 8 || vb.sg % 8)
     return fail(DG_INVALID_ARG, "%s: a and b need 16-byte aligned bases and row/group strides", fname);
+  DG_TRY(check_row_strides(2 * va.sr, 2 * vb.sr, fname));
   if (!aligned(d->data, 2)) return fail(DG_INVALID_ARG, "%s: d must be 2-byte aligned", fname);
   if (mode == dgmi::MODE_CONTIG) {
     if (M % 128 != 0) return fail(DG_INVALID_ARG, "%s: Msum = %lld is not a multiple of 128", fname, (long long)M);

@@ -178,6 +178,10 @@ def test_dense_validation_errors(lib):
     ab = _t((M, K + 8), torch.uint8)[:, :K]
     assert _call_dense(lib, ab, b, sfa, sfb, d) == binding.DG_INVALID_ARG
     assert "aligned" in binding.last_error()
+    # a row stride whose 256-row tile would overflow the kernels' 32-bit offsets
+    wide = _t((2, K), torch.uint8, stride=(1 << 23, 1))
+    assert _call_dense(lib, wide, b, _t((2, K // 128), torch.float32), sfb, _t((2, N), torch.bfloat16)) == binding.DG_UNSUPPORTED
+    assert "row strides" in binding.last_error()
 
 
 def test_masked_validation_errors(lib):
@@ -236,3 +240,41 @@ def test_quantizer_and_pack_validation_errors(lib):
     assert lib.pack_ue8m0_to_int(ctypes.byref(D(s)), ctypes.byref(D(_t((3, 2), torch.int32))), None, None) == binding.DG_INVALID_ARG
     assert lib.pack_ue8m0_to_int(ctypes.byref(D(s)), ctypes.byref(D(_t((3, 3), torch.float32))), None, None) == binding.DG_INVALID_ARG
     assert lib.pack_ue8m0_to_int(None, ctypes.byref(D(_t((3, 3), torch.int32))), None, None) == binding.DG_INVALID_ARG
+
+
+def test_empty_problems_return_ok_without_a_launch(lib):
+    """Zero rows, columns or groups are legal and launch nothing (here, with
+    no GPU, any launch would fail and return LAUNCH_FAILED)."""
+    D = binding.describe
+    K = 256
+    f32, u8, bf, i32 = torch.float32, torch.uint8, torch.bfloat16, torch.int32
+    # dense FP8: M = 0, then N = 0
+    assert _call_dense(lib, _t((0, K), u8), _t((64, K), u8), _t((0, 2), f32), _t((1, 2), f32), _t((0, 64), bf)) == 0
+    assert _call_dense(lib, _t((8, K), u8), _t((0, K), u8), _t((8, 2), f32), _t((0, 2), f32), _t((8, 0), bf)) == 0
+    # masked FP8 and BF16 with no groups, and with max_m = 0
+    for G, max_m in ((0, 64), (3, 0)):
+        assert lib.m_grouped_fp8_gemm_nt_masked(
+            ctypes.byref(D(_t((G, max_m, K), u8))), ctypes.byref(D(_t((G, 128, K), u8))),
+            ctypes.byref(D(_t((G, max_m, 2), f32))), ctypes.byref(D(_t((G, 1, 2), f32))),
+            ctypes.byref(D(_t((G, max_m, 128), bf))), ctypes.byref(D(_t((G,), i32))), max_m, None) == 0
+        assert lib.m_grouped_bf16_gemm_nt_masked(
+            ctypes.byref(D(_t((G, max_m, K), bf))), ctypes.byref(D(_t((G, 128, K), bf))),
+            ctypes.byref(D(_t((G, max_m, 128), bf))), ctypes.byref(D(_t((G,), i32))), max_m, None) == 0
+    # contiguous FP8 and BF16 with no rows
+    assert lib.m_grouped_fp8_gemm_nt_contiguous(
+        ctypes.byref(D(_t((0, K), u8))), ctypes.byref(D(_t((2, 128, K), u8))), ctypes.byref(D(_t((0, 2), f32))),
+        ctypes.byref(D(_t((2, 1, 2), f32))), ctypes.byref(D(_t((0, 128), bf))), ctypes.byref(D(_t((0,), i32))),
+        None) == 0
+    assert lib.m_grouped_bf16_gemm_nt_contiguous(
+        ctypes.byref(D(_t((0, K), bf))), ctypes.byref(D(_t((2, 128, K), bf))), ctypes.byref(D(_t((0, 128), bf))),
+        ctypes.byref(D(_t((0,), i32))), None) == 0
+    # dense BF16 with M = 0
+    assert lib.bf16_gemm_nt(ctypes.byref(D(_t((0, K), bf))), ctypes.byref(D(_t((64, K), bf))), None,
+                            ctypes.byref(D(_t((0, 64), bf))), None) == 0
+    # quantizers with no rows, pack with no scales
+    assert lib.per_token_cast_to_fp8(ctypes.byref(D(_t((0, K), f32))), ctypes.byref(D(_t((0, K), u8))),
+                                     ctypes.byref(D(_t((0, 2), f32))), 0, None) == 0
+    assert lib.per_block_cast_to_fp8(ctypes.byref(D(_t((0, K), f32))), ctypes.byref(D(_t((0, K), u8))),
+                                     ctypes.byref(D(_t((0, 2), f32))), 1, None) == 0
+    assert lib.pack_ue8m0_to_int(ctypes.byref(D(_t((3, 0), f32))), ctypes.byref(D(_t((3, 0), i32))), None, None) == 0
+    assert lib.pack_ue8m0_to_int(ctypes.byref(D(_t((0, 8), f32))), ctypes.byref(D(_t((0, 2), i32))), None, None) == 0
