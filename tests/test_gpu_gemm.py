@@ -216,6 +216,39 @@ def test_dense_accumulate_c(M, N, K, c_kind):
         assert np.all(to_host(cbuf)[:, N:] == 0), "the row padding of c/d was written"
 
 
+def test_dense_row_stride_at_the_32bit_offset_limit():
+    """A and B as row views of buffers whose row stride is the largest the
+    library takes (8 MiB - 16 bytes): a 256-row tile then spans just under
+    2^31 bytes of 32-bit buffer offsets; the next stride up is rejected."""
+    say("fp8_gemm_nt row stride 8 MiB - 16")
+    mg = _mg()
+    from moe_grouped_gemm_x128_amd import binding
+
+    M, N, K = 300, 272, 256
+    ld = (1 << 23) - 16
+    xa = synth.normal_f32(161, (M, K))
+    xb = synth.normal_f32(162, (N, K))
+    a_c, sfa = q_tok(to_dev(xa))
+    b_c, sfb = q_blk(to_dev(xb))
+    abuf = torch.zeros(M * ld, dtype=torch.uint8, device="cuda")
+    bbuf = torch.zeros(N * ld, dtype=torch.uint8, device="cuda")
+    a = abuf.as_strided((M, K), (ld, 1))
+    b = bbuf.as_strided((N, K), (ld, 1))
+    a.copy_(a_c)
+    b.copy_(b_c)
+    d = sentinel_like((M, N))
+    mg.fp8_gemm_nt(a, b, sfa, sfb, None, d)
+    torch.cuda.synchronize()
+    ra, rsfa = oracle.per_token_cast_to_fp8(xa)
+    rb, rsfb = oracle.per_block_cast_to_fp8(xb)
+    assert np.array_equal(to_host(a_c), ra) and np.array_equal(to_host(b_c), rb)
+    assert_bf16_close(to_host(d), oracle.fp8_gemm_nt(ra, rb, rsfa, rsfb), "dense row stride 8 MiB - 16")
+    wide = abuf.as_strided((2, K), (ld + 16, 1))
+    with pytest.raises(binding.DgmiError):
+        mg.fp8_gemm_nt(wide, b, sfa[:2], sfb, None, d[:2])
+    del abuf, bbuf
+
+
 # ---------------------------------------------------------------------------
 # contiguous grouped
 # ---------------------------------------------------------------------------
