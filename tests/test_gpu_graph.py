@@ -212,3 +212,48 @@ def test_every_entry_point_replays_under_capture():
     rb, rsfb = oracle.per_block_cast_to_fp8(to_host(xb))
     ref = oracle.fp8_gemm_nt(ra, rb, rsfa, rsfb, c=to_host(cin).astype(np.float64))
     assert_bf16_close(got["d8"], ref, "replayed dense FP8 with C")
+
+
+def test_two_launch_plan_replays_under_capture():
+    """The BF16 GEMM whose launch plan is two launches over column ranges
+    (4000 x 7100 x 4096: 256 x 256 tiles on [0, 4096), 256 x 192 on the
+    rest) captured once and replayed with new inputs; every replay
+    bit-identical to an eager run."""
+    mg = _mg()
+    from moe_grouped_gemm_x128_amd import binding
+
+    M, N, K = 4000, 7100, 4096
+    c = binding.query_config(binding.DG_KIND_BF16_DENSE, 1, M, N, K)
+    assert (c["n_split"], c["block_n2"]) == (4096, 192)
+    a = torch.empty((M, K), dtype=torch.bfloat16, device="cuda")
+    b = torch.empty((N, K), dtype=torch.bfloat16, device="cuda")
+    d = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+
+    def fill(seed):
+        a.copy_(torch.from_numpy(synth.normal_f32(seed, (M, K))))
+        b.copy_(torch.from_numpy(synth.normal_f32(seed + 1, (N, K))))
+        d.view(torch.int16).fill_(SENTINEL_BF16)
+
+    fill(730)
+    mg.bf16_gemm_nt(a, b, None, d)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        graph.capture_begin()
+        mg.bf16_gemm_nt(a, b, None, d)
+        graph.capture_end()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    for r in range(2):
+        say(f"two-launch plan graph replay {r}")
+        fill(740 + 10 * r)
+        graph.replay()
+        torch.cuda.synchronize()
+        got = to_host(d).copy()
+        fill(740 + 10 * r)
+        mg.bf16_gemm_nt(a, b, None, d)
+        torch.cuda.synchronize()
+        assert np.array_equal(to_host(d), got), f"replay {r} differs from eager"
+        assert not np.any(got == SENTINEL_BF16), "elements left unwritten"
