@@ -12,7 +12,14 @@ per-block promotion): with A [M, K] and B [N, K] holding E4M3 codes, sfa
     D[m, n]    = sum_kb P_kb[m, n] * (sfa[m, kb] * sfb[n // 128, kb])
 
 and D is returned as float64 (no bf16 rounding: the comparison allows for
-the device's bf16 output).
+the device's bf16 output).  sfb may instead hold one scale per row of B,
+[N, ceil(K/128)] (the per-row b_sf of the dense example in "DeepInside
+DeepGEMM", section 4), and then
+
+    D[m, n]    = sum_kb P_kb[m, n] * (sfa[m, kb] * sfb[n, kb]);
+
+the form is told by the row count of sfb (N rows with N != ceil(N/128);
+for N = 1 the two forms coincide).
 
 Exactness: every E4M3 value is an integer multiple of 2^-9 below 2^9, so a
 product is an integer multiple of 2^-18 below 2^18 and a 128-term block sum
@@ -42,12 +49,18 @@ def _scaled_block_gemm(a, b, sfa, sfb):
     sfa = np.asarray(sfa, dtype=np.float64)
     sfb = np.asarray(sfb, dtype=np.float64)
     nkb = -(-K // BLOCK)
-    col_block = np.arange(N) // BLOCK  # which row-block of B each output column uses
+    nnb = -(-N // BLOCK)
+    if sfb.shape[0] == N and N != nnb:
+        scale_row = np.arange(N)  # one scale per row of B
+    elif sfb.shape[0] == nnb:
+        scale_row = np.arange(N) // BLOCK  # one scale per 128-row block of B
+    else:
+        raise ValueError(f"sfb has {sfb.shape[0]} rows; expected {nnb} (128x128 blocks) or {N} (per row)")
     D = np.zeros((M, N), dtype=np.float64)
     for kb in range(nkb):
         ks = slice(kb * BLOCK, (kb + 1) * BLOCK)
         P = A[:, ks] @ B[:, ks].T
-        D += P * (sfa[:, kb][:, None] * sfb[col_block, kb][None, :])
+        D += P * (sfa[:, kb][:, None] * sfb[scale_row, kb][None, :])
     return D
 
 
@@ -55,7 +68,8 @@ def fp8_gemm_nt(a, b, sfa, sfb, c=None):
     """Dense D = C + A . B^T with block scales.
 
     a uint8 [M, K], b uint8 [N, K] (E4M3 codes), sfa float [M, ceil(K/128)],
-    sfb float [ceil(N/128), ceil(K/128)], optional c [M, N] (float64).
+    sfb float [ceil(N/128), ceil(K/128)] or, one per row, [N, ceil(K/128)],
+    optional c [M, N] (float64).
     Returns float64 [M, N].
     """
     D = _scaled_block_gemm(np.asarray(a), np.asarray(b), sfa, sfb)

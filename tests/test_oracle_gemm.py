@@ -114,6 +114,79 @@ def test_dense_ue8m0_scales_from_packed():
     assert _close(oracle.fp8_gemm_nt(a, b, ua, ub), _brute(a, b, sfa, sfb))
 
 
+def _brute_rows(a, b, sfa, sfb_rows):
+    """As _brute with one B scale per row: ... * (B[n,k] * sfb[n, k//128])."""
+    A = _torch_e4m3(a).tolist()
+    B = _torch_e4m3(b).tolist()
+    sa = np.asarray(sfa, dtype=np.float64).tolist()
+    sb = np.asarray(sfb_rows, dtype=np.float64).tolist()
+    M, K = len(A), len(A[0])
+    N = len(B)
+    return np.array([[sum((A[m][k] * sa[m][k // 128]) * (B[n][k] * sb[n][k // 128]) for k in range(K))
+                      for n in range(N)] for m in range(M)])
+
+
+def _row_scaled_operands(seed, M, N, K, ue8m0=False):
+    # B quantized per row (1x128 blocks), as the per-token cast does for A
+    xa = synth.normal_f32(seed, (M, K))
+    xb = synth.normal_f32(seed + 1, (N, K))
+    a, sfa = oracle.per_token_cast_to_fp8(xa, ue8m0)
+    b, sfb = oracle.per_token_cast_to_fp8(xb, ue8m0)
+    return a, b, sfa, sfb
+
+
+@pytest.mark.parametrize("M,N,K", [(3, 260, 384), (2, 129, 300), (5, 7, 128)])
+def test_dense_per_row_b_scales_match_brute_force(M, N, K):
+    a, b, sfa, sfb = _row_scaled_operands(27, M, N, K)
+    assert sfb.shape == (N, -(-K // 128))
+    assert _close(oracle.fp8_gemm_nt(a, b, sfa, sfb), _brute_rows(a, b, sfa, sfb))
+
+
+def test_dense_per_row_b_scales_constant_per_block_equal_block_scales():
+    # a per-row grid that repeats each 128-row block's scale is the block form
+    a, b, sfa, sfb = _random_operands(28, 4, 300, 384)
+    rows = np.repeat(sfb, 128, axis=0)[:300]
+    assert np.array_equal(oracle.fp8_gemm_nt(a, b, sfa, rows), oracle.fp8_gemm_nt(a, b, sfa, sfb))
+    with pytest.raises(ValueError):
+        oracle.fp8_gemm_nt(a, b, sfa, rows[:299])
+
+
+def test_dense_per_row_b_scales_one_hot_closed_form():
+    rng = np.random.default_rng(29)
+    M, N, K = 5, 200, 384
+    a = rng.integers(0, 0x7E, size=(M, K)).astype(np.uint8) | (rng.integers(0, 2, size=(M, K)).astype(np.uint8) << 7)
+    kn = rng.permutation(K)[:N]
+    b = np.zeros((N, K), dtype=np.uint8)
+    b[np.arange(N), kn] = 0x38
+    sfa = np.exp2(rng.integers(-8, 8, size=(M, K // 128))).astype(np.float32)
+    sfb = np.exp2(rng.integers(-8, 8, size=(N, K // 128))).astype(np.float32)
+    got = oracle.fp8_gemm_nt(a, b, sfa, sfb)
+    A = _torch_e4m3(a)
+    want = np.empty((M, N))
+    for n in range(N):
+        k = kn[n]
+        want[:, n] = A[:, k] * sfa[:, k // 128] * sfb[n, k // 128]
+    assert np.array_equal(got, want)
+
+
+def test_grouped_per_row_b_scales_equal_dense_per_group():
+    G, max_m, N, K = 2, 5, 140, 256
+    xa = synth.normal_f32(61, (G, max_m, K))
+    xb = synth.normal_f32(62, (G, N, K))
+    a, sfa = oracle.per_token_cast_to_fp8(xa)
+    b, sfb = oracle.per_token_cast_to_fp8(xb)  # [G, N, K/128]
+    d, w = oracle.m_grouped_fp8_gemm_nt_masked(a, b, sfa, sfb, np.array([3, 5]), max_m)
+    for g, v in ((0, 3), (1, 5)):
+        assert np.array_equal(d[g, :v], oracle.fp8_gemm_nt(a[g, :v], b[g], sfa[g, :v], sfb[g]))
+        assert _close(d[g, :v], _brute_rows(a[g, :v], b[g], sfa[g, :v], sfb[g]))
+    layout = np.array([1, 0], dtype=np.int32)
+    ac, sfac = oracle.per_token_cast_to_fp8(synth.normal_f32(63, (256, K)))
+    dc, wc = oracle.m_grouped_fp8_gemm_nt_contiguous(ac, b, sfac, sfb, layout)
+    assert wc.all()
+    assert np.array_equal(dc[:128], oracle.fp8_gemm_nt(ac[:128], b[1], sfac[:128], sfb[1]))
+    assert np.array_equal(dc[128:], oracle.fp8_gemm_nt(ac[128:], b[0], sfac[128:], sfb[0]))
+
+
 def _masked_case(seed, G, max_m, N, K):
     xa = synth.normal_f32(seed, (G, max_m, K))
     xb = synth.normal_f32(seed + 1, (G, N, K))
