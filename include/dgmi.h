@@ -77,15 +77,19 @@ int dgmi_init(void);
  *   b   E4M3 [N, K]          weights in NT layout (K contiguous)
  *   sfa F32  [M, K/128]      any strides (K-major or M-major), or
  *       I32  [M, ceil(K/512)] packed UE8M0 (byte j of word i: K-block 4i+j)
- *   sfb F32  [ceil(N/128), K/128] or I32 [ceil(N/128), ceil(K/512)]
- *       sfa and sfb must use the same format.
+ *   sfb F32  [ceil(N/128), K/128] or I32 [ceil(N/128), ceil(K/512)]: one
+ *       scale per 128x128 block of B; or F32 [N, K/128] or I32
+ *       [N, ceil(K/512)]: one scale per row of B (the per-row b_sf of the
+ *       section's example), told apart by the row count (for N = 1 the two
+ *       forms are the same).  sfa and sfb must use the same format.
  *   c   NULL, or the accumulate input C: BF16 or F32 [M, N], any row stride
  *       (innermost stride 1), element-aligned; it may be d itself (same base,
  *       dtype and strides: an in-place D += A . B^T), any other overlap with d
  *       is rejected.  Each element of C is added to the FP32 accumulator
  *       before the BF16 rounding (same section: D = C + A @ B.T).
  *   d   BF16 [M, N], any row stride (innermost stride 1)
- * D[m,n] = C[m,n] + sum_kb (sum_{k in kb} A[m,k] B[n,k]) * sfa[m,kb] * sfb[n/128,kb].
+ * D[m,n] = C[m,n] + sum_kb (sum_{k in kb} A[m,k] B[n,k]) * sfa[m,kb] * sfb[n/128,kb]
+ * (sfb[n,kb] with one scale per row of B).
  * K must be a multiple of 128; M and N are arbitrary.
  */
 int fp8_gemm_nt(const dg_tensor* a, const dg_tensor* b, const dg_tensor* sfa,
@@ -97,7 +101,8 @@ int fp8_gemm_nt(const dg_tensor* a, const dg_tensor* b, const dg_tensor* sfa,
  * by Novita AI", section on the contiguous layout for prefill / training).
  *   a   E4M3 [Msum, K], Msum % 128 == 0
  *   b   E4M3 [G, N, K]
- *   sfa as fp8_gemm_nt with M = Msum;  sfb [G, ceil(N/128), ...]
+ *   sfa as fp8_gemm_nt with M = Msum;  sfb [G, ceil(N/128), ...] or, one
+ *       per row of B, [G, N, ...]
  *   d   BF16 [Msum, N]
  *   grouped_layout I32 [Msum/128] on the device: group id of each 128-row
  *       block; a negative id marks a block to skip (its rows of d are not
@@ -114,7 +119,8 @@ int m_grouped_fp8_gemm_nt_contiguous(const dg_tensor* a, const dg_tensor* b,
  *   a   E4M3 [G, max_m, K] (or [G*max_m, K])
  *   b   E4M3 [G, N, K]
  *   sfa F32 [G, max_m, K/128] (or [G*max_m, K/128]) or packed I32
- *   sfb F32 [G, ceil(N/128), K/128] or packed I32
+ *   sfb F32 [G, ceil(N/128), K/128] or packed I32 (or one per row of B:
+ *       [G, N, ...])
  *   d   BF16 [G, max_m, N] (or [G*max_m, N])
  *   masked_m I32 [G] on the device: group g computes its first
  *       clamp(masked_m[g], 0, max_m) rows; every other row of d is left
@@ -215,7 +221,8 @@ typedef struct dg_config {
 
 enum {
   DG_KIND_DENSE = 0, DG_KIND_CONTIGUOUS = 1, DG_KIND_MASKED = 2,            /* FP8 GEMMs */
-  DG_KIND_BF16_MASKED = 3, DG_KIND_BF16_DENSE = 4, DG_KIND_BF16_CONTIGUOUS = 5  /* BF16 GEMMs */
+  DG_KIND_BF16_MASKED = 3, DG_KIND_BF16_DENSE = 4, DG_KIND_BF16_CONTIGUOUS = 5, /* BF16 GEMMs */
+  DG_KIND_DENSE_ROWB = 6, DG_KIND_CONTIGUOUS_ROWB = 7, DG_KIND_MASKED_ROWB = 8  /* FP8, one B scale per row */
 };
 
 /* Fill *out with the configuration `kind` would launch for these sizes

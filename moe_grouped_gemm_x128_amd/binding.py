@@ -17,6 +17,7 @@ DG_F32, DG_BF16, DG_E4M3, DG_I32 = 0, 1, 2, 3
 DG_OK, DG_INVALID_ARG, DG_UNSUPPORTED, DG_LAUNCH_FAILED = 0, 1, 2, 3
 DG_KIND_DENSE, DG_KIND_CONTIGUOUS, DG_KIND_MASKED = 0, 1, 2
 DG_KIND_BF16_MASKED, DG_KIND_BF16_DENSE, DG_KIND_BF16_CONTIGUOUS = 3, 4, 5
+DG_KIND_DENSE_ROWB, DG_KIND_CONTIGUOUS_ROWB, DG_KIND_MASKED_ROWB = 6, 7, 8  # FP8, one B scale per row of B
 
 ENTRY_POINTS = (
     "dg_last_error",

@@ -226,7 +226,10 @@ int fp8_gemm_common(int mode, const dg_tensor* a, const dg_tensor* b, const dg_t
   if (K % 128 != 0) return fail(DG_UNSUPPORTED, "%s: K = %lld is not a multiple of 128", fname, (long long)K);
   const int64_t nkb = K / 128, nnb = (N + 127) / 128;
   DG_TRY(check_scales(sfa, "sfa", sf_fmt, mode == dgmi::MODE_MASKED ? G : 1, rows_pg, M, nkb, &vsa));
-  DG_TRY(check_scales(sfb, "sfb", sf_fmt, mode == dgmi::MODE_DENSE ? 1 : G, 0, nnb, nkb, &vsb));
+  // sfb: one scale per 128x128 block of B, or one per row of B (N rows; for
+  // N = 1 the two forms are the same)
+  const bool rowb = sfb->ndim >= 2 && sfb->shape[sfb->ndim - 2] == N && N != nnb;
+  DG_TRY(check_scales(sfb, "sfb", sf_fmt, mode == dgmi::MODE_DENSE ? 1 : G, 0, rowb ? N : nnb, nkb, &vsb));
   if (mode == dgmi::MODE_DENSE && (sfb->ndim != 2 || sfa->ndim != 2))
     return fail(DG_INVALID_ARG, "%s: sfa and sfb must be 2-D", fname);
   if (mode == dgmi::MODE_CONTIG && sfb->ndim != 3) return fail(DG_INVALID_ARG, "%s: sfb must be [G, ceil(N/128), ..]", fname);
@@ -300,7 +303,7 @@ int fp8_gemm_common(int mode, const dg_tensor* a, const dg_tensor* b, const dg_t
   p.G = (int32_t)G;
   if (M == 0 || N == 0 || G == 0) return ok();
   if (K == 0) return fail(DG_UNSUPPORTED, "%s: K = 0 is not supported", fname);
-  return check_launch(dgmi::launch_fp8_gemm(p, mode, sf_fmt, stream), fname);
+  return check_launch(dgmi::launch_fp8_gemm(p, mode, sf_fmt | (rowb ? dgmi::SF_ROWB : 0), stream), fname);
 }
 
 // Quantizer validation: x [R, K] or [G, R, K]; q same shape; sf [.., R', KB].
@@ -556,7 +559,11 @@ int dg_query_config(int32_t kind, int64_t G, int64_t M, int64_t N, int64_t K, dg
     c = dgmi::bf16_gemm_plan(mode, G, M, N, K);
   } else if (kind >= DG_KIND_DENSE && kind <= DG_KIND_MASKED) {
     mode = kind == DG_KIND_DENSE ? dgmi::MODE_DENSE : (kind == DG_KIND_CONTIGUOUS ? dgmi::MODE_CONTIG : dgmi::MODE_MASKED);
-    c = dgmi::fp8_gemm_plan(mode, G, M, N, K);
+    c = dgmi::fp8_gemm_plan(mode, G, M, N, K, dgmi::SF_F32);
+  } else if (kind >= DG_KIND_DENSE_ROWB && kind <= DG_KIND_MASKED_ROWB) {
+    mode = kind == DG_KIND_DENSE_ROWB ? dgmi::MODE_DENSE
+                                      : (kind == DG_KIND_CONTIGUOUS_ROWB ? dgmi::MODE_CONTIG : dgmi::MODE_MASKED);
+    c = dgmi::fp8_gemm_plan(mode, G, M, N, K, dgmi::SF_F32 | dgmi::SF_ROWB);
   } else {
     return fail(DG_INVALID_ARG, "dg_query_config: unknown kind %d", kind);
   }

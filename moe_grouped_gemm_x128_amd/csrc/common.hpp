@@ -12,8 +12,10 @@ typedef int32_t i32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
-// Scale-factor storage of the FP8 GEMMs.
-enum ScaleFmt : int { SF_F32 = 0, SF_UE8M0 = 1 };
+// Scale-factor storage of the FP8 GEMMs: FP32 or packed UE8M0, and the flag
+// SF_ROWB when B carries one scale per row (per 1x128 block) instead of one
+// per 128x128 block.
+enum ScaleFmt : int { SF_F32 = 0, SF_UE8M0 = 1, SF_ROWB = 2 };
 
 // Tile scheduling of the GEMM kernel.
 enum GemmMode : int { MODE_DENSE = 0, MODE_CONTIG = 1, MODE_MASKED = 2 };

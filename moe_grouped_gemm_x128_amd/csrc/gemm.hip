@@ -135,11 +135,11 @@ struct TileShape {
 template <int SF>
 __device__ __forceinline__ uint32_t load_scale_raw(const void* base, int64_t idx_row, int kb, int64_t s_row, int64_t s_k) {
   const uint32_t* p = static_cast<const uint32_t*>(base);
-  return SF == SF_F32 ? p[idx_row * s_row + (int64_t)kb * s_k] : p[idx_row * s_row + (int64_t)(kb >> 2) * s_k];
+  return (SF & SF_UE8M0) == 0 ? p[idx_row * s_row + (int64_t)kb * s_k] : p[idx_row * s_row + (int64_t)(kb >> 2) * s_k];
 }
 template <int SF>
 __device__ __forceinline__ float scale_value(uint32_t raw, int kb) {
-  return SF == SF_F32 ? __uint_as_float(raw) : ue8m0_to_f32((raw >> ((kb & 3) * 8)) & 0xffu);
+  return (SF & SF_UE8M0) == 0 ? __uint_as_float(raw) : ue8m0_to_f32((raw >> ((kb & 3) * 8)) & 0xffu);
 }
 
 // Tile index of this workgroup after the XCD remap: the hardware deals
@@ -232,6 +232,18 @@ template <class T, int KIND, int SF, int MODE>
 __global__ __launch_bounds__(T::NT) void gemm_kernel(const GemmParams p) {
   constexpr int S = T::STAGES;
   constexpr bool FP8 = KIND == KIND_FP8;
+  constexpr bool UE8 = FP8 && (SF & SF_UE8M0) != 0;
+  // one B scale per row of B ("DeepInside DeepGEMM", section 4: the per-row
+  // b_sf of its dense example): the promote scales each output column by
+  // its own row's scale; the UE8M0 MFMA takes the scale of the B row each
+  // lane supplies
+  constexpr bool ROWB = FP8 && (SF & SF_ROWB) != 0;
+  constexpr bool ROWB_F32 = ROWB && !UE8;
+  static_assert(!ROWB || T::BM + T::BN <= T::NT, "one thread per tile row of A and of B stages its scale");
+  // B scales a lane uses per K-slice: one per wave (or per fragment) for
+  // block scales, one per fragment (its own B row) for UE8M0 row scales;
+  // FP32 row scales are 4-vectors per fragment (below)
+  constexpr int NSB = ROWB ? (UE8 ? T::FN : 1) : T::NSB;
   // one array per stage and operand, so that the compiler can tell the
   // LDS-DMA target of one from the fragment reads of another (it would
   // otherwise drain every load in flight before those reads)
@@ -356,10 +368,12 @@ __global__ __launch_bounds__(T::NT) void gemm_kernel(const GemmParams p) {
   };
 
   // Scale staged by this thread (FP8): A row m0 + tid (tid < BM), B column
-  // block n0/128 + (tid - BM) (BM <= tid < BM + NBT), else a harmless
-  // duplicate of row 0.
-  const bool sc_is_b = tid >= T::BM && tid < T::BM + T::NBT;
-  const int64_t sc_row = sc_is_b ? (int64_t)min(n0 / 128 + (tid - T::BM), NB - 1)
+  // block n0/128 + (tid - BM) (BM <= tid < BM + NBT) or, with row scales, B
+  // row n0 + (tid - BM) (BM <= tid < BM + BN), else a harmless duplicate of
+  // row 0.
+  const bool sc_is_b = tid >= T::BM && tid < T::BM + (ROWB ? T::BN : T::NBT);
+  const int64_t sc_row = sc_is_b ? (ROWB ? (int64_t)min(n0 + (tid - T::BM), p.N - 1)
+                                         : (int64_t)min(n0 / 128 + (tid - T::BM), NB - 1))
                                  : (int64_t)max(0, min(m0 + (tid < T::BM ? tid : 0), row_lim - 1));
   const void* sfa = static_cast<const float*>(p.sfa) + (MODE == MODE_MASKED ? (int64_t)g * p.sfa_gs : 0);
   const void* sfb = static_cast<const float*>(p.sfb) + (MODE == MODE_DENSE ? 0 : (int64_t)g * p.sfb_gs);
@@ -487,12 +501,21 @@ __global__ __launch_bounds__(T::NT) void gemm_kernel(const GemmParams p) {
     return i32x8{l[0], l[1], l[2], l[3], h[0], h[1], h[2], h[3]};
   };
   const int sa_row0 = wm * T::TM + fr;  // this lane's scale slot for fragment row 0
-  // B block scale slots of this wave (one, or one per fragment); slot BM + x
-  // holds column block n0/128 + x
-  int sb_slot[T::NSB];
+  // B scale slots: block scales -- slot BM + x holds column block n0/128 + x
+  // (one per wave, or one per fragment); UE8M0 row scales -- slot BM + r
+  // holds B row n0 + r, the row this lane supplies to fragment f; FP32 row
+  // scales -- the four output columns of this lane in fragment f, from slot
+  // sbv_slot[f] on
+  int sb_slot[NSB];
 #pragma unroll
-  for (int f = 0; f < T::NSB; ++f)
-    sb_slot[f] = T::BM + (T::PERM ? (wn * T::TN) / 128 : ((n0 & 127) + wn * T::TN + 16 * f) / 128);
+  for (int f = 0; f < NSB; ++f)
+    sb_slot[f] = T::BM + (ROWB ? (T::PERM ? wn * T::TN + (fr >> 2) * 16 + 4 * f + (fr & 3) : wn * T::TN + 16 * f + fr)
+                               : (T::PERM ? (wn * T::TN) / 128 : ((n0 & 127) + wn * T::TN + 16 * f) / 128));
+  int sbv_slot[ROWB_F32 ? T::FN : 1];
+#pragma unroll
+  for (int f = 0; f < (ROWB_F32 ? T::FN : 1); ++f)
+    sbv_slot[f] = T::BM + (T::PERM ? wn * T::TN + 16 * (lane >> 4) + 4 * f : wn * T::TN + 16 * f + 4 * (lane >> 4));
+  auto read_sbv = [&](int st, int f) { return *reinterpret_cast<const f32x4*>(&ssc[st][sbv_slot[f]]); };
 
   // ---- K loop: one continuous software pipeline over fragment groups.
   // Group (kb, i) issues the FN MFMAs of A fragment i of slice kb and (FP8)
@@ -515,11 +538,17 @@ __global__ __launch_bounds__(T::NT) void gemm_kernel(const GemmParams p) {
     i32x8 bf[T::FN];
     i32x8 af, af1;             // A fragments of the current and (PF = 2) the next group
     float sa = 0.f, sa1 = 0.f;  // row scales of those groups
-    float sb[T::NSB];           // block scale(s) of the slice
+    float sb[NSB];              // B scale(s) of the slice (1 for FP32 row scales)
     f32x4 P[2][T::FN];          // partials of the current and the previous group
-    float s_prev[T::NSB];       // combined scale(s) of the previous group (the first promote adds 0 * 0)
+    float s_prev[NSB];          // combined scale(s) of the previous group (the first promote adds 0 * 0)
+    // FP32 row scales of the lane's output columns, per fragment: of this
+    // slice and of the previous one (whose last group is promoted in this
+    // slice's first group)
+    f32x4 sbv[ROWB_F32 ? T::FN : 1], sbv_prev[ROWB_F32 ? T::FN : 1];
 #pragma unroll
-    for (int f = 0; f < T::NSB; ++f) sb[f] = s_prev[f] = 0.f;
+    for (int f = 0; f < NSB; ++f) sb[f] = s_prev[f] = 0.f;
+#pragma unroll
+    for (int f = 0; f < (ROWB_F32 ? T::FN : 1); ++f) sbv[f] = sbv_prev[f] = zero;
 #pragma unroll
     for (int f = 0; f < T::FN; ++f) P[(T::FM - 1) & 1][f] = zero;
 #pragma unroll
@@ -529,8 +558,14 @@ __global__ __launch_bounds__(T::NT) void gemm_kernel(const GemmParams p) {
     if constexpr (FP8) {
       sa = ssc[0][sa_row0];
       sa1 = PF == 2 ? ssc[0][sa_row0 + 16] : sa;
+      if constexpr (ROWB_F32) {
+        sb[0] = 1.0f;
 #pragma unroll
-      for (int f = 0; f < T::NSB; ++f) sb[f] = ssc[0][sb_slot[f]];
+        for (int f = 0; f < T::FN; ++f) sbv[f] = read_sbv(0, f);
+      } else {
+#pragma unroll
+        for (int f = 0; f < NSB; ++f) sb[f] = ssc[0][sb_slot[f]];
+      }
     }
 
     auto kblock = [&](auto st_tag, int kb) {
@@ -544,15 +579,16 @@ __global__ __launch_bounds__(T::NT) void gemm_kernel(const GemmParams p) {
       for (int i = 0; i < T::FM; ++i) {
         __builtin_amdgcn_sched_barrier(0);
         if (i == 1) early_sync();
-        float s_cur[T::NSB];
+        float s_cur[NSB];
 #pragma unroll
-        for (int f = 0; f < T::NSB; ++f) s_cur[f] = sa * sb[f];
+        for (int f = 0; f < NSB; ++f) s_cur[f] = sa * sb[f];
         // the A fragment / row scale that become current after this group
         // (n0) and, for PF = 2, the one after (n1)
         i32x8 n0 = af1, n1 = af1;
-        float ns0 = sa1, ns1 = sa1, nsb[T::NSB];
+        float ns0 = sa1, ns1 = sa1, nsb[NSB];
 #pragma unroll
-        for (int f = 0; f < T::NSB; ++f) nsb[f] = sb[f];
+        for (int f = 0; f < NSB; ++f) nsb[f] = sb[f];
+        f32x4 nsbv[ROWB_F32 ? T::FN : 1];
         if (i + 1 < T::FM) {
           if (PF == 1) {
             if constexpr (FP8) ns0 = ssc[ST][sa_row0 + (i + 1) * 16];
@@ -566,12 +602,17 @@ __global__ __launch_bounds__(T::NT) void gemm_kernel(const GemmParams p) {
           if constexpr (FP8) {
             ns0 = ssc[NX][sa_row0];
             if (PF == 2) ns1 = ssc[NX][sa_row0 + 16];
+            if constexpr (ROWB_F32) {
 #pragma unroll
-            for (int f = 0; f < T::NSB; ++f) nsb[f] = ssc[NX][sb_slot[f]];
+              for (int f = 0; f < T::FN; ++f) nsbv[f] = read_sbv(NX, f);
+            } else {
+#pragma unroll
+              for (int f = 0; f < NSB; ++f) nsb[f] = ssc[NX][sb_slot[f]];
+            }
           }
           n0 = a_frag(nxt_a, 0);
         }
-        if constexpr (FP8 && SF == SF_UE8M0) {
+        if constexpr (UE8) {
           // power-of-two scales go into the MFMA itself: its scale operands
           // multiply by 2^(e-127) per A row (the lane's row) and per B row
           // (the fragment's 128-column block), and it accumulates in place
@@ -579,7 +620,7 @@ __global__ __launch_bounds__(T::NT) void gemm_kernel(const GemmParams p) {
 #pragma unroll
           for (int f = 0; f < T::FN; ++f) {
             __builtin_amdgcn_sched_barrier(0);
-            const int eb = (int)(__float_as_uint(sb[T::NSB == 1 ? 0 : f]) >> 23);
+            const int eb = (int)(__float_as_uint(sb[NSB == 1 ? 0 : f]) >> 23);
             acc[i][f] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf[f], af, acc[i][f], 0, 0, 0, eb, 0, ea);
             spread_loads(i, f, cur_a, cur_b, kb);
             if (i + 1 == T::FM) bf[f] = b_frag(nxt_b, f);  // last use of bf[f] in this slice
@@ -593,9 +634,14 @@ __global__ __launch_bounds__(T::NT) void gemm_kernel(const GemmParams p) {
             P[i & 1][f] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf[f], af, zero, 0, 0, 0, 0, 0, 0);
             spread_loads(i, f, cur_a, cur_b, kb);
             __builtin_amdgcn_sched_barrier(0);
-            const float sp = s_prev[T::NSB == 1 ? 0 : f];
-            if (i > 0) acc[i - 1][f] += P[(i - 1) & 1][f] * sp;
-            else acc[T::FM - 1][f] += P[(T::FM - 1) & 1][f] * sp;
+            const float sp = s_prev[NSB == 1 ? 0 : f];
+            if constexpr (ROWB_F32) {
+              if (i > 0) acc[i - 1][f] += P[(i - 1) & 1][f] * (sbv[f] * sp);
+              else acc[T::FM - 1][f] += P[(T::FM - 1) & 1][f] * (sbv_prev[f] * sp);
+            } else {
+              if (i > 0) acc[i - 1][f] += P[(i - 1) & 1][f] * sp;
+              else acc[T::FM - 1][f] += P[(T::FM - 1) & 1][f] * sp;
+            }
             if (i + 1 == T::FM) bf[f] = b_frag(nxt_b, f);  // last use of bf[f] in this slice
           }
         } else {
@@ -622,7 +668,7 @@ __global__ __launch_bounds__(T::NT) void gemm_kernel(const GemmParams p) {
           n1 = a_frag(nxt_a, 1);  // after the B fragments the next group 0 waits for
         }
 #pragma unroll
-        for (int f = 0; f < T::NSB; ++f) s_prev[f] = s_cur[f];
+        for (int f = 0; f < NSB; ++f) s_prev[f] = s_cur[f];
         if (PF == 1) {
           af = n0;
           sa = ns0;
@@ -633,7 +679,16 @@ __global__ __launch_bounds__(T::NT) void gemm_kernel(const GemmParams p) {
           sa1 = ns1;
         }
 #pragma unroll
-        for (int f = 0; f < T::NSB; ++f) sb[f] = nsb[f];
+        for (int f = 0; f < NSB; ++f) sb[f] = nsb[f];
+        if constexpr (ROWB_F32) {
+          if (i + 1 == T::FM) {
+#pragma unroll
+            for (int f = 0; f < T::FN; ++f) {
+              sbv_prev[f] = sbv[f];
+              sbv[f] = nsbv[f];
+            }
+          }
+        }
       }
     };
 
@@ -647,10 +702,13 @@ __global__ __launch_bounds__(T::NT) void gemm_kernel(const GemmParams p) {
     if constexpr (S > 2) {
       if (kb + 1 < KB) kblock(std::integral_constant<int, 1>{}, kb + 1);
     }
-    if constexpr (FP8 && SF == SF_F32) {
+    if constexpr (FP8 && !UE8) {
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int f = 0; f < T::FN; ++f) acc[T::FM - 1][f] += P[(T::FM - 1) & 1][f] * s_prev[T::NSB == 1 ? 0 : f];
+      for (int f = 0; f < T::FN; ++f) {
+        if constexpr (ROWB_F32) acc[T::FM - 1][f] += P[(T::FM - 1) & 1][f] * (sbv_prev[f] * s_prev[0]);
+        else acc[T::FM - 1][f] += P[(T::FM - 1) & 1][f] * s_prev[T::NSB == 1 ? 0 : f];
+      }
     }
   };
 
@@ -748,7 +806,10 @@ using TileN = TileShape<256, 192, 2, 4, 2>;  // 512 threads, wave tile 128 x 48,
 
 enum Variant : int { VAR_L = 0, VAR_W = 1, VAR_S = 2, VAR_T = 3, VAR_N = 4 };
 
-template <class T, int KIND>
+// Launch one tile configuration.  ROWB: whether the per-row B scale kernels
+// exist for this tile (they need a thread per tile row of A and of B and the
+// registers for per-lane column scales: the 256 x 192 and 128-row tiles).
+template <class T, int KIND, bool ROWB>
 hipError_t launch_tile(const GemmParams& p, int mode, int sf_fmt, int64_t grid, hipStream_t stream) {
   const dim3 g((unsigned)grid), b(T::NT);
   if constexpr (KIND == KIND_BF16) {
@@ -756,19 +817,26 @@ hipError_t launch_tile(const GemmParams& p, int mode, int sf_fmt, int64_t grid, 
     else if (mode == MODE_CONTIG) gemm_kernel<T, KIND_BF16, SF_F32, MODE_CONTIG><<<g, b, 0, stream>>>(p);
     else gemm_kernel<T, KIND_BF16, SF_F32, MODE_MASKED><<<g, b, 0, stream>>>(p);
     return hipGetLastError();
-  }
-#define DGMI_LAUNCH(MODE_, SF_) gemm_kernel<T, KIND_FP8, SF_, MODE_><<<g, b, 0, stream>>>(p)
-  if (sf_fmt == SF_F32) {
-    if (mode == MODE_DENSE) DGMI_LAUNCH(MODE_DENSE, SF_F32);
-    else if (mode == MODE_CONTIG) DGMI_LAUNCH(MODE_CONTIG, SF_F32);
-    else DGMI_LAUNCH(MODE_MASKED, SF_F32);
   } else {
-    if (mode == MODE_DENSE) DGMI_LAUNCH(MODE_DENSE, SF_UE8M0);
-    else if (mode == MODE_CONTIG) DGMI_LAUNCH(MODE_CONTIG, SF_UE8M0);
-    else DGMI_LAUNCH(MODE_MASKED, SF_UE8M0);
-  }
+#define DGMI_LAUNCH(SF_)                                                                           \
+  do {                                                                                             \
+    if (mode == MODE_DENSE) gemm_kernel<T, KIND_FP8, SF_, MODE_DENSE><<<g, b, 0, stream>>>(p);     \
+    else if (mode == MODE_CONTIG) gemm_kernel<T, KIND_FP8, SF_, MODE_CONTIG><<<g, b, 0, stream>>>(p); \
+    else gemm_kernel<T, KIND_FP8, SF_, MODE_MASKED><<<g, b, 0, stream>>>(p);                       \
+  } while (0)
+    if (sf_fmt == SF_F32) {
+      DGMI_LAUNCH(SF_F32);
+    } else if (sf_fmt == SF_UE8M0) {
+      DGMI_LAUNCH(SF_UE8M0);
+    } else if constexpr (ROWB) {
+      if (sf_fmt == (SF_F32 | SF_ROWB)) DGMI_LAUNCH(SF_F32 | SF_ROWB);
+      else DGMI_LAUNCH(SF_UE8M0 | SF_ROWB);
+    } else {
+      return hipErrorInvalidValue;  // the launch plan never picks this tile for row scales
+    }
 #undef DGMI_LAUNCH
-  return hipGetLastError();
+    return hipGetLastError();
+  }
 }
 
 template <class T, int KIND>
@@ -786,11 +854,11 @@ template <int KIND>
 hipError_t launch_variant(const TileCfg& cfg, const GemmParams& p, int mode, int sf_fmt, int64_t grid,
                           hipStream_t stream) {
   switch (cfg.variant) {
-    case VAR_L: return launch_tile<TileL, KIND>(p, mode, sf_fmt, grid, stream);
-    case VAR_W: return launch_tile<TileW, KIND>(p, mode, sf_fmt, grid, stream);
-    case VAR_T: return launch_tile<TileT, KIND>(p, mode, sf_fmt, grid, stream);
-    case VAR_N: return launch_tile<TileN, KIND>(p, mode, sf_fmt, grid, stream);
-    default: return launch_tile<TileS, KIND>(p, mode, sf_fmt, grid, stream);
+    case VAR_L: return launch_tile<TileL, KIND, false>(p, mode, sf_fmt, grid, stream);
+    case VAR_W: return launch_tile<TileW, KIND, true>(p, mode, sf_fmt, grid, stream);
+    case VAR_T: return launch_tile<TileT, KIND, false>(p, mode, sf_fmt, grid, stream);
+    case VAR_N: return launch_tile<TileN, KIND, true>(p, mode, sf_fmt, grid, stream);
+    default: return launch_tile<TileS, KIND, true>(p, mode, sf_fmt, grid, stream);
   }
 }
 
@@ -881,7 +949,16 @@ hipError_t launch_plan(const GemmPlan& plan, GemmParams p, int mode, int sf_fmt,
 // large dense and grouped shapes whose tiles fill whole rounds of the CUs,
 // with the 256 x 192 tile taking all or part of the columns when that fills
 // the last round better (plan_large).
-GemmPlan fp8_gemm_plan(int mode, int64_t G, int64_t M, int64_t N, int64_t K) {
+GemmPlan fp8_gemm_plan(int mode, int64_t G, int64_t M, int64_t N, int64_t K, int sf_fmt) {
+  if (M > 128 && (sf_fmt & SF_ROWB)) {
+    // row scales: the 256 x 192 tile (the 256 x 256 FP32 kernel has no
+    // registers left for per-lane column scales)
+    GemmPlan p;
+    p.parts = 1;
+    p.n_split = N;
+    p.cfg[0] = make_cfg<TileN, KIND_FP8>(VAR_N);
+    return p;
+  }
   if (M <= 128) {
     GemmPlan p;
     p.parts = 1;
@@ -906,7 +983,7 @@ int64_t plan_grid(const GemmPlan& plan, int part, int mode, int64_t G, int64_t M
 }
 
 hipError_t launch_fp8_gemm(GemmParams p, int mode, int sf_fmt, hipStream_t stream) {
-  return launch_plan<KIND_FP8>(fp8_gemm_plan(mode, p.G, p.M, p.N, p.k_bytes), p, mode, sf_fmt, stream);
+  return launch_plan<KIND_FP8>(fp8_gemm_plan(mode, p.G, p.M, p.N, p.k_bytes, sf_fmt), p, mode, sf_fmt, stream);
 }
 
 // BF16 GEMMs: the same tile choice as the FP8 GEMM (a K-slice is 64 BF16

@@ -53,10 +53,11 @@ struct GemmPlan {
 
 // GEMMs: the plan for (mode, G, M, N, K) and the grid of each launch (pure
 // functions of the shapes), and the launchers.
-GemmPlan fp8_gemm_plan(int mode, int64_t G, int64_t M, int64_t N, int64_t K);
+GemmPlan fp8_gemm_plan(int mode, int64_t G, int64_t M, int64_t N, int64_t K, int sf_fmt);
 GemmPlan bf16_gemm_plan(int mode, int64_t G, int64_t M, int64_t N, int64_t K);
 int64_t gemm_grid(const TileCfg& cfg, int mode, int64_t G, int64_t M, int64_t N);
 int64_t plan_grid(const GemmPlan& plan, int part, int mode, int64_t G, int64_t M, int64_t N);
+// sf_fmt: SF_F32 or SF_UE8M0, plus SF_ROWB for one B scale per row of B
 hipError_t launch_fp8_gemm(GemmParams p, int mode, int sf_fmt, hipStream_t stream);
 // BF16 GEMMs: same kernel body; byte strides in p, no scales
 hipError_t launch_bf16_gemm(GemmParams p, int mode, hipStream_t stream);

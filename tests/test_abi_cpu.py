@@ -154,10 +154,15 @@ def test_dense_validation_errors(lib):
     assert "dtype" in binding.last_error()
     # K mismatch
     assert _call_dense(lib, a, _t((N, K + 128), torch.uint8), sfa, sfb, d) == binding.DG_INVALID_ARG
-    # wrong scale shape (per-row B scales are not the 128x128 format)
-    assert _call_dense(lib, a, b, sfa, _t((N, K // 128), torch.float32), d) == binding.DG_INVALID_ARG
+    # wrong scale shape (neither one per 128x128 block nor one per row)
+    assert _call_dense(lib, a, b, sfa, _t((N // 128 + 1, K // 128), torch.float32), d) == binding.DG_INVALID_ARG
     # mixed scale formats
     assert _call_dense(lib, a, b, sfa, _t((2, 1), torch.int32), d) == binding.DG_INVALID_ARG
+    # one B scale per row: N rows (any other count is rejected), same format as sfa
+    assert _call_dense(lib, a, b, sfa, _t((N + 1, K // 128), torch.float32), d) == binding.DG_INVALID_ARG
+    assert _call_dense(lib, a, b, sfa, _t((N - 1, K // 128), torch.float32), d) == binding.DG_INVALID_ARG
+    assert _call_dense(lib, a, b, sfa, _t((N, K // 128 + 1), torch.float32), d) == binding.DG_INVALID_ARG
+    assert _call_dense(lib, a, b, _t((M, 1), torch.int32), _t((N, 2), torch.int32), d) == binding.DG_INVALID_ARG
     # non-unit inner stride
     assert _call_dense(lib, a.t(), b, sfa, sfb, d) == binding.DG_INVALID_ARG
     # K not a multiple of 128 -> unsupported
@@ -240,6 +245,16 @@ def test_quantizer_and_pack_validation_errors(lib):
     assert lib.pack_ue8m0_to_int(ctypes.byref(D(s)), ctypes.byref(D(_t((3, 2), torch.int32))), None, None) == binding.DG_INVALID_ARG
     assert lib.pack_ue8m0_to_int(ctypes.byref(D(s)), ctypes.byref(D(_t((3, 3), torch.float32))), None, None) == binding.DG_INVALID_ARG
     assert lib.pack_ue8m0_to_int(None, ctypes.byref(D(_t((3, 3), torch.int32))), None, None) == binding.DG_INVALID_ARG
+
+
+def test_launch_plan_with_per_row_b_scales(lib):
+    # above 128 rows the 256 x 192 tile, one launch, in every form; 128-row
+    # tiles below
+    for kind, G in ((binding.DG_KIND_DENSE_ROWB, 1), (binding.DG_KIND_CONTIGUOUS_ROWB, 4), (binding.DG_KIND_MASKED_ROWB, 4)):
+        c = binding.query_config(kind, G, 4096, 7168, 7168)
+        assert (c["block_m"], c["block_n"], c["block_n2"], c["n_split"]) == (256, 192, 0, 7168)
+    s = binding.query_config(binding.DG_KIND_DENSE_ROWB, 1, 64, 4096, 7168)
+    assert (s["block_m"], s["block_n2"]) == (128, 0)
 
 
 def test_empty_problems_return_ok_without_a_launch(lib):

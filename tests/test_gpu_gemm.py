@@ -482,3 +482,144 @@ def test_masked_decode_full_size_sampled(si):
             rb, rsfb = oracle.per_block_cast_to_fp8(xb_keep[g][cols])
             ref = oracle.fp8_gemm_nt(ra, rb, rsfa, rsfb)
             assert_bf16_close(dh[g, rows][:, cols], ref, f"masked g={g} col block {nb}")
+
+
+# ---------------------------------------------------------------------------
+# one B scale per row of B (the per-row b_sf of "DeepInside DeepGEMM",
+# section 4): B quantized per token like A, sfb [N, K/128]
+# ---------------------------------------------------------------------------
+
+def _rowb_plan(kind, G, M, N, K):
+    from moe_grouped_gemm_x128_amd import binding
+
+    c = binding.query_config(getattr(binding, kind), G, M, N, K)
+    assert c["block_n2"] == 0
+    return c
+
+
+@pytest.mark.parametrize("M,N,K", [(200, 300, 384), (128, 256, 512), (96, 100, 640), (4000, 4000, 256), (1, 130, 128)])
+@pytest.mark.parametrize("ue8m0", [False, True])
+def test_dense_per_row_b_scales_full_compare(M, N, K, ue8m0):
+    say(f"fp8_gemm_nt per-row B scales M={M} N={N} K={K} ue8m0={ue8m0}")
+    mg = _mg()
+    c = _rowb_plan("DG_KIND_DENSE_ROWB", 1, M, N, K)
+    if M > 128:
+        assert (c["block_m"], c["block_n"]) == (256, 192)
+    xa = synth.normal_f32(191, (M, K))
+    xb = synth.normal_f32(192, (N, K))
+    a, sfa = q_tok(to_dev(xa), ue8m0)
+    b, sfb = q_tok(to_dev(xb), ue8m0)  # [N, K/128], N-major view
+    if ue8m0:
+        pa = torch.empty((M, -(-K // 512)), dtype=torch.int32, device="cuda")
+        pb = torch.empty((N, -(-K // 512)), dtype=torch.int32, device="cuda")
+        mg.pack_ue8m0_to_int(sfa.contiguous(), pa)
+        mg.pack_ue8m0_to_int(sfb.contiguous(), pb)
+        dsa, dsb = pa, pb
+    else:
+        dsa, dsb = sfa, sfb.contiguous()  # A scales M-major, B scales K-major
+    d = sentinel_like((M, N))
+    mg.fp8_gemm_nt(a, b, dsa, dsb, None, d)
+    torch.cuda.synchronize()
+    ra, rsfa = oracle.per_token_cast_to_fp8(xa, ue8m0)
+    rb, rsfb = oracle.per_token_cast_to_fp8(xb, ue8m0)
+    assert np.array_equal(to_host(a), ra) and np.array_equal(to_host(b), rb)
+    assert rsfb.shape == (N, K // 128)
+    assert_bf16_close(to_host(d), oracle.fp8_gemm_nt(ra, rb, rsfa, rsfb), f"per-row B scales {M}x{N}x{K}")
+
+
+@pytest.mark.parametrize("M,N,K", [(160, 272, 768), (100, 300, 512), (64, 100, 384)])
+def test_dense_per_row_b_scales_one_hot_bit_exact(M, N, K):
+    """One-hot B with power-of-two per-row scales: every output is
+    sfa[m, kb] * sfb[n, kb] * A[m, kn[n]] exactly; pins the per-lane column
+    scale indexing of each tile."""
+    say(f"fp8_gemm_nt per-row B scales one-hot M={M} N={N} K={K}")
+    mg = _mg()
+    _rowb_plan("DG_KIND_DENSE_ROWB", 1, M, N, K)
+    rng = np.random.default_rng(193)
+    a = (rng.integers(0, 0x7E, size=(M, K)) | (rng.integers(0, 2, size=(M, K)) << 7)).astype(np.uint8)
+    kn = rng.integers(0, K, size=N)
+    b = np.zeros((N, K), dtype=np.uint8)
+    b[np.arange(N), kn] = 0x38
+    sfa = np.exp2(rng.integers(-6, 6, size=(M, K // 128))).astype(np.float32)
+    sfb = np.exp2(rng.integers(-6, 6, size=(N, K // 128))).astype(np.float32)
+    d = sentinel_like((M, N))
+    mg.fp8_gemm_nt(to_dev(a), to_dev(b), to_dev(sfa), to_dev(sfb), None, d)
+    torch.cuda.synchronize()
+    ref = oracle.fp8_gemm_nt(a, b, sfa, sfb)
+    ref_bits = to_host(torch.from_numpy(ref.astype(np.float32)).to(torch.bfloat16))
+    got = to_host(d)
+    bad = np.argwhere(got != ref_bits)
+    assert bad.size == 0, f"{len(bad)} mismatches, first {bad[:5].tolist()}"
+
+
+def test_dense_pages_example_per_row_scales_and_c():
+    """The pages' dense call as printed: M = N = K = 4096, A and B cast from
+    normal values to E4M3, random-normal FP32 scales (either sign) of shape
+    [m, k/128] and [n, k/128], a BF16 accumulate input C; D = C + A . B^T,
+    compared on sampled rows."""
+    say("fp8_gemm_nt pages example 4096^3, per-row B scales, C")
+    mg = _mg()
+    M = N = K = 4096
+    _rowb_plan("DG_KIND_DENSE_ROWB", 1, M, N, K)
+    a = torch.from_numpy(synth.normal_f32(194, (M, K))).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    b = torch.from_numpy(synth.normal_f32(195, (N, K))).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    sfa = synth.normal_f32(196, (M, K // 128))
+    sfb = synth.normal_f32(197, (N, K // 128))
+    cbits = synth.bf16_bits_from_f32(synth.normal_f32(198, (M, N)) * np.float32(16.0))
+    c = to_dev(cbits.view(np.int16)).view(torch.bfloat16)
+    d = sentinel_like((M, N))
+    mg.fp8_gemm_nt(to_dev(a), to_dev(b), to_dev(sfa), to_dev(sfb), c, d)
+    torch.cuda.synchronize()
+    rows = _sample_rows(M, 24, 199)
+    ref = oracle.fp8_gemm_nt(a[rows], b, sfa[rows], sfb, c=oracle.bf16_decode(cbits[rows]))
+    assert_bf16_close(to_host(d)[rows], ref, "pages example")
+
+
+@pytest.mark.parametrize("ue8m0", [False, True])
+def test_grouped_per_row_b_scales(ue8m0):
+    """Masked (with clamping and untouched rows) and contiguous (with skipped
+    and mixed blocks) grouped GEMMs with sfb [G, N, K/128]."""
+    say(f"grouped per-row B scales ue8m0={ue8m0}")
+    mg = _mg()
+    G, max_m, N, K = 4, 160, 200, 512
+    mm = np.array([0, 17, 160, 999], dtype=np.int32)
+    xa = synth.normal_f32(201, (G, max_m, K))
+    xb = synth.normal_f32(202, (G, N, K))
+    a, sfa = q_tok(to_dev(xa), ue8m0)
+    b, sfb = q_tok(to_dev(xb), ue8m0)  # [G, N, K/128]
+    if ue8m0:
+        pa = torch.empty((G, max_m, 1), dtype=torch.int32, device="cuda")
+        pb = torch.empty((G, N, 1), dtype=torch.int32, device="cuda")
+        mg.pack_ue8m0_to_int(sfa, pa)
+        mg.pack_ue8m0_to_int(sfb, pb)
+        dsa, dsb = pa, pb
+    else:
+        dsa, dsb = sfa, sfb
+    d = sentinel_like((G, max_m, N))
+    mg.m_grouped_fp8_gemm_nt_masked(a, b, dsa, dsb, d, to_dev(mm), max_m)
+    torch.cuda.synchronize()
+    ra, rsfa = oracle.per_token_cast_to_fp8(xa, ue8m0)
+    rb, rsfb = oracle.per_token_cast_to_fp8(xb, ue8m0)
+    ref, written = oracle.m_grouped_fp8_gemm_nt_masked(ra, rb, rsfa, rsfb, mm, max_m)
+    got = to_host(d)
+    assert np.all(got[~written] == SENTINEL_BF16)
+    assert_bf16_close(got[written], ref[written], "masked per-row B scales")
+
+    layout = np.array([2, -1, 0, 3, 1, 3], dtype=np.int32)
+    Msum = layout.size * 128
+    xg = synth.normal_f32(203, (Msum, K))
+    ag, sfg = q_tok(to_dev(xg), ue8m0)
+    if ue8m0:
+        pg = torch.empty((Msum, 1), dtype=torch.int32, device="cuda")
+        mg.pack_ue8m0_to_int(sfg.contiguous(), pg)
+        dsg = pg
+    else:
+        dsg = sfg
+    dg = sentinel_like((Msum, N))
+    mg.m_grouped_fp8_gemm_nt_contiguous(ag, b, dsg, dsb, dg, to_dev(layout))
+    torch.cuda.synchronize()
+    rg, rsfg = oracle.per_token_cast_to_fp8(xg, ue8m0)
+    refc, wc = oracle.m_grouped_fp8_gemm_nt_contiguous(rg, rb, rsfg, rsfb, layout)
+    gotc = to_host(dg)
+    assert np.all(gotc[~wc] == SENTINEL_BF16)
+    assert_bf16_close(gotc[wc], refc[wc], "contiguous per-row B scales")
