@@ -30,6 +30,8 @@ Other workloads (for the measurements in the design notes):
                   pack_ue8m0_to_int, FP8 and BF16 masked GEMMs replayed as one hipGraph
   bf16_dense   -- the five dense shapes with BF16 operands through bf16_gemm_nt
                   (metric against the 2.5 PFLOP/s BF16 MFMA peak)
+  dense_rowb   -- the five dense shapes with one B scale per row of B (B cast per
+                  token, scales [N, K/128]), as in the pages' dense example
 """
 
 import argparse
@@ -102,6 +104,39 @@ class DenseWorkload:
     def config(self):
         return {"workload": self.name, "M": self.M, "shapes_NK": self.shapes,
                 "scales": "fp32 1x128 (A) / 128x128 (B)", "out": "bf16"}
+
+
+class DenseRowBWorkload(DenseWorkload):
+    """The five dense shapes with one B scale per row of B (the per-row b_sf
+    of the pages' dense example): B is cast per token like A, its scales
+    [N, K/128]; one step = both casts and the GEMM per shape."""
+    name = "dense_fp8_v3_shapes_row_b_scales"
+
+    def __init__(self, torch, mg, synth):
+        super().__init__(torch, mg, synth)
+        for (N, K), buf in zip(self.shapes, self.bufs):
+            buf["sfb"] = torch.empty((N, K // 128), dtype=torch.float32, device=buf["xb"].device)
+        self.gemm_bytes = [self.M * K + N * K + 4 * (self.M * K // 128 + N * (K // 128)) + 2 * self.M * N
+                           for N, K in self.shapes]
+
+    def step(self, events=None):
+        mg = self.mg
+        for i, b in enumerate(self.bufs):
+            mg.per_token_cast_to_fp8(b["xa"], b["a"], b["sfa"])
+            mg.per_token_cast_to_fp8(b["xb"], b["b"], b["sfb"])
+            if events is not None:
+                events[i][0].record()
+            mg.fp8_gemm_nt(b["a"], b["b"], b["sfa"], b["sfb"], None, b["d"])
+            if events is not None:
+                events[i][1].record()
+
+    def plan_args(self, i):
+        N, K = self.shapes[i]
+        return ("DG_KIND_DENSE_ROWB", 1, self.M, N, K)
+
+    def config(self):
+        return {"workload": self.name, "M": self.M, "shapes_NK": self.shapes,
+                "scales": "fp32 1x128 (A) / 1x128 per row (B)", "out": "bf16"}
 
 
 class Bf16DenseWorkload:
@@ -436,7 +471,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="dense", choices=["dense", "contiguous", "masked", "masked_graph", "bf16_dense"])
+    ap.add_argument("--workload", default="dense",
+                    choices=["dense", "contiguous", "masked", "masked_graph", "bf16_dense", "dense_rowb"])
     ap.add_argument("--settle-seconds", type=float, default=1.0,
                     help="untimed steps run for this long before the warmup steps, so that the timed steps see "
                          "the GPU's steady sustained clock rather than the dip of its first milliseconds under load")
@@ -463,7 +499,8 @@ def main():
 
     log(f"setting up workload {args.workload}")
     W = {"dense": DenseWorkload, "contiguous": ContiguousWorkload, "masked": MaskedWorkload,
-         "masked_graph": MaskedGraphWorkload, "bf16_dense": Bf16DenseWorkload}[args.workload](torch, mg, synth)
+         "masked_graph": MaskedGraphWorkload, "bf16_dense": Bf16DenseWorkload,
+         "dense_rowb": DenseRowBWorkload}[args.workload](torch, mg, synth)
     torch.cuda.synchronize()
 
     # Power-state settle: under sustained GEMM load the clock dips for the first
