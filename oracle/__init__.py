@@ -8,18 +8,21 @@ decoded here from the format definitions, and every result is computed in
 float64 from the plain definition of the operation.
 
 Modules
-  formats  -- OCP E4M3 ("fn") decode/encode, bf16 decode, UE8M0 decode.
+  formats  -- OCP E4M3 ("fn") decode/encode, bf16 decode and rounding,
+              UE8M0 decode.
   quant    -- per-token (1x128) and per-block (128x128) FP8 quantizers and
               the UE8M0 packing of four scales into one int32.
   gemm     -- dense, contiguous-grouped and masked-grouped FP8 GEMMs with
-              fine-grained scales, and the dense, contiguous-grouped and
+              fine-grained scales, the dense one with its output cast
+              per token to FP8, and the dense, contiguous-grouped and
               masked-grouped BF16 GEMMs.
 
 Sources (the pages this follows):
   * "DeepInside DeepGEMM: Unpacking DeepSeek's Unified Tensor Core Library
     for SM90 and SM100", section 2 (NT layout, FP32 scaling factors, packed
-    UE8M0 four to an int) and section 4 (the fp8_gemm_nt example with per
-    128-wide K-block scale factors and D = C + A @ B.T).
+    UE8M0 four to an int), section 4 (the fp8_gemm_nt example with per
+    128-wide K-block scale factors and D = C + A @ B.T) and section 5 (the
+    FP8 cast of a tensor fused into the kernel that produces it).
   * "DeepGEMM CUDA Graph Compatibility for Masked Grouped GEMMs", section
     "Tensor-Based Metadata Arguments" (masked_m on the device,
     max_m_per_group) and the capture example.
@@ -40,12 +43,14 @@ from .formats import (
     e4m3_decode,
     e4m3_encode,
     bf16_decode,
+    bf16_round,
     ue8m0_decode,
 )
 from .quant import per_token_cast_to_fp8, per_block_cast_to_fp8, pack_ue8m0_to_int, AMAX_FLOOR
 from .gemm import (
     bf16_gemm_nt,
     fp8_gemm_nt,
+    fp8_gemm_nt_fp8_out,
     m_grouped_bf16_gemm_nt_contiguous,
     m_grouped_fp8_gemm_nt_contiguous,
     m_grouped_fp8_gemm_nt_masked,
@@ -59,6 +64,7 @@ __all__ = [
     "e4m3_decode",
     "e4m3_encode",
     "bf16_decode",
+    "bf16_round",
     "ue8m0_decode",
     "per_token_cast_to_fp8",
     "per_block_cast_to_fp8",
@@ -66,6 +72,7 @@ __all__ = [
     "bf16_gemm_nt",
     "m_grouped_bf16_gemm_nt_contiguous",
     "fp8_gemm_nt",
+    "fp8_gemm_nt_fp8_out",
     "m_grouped_fp8_gemm_nt_contiguous",
     "m_grouped_fp8_gemm_nt_masked",
     "m_grouped_bf16_gemm_nt_masked",

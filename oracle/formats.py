@@ -15,7 +15,9 @@ fields.
 Pins (tests/test_oracle_formats.py): spec values of named codes
 (tests/golden/e4m3_spec_values.txt), agreement with torch's own float8_e4m3fn
 and bfloat16 conversions on every code / on random values, encode(decode(c))
-== c on every finite code, and ties-to-even on every midpoint.
+== c on every finite code, and ties-to-even on every midpoint; bf16_round
+against torch's float32 -> bfloat16 conversion on random and midpoint values
+and on hand-picked ties.
 """
 
 import numpy as np
@@ -87,6 +89,22 @@ def bf16_decode(bits):
     bits = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16
     with np.errstate(invalid="ignore"):
         return bits.view(np.float32).astype(np.float64)
+
+
+def bf16_round(x):
+    """Round float64 values to the nearest bfloat16 value, ties to even,
+    returned as float64 (one rounding, from the format: 8 significant bits
+    for normal values, a fixed step of 2^-133 below 2^-126; values beyond
+    the largest bfloat16 become infinite)."""
+    x = np.asarray(x, dtype=np.float64)
+    m, e = np.frexp(x)  # x = m * 2^e, 0.5 <= |m| < 1
+    normal = np.ldexp(np.rint(np.ldexp(m, 8)), e - 8)  # np.rint rounds half to even
+    sub = np.ldexp(np.rint(np.ldexp(x, 133)), -133)
+    out = np.where(np.abs(x) < 2.0 ** -126, sub, normal)
+    big = np.abs(out) >= 2.0 ** 128
+    with np.errstate(over="ignore"):
+        out = np.where(big, np.copysign(np.inf, x), out)
+    return np.where(np.isnan(x), np.nan, out)
 
 
 def ue8m0_decode(e):

@@ -35,7 +35,8 @@ matmul when every scale is 1, and the masked/contiguous invariants).
 
 import numpy as np
 
-from .formats import e4m3_decode, bf16_decode, ue8m0_decode
+from .formats import e4m3_decode, bf16_decode, bf16_round, ue8m0_decode
+from .quant import per_token_cast_to_fp8
 
 BLOCK = 128
 
@@ -76,6 +77,24 @@ def fp8_gemm_nt(a, b, sfa, sfb, c=None):
     if c is not None:
         D = D + np.asarray(c, dtype=np.float64)
     return D
+
+
+def fp8_gemm_nt_fp8_out(a, b, sfa, sfb, c=None, use_ue8m0=False):
+    """The dense GEMM with its output cast to FP8 ("DeepInside DeepGEMM",
+    section 5: the FP8 cast of a tensor belongs in the kernel that produces
+    it, not in a separate helper).  The reading taken: the output is what
+    the BF16 GEMM returns, cast per token as per_token_cast_to_fp8 casts a
+    BF16 tensor -- D = C + A . B^T (fp8_gemm_nt), rounded once to bfloat16,
+    then 1x128 blocks per row, s = amax/448 (UE8M0: rounded up to a power of
+    two), q = e4m3(x / s).
+
+    Returns (q uint8 [M, N] E4M3 codes, sf float32 [M, ceil(N/128)]).
+    Pins: tests/test_oracle_gemm.py (hand-built products with a known block
+    maximum of 448, where the code of each element follows from its value,
+    including a value whose code changes if the BF16 rounding is skipped).
+    """
+    D = bf16_round(fp8_gemm_nt(a, b, sfa, sfb, c))
+    return per_token_cast_to_fp8(D.astype(np.float32), use_ue8m0)
 
 
 def m_grouped_fp8_gemm_nt_contiguous(a, b, sfa, sfb, grouped_layout):

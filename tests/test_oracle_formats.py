@@ -102,3 +102,31 @@ def test_ue8m0_decode_closed_form():
     assert np.array_equal(oracle.ue8m0_decode(e), np.array([math.ldexp(1.0, int(v) - 127) for v in e]))
     assert math.isnan(oracle.ue8m0_decode(np.array([255]))[0])
     assert oracle.ue8m0_decode(np.array([127]))[0] == 1.0
+
+
+def test_bf16_round_matches_torch_on_float32():
+    # torch's float32 -> bfloat16 conversion rounds to nearest even: on
+    # float32 inputs the oracle's one rounding from float64 must agree
+    rng = np.random.default_rng(7)
+    x = (rng.standard_normal(20000) * np.exp2(rng.integers(-30, 30, 20000))).astype(np.float32)
+    # exact midpoints between neighbouring bfloat16 values (bit 15 set, bits 0..14 clear)
+    mid = ((rng.integers(0x00800000, 0x7f000000, 5000, dtype=np.int64) & ~0xffff) | 0x8000).astype(np.uint32)
+    x = np.concatenate([x, mid.view(np.float32), -mid.view(np.float32), np.float32([0.0, -0.0, 1.0, 3.0e38])])
+    want = torch.from_numpy(x).to(torch.bfloat16).to(torch.float64).numpy()
+    got = formats.bf16_round(x.astype(np.float64))
+    assert np.array_equal(got, want)
+    assert np.array_equal(np.signbit(got), np.signbit(want))
+
+
+def test_bf16_round_hand_picked_ties():
+    u = 2.0 ** -7  # bfloat16 spacing in [1, 2)
+    assert formats.bf16_round(1 + u / 2) == 1.0  # tie: to the even neighbour 1
+    assert formats.bf16_round(1 + 3 * u / 2) == 1 + 2 * u  # tie: to the even neighbour 1 + 2u
+    assert formats.bf16_round(-(1 + 3 * u / 2)) == -(1 + 2 * u)
+    # one rounding from float64: just above a tie rounds up (rounding through
+    # float32 first would land on the tie and go to the even value 1)
+    assert formats.bf16_round(1 + u / 2 + 2.0 ** -40) == 1 + u
+    # below 2^-126 the step is 2^-133
+    assert formats.bf16_round(2.0 ** -133 * 2.5) == 2.0 ** -133 * 2
+    assert formats.bf16_round(2.0 ** -133 * 3.5) == 2.0 ** -133 * 4
+    assert np.isinf(formats.bf16_round(2.0 ** 128))

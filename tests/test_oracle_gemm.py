@@ -327,3 +327,78 @@ def test_synth_chunked_draw_matches_whole():
     whole = synth.normal_f32(9, (3, 5, 7))
     parts = np.stack(list(synth.normal_f32_chunks(9, (3, 5, 7))))
     assert np.array_equal(whole, parts)
+
+
+# ---------------------------------------------------------------------------
+# dense GEMM with FP8 output
+# ---------------------------------------------------------------------------
+
+def _codes(vals):
+    """E4M3 codes of exactly representable values, by torch's conversion."""
+    t = torch.tensor(np.asarray(vals, dtype=np.float32)).to(torch.float8_e4m3fn)
+    return t.view(torch.uint8).numpy()
+
+
+@pytest.mark.parametrize("ue8m0", [False, True])
+def test_fp8_out_hand_built_blocks(ue8m0):
+    """Rows whose block maximum is 448 (scale 1) or 28 (scale 1/16), both
+    powers of two, so every output code is the code of the exact product;
+    a row given only by C where one value's code depends on the BF16
+    rounding; an all-zero row (the amax floor); N = 130 ends in a partial
+    block of two columns."""
+    M, N, K = 4, 130, 128
+    rng = np.random.default_rng(11)
+    # B column values v_n: E4M3 values with |v| in [2^-5, 28) so 16 v is an
+    # exact E4M3 value in [0.5, 448); column 0 holds 28 (16 * 28 = 448) and
+    # so does column 128, the first of the partial block
+    mant = rng.integers(0, 8, N)
+    expo = rng.integers(-5, 4, N)
+    sign = np.where(rng.random(N) < 0.5, -1.0, 1.0)
+    v = sign * (1 + mant / 8.0) * np.exp2(expo)
+    v[0] = v[128] = 28.0
+    v[129] = -14.0
+    a = np.zeros((M, K), np.uint8)
+    b = np.zeros((N, K), np.uint8)
+    a[0, 0] = _codes([16.0])[0]
+    a[1, 0] = _codes([1.0])[0]
+    b[:, 0] = _codes(v)
+    sfa = np.ones((M, 1), np.float32)
+    sfb = np.ones((2, 1), np.float32)
+    c = np.zeros((M, N))
+    e = 1 + 2.0 ** -4 + 2.0 ** -9  # BF16: 1 + 2^-4, a tie in E4M3 that goes to 1.0
+    c[2, 0], c[2, 1], c[2, 2] = 448.0, e, -e
+    q, sf = oracle.fp8_gemm_nt_fp8_out(a, b, sfa, sfb, c, use_ue8m0=ue8m0)
+    assert q.shape == (M, N) and sf.shape == (M, 2)
+    want0 = _codes(16.0 * v)
+    assert np.array_equal(q[0], want0) and np.array_equal(sf[0], [1.0, 1.0])
+    # row 1 = row 0 / 16: amax 28, scale 1/16 (a power of two), same codes
+    assert np.array_equal(q[1], want0) and np.array_equal(sf[1], [1.0 / 16, 1.0 / 16])
+    # row 2: C only
+    assert q[2, 0] == 0x7E and q[2, 1] == 0x38 and q[2, 2] == 0xB8  # 448, 1.0, -1.0
+    assert _codes([1.125])[0] == 0x39  # (the code without the BF16 rounding)
+    assert np.all(q[2, 3:] == 0) and np.array_equal(sf[2], [1.0, np.float32(1e-4) / np.float32(448)] if not ue8m0
+                                                     else [1.0, 2.0 ** -22])
+    # row 3: all zeros, amax floored at 1e-4
+    floor = 2.0 ** -22 if ue8m0 else np.float32(1e-4) / np.float32(448)
+    assert np.all(q[3] == 0) and np.array_equal(sf[3], [floor, floor])
+
+
+def test_fp8_out_scale_is_the_block_maximum():
+    """On random operands, every block's scale is its largest |D| (as BF16)
+    over 448, at least one code per block is +-448 (0x7E / 0xFE), and
+    decoding q * s recovers D within E4M3's half step."""
+    M, N, K = 8, 300, 256
+    xa = synth.normal_f32(31, (M, K))
+    xb = synth.normal_f32(32, (N, K))
+    a, sfa = oracle.per_token_cast_to_fp8(xa)
+    b, sfb = oracle.per_block_cast_to_fp8(xb)
+    D = oracle.fp8_gemm_nt(a, b, sfa, sfb)
+    q, sf = oracle.fp8_gemm_nt_fp8_out(a, b, sfa, sfb)
+    deq = _torch_e4m3(q) * np.repeat(sf.astype(np.float64), 128, axis=1)[:, :N]
+    for kb in range(3):
+        blk = D[:, kb * 128:(kb + 1) * 128]
+        amax = _torch_bf16(torch.from_numpy(np.abs(blk).max(axis=1)).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16))
+        assert np.allclose(sf[:, kb], amax / 448.0, rtol=2.0 ** -23)
+        assert np.all(np.any((q[:, kb * 128:(kb + 1) * 128] & 0x7F) == 0x7E, axis=1))
+    s = np.repeat(sf.astype(np.float64), 128, axis=1)[:, :N]
+    assert np.all(np.abs(deq - D) <= 2.0 ** -4 * np.abs(D) * (1 + 2.0 ** -7) + 2.0 ** -10 * s + 2.0 ** -8 * np.abs(D))
