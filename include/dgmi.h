@@ -97,6 +97,27 @@ int fp8_gemm_nt(const dg_tensor* a, const dg_tensor* b, const dg_tensor* sfa,
                 hipStream_t stream);
 
 /*
+ * fp8_gemm_nt with its output cast to FP8 in the same kernel ("DeepInside
+ * DeepGEMM", section 5: FP8 casting done by separate helpers costs HBM
+ * bandwidth, and belongs in the kernel that produces the tensor): D is
+ * formed and rounded to BF16 as by fp8_gemm_nt (C added first), then cast
+ * per token exactly as per_token_cast_to_fp8 casts that BF16 tensor, so q
+ * and sfq are bit-identical to fp8_gemm_nt followed by per_token_cast_to_fp8
+ * with the same use_ue8m0.  The BF16 D is never written to memory.
+ *   a, b, sfa, c  as fp8_gemm_nt; sfb one scale per 128x128 block of B only
+ *       (one scale per row of B returns DG_UNSUPPORTED)
+ *   q   E4M3 [M, N], any row stride that is a multiple of 4 (innermost
+ *       stride 1), 4-B aligned base; must not overlap any input
+ *   sfq F32 [M, ceil(N/128)], any strides, 4-B aligned: the scale of each
+ *       1x128 block of D (amax/448 floored as for per_token_cast_to_fp8;
+ *       with use_ue8m0 rounded up to a power of two)
+ * K must be a multiple of 128; M and N are arbitrary.
+ */
+int fp8_gemm_nt_fp8_out(const dg_tensor* a, const dg_tensor* b, const dg_tensor* sfa,
+                        const dg_tensor* sfb, const dg_tensor* c, const dg_tensor* q,
+                        const dg_tensor* sfq, int use_ue8m0, hipStream_t stream);
+
+/*
  * Contiguous grouped FP8 GEMM: groups concatenated along M ("DeepGEMM tested
  * by Novita AI", section on the contiguous layout for prefill / training).
  *   a   E4M3 [Msum, K], Msum % 128 == 0
@@ -222,7 +243,8 @@ typedef struct dg_config {
 enum {
   DG_KIND_DENSE = 0, DG_KIND_CONTIGUOUS = 1, DG_KIND_MASKED = 2,            /* FP8 GEMMs */
   DG_KIND_BF16_MASKED = 3, DG_KIND_BF16_DENSE = 4, DG_KIND_BF16_CONTIGUOUS = 5, /* BF16 GEMMs */
-  DG_KIND_DENSE_ROWB = 6, DG_KIND_CONTIGUOUS_ROWB = 7, DG_KIND_MASKED_ROWB = 8  /* FP8, one B scale per row */
+  DG_KIND_DENSE_ROWB = 6, DG_KIND_CONTIGUOUS_ROWB = 7, DG_KIND_MASKED_ROWB = 8, /* FP8, one B scale per row */
+  DG_KIND_DENSE_FP8_OUT = 9                                                       /* fp8_gemm_nt_fp8_out */
 };
 
 /* Fill *out with the configuration `kind` would launch for these sizes

@@ -13,6 +13,7 @@ from .binding import (  # noqa: F401
     last_error,
     dgmi_init,
     fp8_gemm_nt,
+    fp8_gemm_nt_fp8_out,
     m_grouped_fp8_gemm_nt_contiguous,
     m_grouped_fp8_gemm_nt_masked,
     m_grouped_bf16_gemm_nt_masked,

@@ -18,11 +18,13 @@ DG_OK, DG_INVALID_ARG, DG_UNSUPPORTED, DG_LAUNCH_FAILED = 0, 1, 2, 3
 DG_KIND_DENSE, DG_KIND_CONTIGUOUS, DG_KIND_MASKED = 0, 1, 2
 DG_KIND_BF16_MASKED, DG_KIND_BF16_DENSE, DG_KIND_BF16_CONTIGUOUS = 3, 4, 5
 DG_KIND_DENSE_ROWB, DG_KIND_CONTIGUOUS_ROWB, DG_KIND_MASKED_ROWB = 6, 7, 8  # FP8, one B scale per row of B
+DG_KIND_DENSE_FP8_OUT = 9  # fp8_gemm_nt_fp8_out
 
 ENTRY_POINTS = (
     "dg_last_error",
     "dgmi_init",
     "fp8_gemm_nt",
+    "fp8_gemm_nt_fp8_out",
     "m_grouped_fp8_gemm_nt_contiguous",
     "m_grouped_fp8_gemm_nt_masked",
     "m_grouped_bf16_gemm_nt_masked",
@@ -83,6 +85,7 @@ def load_library(path=None):
         "dg_last_error": ([], ctypes.c_char_p),
         "dgmi_init": ([], ctypes.c_int),
         "fp8_gemm_nt": ([T, T, T, T, T, T, vp], ctypes.c_int),
+        "fp8_gemm_nt_fp8_out": ([T, T, T, T, T, T, T, ctypes.c_int, vp], ctypes.c_int),
         "m_grouped_fp8_gemm_nt_contiguous": ([T, T, T, T, T, T, vp], ctypes.c_int),
         "m_grouped_fp8_gemm_nt_masked": ([T, T, T, T, T, T, i64, vp], ctypes.c_int),
         "m_grouped_bf16_gemm_nt_masked": ([T, T, T, T, i64, vp], ctypes.c_int),
@@ -166,6 +169,15 @@ def fp8_gemm_nt(a, b, sfa, sfb, c, d, stream=None):
     _check(lib.fp8_gemm_nt(_ref(describe(a)), _ref(describe(b)), _ref(describe(sfa)), _ref(describe(sfb)),
                            _ref(describe(c)), _ref(describe(d)), _stream(stream)))
     return d
+
+
+def fp8_gemm_nt_fp8_out(a, b, sfa, sfb, c, q, sfq, use_ue8m0=False, stream=None):
+    """(q, sfq) = per-token FP8 cast of the BF16 D = c + a . b^T, in one kernel."""
+    lib = load_library()
+    _check(lib.fp8_gemm_nt_fp8_out(_ref(describe(a)), _ref(describe(b)), _ref(describe(sfa)), _ref(describe(sfb)),
+                                   _ref(describe(c)), _ref(describe(q)), _ref(describe(sfq)), int(bool(use_ue8m0)),
+                                   _stream(stream)))
+    return q, sfq
 
 
 def m_grouped_fp8_gemm_nt_contiguous(a, b, sfa, sfb, d, grouped_layout, stream=None):

@@ -181,16 +181,22 @@ int check_launch(hipError_t e, const char* what) {
   return ok();
 }
 
-// Common FP8 GEMM validation.  mode: dense / contig / masked.
+// Common FP8 GEMM validation.  mode: dense / contig / masked.  With q != NULL
+// (dense only) the output is D cast per token to FP8: q E4M3 [M, N] and sfq
+// F32 [M, ceil(N/128)] take the place of d (NULL).
 int fp8_gemm_common(int mode, const dg_tensor* a, const dg_tensor* b, const dg_tensor* sfa, const dg_tensor* sfb,
                     const dg_tensor* c, const dg_tensor* d, const dg_tensor* meta, int64_t max_m, hipStream_t stream,
-                    const char* fname) {
+                    const char* fname, const dg_tensor* q = nullptr, const dg_tensor* sfq = nullptr,
+                    int q_ue8m0 = 0) {
+  const bool fp8_out = q != nullptr;
+  if (fp8_out) d = q;  // the output operand, for the shape and alias checks
+  const char* dname = fp8_out ? "q" : "d";
   DG_TRY(check_basic(a, "a", true));
   DG_TRY(check_basic(b, "b", true));
-  DG_TRY(check_basic(d, "d", true));
+  DG_TRY(check_basic(d, dname, true));
   DG_TRY(check_dtype(a, "a", DG_E4M3));
   DG_TRY(check_dtype(b, "b", DG_E4M3));
-  DG_TRY(check_dtype(d, "d", DG_BF16));
+  DG_TRY(check_dtype(d, dname, fp8_out ? DG_E4M3 : DG_BF16));
   if (sfa == nullptr || sfb == nullptr) return fail(DG_INVALID_ARG, "%s: scale descriptors must not be NULL", fname);
   if (sfa->dtype != sfb->dtype) return fail(DG_INVALID_ARG, "%s: sfa and sfb must have the same dtype", fname);
   const int sf_fmt = sfa->dtype == DG_I32 ? dgmi::SF_UE8M0 : dgmi::SF_F32;
@@ -198,7 +204,8 @@ int fp8_gemm_common(int mode, const dg_tensor* a, const dg_tensor* b, const dg_t
   View3 va, vb, vd, vsa, vsb;
   int64_t G = 1, rows_pg = 0;
   if (mode == dgmi::MODE_DENSE) {
-    if (a->ndim != 2 || b->ndim != 2 || d->ndim != 2) return fail(DG_INVALID_ARG, "%s: a, b, d must be 2-D", fname);
+    if (a->ndim != 2 || b->ndim != 2 || d->ndim != 2)
+      return fail(DG_INVALID_ARG, "%s: a, b, %s must be 2-D", fname, dname);
     DG_TRY(view3(b, "b", 1, 0, &vb));
   } else {
     if (b->ndim != 3) return fail(DG_INVALID_ARG, "%s: b must be [G, N, K]", fname);
@@ -211,14 +218,14 @@ int fp8_gemm_common(int mode, const dg_tensor* a, const dg_tensor* b, const dg_t
     DG_TRY(view3(a, "a", G, rows_pg, &va));
     DG_TRY(view3(d, "d", G, rows_pg, &vd));
   } else {
-    if (a->ndim != 2 || d->ndim != 2) return fail(DG_INVALID_ARG, "%s: a and d must be 2-D", fname);
+    if (a->ndim != 2 || d->ndim != 2) return fail(DG_INVALID_ARG, "%s: a and %s must be 2-D", fname, dname);
     DG_TRY(view3(a, "a", 1, 0, &va));
-    DG_TRY(view3(d, "d", 1, 0, &vd));
+    DG_TRY(view3(d, dname, 1, 0, &vd));
   }
   const int64_t M = va.R, K = va.C, N = vb.R;
   if (vb.C != K) return fail(DG_INVALID_ARG, "%s: K mismatch: a has %lld, b has %lld", fname, (long long)K, (long long)vb.C);
   if (vd.R != M || vd.C != N)
-    return fail(DG_INVALID_ARG, "%s: d is [..,%lld,%lld], expected [..,%lld,%lld]", fname, (long long)vd.R,
+    return fail(DG_INVALID_ARG, "%s: %s is [..,%lld,%lld], expected [..,%lld,%lld]", fname, dname, (long long)vd.R,
                 (long long)vd.C, (long long)M, (long long)N);
   if (mode == dgmi::MODE_MASKED && M != max_m)
     return fail(DG_INVALID_ARG, "%s: a has %lld rows per group, max_m_per_group is %lld", fname, (long long)M,
@@ -233,12 +240,26 @@ int fp8_gemm_common(int mode, const dg_tensor* a, const dg_tensor* b, const dg_t
   if (mode == dgmi::MODE_DENSE && (sfb->ndim != 2 || sfa->ndim != 2))
     return fail(DG_INVALID_ARG, "%s: sfa and sfb must be 2-D", fname);
   if (mode == dgmi::MODE_CONTIG && sfb->ndim != 3) return fail(DG_INVALID_ARG, "%s: sfb must be [G, ceil(N/128), ..]", fname);
+  if (fp8_out && rowb)
+    return fail(DG_UNSUPPORTED, "%s: one B scale per row is not supported with FP8 output", fname);
 
   // alignment: 16-B operand rows (the kernels load 16-B chunks), 16-B output rows
   if (!aligned(a->data, 16) || !aligned(b->data, 16) || va.sr % 16 || vb.sr % 16 || va.sg % 16 || vb.sg % 16)
     return fail(DG_INVALID_ARG, "%s: a and b need 16-byte aligned bases and row/group strides", fname);
   DG_TRY(check_row_strides(va.sr, vb.sr, fname));
-  if (!aligned(d->data, 2)) return fail(DG_INVALID_ARG, "%s: d must be 2-byte aligned", fname);
+  if (fp8_out) {
+    // q rows are written in 4-byte words (16-byte stores when 16-byte aligned)
+    if (!aligned(d->data, 4) || (M > 1 && N > 0 && vd.sr % 4))
+      return fail(DG_INVALID_ARG, "%s: q needs a 4-byte aligned base and row stride", fname);
+    DG_TRY(check_basic(sfq, "sfq", false));
+    DG_TRY(check_dtype(sfq, "sfq", DG_F32));
+    if (sfq->ndim != 2 || sfq->shape[0] != M || sfq->shape[1] != nnb)
+      return fail(DG_INVALID_ARG, "%s: sfq must be F32 [M, ceil(N/128)] = [%lld, %lld]", fname, (long long)M,
+                  (long long)nnb);
+    if (!aligned(sfq->data, 4)) return fail(DG_INVALID_ARG, "%s: sfq must be 4-byte aligned", fname);
+  } else if (!aligned(d->data, 2)) {
+    return fail(DG_INVALID_ARG, "%s: d must be 2-byte aligned", fname);
+  }
   if (!aligned(sfa->data, 4) || !aligned(sfb->data, 4)) return fail(DG_INVALID_ARG, "%s: scales must be 4-byte aligned", fname);
 
   if (mode == dgmi::MODE_CONTIG) {
@@ -253,11 +274,19 @@ int fp8_gemm_common(int mode, const dg_tensor* a, const dg_tensor* b, const dg_t
     if (meta->ndim != 1 || meta->shape[0] != G)
       return fail(DG_INVALID_ARG, "%s: masked_m must be I32 [G = %lld]", fname, (long long)G);
   }
-  DG_TRY(check_no_alias(d, "d", a, "a"));
-  DG_TRY(check_no_alias(d, "d", b, "b"));
-  DG_TRY(check_no_alias(d, "d", sfa, "sfa"));
-  DG_TRY(check_no_alias(d, "d", sfb, "sfb"));
-  if (meta != nullptr) DG_TRY(check_no_alias(d, "d", meta, "metadata"));
+  DG_TRY(check_no_alias(d, dname, a, "a"));
+  DG_TRY(check_no_alias(d, dname, b, "b"));
+  DG_TRY(check_no_alias(d, dname, sfa, "sfa"));
+  DG_TRY(check_no_alias(d, dname, sfb, "sfb"));
+  if (meta != nullptr) DG_TRY(check_no_alias(d, dname, meta, "metadata"));
+  if (fp8_out) {
+    DG_TRY(check_no_alias(sfq, "sfq", a, "a"));
+    DG_TRY(check_no_alias(sfq, "sfq", b, "b"));
+    DG_TRY(check_no_alias(sfq, "sfq", sfa, "sfa"));
+    DG_TRY(check_no_alias(sfq, "sfq", sfb, "sfb"));
+    DG_TRY(check_no_alias(sfq, "sfq", q, "q"));
+    DG_TRY(check_no_alias(sfq, "sfq", c, "c"));
+  }
   // accumulate input (dense form only): D = C + A . B^T, C BF16 or F32 [M, N];
   // c may be d itself (same base and strides), any other overlap is rejected
   bool c_f32 = false;
@@ -271,8 +300,9 @@ int fp8_gemm_common(int mode, const dg_tensor* a, const dg_tensor* b, const dg_t
     c_f32 = c->dtype == DG_F32;
     if (!aligned(c->data, c_f32 ? 4 : 2)) return fail(DG_INVALID_ARG, "%s: c must be element-aligned", fname);
     ldc = c->stride[0];
+    // (with FP8 output, c and q differ in dtype and must not overlap)
     const bool same_as_d = c->data == d->data && c->dtype == d->dtype && ldc == d->stride[0];
-    if (!same_as_d) DG_TRY(check_no_alias(d, "d", c, "c"));
+    if (!same_as_d) DG_TRY(check_no_alias(d, dname, c, "c"));
   }
 
   dgmi::GemmParams p = {};
@@ -280,7 +310,15 @@ int fp8_gemm_common(int mode, const dg_tensor* a, const dg_tensor* b, const dg_t
   p.b = static_cast<const uint8_t*>(b->data);
   p.sfa = sfa->data;
   p.sfb = sfb->data;
-  p.d = static_cast<uint16_t*>(d->data);
+  p.d = fp8_out ? nullptr : static_cast<uint16_t*>(d->data);
+  if (fp8_out) {
+    p.q = static_cast<uint8_t*>(q->data);
+    p.ldq = vd.sr;
+    p.sfq = static_cast<float*>(sfq->data);
+    p.sfq_sm = sfq->stride[0];
+    p.sfq_sn = sfq->stride[1];
+    p.q_ue8m0 = q_ue8m0 ? 1 : 0;
+  }
   p.c = c != nullptr ? c->data : nullptr;
   p.ldc = ldc;
   p.c_f32 = c_f32 ? 1 : 0;
@@ -303,6 +341,7 @@ int fp8_gemm_common(int mode, const dg_tensor* a, const dg_tensor* b, const dg_t
   p.G = (int32_t)G;
   if (M == 0 || N == 0 || G == 0) return ok();
   if (K == 0) return fail(DG_UNSUPPORTED, "%s: K = 0 is not supported", fname);
+  if (fp8_out) return check_launch(dgmi::launch_fp8_gemm_fp8_out(p, sf_fmt, stream), fname);
   return check_launch(dgmi::launch_fp8_gemm(p, mode, sf_fmt | (rowb ? dgmi::SF_ROWB : 0), stream), fname);
 }
 
@@ -470,6 +509,14 @@ int fp8_gemm_nt(const dg_tensor* a, const dg_tensor* b, const dg_tensor* sfa, co
   return fp8_gemm_common(dgmi::MODE_DENSE, a, b, sfa, sfb, c, d, nullptr, 0, stream, "fp8_gemm_nt");
 }
 
+int fp8_gemm_nt_fp8_out(const dg_tensor* a, const dg_tensor* b, const dg_tensor* sfa, const dg_tensor* sfb,
+                        const dg_tensor* c, const dg_tensor* q, const dg_tensor* sfq, int use_ue8m0,
+                        hipStream_t stream) {
+  if (q == nullptr || sfq == nullptr) return fail(DG_INVALID_ARG, "fp8_gemm_nt_fp8_out: q and sfq must not be NULL");
+  return fp8_gemm_common(dgmi::MODE_DENSE, a, b, sfa, sfb, c, nullptr, nullptr, 0, stream, "fp8_gemm_nt_fp8_out", q,
+                         sfq, use_ue8m0);
+}
+
 int m_grouped_fp8_gemm_nt_contiguous(const dg_tensor* a, const dg_tensor* b, const dg_tensor* sfa,
                                      const dg_tensor* sfb, const dg_tensor* d, const dg_tensor* grouped_layout,
                                      hipStream_t stream) {
@@ -560,6 +607,9 @@ int dg_query_config(int32_t kind, int64_t G, int64_t M, int64_t N, int64_t K, dg
   } else if (kind >= DG_KIND_DENSE && kind <= DG_KIND_MASKED) {
     mode = kind == DG_KIND_DENSE ? dgmi::MODE_DENSE : (kind == DG_KIND_CONTIGUOUS ? dgmi::MODE_CONTIG : dgmi::MODE_MASKED);
     c = dgmi::fp8_gemm_plan(mode, G, M, N, K, dgmi::SF_F32);
+  } else if (kind == DG_KIND_DENSE_FP8_OUT) {
+    mode = dgmi::MODE_DENSE;
+    c = dgmi::fp8_out_gemm_plan(M, N);
   } else if (kind >= DG_KIND_DENSE_ROWB && kind <= DG_KIND_MASKED_ROWB) {
     mode = kind == DG_KIND_DENSE_ROWB ? dgmi::MODE_DENSE
                                       : (kind == DG_KIND_CONTIGUOUS_ROWB ? dgmi::MODE_CONTIG : dgmi::MODE_MASKED);

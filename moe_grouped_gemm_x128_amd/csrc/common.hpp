@@ -11,6 +11,7 @@ typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
 typedef int32_t i32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 
 // Scale-factor storage of the FP8 GEMMs: FP32 or packed UE8M0, and the flag
 // SF_ROWB when B carries one scale per row (per 1x128 block) instead of one
@@ -44,7 +45,16 @@ struct GemmParams {
   int32_t M;       // dense: M; contiguous: Msum; masked: max_m
   int32_t N, k_bytes, G;
   int32_t tiles_m, tiles_n;
+  // FP8 output (dense only): D cast per token to E4M3 q [M, N] (row stride
+  // ldq bytes) with FP32 scales sfq [M, ceil(N/128)] (strides in elements)
+  uint8_t* q;
+  float* sfq;
+  int64_t ldq, sfq_sm, sfq_sn;
+  int32_t q_ue8m0;
 };
+
+// Output of a GEMM: BF16 D, or D cast per token to FP8.
+enum GemmOut : int { OUT_BF16 = 0, OUT_FP8 = 1 };
 
 // float -> bfloat16 bits, round to nearest even (NaN stays NaN).
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
@@ -59,6 +69,61 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_floa
 // 2^(e-127) for an unsigned E8M0 exponent byte (byte 0 is the subnormal 2^-127).
 __device__ __forceinline__ float ue8m0_to_f32(uint32_t e) {
   return e == 0 ? __uint_as_float(0x00400000u) : __uint_as_float(e << 23);
+}
+
+// ---------------------------------------------------------------------------
+// FP8 (E4M3) casting of a 1x128 or 128x128 block (the quantizers, and the
+// GEMM epilogue that writes FP8 output):
+//   amax = max |x| over the block, floored at 1e-4
+//   s    = amax / 448 (correctly rounded), or the next power of two (UE8M0)
+//   q    = e4m3(clamp(x / s, -448, 448)) with the correctly rounded quotient
+// ---------------------------------------------------------------------------
+
+// Block scale from the block maximum.
+__device__ __forceinline__ float block_scale(float amax, int ue8m0) {
+  amax = fmaxf(amax, 1e-4f);
+  float s = __fdiv_rn(amax, 448.0f);
+  if (ue8m0) {
+    uint32_t u = __float_as_uint(s);  // s is a positive normal number
+    if (u & 0x007fffffu) u = (u & 0x7f800000u) + 0x00800000u;
+    s = __uint_as_float(u);
+  }
+  return s;
+}
+
+// The correctly rounded binary32 quotient x / s, given r = RN(1 / s) (one
+// correctly rounded division per block): y = RN(x r) is within one ulp of
+// x / s, the residual x - y s is exact with an FMA, and RN(y + r (x - y s))
+// is the correctly rounded quotient (Markstein's correction step) whenever
+// it is a normal number.  Smaller quotients (below 2^-126) encode to E4M3
+// zero whichever way they round, so the FP8 bytes are those of x / s.  The
+// sign is copied from x (s > 0): the correction would turn -0 into +0.
+struct Recip {
+  float s, r;
+};
+__device__ __forceinline__ Recip recip_of(float s) { return Recip{s, __fdiv_rn(1.0f, s)}; }
+__device__ __forceinline__ float quot(float x, Recip d) {
+  const float y = x * d.r;
+  const float e = __builtin_fmaf(-y, d.s, x);
+  return __builtin_copysignf(__builtin_fmaf(e, d.r, y), x);
+}
+
+// Four values -> four E4M3 bytes (little-endian in one word), x / s rounded
+// to nearest even by the hardware conversion after clamping to +-448.
+__device__ __forceinline__ uint32_t encode4(const float v[4], Recip d) {
+  float t[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) t[j] = fminf(fmaxf(quot(v[j], d), -448.0f), 448.0f);
+  // bytes 0-1, then 2-3 (the first conversion's old word only supplies
+  // bits 16-31, which the second overwrites)
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(t[0], t[1], __float_as_int(t[0]), false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(t[2], t[3], w, true);
+  return (uint32_t)w;
+}
+
+__device__ __forceinline__ uint32_t encode1(float v, Recip d) {
+  float t = fminf(fmaxf(quot(v, d), -448.0f), 448.0f);
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(t, 0.0f, 0, false) & 0xffu;
 }
 
 }  // namespace dgmi

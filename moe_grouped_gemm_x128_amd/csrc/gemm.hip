@@ -228,7 +228,126 @@ __device__ __forceinline__ void epilogue_cols4(const GemmParams& p, uint16_t* D,
   }
 }
 
-template <class T, int KIND, int SF, int MODE>
+// Adds C[row, cc .. cc+15] to one row of a wave's accumulators in the
+// permuted layout (16 consecutive columns per lane; columns >= N untouched).
+template <class T>
+__device__ __forceinline__ void add_c_perm(const GemmParams& p, f32x4 (&acc)[T::FN], int row, int cc) {
+  static_assert(T::FN == 4, "16 columns per lane");
+  if (p.c_f32) {
+    const float* crow = static_cast<const float*>(p.c) + (int64_t)row * p.ldc;
+    const bool cvec = ((p.ldc & 3) == 0) && ((reinterpret_cast<uintptr_t>(p.c) & 15) == 0) && cc + 16 <= p.N;
+#pragma unroll
+    for (int f = 0; f < T::FN; ++f) {
+      if (cvec) {
+        const f32x4 cv = *reinterpret_cast<const f32x4*>(crow + cc + 4 * f);
+        acc[f] += cv;
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (cc + 4 * f + e < p.N) acc[f][e] += crow[cc + 4 * f + e];
+      }
+    }
+  } else {
+    const uint16_t* crow = static_cast<const uint16_t*>(p.c) + (int64_t)row * p.ldc;
+    const bool cvec = ((p.ldc & 7) == 0) && ((reinterpret_cast<uintptr_t>(p.c) & 15) == 0) && cc + 16 <= p.N;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      if (cvec) {
+        const i32x4 cv = *reinterpret_cast<const i32x4*>(crow + cc + 8 * h);
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          acc[2 * h + w / 2][2 * (w & 1)] += __uint_as_float((uint32_t)cv[w] << 16);
+          acc[2 * h + w / 2][2 * (w & 1) + 1] += __uint_as_float((uint32_t)cv[w] & 0xffff0000u);
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          if (cc + 8 * h + e < p.N) acc[2 * h + e / 4][e & 3] += bf16_to_f32(crow[cc + 8 * h + e]);
+      }
+    }
+  }
+}
+
+// FP8-output epilogue (dense, 64-column wave tiles in the permuted layout):
+// D is rounded to BF16 (C added first, as in the BF16 epilogue) and cast per
+// token exactly as per_token_cast_to_fp8 casts a BF16 tensor: per row and
+// 128-column block, amax over the block (the 16 columns of each of four lanes
+// of a wave, and of its neighbouring wave, exchanged through LDS), s =
+// amax/448 or its UE8M0 round-up, q = e4m3(x / s).  ("DeepInside DeepGEMM",
+// section 5: the FP8 cast fused into the kernel that produces the tensor.)
+template <class T>
+__device__ __forceinline__ void epilogue_fp8(const GemmParams& p, f32x4 (&acc)[T::FM][T::FN], uint8_t* lds, int m0,
+                                             int n0, int wm, int wn, int lane, int row_lim) {
+  static_assert(T::PERM && T::WN % 2 == 0 && T::BN % 128 == 0 && T::BM * T::WN * 4 <= T::B_BYTES,
+                "a 128-column block is the 64 columns of two neighbouring waves");
+  const int fr = lane & 15;
+  const int col0 = n0 + wn * T::TN + (lane >> 4) * 16;  // this lane's 16 consecutive columns
+  float* xch = reinterpret_cast<float*>(lds);  // [BM][WN] wave maxima per row
+  float wmax[T::FM];
+  // every wave is past its K loop (its LDS reads and loads drained) before
+  // the stages are reused; the barriers order the LDS exchange (fenced, so
+  // the compiler keeps the LDS accesses on their side)
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < T::FM; ++i) {
+    const int rl = wm * T::TM + i * 16 + fr;
+    const int row = m0 + rl;
+    if (p.c != nullptr && row < row_lim) add_c_perm<T>(p, acc[i], row, col0);
+    // the BF16 value of D (the hardware conversion rounds to nearest even,
+    // as the BF16 epilogue does).  Columns past N hold +0 (B rows past N load
+    // as zeros, C is not added there) or NaN (a non-finite B scale), and
+    // neither changes the block maximum: fmaxf passes over NaN.
+    float m = 0.0f;
+#pragma unroll
+    for (int f = 0; f < T::FN; ++f) {
+      acc[i][f] = __builtin_convertvector(__builtin_convertvector(acc[i][f], bf16x4), f32x4);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) m = fmaxf(m, fabsf(acc[i][f][e]));
+    }
+    m = fmaxf(m, __shfl_xor(m, 16, 64));
+    m = fmaxf(m, __shfl_xor(m, 32, 64));
+    wmax[i] = m;
+    if ((lane >> 4) == 0) xch[rl * T::WN + wn] = m;
+  }
+  __syncthreads();
+  const bool vec_ok = ((p.ldq & 15) == 0) && ((reinterpret_cast<uintptr_t>(p.q) & 15) == 0);
+  const int blk = (n0 + (wn & ~1) * T::TN) / 128;  // this wave pair's 128-column block
+#pragma unroll
+  for (int i = 0; i < T::FM; ++i) {
+    const int rl = wm * T::TM + i * 16 + fr;
+    const int row = m0 + rl;
+    if (row >= row_lim || blk * 128 >= p.N) continue;
+    const float amax = fmaxf(wmax[i], xch[rl * T::WN + (wn ^ 1)]);
+    const float s = block_scale(amax, p.q_ue8m0);
+    const Recip d = recip_of(s);
+    uint32_t w[T::FN];
+#pragma unroll
+    for (int f = 0; f < T::FN; ++f) {
+      const float v[4] = {acc[i][f][0], acc[i][f][1], acc[i][f][2], acc[i][f][3]};
+      w[f] = encode4(v, d);
+    }
+    uint8_t* qrow = p.q + (int64_t)row * p.ldq;
+    if (vec_ok && col0 + 16 <= p.N) {
+      *reinterpret_cast<i32x4*>(qrow + col0) = i32x4{(int)w[0], (int)w[1], (int)w[2], (int)w[3]};
+    } else {
+      // q rows are 4-byte aligned
+#pragma unroll
+      for (int f = 0; f < T::FN; ++f) {
+        const int c = col0 + 4 * f;
+        if (c + 4 <= p.N) {
+          *reinterpret_cast<uint32_t*>(qrow + c) = w[f];
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (c + e < p.N) qrow[c + e] = (uint8_t)(w[f] >> (8 * e));
+        }
+      }
+    }
+    if ((lane >> 4) == 0 && (wn & 1) == 0) p.sfq[(int64_t)row * p.sfq_sm + (int64_t)blk * p.sfq_sn] = s;
+  }
+}
+
+template <class T, int KIND, int SF, int MODE, int OUT = OUT_BF16>
 __global__ __launch_bounds__(T::NT) void gemm_kernel(const GemmParams p) {
   constexpr int S = T::STAGES;
   constexpr bool FP8 = KIND == KIND_FP8;
@@ -723,9 +842,19 @@ __global__ __launch_bounds__(T::NT) void gemm_kernel(const GemmParams p) {
     }
   }
   __builtin_amdgcn_s_waitcnt(0);  // drain the redundant last loads before LDS is reused or freed
-  if (!live) return;
+  if (!live) {
+    if constexpr (OUT == OUT_FP8) {
+      // the FP8 epilogue's two barriers (the rows of this wave are past M,
+      // and so are those of its partner wave, so nothing here is read)
+      __syncthreads();
+      __syncthreads();
+    }
+    return;
+  }
 
-  if constexpr (!T::PERM) {
+  if constexpr (OUT == OUT_FP8) {
+    epilogue_fp8<T>(p, acc, lds_b0, m0, n0, wm, wn, lane, row_lim);
+  } else if constexpr (!T::PERM) {
     epilogue_cols4<T>(p, D, acc, m0, n0, wm, wn, lane, lo, hi, row_lim, MODE == MODE_DENSE);
   } else {
     // ---- epilogue: BF16, row m = lane%16 of each fragment row, 16 consecutive columns per lane
@@ -837,6 +966,17 @@ hipError_t launch_tile(const GemmParams& p, int mode, int sf_fmt, int64_t grid, 
 #undef DGMI_LAUNCH
     return hipGetLastError();
   }
+}
+
+// Launch one tile configuration of the dense FP8 GEMM with FP8 output
+// (block scales only).
+template <class T>
+hipError_t launch_tile_fp8_out(const GemmParams& p, int sf_fmt, int64_t grid, hipStream_t stream) {
+  const dim3 g((unsigned)grid), b(T::NT);
+  if (sf_fmt == SF_F32) gemm_kernel<T, KIND_FP8, SF_F32, MODE_DENSE, OUT_FP8><<<g, b, 0, stream>>>(p);
+  else if (sf_fmt == SF_UE8M0) gemm_kernel<T, KIND_FP8, SF_UE8M0, MODE_DENSE, OUT_FP8><<<g, b, 0, stream>>>(p);
+  else return hipErrorInvalidValue;
+  return hipGetLastError();
 }
 
 template <class T, int KIND>
@@ -984,6 +1124,31 @@ int64_t plan_grid(const GemmPlan& plan, int part, int mode, int64_t G, int64_t M
 
 hipError_t launch_fp8_gemm(GemmParams p, int mode, int sf_fmt, hipStream_t stream) {
   return launch_plan<KIND_FP8>(fp8_gemm_plan(mode, p.G, p.M, p.N, p.k_bytes, sf_fmt), p, mode, sf_fmt, stream);
+}
+
+// Dense FP8 GEMM with FP8 output: the tiles whose waves cover 64 columns
+// (a 128-column block is two neighbouring waves), one launch: 256 x 256
+// above 128 rows, the 128-row tiles below.
+GemmPlan fp8_out_gemm_plan(int64_t M, int64_t N) {
+  GemmPlan p;
+  p.parts = 1;
+  p.n_split = N;
+  if (M > 128) p.cfg[0] = make_cfg<TileL, KIND_FP8>(VAR_L);
+  else p.cfg[0] = N <= 128 ? make_cfg<TileS, KIND_FP8>(VAR_S) : make_cfg<TileW, KIND_FP8>(VAR_W);
+  return p;
+}
+
+hipError_t launch_fp8_gemm_fp8_out(GemmParams p, int sf_fmt, hipStream_t stream) {
+  const TileCfg cfg = fp8_out_gemm_plan(p.M, p.N).cfg[0];
+  p.tiles_m = (p.M + cfg.bm - 1) / cfg.bm;
+  p.tiles_n = (p.N + cfg.bn - 1) / cfg.bn;
+  const int64_t grid = gemm_grid(cfg, MODE_DENSE, 1, p.M, p.N);
+  if (grid == 0) return hipSuccess;
+  switch (cfg.variant) {
+    case VAR_L: return launch_tile_fp8_out<TileL>(p, sf_fmt, grid, stream);
+    case VAR_W: return launch_tile_fp8_out<TileW>(p, sf_fmt, grid, stream);
+    default: return launch_tile_fp8_out<TileS>(p, sf_fmt, grid, stream);
+  }
 }
 
 // BF16 GEMMs: the same tile choice as the FP8 GEMM (a K-slice is 64 BF16

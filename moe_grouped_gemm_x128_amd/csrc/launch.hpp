@@ -59,6 +59,10 @@ int64_t gemm_grid(const TileCfg& cfg, int mode, int64_t G, int64_t M, int64_t N)
 int64_t plan_grid(const GemmPlan& plan, int part, int mode, int64_t G, int64_t M, int64_t N);
 // sf_fmt: SF_F32 or SF_UE8M0, plus SF_ROWB for one B scale per row of B
 hipError_t launch_fp8_gemm(GemmParams p, int mode, int sf_fmt, hipStream_t stream);
+// Dense FP8 GEMM whose output D is cast per token to FP8 (p.q, p.sfq) in the
+// epilogue; block scales only (sf_fmt SF_F32 or SF_UE8M0).
+GemmPlan fp8_out_gemm_plan(int64_t M, int64_t N);
+hipError_t launch_fp8_gemm_fp8_out(GemmParams p, int sf_fmt, hipStream_t stream);
 // BF16 GEMMs: same kernel body; byte strides in p, no scales
 hipError_t launch_bf16_gemm(GemmParams p, int mode, hipStream_t stream);
 

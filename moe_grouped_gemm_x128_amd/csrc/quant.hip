@@ -39,50 +39,8 @@ __device__ __forceinline__ void load4(const uint16_t* p, float v[4]) {
   v[3] = __uint_as_float(t.y & 0xffff0000u);
 }
 
-// Block scale from the block maximum.
-__device__ __forceinline__ float block_scale(float amax, int ue8m0) {
-  amax = fmaxf(amax, 1e-4f);
-  float s = __fdiv_rn(amax, 448.0f);
-  if (ue8m0) {
-    uint32_t u = __float_as_uint(s);  // s is a positive normal number
-    if (u & 0x007fffffu) u = (u & 0x7f800000u) + 0x00800000u;
-    s = __uint_as_float(u);
-  }
-  return s;
-}
-
-// The correctly rounded binary32 quotient x / s, given r = RN(1 / s) (one
-// correctly rounded division per block): y = RN(x r) is within one ulp of
-// x / s, the residual x - y s is exact with an FMA, and RN(y + r (x - y s))
-// is the correctly rounded quotient (Markstein's correction step) whenever
-// it is a normal number.  Smaller quotients (below 2^-126) encode to E4M3
-// zero whichever way they round, so the FP8 bytes are those of x / s.  The
-// sign is copied from x (s > 0): the correction would turn -0 into +0.
-struct Recip {
-  float s, r;
-};
-__device__ __forceinline__ Recip recip_of(float s) { return Recip{s, __fdiv_rn(1.0f, s)}; }
-__device__ __forceinline__ float quot(float x, Recip d) {
-  const float y = x * d.r;
-  const float e = __builtin_fmaf(-y, d.s, x);
-  return __builtin_copysignf(__builtin_fmaf(e, d.r, y), x);
-}
-
-// Four values -> four E4M3 bytes (little-endian in one word), x / s rounded
-// to nearest even by the hardware conversion after clamping to +-448.
-__device__ __forceinline__ uint32_t encode4(const float v[4], Recip d) {
-  float t[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) t[j] = fminf(fmaxf(quot(v[j], d), -448.0f), 448.0f);
-  int w = __builtin_amdgcn_cvt_pk_fp8_f32(t[0], t[1], 0, false);
-  w = __builtin_amdgcn_cvt_pk_fp8_f32(t[2], t[3], w, true);
-  return (uint32_t)w;
-}
-
-__device__ __forceinline__ uint32_t encode1(float v, Recip d) {
-  float t = fminf(fmaxf(quot(v, d), -448.0f), 448.0f);
-  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(t, 0.0f, 0, false) & 0xffu;
-}
+// block_scale, Recip, quot, encode4 and encode1: common.hpp (shared with the
+// GEMM epilogue that writes FP8 output).
 
 // ---------------------------------------------------------------------------
 // per-token: one half-wave (32 lanes x 4 elements) per 1x128 block, four

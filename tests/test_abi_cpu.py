@@ -87,7 +87,23 @@ def test_query_config_is_a_pure_function_of_shapes(lib):
     # 256-row contiguous tiles launch a second grid copy for tiles split between two groups
     assert c["grid"] == (2 * tiles if c["block_m"] == 256 else tiles) and bc["grid"] == c["grid"]
     with pytest.raises(binding.DgmiError):
-        binding.query_config(9, 1, 1, 1, 1)
+        binding.query_config(10, 1, 1, 1, 1)
+
+
+@pytest.mark.parametrize("M,N,tile", [
+    (4096, 7168, (256, 256, 512)),  # above 128 rows: 256 x 256, whatever fills the last round
+    (4096, 2112, (256, 256, 512)),
+    (129, 4096, (256, 256, 512)),
+    (128, 4096, (128, 256, 512)),  # up to 128 rows: the 128-row tiles
+    (64, 128, (128, 128, 256)),
+    (1, 100, (128, 128, 256)),
+])
+def test_fp8_out_plan(lib, M, N, tile):
+    # the FP8-output GEMM uses only the tiles whose waves cover 64 columns, one launch
+    c = binding.query_config(binding.DG_KIND_DENSE_FP8_OUT, 1, M, N, 7168)
+    assert (c["block_m"], c["block_n"], c["threads"]) == tile
+    assert c["n_split"] == N and c["block_n2"] == 0 and c["grid2"] == 0
+    assert c["grid"] == -(-M // tile[0]) * -(-N // tile[1])
 
 
 @pytest.mark.parametrize("N,K,fp8_plan,bf16_plan", [
@@ -293,3 +309,52 @@ def test_empty_problems_return_ok_without_a_launch(lib):
                                      ctypes.byref(D(_t((0, 2), f32))), 1, None) == 0
     assert lib.pack_ue8m0_to_int(ctypes.byref(D(_t((3, 0), f32))), ctypes.byref(D(_t((3, 0), i32))), None, None) == 0
     assert lib.pack_ue8m0_to_int(ctypes.byref(D(_t((0, 8), f32))), ctypes.byref(D(_t((0, 2), i32))), None, None) == 0
+
+
+def _call_fp8_out(lib, a, b, sfa, sfb, q, sfq, c=None, ue8m0=0):
+    D = binding.describe
+    r = lambda t: ctypes.byref(D(t)) if t is not None else None  # noqa: E731
+    return lib.fp8_gemm_nt_fp8_out(r(a), r(b), r(sfa), r(sfb), r(c), r(q), r(sfq), ue8m0, None)
+
+
+def test_fp8_out_validation_errors(lib):
+    M, N, K = 128, 256, 512
+    f32, u8, bf = torch.float32, torch.uint8, torch.bfloat16
+    a, b = _t((M, K), u8), _t((N, K), u8)
+    sfa, sfb = _t((M, K // 128), f32), _t((N // 128, K // 128), f32)
+    q, sfq = _t((M, N), u8), _t((M, N // 128), f32)
+    # missing outputs
+    assert _call_fp8_out(lib, a, b, sfa, sfb, None, sfq) == binding.DG_INVALID_ARG
+    assert _call_fp8_out(lib, a, b, sfa, sfb, q, None) == binding.DG_INVALID_ARG
+    # q must be E4M3 [M, N]
+    assert _call_fp8_out(lib, a, b, sfa, sfb, _t((M, N), bf), sfq) == binding.DG_INVALID_ARG
+    assert _call_fp8_out(lib, a, b, sfa, sfb, _t((M, N + 1), u8), sfq) == binding.DG_INVALID_ARG
+    # q rows 4-byte aligned
+    assert _call_fp8_out(lib, a, b, sfa, sfb, _t((M, N + 2), u8)[:, :N], sfq) == binding.DG_INVALID_ARG
+    assert "4-byte" in binding.last_error()
+    # sfq F32 [M, ceil(N/128)]
+    assert _call_fp8_out(lib, a, b, sfa, sfb, q, _t((M, N // 128 + 1), f32)) == binding.DG_INVALID_ARG
+    assert _call_fp8_out(lib, a, b, sfa, sfb, q, _t((M, N // 128), bf)) == binding.DG_INVALID_ARG
+    assert _call_fp8_out(lib, a, b, sfa, sfb, q, _t((M + 1, N // 128), f32)) == binding.DG_INVALID_ARG
+    # one B scale per row: not supported with FP8 output
+    assert _call_fp8_out(lib, a, b, sfa, _t((N, K // 128), f32), q, sfq) == binding.DG_UNSUPPORTED
+    # sfq overlapping q, c overlapping q
+    buf = torch.empty(M * N + 64, dtype=u8)
+    q2 = buf[: M * N].view(M, N)
+    sfq2 = buf[:8].view(f32)[: M * (N // 128)].view(M, N // 128) if M * N // 128 * 4 <= 8 else None
+    alias = torch.empty(M * N, dtype=u8)
+    assert _call_fp8_out(lib, a, b, sfa, sfb, alias.view(M, N), alias[: M * (N // 128) * 4].view(f32).view(M, N // 128)) \
+        == binding.DG_INVALID_ARG
+    assert "overlaps" in binding.last_error()
+    cbuf = torch.empty(M * N, dtype=bf)
+    assert _call_fp8_out(lib, a, b, sfa, sfb, cbuf.view(u8)[: M * N].view(M, N), sfq, c=cbuf.view(M, N)) \
+        == binding.DG_INVALID_ARG
+    del q2, sfq2
+    # c of the wrong shape
+    assert _call_fp8_out(lib, a, b, sfa, sfb, q, sfq, c=_t((M, N - 1), bf)) == binding.DG_INVALID_ARG
+    # K not a multiple of 128
+    assert _call_fp8_out(lib, _t((M, 200), u8), _t((N, 200), u8), _t((M, 2), f32), _t((2, 2), f32), q, sfq) \
+        == binding.DG_UNSUPPORTED
+    # empty problems launch nothing
+    assert _call_fp8_out(lib, _t((0, K), u8), b, _t((0, 4), f32), sfb, _t((0, N), u8), _t((0, 2), f32)) == 0
+    assert _call_fp8_out(lib, a, _t((0, K), u8), sfa, _t((0, 4), f32), _t((M, 0), u8), _t((M, 0), f32)) == 0
