@@ -8,6 +8,7 @@
 namespace dgmi {
 
 typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+typedef int32_t i32x2 __attribute__((ext_vector_type(2)));
 typedef int32_t i32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -65,6 +66,19 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
 }
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
+
+// Four floats -> four bfloat16 (bits, little-endian in two words), rounded to
+// nearest even by the hardware conversion (two v_cvt_pk_bf16_f32): the
+// values of f32_to_bf16_rne for every non-NaN input; NaN stays NaN.
+__device__ __forceinline__ i32x2 to_bf16x4_bits(f32x4 v) {
+  return __builtin_bit_cast(i32x2, __builtin_convertvector(v, bf16x4));
+}
+
+// The same four values rounded by f32_to_bf16_rne (integer arithmetic).
+__device__ __forceinline__ i32x2 to_bf16x4_bits_int(f32x4 v) {
+  return i32x2{(int)((uint32_t)f32_to_bf16_rne(v[0]) | ((uint32_t)f32_to_bf16_rne(v[1]) << 16)),
+               (int)((uint32_t)f32_to_bf16_rne(v[2]) | ((uint32_t)f32_to_bf16_rne(v[3]) << 16))};
+}
 
 // 2^(e-127) for an unsigned E8M0 exponent byte (byte 0 is the subnormal 2^-127).
 __device__ __forceinline__ float ue8m0_to_f32(uint32_t e) {

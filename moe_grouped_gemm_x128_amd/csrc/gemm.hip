@@ -162,7 +162,6 @@ __device__ __forceinline__ void band_order(int t, int tiles_m, int tiles_n, int 
   tn = in_band / rows;
 }
 
-typedef int32_t i32x2 __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ bf16x8 lo_bf16(const i32x8& v) { return __builtin_bit_cast(bf16x8, i32x4{v[0], v[1], v[2], v[3]}); }
 __device__ __forceinline__ bf16x8 hi_bf16(const i32x8& v) { return __builtin_bit_cast(bf16x8, i32x4{v[4], v[5], v[6], v[7]}); }
@@ -215,8 +214,8 @@ __device__ __forceinline__ void epilogue_cols4(const GemmParams& p, uint16_t* D,
           }
         }
       }
-      const uint32_t w0 = (uint32_t)f32_to_bf16_rne(v[0]) | ((uint32_t)f32_to_bf16_rne(v[1]) << 16);
-      const uint32_t w1 = (uint32_t)f32_to_bf16_rne(v[2]) | ((uint32_t)f32_to_bf16_rne(v[3]) << 16);
+      const i32x2 wv = to_bf16x4_bits(v);
+      const uint32_t w0 = (uint32_t)wv[0], w1 = (uint32_t)wv[1];
       if (vec_ok && c + 4 <= p.N) {
         *reinterpret_cast<i32x2*>(drow + c) = i32x2{(int)w0, (int)w1};
       } else {
@@ -907,8 +906,11 @@ __global__ __launch_bounds__(T::NT) void gemm_kernel(const GemmParams p) {
       uint32_t packed[8];
 #pragma unroll
       for (int f = 0; f < T::FN; ++f) {
-        packed[2 * f] = (uint32_t)f32_to_bf16_rne(acc[i][f][0]) | ((uint32_t)f32_to_bf16_rne(acc[i][f][1]) << 16);
-        packed[2 * f + 1] = (uint32_t)f32_to_bf16_rne(acc[i][f][2]) | ((uint32_t)f32_to_bf16_rne(acc[i][f][3]) << 16);
+        // (the contiguous kernels keep the integer rounding: with the
+        // hardware conversion the 256 x 256 UE8M0 one spills in its K loop)
+        const i32x2 wv = MODE == MODE_CONTIG ? to_bf16x4_bits_int(acc[i][f]) : to_bf16x4_bits(acc[i][f]);
+        packed[2 * f] = (uint32_t)wv[0];
+        packed[2 * f + 1] = (uint32_t)wv[1];
       }
       uint16_t* drow = D + (int64_t)row * p.ldd;
 #pragma unroll
