@@ -1,7 +1,7 @@
 """Benchmark of the block-scaled FP8 GEMM path on one MI355X.
 
     python bench.py [--steps K] [--warmup W] [--settle-seconds S]
-                    [--workload dense|contiguous|masked|masked_graph|bf16_dense]
+                    [--workload dense|contiguous|masked|masked_graph|bf16_dense|dense_rowb|dense_fp8_out]
 
 Before the W warmup steps, untimed steps run for S seconds (default 1): under
 sustained GEMM load the GPU clock dips for the first few milliseconds and
@@ -32,6 +32,8 @@ Other workloads (for the measurements in the design notes):
                   (metric against the 2.5 PFLOP/s BF16 MFMA peak)
   dense_rowb   -- the five dense shapes with one B scale per row of B (B cast per
                   token, scales [N, K/128]), as in the pages' dense example
+  dense_fp8_out -- the five dense shapes with FP8 output: the GEMM's BF16 result
+                  cast per token to E4M3 in its epilogue (fp8_gemm_nt_fp8_out)
 """
 
 import argparse
@@ -137,6 +139,42 @@ class DenseRowBWorkload(DenseWorkload):
     def config(self):
         return {"workload": self.name, "M": self.M, "shapes_NK": self.shapes,
                 "scales": "fp32 1x128 (A) / 1x128 per row (B)", "out": "bf16"}
+
+
+class DenseFp8OutWorkload(DenseWorkload):
+    """The five dense shapes with FP8 output: fp8_gemm_nt_fp8_out casts the
+    BF16 result per token in the GEMM's epilogue (q [M, N] E4M3 and scales
+    [M, N/128]); one step = both input casts and the GEMM per shape."""
+    name = "dense_fp8_v3_shapes_fp8_out"
+
+    def __init__(self, torch, mg, synth):
+        super().__init__(torch, mg, synth)
+        for (N, K), buf in zip(self.shapes, self.bufs):
+            dev = buf["xa"].device
+            del buf["d"]
+            buf["q"] = torch.empty((self.M, N), dtype=torch.uint8, device=dev)
+            buf["sfq"] = torch.empty((self.M, (N + 127) // 128), dtype=torch.float32, device=dev)
+        self.gemm_bytes = [self.M * K + N * K + 4 * (self.M * K // 128 + ((N + 127) // 128) * (K // 128))
+                           + self.M * N + 4 * self.M * ((N + 127) // 128) for N, K in self.shapes]
+
+    def step(self, events=None):
+        mg = self.mg
+        for i, b in enumerate(self.bufs):
+            mg.per_token_cast_to_fp8(b["xa"], b["a"], b["sfa"])
+            mg.per_block_cast_to_fp8(b["xb"], b["b"], b["sfb"])
+            if events is not None:
+                events[i][0].record()
+            mg.fp8_gemm_nt_fp8_out(b["a"], b["b"], b["sfa"], b["sfb"], None, b["q"], b["sfq"])
+            if events is not None:
+                events[i][1].record()
+
+    def plan_args(self, i):
+        N, K = self.shapes[i]
+        return ("DG_KIND_DENSE_FP8_OUT", 1, self.M, N, K)
+
+    def config(self):
+        return {"workload": self.name, "M": self.M, "shapes_NK": self.shapes,
+                "scales": "fp32 1x128 (A) / 128x128 (B)", "out": "fp8 e4m3, fp32 1x128 scales (per-token cast fused)"}
 
 
 class Bf16DenseWorkload:
@@ -472,7 +510,8 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="dense",
-                    choices=["dense", "contiguous", "masked", "masked_graph", "bf16_dense", "dense_rowb"])
+                    choices=["dense", "contiguous", "masked", "masked_graph", "bf16_dense", "dense_rowb",
+                             "dense_fp8_out"])
     ap.add_argument("--settle-seconds", type=float, default=1.0,
                     help="untimed steps run for this long before the warmup steps, so that the timed steps see "
                          "the GPU's steady sustained clock rather than the dip of its first milliseconds under load")
@@ -500,7 +539,7 @@ def main():
     log(f"setting up workload {args.workload}")
     W = {"dense": DenseWorkload, "contiguous": ContiguousWorkload, "masked": MaskedWorkload,
          "masked_graph": MaskedGraphWorkload, "bf16_dense": Bf16DenseWorkload,
-         "dense_rowb": DenseRowBWorkload}[args.workload](torch, mg, synth)
+         "dense_rowb": DenseRowBWorkload, "dense_fp8_out": DenseFp8OutWorkload}[args.workload](torch, mg, synth)
     torch.cuda.synchronize()
 
     # Power-state settle: under sustained GEMM load the clock dips for the first
@@ -613,6 +652,10 @@ def main():
         metric = "BF16 GEMM TFLOPS (% BF16 MFMA peak)"
         unit = "TFLOPS"
         roof["kernel"] = "gemm_kernel (BF16 kind)"
+    elif args.workload == "dense_fp8_out":
+        metric = "FP8 block-scaled GEMM with per-token FP8 output TFLOPS (% FP8 MFMA peak)"
+        unit = "TFLOPS"
+        roof["kernel"] = "gemm_kernel (FP8 kind, FP8-output epilogue)"
     else:
         metric = "FP8 block-scaled GEMM TFLOPS (% FP8 MFMA peak)"
         unit = "TFLOPS"
