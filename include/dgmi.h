@@ -87,7 +87,11 @@ int dgmi_init(void);
  *       dtype and strides: an in-place D += A . B^T), any other overlap with d
  *       is rejected.  Each element of C is added to the FP32 accumulator
  *       before the BF16 rounding (same section: D = C + A @ B.T).
- *   d   BF16 [M, N], any row stride (innermost stride 1)
+ *   d   BF16 [M, N], any row stride (innermost stride 1); or F32 [M, N],
+ *       4-B aligned: the FP32 accumulator (C added) stored without rounding
+ *       (the section's call takes the output dtype as an argument); with
+ *       c = d in F32 this is the in-place D += A . B^T.  F32 d takes one
+ *       scale per 128x128 block of B only (per-row scales: DG_UNSUPPORTED).
  * D[m,n] = C[m,n] + sum_kb (sum_{k in kb} A[m,k] B[n,k]) * sfa[m,kb] * sfb[n/128,kb]
  * (sfb[n,kb] with one scale per row of B).
  * K must be a multiple of 128; M and N are arbitrary.
@@ -170,7 +174,8 @@ int m_grouped_bf16_gemm_nt_masked(const dg_tensor* a, const dg_tensor* b,
  * layout and accumulate form of fp8_gemm_nt, FP32 accumulation, BF16 out.
  *   a BF16 [M, K], b BF16 [N, K] (row strides multiples of 8 elements,
  *   16-B aligned bases); c NULL or BF16/F32 [M, N] as for fp8_gemm_nt (may be
- *   d itself); d BF16 [M, N], any row stride.  K must be a multiple of 64.
+ *   d itself); d BF16 [M, N] or F32 [M, N] (4-B aligned, the FP32 accumulator
+ *   stored as is), any row stride.  K must be a multiple of 64.
  */
 int bf16_gemm_nt(const dg_tensor* a, const dg_tensor* b, const dg_tensor* c, const dg_tensor* d,
                  hipStream_t stream);

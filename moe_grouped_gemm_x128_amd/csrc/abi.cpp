@@ -196,7 +196,9 @@ int fp8_gemm_common(int mode, const dg_tensor* a, const dg_tensor* b, const dg_t
   DG_TRY(check_basic(d, dname, true));
   DG_TRY(check_dtype(a, "a", DG_E4M3));
   DG_TRY(check_dtype(b, "b", DG_E4M3));
-  DG_TRY(check_dtype(d, dname, fp8_out ? DG_E4M3 : DG_BF16));
+  // d: BF16, or F32 for the dense GEMM (the FP32 accumulator stored as is)
+  const bool d_f32 = !fp8_out && mode == dgmi::MODE_DENSE && d->dtype == DG_F32;
+  DG_TRY(check_dtype(d, dname, fp8_out ? DG_E4M3 : (d_f32 ? DG_F32 : DG_BF16)));
   if (sfa == nullptr || sfb == nullptr) return fail(DG_INVALID_ARG, "%s: scale descriptors must not be NULL", fname);
   if (sfa->dtype != sfb->dtype) return fail(DG_INVALID_ARG, "%s: sfa and sfb must have the same dtype", fname);
   const int sf_fmt = sfa->dtype == DG_I32 ? dgmi::SF_UE8M0 : dgmi::SF_F32;
@@ -240,8 +242,9 @@ int fp8_gemm_common(int mode, const dg_tensor* a, const dg_tensor* b, const dg_t
   if (mode == dgmi::MODE_DENSE && (sfb->ndim != 2 || sfa->ndim != 2))
     return fail(DG_INVALID_ARG, "%s: sfa and sfb must be 2-D", fname);
   if (mode == dgmi::MODE_CONTIG && sfb->ndim != 3) return fail(DG_INVALID_ARG, "%s: sfb must be [G, ceil(N/128), ..]", fname);
-  if (fp8_out && rowb)
-    return fail(DG_UNSUPPORTED, "%s: one B scale per row is not supported with FP8 output", fname);
+  if ((fp8_out || d_f32) && rowb)
+    return fail(DG_UNSUPPORTED, "%s: one B scale per row is not supported with %s output", fname,
+                fp8_out ? "FP8" : "F32");
 
   // alignment: 16-B operand rows (the kernels load 16-B chunks), 16-B output rows
   if (!aligned(a->data, 16) || !aligned(b->data, 16) || va.sr % 16 || vb.sr % 16 || va.sg % 16 || vb.sg % 16)
@@ -257,8 +260,8 @@ int fp8_gemm_common(int mode, const dg_tensor* a, const dg_tensor* b, const dg_t
       return fail(DG_INVALID_ARG, "%s: sfq must be F32 [M, ceil(N/128)] = [%lld, %lld]", fname, (long long)M,
                   (long long)nnb);
     if (!aligned(sfq->data, 4)) return fail(DG_INVALID_ARG, "%s: sfq must be 4-byte aligned", fname);
-  } else if (!aligned(d->data, 2)) {
-    return fail(DG_INVALID_ARG, "%s: d must be 2-byte aligned", fname);
+  } else if (!aligned(d->data, d_f32 ? 4 : 2)) {
+    return fail(DG_INVALID_ARG, "%s: d must be element-aligned", fname);
   }
   if (!aligned(sfa->data, 4) || !aligned(sfb->data, 4)) return fail(DG_INVALID_ARG, "%s: scales must be 4-byte aligned", fname);
 
@@ -311,6 +314,7 @@ int fp8_gemm_common(int mode, const dg_tensor* a, const dg_tensor* b, const dg_t
   p.sfa = sfa->data;
   p.sfb = sfb->data;
   p.d = fp8_out ? nullptr : static_cast<uint16_t*>(d->data);
+  p.d_f32 = d_f32 ? 1 : 0;
   if (fp8_out) {
     p.q = static_cast<uint8_t*>(q->data);
     p.ldq = vd.sr;
@@ -405,7 +409,9 @@ int bf16_gemm_common(int mode, const dg_tensor* a, const dg_tensor* b, const dg_
   DG_TRY(check_basic(d, "d", true));
   DG_TRY(check_dtype(a, "a", DG_BF16));
   DG_TRY(check_dtype(b, "b", DG_BF16));
-  DG_TRY(check_dtype(d, "d", DG_BF16));
+  // d: BF16, or F32 for the dense GEMM (the FP32 accumulator stored as is)
+  const bool d_f32 = mode == dgmi::MODE_DENSE && d->dtype == DG_F32;
+  DG_TRY(check_dtype(d, "d", d_f32 ? DG_F32 : DG_BF16));
   View3 va, vb, vd;
   int64_t G = 1;
   if (mode == dgmi::MODE_DENSE) {
@@ -434,7 +440,7 @@ int bf16_gemm_common(int mode, const dg_tensor* a, const dg_tensor* b, const dg_
   if (!aligned(a->data, 16) || !aligned(b->data, 16) || va.sr % 8 || vb.sr % 8 || va.sg % 8 || vb.sg % 8)
     return fail(DG_INVALID_ARG, "%s: a and b need 16-byte aligned bases and row/group strides", fname);
   DG_TRY(check_row_strides(2 * va.sr, 2 * vb.sr, fname));
-  if (!aligned(d->data, 2)) return fail(DG_INVALID_ARG, "%s: d must be 2-byte aligned", fname);
+  if (!aligned(d->data, d_f32 ? 4 : 2)) return fail(DG_INVALID_ARG, "%s: d must be element-aligned", fname);
   if (mode == dgmi::MODE_CONTIG) {
     if (M % 128 != 0) return fail(DG_INVALID_ARG, "%s: Msum = %lld is not a multiple of 128", fname, (long long)M);
     DG_TRY(check_basic(meta, "grouped_layout", true));
@@ -467,6 +473,7 @@ int bf16_gemm_common(int mode, const dg_tensor* a, const dg_tensor* b, const dg_
   p.a = static_cast<const uint8_t*>(a->data);
   p.b = static_cast<const uint8_t*>(b->data);
   p.d = static_cast<uint16_t*>(d->data);
+  p.d_f32 = d_f32 ? 1 : 0;
   p.c = c != nullptr ? c->data : nullptr;
   p.ldc = ldc;
   p.c_f32 = c_f32 ? 1 : 0;

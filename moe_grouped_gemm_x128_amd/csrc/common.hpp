@@ -52,10 +52,11 @@ struct GemmParams {
   float* sfq;
   int64_t ldq, sfq_sm, sfq_sn;
   int32_t q_ue8m0;
+  int32_t d_f32;  // dense only: d holds F32 (row stride ldd in F32 elements)
 };
 
-// Output of a GEMM: BF16 D, or D cast per token to FP8.
-enum GemmOut : int { OUT_BF16 = 0, OUT_FP8 = 1 };
+// Output of a GEMM: BF16 D, D cast per token to FP8, or the FP32 D itself.
+enum GemmOut : int { OUT_BF16 = 0, OUT_FP8 = 1, OUT_F32 = 2 };
 
 // float -> bfloat16 bits, round to nearest even (NaN stays NaN).
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {

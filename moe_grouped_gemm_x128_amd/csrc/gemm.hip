@@ -171,7 +171,7 @@ __device__ __forceinline__ bf16x8 hi_bf16(const i32x8& v) { return __builtin_bit
 // m = lane%16 of each fragment row.  Optional C (dense only) is added to the
 // FP32 accumulator before the BF16 rounding; c may alias d (each element of
 // C is read before the same thread writes it).  8-byte stores of four BF16.
-template <class T>
+template <class T, int OUT>
 __device__ __forceinline__ void epilogue_cols4(const GemmParams& p, uint16_t* D, f32x4 (&acc)[T::FM][T::FN], int m0,
                                                int n0, int wm, int wn, int lane, int lo, int hi, int row_lim,
                                                bool dense) {
@@ -213,6 +213,18 @@ __device__ __forceinline__ void epilogue_cols4(const GemmParams& p, uint16_t* D,
               if (c + e < p.N) v[e] += bf16_to_f32(crow[c + e]);
           }
         }
+      }
+      if constexpr (OUT == OUT_F32) {
+        // the FP32 values themselves (dense): one 16-byte store of 4 columns
+        float* frow = reinterpret_cast<float*>(D) + (int64_t)row * p.ldd;
+        if (((p.ldd & 3) == 0) && ((reinterpret_cast<uintptr_t>(D) & 15) == 0) && c + 4 <= p.N) {
+          *reinterpret_cast<f32x4*>(frow + c) = v;
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (c + e < p.N) frow[c + e] = v[e];
+        }
+        continue;
       }
       const i32x2 wv = to_bf16x4_bits(v);
       const uint32_t w0 = (uint32_t)wv[0], w1 = (uint32_t)wv[1];
@@ -854,7 +866,7 @@ __global__ __launch_bounds__(T::NT) void gemm_kernel(const GemmParams p) {
   if constexpr (OUT == OUT_FP8) {
     epilogue_fp8<T>(p, acc, lds_b0, m0, n0, wm, wn, lane, row_lim);
   } else if constexpr (!T::PERM) {
-    epilogue_cols4<T>(p, D, acc, m0, n0, wm, wn, lane, lo, hi, row_lim, MODE == MODE_DENSE);
+    epilogue_cols4<T, OUT>(p, D, acc, m0, n0, wm, wn, lane, lo, hi, row_lim, MODE == MODE_DENSE);
   } else {
     // ---- epilogue: BF16, row m = lane%16 of each fragment row, 16 consecutive columns per lane
     const int col0 = n0 + wn * T::TN + (lane >> 4) * 16;
@@ -903,6 +915,23 @@ __global__ __launch_bounds__(T::NT) void gemm_kernel(const GemmParams p) {
           }
         }
       }
+      if constexpr (OUT == OUT_F32) {
+        // the FP32 values themselves (dense): four 16-byte stores of 4 columns
+        float* frow = reinterpret_cast<float*>(D) + (int64_t)row * p.ldd;
+        const bool f_ok = ((p.ldd & 3) == 0) && ((reinterpret_cast<uintptr_t>(D) & 15) == 0);
+#pragma unroll
+        for (int f = 0; f < T::FN; ++f) {
+          const int c = col0 + 4 * f;
+          if (f_ok && c + 4 <= p.N) {
+            *reinterpret_cast<f32x4*>(frow + c) = acc[i][f];
+          } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              if (c + e < p.N) frow[c + e] = acc[i][f][e];
+          }
+        }
+        continue;
+      }
       uint32_t packed[8];
 #pragma unroll
       for (int f = 0; f < T::FN; ++f) {
@@ -943,6 +972,18 @@ enum Variant : int { VAR_L = 0, VAR_W = 1, VAR_S = 2, VAR_T = 3, VAR_N = 4 };
 template <class T, int KIND, bool ROWB>
 hipError_t launch_tile(const GemmParams& p, int mode, int sf_fmt, int64_t grid, hipStream_t stream) {
   const dim3 g((unsigned)grid), b(T::NT);
+  if (p.d_f32) {
+    // FP32 D: dense, block scales
+    if (mode != MODE_DENSE) return hipErrorInvalidValue;
+    if constexpr (KIND == KIND_BF16) {
+      gemm_kernel<T, KIND_BF16, SF_F32, MODE_DENSE, OUT_F32><<<g, b, 0, stream>>>(p);
+    } else {
+      if (sf_fmt == SF_F32) gemm_kernel<T, KIND_FP8, SF_F32, MODE_DENSE, OUT_F32><<<g, b, 0, stream>>>(p);
+      else if (sf_fmt == SF_UE8M0) gemm_kernel<T, KIND_FP8, SF_UE8M0, MODE_DENSE, OUT_F32><<<g, b, 0, stream>>>(p);
+      else return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+  }
   if constexpr (KIND == KIND_BF16) {
     if (mode == MODE_DENSE) gemm_kernel<T, KIND_BF16, SF_F32, MODE_DENSE><<<g, b, 0, stream>>>(p);
     else if (mode == MODE_CONTIG) gemm_kernel<T, KIND_BF16, SF_F32, MODE_CONTIG><<<g, b, 0, stream>>>(p);
@@ -1067,7 +1108,7 @@ hipError_t launch_plan(const GemmPlan& plan, GemmParams p, int mode, int sf_fmt,
       // blocks (n_off is a multiple of 256), D and C columns
       q.b = p.b + n_off * p.ldb;
       if (KIND == KIND_FP8) q.sfb = static_cast<const uint32_t*>(p.sfb) + (n_off / 128) * p.sfb_sn;
-      q.d = p.d + n_off;
+      q.d = p.d + n_off * (p.d_f32 ? 2 : 1);  // (F32 D: two BF16-sized units per element)
       if (p.c != nullptr) q.c = static_cast<const uint8_t*>(p.c) + n_off * (p.c_f32 ? 4 : 2);
     }
     q.N = (int32_t)n_len;

@@ -56,6 +56,12 @@ def test_bf16_gemm_validation_errors(lib):
     assert dense(a, b, None, _t((M, N + 1), torch.bfloat16)) == binding.DG_INVALID_ARG  # d shape
     assert dense(_t((M, 96), torch.bfloat16), _t((N, 96), torch.bfloat16), None, d) == binding.DG_UNSUPPORTED  # K % 64
     assert dense(a, b, _t((M, N), torch.int32), d) == binding.DG_INVALID_ARG  # c dtype
+    assert dense(a, b, None, _t((M, N), torch.int32)) == binding.DG_INVALID_ARG  # d dtype (BF16 or F32)
+    dmis = D(_t((M, N), torch.float32))
+    dmis.data += 2  # F32 d not 4-byte aligned
+    assert lib.bf16_gemm_nt(ctypes.byref(D(a)), ctypes.byref(D(b)), None, ctypes.byref(dmis), None) \
+        == binding.DG_INVALID_ARG
+    assert "aligned" in binding.last_error()
     lay = _t((2,), torch.int32)
     bg = _t((3, N, K), torch.bfloat16)
     dg = _t((256, N), torch.bfloat16)
@@ -165,9 +171,20 @@ def test_dense_validation_errors(lib):
     sfa = _t((M, K // 128), torch.float32)
     sfb = _t((N // 128, K // 128), torch.float32)
     d = _t((M, N), torch.bfloat16)
-    # wrong dtype of d
-    assert _call_dense(lib, a, b, sfa, sfb, d.float()) == binding.DG_INVALID_ARG
+    # wrong dtype of d (BF16 or F32 only)
+    assert _call_dense(lib, a, b, sfa, sfb, _t((M, N), torch.int32)) == binding.DG_INVALID_ARG
     assert "dtype" in binding.last_error()
+    # F32 d: 4-byte aligned, block scales only, dense only
+    D = binding.describe
+    f32buf = torch.empty((M, N + 1), dtype=torch.float32)
+    dmis = D(f32buf[:, :N])
+    dmis.data += 2
+    assert lib.fp8_gemm_nt(ctypes.byref(D(a)), ctypes.byref(D(b)), ctypes.byref(D(sfa)), ctypes.byref(D(sfb)), None,
+                           ctypes.byref(dmis), None) == binding.DG_INVALID_ARG
+    assert "aligned" in binding.last_error()
+    assert _call_dense(lib, a, b, sfa, _t((N, K // 128), torch.float32), _t((M, N), torch.float32)) \
+        == binding.DG_UNSUPPORTED
+    assert "F32 output" in binding.last_error()
     # K mismatch
     assert _call_dense(lib, a, _t((N, K + 128), torch.uint8), sfa, sfb, d) == binding.DG_INVALID_ARG
     # wrong scale shape (neither one per 128x128 block nor one per row)
@@ -225,6 +242,7 @@ def test_masked_validation_errors(lib):
     assert call(mm=_t((G,), torch.float32)) == binding.DG_INVALID_ARG
     assert call(max_m=max_m + 1) == binding.DG_INVALID_ARG
     assert call(d=_t((G, max_m, N + 8), torch.bfloat16)) == binding.DG_INVALID_ARG
+    assert call(d=_t((G, max_m, N), torch.float32)) == binding.DG_INVALID_ARG  # F32 d: dense only
     assert call(max_m=-1) == binding.DG_INVALID_ARG
 
 
