@@ -16,6 +16,9 @@ Modules
               fine-grained scales, the dense one with its output cast
               per token to FP8, and the dense, contiguous-grouped and
               masked-grouped BF16 GEMMs.
+  moe      -- the steps either side of the masked grouped GEMM: routing of
+              (token, choice) pairs into expert buffers with the per-token
+              cast, and the weighted combine of the GEMM's rows per token.
 
 Sources (the pages this follows):
   * "DeepInside DeepGEMM: Unpacking DeepSeek's Unified Tensor Core Library
@@ -57,6 +60,7 @@ from .gemm import (
     m_grouped_bf16_gemm_nt_masked,
     scales_from_packed_ue8m0,
 )
+from .moe import moe_route, moe_dispatch_fp8, moe_combine
 
 __all__ = [
     "E4M3_MAX",
@@ -77,4 +81,7 @@ __all__ = [
     "m_grouped_fp8_gemm_nt_masked",
     "m_grouped_bf16_gemm_nt_masked",
     "scales_from_packed_ue8m0",
+    "moe_route",
+    "moe_dispatch_fp8",
+    "moe_combine",
 ]
