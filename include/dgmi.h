@@ -227,6 +227,48 @@ int per_block_cast_to_fp8(const dg_tensor* x, const dg_tensor* q, const dg_tenso
 int pack_ue8m0_to_int(const dg_tensor* x, const dg_tensor* out, int32_t* invalid_count,
                       hipStream_t stream);
 
+/*
+ * MoE dispatch into the masked layout, with the per-token FP8 cast of the
+ * routed tokens ("DeepGEMM tested by Novita AI", decode section: each expert
+ * owns a padded buffer of max_m rows of which masked_m[e] are valid;
+ * "DeepGEMM CUDA Graph Compatibility for Masked Grouped GEMMs", last
+ * section: the fused MoE path chains the input casting and the masked GEMM
+ * calls; "DeepInside DeepGEMM", section 5: the cast done where the tensor
+ * is produced).  Two kernels on `stream`, no allocation, no host sync.
+ *   x        F32 or BF16 [T, K] tokens (16-B aligned base and row stride)
+ *   topk_idx I32 [T, k] contiguous: the expert of each (token, choice); ids
+ *            outside [0, G) route nowhere
+ *   a        E4M3 [G, max_m, K] out (4-B aligned rows): row r of expert e is
+ *            its r-th routed token, cast as per_token_cast_to_fp8 casts it;
+ *            rows >= masked_m[e] are left untouched
+ *   sfa      F32 [G, max_m, ceil(K/128)] out, any strides: its scales
+ *   masked_m I32 [G] out: min(tokens routed to e, max_m)
+ *   slot     I32 [T, k] out, contiguous: e * max_m + r where (t, j) landed,
+ *            -1 if routed nowhere or dropped
+ *   src      I32 [G, max_m] out, contiguous: the token of each row (rows <
+ *            masked_m[e] only)
+ * Pairs routed to an expert take its rows in row-major (t, j) order; those
+ * beyond max_m rows are dropped (slot -1).  The outputs feed
+ * m_grouped_fp8_gemm_nt_masked (a, sfa, masked_m, max_m) and moe_combine
+ * (slot).  G * max_m and T * k must fit in int32 (else DG_UNSUPPORTED).
+ */
+int moe_dispatch_masked_fp8(const dg_tensor* x, const dg_tensor* topk_idx, const dg_tensor* a,
+                            const dg_tensor* sfa, const dg_tensor* masked_m, const dg_tensor* slot,
+                            const dg_tensor* src, int use_ue8m0, hipStream_t stream);
+
+/*
+ * MoE combine: y[t] = sum over j of topk_weights[t, j] * d[slot[t, j]], the
+ * rows of the masked GEMM's output picked by moe_dispatch_masked_fp8's slot
+ * table; slots outside [0, G * max_m) (not routed, dropped) add nothing.
+ * FP32 sum in increasing j, one FMA per term, rounded to BF16.
+ *   d            BF16 [G, max_m, N], any row/group strides (innermost 1)
+ *   slot         I32 [T, k] contiguous
+ *   topk_weights F32 [T, k] contiguous
+ *   y            BF16 [T, N] out, any row stride; must not overlap d
+ */
+int moe_combine(const dg_tensor* d, const dg_tensor* slot, const dg_tensor* topk_weights,
+                const dg_tensor* y, hipStream_t stream);
+
 /* Launch configuration chosen for a GEMM (a pure function of the shapes).
  * A GEMM is one launch over all N columns, or two launches in stream order:
  * the first over columns [0, n_split), the second (block_n2 > 0) over

@@ -22,5 +22,7 @@ from .binding import (  # noqa: F401
     per_token_cast_to_fp8,
     per_block_cast_to_fp8,
     pack_ue8m0_to_int,
+    moe_dispatch_masked_fp8,
+    moe_combine,
     query_config,
 )

@@ -33,6 +33,8 @@ ENTRY_POINTS = (
     "per_token_cast_to_fp8",
     "per_block_cast_to_fp8",
     "pack_ue8m0_to_int",
+    "moe_dispatch_masked_fp8",
+    "moe_combine",
     "dg_query_config",
 )
 
@@ -94,6 +96,8 @@ def load_library(path=None):
         "per_token_cast_to_fp8": ([T, T, T, ctypes.c_int, vp], ctypes.c_int),
         "per_block_cast_to_fp8": ([T, T, T, ctypes.c_int, vp], ctypes.c_int),
         "pack_ue8m0_to_int": ([T, T, vp, vp], ctypes.c_int),
+        "moe_dispatch_masked_fp8": ([T, T, T, T, T, T, T, ctypes.c_int, vp], ctypes.c_int),
+        "moe_combine": ([T, T, T, T, vp], ctypes.c_int),
         "dg_query_config": ([i32, i64, i64, i64, i64, ctypes.POINTER(DgConfig)], ctypes.c_int),
     }
     for name, (args, res) in sig.items():
@@ -240,6 +244,24 @@ def pack_ue8m0_to_int(x, out, invalid_count=None, stream=None):
     cnt = ctypes.c_void_p(invalid_count.data_ptr()) if invalid_count is not None else None
     _check(lib.pack_ue8m0_to_int(_ref(describe(x)), _ref(describe(out)), cnt, _stream(stream)))
     return out
+
+
+def moe_dispatch_masked_fp8(x, topk_idx, a, sfa, masked_m, slot, src, use_ue8m0=False, stream=None):
+    """Route (token, choice) pairs into the expert buffers a / sfa (masked
+    layout) with the per-token FP8 cast; fills masked_m, slot and src."""
+    lib = load_library()
+    _check(lib.moe_dispatch_masked_fp8(_ref(describe(x)), _ref(describe(topk_idx)), _ref(describe(a)),
+                                       _ref(describe(sfa)), _ref(describe(masked_m)), _ref(describe(slot)),
+                                       _ref(describe(src)), int(bool(use_ue8m0)), _stream(stream)))
+    return a, sfa, masked_m, slot, src
+
+
+def moe_combine(d, slot, topk_weights, y, stream=None):
+    """y[t] = sum_j topk_weights[t, j] * d[slot[t, j]] (BF16 out)."""
+    lib = load_library()
+    _check(lib.moe_combine(_ref(describe(d)), _ref(describe(slot)), _ref(describe(topk_weights)), _ref(describe(y)),
+                           _stream(stream)))
+    return y
 
 
 def query_config(kind, G, M, N, K):

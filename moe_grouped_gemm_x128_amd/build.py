@@ -23,7 +23,7 @@ LIB = os.path.join(HERE, "libdgmi.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-SOURCES = ["abi.cpp", "quant.hip", "gemm.hip"]
+SOURCES = ["abi.cpp", "quant.hip", "gemm.hip", "moe.hip"]
 
 COMMON_FLAGS = [
     f"--offload-arch={ARCH}",

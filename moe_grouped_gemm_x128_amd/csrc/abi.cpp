@@ -602,6 +602,137 @@ int pack_ue8m0_to_int(const dg_tensor* x, const dg_tensor* out, int32_t* invalid
   return check_launch(dgmi::launch_pack_ue8m0(p, stream), fname);
 }
 
+int moe_dispatch_masked_fp8(const dg_tensor* x, const dg_tensor* topk_idx, const dg_tensor* a, const dg_tensor* sfa,
+                            const dg_tensor* masked_m, const dg_tensor* slot, const dg_tensor* src, int use_ue8m0,
+                            hipStream_t stream) {
+  const char* fname = "moe_dispatch_masked_fp8";
+  DG_TRY(check_basic(x, "x", true));
+  DG_TRY(check_basic(topk_idx, "topk_idx", true));
+  DG_TRY(check_basic(a, "a", true));
+  DG_TRY(check_basic(sfa, "sfa", false));
+  DG_TRY(check_basic(masked_m, "masked_m", true));
+  DG_TRY(check_basic(slot, "slot", true));
+  DG_TRY(check_basic(src, "src", true));
+  if (x->dtype != DG_F32 && x->dtype != DG_BF16) return fail(DG_INVALID_ARG, "%s: x must be F32 or BF16", fname);
+  DG_TRY(check_dtype(topk_idx, "topk_idx", DG_I32));
+  DG_TRY(check_dtype(a, "a", DG_E4M3));
+  DG_TRY(check_dtype(sfa, "sfa", DG_F32));
+  DG_TRY(check_dtype(masked_m, "masked_m", DG_I32));
+  DG_TRY(check_dtype(slot, "slot", DG_I32));
+  DG_TRY(check_dtype(src, "src", DG_I32));
+  if (x->ndim != 2 || topk_idx->ndim != 2 || a->ndim != 3 || sfa->ndim != 3 || masked_m->ndim != 1 ||
+      slot->ndim != 2 || src->ndim != 2)
+    return fail(DG_INVALID_ARG, "%s: x [T, K], topk_idx [T, k], a [G, max_m, K], sfa [G, max_m, K/128], "
+                "masked_m [G], slot [T, k], src [G, max_m]", fname);
+  const int64_t T = x->shape[0], K = x->shape[1], k = topk_idx->shape[1];
+  const int64_t G = a->shape[0], max_m = a->shape[1];
+  if (topk_idx->shape[0] != T) return fail(DG_INVALID_ARG, "%s: topk_idx must have T = %lld rows", fname, (long long)T);
+  if (a->shape[2] != K) return fail(DG_INVALID_ARG, "%s: a must be [G, max_m, K = %lld]", fname, (long long)K);
+  if (sfa->shape[0] != G || sfa->shape[1] != max_m || sfa->shape[2] != (K + 127) / 128)
+    return fail(DG_INVALID_ARG, "%s: sfa must be [G, max_m, ceil(K/128)] = [%lld, %lld, %lld]", fname, (long long)G,
+                (long long)max_m, (long long)((K + 127) / 128));
+  if (masked_m->shape[0] != G) return fail(DG_INVALID_ARG, "%s: masked_m must be [G = %lld]", fname, (long long)G);
+  if (slot->shape[0] != T || slot->shape[1] != k)
+    return fail(DG_INVALID_ARG, "%s: slot must have the shape of topk_idx", fname);
+  if (src->shape[0] != G || src->shape[1] != max_m)
+    return fail(DG_INVALID_ARG, "%s: src must be [G, max_m] = [%lld, %lld]", fname, (long long)G, (long long)max_m);
+  // the routing tables are read and written as flat arrays
+  if ((T > 1 && topk_idx->stride[0] != k) || (T > 1 && slot->stride[0] != k) || (G > 1 && src->stride[0] != max_m))
+    return fail(DG_INVALID_ARG, "%s: topk_idx, slot and src must be contiguous", fname);
+  if (G * max_m > INT32_MAX || T * k > INT32_MAX)
+    return fail(DG_UNSUPPORTED, "%s: G * max_m and T * k must fit in int32", fname);
+  const int xe = elem_size(x->dtype);
+  if (!aligned(x->data, 16) || (T > 1 && (x->stride[0] * xe) % 16))
+    return fail(DG_INVALID_ARG, "%s: x needs a 16-byte aligned base and row stride", fname);
+  if (!aligned(a->data, 4) || (max_m > 1 && a->stride[1] % 4) || (G > 1 && a->stride[0] % 4))
+    return fail(DG_INVALID_ARG, "%s: a needs a 4-byte aligned base and row/group strides", fname);
+  if (!aligned(sfa->data, 4)) return fail(DG_INVALID_ARG, "%s: sfa must be 4-byte aligned", fname);
+  const dg_tensor* outs[] = {a, sfa, masked_m, slot, src};
+  const char* onames[] = {"a", "sfa", "masked_m", "slot", "src"};
+  for (int i = 0; i < 5; ++i) {
+    DG_TRY(check_no_alias(outs[i], onames[i], x, "x"));
+    DG_TRY(check_no_alias(outs[i], onames[i], topk_idx, "topk_idx"));
+    for (int j = i + 1; j < 5; ++j) DG_TRY(check_no_alias(outs[i], onames[i], outs[j], onames[j]));
+  }
+  if (G == 0) return ok();
+  dgmi::MoeRouteArgs r = {};
+  r.topk = static_cast<const int32_t*>(topk_idx->data);
+  r.T = (int32_t)T;
+  r.k = (int32_t)k;
+  r.G = (int32_t)G;
+  r.max_m = (int32_t)max_m;
+  r.vec = aligned(topk_idx->data, 16) ? 1 : 0;
+  r.masked_m = static_cast<int32_t*>(masked_m->data);
+  r.slot = static_cast<int32_t*>(slot->data);
+  r.src = static_cast<int32_t*>(src->data);
+  hipError_t e = dgmi::launch_moe_route(r, stream);
+  if (e != hipSuccess || max_m == 0 || K == 0) return check_launch(e, fname);
+  // the per-token cast of the routed tokens, through src and masked_m
+  dgmi::QuantGatherArgs q = {};
+  q.x = x->data;
+  q.x_bf16 = x->dtype == DG_BF16;
+  q.sx_g = 0;
+  q.sx_r = x->stride[0];
+  q.q = static_cast<uint8_t*>(a->data);
+  q.sq_g = a->stride[0];
+  q.sq_r = a->stride[1];
+  q.sf = static_cast<float*>(sfa->data);
+  q.ssf_g = sfa->stride[0];
+  q.ssf_r = sfa->stride[1];
+  q.ssf_k = sfa->stride[2];
+  q.G = (int32_t)G;
+  q.R = (int32_t)max_m;
+  q.K = (int32_t)K;
+  q.ue8m0 = use_ue8m0 ? 1 : 0;
+  q.src = r.src;
+  q.count = r.masked_m;
+  return check_launch(dgmi::launch_per_token_gather(q, stream), fname);
+}
+
+int moe_combine(const dg_tensor* d, const dg_tensor* slot, const dg_tensor* topk_weights, const dg_tensor* y,
+                hipStream_t stream) {
+  const char* fname = "moe_combine";
+  DG_TRY(check_basic(d, "d", true));
+  DG_TRY(check_basic(slot, "slot", true));
+  DG_TRY(check_basic(topk_weights, "topk_weights", true));
+  DG_TRY(check_basic(y, "y", true));
+  DG_TRY(check_dtype(d, "d", DG_BF16));
+  DG_TRY(check_dtype(slot, "slot", DG_I32));
+  DG_TRY(check_dtype(topk_weights, "topk_weights", DG_F32));
+  DG_TRY(check_dtype(y, "y", DG_BF16));
+  if (d->ndim != 3 || slot->ndim != 2 || topk_weights->ndim != 2 || y->ndim != 2)
+    return fail(DG_INVALID_ARG, "%s: d [G, max_m, N], slot [T, k], topk_weights [T, k], y [T, N]", fname);
+  const int64_t G = d->shape[0], max_m = d->shape[1], N = d->shape[2], T = slot->shape[0], k = slot->shape[1];
+  if (topk_weights->shape[0] != T || topk_weights->shape[1] != k)
+    return fail(DG_INVALID_ARG, "%s: topk_weights must have the shape of slot", fname);
+  if (y->shape[0] != T || y->shape[1] != N)
+    return fail(DG_INVALID_ARG, "%s: y must be [T, N] = [%lld, %lld]", fname, (long long)T, (long long)N);
+  if ((T > 1 && slot->stride[0] != k) || (T > 1 && topk_weights->stride[0] != k))
+    return fail(DG_INVALID_ARG, "%s: slot and topk_weights must be contiguous", fname);
+  if (G * max_m > INT32_MAX) return fail(DG_UNSUPPORTED, "%s: G * max_m must fit in int32", fname);
+  if (!aligned(d->data, 2) || !aligned(y->data, 2)) return fail(DG_INVALID_ARG, "%s: d and y must be 2-byte aligned", fname);
+  DG_TRY(check_no_alias(y, "y", d, "d"));
+  DG_TRY(check_no_alias(y, "y", slot, "slot"));
+  DG_TRY(check_no_alias(y, "y", topk_weights, "topk_weights"));
+  dgmi::MoeCombineArgs p = {};
+  p.d = static_cast<const uint16_t*>(d->data);
+  p.sd_g = d->stride[0];
+  p.sd_r = d->stride[1];
+  p.G = (int32_t)G;
+  p.max_m = (int32_t)max_m;
+  p.N = (int32_t)N;
+  p.slot = static_cast<const int32_t*>(slot->data);
+  p.w = static_cast<const float*>(topk_weights->data);
+  p.T = (int32_t)T;
+  p.k = (int32_t)k;
+  p.y = static_cast<uint16_t*>(y->data);
+  p.sy = y->stride[0];
+  p.vec = (aligned(d->data, 16) && (max_m <= 1 || d->stride[1] % 8 == 0) && (G <= 1 || d->stride[0] % 8 == 0)) ? 1 : 0;
+  p.y_vec = (aligned(y->data, 16) && (T <= 1 || y->stride[0] % 8 == 0)) ? 1 : 0;
+  if (T == 0 || N == 0) return ok();
+  return check_launch(dgmi::launch_moe_combine(p, stream), fname);
+}
+
 int dg_query_config(int32_t kind, int64_t G, int64_t M, int64_t N, int64_t K, dg_config* out) {
   if (out == nullptr) return fail(DG_INVALID_ARG, "dg_query_config: out is NULL");
   if (G < 0 || M < 0 || N < 0 || K < 0) return fail(DG_INVALID_ARG, "dg_query_config: negative size");

@@ -23,6 +23,40 @@ struct QuantArgs {
   int32_t ue8m0;
 };
 
+// Per-token cast through a row map: row r < count[g] of group g reads row
+// src[g * R + r] of a 2-D x (stride sx_r; sx_g unused); rows past count[g]
+// are skipped.
+struct QuantGatherArgs : QuantArgs {
+  const int32_t* src;
+  const int32_t* count;
+};
+
+// MoE routing into the masked layout (moe.hip): topk [T, k] contiguous,
+// slot [T, k] contiguous, src [G, max_m] contiguous, masked_m [G].
+struct MoeRouteArgs {
+  const int32_t* topk;
+  int32_t T, k, G, max_m;
+  int32_t vec;  // topk is 16-byte aligned: 16-byte loads
+  int32_t* masked_m;
+  int32_t* slot;
+  int32_t* src;
+};
+
+// MoE combine (moe.hip): d BF16 [G, max_m, N] (strides in elements), slot and
+// w [T, k] contiguous, y BF16 [T, N] (row stride sy).
+struct MoeCombineArgs {
+  const uint16_t* d;
+  int64_t sd_g, sd_r;
+  int32_t G, max_m, N;
+  const int32_t* slot;
+  const float* w;
+  int32_t T, k;
+  uint16_t* y;
+  int64_t sy;
+  int32_t vec, y_vec;  // 16-byte loads of d rows, 16-byte stores of y rows
+  int32_t col_blocks;  // set by the launcher
+};
+
 struct PackArgs {
   const float* x;
   int64_t sx_g, sx_r;
@@ -39,6 +73,9 @@ struct TileCfg {
 };
 
 hipError_t launch_per_token(const QuantArgs& p, hipStream_t stream);
+hipError_t launch_per_token_gather(const QuantGatherArgs& p, hipStream_t stream);
+hipError_t launch_moe_route(const MoeRouteArgs& p, hipStream_t stream);
+hipError_t launch_moe_combine(const MoeCombineArgs& p, hipStream_t stream);
 hipError_t launch_per_block(const QuantArgs& p, hipStream_t stream);
 hipError_t launch_pack_ue8m0(const PackArgs& p, hipStream_t stream);
 

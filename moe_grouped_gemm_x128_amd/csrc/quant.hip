@@ -49,8 +49,8 @@ __device__ __forceinline__ void load4(const uint16_t* p, float v[4]) {
 // ---------------------------------------------------------------------------
 constexpr int TOKEN_BLOCKS = 4;
 
-template <typename TIn>
-__global__ __launch_bounds__(256) void per_token_kernel(QuantArgs p) {
+template <typename TIn, bool GATHER = false, class Args = QuantArgs>
+__global__ __launch_bounds__(256) void per_token_kernel(Args p) {
   const TIn* __restrict__ x = static_cast<const TIn*>(p.x);
   const int lane32 = threadIdx.x & 31;
   const int KB = (p.K + 127) / 128;
@@ -62,7 +62,13 @@ __global__ __launch_bounds__(256) void per_token_kernel(QuantArgs p) {
   const int64_t rr = grp / KQ;
   const int r = (int)(rr % p.R);
   const int g = (int)(rr / p.R);
-  const TIn* xr = x + g * p.sx_g + r * p.sx_r;
+  const TIn* xr;
+  if constexpr (GATHER) {
+    if (r >= p.count[g]) return;  // row past the group's count: left untouched
+    xr = x + (int64_t)p.src[(int64_t)g * p.R + r] * p.sx_r;
+  } else {
+    xr = x + g * p.sx_g + r * p.sx_r;
+  }
   uint8_t* qr = p.q + g * p.sq_g + r * p.sq_r;
   const int kb0 = kq * TOKEN_BLOCKS;
 
@@ -204,6 +210,18 @@ hipError_t launch_per_token(const QuantArgs& p, hipStream_t stream) {
     per_token_kernel<uint16_t><<<dim3((unsigned)blocks), dim3(256), 0, stream>>>(p);
   else
     per_token_kernel<float><<<dim3((unsigned)blocks), dim3(256), 0, stream>>>(p);
+  return hipGetLastError();
+}
+
+hipError_t launch_per_token_gather(const QuantGatherArgs& p, hipStream_t stream) {
+  const int64_t KB = (p.K + 127) / 128;
+  const int64_t KQ = (KB + TOKEN_BLOCKS - 1) / TOKEN_BLOCKS;
+  const int64_t blocks = ((int64_t)p.G * p.R * KQ + 7) / 8;
+  if (blocks == 0) return hipSuccess;
+  if (p.x_bf16)
+    per_token_kernel<uint16_t, true, QuantGatherArgs><<<dim3((unsigned)blocks), dim3(256), 0, stream>>>(p);
+  else
+    per_token_kernel<float, true, QuantGatherArgs><<<dim3((unsigned)blocks), dim3(256), 0, stream>>>(p);
   return hipGetLastError();
 }
 

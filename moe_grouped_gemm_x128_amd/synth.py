@@ -31,6 +31,10 @@ MASKED = dict(G=32, max_m=256, shapes=[(4096, 7168), (7168, 2048)], seed_a=401, 
 # masked grouped decode under graph replay: 64 experts, 128-row buffer
 MASKED_GRAPH = dict(G=64, max_m=128, N=7168, K=2048, seed_a=501, seed_b=502, seed_m=503)
 
+# MoE decode around the masked GEMM: 768 tokens, each to 8 of 32 experts
+# (mean 192 rows per expert, the masked decode's centre), 256-row buffers
+MOE_DECODE = dict(T=768, k=8, G=32, max_m=256, N=4096, K=7168, seed_x=601, seed_b=602, seed_r=603)
+
 
 def dense_v3_seeds(i):
     return 201 + 2 * i, 202 + 2 * i
@@ -80,6 +84,22 @@ def shuffled_layout(seed, G, nblocks, p_skip=0.15):
     ids = rng.integers(0, G, size=nblocks, dtype=np.int32)
     ids[rng.uniform(size=nblocks) < p_skip] = -1
     return ids
+
+
+def moe_routing(seed, T, G, k, p_none=0.0):
+    """Routing of T tokens: each picks k distinct experts of G uniformly
+    (topk_idx int32 [T, k]) with positive weights summing to 1 per token
+    (float32 [T, k]); a fraction p_none of the choices is set to -1 (routed
+    nowhere, as a token whose expert lives on another GPU)."""
+    if k > G:
+        raise ValueError(f"k = {k} distinct experts out of G = {G}")
+    rng = np.random.default_rng(seed)
+    idx = np.argsort(rng.uniform(size=(T, G)), axis=1)[:, :k].astype(np.int32)
+    w = rng.uniform(0.05, 1.0, size=(T, k))
+    w = (w / w.sum(axis=1, keepdims=True)).astype(np.float32)
+    if p_none > 0:
+        idx[rng.uniform(size=(T, k)) < p_none] = -1
+    return idx, w
 
 
 def bf16_bits_from_f32(x):

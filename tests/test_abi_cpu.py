@@ -376,3 +376,53 @@ def test_fp8_out_validation_errors(lib):
     # empty problems launch nothing
     assert _call_fp8_out(lib, _t((0, K), u8), b, _t((0, 4), f32), sfb, _t((0, N), u8), _t((0, 2), f32)) == 0
     assert _call_fp8_out(lib, a, _t((0, K), u8), sfa, _t((0, 4), f32), _t((M, 0), u8), _t((M, 0), f32)) == 0
+
+
+def test_moe_dispatch_and_combine_validation_errors(lib):
+    D = binding.describe
+    f32, bf, u8, i32 = torch.float32, torch.bfloat16, torch.uint8, torch.int32
+    T, K, k, G, max_m, N = 16, 256, 4, 8, 32, 128
+
+    def dispatch(x=None, topk=None, a=None, sfa=None, mm=None, slot=None, src=None):
+        x = _t((T, K), f32) if x is None else x
+        topk = _t((T, k), i32) if topk is None else topk
+        a = _t((G, max_m, K), u8) if a is None else a
+        sfa = _t((G, max_m, K // 128), f32) if sfa is None else sfa
+        mm = _t((G,), i32) if mm is None else mm
+        slot = _t((T, k), i32) if slot is None else slot
+        src = _t((G, max_m), i32) if src is None else src
+        return lib.moe_dispatch_masked_fp8(*(ctypes.byref(D(t)) for t in (x, topk, a, sfa, mm, slot, src)), 0, None)
+
+    assert dispatch(x=_t((T, K), i32)) == binding.DG_INVALID_ARG  # x dtype
+    assert dispatch(topk=_t((T, k), f32)) == binding.DG_INVALID_ARG  # topk dtype
+    assert dispatch(topk=_t((T + 1, k), i32)) == binding.DG_INVALID_ARG  # T mismatch
+    assert dispatch(a=_t((G, max_m, K + 128), u8)) == binding.DG_INVALID_ARG  # K mismatch
+    assert dispatch(sfa=_t((G, max_m, 1), f32)) == binding.DG_INVALID_ARG  # scale blocks
+    assert dispatch(mm=_t((G + 1,), i32)) == binding.DG_INVALID_ARG  # masked_m length
+    assert dispatch(slot=_t((T, k + 1), i32)) == binding.DG_INVALID_ARG  # slot shape
+    assert dispatch(src=_t((G, max_m - 1), i32)) == binding.DG_INVALID_ARG  # src shape
+    assert dispatch(topk=_t((T, 2 * k), i32)[:, :k]) == binding.DG_INVALID_ARG  # not contiguous
+    assert "contiguous" in binding.last_error()
+    assert dispatch(x=_t((T, K + 2), f32)[:, :K]) == binding.DG_INVALID_ARG  # x rows not 16-B aligned
+    shared = torch.empty(G * max_m + 64, dtype=i32)
+    assert dispatch(mm=shared[:G], src=shared[:G * max_m].view(G, max_m)) == binding.DG_INVALID_ARG  # overlap
+    assert "overlaps" in binding.last_error()
+    # no experts: nothing to do
+    assert dispatch(a=_t((0, max_m, K), u8), sfa=_t((0, max_m, 2), f32), mm=_t((0,), i32), src=_t((0, max_m), i32)) == 0
+
+    def combine(d=None, slot=None, w=None, y=None):
+        d = _t((G, max_m, N), bf) if d is None else d
+        slot = _t((T, k), i32) if slot is None else slot
+        w = _t((T, k), f32) if w is None else w
+        y = _t((T, N), bf) if y is None else y
+        return lib.moe_combine(*(ctypes.byref(D(t)) for t in (d, slot, w, y)), None)
+
+    assert combine(d=_t((G, max_m, N), f32)) == binding.DG_INVALID_ARG  # d dtype
+    assert combine(w=_t((T, k), bf)) == binding.DG_INVALID_ARG  # weights dtype
+    assert combine(w=_t((T, k + 1), f32)) == binding.DG_INVALID_ARG  # weights shape
+    assert combine(y=_t((T, N + 1), bf)) == binding.DG_INVALID_ARG  # y shape
+    assert combine(slot=_t((T, 2 * k), i32)[:, :k]) == binding.DG_INVALID_ARG  # not contiguous
+    buf = torch.empty(G * max_m * N, dtype=bf)
+    assert combine(d=buf.view(G, max_m, N), y=buf[:T * N].view(T, N)) == binding.DG_INVALID_ARG  # y overlaps d
+    # no tokens: nothing to do
+    assert combine(slot=_t((0, k), i32), w=_t((0, k), f32), y=_t((0, N), bf)) == 0
