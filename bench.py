@@ -1,7 +1,8 @@
 """Benchmark of the block-scaled FP8 GEMM path on one MI355X.
 
     python bench.py [--steps K] [--warmup W] [--settle-seconds S]
-                    [--workload dense|contiguous|masked|masked_graph|bf16_dense|dense_rowb|dense_fp8_out]
+                    [--workload dense|contiguous|masked|masked_graph|bf16_dense|dense_rowb|dense_fp8_out|
+                                moe_decode]
 
 Before the W warmup steps, untimed steps run for S seconds (default 1): under
 sustained GEMM load the GPU clock dips for the first few milliseconds and
@@ -34,6 +35,8 @@ Other workloads (for the measurements in the design notes):
                   token, scales [N, K/128]), as in the pages' dense example
   dense_fp8_out -- the five dense shapes with FP8 output: the GEMM's BF16 result
                   cast per token to E4M3 in its epilogue (fp8_gemm_nt_fp8_out)
+  moe_decode   -- 768 tokens to 8 of 32 experts: moe_dispatch_masked_fp8 (routing +
+                  per-token cast), the masked FP8 GEMM (N 4096, K 7168), moe_combine
 """
 
 import argparse
@@ -311,6 +314,86 @@ class MaskedWorkload:
                 "sum_masked_m": int(self.mm_host.sum()), "shapes_NK": self.shapes}
 
 
+class MoeDecodeWorkload:
+    """MoE decode on one GPU around the masked GEMM: 768 tokens routed to 8
+    of 32 experts (256-row buffers, about 192 rows each), N 4096, K 7168.
+    One step = moe_dispatch_masked_fp8 (routing + per-token cast of the
+    routed tokens), the masked FP8 GEMM, and moe_combine."""
+    name = "moe_decode_dispatch_gemm_combine"
+
+    def __init__(self, torch, mg, synth):
+        self.torch, self.mg = torch, mg
+        dev = torch.device("cuda")
+        c = synth.MOE_DECODE
+        T, k, G, max_m, N, K = c["T"], c["k"], c["G"], c["max_m"], c["N"], c["K"]
+        self.T, self.k, self.G, self.max_m, self.N, self.K = T, k, G, max_m, N, K
+        self.shapes = [(N, K)]
+        topk, w = synth.moe_routing(c["seed_r"], T, G, k)
+        self.x = torch.from_numpy(synth.normal_f32(c["seed_x"], (T, K))).to(dev)
+        self.topk = torch.from_numpy(topk).to(dev)
+        self.w = torch.from_numpy(w).to(dev)
+        self.b = torch.empty((G, N, K), dtype=torch.uint8, device=dev)
+        self.sfb = torch.empty((G, N // 128, K // 128), dtype=torch.float32, device=dev)
+        xb = torch.empty((N, K), dtype=torch.float32, device=dev)
+        for g, chunk in enumerate(synth.normal_f32_chunks(c["seed_b"], (G, N, K))):
+            xb.copy_(torch.from_numpy(chunk))
+            mg.per_block_cast_to_fp8(xb, self.b[g], self.sfb[g])  # expert weights: quantized once
+        del xb
+        self.a = torch.empty((G, max_m, K), dtype=torch.uint8, device=dev)
+        self.sfa = torch.empty((G, max_m, K // 128), dtype=torch.float32, device=dev)
+        self.masked_m = torch.empty((G,), dtype=torch.int32, device=dev)
+        self.slot = torch.empty((T, k), dtype=torch.int32, device=dev)
+        self.src = torch.empty((G, max_m), dtype=torch.int32, device=dev)
+        self.d = torch.empty((G, max_m, N), dtype=torch.bfloat16, device=dev)
+        self.y = torch.empty((T, N), dtype=torch.bfloat16, device=dev)
+        self.step()
+        torch.cuda.synchronize()
+        mm = self.masked_m.cpu().numpy()
+        self.mm_host = mm
+        rows, active = int(mm.sum()), int((mm > 0).sum())
+        placed = int((self.slot.cpu().numpy() >= 0).sum())
+        self.flops = [2.0 * rows * N * K]
+        self.gemm_bytes = [active * (N * K + 4 * (N // 128) * (K // 128)) + rows * (K + 4 * (K // 128) + 2 * N) + 4 * G]
+        self.dispatch_bytes = 4 * T * K + 2 * 4 * T * k + rows * (K + 4 * (K // 128)) + 4 * G + 4 * rows
+        self.combine_bytes = placed * 2 * N + 2 * 4 * T * k + 2 * T * N
+        self.step_bytes_total = self.dispatch_bytes + self.gemm_bytes[0] + self.combine_bytes
+        self.extra_events = []
+
+    def step(self, events=None):
+        mg = self.mg
+        ev = None
+        if events is not None:
+            ev = [self.torch.cuda.Event(enable_timing=True) for _ in range(4)]
+            ev[0].record()
+        mg.moe_dispatch_masked_fp8(self.x, self.topk, self.a, self.sfa, self.masked_m, self.slot, self.src)
+        if events is not None:
+            ev[1].record()
+            events[0][0].record()
+        mg.m_grouped_fp8_gemm_nt_masked(self.a, self.b, self.sfa, self.sfb, self.d, self.masked_m, self.max_m)
+        if events is not None:
+            events[0][1].record()
+            ev[2].record()
+        mg.moe_combine(self.d, self.slot, self.w, self.y)
+        if events is not None:
+            ev[3].record()
+            self.extra_events.append(ev)
+
+    def extra(self):
+        disp = float(np.mean([e[0].elapsed_time(e[1]) for e in self.extra_events])) * 1e3
+        comb = float(np.mean([e[2].elapsed_time(e[3]) for e in self.extra_events])) * 1e3
+        return {"dispatch_us": disp, "dispatch_gbs": self.dispatch_bytes / (disp * 1e-6) / 1e9,
+                "combine_us": comb, "combine_gbs": self.combine_bytes / (comb * 1e-6) / 1e9,
+                "dispatch_bytes": self.dispatch_bytes, "combine_bytes": self.combine_bytes}
+
+    def plan_args(self, i):
+        return ("DG_KIND_MASKED", self.G, self.max_m, self.N, self.K)
+
+    def config(self):
+        return {"workload": self.name, "tokens": self.T, "topk": self.k, "experts": self.G, "max_m": self.max_m,
+                "N": self.N, "K": self.K, "sum_masked_m": int(self.mm_host.sum()),
+                "step": "moe_dispatch_masked_fp8 (route + per-token cast), masked FP8 GEMM, moe_combine"}
+
+
 class MaskedGraphWorkload:
     """64 experts x 128 rows, N 7168, K 2048: per-token UE8M0 cast of the
     activations, pack_ue8m0_to_int of both scale tensors, the masked FP8 GEMM
@@ -511,7 +594,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="dense",
                     choices=["dense", "contiguous", "masked", "masked_graph", "bf16_dense", "dense_rowb",
-                             "dense_fp8_out"])
+                             "dense_fp8_out", "moe_decode"])
     ap.add_argument("--settle-seconds", type=float, default=1.0,
                     help="untimed steps run for this long before the warmup steps, so that the timed steps see "
                          "the GPU's steady sustained clock rather than the dip of its first milliseconds under load")
@@ -539,7 +622,8 @@ def main():
     log(f"setting up workload {args.workload}")
     W = {"dense": DenseWorkload, "contiguous": ContiguousWorkload, "masked": MaskedWorkload,
          "masked_graph": MaskedGraphWorkload, "bf16_dense": Bf16DenseWorkload,
-         "dense_rowb": DenseRowBWorkload, "dense_fp8_out": DenseFp8OutWorkload}[args.workload](torch, mg, synth)
+         "dense_rowb": DenseRowBWorkload, "dense_fp8_out": DenseFp8OutWorkload,
+         "moe_decode": MoeDecodeWorkload}[args.workload](torch, mg, synth)
     torch.cuda.synchronize()
 
     # Power-state settle: under sustained GEMM load the clock dips for the first
@@ -593,7 +677,7 @@ def main():
     value = total_flops / (ms_per_step * 1e-3) / 1e12
     mean_launch_ms = float(np.mean(gemm_ms))
     mean_flops = total_flops / nshape
-    is_masked = args.workload in ("masked", "masked_graph")
+    is_masked = args.workload in ("masked", "masked_graph", "moe_decode")
     if graph_wl:
         # dominant kernel: the GEMM with the longest launches
         dom = int(np.argmax(gemm_ms))
@@ -643,6 +727,13 @@ def main():
         value = W.step_bytes() / (ms_per_step * 1e-3) / 1e9
         per_shape[0]["kernel"] = "fp8 masked, UE8M0 packed scales"
         per_shape[1]["kernel"] = "bf16 masked"
+    elif args.workload == "moe_decode":
+        metric = "MoE decode (dispatch + per-token cast, masked FP8 GEMM, combine) GB/s (% HBM)"
+        unit = "GB/s"
+        value = W.step_bytes_total / (ms_per_step * 1e-3) / 1e9
+        per_shape[0]["kernel"] = "fp8 masked"
+        per_shape[0].update(W.extra())
+        per_shape[0]["tokens_per_s"] = W.T / (ms_per_step * 1e-3)
     elif is_masked:
         metric = "masked grouped FP8 GEMM GB/s (% HBM)"
         unit = "GB/s"

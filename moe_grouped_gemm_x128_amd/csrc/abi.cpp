@@ -666,9 +666,9 @@ int moe_dispatch_masked_fp8(const dg_tensor* x, const dg_tensor* topk_idx, const
   r.slot = static_cast<int32_t*>(slot->data);
   r.src = static_cast<int32_t*>(src->data);
   hipError_t e = dgmi::launch_moe_route(r, stream);
-  if (e != hipSuccess || max_m == 0 || K == 0) return check_launch(e, fname);
-  // the per-token cast of the routed tokens, through src and masked_m
-  dgmi::QuantGatherArgs q = {};
+  if (e != hipSuccess || max_m == 0 || K == 0 || T == 0 || k == 0) return check_launch(e, fname);
+  // the per-token cast of each token, stored into every row its slots name
+  dgmi::QuantScatterArgs q = {};
   q.x = x->data;
   q.x_bf16 = x->dtype == DG_BF16;
   q.sx_g = 0;
@@ -680,13 +680,16 @@ int moe_dispatch_masked_fp8(const dg_tensor* x, const dg_tensor* topk_idx, const
   q.ssf_g = sfa->stride[0];
   q.ssf_r = sfa->stride[1];
   q.ssf_k = sfa->stride[2];
-  q.G = (int32_t)G;
-  q.R = (int32_t)max_m;
+  q.G = 1;
+  q.R = (int32_t)T;
   q.K = (int32_t)K;
   q.ue8m0 = use_ue8m0 ? 1 : 0;
-  q.src = r.src;
-  q.count = r.masked_m;
-  return check_launch(dgmi::launch_per_token_gather(q, stream), fname);
+  q.slot = r.slot;
+  q.k = (int32_t)k;
+  q.max_m = (int32_t)max_m;
+  q.rows = (int32_t)(G * max_m);
+  q.flat = (q.sq_g == max_m * q.sq_r && q.ssf_g == max_m * q.ssf_r) ? 1 : 0;
+  return check_launch(dgmi::launch_per_token_scatter(q, stream), fname);
 }
 
 int moe_combine(const dg_tensor* d, const dg_tensor* slot, const dg_tensor* topk_weights, const dg_tensor* y,

@@ -23,12 +23,14 @@ struct QuantArgs {
   int32_t ue8m0;
 };
 
-// Per-token cast through a row map: row r < count[g] of group g reads row
-// src[g * R + r] of a 2-D x (stride sx_r; sx_g unused); rows past count[g]
-// are skipped.
-struct QuantGatherArgs : QuantArgs {
-  const int32_t* src;
-  const int32_t* count;
+// Per-token cast of the tokens x [T, K] (G = 1, R = T) into the rows their
+// slots name: slot[t * k + j] = e * max_m + row in [0, rows) selects row
+// `row` of group e of q and sf (strides sq_g / sq_r, ssf_g / ssf_r); other
+// values are skipped.
+struct QuantScatterArgs : QuantArgs {
+  const int32_t* slot;
+  int32_t k, max_m, rows;
+  int32_t flat;  // sq_g == max_m * sq_r and ssf_g == max_m * ssf_r
 };
 
 // MoE routing into the masked layout (moe.hip): topk [T, k] contiguous,
@@ -73,7 +75,7 @@ struct TileCfg {
 };
 
 hipError_t launch_per_token(const QuantArgs& p, hipStream_t stream);
-hipError_t launch_per_token_gather(const QuantGatherArgs& p, hipStream_t stream);
+hipError_t launch_per_token_scatter(const QuantScatterArgs& p, hipStream_t stream);
 hipError_t launch_moe_route(const MoeRouteArgs& p, hipStream_t stream);
 hipError_t launch_moe_combine(const MoeCombineArgs& p, hipStream_t stream);
 hipError_t launch_per_block(const QuantArgs& p, hipStream_t stream);

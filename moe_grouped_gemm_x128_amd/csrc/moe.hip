@@ -2,9 +2,10 @@
 // routing of (token, choice) pairs into per-expert buffers (the masked
 // layout of "DeepGEMM tested by Novita AI", decode section: max_m rows per
 // expert, masked_m[e] of them valid), whose per-token FP8 cast is the
-// quantizer's own kernel reading its rows through the routing ("DeepInside
-// DeepGEMM", section 5: the cast done by the kernel that produces the
-// tensor), and the weighted combine of the GEMM's output rows per token.
+// quantizer's own kernel casting each token once and storing its codes into
+// every row the routing gives it ("DeepInside DeepGEMM", section 5: the cast
+// done by the kernel that produces the tensor), and the weighted combine of
+// the GEMM's output rows per token.
 //
 //   route:   pairs routed to expert e take its rows 0, 1, ... in row-major
 //            (token, choice) order; pairs beyond max_m rows are dropped;
@@ -25,8 +26,8 @@ namespace dgmi {
 
 namespace {
 
-constexpr int ROUTE_THREADS = 256;
-constexpr int ROUTE_PER_THREAD = 16;  // consecutive pairs per thread per pass
+constexpr int ROUTE_THREADS = 1024;
+constexpr int ROUTE_PER_THREAD = 8;  // consecutive pairs per thread per pass (8192 per pass)
 
 __global__ __launch_bounds__(ROUTE_THREADS) void moe_route_kernel(const MoeRouteArgs p) {
   __shared__ int wave_sum[ROUTE_THREADS / 64];

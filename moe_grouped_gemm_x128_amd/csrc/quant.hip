@@ -48,8 +48,11 @@ __device__ __forceinline__ void load4(const uint16_t* p, float v[4]) {
 // before the first reduction (four 16-byte loads in flight per lane)
 // ---------------------------------------------------------------------------
 constexpr int TOKEN_BLOCKS = 4;
+constexpr int SCATTER_K = 8;  // destinations per token held in registers
 
-template <typename TIn, bool GATHER = false, class Args = QuantArgs>
+// SCATTER (MoE dispatch): x is [T, K] (G = 1, R = T) and each token's
+// codes and scales go to every row its slots name instead of row r of q.
+template <typename TIn, bool SCATTER = false, class Args = QuantArgs>
 __global__ __launch_bounds__(256) void per_token_kernel(Args p) {
   const TIn* __restrict__ x = static_cast<const TIn*>(p.x);
   const int lane32 = threadIdx.x & 31;
@@ -62,15 +65,29 @@ __global__ __launch_bounds__(256) void per_token_kernel(Args p) {
   const int64_t rr = grp / KQ;
   const int r = (int)(rr % p.R);
   const int g = (int)(rr / p.R);
-  const TIn* xr;
-  if constexpr (GATHER) {
-    if (r >= p.count[g]) return;  // row past the group's count: left untouched
-    xr = x + (int64_t)p.src[(int64_t)g * p.R + r] * p.sx_r;
-  } else {
-    xr = x + g * p.sx_g + r * p.sx_r;
-  }
+  const TIn* xr = x + g * p.sx_g + r * p.sx_r;
   uint8_t* qr = p.q + g * p.sq_g + r * p.sq_r;
   const int kb0 = kq * TOKEN_BLOCKS;
+  // SCATTER: the destinations of this token's first SCATTER_K slots, read
+  // once (q row offset in bytes, scale row offset in elements; -1: none)
+  int64_t dq[SCATTER_K], ds[SCATTER_K];
+  if constexpr (SCATTER) {
+#pragma unroll
+    for (int j = 0; j < SCATTER_K; ++j) {
+      const int32_t sl = j < p.k ? p.slot[(int64_t)r * p.k + j] : -1;
+      dq[j] = ds[j] = -1;
+      if (sl >= 0 && sl < p.rows) {
+        if (p.flat) {  // q and sf hold their groups back to back: no division
+          dq[j] = (int64_t)sl * p.sq_r;
+          ds[j] = (int64_t)sl * p.ssf_r;
+        } else {
+          const int e = sl / p.max_m, row = sl % p.max_m;
+          dq[j] = e * p.sq_g + row * p.sq_r;
+          ds[j] = e * p.ssf_g + row * p.ssf_r;
+        }
+      }
+    }
+  }
 
   float v[TOKEN_BLOCKS][4];
 #pragma unroll
@@ -99,13 +116,38 @@ __global__ __launch_bounds__(256) void per_token_kernel(Args p) {
     const float s = block_scale(amax[b], p.ue8m0);
     const Recip d = recip_of(s);
     const int k0 = kb * 128 + lane32 * 4;
-    if (k0 + 3 < p.K) {
-      *reinterpret_cast<uint32_t*>(qr + k0) = encode4(v[b], d);
+    if constexpr (SCATTER) {
+      // cast once (elements past K are zeros and their bytes are not stored),
+      // store to each destination row
+      const uint32_t w = encode4(v[b], d);
+      auto put = [&](int64_t oq, int64_t os) {
+        uint8_t* qd = p.q + oq;
+        if (k0 + 3 < p.K) {
+          *reinterpret_cast<uint32_t*>(qd + k0) = w;
+        } else {
+          for (int i = 0; i < 4; ++i)
+            if (k0 + i < p.K) qd[k0 + i] = (uint8_t)(w >> (8 * i));
+        }
+        if (lane32 == 0) p.sf[os + kb * p.ssf_k] = s;
+      };
+#pragma unroll
+      for (int j = 0; j < SCATTER_K; ++j)
+        if (dq[j] >= 0) put(dq[j], ds[j]);
+      for (int j = SCATTER_K; j < p.k; ++j) {  // more choices per token than SCATTER_K
+        const int32_t sl = p.slot[(int64_t)r * p.k + j];
+        if (sl < 0 || sl >= p.rows) continue;  // routed nowhere or dropped
+        const int e = sl / p.max_m, row = sl % p.max_m;
+        put(e * p.sq_g + row * p.sq_r, e * p.ssf_g + row * p.ssf_r);
+      }
     } else {
-      for (int j = 0; j < 4; ++j)
-        if (k0 + j < p.K) qr[k0 + j] = (uint8_t)encode1(v[b][j], d);
+      if (k0 + 3 < p.K) {
+        *reinterpret_cast<uint32_t*>(qr + k0) = encode4(v[b], d);
+      } else {
+        for (int j = 0; j < 4; ++j)
+          if (k0 + j < p.K) qr[k0 + j] = (uint8_t)encode1(v[b][j], d);
+      }
+      if (lane32 == 0) p.sf[g * p.ssf_g + r * p.ssf_r + kb * p.ssf_k] = s;
     }
-    if (lane32 == 0) p.sf[g * p.ssf_g + r * p.ssf_r + kb * p.ssf_k] = s;
   }
 }
 
@@ -213,15 +255,15 @@ hipError_t launch_per_token(const QuantArgs& p, hipStream_t stream) {
   return hipGetLastError();
 }
 
-hipError_t launch_per_token_gather(const QuantGatherArgs& p, hipStream_t stream) {
+hipError_t launch_per_token_scatter(const QuantScatterArgs& p, hipStream_t stream) {
   const int64_t KB = (p.K + 127) / 128;
   const int64_t KQ = (KB + TOKEN_BLOCKS - 1) / TOKEN_BLOCKS;
   const int64_t blocks = ((int64_t)p.G * p.R * KQ + 7) / 8;
   if (blocks == 0) return hipSuccess;
   if (p.x_bf16)
-    per_token_kernel<uint16_t, true, QuantGatherArgs><<<dim3((unsigned)blocks), dim3(256), 0, stream>>>(p);
+    per_token_kernel<uint16_t, true, QuantScatterArgs><<<dim3((unsigned)blocks), dim3(256), 0, stream>>>(p);
   else
-    per_token_kernel<float, true, QuantGatherArgs><<<dim3((unsigned)blocks), dim3(256), 0, stream>>>(p);
+    per_token_kernel<float, true, QuantScatterArgs><<<dim3((unsigned)blocks), dim3(256), 0, stream>>>(p);
   return hipGetLastError();
 }
 
