@@ -60,7 +60,7 @@ from .gemm import (
     m_grouped_bf16_gemm_nt_masked,
     scales_from_packed_ue8m0,
 )
-from .moe import moe_route, moe_dispatch_fp8, moe_combine
+from .moe import moe_route, moe_dispatch_fp8, moe_combine, moe_route_contiguous, moe_dispatch_contiguous_fp8
 
 __all__ = [
     "E4M3_MAX",
@@ -84,4 +84,6 @@ __all__ = [
     "moe_route",
     "moe_dispatch_fp8",
     "moe_combine",
+    "moe_route_contiguous",
+    "moe_dispatch_contiguous_fp8",
 ]

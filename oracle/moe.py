@@ -19,6 +19,13 @@ the reading taken (listed in the design notes):
     cast per token to FP8 exactly as per_token_cast_to_fp8 casts it.
   * Combine: y[t] = sum over j with slot[t, j] >= 0 of w[t, j] * D[slot[t,
     j]], where D is the masked GEMM's BF16 output [G, max_m, N].
+  * Contiguous layout (prefill, "DeepGEMM tested by Novita AI", contiguous
+    layout: groups concatenated along M in 128-row blocks, a group id per
+    block): expert e's pairs fill a region of ceil(count_e / 128) blocks
+    that starts where expert e - 1's region ends; rows past the capacity
+    Mcap are dropped; blocks past the last region get id -1.  slot[t, j] is
+    the row in the concatenated buffer (or -1); rows of a region past its
+    count are padding that no token owns.
 
 Pins: tests/test_oracle_moe.py (a hand-worked routing example with its
 expected table, capacity overflow, invariants on random routings, and the
@@ -88,3 +95,55 @@ def moe_combine(d_bits, slot, topk_weights):
         ok = slot[:, j] >= 0
         y[ok] += w[ok, j][:, None] * rows[slot[ok, j]]
     return y
+
+
+def moe_route_contiguous(topk_idx, G, Mcap):
+    """Returns (counts int64 [G] before capping, slot int32 [T, k],
+    grouped_layout int32 [Mcap / 128], start int64 [G] first row of each
+    expert's region)."""
+    topk = np.asarray(topk_idx, dtype=np.int64)
+    T, k = topk.shape
+    counts = np.zeros(G, dtype=np.int64)
+    for t in range(T):
+        for j in range(k):
+            e = int(topk[t, j])
+            if 0 <= e < G:
+                counts[e] += 1
+    blocks = -(-counts // 128)
+    start = np.concatenate([[0], np.cumsum(blocks)[:-1]]) * 128
+    layout = np.full(Mcap // 128, -1, dtype=np.int32)
+    for e in range(G):
+        b0 = start[e] // 128
+        for b in range(b0, min(b0 + blocks[e], Mcap // 128)):
+            layout[b] = e
+    slot = np.full((T, k), -1, dtype=np.int32)
+    seen = np.zeros(G, dtype=np.int64)
+    for t in range(T):
+        for j in range(k):
+            e = int(topk[t, j])
+            if e < 0 or e >= G:
+                continue
+            row = start[e] + seen[e]
+            seen[e] += 1
+            if row < Mcap:
+                slot[t, j] = row
+    return counts, slot, layout, start
+
+
+def moe_dispatch_contiguous_fp8(x, topk_idx, G, Mcap, use_ue8m0=False):
+    """Route into the contiguous layout and cast the routed tokens.
+
+    Returns (a uint8 [Mcap, K], sfa float32 [Mcap, ceil(K/128)], owned bool
+    [Mcap] (rows a token was cast into), grouped_layout, counts, slot)."""
+    x = np.asarray(x, dtype=np.float32)
+    T, K = x.shape
+    counts, slot, layout, _ = moe_route_contiguous(topk_idx, G, Mcap)
+    a = np.zeros((Mcap, K), dtype=np.uint8)
+    sfa = np.zeros((Mcap, -(-K // 128)), dtype=np.float32)
+    owned = np.zeros(Mcap, dtype=bool)
+    q, sf = per_token_cast_to_fp8(x, use_ue8m0) if T else (np.zeros((0, K), np.uint8), None)
+    for t in range(T):
+        for row in slot[t]:
+            if row >= 0:
+                a[row], sfa[row], owned[row] = q[t], sf[t], True
+    return a, sfa, owned, layout, counts, slot

@@ -22,7 +22,7 @@ def _golden():
             continue
         key, rest = line.split(None, 1)
         rows = [[int(v) for v in r.split()] for r in rest.split("|")]
-        rec[key] = rows[0][0] if key in ("G", "max_m") else np.array(rows if len(rows) > 1 else rows[0])
+        rec[key] = rows[0][0] if key in ("G", "max_m", "c_Mcap", "c2_Mcap") else np.array(rows if len(rows) > 1 else rows[0])
     return rec
 
 
@@ -107,3 +107,49 @@ def test_combine_brute_force_and_closed_forms():
     s1 = np.array([[5], [-1]], dtype=np.int32)
     y1 = oracle.moe_combine(d_bits, s1, np.ones((2, 1), np.float32))
     assert np.array_equal(y1[0], D[5]) and not y1[1].any()
+
+
+def test_route_contiguous_hand_worked_example():
+    g = _golden()
+    for pre in ("c_", "c2_"):
+        counts, slot, layout, _ = oracle.moe_route_contiguous(g["topk"], g["G"], g[pre + "Mcap"])
+        assert counts.tolist() == g["counts"].tolist()
+        assert layout.tolist() == g[pre + "layout"].tolist()
+        assert slot.tolist() == g[pre + "slot"].tolist()
+
+
+@pytest.mark.parametrize("T,k,G,Mcap,seed", [(300, 8, 16, 4096, 1), (300, 8, 16, 1024, 2), (40, 3, 7, 1024, 3)])
+def test_route_contiguous_matches_vectorised_construction(T, k, G, Mcap, seed):
+    rng = np.random.default_rng(seed)
+    topk = rng.integers(-1, G + 1, size=(T, k))
+    flat = topk.reshape(-1)
+    counts = np.array([(flat == e).sum() for e in range(G)])
+    start = np.concatenate([[0], np.cumsum(-(-counts // 128))[:-1]]) * 128
+    slot = np.full(T * k, -1)
+    layout = np.full(Mcap // 128, -1)
+    for e in range(G):
+        idx = np.flatnonzero(flat == e)
+        rows = start[e] + np.arange(idx.size)
+        slot[idx[rows < Mcap]] = rows[rows < Mcap]
+        nb = -(-counts[e] // 128)
+        layout[start[e] // 128:min(start[e] // 128 + nb, Mcap // 128)] = e
+    got = oracle.moe_route_contiguous(topk, G, Mcap)
+    assert np.array_equal(got[0], counts)
+    assert np.array_equal(got[1], slot.reshape(T, k))
+    assert np.array_equal(got[2], layout)
+    # every owned row belongs to a block of its own expert
+    for t in range(T):
+        for j in range(k):
+            if got[1][t, j] >= 0:
+                assert got[2][got[1][t, j] // 128] == topk[t, j]
+
+
+def test_dispatch_contiguous_rows_are_the_tokens_casts():
+    x = synth.normal_f32(71, (20, 256))
+    topk, _ = synth.moe_routing(72, 20, 5, 3)
+    a, sfa, owned, layout, counts, slot = oracle.moe_dispatch_contiguous_fp8(x, topk, 5, 1024)
+    q, s = oracle.per_token_cast_to_fp8(x)
+    for t in range(20):
+        for row in slot[t]:
+            assert row >= 0 and np.array_equal(a[row], q[t]) and np.array_equal(sfa[row], s[t])
+    assert owned.sum() == 60 and not a[~owned].any()
