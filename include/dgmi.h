@@ -257,6 +257,33 @@ int moe_dispatch_masked_fp8(const dg_tensor* x, const dg_tensor* topk_idx, const
                             const dg_tensor* src, int use_ue8m0, hipStream_t stream);
 
 /*
+ * MoE dispatch into the contiguous layout of m_grouped_fp8_gemm_nt_contiguous
+ * (prefill: "DeepGEMM tested by Novita AI", contiguous layout, groups
+ * concatenated along M in 128-row blocks with a group id per block), with
+ * the per-token FP8 cast of the routed tokens as in moe_dispatch_masked_fp8.
+ * Three kernels on `stream` (count, place, cast), no allocation, no host sync.
+ *   x, topk_idx     as moe_dispatch_masked_fp8
+ *   a               E4M3 [Mcap, K] out (Mcap % 128 == 0, 4-B aligned rows):
+ *                   expert e's routed tokens fill a region of
+ *                   ceil(count_e / 128) whole blocks, regions in expert
+ *                   order, tokens in row-major (t, j) order; the rows of a
+ *                   region past count_e are padding and left untouched
+ *   sfa             F32 [Mcap, ceil(K/128)] out, any strides: their scales
+ *   grouped_layout  I32 [Mcap/128] out: e for the blocks of e's region, -1
+ *                   for the blocks past the last region
+ *   counts          I32 [G] out: pairs routed to each expert
+ *   slot            I32 [T, k] out, contiguous: the row of a where (t, j)
+ *                   landed, -1 if routed nowhere or past the capacity Mcap
+ * Mcap >= T * k + 127 * G holds every routing.  The outputs feed
+ * m_grouped_fp8_gemm_nt_contiguous (a, sfa, grouped_layout) and moe_combine
+ * (slot, with the GEMM's [Mcap, N] output viewed as [1, Mcap, N]).
+ */
+int moe_dispatch_contiguous_fp8(const dg_tensor* x, const dg_tensor* topk_idx, const dg_tensor* a,
+                                const dg_tensor* sfa, const dg_tensor* grouped_layout,
+                                const dg_tensor* counts, const dg_tensor* slot, int use_ue8m0,
+                                hipStream_t stream);
+
+/*
  * MoE combine: y[t] = sum over j of topk_weights[t, j] * d[slot[t, j]], the
  * rows of the masked GEMM's output picked by moe_dispatch_masked_fp8's slot
  * table; slots outside [0, G * max_m) (not routed, dropped) add nothing.

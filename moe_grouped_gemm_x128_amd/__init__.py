@@ -23,6 +23,7 @@ from .binding import (  # noqa: F401
     per_block_cast_to_fp8,
     pack_ue8m0_to_int,
     moe_dispatch_masked_fp8,
+    moe_dispatch_contiguous_fp8,
     moe_combine,
     query_config,
 )

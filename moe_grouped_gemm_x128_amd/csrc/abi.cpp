@@ -58,7 +58,8 @@ const char* dtype_name(int32_t dtype) {
 }
 
 // Basic well-formedness: non-null, known dtype, 1..4 dims, non-negative
-// shape, non-negative strides, innermost stride 1 when `unit_inner`.
+// shape, non-negative strides, innermost stride 1 when `unit_inner` (for a
+// tensor with elements).
 int check_basic(const dg_tensor* t, const char* name, bool unit_inner) {
   if (t == nullptr) return fail(DG_INVALID_ARG, "%s: descriptor is NULL", name);
   if (elem_size(t->dtype) == 0) return fail(DG_INVALID_ARG, "%s: unknown dtype %d", name, t->dtype);
@@ -71,7 +72,7 @@ int check_basic(const dg_tensor* t, const char* name, bool unit_inner) {
     numel *= t->shape[i];
   }
   if (numel > 0 && t->data == nullptr) return fail(DG_INVALID_ARG, "%s: data pointer is NULL", name);
-  if (unit_inner && t->shape[t->ndim - 1] > 1 && t->stride[t->ndim - 1] != 1)
+  if (unit_inner && numel > 0 && t->shape[t->ndim - 1] > 1 && t->stride[t->ndim - 1] != 1)
     return fail(DG_INVALID_ARG, "%s: innermost stride must be 1 (got %lld)", name, (long long)t->stride[t->ndim - 1]);
   return DG_OK;
 }
@@ -689,6 +690,95 @@ int moe_dispatch_masked_fp8(const dg_tensor* x, const dg_tensor* topk_idx, const
   q.max_m = (int32_t)max_m;
   q.rows = (int32_t)(G * max_m);
   q.flat = (q.sq_g == max_m * q.sq_r && q.ssf_g == max_m * q.ssf_r) ? 1 : 0;
+  return check_launch(dgmi::launch_per_token_scatter(q, stream), fname);
+}
+
+int moe_dispatch_contiguous_fp8(const dg_tensor* x, const dg_tensor* topk_idx, const dg_tensor* a,
+                                const dg_tensor* sfa, const dg_tensor* grouped_layout, const dg_tensor* counts,
+                                const dg_tensor* slot, int use_ue8m0, hipStream_t stream) {
+  const char* fname = "moe_dispatch_contiguous_fp8";
+  DG_TRY(check_basic(x, "x", true));
+  DG_TRY(check_basic(topk_idx, "topk_idx", true));
+  DG_TRY(check_basic(a, "a", true));
+  DG_TRY(check_basic(sfa, "sfa", false));
+  DG_TRY(check_basic(grouped_layout, "grouped_layout", true));
+  DG_TRY(check_basic(counts, "counts", true));
+  DG_TRY(check_basic(slot, "slot", true));
+  if (x->dtype != DG_F32 && x->dtype != DG_BF16) return fail(DG_INVALID_ARG, "%s: x must be F32 or BF16", fname);
+  DG_TRY(check_dtype(topk_idx, "topk_idx", DG_I32));
+  DG_TRY(check_dtype(a, "a", DG_E4M3));
+  DG_TRY(check_dtype(sfa, "sfa", DG_F32));
+  DG_TRY(check_dtype(grouped_layout, "grouped_layout", DG_I32));
+  DG_TRY(check_dtype(counts, "counts", DG_I32));
+  DG_TRY(check_dtype(slot, "slot", DG_I32));
+  if (x->ndim != 2 || topk_idx->ndim != 2 || a->ndim != 2 || sfa->ndim != 2 || grouped_layout->ndim != 1 ||
+      counts->ndim != 1 || slot->ndim != 2)
+    return fail(DG_INVALID_ARG, "%s: x [T, K], topk_idx [T, k], a [Mcap, K], sfa [Mcap, K/128], "
+                "grouped_layout [Mcap/128], counts [G], slot [T, k]", fname);
+  const int64_t T = x->shape[0], K = x->shape[1], k = topk_idx->shape[1];
+  const int64_t Mcap = a->shape[0], G = counts->shape[0];
+  if (topk_idx->shape[0] != T) return fail(DG_INVALID_ARG, "%s: topk_idx must have T = %lld rows", fname, (long long)T);
+  if (a->shape[1] != K) return fail(DG_INVALID_ARG, "%s: a must be [Mcap, K = %lld]", fname, (long long)K);
+  if (Mcap % 128 != 0) return fail(DG_INVALID_ARG, "%s: Mcap = %lld is not a multiple of 128", fname, (long long)Mcap);
+  if (sfa->shape[0] != Mcap || sfa->shape[1] != (K + 127) / 128)
+    return fail(DG_INVALID_ARG, "%s: sfa must be [Mcap, ceil(K/128)] = [%lld, %lld]", fname, (long long)Mcap,
+                (long long)((K + 127) / 128));
+  if (grouped_layout->shape[0] != Mcap / 128)
+    return fail(DG_INVALID_ARG, "%s: grouped_layout must be [Mcap/128 = %lld]", fname, (long long)(Mcap / 128));
+  if (slot->shape[0] != T || slot->shape[1] != k)
+    return fail(DG_INVALID_ARG, "%s: slot must have the shape of topk_idx", fname);
+  if ((T > 1 && topk_idx->stride[0] != k) || (T > 1 && slot->stride[0] != k))
+    return fail(DG_INVALID_ARG, "%s: topk_idx and slot must be contiguous", fname);
+  if (Mcap > INT32_MAX || T * k > INT32_MAX)
+    return fail(DG_UNSUPPORTED, "%s: Mcap and T * k must fit in int32", fname);
+  const int xe = elem_size(x->dtype);
+  if (!aligned(x->data, 16) || (T > 1 && (x->stride[0] * xe) % 16))
+    return fail(DG_INVALID_ARG, "%s: x needs a 16-byte aligned base and row stride", fname);
+  if (!aligned(a->data, 4) || (Mcap > 1 && a->stride[0] % 4))
+    return fail(DG_INVALID_ARG, "%s: a needs a 4-byte aligned base and row stride", fname);
+  if (!aligned(sfa->data, 4)) return fail(DG_INVALID_ARG, "%s: sfa must be 4-byte aligned", fname);
+  const dg_tensor* outs[] = {a, sfa, grouped_layout, counts, slot};
+  const char* onames[] = {"a", "sfa", "grouped_layout", "counts", "slot"};
+  for (int i = 0; i < 5; ++i) {
+    DG_TRY(check_no_alias(outs[i], onames[i], x, "x"));
+    DG_TRY(check_no_alias(outs[i], onames[i], topk_idx, "topk_idx"));
+    for (int j = i + 1; j < 5; ++j) DG_TRY(check_no_alias(outs[i], onames[i], outs[j], onames[j]));
+  }
+  if (Mcap == 0 && G == 0) return ok();
+  dgmi::MoeRouteArgs r = {};
+  r.topk = static_cast<const int32_t*>(topk_idx->data);
+  r.T = (int32_t)T;
+  r.k = (int32_t)k;
+  r.G = (int32_t)G;
+  r.vec = aligned(topk_idx->data, 16) ? 1 : 0;
+  r.slot = static_cast<int32_t*>(slot->data);
+  r.counts = static_cast<int32_t*>(counts->data);
+  r.layout = static_cast<int32_t*>(grouped_layout->data);
+  r.mcap = Mcap;
+  hipError_t e = dgmi::launch_moe_route_contiguous(r, stream);
+  if (e != hipSuccess || Mcap == 0 || K == 0 || T == 0 || k == 0) return check_launch(e, fname);
+  // the per-token cast of each token, stored into every row its slots name
+  dgmi::QuantScatterArgs q = {};
+  q.x = x->data;
+  q.x_bf16 = x->dtype == DG_BF16;
+  q.sx_g = 0;
+  q.sx_r = x->stride[0];
+  q.q = static_cast<uint8_t*>(a->data);
+  q.sq_g = 0;
+  q.sq_r = a->stride[0];
+  q.sf = static_cast<float*>(sfa->data);
+  q.ssf_g = 0;
+  q.ssf_r = sfa->stride[0];
+  q.ssf_k = sfa->stride[1];
+  q.G = 1;
+  q.R = (int32_t)T;
+  q.K = (int32_t)K;
+  q.ue8m0 = use_ue8m0 ? 1 : 0;
+  q.slot = r.slot;
+  q.k = (int32_t)k;
+  q.max_m = (int32_t)Mcap;
+  q.rows = (int32_t)Mcap;
+  q.flat = 1;  // a slot is a row of a and sfa
   return check_launch(dgmi::launch_per_token_scatter(q, stream), fname);
 }
 

@@ -42,6 +42,11 @@ struct MoeRouteArgs {
   int32_t* masked_m;
   int32_t* slot;
   int32_t* src;
+  // contiguous layout: counts [G] (written by the count pass, then read),
+  // layout [mcap / 128], capacity mcap rows (a multiple of 128)
+  int32_t* counts;
+  int32_t* layout;
+  int64_t mcap;
 };
 
 // MoE combine (moe.hip): d BF16 [G, max_m, N] (strides in elements), slot and
@@ -77,6 +82,7 @@ struct TileCfg {
 hipError_t launch_per_token(const QuantArgs& p, hipStream_t stream);
 hipError_t launch_per_token_scatter(const QuantScatterArgs& p, hipStream_t stream);
 hipError_t launch_moe_route(const MoeRouteArgs& p, hipStream_t stream);
+hipError_t launch_moe_route_contiguous(const MoeRouteArgs& p, hipStream_t stream);
 hipError_t launch_moe_combine(const MoeCombineArgs& p, hipStream_t stream);
 hipError_t launch_per_block(const QuantArgs& p, hipStream_t stream);
 hipError_t launch_pack_ue8m0(const PackArgs& p, hipStream_t stream);

@@ -26,14 +26,57 @@ namespace dgmi {
 
 namespace {
 
+enum RouteMode : int { ROUTE_MASKED = 0, ROUTE_COUNT = 1, ROUTE_CONTIG = 2 };
+
 constexpr int ROUTE_THREADS = 1024;
 constexpr int ROUTE_PER_THREAD = 8;  // consecutive pairs per thread per pass (8192 per pass)
 
+// Sum of v over the workgroup (every thread gets it).
+__device__ __forceinline__ int64_t block_sum(int64_t v, int64_t* red) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+  if (lane == 0) red[wave] = v;
+  __syncthreads();
+  int64_t total = 0;
+#pragma unroll
+  for (int w = 0; w < ROUTE_THREADS / 64; ++w) total += red[w];
+  __syncthreads();
+  return total;
+}
+
+// MODE: ROUTE_MASKED (rows of expert e's own buffer, capacity max_m),
+// ROUTE_COUNT (counts[e] only), ROUTE_CONTIG (rows of the concatenated
+// buffer: expert e's region of whole 128-row blocks starts after the
+// regions of experts 0..e-1, from counts; capacity mcap rows; the region's
+// blocks get id e in layout, blocks past the last region -1).  One workgroup
+// per expert (ROUTE_CONTIG: at least one, for the layout).
+template <int MODE>
 __global__ __launch_bounds__(ROUTE_THREADS) void moe_route_kernel(const MoeRouteArgs p) {
   __shared__ int wave_sum[ROUTE_THREADS / 64];
+  __shared__ int64_t red[ROUTE_THREADS / 64];
   const int e = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t n = (int64_t)p.T * p.k;
+  int64_t start = 0;  // ROUTE_CONTIG: first row of e's region
+  if constexpr (MODE == ROUTE_CONTIG) {
+    int64_t before = 0, all = 0;
+    for (int f = tid; f < p.G; f += ROUTE_THREADS) {
+      const int64_t rows = ((int64_t)p.counts[f] + 127) / 128 * 128;
+      all += rows;
+      before += f < e ? rows : 0;
+    }
+    start = block_sum(before, red);
+    const int64_t total = block_sum(all, red);
+    const int64_t nblk = p.mcap / 128;
+    if (e < p.G) {
+      const int64_t b0 = start / 128, b1 = (start + ((int64_t)p.counts[e] + 127) / 128 * 128) / 128;
+      for (int64_t b = b0 + tid; b < b1 && b < nblk; b += ROUTE_THREADS) p.layout[b] = e;
+    }
+    if (e == 0)
+      for (int64_t b = total / 128 + tid; b < nblk; b += ROUTE_THREADS) p.layout[b] = -1;
+    if (e >= p.G) return;  // (no experts: the layout only)
+  }
   int count = 0;  // pairs routed to e so far (the same in every thread)
   for (int64_t base = 0; base < n; base += (int64_t)ROUTE_THREADS * ROUTE_PER_THREAD) {
     const int64_t i0 = base + (int64_t)tid * ROUTE_PER_THREAD;
@@ -72,24 +115,34 @@ __global__ __launch_bounds__(ROUTE_THREADS) void moe_route_kernel(const MoeRoute
     }
     __syncthreads();  // every wave has read wave_sum before the next pass writes it
     int rank = count + before + incl - mine;
+    if constexpr (MODE != ROUTE_COUNT) {
 #pragma unroll
-    for (int q = 0; q < ROUTE_PER_THREAD; ++q) {
-      const int64_t i = i0 + q;
-      if (v[q] == e) {
-        if (rank < p.max_m) {
-          p.slot[i] = e * p.max_m + rank;
-          p.src[(int64_t)e * p.max_m + rank] = (int32_t)(i / p.k);
-        } else {
-          p.slot[i] = -1;  // over capacity: dropped
+      for (int q = 0; q < ROUTE_PER_THREAD; ++q) {
+        const int64_t i = i0 + q;
+        if (v[q] == e) {
+          if constexpr (MODE == ROUTE_MASKED) {
+            if (rank < p.max_m) {
+              p.slot[i] = e * p.max_m + rank;
+              p.src[(int64_t)e * p.max_m + rank] = (int32_t)(i / p.k);
+            } else {
+              p.slot[i] = -1;  // over capacity: dropped
+            }
+          } else {
+            const int64_t row = start + rank;
+            p.slot[i] = row < p.mcap ? (int32_t)row : -1;  // past the capacity: dropped
+          }
+          ++rank;
+        } else if (e == 0 && i < n && (v[q] < 0 || v[q] >= p.G)) {
+          p.slot[i] = -1;  // routed nowhere
         }
-        ++rank;
-      } else if (e == 0 && i < n && (v[q] < 0 || v[q] >= p.G)) {
-        p.slot[i] = -1;  // routed nowhere
       }
     }
     count += total;
   }
-  if (tid == 0) p.masked_m[e] = count < p.max_m ? count : p.max_m;
+  if (tid == 0) {
+    if constexpr (MODE == ROUTE_MASKED) p.masked_m[e] = count < p.max_m ? count : p.max_m;
+    if constexpr (MODE == ROUTE_COUNT) p.counts[e] = count;
+  }
 }
 
 constexpr int COMBINE_THREADS = 256;  // 8 columns per thread
@@ -142,7 +195,17 @@ __global__ __launch_bounds__(COMBINE_THREADS) void moe_combine_kernel(const MoeC
 
 hipError_t launch_moe_route(const MoeRouteArgs& p, hipStream_t stream) {
   if (p.G == 0) return hipSuccess;
-  moe_route_kernel<<<dim3((unsigned)p.G), dim3(ROUTE_THREADS), 0, stream>>>(p);
+  moe_route_kernel<ROUTE_MASKED><<<dim3((unsigned)p.G), dim3(ROUTE_THREADS), 0, stream>>>(p);
+  return hipGetLastError();
+}
+
+hipError_t launch_moe_route_contiguous(const MoeRouteArgs& p, hipStream_t stream) {
+  if (p.G > 0) {
+    moe_route_kernel<ROUTE_COUNT><<<dim3((unsigned)p.G), dim3(ROUTE_THREADS), 0, stream>>>(p);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  moe_route_kernel<ROUTE_CONTIG><<<dim3((unsigned)(p.G > 0 ? p.G : 1)), dim3(ROUTE_THREADS), 0, stream>>>(p);
   return hipGetLastError();
 }
 

@@ -426,3 +426,31 @@ def test_moe_dispatch_and_combine_validation_errors(lib):
     assert combine(d=buf.view(G, max_m, N), y=buf[:T * N].view(T, N)) == binding.DG_INVALID_ARG  # y overlaps d
     # no tokens: nothing to do
     assert combine(slot=_t((0, k), i32), w=_t((0, k), f32), y=_t((0, N), bf)) == 0
+
+
+def test_moe_dispatch_contiguous_validation_errors(lib):
+    D = binding.describe
+    f32, u8, i32 = torch.float32, torch.uint8, torch.int32
+    T, K, k, G, Mcap = 16, 256, 4, 8, 1024
+
+    def dispatch(x=None, topk=None, a=None, sfa=None, lay=None, cnt=None, slot=None):
+        x = _t((T, K), f32) if x is None else x
+        topk = _t((T, k), i32) if topk is None else topk
+        a = _t((Mcap, K), u8) if a is None else a
+        sfa = _t((Mcap, K // 128), f32) if sfa is None else sfa
+        lay = _t((Mcap // 128,), i32) if lay is None else lay
+        cnt = _t((G,), i32) if cnt is None else cnt
+        slot = _t((T, k), i32) if slot is None else slot
+        return lib.moe_dispatch_contiguous_fp8(*(ctypes.byref(D(t)) for t in (x, topk, a, sfa, lay, cnt, slot)), 0, None)
+
+    assert dispatch(a=_t((1000, K), u8), sfa=_t((1000, 2), f32), lay=_t((7,), i32)) == binding.DG_INVALID_ARG  # Mcap % 128
+    assert "multiple of 128" in binding.last_error()
+    assert dispatch(lay=_t((Mcap // 128 + 1,), i32)) == binding.DG_INVALID_ARG  # layout length
+    assert dispatch(sfa=_t((Mcap, 1), f32)) == binding.DG_INVALID_ARG  # scale blocks
+    assert dispatch(cnt=_t((G,), f32)) == binding.DG_INVALID_ARG  # counts dtype
+    assert dispatch(slot=_t((T, k + 1), i32)) == binding.DG_INVALID_ARG  # slot shape
+    assert dispatch(a=_t((Mcap, K + 128), u8)) == binding.DG_INVALID_ARG  # K mismatch
+    shared = torch.empty(Mcap, dtype=i32)
+    assert dispatch(lay=shared[:Mcap // 128], cnt=shared[:G]) == binding.DG_INVALID_ARG  # overlap
+    # nothing to route into and no experts: nothing to do
+    assert dispatch(a=_t((0, K), u8), sfa=_t((0, 2), f32), lay=_t((0,), i32), cnt=_t((0,), i32)) == 0

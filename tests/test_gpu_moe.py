@@ -178,3 +178,84 @@ def test_moe_chain_dispatch_gemm_combine():
     # the GEMM's band carried through the weighted sum, then one BF16 rounding
     bound = band * (1 + REL_TOL) + REL_TOL * np.abs(y_ref) + 1e-6 * (np.abs(y_ref) + band)
     assert np.all(err <= bound), f"chain: {int((err > bound).sum())} outside the bound"
+
+
+# ---------------------------------------------------------------------------
+# contiguous layout (prefill)
+# ---------------------------------------------------------------------------
+
+def _contig_buffers(T, K, k, G, Mcap):
+    a = torch.full((Mcap, K), 0x55, dtype=torch.uint8, device="cuda")
+    sfa = torch.full((Mcap, -(-K // 128)), float("nan"), dtype=torch.float32, device="cuda")
+    layout = torch.full((Mcap // 128,), -7, dtype=torch.int32, device="cuda")
+    counts = torch.full((G,), -7, dtype=torch.int32, device="cuda")
+    slot = torch.full((T, k), -7, dtype=torch.int32, device="cuda")
+    return a, sfa, layout, counts, slot
+
+
+@pytest.mark.parametrize("T,k,G,Mcap,K,p_none,x_bf16", [
+    (4096, 8, 32, 36864, 7168, 0.0, False),  # a prefill routing: every pair fits
+    (50, 3, 7, 512, 200, 0.1, True),         # regions past the capacity: experts 4..6 dropped
+    (1, 1, 1, 128, 128, 0.0, False),
+    (0, 2, 4, 256, 256, 0.0, False),         # no tokens: counts 0, every block -1
+])
+def test_dispatch_contiguous_matches_oracle(T, k, G, Mcap, K, p_none, x_bf16):
+    say(f"moe_dispatch_contiguous_fp8 T={T} k={k} G={G} Mcap={Mcap} K={K} bf16={x_bf16}")
+    mg = _mg()
+    x = synth.normal_f32(651, (T, K))
+    topk, _ = synth.moe_routing(652, T, G, k, p_none)
+    if x_bf16:
+        xb = synth.bf16_bits_from_f32(x)
+        xd = to_dev(xb.view(np.int16)).view(torch.bfloat16)
+        x = oracle.bf16_decode(xb).astype(np.float32)
+    else:
+        xd = to_dev(x)
+    outs = _contig_buffers(T, K, k, G, Mcap)
+    mg.moe_dispatch_contiguous_fp8(xd, to_dev(topk), *outs)
+    torch.cuda.synchronize()
+    a, sfa, layout, counts, slot = (to_host(t) for t in outs)
+    ra, rsfa, owned, rlayout, rcounts, rslot = oracle.moe_dispatch_contiguous_fp8(x, topk, G, Mcap)
+    assert np.array_equal(counts, rcounts) and np.array_equal(layout, rlayout) and np.array_equal(slot, rslot)
+    assert np.array_equal(a[owned], ra[owned]), "codes"
+    assert np.array_equal(sfa[owned].view(np.uint32), rsfa[owned].view(np.uint32)), "scales"
+    assert np.all(a[~owned] == 0x55) and np.all(np.isnan(sfa[~owned])), "padding rows written"
+
+
+def test_moe_chain_contiguous_dispatch_gemm_combine():
+    """dispatch (contiguous) -> contiguous FP8 GEMM -> combine, against the
+    oracle's chain."""
+    mg = _mg()
+    T, k, G, N, K = 512, 4, 8, 512, 1024
+    Mcap = -(-(T * k + 127 * G) // 128) * 128
+    say(f"moe contiguous chain T={T} k={k} G={G} Mcap={Mcap} N={N} K={K}")
+    x = synth.normal_f32(661, (T, K))
+    xb = synth.normal_f32(662, (G, N, K))
+    topk, w = synth.moe_routing(663, T, G, k)
+    a, sfa, layout, counts, slot = _contig_buffers(T, K, k, G, Mcap)
+    mg.moe_dispatch_contiguous_fp8(to_dev(x), to_dev(topk), a, sfa, layout, counts, slot)
+    qb = torch.empty((G, N, K), dtype=torch.uint8, device="cuda")
+    sfb = torch.empty((G, N // 128, K // 128), dtype=torch.float32, device="cuda")
+    mg.per_block_cast_to_fp8(to_dev(xb), qb, sfb)
+    d = torch.zeros((Mcap, N), dtype=torch.bfloat16, device="cuda")
+    mg.m_grouped_fp8_gemm_nt_contiguous(a, qb, sfa, sfb, d, layout)
+    y = torch.empty((T, N), dtype=torch.bfloat16, device="cuda")
+    mg.moe_combine(d.view(1, Mcap, N), slot, to_dev(w), y)
+    torch.cuda.synchronize()
+    ra, rsfa, owned, rlayout, _, rslot = oracle.moe_dispatch_contiguous_fp8(x, topk, G, Mcap)
+    rb, rsfb = oracle.per_block_cast_to_fp8(xb)
+    rows = np.zeros((Mcap, N))
+    for e in range(G):
+        sel = owned & (np.repeat(rlayout, 128) == e)
+        rows[sel] = oracle.fp8_gemm_nt(ra[sel], rb[e], rsfa[sel], rsfb[e])
+    rms = float(np.sqrt(np.mean(rows[owned] ** 2)))
+    y_ref = np.zeros((T, N))
+    band = np.zeros((T, N))
+    for j in range(k):
+        ok = rslot[:, j] >= 0
+        wj = w[ok, j].astype(np.float64)[:, None]
+        y_ref[ok] += wj * rows[rslot[ok, j]]
+        band[ok] += wj * (ABS_RMS_TOL * rms + REL_TOL * np.abs(rows[rslot[ok, j]]))
+    got = oracle.bf16_decode(to_host(y))
+    bound = band * (1 + REL_TOL) + REL_TOL * np.abs(y_ref) + 1e-6 * (np.abs(y_ref) + band)
+    err = np.abs(got - y_ref)
+    assert np.all(err <= bound), f"contiguous chain: {int((err > bound).sum())} outside the bound"
