@@ -2,7 +2,7 @@
 
     python bench.py [--steps K] [--warmup W] [--settle-seconds S]
                     [--workload dense|contiguous|masked|masked_graph|bf16_dense|dense_rowb|dense_fp8_out|
-                                moe_decode]
+                                moe_decode|moe_prefill]
 
 Before the W warmup steps, untimed steps run for S seconds (default 1): under
 sustained GEMM load the GPU clock dips for the first few milliseconds and
@@ -37,6 +37,8 @@ Other workloads (for the measurements in the design notes):
                   cast per token to E4M3 in its epilogue (fp8_gemm_nt_fp8_out)
   moe_decode   -- 768 tokens to 8 of 32 experts: moe_dispatch_masked_fp8 (routing +
                   per-token cast), the masked FP8 GEMM (N 4096, K 7168), moe_combine
+  moe_prefill  -- 4096 tokens to 8 of 32 experts: moe_dispatch_contiguous_fp8, the
+                  contiguous FP8 GEMM (N 4096, K 7168), moe_combine
 """
 
 import argparse
@@ -318,14 +320,19 @@ class MoeDecodeWorkload:
     """MoE decode on one GPU around the masked GEMM: 768 tokens routed to 8
     of 32 experts (256-row buffers, about 192 rows each), N 4096, K 7168.
     One step = moe_dispatch_masked_fp8 (routing + per-token cast of the
-    routed tokens), the masked FP8 GEMM, and moe_combine."""
+    routed tokens), the masked FP8 GEMM, and moe_combine.  With contig=True
+    (MoePrefillWorkload): moe_dispatch_contiguous_fp8, the contiguous FP8
+    GEMM and moe_combine on 4096 tokens."""
     name = "moe_decode_dispatch_gemm_combine"
+    contig = False
 
     def __init__(self, torch, mg, synth):
         self.torch, self.mg = torch, mg
         dev = torch.device("cuda")
-        c = synth.MOE_DECODE
-        T, k, G, max_m, N, K = c["T"], c["k"], c["G"], c["max_m"], c["N"], c["K"]
+        c = synth.MOE_PREFILL if self.contig else synth.MOE_DECODE
+        T, k, G, N, K = c["T"], c["k"], c["G"], c["N"], c["K"]
+        # contiguous layout: one "group" of Mcap rows holding every region
+        max_m = -(-(T * k + 255 * G) // 256) * 256 if self.contig else c["max_m"]
         self.T, self.k, self.G, self.max_m, self.N, self.K = T, k, G, max_m, N, K
         self.shapes = [(N, K)]
         topk, w = synth.moe_routing(c["seed_r"], T, G, k)
@@ -339,22 +346,30 @@ class MoeDecodeWorkload:
             xb.copy_(torch.from_numpy(chunk))
             mg.per_block_cast_to_fp8(xb, self.b[g], self.sfb[g])  # expert weights: quantized once
         del xb
-        self.a = torch.empty((G, max_m, K), dtype=torch.uint8, device=dev)
-        self.sfa = torch.empty((G, max_m, K // 128), dtype=torch.float32, device=dev)
-        self.masked_m = torch.empty((G,), dtype=torch.int32, device=dev)
+        ga = 1 if self.contig else G
+        self.a = torch.empty((ga, max_m, K), dtype=torch.uint8, device=dev)
+        self.sfa = torch.empty((ga, max_m, K // 128), dtype=torch.float32, device=dev)
+        self.masked_m = torch.empty((G,), dtype=torch.int32, device=dev)  # contiguous: the counts
+        self.layout = torch.empty((max_m // 128,), dtype=torch.int32, device=dev)
         self.slot = torch.empty((T, k), dtype=torch.int32, device=dev)
-        self.src = torch.empty((G, max_m), dtype=torch.int32, device=dev)
-        self.d = torch.empty((G, max_m, N), dtype=torch.bfloat16, device=dev)
+        self.src = None if self.contig else torch.empty((G, max_m), dtype=torch.int32, device=dev)
+        self.d = torch.empty((ga, max_m, N), dtype=torch.bfloat16, device=dev)
         self.y = torch.empty((T, N), dtype=torch.bfloat16, device=dev)
         self.step()
         torch.cuda.synchronize()
         mm = self.masked_m.cpu().numpy()
         self.mm_host = mm
-        rows, active = int(mm.sum()), int((mm > 0).sum())
         placed = int((self.slot.cpu().numpy() >= 0).sum())
+        if self.contig:
+            # the GEMM computes every block of every region (padding included)
+            rows = int(sum(-(-int(c_) // 256) * 256 for c_ in mm))
+        else:
+            rows = int(mm.sum())
+        active = int((mm > 0).sum())
         self.flops = [2.0 * rows * N * K]
         self.gemm_bytes = [active * (N * K + 4 * (N // 128) * (K // 128)) + rows * (K + 4 * (K // 128) + 2 * N) + 4 * G]
-        self.dispatch_bytes = 4 * T * K + 2 * 4 * T * k + rows * (K + 4 * (K // 128)) + 4 * G + 4 * rows
+        # x read once, routing tables, the routed rows written with their scales
+        self.dispatch_bytes = 4 * T * K + 2 * 4 * T * k + placed * (K + 4 * (K // 128)) + 4 * G
         self.combine_bytes = placed * 2 * N + 2 * 4 * T * k + 2 * T * N
         self.step_bytes_total = self.dispatch_bytes + self.gemm_bytes[0] + self.combine_bytes
         self.extra_events = []
@@ -365,11 +380,19 @@ class MoeDecodeWorkload:
         if events is not None:
             ev = [self.torch.cuda.Event(enable_timing=True) for _ in range(4)]
             ev[0].record()
-        mg.moe_dispatch_masked_fp8(self.x, self.topk, self.a, self.sfa, self.masked_m, self.slot, self.src)
+        if self.contig:
+            # regions in 256-row granules: no 256-row tile of the GEMM holds two experts
+            mg.moe_dispatch_contiguous_fp8(self.x, self.topk, self.a[0], self.sfa[0], self.layout, self.masked_m,
+                                           self.slot, align=256)
+        else:
+            mg.moe_dispatch_masked_fp8(self.x, self.topk, self.a, self.sfa, self.masked_m, self.slot, self.src)
         if events is not None:
             ev[1].record()
             events[0][0].record()
-        mg.m_grouped_fp8_gemm_nt_masked(self.a, self.b, self.sfa, self.sfb, self.d, self.masked_m, self.max_m)
+        if self.contig:
+            mg.m_grouped_fp8_gemm_nt_contiguous(self.a[0], self.b, self.sfa[0], self.sfb, self.d[0], self.layout)
+        else:
+            mg.m_grouped_fp8_gemm_nt_masked(self.a, self.b, self.sfa, self.sfb, self.d, self.masked_m, self.max_m)
         if events is not None:
             events[0][1].record()
             ev[2].record()
@@ -386,12 +409,24 @@ class MoeDecodeWorkload:
                 "dispatch_bytes": self.dispatch_bytes, "combine_bytes": self.combine_bytes}
 
     def plan_args(self, i):
+        if self.contig:
+            return ("DG_KIND_CONTIGUOUS", self.G, self.max_m, self.N, self.K)
         return ("DG_KIND_MASKED", self.G, self.max_m, self.N, self.K)
 
     def config(self):
+        if self.contig:
+            return {"workload": self.name, "tokens": self.T, "topk": self.k, "experts": self.G, "rows": self.max_m,
+                    "N": self.N, "K": self.K, "routed_pairs": int(self.mm_host.sum()),
+                    "step": "moe_dispatch_contiguous_fp8 (count, place, per-token cast), contiguous FP8 GEMM, "
+                            "moe_combine"}
         return {"workload": self.name, "tokens": self.T, "topk": self.k, "experts": self.G, "max_m": self.max_m,
                 "N": self.N, "K": self.K, "sum_masked_m": int(self.mm_host.sum()),
                 "step": "moe_dispatch_masked_fp8 (route + per-token cast), masked FP8 GEMM, moe_combine"}
+
+
+class MoePrefillWorkload(MoeDecodeWorkload):
+    name = "moe_prefill_dispatch_gemm_combine"
+    contig = True
 
 
 class MaskedGraphWorkload:
@@ -594,7 +629,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="dense",
                     choices=["dense", "contiguous", "masked", "masked_graph", "bf16_dense", "dense_rowb",
-                             "dense_fp8_out", "moe_decode"])
+                             "dense_fp8_out", "moe_decode", "moe_prefill"])
     ap.add_argument("--settle-seconds", type=float, default=1.0,
                     help="untimed steps run for this long before the warmup steps, so that the timed steps see "
                          "the GPU's steady sustained clock rather than the dip of its first milliseconds under load")
@@ -623,7 +658,7 @@ def main():
     W = {"dense": DenseWorkload, "contiguous": ContiguousWorkload, "masked": MaskedWorkload,
          "masked_graph": MaskedGraphWorkload, "bf16_dense": Bf16DenseWorkload,
          "dense_rowb": DenseRowBWorkload, "dense_fp8_out": DenseFp8OutWorkload,
-         "moe_decode": MoeDecodeWorkload}[args.workload](torch, mg, synth)
+         "moe_decode": MoeDecodeWorkload, "moe_prefill": MoePrefillWorkload}[args.workload](torch, mg, synth)
     torch.cuda.synchronize()
 
     # Power-state settle: under sustained GEMM load the clock dips for the first
@@ -678,6 +713,7 @@ def main():
     mean_launch_ms = float(np.mean(gemm_ms))
     mean_flops = total_flops / nshape
     is_masked = args.workload in ("masked", "masked_graph", "moe_decode")
+    is_moe = args.workload in ("moe_decode", "moe_prefill")
     if graph_wl:
         # dominant kernel: the GEMM with the longest launches
         dom = int(np.argmax(gemm_ms))
@@ -732,6 +768,12 @@ def main():
         unit = "GB/s"
         value = W.step_bytes_total / (ms_per_step * 1e-3) / 1e9
         per_shape[0]["kernel"] = "fp8 masked"
+        per_shape[0].update(W.extra())
+        per_shape[0]["tokens_per_s"] = W.T / (ms_per_step * 1e-3)
+    elif args.workload == "moe_prefill":
+        metric = "MoE prefill (dispatch + per-token cast, contiguous FP8 GEMM, combine) TFLOPS (% FP8 MFMA peak)"
+        unit = "TFLOPS"
+        per_shape[0]["kernel"] = "fp8 contiguous"
         per_shape[0].update(W.extra())
         per_shape[0]["tokens_per_s"] = W.T / (ms_per_step * 1e-3)
     elif is_masked:

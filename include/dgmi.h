@@ -265,7 +265,7 @@ int moe_dispatch_masked_fp8(const dg_tensor* x, const dg_tensor* topk_idx, const
  *   x, topk_idx     as moe_dispatch_masked_fp8
  *   a               E4M3 [Mcap, K] out (Mcap % 128 == 0, 4-B aligned rows):
  *                   expert e's routed tokens fill a region of
- *                   ceil(count_e / 128) whole blocks, regions in expert
+ *                   ceil(count_e / align) * align rows, regions in expert
  *                   order, tokens in row-major (t, j) order; the rows of a
  *                   region past count_e are padding and left untouched
  *   sfa             F32 [Mcap, ceil(K/128)] out, any strides: their scales
@@ -274,14 +274,17 @@ int moe_dispatch_masked_fp8(const dg_tensor* x, const dg_tensor* topk_idx, const
  *   counts          I32 [G] out: pairs routed to each expert
  *   slot            I32 [T, k] out, contiguous: the row of a where (t, j)
  *                   landed, -1 if routed nowhere or past the capacity Mcap
- * Mcap >= T * k + 127 * G holds every routing.  The outputs feed
+ *   align           128 (whole blocks), or 256: no 256-row tile of the
+ *                   contiguous GEMM then holds two experts, which it would
+ *                   compute twice (one pass per expert)
+ * Mcap >= T * k + (align - 1) * G holds every routing.  The outputs feed
  * m_grouped_fp8_gemm_nt_contiguous (a, sfa, grouped_layout) and moe_combine
  * (slot, with the GEMM's [Mcap, N] output viewed as [1, Mcap, N]).
  */
 int moe_dispatch_contiguous_fp8(const dg_tensor* x, const dg_tensor* topk_idx, const dg_tensor* a,
                                 const dg_tensor* sfa, const dg_tensor* grouped_layout,
-                                const dg_tensor* counts, const dg_tensor* slot, int use_ue8m0,
-                                hipStream_t stream);
+                                const dg_tensor* counts, const dg_tensor* slot, int32_t align,
+                                int use_ue8m0, hipStream_t stream);
 
 /*
  * MoE combine: y[t] = sum over j of topk_weights[t, j] * d[slot[t, j]], the

@@ -98,7 +98,7 @@ def load_library(path=None):
         "per_block_cast_to_fp8": ([T, T, T, ctypes.c_int, vp], ctypes.c_int),
         "pack_ue8m0_to_int": ([T, T, vp, vp], ctypes.c_int),
         "moe_dispatch_masked_fp8": ([T, T, T, T, T, T, T, ctypes.c_int, vp], ctypes.c_int),
-        "moe_dispatch_contiguous_fp8": ([T, T, T, T, T, T, T, ctypes.c_int, vp], ctypes.c_int),
+        "moe_dispatch_contiguous_fp8": ([T, T, T, T, T, T, T, i32, ctypes.c_int, vp], ctypes.c_int),
         "moe_combine": ([T, T, T, T, vp], ctypes.c_int),
         "dg_query_config": ([i32, i64, i64, i64, i64, ctypes.POINTER(DgConfig)], ctypes.c_int),
     }
@@ -258,14 +258,15 @@ def moe_dispatch_masked_fp8(x, topk_idx, a, sfa, masked_m, slot, src, use_ue8m0=
     return a, sfa, masked_m, slot, src
 
 
-def moe_dispatch_contiguous_fp8(x, topk_idx, a, sfa, grouped_layout, counts, slot, use_ue8m0=False, stream=None):
-    """Route (token, choice) pairs into the contiguous layout (regions of
-    whole 128-row blocks per expert) with the per-token FP8 cast; fills
-    grouped_layout, counts and slot."""
+def moe_dispatch_contiguous_fp8(x, topk_idx, a, sfa, grouped_layout, counts, slot, align=128, use_ue8m0=False,
+                                stream=None):
+    """Route (token, choice) pairs into the contiguous layout (a region of
+    whole `align`-row granules per expert, align 128 or 256) with the
+    per-token FP8 cast; fills grouped_layout, counts and slot."""
     lib = load_library()
     _check(lib.moe_dispatch_contiguous_fp8(_ref(describe(x)), _ref(describe(topk_idx)), _ref(describe(a)),
                                            _ref(describe(sfa)), _ref(describe(grouped_layout)), _ref(describe(counts)),
-                                           _ref(describe(slot)), int(bool(use_ue8m0)), _stream(stream)))
+                                           _ref(describe(slot)), int(align), int(bool(use_ue8m0)), _stream(stream)))
     return a, sfa, grouped_layout, counts, slot
 
 

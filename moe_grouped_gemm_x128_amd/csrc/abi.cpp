@@ -695,8 +695,9 @@ int moe_dispatch_masked_fp8(const dg_tensor* x, const dg_tensor* topk_idx, const
 
 int moe_dispatch_contiguous_fp8(const dg_tensor* x, const dg_tensor* topk_idx, const dg_tensor* a,
                                 const dg_tensor* sfa, const dg_tensor* grouped_layout, const dg_tensor* counts,
-                                const dg_tensor* slot, int use_ue8m0, hipStream_t stream) {
+                                const dg_tensor* slot, int32_t align, int use_ue8m0, hipStream_t stream) {
   const char* fname = "moe_dispatch_contiguous_fp8";
+  if (align != 128 && align != 256) return fail(DG_INVALID_ARG, "%s: align must be 128 or 256 (got %d)", fname, align);
   DG_TRY(check_basic(x, "x", true));
   DG_TRY(check_basic(topk_idx, "topk_idx", true));
   DG_TRY(check_basic(a, "a", true));
@@ -755,6 +756,7 @@ int moe_dispatch_contiguous_fp8(const dg_tensor* x, const dg_tensor* topk_idx, c
   r.counts = static_cast<int32_t*>(counts->data);
   r.layout = static_cast<int32_t*>(grouped_layout->data);
   r.mcap = Mcap;
+  r.align = align;
   hipError_t e = dgmi::launch_moe_route_contiguous(r, stream);
   if (e != hipSuccess || Mcap == 0 || K == 0 || T == 0 || k == 0) return check_launch(e, fname);
   // the per-token cast of each token, stored into every row its slots name

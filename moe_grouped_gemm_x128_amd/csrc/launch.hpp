@@ -47,6 +47,7 @@ struct MoeRouteArgs {
   int32_t* counts;
   int32_t* layout;
   int64_t mcap;
+  int32_t align;  // region granule in rows: 128 or 256
 };
 
 // MoE combine (moe.hip): d BF16 [G, max_m, N] (strides in elements), slot and

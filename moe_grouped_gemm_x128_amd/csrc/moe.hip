@@ -47,8 +47,8 @@ __device__ __forceinline__ int64_t block_sum(int64_t v, int64_t* red) {
 
 // MODE: ROUTE_MASKED (rows of expert e's own buffer, capacity max_m),
 // ROUTE_COUNT (counts[e] only), ROUTE_CONTIG (rows of the concatenated
-// buffer: expert e's region of whole 128-row blocks starts after the
-// regions of experts 0..e-1, from counts; capacity mcap rows; the region's
+// buffer: expert e's region of ceil(count / align) * align rows starts after
+// the regions of experts 0..e-1, from counts; capacity mcap rows; the region's
 // blocks get id e in layout, blocks past the last region -1).  One workgroup
 // per expert (ROUTE_CONTIG: at least one, for the layout).
 template <int MODE>
@@ -62,7 +62,7 @@ __global__ __launch_bounds__(ROUTE_THREADS) void moe_route_kernel(const MoeRoute
   if constexpr (MODE == ROUTE_CONTIG) {
     int64_t before = 0, all = 0;
     for (int f = tid; f < p.G; f += ROUTE_THREADS) {
-      const int64_t rows = ((int64_t)p.counts[f] + 127) / 128 * 128;
+      const int64_t rows = ((int64_t)p.counts[f] + p.align - 1) / p.align * p.align;
       all += rows;
       before += f < e ? rows : 0;
     }
@@ -70,7 +70,7 @@ __global__ __launch_bounds__(ROUTE_THREADS) void moe_route_kernel(const MoeRoute
     const int64_t total = block_sum(all, red);
     const int64_t nblk = p.mcap / 128;
     if (e < p.G) {
-      const int64_t b0 = start / 128, b1 = (start + ((int64_t)p.counts[e] + 127) / 128 * 128) / 128;
+      const int64_t b0 = start / 128, b1 = (start + ((int64_t)p.counts[e] + p.align - 1) / p.align * p.align) / 128;
       for (int64_t b = b0 + tid; b < b1 && b < nblk; b += ROUTE_THREADS) p.layout[b] = e;
     }
     if (e == 0)

@@ -35,6 +35,10 @@ MASKED_GRAPH = dict(G=64, max_m=128, N=7168, K=2048, seed_a=501, seed_b=502, see
 # (mean 192 rows per expert, the masked decode's centre), 256-row buffers
 MOE_DECODE = dict(T=768, k=8, G=32, max_m=256, N=4096, K=7168, seed_x=601, seed_b=602, seed_r=603)
 
+# MoE prefill around the contiguous GEMM: 4096 tokens, each to 8 of 32 experts
+# (1024 rows per expert on average), capacity T * k + 127 * G rounded to 128
+MOE_PREFILL = dict(T=4096, k=8, G=32, N=4096, K=7168, seed_x=671, seed_b=672, seed_r=673)
+
 
 def dense_v3_seeds(i):
     return 201 + 2 * i, 202 + 2 * i

@@ -21,9 +21,10 @@ the reading taken (listed in the design notes):
     j]], where D is the masked GEMM's BF16 output [G, max_m, N].
   * Contiguous layout (prefill, "DeepGEMM tested by Novita AI", contiguous
     layout: groups concatenated along M in 128-row blocks, a group id per
-    block): expert e's pairs fill a region of ceil(count_e / 128) blocks
-    that starts where expert e - 1's region ends; rows past the capacity
-    Mcap are dropped; blocks past the last region get id -1.  slot[t, j] is
+    block): expert e's pairs fill a region of ceil(count_e / align) * align
+    rows (align 128, or 256 so that no 256-row tile holds two experts) that
+    starts where expert e - 1's region ends; rows past the capacity Mcap are
+    dropped; blocks past the last region get id -1.  slot[t, j] is
     the row in the concatenated buffer (or -1); rows of a region past its
     count are padding that no token owns.
 
@@ -97,7 +98,7 @@ def moe_combine(d_bits, slot, topk_weights):
     return y
 
 
-def moe_route_contiguous(topk_idx, G, Mcap):
+def moe_route_contiguous(topk_idx, G, Mcap, align=128):
     """Returns (counts int64 [G] before capping, slot int32 [T, k],
     grouped_layout int32 [Mcap / 128], start int64 [G] first row of each
     expert's region)."""
@@ -109,7 +110,7 @@ def moe_route_contiguous(topk_idx, G, Mcap):
             e = int(topk[t, j])
             if 0 <= e < G:
                 counts[e] += 1
-    blocks = -(-counts // 128)
+    blocks = -(-counts // align) * (align // 128)
     start = np.concatenate([[0], np.cumsum(blocks)[:-1]]) * 128
     layout = np.full(Mcap // 128, -1, dtype=np.int32)
     for e in range(G):
@@ -130,14 +131,14 @@ def moe_route_contiguous(topk_idx, G, Mcap):
     return counts, slot, layout, start
 
 
-def moe_dispatch_contiguous_fp8(x, topk_idx, G, Mcap, use_ue8m0=False):
+def moe_dispatch_contiguous_fp8(x, topk_idx, G, Mcap, use_ue8m0=False, align=128):
     """Route into the contiguous layout and cast the routed tokens.
 
     Returns (a uint8 [Mcap, K], sfa float32 [Mcap, ceil(K/128)], owned bool
     [Mcap] (rows a token was cast into), grouped_layout, counts, slot)."""
     x = np.asarray(x, dtype=np.float32)
     T, K = x.shape
-    counts, slot, layout, _ = moe_route_contiguous(topk_idx, G, Mcap)
+    counts, slot, layout, _ = moe_route_contiguous(topk_idx, G, Mcap, align)
     a = np.zeros((Mcap, K), dtype=np.uint8)
     sfa = np.zeros((Mcap, -(-K // 128)), dtype=np.float32)
     owned = np.zeros(Mcap, dtype=bool)

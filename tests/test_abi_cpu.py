@@ -433,7 +433,7 @@ def test_moe_dispatch_contiguous_validation_errors(lib):
     f32, u8, i32 = torch.float32, torch.uint8, torch.int32
     T, K, k, G, Mcap = 16, 256, 4, 8, 1024
 
-    def dispatch(x=None, topk=None, a=None, sfa=None, lay=None, cnt=None, slot=None):
+    def dispatch(x=None, topk=None, a=None, sfa=None, lay=None, cnt=None, slot=None, align=128):
         x = _t((T, K), f32) if x is None else x
         topk = _t((T, k), i32) if topk is None else topk
         a = _t((Mcap, K), u8) if a is None else a
@@ -441,11 +441,14 @@ def test_moe_dispatch_contiguous_validation_errors(lib):
         lay = _t((Mcap // 128,), i32) if lay is None else lay
         cnt = _t((G,), i32) if cnt is None else cnt
         slot = _t((T, k), i32) if slot is None else slot
-        return lib.moe_dispatch_contiguous_fp8(*(ctypes.byref(D(t)) for t in (x, topk, a, sfa, lay, cnt, slot)), 0, None)
+        return lib.moe_dispatch_contiguous_fp8(*(ctypes.byref(D(t)) for t in (x, topk, a, sfa, lay, cnt, slot)), align, 0,
+                                               None)
 
     assert dispatch(a=_t((1000, K), u8), sfa=_t((1000, 2), f32), lay=_t((7,), i32)) == binding.DG_INVALID_ARG  # Mcap % 128
     assert "multiple of 128" in binding.last_error()
     assert dispatch(lay=_t((Mcap // 128 + 1,), i32)) == binding.DG_INVALID_ARG  # layout length
+    assert dispatch(align=192) == binding.DG_INVALID_ARG  # granule
+    assert "align" in binding.last_error()
     assert dispatch(sfa=_t((Mcap, 1), f32)) == binding.DG_INVALID_ARG  # scale blocks
     assert dispatch(cnt=_t((G,), f32)) == binding.DG_INVALID_ARG  # counts dtype
     assert dispatch(slot=_t((T, k + 1), i32)) == binding.DG_INVALID_ARG  # slot shape

@@ -193,14 +193,16 @@ def _contig_buffers(T, K, k, G, Mcap):
     return a, sfa, layout, counts, slot
 
 
-@pytest.mark.parametrize("T,k,G,Mcap,K,p_none,x_bf16", [
-    (4096, 8, 32, 36864, 7168, 0.0, False),  # a prefill routing: every pair fits
-    (50, 3, 7, 512, 200, 0.1, True),         # regions past the capacity: experts 4..6 dropped
-    (1, 1, 1, 128, 128, 0.0, False),
-    (0, 2, 4, 256, 256, 0.0, False),         # no tokens: counts 0, every block -1
+@pytest.mark.parametrize("T,k,G,Mcap,K,p_none,x_bf16,align", [
+    (4096, 8, 32, 36864, 7168, 0.0, False, 128),  # a prefill routing: every pair fits
+    (4096, 8, 32, 40960, 7168, 0.0, False, 256),  # the same in 256-row granules
+    (50, 3, 7, 512, 200, 0.1, True, 128),         # regions past the capacity: experts 4..6 dropped
+    (50, 3, 7, 1024, 200, 0.1, True, 256),        # (256: experts 4..6 dropped as well)
+    (1, 1, 1, 128, 128, 0.0, False, 256),         # a region larger than the capacity
+    (0, 2, 4, 256, 256, 0.0, False, 128),         # no tokens: counts 0, every block -1
 ])
-def test_dispatch_contiguous_matches_oracle(T, k, G, Mcap, K, p_none, x_bf16):
-    say(f"moe_dispatch_contiguous_fp8 T={T} k={k} G={G} Mcap={Mcap} K={K} bf16={x_bf16}")
+def test_dispatch_contiguous_matches_oracle(T, k, G, Mcap, K, p_none, x_bf16, align):
+    say(f"moe_dispatch_contiguous_fp8 T={T} k={k} G={G} Mcap={Mcap} K={K} bf16={x_bf16} align={align}")
     mg = _mg()
     x = synth.normal_f32(651, (T, K))
     topk, _ = synth.moe_routing(652, T, G, k, p_none)
@@ -211,28 +213,29 @@ def test_dispatch_contiguous_matches_oracle(T, k, G, Mcap, K, p_none, x_bf16):
     else:
         xd = to_dev(x)
     outs = _contig_buffers(T, K, k, G, Mcap)
-    mg.moe_dispatch_contiguous_fp8(xd, to_dev(topk), *outs)
+    mg.moe_dispatch_contiguous_fp8(xd, to_dev(topk), *outs, align=align)
     torch.cuda.synchronize()
     a, sfa, layout, counts, slot = (to_host(t) for t in outs)
-    ra, rsfa, owned, rlayout, rcounts, rslot = oracle.moe_dispatch_contiguous_fp8(x, topk, G, Mcap)
+    ra, rsfa, owned, rlayout, rcounts, rslot = oracle.moe_dispatch_contiguous_fp8(x, topk, G, Mcap, align=align)
     assert np.array_equal(counts, rcounts) and np.array_equal(layout, rlayout) and np.array_equal(slot, rslot)
     assert np.array_equal(a[owned], ra[owned]), "codes"
     assert np.array_equal(sfa[owned].view(np.uint32), rsfa[owned].view(np.uint32)), "scales"
     assert np.all(a[~owned] == 0x55) and np.all(np.isnan(sfa[~owned])), "padding rows written"
 
 
-def test_moe_chain_contiguous_dispatch_gemm_combine():
+@pytest.mark.parametrize("align", [128, 256])
+def test_moe_chain_contiguous_dispatch_gemm_combine(align):
     """dispatch (contiguous) -> contiguous FP8 GEMM -> combine, against the
     oracle's chain."""
     mg = _mg()
     T, k, G, N, K = 512, 4, 8, 512, 1024
-    Mcap = -(-(T * k + 127 * G) // 128) * 128
+    Mcap = -(-(T * k + (align - 1) * G) // 128) * 128
     say(f"moe contiguous chain T={T} k={k} G={G} Mcap={Mcap} N={N} K={K}")
     x = synth.normal_f32(661, (T, K))
     xb = synth.normal_f32(662, (G, N, K))
     topk, w = synth.moe_routing(663, T, G, k)
     a, sfa, layout, counts, slot = _contig_buffers(T, K, k, G, Mcap)
-    mg.moe_dispatch_contiguous_fp8(to_dev(x), to_dev(topk), a, sfa, layout, counts, slot)
+    mg.moe_dispatch_contiguous_fp8(to_dev(x), to_dev(topk), a, sfa, layout, counts, slot, align=align)
     qb = torch.empty((G, N, K), dtype=torch.uint8, device="cuda")
     sfb = torch.empty((G, N // 128, K // 128), dtype=torch.float32, device="cuda")
     mg.per_block_cast_to_fp8(to_dev(xb), qb, sfb)
@@ -241,7 +244,7 @@ def test_moe_chain_contiguous_dispatch_gemm_combine():
     y = torch.empty((T, N), dtype=torch.bfloat16, device="cuda")
     mg.moe_combine(d.view(1, Mcap, N), slot, to_dev(w), y)
     torch.cuda.synchronize()
-    ra, rsfa, owned, rlayout, _, rslot = oracle.moe_dispatch_contiguous_fp8(x, topk, G, Mcap)
+    ra, rsfa, owned, rlayout, _, rslot = oracle.moe_dispatch_contiguous_fp8(x, topk, G, Mcap, align=align)
     rb, rsfb = oracle.per_block_cast_to_fp8(xb)
     rows = np.zeros((Mcap, N))
     for e in range(G):

@@ -22,7 +22,8 @@ def _golden():
             continue
         key, rest = line.split(None, 1)
         rows = [[int(v) for v in r.split()] for r in rest.split("|")]
-        rec[key] = rows[0][0] if key in ("G", "max_m", "c_Mcap", "c2_Mcap") else np.array(rows if len(rows) > 1 else rows[0])
+        scalar = key in ("G", "max_m") or key.endswith("_Mcap") or key.endswith("_align")
+        rec[key] = rows[0][0] if scalar else np.array(rows if len(rows) > 1 else rows[0])
     return rec
 
 
@@ -111,29 +112,30 @@ def test_combine_brute_force_and_closed_forms():
 
 def test_route_contiguous_hand_worked_example():
     g = _golden()
-    for pre in ("c_", "c2_"):
-        counts, slot, layout, _ = oracle.moe_route_contiguous(g["topk"], g["G"], g[pre + "Mcap"])
+    for pre in ("c_", "c2_", "c3_"):
+        counts, slot, layout, _ = oracle.moe_route_contiguous(g["topk"], g["G"], g[pre + "Mcap"], g.get(pre + "align", 128))
         assert counts.tolist() == g["counts"].tolist()
         assert layout.tolist() == g[pre + "layout"].tolist()
         assert slot.tolist() == g[pre + "slot"].tolist()
 
 
+@pytest.mark.parametrize("align", [128, 256])
 @pytest.mark.parametrize("T,k,G,Mcap,seed", [(300, 8, 16, 4096, 1), (300, 8, 16, 1024, 2), (40, 3, 7, 1024, 3)])
-def test_route_contiguous_matches_vectorised_construction(T, k, G, Mcap, seed):
+def test_route_contiguous_matches_vectorised_construction(T, k, G, Mcap, seed, align):
     rng = np.random.default_rng(seed)
     topk = rng.integers(-1, G + 1, size=(T, k))
     flat = topk.reshape(-1)
     counts = np.array([(flat == e).sum() for e in range(G)])
-    start = np.concatenate([[0], np.cumsum(-(-counts // 128))[:-1]]) * 128
+    start = np.concatenate([[0], np.cumsum(-(-counts // align) * align)[:-1]])
     slot = np.full(T * k, -1)
     layout = np.full(Mcap // 128, -1)
     for e in range(G):
         idx = np.flatnonzero(flat == e)
         rows = start[e] + np.arange(idx.size)
         slot[idx[rows < Mcap]] = rows[rows < Mcap]
-        nb = -(-counts[e] // 128)
+        nb = -(-counts[e] // align) * align // 128
         layout[start[e] // 128:min(start[e] // 128 + nb, Mcap // 128)] = e
-    got = oracle.moe_route_contiguous(topk, G, Mcap)
+    got = oracle.moe_route_contiguous(topk, G, Mcap, align)
     assert np.array_equal(got[0], counts)
     assert np.array_equal(got[1], slot.reshape(T, k))
     assert np.array_equal(got[2], layout)
