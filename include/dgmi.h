@@ -196,9 +196,14 @@ int m_grouped_bf16_gemm_nt_contiguous(const dg_tensor* a, const dg_tensor* b, co
  * scale s = amax/448 (amax floored at 1e-4; with use_ue8m0 rounded up to a
  * power of two), q = e4m3(x/s) rounded to nearest even after clamping to
  * +-448 ("DeepInside DeepGEMM", section 5: the FP8 casting helpers).
- *   x  F32 or BF16 [R, K] or [G, R, K]
- *   q  E4M3 same shape
+ *   x  F32 or BF16 [R, K] or [G, R, K]: K-major (innermost stride 1, 16-B
+ *      aligned rows), or MN-major (stride 1 along R: the transpose of a
+ *      row-major [K, R] tensor, e.g. an activation kept [K, M] for the TN
+ *      GEMM), read through a transposing LDS tile ("DeepInside DeepGEMM",
+ *      section 5: transposition and casting fused into the producer)
+ *   q  E4M3 same shape, K-major: the operand layout of the NT GEMMs
  *   sf F32 [R, ceil(K/128)] (or [G, R, ...]) with any strides
+ * The bytes do not depend on the layout of x.
  */
 int per_token_cast_to_fp8(const dg_tensor* x, const dg_tensor* q, const dg_tensor* sf,
                           int use_ue8m0, hipStream_t stream);
@@ -206,7 +211,9 @@ int per_token_cast_to_fp8(const dg_tensor* x, const dg_tensor* q, const dg_tenso
 /*
  * Per-block FP8 cast over 128x128 blocks (weights): as per_token_cast_to_fp8
  * with one scale per block.
- *   x  F32 or BF16 [N, K] or [G, N, K];  q E4M3 same shape
+ *   x  F32 or BF16 [N, K] or [G, N, K], K-major or MN-major as for
+ *      per_token_cast_to_fp8 (a weight kept [K, N] for the NN / TT GEMMs);
+ *      q E4M3 same shape, K-major
  *   sf F32 [ceil(N/128), ceil(K/128)] or [G, ...] with any strides
  */
 int per_block_cast_to_fp8(const dg_tensor* x, const dg_tensor* q, const dg_tensor* sf,

@@ -351,9 +351,13 @@ int fp8_gemm_common(int mode, const dg_tensor* a, const dg_tensor* b, const dg_t
 }
 
 // Quantizer validation: x [R, K] or [G, R, K]; q same shape; sf [.., R', KB].
+// x is K-major (innermost stride 1) or MN-major (stride 1 along the rows:
+// the transpose of a row-major [K, R] tensor), q is K-major.
 int quant_common(const dg_tensor* x, const dg_tensor* q, const dg_tensor* sf, int use_ue8m0, hipStream_t stream,
                  bool per_block, const char* fname) {
-  DG_TRY(check_basic(x, "x", true));
+  const bool mn_major = x != nullptr && x->ndim >= 2 && x->shape[x->ndim - 1] > 1 && x->stride[x->ndim - 1] != 1 &&
+                        (x->shape[x->ndim - 2] <= 1 || x->stride[x->ndim - 2] == 1);
+  DG_TRY(check_basic(x, "x", !mn_major));
   DG_TRY(check_basic(q, "q", true));
   DG_TRY(check_basic(sf, "sf", false));
   if (x->dtype != DG_F32 && x->dtype != DG_BF16) return fail(DG_INVALID_ARG, "%s: x must be F32 or BF16", fname);
@@ -373,8 +377,9 @@ int quant_common(const dg_tensor* x, const dg_tensor* q, const dg_tensor* sf, in
     return fail(DG_INVALID_ARG, "%s: sf is [..,%lld,%lld], expected [..,%lld,%lld]", fname, (long long)vs.R,
                 (long long)vs.C, (long long)srows, (long long)((K + 127) / 128));
   const int xe = elem_size(x->dtype);
-  if (!aligned(x->data, 16) || (vx.sr * xe) % 16 || (vx.sg * xe) % 16)
+  if (!mn_major && (!aligned(x->data, 16) || (vx.sr * xe) % 16 || (vx.sg * xe) % 16))
     return fail(DG_INVALID_ARG, "%s: x needs a 16-byte aligned base and row/group strides", fname);
+  if (mn_major && !aligned(x->data, xe)) return fail(DG_INVALID_ARG, "%s: x must be element-aligned", fname);
   if (!aligned(q->data, 4) || vq.sr % 4 || vq.sg % 4)
     return fail(DG_INVALID_ARG, "%s: q needs a 4-byte aligned base and row/group strides", fname);
   if (!aligned(sf->data, 4)) return fail(DG_INVALID_ARG, "%s: sf must be 4-byte aligned", fname);
@@ -398,6 +403,16 @@ int quant_common(const dg_tensor* x, const dg_tensor* q, const dg_tensor* sf, in
   p.K = (int32_t)K;
   p.ue8m0 = use_ue8m0 ? 1 : 0;
   if (vx.G == 0 || R == 0 || K == 0) return ok();
+  if (mn_major) {
+    // read through a transposing LDS tile
+    dgmi::QuantTArgs t = {};
+    static_cast<dgmi::QuantArgs&>(t) = p;
+    t.sx_k = x->stride[x->ndim - 1];
+    const int64_t lb = x->dtype == DG_F32 ? 16 : 8;  // bytes of four elements
+    t.vec = (aligned(x->data, (int)lb) && (t.sx_k * xe) % lb == 0 && (vx.sg * xe) % lb == 0) ? 1 : 0;
+    t.qvec = (aligned(q->data, 16) && (R <= 1 || vq.sr % 16 == 0) && (vx.G <= 1 || vq.sg % 16 == 0)) ? 1 : 0;
+    return check_launch(dgmi::launch_cast_mn(t, per_block, stream), fname);
+  }
   return check_launch(per_block ? dgmi::launch_per_block(p, stream) : dgmi::launch_per_token(p, stream), fname);
 }
 

@@ -23,6 +23,14 @@ struct QuantArgs {
   int32_t ue8m0;
 };
 
+// Casts of an MN-major x: element (g, r, k) at x[g * sx_g + k * sx_k + r]
+// (sx_r unused); vec: 16-byte (f32) / 8-byte (bf16) loads along r are
+// aligned; qvec: q rows take 16-byte stores.
+struct QuantTArgs : QuantArgs {
+  int64_t sx_k;
+  int32_t vec, qvec;
+};
+
 // Per-token cast of the tokens x [T, K] (G = 1, R = T) into the rows their
 // slots name: slot[t * k + j] = e * max_m + row in [0, rows) selects row
 // `row` of group e of q and sf (strides sq_g / sq_r, ssf_g / ssf_r); other
@@ -82,6 +90,7 @@ struct TileCfg {
 
 hipError_t launch_per_token(const QuantArgs& p, hipStream_t stream);
 hipError_t launch_per_token_scatter(const QuantScatterArgs& p, hipStream_t stream);
+hipError_t launch_cast_mn(const QuantTArgs& p, bool per_block, hipStream_t stream);
 hipError_t launch_moe_route(const MoeRouteArgs& p, hipStream_t stream);
 hipError_t launch_moe_route_contiguous(const MoeRouteArgs& p, hipStream_t stream);
 hipError_t launch_moe_combine(const MoeCombineArgs& p, hipStream_t stream);

@@ -241,7 +241,126 @@ __global__ __launch_bounds__(256) void pack_ue8m0_kernel(PackArgs p) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Casts of an MN-major x: element (g, r, k) at x[g * sx_g + k * sx_k + r]
+// (the transpose of a row-major [K, R] tensor), written K-major as the NT
+// GEMM reads it ("DeepInside DeepGEMM", section 5: transposition and FP8
+// casting fused into one producer instead of separate helpers).  One
+// workgroup per 128 (K) x TR (rows) tile: the tile is read with loads that
+// run along the rows (coalesced), staged through LDS as [k][r] (one float of
+// padding per k), and each row's 128-element K-run is then read down a
+// column (64 lanes of a wave on 64 consecutive rows: no bank conflicts).
+// Per-token (TR = 64): four waves hold 32 k each of the same 64 rows, the
+// row's block maximum is combined through LDS.  Per-block (TR = 128): the
+// block maximum over the whole tile.  The scale and codes are those of the
+// row-major casts above, bit for bit.
+// ---------------------------------------------------------------------------
+template <typename TIn, bool PER_BLOCK>
+__global__ __launch_bounds__(256) void cast_mn_kernel(QuantTArgs p) {
+  constexpr int TR = PER_BLOCK ? 128 : 64;  // rows of the tile
+  constexpr int LD = TR + 1;                // LDS row pitch (floats)
+  constexpr int KPT = PER_BLOCK ? 64 : 32;  // k values per thread in the column phase
+  __shared__ float tile[128 * LD];
+  __shared__ float part[256 / 64 * 64];
+  const TIn* __restrict__ x = static_cast<const TIn*>(p.x);
+  const int RB = (p.R + TR - 1) / TR, KB = (p.K + 127) / 128;
+  int blk = blockIdx.x;
+  const int kb = blk % KB;
+  blk /= KB;
+  const int rb = blk % RB;
+  const int g = blk / RB;
+  const int tid = threadIdx.x;
+  const int r0 = rb * TR, k0 = kb * 128;
+  const TIn* xg = x + g * p.sx_g;
+
+  // phase 1: 128 k-rows of TR values, four consecutive rows per thread
+  constexpr int GROUPS = TR / 4;           // threads per k-row
+  constexpr int KROWS = 256 / GROUPS;      // k-rows per pass
+#pragma unroll 4
+  for (int kk = tid / GROUPS; kk < 128; kk += KROWS) {
+    const int rq = (tid % GROUPS) * 4;
+    const int gk = k0 + kk, gr = r0 + rq;
+    float v[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    if (gk < p.K) {
+      const TIn* src = xg + (int64_t)gk * p.sx_k + gr;
+      if (p.vec && gr + 3 < p.R) {
+        load4(src, v);
+      } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          if (gr + j < p.R) v[j] = load_elem(src + j);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) tile[kk * LD + rq + j] = v[j];
+  }
+  __syncthreads();
+
+  // phase 2: thread (c, r) holds k = c * KPT .. + KPT - 1 of row r
+  const int r = tid % TR, c = tid / TR;
+  float v[KPT];
+  float m = 0.0f;
+#pragma unroll
+  for (int i = 0; i < KPT; ++i) {
+    v[i] = tile[(c * KPT + i) * LD + r];
+    m = fmaxf(m, fabsf(v[i]));
+  }
+  float amax;
+  if constexpr (PER_BLOCK) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
+    if ((tid & 63) == 0) part[tid >> 6] = m;
+    __syncthreads();
+    amax = fmaxf(fmaxf(part[0], part[1]), fmaxf(part[2], part[3]));
+  } else {
+    part[c * 64 + r] = m;
+    __syncthreads();
+    amax = fmaxf(fmaxf(part[r], part[64 + r]), fmaxf(part[128 + r], part[192 + r]));
+  }
+  const float s = block_scale(amax, p.ue8m0);
+  const Recip d = recip_of(s);
+  const int gr = r0 + r;
+  if (gr >= p.R) return;
+  uint8_t* qr = p.q + g * p.sq_g + (int64_t)gr * p.sq_r;
+  const int kc = k0 + c * KPT;  // first k of this thread
+  uint32_t w[KPT / 4];
+#pragma unroll
+  for (int i = 0; i < KPT / 4; ++i) {
+    const float t4[4] = {v[4 * i], v[4 * i + 1], v[4 * i + 2], v[4 * i + 3]};
+    w[i] = encode4(t4, d);
+  }
+  if (p.qvec && kc + KPT <= p.K) {
+#pragma unroll
+    for (int i = 0; i < KPT / 16; ++i)
+      *reinterpret_cast<i32x4*>(qr + kc + 16 * i) =
+          i32x4{(int)w[4 * i], (int)w[4 * i + 1], (int)w[4 * i + 2], (int)w[4 * i + 3]};
+  } else {
+#pragma unroll
+    for (int i = 0; i < KPT; ++i)
+      if (kc + i < p.K) qr[kc + i] = (uint8_t)(w[i / 4] >> (8 * (i & 3)));
+  }
+  if (PER_BLOCK ? (tid == 0) : (c == 0)) {
+    const int srow = PER_BLOCK ? rb : gr;
+    p.sf[g * p.ssf_g + (int64_t)srow * p.ssf_r + kb * p.ssf_k] = s;
+  }
+}
+
 }  // namespace
+
+hipError_t launch_cast_mn(const QuantTArgs& p, bool per_block, hipStream_t stream) {
+  const int TR = per_block ? 128 : 64;
+  const int64_t blocks = (int64_t)p.G * ((p.R + TR - 1) / TR) * ((p.K + 127) / 128);
+  if (blocks == 0) return hipSuccess;
+  const dim3 g((unsigned)blocks), b(256);
+  if (per_block) {
+    if (p.x_bf16) cast_mn_kernel<uint16_t, true><<<g, b, 0, stream>>>(p);
+    else cast_mn_kernel<float, true><<<g, b, 0, stream>>>(p);
+  } else {
+    if (p.x_bf16) cast_mn_kernel<uint16_t, false><<<g, b, 0, stream>>>(p);
+    else cast_mn_kernel<float, false><<<g, b, 0, stream>>>(p);
+  }
+  return hipGetLastError();
+}
 
 hipError_t launch_per_token(const QuantArgs& p, hipStream_t stream) {
   const int64_t KB = (p.K + 127) / 128;

@@ -262,3 +262,65 @@ def test_moe_chain_contiguous_dispatch_gemm_combine(align):
     bound = band * (1 + REL_TOL) + REL_TOL * np.abs(y_ref) + 1e-6 * (np.abs(y_ref) + band)
     err = np.abs(got - y_ref)
     assert np.all(err <= bound), f"contiguous chain: {int((err > bound).sum())} outside the bound"
+
+
+def test_moe_decode_chain_graph_replay():
+    """dispatch -> masked FP8 GEMM -> combine captured once in a hipGraph and
+    replayed with new routing and tokens written before each replay (the
+    fused MoE path's graph compatibility, "DeepGEMM CUDA Graph Compatibility
+    for Masked Grouped GEMMs", last section); every replay equals an eager
+    run of the same calls, bit for bit."""
+    mg = _mg()
+    T, k, G, max_m, N, K = 256, 4, 16, 128, 512, 1024
+    say(f"moe decode chain graph replay T={T} k={k} G={G} max_m={max_m} N={N} K={K}")
+    qb = torch.empty((G, N, K), dtype=torch.uint8, device="cuda")
+    sfb = torch.empty((G, N // 128, K // 128), dtype=torch.float32, device="cuda")
+    mg.per_block_cast_to_fp8(to_dev(synth.normal_f32(671, (G, N, K))), qb, sfb)
+    x = torch.empty((T, K), dtype=torch.float32, device="cuda")
+    topk = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    w = torch.empty((T, k), dtype=torch.float32, device="cuda")
+
+    def buffers():
+        a, sfa, masked_m, slot, src = _dispatch_buffers(T, K, k, G, max_m)
+        d = torch.zeros((G, max_m, N), dtype=torch.bfloat16, device="cuda")
+        y = torch.zeros((T, N), dtype=torch.bfloat16, device="cuda")
+        return a, sfa, masked_m, slot, src, d, y
+
+    def calls(bufs, stream=None):
+        a, sfa, masked_m, slot, src, d, y = bufs
+        mg.moe_dispatch_masked_fp8(x, topk, a, sfa, masked_m, slot, src, stream=stream)
+        mg.m_grouped_fp8_gemm_nt_masked(a, qb, sfa, sfb, d, masked_m, max_m, stream=stream)
+        mg.moe_combine(d, slot, w, y, stream=stream)
+
+    gbufs = buffers()
+    x.copy_(to_dev(synth.normal_f32(672, (T, K))))
+    t0, w0 = synth.moe_routing(673, T, G, k)
+    topk.copy_(to_dev(t0))
+    w.copy_(to_dev(w0))
+    calls(gbufs)  # eager warm-up
+    torch.cuda.synchronize()
+    stream = torch.cuda.Stream()
+    stream.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(stream):
+        with torch.cuda.graph(graph, stream=stream):
+            calls(gbufs, stream=stream)
+    torch.cuda.current_stream().wait_stream(stream)
+    torch.cuda.synchronize()
+    for r in range(3):
+        x.copy_(to_dev(synth.normal_f32(680 + r, (T, K))))
+        tr, wr = synth.moe_routing(690 + r, T, G, k, 0.2 * r)
+        topk.copy_(to_dev(tr))
+        w.copy_(to_dev(wr))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        ebufs = buffers()
+        calls(ebufs)
+        torch.cuda.synchronize()
+        y_g, y_e = gbufs[6], ebufs[6]
+        assert torch.equal(y_g.view(torch.int16), y_e.view(torch.int16)), f"replay {r}: combine output"
+        assert torch.equal(gbufs[2], ebufs[2]) and torch.equal(gbufs[3], ebufs[3]), f"replay {r}: routing"
+        # and the routing against the oracle
+        rmm, rslot, _, _ = oracle.moe_route(tr, G, max_m)
+        assert np.array_equal(to_host(gbufs[2]), rmm) and np.array_equal(to_host(gbufs[3]), rslot), f"replay {r}"
