@@ -246,22 +246,25 @@ __global__ __launch_bounds__(256) void pack_ue8m0_kernel(PackArgs p) {
 // (the transpose of a row-major [K, R] tensor), written K-major as the NT
 // GEMM reads it ("DeepInside DeepGEMM", section 5: transposition and FP8
 // casting fused into one producer instead of separate helpers).  One
-// workgroup per 128 (K) x TR (rows) tile: the tile is read with loads that
-// run along the rows (coalesced), staged through LDS as [k][r] (one float of
-// padding per k), and each row's 128-element K-run is then read down a
-// column (64 lanes of a wave on 64 consecutive rows: no bank conflicts).
-// Per-token (TR = 64): four waves hold 32 k each of the same 64 rows, the
-// row's block maximum is combined through LDS.  Per-block (TR = 128): the
-// block maximum over the whole tile.  The scale and codes are those of the
-// row-major casts above, bit for bit.
+// workgroup per 128 (K) x TR (rows) tile.  Each thread loads 4 x 4 blocks
+// (four consecutive rows at four consecutive k: loads run along the rows,
+// coalesced) and keeps them in registers; the block maximum is reduced from
+// registers (per-token: over the 16 threads holding the same rows, through
+// shuffles and an LDS exchange between the four waves; per-block: over the
+// workgroup).  encode4 on a column of a 4 x 4 block gives one row's four
+// consecutive codes as one word, so only the codes pass through LDS, as
+// [r][k] bytes, and each row leaves as contiguous 16-byte pieces.  The scale
+// and codes are those of the row-major casts above, bit for bit.
 // ---------------------------------------------------------------------------
 template <typename TIn, bool PER_BLOCK>
 __global__ __launch_bounds__(256) void cast_mn_kernel(QuantTArgs p) {
   constexpr int TR = PER_BLOCK ? 128 : 64;  // rows of the tile
-  constexpr int LD = TR + 1;                // LDS row pitch (floats)
-  constexpr int KPT = PER_BLOCK ? 64 : 32;  // k values per thread in the column phase
-  __shared__ float tile[128 * LD];
-  __shared__ float part[256 / 64 * 64];
+  constexpr int RQ = TR / 4;                // row quads
+  constexpr int NB = 128 * TR / 16 / 256;   // 4 x 4 blocks per thread (2 or 4)
+  constexpr int KQS = 256 / RQ;             // k-quad stride between a thread's blocks
+  constexpr int P = 128 + 16;               // LDS row pitch of the codes (bytes)
+  __shared__ __attribute__((aligned(16))) uint8_t codes[TR * P];
+  __shared__ float part[4 * 64];
   const TIn* __restrict__ x = static_cast<const TIn*>(p.x);
   const int RB = (p.R + TR - 1) / TR, KB = (p.K + 127) / 128;
   int blk = blockIdx.x;
@@ -269,79 +272,113 @@ __global__ __launch_bounds__(256) void cast_mn_kernel(QuantTArgs p) {
   blk /= KB;
   const int rb = blk % RB;
   const int g = blk / RB;
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r0 = rb * TR, k0 = kb * 128;
   const TIn* xg = x + g * p.sx_g;
+  const int rq = tid % RQ;  // rows 4 rq .. 4 rq + 3 of the tile
 
-  // phase 1: 128 k-rows of TR values, four consecutive rows per thread
-  constexpr int GROUPS = TR / 4;           // threads per k-row
-  constexpr int KROWS = 256 / GROUPS;      // k-rows per pass
-#pragma unroll 4
-  for (int kk = tid / GROUPS; kk < 128; kk += KROWS) {
-    const int rq = (tid % GROUPS) * 4;
-    const int gk = k0 + kk, gr = r0 + rq;
-    float v[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-    if (gk < p.K) {
-      const TIn* src = xg + (int64_t)gk * p.sx_k + gr;
-      if (p.vec && gr + 3 < p.R) {
-        load4(src, v);
-      } else {
+  // phase 1: NB blocks of 4 k x 4 rows (v[b][kk][j]: k = 4 kq + kk, row 4 rq + j)
+  float v[NB][4][4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-          if (gr + j < p.R) v[j] = load_elem(src + j);
+  for (int b = 0; b < NB; ++b) {
+    const int kq = tid / RQ + KQS * b;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      const int gk = k0 + 4 * kq + kk, gr = r0 + 4 * rq;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) v[b][kk][j] = 0.0f;
+      if (gk < p.K) {
+        const TIn* src = xg + (int64_t)gk * p.sx_k + gr;
+        if (p.vec && gr + 3 < p.R) {
+          load4(src, v[b][kk]);
+        } else {
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            if (gr + j < p.R) v[b][kk][j] = load_elem(src + j);
+        }
       }
     }
+  }
+  // block maxima: per row (per-token) or over the tile (per-block)
+  float m[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-    for (int j = 0; j < 4; ++j) tile[kk * LD + rq + j] = v[j];
+  for (int b = 0; b < NB; ++b)
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) m[j] = fmaxf(m[j], fabsf(v[b][kk][j]));
+  float amax[4];
+  if constexpr (PER_BLOCK) {
+    float t = fmaxf(fmaxf(m[0], m[1]), fmaxf(m[2], m[3]));
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) t = fmaxf(t, __shfl_xor(t, off, 64));
+    if (lane == 0) part[wave] = t;
+    __syncthreads();
+    const float a = fmaxf(fmaxf(part[0], part[1]), fmaxf(part[2], part[3]));
+#pragma unroll
+    for (int j = 0; j < 4; ++j) amax[j] = a;
+  } else {
+    // the 16 threads of row quad rq: lanes rq, rq + 16, rq + 32, rq + 48 of each wave
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      m[j] = fmaxf(m[j], __shfl_xor(m[j], 16, 64));
+      m[j] = fmaxf(m[j], __shfl_xor(m[j], 32, 64));
+    }
+    if (lane < 16) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) part[wave * 64 + 4 * rq + j] = m[j];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int rr = 4 * rq + j;
+      amax[j] = fmaxf(fmaxf(part[rr], part[64 + rr]), fmaxf(part[128 + rr], part[192 + rr]));
+    }
+  }
+  float sc[4];
+  Recip d[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    sc[j] = block_scale(amax[j], p.ue8m0);
+    d[j] = recip_of(sc[j]);
+  }
+  // phase 2: codes of row 4 rq + j at k = 4 kq .. 4 kq + 3 as one word into LDS
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    const int kq = tid / RQ + KQS * b;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float col[4] = {v[b][0][j], v[b][1][j], v[b][2][j], v[b][3][j]};
+      *reinterpret_cast<uint32_t*>(codes + (4 * rq + j) * P + 4 * kq) = encode4(col, d[j]);
+    }
+  }
+  // scales: per row (the thread of k-quad 0 of the row quad), or one per tile
+  if constexpr (PER_BLOCK) {
+    if (tid == 0) p.sf[g * p.ssf_g + (int64_t)rb * p.ssf_r + kb * p.ssf_k] = sc[0];
+  } else {
+    if (tid < RQ) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        if (r0 + 4 * rq + j < p.R) p.sf[g * p.ssf_g + (int64_t)(r0 + 4 * rq + j) * p.ssf_r + kb * p.ssf_k] = sc[j];
+    }
   }
   __syncthreads();
-
-  // phase 2: thread (c, r) holds k = c * KPT .. + KPT - 1 of row r
-  const int r = tid % TR, c = tid / TR;
-  float v[KPT];
-  float m = 0.0f;
+  // phase 3: each row's 128 codes as eight 16-byte pieces
 #pragma unroll
-  for (int i = 0; i < KPT; ++i) {
-    v[i] = tile[(c * KPT + i) * LD + r];
-    m = fmaxf(m, fabsf(v[i]));
-  }
-  float amax;
-  if constexpr (PER_BLOCK) {
+  for (int i = 0; i < TR * 8 / 256; ++i) {
+    const int piece = tid + 256 * i;
+    const int r = piece / 8, kp = (piece % 8) * 16;
+    const int gr = r0 + r, gk = k0 + kp;
+    if (gr >= p.R || gk >= p.K) continue;
+    const i32x4 w = *reinterpret_cast<const i32x4*>(codes + r * P + kp);
+    uint8_t* qd = p.q + g * p.sq_g + (int64_t)gr * p.sq_r + gk;
+    if (p.qvec && gk + 16 <= p.K) {
+      *reinterpret_cast<i32x4*>(qd) = w;
+    } else {
 #pragma unroll
-    for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
-    if ((tid & 63) == 0) part[tid >> 6] = m;
-    __syncthreads();
-    amax = fmaxf(fmaxf(part[0], part[1]), fmaxf(part[2], part[3]));
-  } else {
-    part[c * 64 + r] = m;
-    __syncthreads();
-    amax = fmaxf(fmaxf(part[r], part[64 + r]), fmaxf(part[128 + r], part[192 + r]));
-  }
-  const float s = block_scale(amax, p.ue8m0);
-  const Recip d = recip_of(s);
-  const int gr = r0 + r;
-  if (gr >= p.R) return;
-  uint8_t* qr = p.q + g * p.sq_g + (int64_t)gr * p.sq_r;
-  const int kc = k0 + c * KPT;  // first k of this thread
-  uint32_t w[KPT / 4];
-#pragma unroll
-  for (int i = 0; i < KPT / 4; ++i) {
-    const float t4[4] = {v[4 * i], v[4 * i + 1], v[4 * i + 2], v[4 * i + 3]};
-    w[i] = encode4(t4, d);
-  }
-  if (p.qvec && kc + KPT <= p.K) {
-#pragma unroll
-    for (int i = 0; i < KPT / 16; ++i)
-      *reinterpret_cast<i32x4*>(qr + kc + 16 * i) =
-          i32x4{(int)w[4 * i], (int)w[4 * i + 1], (int)w[4 * i + 2], (int)w[4 * i + 3]};
-  } else {
-#pragma unroll
-    for (int i = 0; i < KPT; ++i)
-      if (kc + i < p.K) qr[kc + i] = (uint8_t)(w[i / 4] >> (8 * (i & 3)));
-  }
-  if (PER_BLOCK ? (tid == 0) : (c == 0)) {
-    const int srow = PER_BLOCK ? rb : gr;
-    p.sf[g * p.ssf_g + (int64_t)srow * p.ssf_r + kb * p.ssf_k] = s;
+      for (int e = 0; e < 16; ++e)
+        if (gk + e < p.K) qd[e] = (uint8_t)((uint32_t)w[e / 4] >> (8 * (e & 3)));
+    }
   }
 }
 
