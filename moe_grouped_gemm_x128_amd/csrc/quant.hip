@@ -43,11 +43,15 @@ __device__ __forceinline__ void load4(const uint16_t* p, float v[4]) {
 // GEMM epilogue that writes FP8 output).
 
 // ---------------------------------------------------------------------------
-// per-token: one half-wave (32 lanes x 4 elements) per 1x128 block, four
-// consecutive blocks of a row per half-wave with all their loads issued
-// before the first reduction (four 16-byte loads in flight per lane)
+// per-token: eight lanes per 1x128 block, 16 elements per lane in four
+// chunks of four that lie 32 elements apart, so that each load instruction
+// reads 128 contiguous bytes (F32) per block.  The block's scale and
+// reciprocal (two correctly rounded divisions, executed by every lane) are
+// spread over 16 elements per lane: the cast is bound by instruction issue,
+// not by HBM, at four elements per lane.
 // ---------------------------------------------------------------------------
-constexpr int TOKEN_BLOCKS = 4;
+constexpr int TOKEN_LANES = 8;     // lanes per block
+constexpr int TOKEN_GROUPS = 256 / TOKEN_LANES;  // blocks per workgroup
 constexpr int SCATTER_K = 8;  // destinations per token held in registers
 
 // SCATTER (MoE dispatch): x is [T, K] (G = 1, R = T) and each token's
@@ -55,19 +59,17 @@ constexpr int SCATTER_K = 8;  // destinations per token held in registers
 template <typename TIn, bool SCATTER = false, class Args = QuantArgs>
 __global__ __launch_bounds__(256) void per_token_kernel(Args p) {
   const TIn* __restrict__ x = static_cast<const TIn*>(p.x);
-  const int lane32 = threadIdx.x & 31;
+  const int sub = threadIdx.x & (TOKEN_LANES - 1);
   const int KB = (p.K + 127) / 128;
-  const int KQ = (KB + TOKEN_BLOCKS - 1) / TOKEN_BLOCKS;  // block groups per row
-  const int64_t total = (int64_t)p.G * p.R * KQ;
-  const int64_t grp = (int64_t)blockIdx.x * 8 + (threadIdx.x >> 5);
-  if (grp >= total) return;  // whole half-waves only; the shuffles below stay within a half
-  const int kq = (int)(grp % KQ);
-  const int64_t rr = grp / KQ;
+  const int64_t total = (int64_t)p.G * p.R * KB;
+  const int64_t grp = (int64_t)blockIdx.x * TOKEN_GROUPS + (threadIdx.x / TOKEN_LANES);
+  if (grp >= total) return;  // whole 8-lane groups only; the shuffles below stay within a group
+  const int kb = (int)(grp % KB);
+  const int64_t rr = grp / KB;
   const int r = (int)(rr % p.R);
   const int g = (int)(rr / p.R);
   const TIn* xr = x + g * p.sx_g + r * p.sx_r;
   uint8_t* qr = p.q + g * p.sq_g + r * p.sq_r;
-  const int kb0 = kq * TOKEN_BLOCKS;
   // SCATTER: the destinations of this token's first SCATTER_K slots, read
   // once (q row offset in bytes, scale row offset in elements; -1: none)
   int64_t dq[SCATTER_K], ds[SCATTER_K];
@@ -89,38 +91,34 @@ __global__ __launch_bounds__(256) void per_token_kernel(Args p) {
     }
   }
 
-  float v[TOKEN_BLOCKS][4];
+  float v[4][4];
 #pragma unroll
-  for (int b = 0; b < TOKEN_BLOCKS; ++b) {
-    const int k0 = (kb0 + b) * 128 + lane32 * 4;
+  for (int c = 0; c < 4; ++c) {
+    const int k0 = kb * 128 + c * 32 + sub * 4;
     if (k0 + 3 < p.K) {
-      load4(xr + k0, v[b]);
+      load4(xr + k0, v[c]);
     } else {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) v[b][j] = (k0 + j < p.K) ? load_elem(xr + k0 + j) : 0.0f;
+      for (int j = 0; j < 4; ++j) v[c][j] = (k0 + j < p.K) ? load_elem(xr + k0 + j) : 0.0f;
     }
   }
-  float amax[TOKEN_BLOCKS];
+  float amax = 0.0f;
 #pragma unroll
-  for (int b = 0; b < TOKEN_BLOCKS; ++b)
-    amax[b] = fmaxf(fmaxf(fabsf(v[b][0]), fabsf(v[b][1])), fmaxf(fabsf(v[b][2]), fabsf(v[b][3])));
+  for (int c = 0; c < 4; ++c)
+    amax = fmaxf(amax, fmaxf(fmaxf(fabsf(v[c][0]), fabsf(v[c][1])), fmaxf(fabsf(v[c][2]), fabsf(v[c][3]))));
 #pragma unroll
-  for (int off = 16; off > 0; off >>= 1)
-#pragma unroll
-    for (int b = 0; b < TOKEN_BLOCKS; ++b) amax[b] = fmaxf(amax[b], __shfl_xor(amax[b], off, 32));
+  for (int off = TOKEN_LANES / 2; off > 0; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, TOKEN_LANES));
+  const float s = block_scale(amax, p.ue8m0);
+  const Recip d = recip_of(s);
 
 #pragma unroll
-  for (int b = 0; b < TOKEN_BLOCKS; ++b) {
-    const int kb = kb0 + b;
-    if (kb >= KB) break;
-    const float s = block_scale(amax[b], p.ue8m0);
-    const Recip d = recip_of(s);
-    const int k0 = kb * 128 + lane32 * 4;
+  for (int c = 0; c < 4; ++c) {
+    const int k0 = kb * 128 + c * 32 + sub * 4;
     if constexpr (SCATTER) {
       // cast once (elements past K are zeros and their bytes are not stored),
       // store to each destination row
-      const uint32_t w = encode4(v[b], d);
-      auto put = [&](int64_t oq, int64_t os) {
+      const uint32_t w = encode4(v[c], d);
+      auto put = [&](int64_t oq) {
         uint8_t* qd = p.q + oq;
         if (k0 + 3 < p.K) {
           *reinterpret_cast<uint32_t*>(qd + k0) = w;
@@ -128,25 +126,38 @@ __global__ __launch_bounds__(256) void per_token_kernel(Args p) {
           for (int i = 0; i < 4; ++i)
             if (k0 + i < p.K) qd[k0 + i] = (uint8_t)(w >> (8 * i));
         }
-        if (lane32 == 0) p.sf[os + kb * p.ssf_k] = s;
       };
 #pragma unroll
       for (int j = 0; j < SCATTER_K; ++j)
-        if (dq[j] >= 0) put(dq[j], ds[j]);
+        if (dq[j] >= 0) put(dq[j]);
       for (int j = SCATTER_K; j < p.k; ++j) {  // more choices per token than SCATTER_K
         const int32_t sl = p.slot[(int64_t)r * p.k + j];
         if (sl < 0 || sl >= p.rows) continue;  // routed nowhere or dropped
         const int e = sl / p.max_m, row = sl % p.max_m;
-        put(e * p.sq_g + row * p.sq_r, e * p.ssf_g + row * p.ssf_r);
+        put(e * p.sq_g + row * p.sq_r);
       }
     } else {
       if (k0 + 3 < p.K) {
-        *reinterpret_cast<uint32_t*>(qr + k0) = encode4(v[b], d);
+        *reinterpret_cast<uint32_t*>(qr + k0) = encode4(v[c], d);
       } else {
         for (int j = 0; j < 4; ++j)
-          if (k0 + j < p.K) qr[k0 + j] = (uint8_t)encode1(v[b][j], d);
+          if (k0 + j < p.K) qr[k0 + j] = (uint8_t)encode1(v[c][j], d);
       }
-      if (lane32 == 0) p.sf[g * p.ssf_g + r * p.ssf_r + kb * p.ssf_k] = s;
+    }
+  }
+  if (sub == 0) {
+    if constexpr (SCATTER) {
+#pragma unroll
+      for (int j = 0; j < SCATTER_K; ++j)
+        if (ds[j] >= 0) p.sf[ds[j] + kb * p.ssf_k] = s;
+      for (int j = SCATTER_K; j < p.k; ++j) {
+        const int32_t sl = p.slot[(int64_t)r * p.k + j];
+        if (sl < 0 || sl >= p.rows) continue;
+        const int e = sl / p.max_m, row = sl % p.max_m;
+        p.sf[e * p.ssf_g + row * p.ssf_r + kb * p.ssf_k] = s;
+      }
+    } else {
+      p.sf[g * p.ssf_g + r * p.ssf_r + kb * p.ssf_k] = s;
     }
   }
 }
@@ -401,8 +412,7 @@ hipError_t launch_cast_mn(const QuantTArgs& p, bool per_block, hipStream_t strea
 
 hipError_t launch_per_token(const QuantArgs& p, hipStream_t stream) {
   const int64_t KB = (p.K + 127) / 128;
-  const int64_t KQ = (KB + TOKEN_BLOCKS - 1) / TOKEN_BLOCKS;
-  const int64_t blocks = ((int64_t)p.G * p.R * KQ + 7) / 8;
+  const int64_t blocks = ((int64_t)p.G * p.R * KB + TOKEN_GROUPS - 1) / TOKEN_GROUPS;
   if (blocks == 0) return hipSuccess;
   if (p.x_bf16)
     per_token_kernel<uint16_t><<<dim3((unsigned)blocks), dim3(256), 0, stream>>>(p);
@@ -413,8 +423,7 @@ hipError_t launch_per_token(const QuantArgs& p, hipStream_t stream) {
 
 hipError_t launch_per_token_scatter(const QuantScatterArgs& p, hipStream_t stream) {
   const int64_t KB = (p.K + 127) / 128;
-  const int64_t KQ = (KB + TOKEN_BLOCKS - 1) / TOKEN_BLOCKS;
-  const int64_t blocks = ((int64_t)p.G * p.R * KQ + 7) / 8;
+  const int64_t blocks = ((int64_t)p.G * p.R * KB + TOKEN_GROUPS - 1) / TOKEN_GROUPS;
   if (blocks == 0) return hipSuccess;
   if (p.x_bf16)
     per_token_kernel<uint16_t, true, QuantScatterArgs><<<dim3((unsigned)blocks), dim3(256), 0, stream>>>(p);
