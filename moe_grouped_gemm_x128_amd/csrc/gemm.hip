@@ -963,8 +963,9 @@ using TileW = TileShape<128, 256, 2, 4, 3>;  // 512 threads, wave tile  64 x 64,
 using TileS = TileShape<128, 128, 2, 2, 3>;  // 256 threads, wave tile  64 x 64, 3 x 32 KB stages
 using TileT = TileShape<256, 128, 4, 2, 3>;  // 512 threads, wave tile  64 x 64, 3 x 48 KB stages
 using TileN = TileShape<256, 192, 2, 4, 2>;  // 512 threads, wave tile 128 x 48, 2 x 56 KB stages
+using TileQ = TileShape<192, 192, 2, 4, 2>;  // 512 threads, wave tile  96 x 48, 2 x 48 KB stages (dense FP8)
 
-enum Variant : int { VAR_L = 0, VAR_W = 1, VAR_S = 2, VAR_T = 3, VAR_N = 4 };
+enum Variant : int { VAR_L = 0, VAR_W = 1, VAR_S = 2, VAR_T = 3, VAR_N = 4, VAR_Q = 5 };
 
 // Launch one tile configuration.  ROWB: whether the per-row B scale kernels
 // exist for this tile (they need a thread per tile row of A and of B and the
@@ -1022,6 +1023,27 @@ hipError_t launch_tile_fp8_out(const GemmParams& p, int sf_fmt, int64_t grid, hi
   return hipGetLastError();
 }
 
+// Launch the 192 x 192 tile: the dense FP8 GEMM only (block scales, FP32 or
+// UE8M0; BF16 or FP32 output).  Its 192-row tiles do not align with the
+// 128-row blocks of the grouped layouts.
+template <int KIND>
+hipError_t launch_tile_q(const GemmParams& p, int mode, int sf_fmt, int64_t grid, hipStream_t stream) {
+  if constexpr (KIND == KIND_FP8) {
+    if (mode != MODE_DENSE || (sf_fmt != SF_F32 && sf_fmt != SF_UE8M0)) return hipErrorInvalidValue;
+    const dim3 g((unsigned)grid), b(TileQ::NT);
+    if (p.d_f32) {
+      if (sf_fmt == SF_F32) gemm_kernel<TileQ, KIND_FP8, SF_F32, MODE_DENSE, OUT_F32><<<g, b, 0, stream>>>(p);
+      else gemm_kernel<TileQ, KIND_FP8, SF_UE8M0, MODE_DENSE, OUT_F32><<<g, b, 0, stream>>>(p);
+    } else {
+      if (sf_fmt == SF_F32) gemm_kernel<TileQ, KIND_FP8, SF_F32, MODE_DENSE><<<g, b, 0, stream>>>(p);
+      else gemm_kernel<TileQ, KIND_FP8, SF_UE8M0, MODE_DENSE><<<g, b, 0, stream>>>(p);
+    }
+    return hipGetLastError();
+  } else {
+    return hipErrorInvalidValue;
+  }
+}
+
 template <class T, int KIND>
 TileCfg make_cfg(int variant) {
   TileCfg c;
@@ -1041,6 +1063,7 @@ hipError_t launch_variant(const TileCfg& cfg, const GemmParams& p, int mode, int
     case VAR_W: return launch_tile<TileW, KIND, true>(p, mode, sf_fmt, grid, stream);
     case VAR_T: return launch_tile<TileT, KIND, false>(p, mode, sf_fmt, grid, stream);
     case VAR_N: return launch_tile<TileN, KIND, true>(p, mode, sf_fmt, grid, stream);
+    case VAR_Q: return launch_tile_q<KIND>(p, mode, sf_fmt, grid, stream);
     default: return launch_tile<TileS, KIND, true>(p, mode, sf_fmt, grid, stream);
   }
 }
@@ -1058,6 +1081,9 @@ hipError_t launch_variant(const TileCfg& cfg, const GemmParams& p, int mode, int
 // rounds(tiles) * (KB * slice + 7).  E.g. M = 4096: N = 2112, K = 7168 goes
 // to 176 tiles of 256 x 192 (63 -> 56.3); BF16 N = 7168, K = 16384 (256
 // slices) splits at 4096 (526 -> 501); N = 7168, K = 2048 stays on 256 x 256.
+// The dense FP8 GEMM may also take 192 x 192 tiles (slice 0.75 from the same
+// stamps-and-timing fit: 4096 x 2112 x 7168 on 242 tiles of 192 x 192 took
+// 70.3 us against 80.9 us on 176 of 256 x 192, builds alternated).
 // Only the BF16 kind splits: the FP8 kernel runs at the power limit, and in
 // a partly idle last round its busy CUs clock higher (2.03 GHz with 176 of
 // 256 busy, 1.86 with all), which recovers what the second launch would
@@ -1069,7 +1095,7 @@ constexpr int NUM_CU = 256;
 template <int KIND>
 GemmPlan plan_large(int mode, int64_t G, int64_t M, int64_t N, int64_t KB) {
   const int64_t units = (mode == MODE_MASKED ? G : 1) * ((M + 255) / 256);
-  const double slice_n = 0.88, per_round = 7.0, per_launch = 5.7;
+  const double slice_n = 0.88, slice_q = 0.75, per_round = 7.0, per_launch = 5.7;
   auto cost = [&](int64_t cols, int64_t bn, double slice) {
     const int64_t rounds = (units * ((cols + bn - 1) / bn) + NUM_CU - 1) / NUM_CU;
     return (double)rounds * ((double)KB * slice + per_round);
@@ -1083,6 +1109,15 @@ GemmPlan plan_large(int mode, int64_t G, int64_t M, int64_t N, int64_t KB) {
   if (only_n < best_cost) {
     best_cost = only_n;
     best.cfg[0] = make_cfg<TileN, KIND>(VAR_N);
+  }
+  if (KIND == KIND_FP8 && mode == MODE_DENSE) {
+    // 192 x 192 tiles: (M/192) (N/192) of them, a slice at 0.75 of a 256 x 256 one
+    const int64_t rounds = ((M + 191) / 192 * ((N + 191) / 192) + NUM_CU - 1) / NUM_CU;
+    const double only_q = (double)rounds * ((double)KB * slice_q + per_round);
+    if (only_q < best_cost) {
+      best_cost = only_q;
+      best.cfg[0] = make_cfg<TileQ, KIND>(VAR_Q);
+    }
   }
   for (int64_t n1 = 256; KIND == KIND_BF16 && n1 < N; n1 += 256) {
     const double c = cost(n1, 256, 1.0) + cost(N - n1, 192, slice_n) + per_launch;

@@ -113,24 +113,27 @@ def test_fp8_out_plan(lib, M, N, tile):
 
 
 @pytest.mark.parametrize("N,K,fp8_plan,bf16_plan", [
-    # 144 tiles of 256 x 256 fill 56% of one round: 176 of 256 x 192
-    (2112, 7168, (192, 2112, 0), (192, 2112, 0)),
-    (24576, 1536, (256, 24576, 0), (256, 24576, 0)),    # 6 whole rounds
+    # 144 tiles of 256 x 256 fill 56% of one round: FP8 242 of 192 x 192,
+    # BF16 176 of 256 x 192
+    (2112, 7168, (192, 192, 2112, 0), (256, 192, 2112, 0)),
+    (24576, 1536, (256, 256, 24576, 0), (256, 256, 24576, 0)),    # 6 whole rounds
     # 1.75 rounds: BF16 splits into 256 tiles of 256 x 256, then 256 of
     # 256 x 192; the FP8 kernel gains nothing from it (power-limited clock)
-    (7168, 16384, (256, 7168, 0), (256, 4096, 192)),
-    (4096, 7168, (256, 4096, 0), (256, 4096, 0)),        # one whole round
-    (7168, 2048, (256, 7168, 0), (256, 7168, 0)),        # too few K-slices to pay for a second launch
+    (7168, 16384, (256, 256, 7168, 0), (256, 256, 4096, 192)),
+    (4096, 7168, (256, 256, 4096, 0), (256, 256, 4096, 0)),        # one whole round
+    (7168, 2048, (256, 256, 7168, 0), (256, 256, 7168, 0)),        # too few K-slices to pay for a second launch
+    (2880, 256, (256, 192, 2880, 0), (256, 192, 2880, 0)),         # 240 tiles of 256 x 192: one round
 ])
 def test_launch_plan_of_the_dense_v3_shapes(lib, N, K, fp8_plan, bf16_plan):
     """The launch plan fills whole rounds of one workgroup per compute unit
-    (256): one launch of the 256 x 256 or of the 256 x 192 tile, or (BF16)
-    columns [0, n_split) on the first and [n_split, N) on the second."""
+    (256): one launch of the 256 x 256, 256 x 192 or (dense FP8) 192 x 192
+    tile, or (BF16) columns [0, n_split) on the first and [n_split, N) on the
+    second."""
     for kind, plan in ((binding.DG_KIND_DENSE, fp8_plan), (binding.DG_KIND_BF16_DENSE, bf16_plan)):
-        block_n, n_split, block_n2 = plan
+        block_m, block_n, n_split, block_n2 = plan
         c = binding.query_config(kind, 1, 4096, N, K)
-        assert (c["block_m"], c["block_n"], c["n_split"], c["block_n2"]) == (256, block_n, n_split, block_n2)
-        assert c["grid"] == 16 * -(-n_split // block_n)
+        assert (c["block_m"], c["block_n"], c["n_split"], c["block_n2"]) == (block_m, block_n, n_split, block_n2)
+        assert c["grid"] == -(-4096 // block_m) * -(-n_split // block_n)
         assert c["grid2"] == (16 * -(-(N - n_split) // block_n2) if block_n2 else 0)
         assert c["lds_bytes"] <= 160 * 1024 and c["lds_bytes2"] <= 160 * 1024
 

@@ -57,9 +57,12 @@ def sentinel_like(shape):
 # ---------------------------------------------------------------------------
 
 # Shapes of every launch plan of the FP8 GEMM, with ragged M and N: rows
-# <= 128 (128-row tiles), one launch of the 256 x 192 tile (below one round
-# of tiles) and one whole round of 256 x 256 tiles (4000 x 4000).
+# <= 128 (128-row tiles), one round of 192 x 192 tiles (problems below one
+# round of the larger tiles), one round of 256 x 192 tiles (4096 x 2880: 240
+# tiles, where 192 x 192 would take two rounds) and one whole round of
+# 256 x 256 tiles (4000 x 4000).
 PLAN_L = (4000, 4000, 256)
+PLAN_N = (4096, 2880, 256)
 
 
 def _expect_plan(kind, M, N, K):
@@ -68,13 +71,15 @@ def _expect_plan(kind, M, N, K):
     c = binding.query_config(getattr(binding, kind), 1, M, N, K)
     if (M, N) == PLAN_L[:2]:
         assert (c["block_m"], c["block_n"], c["block_n2"]) == (256, 256, 0)
-    elif M > 128:
+    elif (M, N) == PLAN_N[:2]:
         assert (c["block_m"], c["block_n"], c["block_n2"]) == (256, 192, 0)
+    elif M > 128:
+        assert (c["block_m"], c["block_n"], c["block_n2"]) == (192, 192, 0)
     return c
 
 
 @pytest.mark.parametrize("M,N,K", [(128, 256, 512), (200, 300, 384), (1, 130, 128), (257, 64, 256), (64, 2112, 1024),
-                                   (96, 100, 640), (128, 128, 384), PLAN_L])
+                                   (96, 100, 640), (128, 128, 384), (1000, 700, 512), PLAN_N, PLAN_L])
 def test_dense_full_compare(M, N, K):
     say(f"fp8_gemm_nt M={M} N={N} K={K}")
     mg = _mg()
