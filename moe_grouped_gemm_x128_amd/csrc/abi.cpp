@@ -705,6 +705,7 @@ int moe_dispatch_masked_fp8(const dg_tensor* x, const dg_tensor* topk_idx, const
   q.max_m = (int32_t)max_m;
   q.rows = (int32_t)(G * max_m);
   q.flat = (q.sq_g == max_m * q.sq_r && q.ssf_g == max_m * q.ssf_r) ? 1 : 0;
+  q.qvec = (aligned(a->data, 16) && q.sq_r % 16 == 0 && q.sq_g % 16 == 0) ? 1 : 0;
   return check_launch(dgmi::launch_per_token_scatter(q, stream), fname);
 }
 
@@ -796,6 +797,7 @@ int moe_dispatch_contiguous_fp8(const dg_tensor* x, const dg_tensor* topk_idx, c
   q.max_m = (int32_t)Mcap;
   q.rows = (int32_t)Mcap;
   q.flat = 1;  // a slot is a row of a and sfa
+  q.qvec = (aligned(a->data, 16) && q.sq_r % 16 == 0) ? 1 : 0;
   return check_launch(dgmi::launch_per_token_scatter(q, stream), fname);
 }
 

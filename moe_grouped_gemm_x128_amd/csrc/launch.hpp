@@ -39,6 +39,7 @@ struct QuantScatterArgs : QuantArgs {
   const int32_t* slot;
   int32_t k, max_m, rows;
   int32_t flat;  // sq_g == max_m * sq_r and ssf_g == max_m * ssf_r
+  int32_t qvec;  // q, sq_r and sq_g are multiples of 16 bytes
 };
 
 // MoE routing into the masked layout (moe.hip): topk [T, k] contiguous,

@@ -56,6 +56,14 @@ constexpr int SCATTER_K = 8;  // destinations per token held in registers
 
 // SCATTER (MoE dispatch): x is [T, K] (G = 1, R = T) and each token's
 // codes and scales go to every row its slots name instead of row r of q.
+// Its stores outnumber its loads (one per destination), so there each lane
+// holds 16 consecutive elements: its codes leave as one 16-byte store per
+// destination and a block's eight lanes write 128 contiguous bytes.
+template <bool SCATTER>
+__device__ __forceinline__ int chunk_offset(int c, int sub) {
+  return SCATTER ? sub * 16 + c * 4 : c * 32 + sub * 4;
+}
+
 template <typename TIn, bool SCATTER = false, class Args = QuantArgs>
 __global__ __launch_bounds__(256) void per_token_kernel(Args p) {
   const TIn* __restrict__ x = static_cast<const TIn*>(p.x);
@@ -94,7 +102,7 @@ __global__ __launch_bounds__(256) void per_token_kernel(Args p) {
   float v[4][4];
 #pragma unroll
   for (int c = 0; c < 4; ++c) {
-    const int k0 = kb * 128 + c * 32 + sub * 4;
+    const int k0 = kb * 128 + chunk_offset<SCATTER>(c, sub);
     if (k0 + 3 < p.K) {
       load4(xr + k0, v[c]);
     } else {
@@ -111,32 +119,36 @@ __global__ __launch_bounds__(256) void per_token_kernel(Args p) {
   const float s = block_scale(amax, p.ue8m0);
   const Recip d = recip_of(s);
 
+  if constexpr (SCATTER) {
+    // cast once (elements past K are zeros and their bytes are not stored),
+    // store to each destination row
+    const int k0 = kb * 128 + sub * 16;
+    uint32_t w[4];
 #pragma unroll
-  for (int c = 0; c < 4; ++c) {
-    const int k0 = kb * 128 + c * 32 + sub * 4;
-    if constexpr (SCATTER) {
-      // cast once (elements past K are zeros and their bytes are not stored),
-      // store to each destination row
-      const uint32_t w = encode4(v[c], d);
-      auto put = [&](int64_t oq) {
-        uint8_t* qd = p.q + oq;
-        if (k0 + 3 < p.K) {
-          *reinterpret_cast<uint32_t*>(qd + k0) = w;
-        } else {
-          for (int i = 0; i < 4; ++i)
-            if (k0 + i < p.K) qd[k0 + i] = (uint8_t)(w >> (8 * i));
-        }
-      };
-#pragma unroll
-      for (int j = 0; j < SCATTER_K; ++j)
-        if (dq[j] >= 0) put(dq[j]);
-      for (int j = SCATTER_K; j < p.k; ++j) {  // more choices per token than SCATTER_K
-        const int32_t sl = p.slot[(int64_t)r * p.k + j];
-        if (sl < 0 || sl >= p.rows) continue;  // routed nowhere or dropped
-        const int e = sl / p.max_m, row = sl % p.max_m;
-        put(e * p.sq_g + row * p.sq_r);
+    for (int c = 0; c < 4; ++c) w[c] = encode4(v[c], d);
+    const bool whole = p.qvec && k0 + 15 < p.K;
+    auto put = [&](int64_t oq) {
+      uint8_t* qd = p.q + oq + k0;
+      if (whole) {
+        *reinterpret_cast<i32x4*>(qd) = i32x4{(int)w[0], (int)w[1], (int)w[2], (int)w[3]};
+      } else {
+        for (int i = 0; i < 16; ++i)
+          if (k0 + i < p.K) qd[i] = (uint8_t)(w[i / 4] >> (8 * (i % 4)));
       }
-    } else {
+    };
+#pragma unroll
+    for (int j = 0; j < SCATTER_K; ++j)
+      if (dq[j] >= 0) put(dq[j]);
+    for (int j = SCATTER_K; j < p.k; ++j) {  // more choices per token than SCATTER_K
+      const int32_t sl = p.slot[(int64_t)r * p.k + j];
+      if (sl < 0 || sl >= p.rows) continue;  // routed nowhere or dropped
+      const int e = sl / p.max_m, row = sl % p.max_m;
+      put(e * p.sq_g + row * p.sq_r);
+    }
+  } else {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int k0 = kb * 128 + c * 32 + sub * 4;
       if (k0 + 3 < p.K) {
         *reinterpret_cast<uint32_t*>(qr + k0) = encode4(v[c], d);
       } else {

@@ -58,6 +58,7 @@ def _check_dispatch(x, topk, G, max_m, ue8m0, outs, what):
     (50, 4, 5, 64, 200, 0.0, False, True),        # partial last K-block, UE8M0 scales
     (1, 1, 1, 1, 128, 0.0, True, True),
     (4097, 2, 3, 2048, 256, 0.0, False, False),   # several routing passes, capacity reached (about 2731)
+    (64, 10, 12, 64, 272, 0.05, True, False),      # more choices per token than destinations held in registers
 ])
 def test_dispatch_matches_oracle(T, k, G, max_m, K, p_none, x_bf16, ue8m0):
     say(f"moe_dispatch_masked_fp8 T={T} k={k} G={G} max_m={max_m} K={K} bf16={x_bf16} ue8m0={ue8m0}")
