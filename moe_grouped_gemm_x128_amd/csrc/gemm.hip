@@ -963,7 +963,7 @@ using TileW = TileShape<128, 256, 2, 4, 3>;  // 512 threads, wave tile  64 x 64,
 using TileS = TileShape<128, 128, 2, 2, 3>;  // 256 threads, wave tile  64 x 64, 3 x 32 KB stages
 using TileT = TileShape<256, 128, 4, 2, 3>;  // 512 threads, wave tile  64 x 64, 3 x 48 KB stages
 using TileN = TileShape<256, 192, 2, 4, 2>;  // 512 threads, wave tile 128 x 48, 2 x 56 KB stages
-using TileQ = TileShape<192, 192, 2, 4, 2>;  // 512 threads, wave tile  96 x 48, 2 x 48 KB stages (dense FP8)
+using TileQ = TileShape<192, 192, 2, 4, 2>;  // 512 threads, wave tile  96 x 48, 2 x 48 KB stages (dense only)
 
 enum Variant : int { VAR_L = 0, VAR_W = 1, VAR_S = 2, VAR_T = 3, VAR_N = 4, VAR_Q = 5 };
 
@@ -1023,9 +1023,9 @@ hipError_t launch_tile_fp8_out(const GemmParams& p, int sf_fmt, int64_t grid, hi
   return hipGetLastError();
 }
 
-// Launch the 192 x 192 tile: the dense FP8 GEMM only (block scales, FP32 or
-// UE8M0; BF16 or FP32 output).  Its 192-row tiles do not align with the
-// 128-row blocks of the grouped layouts.
+// Launch the 192 x 192 tile: the dense GEMMs only (FP8 with block scales,
+// FP32 or UE8M0, or BF16; BF16 or FP32 output).  Its 192-row tiles do not
+// align with the 128-row blocks of the grouped layouts.
 template <int KIND>
 hipError_t launch_tile_q(const GemmParams& p, int mode, int sf_fmt, int64_t grid, hipStream_t stream) {
   if constexpr (KIND == KIND_FP8) {
@@ -1040,7 +1040,11 @@ hipError_t launch_tile_q(const GemmParams& p, int mode, int sf_fmt, int64_t grid
     }
     return hipGetLastError();
   } else {
-    return hipErrorInvalidValue;
+    if (mode != MODE_DENSE) return hipErrorInvalidValue;
+    const dim3 g((unsigned)grid), b(TileQ::NT);
+    if (p.d_f32) gemm_kernel<TileQ, KIND_BF16, SF_F32, MODE_DENSE, OUT_F32><<<g, b, 0, stream>>>(p);
+    else gemm_kernel<TileQ, KIND_BF16, SF_F32, MODE_DENSE><<<g, b, 0, stream>>>(p);
+    return hipGetLastError();
   }
 }
 
@@ -1110,7 +1114,7 @@ GemmPlan plan_large(int mode, int64_t G, int64_t M, int64_t N, int64_t KB) {
     best_cost = only_n;
     best.cfg[0] = make_cfg<TileN, KIND>(VAR_N);
   }
-  if (KIND == KIND_FP8 && mode == MODE_DENSE) {
+  if (mode == MODE_DENSE) {
     // 192 x 192 tiles: (M/192) (N/192) of them, a slice at 0.75 of a 256 x 256 one
     const int64_t rounds = ((M + 191) / 192 * ((N + 191) / 192) + NUM_CU - 1) / NUM_CU;
     const double only_q = (double)rounds * ((double)KB * slice_q + per_round);
