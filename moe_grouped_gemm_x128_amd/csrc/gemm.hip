@@ -1029,9 +1029,15 @@ hipError_t launch_tile_fp8_out(const GemmParams& p, int sf_fmt, int64_t grid, hi
 template <int KIND>
 hipError_t launch_tile_q(const GemmParams& p, int mode, int sf_fmt, int64_t grid, hipStream_t stream) {
   if constexpr (KIND == KIND_FP8) {
-    if (mode != MODE_DENSE || (sf_fmt != SF_F32 && sf_fmt != SF_UE8M0)) return hipErrorInvalidValue;
+    if (mode != MODE_DENSE) return hipErrorInvalidValue;
     const dim3 g((unsigned)grid), b(TileQ::NT);
-    if (p.d_f32) {
+    if (sf_fmt == (SF_F32 | SF_ROWB) && !p.d_f32) {
+      gemm_kernel<TileQ, KIND_FP8, SF_F32 | SF_ROWB, MODE_DENSE><<<g, b, 0, stream>>>(p);
+    } else if (sf_fmt == (SF_UE8M0 | SF_ROWB) && !p.d_f32) {
+      gemm_kernel<TileQ, KIND_FP8, SF_UE8M0 | SF_ROWB, MODE_DENSE><<<g, b, 0, stream>>>(p);
+    } else if (sf_fmt != SF_F32 && sf_fmt != SF_UE8M0) {
+      return hipErrorInvalidValue;
+    } else if (p.d_f32) {
       if (sf_fmt == SF_F32) gemm_kernel<TileQ, KIND_FP8, SF_F32, MODE_DENSE, OUT_F32><<<g, b, 0, stream>>>(p);
       else gemm_kernel<TileQ, KIND_FP8, SF_UE8M0, MODE_DENSE, OUT_F32><<<g, b, 0, stream>>>(p);
     } else {
@@ -1179,6 +1185,13 @@ GemmPlan fp8_gemm_plan(int mode, int64_t G, int64_t M, int64_t N, int64_t K, int
     p.parts = 1;
     p.n_split = N;
     p.cfg[0] = make_cfg<TileN, KIND_FP8>(VAR_N);
+    if (mode == MODE_DENSE) {  // or 192 x 192 tiles where one round of them costs less (plan_large)
+      const int64_t KB = (K + 127) / 128;
+      const int64_t rq = ((M + 191) / 192 * ((N + 191) / 192) + NUM_CU - 1) / NUM_CU;
+      const int64_t rn = ((M + 255) / 256 * ((N + 191) / 192) + NUM_CU - 1) / NUM_CU;
+      if ((double)rq * ((double)KB * 0.75 + 7.0) < (double)rn * ((double)KB * 0.88 + 7.0))
+        p.cfg[0] = make_cfg<TileQ, KIND_FP8>(VAR_Q);
+    }
     return p;
   }
   if (M <= 128) {
