@@ -28,7 +28,11 @@ Readings where the pages are silent (each listed in the design notes):
   * A partial last block (K % 128 != 0 or rows % 128 != 0) uses the
     elements that exist.
 
-Pins: tests/test_oracle_quant.py and tests/test_oracle_pack.py.
+Pins: tests/test_oracle_quant.py (including an exact pin of the scale and
+quotient rule: every scale equals RN32(max(amax, 1e-4) / 448) and every
+code e4m3(RN32(x / s)), both quotients computed with integer arithmetic on
+the binary32 inputs, on 10^4+ blocks of FP32 and BF16-valued sources) and
+tests/test_oracle_pack.py.
 """
 
 import numpy as np

@@ -71,3 +71,66 @@ def assert_bf16_close(got_bits, ref, what=""):
         idx = np.argwhere(bad)[:5]
         details = ", ".join(f"{tuple(i)}: got {got[tuple(i)]:.6g} ref {ref[tuple(i)]:.6g}" for i in idx)
         raise AssertionError(f"{what}: {int(bad.sum())} elements outside tolerance (rms {rms:.4g}); {details}")
+
+
+# ---------------------------------------------------------------------------
+# Exact binary32 rounding (host-side pins; no numpy float32 arithmetic)
+# ---------------------------------------------------------------------------
+
+def rn32(v):
+    """Round a rational (fractions.Fraction) to the nearest binary32 value,
+    ties to even, with binary32's subnormal range; returns a Fraction."""
+    from fractions import Fraction as F
+
+    if v == 0:
+        return F(0)
+    sgn = -1 if v < 0 else 1
+    a = abs(v)
+    e = a.numerator.bit_length() - a.denominator.bit_length()
+    if F(2) ** e > a:
+        e -= 1
+    while F(2) ** (e + 1) <= a:
+        e += 1
+    e = max(e, -126)
+    unit = F(2) ** (e - 23)
+    m = a / unit
+    fl = m.numerator // m.denominator
+    rem = m - fl
+    if rem > F(1, 2) or (rem == F(1, 2) and fl % 2 == 1):
+        fl += 1
+    return sgn * fl * unit
+
+
+def _mant_exp(v):
+    """|v| = m * 2^e with m a non-negative integer (v a finite Python float)."""
+    import math
+
+    f, e = math.frexp(abs(v))
+    return int(f * (1 << 53)), e - 53
+
+
+def rn32_quot(x, y):
+    """The correctly rounded binary32 quotient RN(x / y) of two finite
+    binary32 values (y != 0), ties to even, computed with integer arithmetic
+    only; returned as a Python float (which holds every binary32 exactly).
+    The sign of a zero result is the sign of the exact quotient."""
+    import math
+
+    neg = (math.copysign(1.0, x) < 0) != (y < 0)
+    if x == 0:
+        return -0.0 if neg else 0.0
+    mx, ex = _mant_exp(x)
+    my, ey = _mant_exp(y)
+    P = 64
+    q, r = divmod(mx << P, my)  # |x / y| = (q + r / my) * 2^(ex - ey - P), q >= 2^63
+    base = ex - ey - P
+    e_top = q.bit_length() - 1 + base  # floor(log2 |x / y|)
+    e_eff = max(e_top, -126)
+    drop = (e_eff - 23) - base  # bits of q below the binary32 unit in the last place (> 0)
+    kept = q >> drop
+    rem = q - (kept << drop)
+    half = 1 << (drop - 1)
+    if rem > half or (rem == half and (r != 0 or kept & 1)):
+        kept += 1
+    val = math.ldexp(kept, e_eff - 23)
+    return -val if neg else val

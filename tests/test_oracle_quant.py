@@ -144,3 +144,155 @@ def test_ue8m0_scale_of_exact_power_of_two_is_kept():
     x[0, 5] = np.nextafter(np.float32(56.0), np.float32(100.0))
     _, sf = oracle.per_token_cast_to_fp8(x, use_ue8m0=True)
     assert sf[0, 0] == np.float32(0.25)
+
+
+# ---------------------------------------------------------------------------
+# Exact pin of the scale and quotient rule (reading of "FP32 amax/448 scales",
+# "DeepInside DeepGEMM", section 4: FP32 scale factors per 128-wide K-block):
+#   s = RN32(max(amax, 1e-4) / 448), q = e4m3(RN32(x / s)),
+# each quotient the correctly rounded binary32 one.  The expected values come
+# from integer arithmetic on the binary32 inputs (helpers.rn32_quot), never
+# from numpy's float32 division, so a scale taken as amax * RN(1/448) or a
+# quotient taken as x * RN(1/s) fails here.
+# ---------------------------------------------------------------------------
+
+from helpers import rn32_quot  # noqa: E402
+
+FLOOR = float(np.float32(1e-4))
+
+
+def _exact_scale(amax, ue8m0):
+    import math
+
+    s = rn32_quot(max(float(amax), FLOOR), 448.0)
+    if ue8m0:
+        f, e = math.frexp(s)
+        s = s if f == 0.5 else math.ldexp(1.0, e)
+    return s
+
+
+def _exact_codes(vals, s):
+    t = np.array([rn32_quot(float(v), s) for v in vals], dtype=np.float64)
+    return oracle.e4m3_encode(t)
+
+
+def _varied_rows(seed, rows, K, bf16):
+    """N(0,1) rows whose 1x128 blocks span many binades (some below the
+    amax floor, some all zero), optionally rounded to bfloat16 values."""
+    rng = np.random.default_rng(seed)
+    x = synth.normal_f32(seed, (rows, K))
+    mag = np.exp2(rng.integers(-30, 12, size=(rows, K // 128))).astype(np.float32)
+    x = (x.reshape(rows, K // 128, 128) * mag[..., None]).reshape(rows, K)
+    x[0, :128] = 0.0
+    x[1, 128:256] = 0.0
+    x[1, 200] = -3.0  # amax 3: RN(3/448) differs from 3 * RN(1/448)
+    if bf16:
+        x = (x.view(np.uint32) & np.uint32(0xFFFF0000)).view(np.float32)
+    return x
+
+
+def _per_token_mismatches(x, q, sf, ue8m0, code_rows=None):
+    R, K = x.shape
+    bad_s = bad_q = 0
+    for r in range(R):
+        for kb in range(K // 128):
+            blk = x[r, kb * 128:(kb + 1) * 128]
+            s = _exact_scale(np.abs(blk).max(), ue8m0)
+            bad_s += int(float(sf[r, kb]) != s)
+            if code_rows is None or r in code_rows:
+                bad_q += int(np.count_nonzero(_exact_codes(blk, s) != q[r, kb * 128:(kb + 1) * 128]))
+    return bad_s, bad_q
+
+
+@pytest.mark.parametrize("bf16", [False, True])
+def test_per_token_scale_and_codes_exact(bf16):
+    # 5120 blocks per source; every code of every block
+    x = _varied_rows(21 + bf16, 40, 128 * 128, bf16)
+    q, sf = oracle.per_token_cast_to_fp8(x)
+    assert (np.abs(x).reshape(40, 128, 128).max(axis=-1) < FLOOR).any()  # the floor is exercised
+    assert _per_token_mismatches(x, q, sf, False) == (0, 0)
+
+
+@pytest.mark.parametrize("bf16", [False, True])
+def test_per_token_ue8m0_scale_exact(bf16):
+    x = _varied_rows(23 + bf16, 16, 128 * 64, bf16)
+    q, sf = oracle.per_token_cast_to_fp8(x, use_ue8m0=True)
+    assert _per_token_mismatches(x, q, sf, True, code_rows={0, 1, 2, 3}) == (0, 0)
+
+
+@pytest.mark.parametrize("bf16", [False, True])
+def test_per_block_scale_and_codes_exact(bf16):
+    rng = np.random.default_rng(25 + bf16)
+    G, N, K = 3, 384, 2048
+    x = synth.normal_f32(25 + bf16, (G, N, K))
+    mag = np.exp2(rng.integers(-30, 12, size=(G, N // 128, K // 128))).astype(np.float32)
+    x = (x.reshape(G, N // 128, 128, K // 128, 128) * mag[:, :, None, :, None]).reshape(G, N, K)
+    x[1, :128, :128] = 0.0
+    if bf16:
+        x = (x.view(np.uint32) & np.uint32(0xFFFF0000)).view(np.float32)
+    q, sf = oracle.per_block_cast_to_fp8(x)
+    for g in range(G):
+        for nb in range(N // 128):
+            for kb in range(K // 128):
+                blk = x[g, nb * 128:(nb + 1) * 128, kb * 128:(kb + 1) * 128].ravel()
+                qb = q[g, nb * 128:(nb + 1) * 128, kb * 128:(kb + 1) * 128].ravel()
+                s = _exact_scale(np.abs(blk).max(), False)
+                assert float(sf[g, nb, kb]) == s, (g, nb, kb)
+                idx = np.unique(np.concatenate([rng.choice(blk.size, 1024, replace=False),
+                                                [int(np.argmax(np.abs(blk)))]]))
+                assert np.array_equal(_exact_codes(blk[idx], s), qb[idx]), (g, nb, kb)
+
+
+def test_scale_of_amax_3_is_the_correctly_rounded_quotient():
+    # 3/448 = (0.011011...)_2 * 2^-6 = 1.1011011..._2 * 2^-8; the 23 fraction
+    # bits 10110110110110110110110 are followed by 1101..., so the correctly
+    # rounded binary32 is fraction 0x5B6DB7 with biased exponent 119:
+    # 0x3BDB6DB7.  3 * RN(1/448) rounds to 0x3BDB6DB8 instead.
+    x = np.zeros((1, 128), dtype=np.float32)
+    x[0, 7] = 3.0
+    x[0, 8] = -1.0
+    _, sf = oracle.per_token_cast_to_fp8(x)
+    assert int(sf.view(np.uint32)[0, 0]) == 0x3BDB6DB7
+    assert rn32_quot(3.0, 448.0) == float(np.array([0x3BDB6DB7], dtype=np.uint32).view(np.float32)[0])
+    recip = np.float32(np.float32(3.0) * (np.float32(1.0) / np.float32(448.0)))
+    assert int(recip.view(np.uint32)) == 0x3BDB6DB8
+
+
+def test_exact_pin_rejects_a_reciprocal_multiply_scale(monkeypatch):
+    # a planted mistake in the oracle: s = amax * RN(1/448)
+    import oracle.quant as oq
+
+    def wrong_scale(amax, use_ue8m0):
+        amax = np.maximum(np.asarray(amax, dtype=np.float32), oq.AMAX_FLOOR)
+        return (amax * (np.float32(1.0) / np.float32(448.0))).astype(np.float32)
+
+    monkeypatch.setattr(oq, "_scale_from_amax", wrong_scale)
+    x = _varied_rows(27, 8, 128 * 32, False)
+    q, sf = oracle.per_token_cast_to_fp8(x)
+    bad_s, _ = _per_token_mismatches(x, q, sf, False, code_rows=set())
+    assert bad_s > 0
+
+
+def test_exact_pin_rejects_a_reciprocal_multiply_quotient():
+    # a planted mistake, q = e4m3(RN(x * RN(1/s))): a one-ulp quotient error
+    # flips a code only next to a midpoint between E4M3 values, so the block
+    # holds values placed there (x = RN(m s) + j ulp for midpoints m)
+    rng = np.random.default_rng(28)
+    pos = oracle.e4m3_decode(np.arange(127, dtype=np.uint8))
+    mids = (pos[:-1] + pos[1:]) / 2
+    x = np.zeros((64, 128), dtype=np.float32)
+    for r in range(64):
+        amax = np.float32(abs(rng.standard_normal()) * 3.0 + 0.1)
+        s = np.float32(amax / np.float32(448.0))
+        x[r, 0] = amax
+        m = mids[rng.integers(mids.size, size=127)].astype(np.float32)
+        v = (m * s).astype(np.float32)
+        j = rng.integers(-3, 4, size=127)
+        x[r, 1:] = (v.view(np.int32) + j.astype(np.int32)).view(np.float32)
+    q, sf = oracle.per_token_cast_to_fp8(x)
+    assert _per_token_mismatches(x, q, sf, False) == (0, 0)
+    s_full = np.repeat(sf, 128, axis=-1)
+    q_bad = oracle.e4m3_encode((x * (np.float32(1.0) / s_full).astype(np.float32)).astype(np.float32))
+    assert not np.array_equal(q_bad, q)
+    _, bad_q = _per_token_mismatches(x, q_bad, sf, False)
+    assert bad_q > 0

@@ -13,27 +13,7 @@ from fractions import Fraction as F
 import numpy as np
 
 import oracle
-
-
-def rn32(v):
-    """Round a rational to the nearest binary32 value, ties to even."""
-    if v == 0:
-        return F(0)
-    sgn = -1 if v < 0 else 1
-    a = abs(v)
-    e = a.numerator.bit_length() - a.denominator.bit_length()
-    if F(2) ** e > a:
-        e -= 1
-    while F(2) ** (e + 1) <= a:
-        e += 1
-    e = max(e, -126)
-    unit = F(2) ** (e - 23)
-    m = a / unit
-    fl = m.numerator // m.denominator
-    rem = m - fl
-    if rem > F(1, 2) or (rem == F(1, 2) and fl % 2 == 1):
-        fl += 1
-    return sgn * fl * unit
+from helpers import rn32
 
 
 def step(x, s):
