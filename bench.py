@@ -1,13 +1,9 @@
 """Benchmark of the block-scaled FP8 GEMM path on one MI355X.
 
-    python bench.py [--steps K] [--warmup W] [--settle-seconds S]
+    python bench.py [--steps K] [--warmup W] [--settle-seconds S] [--reps R]
                     [--workload dense|contiguous|masked|masked_graph|bf16_dense|dense_rowb|dense_fp8_out|
                                 moe_decode|moe_prefill]
-
-Before the W warmup steps, untimed steps run for S seconds (default 1): under
-sustained GEMM load the GPU clock dips for the first few milliseconds and
-settles within a few tens of milliseconds, and the K timed steps measure the
-settled, sustained rate.
+                    [--no-masked] [--no-cpu-baseline]
 
 Default workload ("dense"): the five DeepSeek-V3-shaped dense GEMMs,
 M = 4096 with (N, K) in {(2112, 7168), (24576, 1536), (7168, 16384),
@@ -16,12 +12,33 @@ One step = for every shape: per-token FP8 cast of A (1x128 scales),
 per-block FP8 cast of B (128x128 scales), and the block-scaled FP8 GEMM
 with BF16 output -- the whole hot path, no work skipped.
 
-Prints ONE JSON line.  `value` is GEMM FLOPs (2*M*N*K summed over the
-shapes) per second of whole-step time; `roofline` describes the dominant
-kernel (the FP8 GEMM) from HIP events recorded around each GEMM call on the
-launch stream (a call is one kernel launch, or two in stream order where the
-launch plan splits the columns); `cpu_baseline` times the CPU oracle on a
-bounded sample of the same workload.
+Prints ONE JSON line.
+
+* `value`: GEMM FLOPs (2*M*N*K summed over the shapes) per second of
+  whole-step time over the K timed steps (after untimed settle steps for S
+  seconds -- the GPU clock dips for the first milliseconds of sustained load
+  -- and W warmup steps).
+* `roofline`: the dominant kernel (the FP8 GEMM), timed by the protocol of
+  the pages' test suite ("DeepGEMM CUDA Graph Compatibility for Masked
+  Grouped GEMMs", Verification via Test Suite: graph-mode timing, median):
+  each GEMM call is captured once as a hipGraph, replayed 5 times untimed,
+  then R times with HIP events around the replay on the launch stream; a
+  1 GiB cache flush (a read of a 1 GiB scratch tensor) runs before every
+  timed replay, outside the events, so every replay starts with cold, clean
+  L2s and MALL (a writing flush, whose dirty lines the call would then write
+  back, is reported beside it).  `achieved` = the shapes' FLOPs / the sum of their median replay
+  times; the spread (min, p10, p90, max) is listed per shape, next to the
+  warm in-step figure (HIP events around the GEMM calls of the timed steps).
+* `masked`: the second half of the metric -- the masked grouped GEMMs
+  against HBM bandwidth, by the same graph-replay protocol: MoE decode
+  (32 experts x 256 rows, masked_m ~ floor(192 U(0.7, 1.3)), (N, K) =
+  (4096, 7168) and (7168, 2048), FP32 scales) and the graph workload (64
+  experts x 128 rows, N 7168, K 2048, a fresh uniform masked_m written before
+  every replay, outside the events; FP8 with packed UE8M0 scales and BF16).
+  GB/s = algorithmic bytes of the draw (B once per active expert, A and D
+  over valid rows, scales) / median replay time.
+* `cpu_baseline`: the CPU oracle timed per configuration on bounded samples
+  (about 10-30 s in total), with the host's core count and CPU model.
 
 Other workloads (for the measurements in the design notes):
   contiguous   -- MoE prefill: 4 groups x 8192 rows, (N, K) = (4096, 7168) and (7168, 2048)
@@ -56,6 +73,7 @@ if ROOT not in sys.path:
 FP8_PEAK_TFLOPS = 5000.0   # MI355X dense FP8 MFMA
 BF16_PEAK_TFLOPS = 2500.0  # MI355X dense BF16 MFMA
 HBM_PEAK_GBS = 8000.0      # MI355X HBM3E
+FLUSH_BYTES = 1 << 30      # cache flush before every timed graph replay (L2 4 MB x 8, MALL 256 MB)
 
 
 def log(msg):
@@ -103,6 +121,10 @@ class DenseWorkload:
             mg.fp8_gemm_nt(b["a"], b["b"], b["sfa"], b["sfb"], None, b["d"])
             if events is not None:
                 events[i][1].record()
+
+    def gemm_call(self, i):
+        b = self.bufs[i]
+        return lambda: self.mg.fp8_gemm_nt(b["a"], b["b"], b["sfa"], b["sfb"], None, b["d"])
 
     def plan_args(self, i):
         N, K = self.shapes[i]
@@ -173,6 +195,10 @@ class DenseFp8OutWorkload(DenseWorkload):
             if events is not None:
                 events[i][1].record()
 
+    def gemm_call(self, i):
+        b = self.bufs[i]
+        return lambda: self.mg.fp8_gemm_nt_fp8_out(b["a"], b["b"], b["sfa"], b["sfb"], None, b["q"], b["sfq"])
+
     def plan_args(self, i):
         N, K = self.shapes[i]
         return ("DG_KIND_DENSE_FP8_OUT", 1, self.M, N, K)
@@ -209,6 +235,10 @@ class Bf16DenseWorkload:
             self.mg.bf16_gemm_nt(a, b, None, d)
             if events is not None:
                 events[i][1].record()
+
+    def gemm_call(self, i):
+        a, b, d = self.bufs[i]
+        return lambda: self.mg.bf16_gemm_nt(a, b, None, d)
 
     def plan_args(self, i):
         N, K = self.shapes[i]
@@ -255,6 +285,11 @@ class ContiguousWorkload:
             mg.m_grouped_fp8_gemm_nt_contiguous(b["a"], b["b"], b["sfa"], b["sfb"], b["d"], self.layout)
             if events is not None:
                 events[i][1].record()
+
+    def gemm_call(self, i):
+        b = self.bufs[i]
+        return lambda: self.mg.m_grouped_fp8_gemm_nt_contiguous(b["a"], b["b"], b["sfa"], b["sfb"], b["d"],
+                                                                self.layout)
 
     def plan_args(self, i):
         N, K = self.shapes[i]
@@ -306,6 +341,11 @@ class MaskedWorkload:
             mg.m_grouped_fp8_gemm_nt_masked(b["a"], b["b"], b["sfa"], b["sfb"], b["d"], self.masked_m, self.max_m)
             if events is not None:
                 events[i][1].record()
+
+    def gemm_call(self, i):
+        b = self.bufs[i]
+        return lambda: self.mg.m_grouped_fp8_gemm_nt_masked(b["a"], b["b"], b["sfa"], b["sfb"], b["d"],
+                                                            self.masked_m, self.max_m)
 
     def plan_args(self, i):
         N, K = self.shapes[i]
@@ -407,6 +447,14 @@ class MoeDecodeWorkload:
         return {"dispatch_us": disp, "dispatch_gbs": self.dispatch_bytes / (disp * 1e-6) / 1e9,
                 "combine_us": comb, "combine_gbs": self.combine_bytes / (comb * 1e-6) / 1e9,
                 "dispatch_bytes": self.dispatch_bytes, "combine_bytes": self.combine_bytes}
+
+    def gemm_call(self, i):
+        mg = self.mg
+        if self.contig:
+            return lambda: mg.m_grouped_fp8_gemm_nt_contiguous(self.a[0], self.b, self.sfa[0], self.sfb, self.d[0],
+                                                               self.layout)
+        return lambda: mg.m_grouped_fp8_gemm_nt_masked(self.a, self.b, self.sfa, self.sfb, self.d, self.masked_m,
+                                                       self.max_m)
 
     def plan_args(self, i):
         if self.contig:
@@ -540,6 +588,13 @@ class MaskedGraphWorkload:
         self.flops = [f / n for f in self.flops]
         self.gemm_bytes = [b / n for b in self.gemm_bytes]
 
+    def gemm_call(self, i):
+        mg = self.mg
+        if i == 0:
+            return lambda: mg.m_grouped_fp8_gemm_nt_masked(self.qa, self.qb, self.pa, self.pb, self.d8,
+                                                           self.masked_m, self.max_m)
+        return lambda: mg.m_grouped_bf16_gemm_nt_masked(self.a16, self.b16, self.d16, self.masked_m, self.max_m)
+
     def plan_args(self, i):
         return ("DG_KIND_MASKED" if i == 0 else "DG_KIND_BF16_MASKED", self.G, self.max_m, self.N, self.K)
 
@@ -548,6 +603,141 @@ class MaskedGraphWorkload:
                 "mean_sum_masked_m": float(np.mean([m.sum() for m in self.mm_host])) if self.mm_host else 0.0,
                 "kernels": ["gemm_kernel FP8 kind (UE8M0 packed scales)", "gemm_kernel BF16 kind"],
                 "step": "one hipGraph replay: UE8M0 cast of A, 2 packs, FP8 masked GEMM, BF16 masked GEMM"}
+
+
+# ---------------------------------------------------------------------------
+# timing: one call captured as a hipGraph, replayed with a cold cache
+# ---------------------------------------------------------------------------
+
+def _stats(us):
+    a = np.sort(np.asarray(us, dtype=np.float64))
+    return {"median_us": float(np.median(a)), "min_us": float(a[0]), "p10_us": float(np.percentile(a, 10)),
+            "p90_us": float(np.percentile(a, 90)), "max_us": float(a[-1]), "replays": int(a.size)}
+
+
+class GraphTimer:
+    """Captures a call once (torch.cuda.graph) and times its replays with HIP
+    events on the current stream, a 1 GiB flush before each timed replay
+    (outside the events).
+
+    The flush reads the 1 GiB scratch tensor (a sum): afterwards neither the
+    per-XCD L2s nor the 256 MB MALL hold any of the call's operands, and no
+    dirty line is left behind.  A flush that writes 1 GiB instead leaves the
+    MALL full of dirty lines, whose write-back to HBM the next call then pays
+    for out of its own bandwidth; that variant is reported separately
+    (write_flush)."""
+
+    def __init__(self, torch, write_flush=False):
+        self.torch = torch
+        self.write_flush = write_flush
+        self.flush = torch.ones(FLUSH_BYTES // 4, dtype=torch.float32, device="cuda")
+        self.sink = None
+
+    def _flush(self):
+        if self.write_flush:
+            self.flush.fill_(1.0)
+        else:
+            self.sink = self.flush.sum()
+
+    def capture(self, fn):
+        torch = self.torch
+        fn()  # eager call first (nothing lazy left for the capture)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            fn()
+        torch.cuda.synchronize()
+        return g
+
+    def time(self, fn, reps, warm=5, before=None):
+        """Returns (per-replay microseconds, per-replay results of before())."""
+        torch = self.torch
+        g = self.capture(fn)
+        for _ in range(warm):
+            if before is not None:
+                before()
+            g.replay()
+        torch.cuda.synchronize()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        tags = []
+        for e0, e1 in evs:
+            if before is not None:
+                tags.append(before())
+            self._flush()
+            e0.record()
+            g.replay()
+            e1.record()
+        torch.cuda.synchronize()
+        us = [e0.elapsed_time(e1) * 1e3 for e0, e1 in evs]
+        del g
+        return us, tags
+
+
+def time_gemms(torch, W, timer, reps):
+    """Graph-replay timing of every GEMM call of a workload."""
+    out = []
+    for i in range(len(W.flops)):
+        us, _ = timer.time(W.gemm_call(i), reps)
+        out.append(_stats(us))
+    return out
+
+
+# ---------------------------------------------------------------------------
+# masked block: the masked grouped GEMMs against HBM
+# ---------------------------------------------------------------------------
+
+def masked_block(torch, mg, synth, timer, reps):
+    """MoE decode (32 x 256 rows, FP32 scales) and the graph workload (64 x
+    128 rows, FP8 UE8M0 and BF16), each GEMM by the graph-replay protocol."""
+    res = {}
+    log("masked block: decode workload (32 experts x 256 rows)")
+    Wd = MaskedWorkload(torch, mg, synth)
+    Wd.step()  # the per-token casts of A
+    torch.cuda.synchronize()
+    dec = []
+    for i, (N, K) in enumerate(Wd.shapes):
+        st = _stats(timer.time(Wd.gemm_call(i), reps)[0])
+        st.update({"N": N, "K": K, "algorithmic_bytes": Wd.gemm_bytes[i],
+                   "gbs": Wd.gemm_bytes[i] / (st["median_us"] * 1e-6) / 1e9,
+                   "tflops": Wd.flops[i] / (st["median_us"] * 1e-6) / 1e12})
+        dec.append(st)
+    tot_b = float(sum(Wd.gemm_bytes))
+    tot_t = sum(s["median_us"] for s in dec) * 1e-6
+    res["decode"] = {"workload": Wd.name, "experts": Wd.G, "max_m": Wd.max_m,
+                     "sum_masked_m": int(Wd.mm_host.sum()), "scales": "fp32 1x128 (A) / 128x128 (B)",
+                     "gbs": tot_b / tot_t / 1e9, "frac": tot_b / tot_t / 1e9 / HBM_PEAK_GBS, "per_shape": dec}
+    del Wd
+    torch.cuda.empty_cache()
+
+    log("masked block: graph workload (64 experts x 128 rows, FP8 UE8M0 and BF16)")
+    Wg = MaskedGraphWorkload(torch, mg, synth)
+    draws = []
+
+    def fresh():
+        mm = Wg._next_masked_m()
+        Wg.masked_m.copy_(torch.from_numpy(mm))
+        draws.append(mm)
+        return mm
+
+    graph = {}
+    for i, kind in enumerate(("fp8_ue8m0", "bf16")):
+        us, tags = timer.time(Wg.gemm_call(i), reps, before=fresh)
+        b = np.array([Wg._bytes(m)[1 + i] for m in tags])
+        gbs = b / (np.asarray(us) * 1e-6) / 1e9
+        st = _stats(us)
+        st.update({"gbs_median": float(np.median(gbs)), "gbs_p10": float(np.percentile(gbs, 10)),
+                   "gbs_p90": float(np.percentile(gbs, 90)), "mean_algorithmic_bytes": float(b.mean()),
+                   "mean_sum_masked_m": float(np.mean([m.sum() for m in tags]))})
+        st["frac"] = st["gbs_median"] / HBM_PEAK_GBS
+        graph[kind] = st
+    res["graph"] = {"workload": Wg.name, "experts": Wg.G, "max_m": Wg.max_m, "N": Wg.N, "K": Wg.K,
+                    "masked_m": "uniform integers 0..128, a fresh draw before every replay", **graph}
+    del Wg
+    torch.cuda.empty_cache()
+    res["roofline"] = {"bound": "hbm", "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                       "decode_frac": res["decode"]["frac"],
+                       "graph_fp8_ue8m0_frac": graph["fp8_ue8m0"]["frac"], "graph_bf16_frac": graph["bf16"]["frac"]}
+    return res
 
 
 # ---------------------------------------------------------------------------
@@ -581,10 +771,23 @@ def recorded_traffic(workload):
 
 
 # ---------------------------------------------------------------------------
-# CPU baseline: the oracle on a bounded sample of the dense workload
+# CPU baseline: the oracle per configuration on bounded samples
 # ---------------------------------------------------------------------------
 
-def time_cpu_baseline(rows_a=512, rows_b=8192):
+def _cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def time_cpu_baseline():
+    """The oracle (numpy float64; the per-128-block products go through the
+    BLAS matmul, the rest is single-threaded numpy) on a bounded sample of
+    every configuration.  Returns the dense sample's TFLOP/s as `value`."""
     import oracle
     from moe_grouped_gemm_x128_amd import synth
 
@@ -594,27 +797,113 @@ def time_cpu_baseline(rows_a=512, rows_b=8192):
         blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:
         blas_threads = 1
-    flops = 0.0
-    spent = 0.0
+    per = {}
+
+    def timed(fn):
+        t = time.perf_counter()
+        fn()
+        return time.perf_counter() - t
+
+    # dense small, whole: quantize both operands + GEMM
+    c = synth.DENSE_SMALL
+    xa, xb = synth.normal_f32(c["seed_a"], (c["M"], c["K"])), synth.normal_f32(c["seed_b"], (c["N"], c["K"]))
+
+    def run_small():
+        a, sfa = oracle.per_token_cast_to_fp8(xa)
+        b, sfb = oracle.per_block_cast_to_fp8(xb)
+        oracle.fp8_gemm_nt(a, b, sfa, sfb)
+
+    s = timed(run_small)
+    f = 2.0 * c["M"] * c["N"] * c["K"]
+    per["dense_small"] = {"seconds": s, "gflops": f / s / 1e9, "sample": "whole (128 x 256 x 512)"}
+
+    # dense V3 shapes: 256 rows of A x 2048 rows of B per shape, full K
+    rows_a, rows_b = 256, 2048
+    flops, spent = 0.0, 0.0
     for i, (N, K) in enumerate(synth.DENSE_V3_SHAPES):
         sa, sb = synth.dense_v3_seeds(i)
-        rng_a = synth.normal_f32(sa, (synth.DENSE_V3_M, K))[:rows_a]
-        rng_b = synth.normal_f32(sb, (N, K))[:rows_b]
-        t = time.perf_counter()
-        a, sfa = oracle.per_token_cast_to_fp8(rng_a)
-        b, sfb = oracle.per_block_cast_to_fp8(rng_b)
-        oracle.fp8_gemm_nt(a, b, sfa, sfb)
-        spent += time.perf_counter() - t
+        ra = synth.normal_f32(sa, (rows_a, K))
+        rb = synth.normal_f32(sb, (min(rows_b, N), K))
+
+        def run():
+            a, sfa = oracle.per_token_cast_to_fp8(ra)
+            b, sfb = oracle.per_block_cast_to_fp8(rb)
+            oracle.fp8_gemm_nt(a, b, sfa, sfb)
+
+        spent += timed(run)
         flops += 2.0 * rows_a * min(rows_b, N) * K
+    per["dense_v3"] = {"seconds": spent, "gflops": flops / spent / 1e9,
+                       "sample": f"per shape: {rows_a} rows of A x {rows_b} rows of B, full K, quantize + GEMM"}
+    dense_tflops = flops / spent / 1e12
+
+    # contiguous prefill: one 128-row block per group, 1024 rows of each group's B
+    cc = synth.CONTIG
+    G = cc["G"]
+    flops, spent = 0.0, 0.0
+    for si, (N, K) in enumerate(cc["shapes"]):
+        xa = synth.normal_f32(cc["seed_a"] + 10 * si, (G * 128, K))
+        xb = synth.normal_f32(cc["seed_b"] + 10 * si, (G, 1024, K))
+        layout = np.arange(G, dtype=np.int32)
+
+        def run():
+            a, sfa = oracle.per_token_cast_to_fp8(xa)
+            b, sfb = oracle.per_block_cast_to_fp8(xb)
+            oracle.m_grouped_fp8_gemm_nt_contiguous(a, b, sfa, sfb, layout)
+
+        spent += timed(run)
+        flops += 2.0 * G * 128 * 1024 * K
+    per["contiguous_prefill"] = {"seconds": spent, "gflops": flops / spent / 1e9,
+                                 "sample": "per shape: one 128-row block per group x 1024 rows of its B"}
+
+    # masked decode: 2 experts (their masked_m rows) x 1024 rows of B
+    cm = synth.MASKED
+    mm = synth.masked_m_decode(cm["seed_m"], cm["G"])[:2]
+    flops, spent = 0.0, 0.0
+    for si, (N, K) in enumerate(cm["shapes"]):
+        xa = synth.normal_f32(cm["seed_a"] + 10 * si, (2, cm["max_m"], K))
+        xb = synth.normal_f32(cm["seed_b"] + 10 * si, (2, 1024, K))
+
+        def run():
+            a, sfa = oracle.per_token_cast_to_fp8(xa)
+            b, sfb = oracle.per_block_cast_to_fp8(xb)
+            oracle.m_grouped_fp8_gemm_nt_masked(a, b, sfa, sfb, mm, cm["max_m"])
+
+        spent += timed(run)
+        flops += 2.0 * int(mm.sum()) * 1024 * K
+    per["masked_decode"] = {"seconds": spent, "gflops": flops / spent / 1e9,
+                            "sample": "per shape: 2 experts (their masked_m rows) x 1024 rows of B"}
+
+    # masked graph: 4 experts, FP8 with UE8M0 scales and BF16, 1024 rows of B
+    cg = synth.MASKED_GRAPH
+    mm = synth.masked_m_uniform(cg["seed_m"] + 2, cg["G"], cg["max_m"])[:4]
+    xa = synth.normal_f32(cg["seed_a"], (4, cg["max_m"], cg["K"]))
+    xb = synth.normal_f32(cg["seed_b"], (4, 1024, cg["K"]))
+
+    def run_g():
+        a, sfa = oracle.per_token_cast_to_fp8(xa, use_ue8m0=True)
+        b, sfb = oracle.per_block_cast_to_fp8(xb, use_ue8m0=True)
+        oracle.m_grouped_fp8_gemm_nt_masked(a, b, sfa, sfb, mm, cg["max_m"])
+        ab = synth.bf16_bits_from_f32(xa)
+        bb = synth.bf16_bits_from_f32(xb)
+        oracle.m_grouped_bf16_gemm_nt_masked(ab, bb, mm, cg["max_m"])
+
+    s = timed(run_g)
+    f = 2 * 2.0 * int(mm.sum()) * 1024 * cg["K"]
+    per["masked_graph"] = {"seconds": s, "gflops": f / s / 1e9,
+                           "sample": "4 experts (their masked_m rows) x 1024 rows of B, FP8 UE8M0 + BF16"}
+    total = sum(v["seconds"] for v in per.values())
     return {
-        "value": flops / spent / 1e12,
+        "value": dense_tflops,
         "unit": "TFLOPS",
         "cores": blas_threads,
         "kind": "oracle",
-        "sample": (f"per shape: first {rows_a} rows of A x first {rows_b} rows of B, per-token + per-block quantize "
-                   f"+ block-scaled GEMM in float64 (numpy; elementwise work single-threaded, matmul on "
-                   f"{blas_threads} BLAS threads); {spent:.1f} s of oracle time"),
-        "seconds": spent,
+        "sample": (f"dense V3 shapes, {rows_a} rows of A x {rows_b} rows of B per shape, quantize + block-scaled "
+                   f"GEMM in float64 (numpy; the block products on {blas_threads} BLAS threads, the rest "
+                   f"single-threaded); every configuration under per_config; {total:.1f} s of oracle time"),
+        "host_cores_available": len(os.sched_getaffinity(0)),
+        "cpu_model": _cpu_model(),
+        "per_config": per,
+        "seconds": total,
     }
 
 
@@ -633,8 +922,10 @@ def main():
     ap.add_argument("--settle-seconds", type=float, default=1.0,
                     help="untimed steps run for this long before the warmup steps, so that the timed steps see "
                          "the GPU's steady sustained clock rather than the dip of its first milliseconds under load")
+    ap.add_argument("--reps", type=int, default=25, help="timed graph replays per GEMM call (kernel timing)")
     ap.add_argument("--event-every", type=int, default=10,
                     help="record HIP events around the GEMM calls of one timed step in this many (plus the last)")
+    ap.add_argument("--no-masked", action="store_true", help="dense: skip the masked grouped GEMM block")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run one 1 GiB device copy (calibrates rocprofv3 FETCH/WRITE_SIZE counters)")
@@ -664,8 +955,8 @@ def main():
     torch.cuda.synchronize()
 
     # Power-state settle: under sustained GEMM load the clock dips for the first
-    # few milliseconds (to ~1.4 GHz) and recovers to its steady level within a
-    # few tens of milliseconds; steps run here are not timed and not counted.
+    # few milliseconds and recovers within a few tens of milliseconds; steps run
+    # here are not timed and not counted.
     settle_steps = 0
     t_settle = time.perf_counter() + args.settle_seconds
     while time.perf_counter() < t_settle:
@@ -678,23 +969,21 @@ def main():
     for _ in range(args.warmup):
         W.step()
     torch.cuda.synchronize()
-    if hasattr(W, "timing_pass"):
+    graph_wl = hasattr(W, "timing_pass")
+    if graph_wl:
         W.mm_host = []  # count the timed replays only
     log(f"warmup done ({args.warmup} steps); timing {args.steps} steps")
 
     nshape = len(W.flops)
     events = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(nshape)]
               for _ in range(args.steps)]
-    # HIP events around the GEMM calls of one timed step in `event_every`
-    # (and of the last step): each event record is a marker in the stream
-    # that the next kernel waits behind (about 5.6 us on this GPU), so
-    # recording them on every step would add ~10% of gaps to a step of
-    # fifteen kernels
+    # HIP events around the GEMM calls of one timed step in `event_every` (and
+    # of the last step): an event record is a marker that the next kernel waits
+    # behind, so recording them on every step would add gaps to the step
     timed = [s for s in range(args.steps) if s % args.event_every == args.event_every - 1]
     if args.steps - 1 not in timed:
         timed.append(args.steps - 1)
     torch.cuda.synchronize()
-    graph_wl = hasattr(W, "timing_pass")
     t0 = time.perf_counter()
     for s in range(args.steps):
         W.step(events[s] if (s in timed and not graph_wl) else None)
@@ -715,45 +1004,69 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    # per-shape average GEMM launch duration (ms)
-    gemm_ms = [float(np.mean([events[s][i][0].elapsed_time(events[s][i][1]) for s in timed])) for i in range(nshape)]
+    # warm in-step GEMM durations (ms) from the timed steps' events
+    step_ms = [float(np.mean([events[s][i][0].elapsed_time(events[s][i][1]) for s in timed])) for i in range(nshape)]
     ms_per_step = wall * 1e3 / args.steps
     total_flops = float(sum(W.flops))
     value = total_flops / (ms_per_step * 1e-3) / 1e12
-    mean_launch_ms = float(np.mean(gemm_ms))
-    mean_flops = total_flops / nshape
-    is_masked = args.workload in ("masked", "masked_graph", "moe_decode")
-    is_moe = args.workload in ("moe_decode", "moe_prefill")
+
+    # kernel timing by the graph-replay protocol (cold cache, median)
+    log(f"graph-replay timing of the GEMM calls ({args.reps} replays each, 1 GiB flush before each)")
+    timer = GraphTimer(torch)
     if graph_wl:
-        # dominant kernel: the GEMM with the longest launches
-        dom = int(np.argmax(gemm_ms))
-        achieved = W.gemm_bytes[dom] / (gemm_ms[dom] * 1e-3) / 1e9
-        roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": achieved / HBM_PEAK_GBS, "traffic": None}
-    elif is_masked:
-        mean_bytes = float(np.mean(W.gemm_bytes))
-        achieved = mean_bytes / (mean_launch_ms * 1e-3) / 1e9
-        roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": achieved / HBM_PEAK_GBS, "traffic": None}
+        kt = []
+        for i in range(nshape):
+            us, tags = timer.time(W.gemm_call(i), args.reps,
+                                  before=lambda: (W.masked_m.copy_(torch.from_numpy(W._next_masked_m())), None)[1])
+            kt.append(_stats(us))
     else:
-        peak = BF16_PEAK_TFLOPS if args.workload == "bf16_dense" else FP8_PEAK_TFLOPS
-        achieved = mean_flops / (mean_launch_ms * 1e-3) / 1e12
-        roof = {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
-                "frac": achieved / peak, "traffic": None}
+        kt = time_gemms(torch, W, timer, args.reps)
+        wtimer = GraphTimer(torch, write_flush=True)
+        wflush = [k["median_us"] for k in time_gemms(torch, W, wtimer, args.reps)]
+        del wtimer
+        for k, w in zip(kt, wflush):
+            k["write_flush_median_us"] = w
+    gemm_us = [k["median_us"] for k in kt]
+
+    is_masked = args.workload in ("masked", "masked_graph", "moe_decode")
+    peak = BF16_PEAK_TFLOPS if args.workload == "bf16_dense" else FP8_PEAK_TFLOPS
+    if is_masked:
+        if graph_wl:
+            dom = int(np.argmax(gemm_us))
+            achieved = W.gemm_bytes[dom] / (gemm_us[dom] * 1e-6) / 1e9
+            alg = float(W.gemm_bytes[dom])
+            avg_us = gemm_us[dom]
+        else:
+            alg = float(np.mean(W.gemm_bytes))
+            avg_us = float(np.mean(gemm_us))
+            achieved = float(sum(W.gemm_bytes)) / (sum(gemm_us) * 1e-6) / 1e9
+        roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": achieved / HBM_PEAK_GBS}
+    else:
+        achieved = total_flops / (sum(gemm_us) * 1e-6) / 1e12
+        alg = float(np.mean(W.gemm_bytes))
+        avg_us = float(np.mean(gemm_us))
+        roof = {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s", "frac": achieved / peak}
     roof["traffic"] = recorded_traffic(args.workload)
     roof["traffic_unit"] = "HBM bytes per GEMM call (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)"
-    roof["algorithmic_bytes_per_launch"] = float(np.mean(W.gemm_bytes))
-    roof["kernel"] = "gemm_kernel (FP8 kind)"
-    roof["avg_launch_us"] = mean_launch_ms * 1e3
-    roof["per_launch"] = ("mean over the workload's GEMM calls of one step (algorithmic work / HIP-event duration "
-                          "around the call; a call is one kernel launch, or two in stream order where the launch "
-                          "plan splits the columns, see gemm_per_shape); events recorded on %d of the %d timed "
-                          "steps" % (len(timed), args.steps))
-    if graph_wl:
-        roof["algorithmic_bytes_per_launch"] = float(W.gemm_bytes[dom])
-        roof["kernel"] = ["gemm_kernel (FP8 kind, UE8M0)", "gemm_kernel (BF16 kind)"][dom]
-        roof["avg_launch_us"] = gemm_ms[dom] * 1e3
-        roof["per_launch"] = "the longer of the two GEMM kernels (algorithmic bytes / HIP-event duration of eager launches)"
+    roof["algorithmic_bytes_per_launch"] = alg
+    roof["kernel"] = "gemm_kernel (BF16 kind)" if args.workload == "bf16_dense" else "gemm_kernel (FP8 kind)"
+    roof["avg_launch_us"] = avg_us
+    roof["per_launch"] = ("each GEMM call captured once as a hipGraph, 5 untimed replays, then %d replays with HIP "
+                          "events around the replay on the launch stream and a 1 GiB cache flush (a read of a 1 GiB "
+                          "scratch tensor) before each, outside the events; achieved = the calls' algorithmic work / "
+                          "the sum of their median replay times (a call is one kernel launch, or two in stream order "
+                          "where the launch plan splits the columns)" % args.reps)
+    if not is_masked and not graph_wl:
+        wf = total_flops / (sum(k["write_flush_median_us"] for k in kt) * 1e-6) / 1e12
+        roof["write_flush"] = {"achieved": wf, "frac": wf / peak,
+                               "note": "the same protocol with a flush that writes 1 GiB: the call also pays the "
+                                       "write-back of the dirty lines the flush leaves in the MALL"}
+    in_step = total_flops / (sum(step_ms) * 1e-3) / 1e12 if not is_masked else None
+    roof["warm_in_step"] = {"achieved": in_step, "frac": in_step / peak if in_step else None,
+                            "per_call_us": [m * 1e3 for m in step_ms],
+                            "note": "HIP events around the GEMM calls of %d of the %d timed steps (warm cache, "
+                                    "operands just written by the casts)" % (len(timed), args.steps)}
 
     per_shape = []
     for i in range(nshape):
@@ -763,10 +1076,11 @@ def main():
         tiles = f"{plan['block_m']}x{plan['block_n']}"
         if plan["block_n2"]:
             tiles += f" on columns [0, {plan['n_split']}), {plan['block_m']}x{plan['block_n2']} on the rest"
-        per_shape.append({"N": N, "K": K, "gemm_us": gemm_ms[i] * 1e3,
-                          "tflops": W.flops[i] / (gemm_ms[i] * 1e-3) / 1e12,
-                          "gbs": W.gemm_bytes[i] / (gemm_ms[i] * 1e-3) / 1e9,
-                          "launches": 2 if plan["block_n2"] else 1, "tiles": tiles})
+        e = {"N": N, "K": K, "tflops": W.flops[i] / (gemm_us[i] * 1e-6) / 1e12,
+             "gbs": W.gemm_bytes[i] / (gemm_us[i] * 1e-6) / 1e9,
+             "in_step_us": step_ms[i] * 1e3, "launches": 2 if plan["block_n2"] else 1, "tiles": tiles}
+        e.update(kt[i])
+        per_shape.append(e)
 
     if graph_wl:
         metric = "masked grouped FP8 (UE8M0) + BF16 GEMM GB/s under graph replay (% HBM)"
@@ -790,18 +1104,16 @@ def main():
     elif is_masked:
         metric = "masked grouped FP8 GEMM GB/s (% HBM)"
         unit = "GB/s"
-        step_bytes = float(sum(W.gemm_bytes))
-        value = step_bytes / (ms_per_step * 1e-3) / 1e9
+        value = float(sum(W.gemm_bytes)) / (ms_per_step * 1e-3) / 1e9
     elif args.workload == "bf16_dense":
         metric = "BF16 GEMM TFLOPS (% BF16 MFMA peak)"
         unit = "TFLOPS"
-        roof["kernel"] = "gemm_kernel (BF16 kind)"
     elif args.workload == "dense_fp8_out":
         metric = "FP8 block-scaled GEMM with per-token FP8 output TFLOPS (% FP8 MFMA peak)"
         unit = "TFLOPS"
         roof["kernel"] = "gemm_kernel (FP8 kind, FP8-output epilogue)"
     else:
-        metric = "FP8 block-scaled GEMM TFLOPS (% FP8 MFMA peak)"
+        metric = "FP8 block-scaled GEMM TFLOPS (% FP8 MFMA peak); masked-grouped GB/s (% HBM)"
         unit = "TFLOPS"
 
     out = {
@@ -821,10 +1133,13 @@ def main():
         "config": W.config(),
         "roofline": roof,
         "gemm_per_shape": per_shape,
-        "gemm_only_value": mean_flops / (mean_launch_ms * 1e-3) / 1e12 if not is_masked else achieved,
     }
+    del W
+    torch.cuda.empty_cache()
+    if args.workload == "dense" and not args.no_masked:
+        out["masked"] = masked_block(torch, mg, synth, timer, args.reps)
     if not args.no_cpu_baseline and args.workload == "dense":
-        log("timing the CPU oracle on a bounded sample")
+        log("timing the CPU oracle on bounded samples")
         out["cpu_baseline"] = time_cpu_baseline()
     else:
         out["cpu_baseline"] = None

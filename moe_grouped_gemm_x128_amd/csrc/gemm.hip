@@ -163,6 +163,18 @@ __device__ __forceinline__ void band_order(int t, int tiles_m, int tiles_n, int 
 }
 
 
+// One FP8 block product of a 16x16 fragment over 128 K values, P = B . A^T
+// added to c, with no scaling (the FP32-scale kinds promote P themselves).
+// The f8f6f4 matrix core has no builtin of its own without scales: the
+// scaled builtin with literal zero scale operands is what the backend lowers
+// to the unscaled v_mfma_f32_16x16x128_f8f6f4.  The zeros must stay literals
+// inside this helper -- a non-constant scale operand selects the scaled
+// instruction, where a scale byte of 0 multiplies by 2^-127 and would zero
+// every product.
+__device__ __forceinline__ f32x4 mfma_fp8_unscaled(const i32x8& b, const i32x8& a, const f32x4& c) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(b, a, c, 0, 0, 0, /*scale_b=*/0, 0, /*scale_a=*/0);
+}
+
 __device__ __forceinline__ bf16x8 lo_bf16(const i32x8& v) { return __builtin_bit_cast(bf16x8, i32x4{v[0], v[1], v[2], v[3]}); }
 __device__ __forceinline__ bf16x8 hi_bf16(const i32x8& v) { return __builtin_bit_cast(bf16x8, i32x4{v[4], v[5], v[6], v[7]}); }
 
@@ -761,7 +773,7 @@ __global__ __launch_bounds__(T::NT) void gemm_kernel(const GemmParams p) {
 #pragma unroll
           for (int f = 0; f < T::FN; ++f) {
             __builtin_amdgcn_sched_barrier(0);
-            P[i & 1][f] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf[f], af, zero, 0, 0, 0, 0, 0, 0);
+            P[i & 1][f] = mfma_fp8_unscaled(bf[f], af, zero);
             spread_loads(i, f, cur_a, cur_b, kb);
             __builtin_amdgcn_sched_barrier(0);
             const float sp = s_prev[NSB == 1 ? 0 : f];
@@ -1101,36 +1113,44 @@ hipError_t launch_variant(const TileCfg& cfg, const GemmParams& p, int mode, int
 // split 390.7 against 391.6 us back to back and 387.6 against 380.4 us in
 // the benchmark's step; BF16 split 3% faster in both.
 constexpr int NUM_CU = 256;
+// Cost model constants, in K-loop slices of the 256 x 256 tile (above).
+constexpr double SLICE_256x192 = 0.88, SLICE_192x192 = 0.75, PER_ROUND = 7.0, PER_LAUNCH = 5.7;
+
+// Cost of one launch of `tiles` tiles of KB slices each, at `slice` per slice:
+// whole rounds of one tile per CU.
+double launch_cost(int64_t tiles, int64_t KB, double slice) {
+  const int64_t rounds = (tiles + NUM_CU - 1) / NUM_CU;
+  return (double)rounds * ((double)KB * slice + PER_ROUND);
+}
+
+// Whether the dense 192 x 192 tile costs less than `other` (one launch).
+bool dense_q_wins(int64_t M, int64_t N, int64_t KB, double other) {
+  return launch_cost(((M + 191) / 192) * ((N + 191) / 192), KB, SLICE_192x192) < other;
+}
 
 template <int KIND>
 GemmPlan plan_large(int mode, int64_t G, int64_t M, int64_t N, int64_t KB) {
   const int64_t units = (mode == MODE_MASKED ? G : 1) * ((M + 255) / 256);
-  const double slice_n = 0.88, slice_q = 0.75, per_round = 7.0, per_launch = 5.7;
   auto cost = [&](int64_t cols, int64_t bn, double slice) {
-    const int64_t rounds = (units * ((cols + bn - 1) / bn) + NUM_CU - 1) / NUM_CU;
-    return (double)rounds * ((double)KB * slice + per_round);
+    return launch_cost(units * ((cols + bn - 1) / bn), KB, slice);
   };
   GemmPlan best;
   best.parts = 1;
   best.n_split = N;
   best.cfg[0] = make_cfg<TileL, KIND>(VAR_L);
   double best_cost = cost(N, 256, 1.0);
-  const double only_n = cost(N, 192, slice_n);
+  const double only_n = cost(N, 192, SLICE_256x192);
   if (only_n < best_cost) {
     best_cost = only_n;
     best.cfg[0] = make_cfg<TileN, KIND>(VAR_N);
   }
-  if (mode == MODE_DENSE) {
-    // 192 x 192 tiles: (M/192) (N/192) of them, a slice at 0.75 of a 256 x 256 one
-    const int64_t rounds = ((M + 191) / 192 * ((N + 191) / 192) + NUM_CU - 1) / NUM_CU;
-    const double only_q = (double)rounds * ((double)KB * slice_q + per_round);
-    if (only_q < best_cost) {
-      best_cost = only_q;
-      best.cfg[0] = make_cfg<TileQ, KIND>(VAR_Q);
-    }
+  if (mode == MODE_DENSE && dense_q_wins(M, N, KB, best_cost)) {
+    // 192 x 192 tiles (dense only: they do not align with the grouped layouts' 128-row blocks)
+    best_cost = launch_cost(((M + 191) / 192) * ((N + 191) / 192), KB, SLICE_192x192);
+    best.cfg[0] = make_cfg<TileQ, KIND>(VAR_Q);
   }
   for (int64_t n1 = 256; KIND == KIND_BF16 && n1 < N; n1 += 256) {
-    const double c = cost(n1, 256, 1.0) + cost(N - n1, 192, slice_n) + per_launch;
+    const double c = cost(n1, 256, 1.0) + cost(N - n1, 192, SLICE_256x192) + PER_LAUNCH;
     if (c < best_cost) {
       best_cost = c;
       best.parts = 2;
@@ -1185,11 +1205,9 @@ GemmPlan fp8_gemm_plan(int mode, int64_t G, int64_t M, int64_t N, int64_t K, int
     p.parts = 1;
     p.n_split = N;
     p.cfg[0] = make_cfg<TileN, KIND_FP8>(VAR_N);
-    if (mode == MODE_DENSE) {  // or 192 x 192 tiles where one round of them costs less (plan_large)
+    if (mode == MODE_DENSE) {  // or 192 x 192 tiles where they cost less (plan_large's model)
       const int64_t KB = (K + 127) / 128;
-      const int64_t rq = ((M + 191) / 192 * ((N + 191) / 192) + NUM_CU - 1) / NUM_CU;
-      const int64_t rn = ((M + 255) / 256 * ((N + 191) / 192) + NUM_CU - 1) / NUM_CU;
-      if ((double)rq * ((double)KB * 0.75 + 7.0) < (double)rn * ((double)KB * 0.88 + 7.0))
+      if (dense_q_wins(M, N, KB, launch_cost(((M + 255) / 256) * ((N + 191) / 192), KB, SLICE_256x192)))
         p.cfg[0] = make_cfg<TileQ, KIND_FP8>(VAR_Q);
     }
     return p;

@@ -1,0 +1,92 @@
+"""Checks on the gfx950 machine code of this library's own GEMM kernels
+(read from the device code object in the in-tree build; host-side only).
+
+* The FP32-scale FP8 kinds must contain the unscaled block product
+  v_mfma_f32_16x16x128_f8f6f4 and no scaled one: their partials are promoted
+  by FP32 FMAs, and a scaled instruction would apply E8M0 scale bytes of 0
+  (2^-127) to every product.  The UE8M0 kinds must use the scaled instruction
+  (the power-of-two scales are applied inside the matrix core).
+* No GEMM kernel may spill to scratch (private segment size 0).
+
+Skipped when the library has not been built here or the LLVM tools of the
+ROCm install are missing."""
+
+import os
+import re
+import shutil
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+OBJ = os.path.join(ROOT, "moe_grouped_gemm_x128_amd", "_build", "gemm.hip.o")
+LLVM = "/opt/rocm/lib/llvm/bin"
+TOOLS = ["llvm-objcopy", "clang-offload-bundler", "llvm-objdump", "llvm-readelf"]
+
+# gemm_kernel<TileShape<BM, BN, WM, WN, S>, KIND, SF, MODE, OUT>
+KERNEL_RE = re.compile(r"gemm_kernelINS0_9TileShapeI((?:Li\d+E){5})EELi(\d+)ELi(\d+)ELi(\d+)ELi(\d+)E")
+
+
+@pytest.fixture(scope="module")
+def code_object(tmp_path_factory):
+    if not os.path.exists(OBJ):
+        pytest.skip("library not built in-tree")
+    if not all(os.path.exists(os.path.join(LLVM, t)) for t in TOOLS):
+        pytest.skip("ROCm LLVM tools not found")
+    d = tmp_path_factory.mktemp("isa")
+    fat = str(d / "gemm.fatbin")
+    co = str(d / "gemm_gfx950.co")
+    subprocess.run([os.path.join(LLVM, "llvm-objcopy"), f"--dump-section=.hip_fatbin={fat}", OBJ, str(d / "x.o")],
+                   check=True, capture_output=True)
+    subprocess.run([os.path.join(LLVM, "clang-offload-bundler"), "--unbundle", "--type=o",
+                    "--targets=hipv4-amdgcn-amd-amdhsa--gfx950", f"--input={fat}", f"--output={co}"],
+                   check=True, capture_output=True)
+    return co
+
+
+def _functions(co):
+    """{mangled kernel name: disassembly text} for every GEMM kernel."""
+    out = subprocess.run([os.path.join(LLVM, "llvm-objdump"), "-d", co], check=True, capture_output=True,
+                         text=True).stdout
+    funcs, cur = {}, None
+    for line in out.splitlines():
+        m = re.match(r"^[0-9a-f]+ <(\S+)>:$", line)
+        if m:
+            cur = m.group(1) if "gemm_kernel" in m.group(1) else None
+            if cur:
+                funcs[cur] = []
+        elif cur:
+            funcs[cur].append(line)
+    return {k: "\n".join(v) for k, v in funcs.items()}
+
+
+def test_fp32_scale_kinds_use_the_unscaled_block_product(code_object):
+    funcs = _functions(code_object)
+    checked = 0
+    for name, text in funcs.items():
+        m = KERNEL_RE.search(name)
+        assert m, name
+        kind, sf = int(m.group(2)), int(m.group(3))
+        if kind != 0:  # BF16 kind
+            continue
+        if sf & 1:  # UE8M0: scales inside the matrix core
+            assert "v_mfma_scale_f32_16x16x128_f8f6f4" in text, name
+        else:
+            assert "v_mfma_scale_f32" not in text, name
+            assert "v_mfma_f32_16x16x128_f8f6f4" in text, name
+        checked += 1
+    assert checked >= 20
+
+
+def test_no_gemm_kernel_spills(code_object):
+    notes = subprocess.run([os.path.join(LLVM, "llvm-readelf"), "--notes", code_object], check=True,
+                           capture_output=True, text=True).stdout
+    name, seen = None, 0
+    for line in notes.splitlines():
+        s = line.strip()
+        if s.startswith(".name:"):
+            name = s.split(":", 1)[1].strip()
+        elif s.startswith(".private_segment_fixed_size:") and name and "gemm_kernel" in name:
+            assert int(s.split(":", 1)[1]) == 0, f"{name} uses scratch"
+            seen += 1
+    assert seen >= 20
