@@ -95,10 +95,39 @@ int dgmi_init(void);
  * D[m,n] = C[m,n] + sum_kb (sum_{k in kb} A[m,k] B[n,k]) * sfa[m,kb] * sfb[n/128,kb]
  * (sfb[n,kb] with one scale per row of B).
  * K must be a multiple of 128; M and N are arbitrary.
+ * a or b may also be MN-major: the transposed view ([M, K] with strides
+ * (1, lda)) of a row-major [K, M] tensor, likewise b of a [K, N] one -- the
+ * layouts of fp8_gemm_nn / _tn / _tt below, with their conditions.
  */
 int fp8_gemm_nt(const dg_tensor* a, const dg_tensor* b, const dg_tensor* sfa,
                 const dg_tensor* sfb, const dg_tensor* c, const dg_tensor* d,
                 hipStream_t stream);
+
+/*
+ * The NN, TN and TT layouts of the same GEMM ("DeepInside DeepGEMM", section
+ * 2: besides NT, the NN, TN and TT layouts of the FP8 GEMM), for operands
+ * already in FP8 and stored MN-major.  The first letter is A's layout, the
+ * second B's, read as D = op(A) . op(B):
+ *   fp8_gemm_nn  a E4M3 [M, K] (K contiguous),  b E4M3 [K, N] (N contiguous)
+ *   fp8_gemm_tn  a E4M3 [K, M] (M contiguous),  b E4M3 [K, N]
+ *   fp8_gemm_tt  a E4M3 [K, M],                 b E4M3 [N, K] (K contiguous)
+ * so D[m,n] = C[m,n] + sum_kb (sum_{k in kb} A[m,k] B[n,k]) sfa[m,kb] sfb[n/128,kb]
+ * with A[m,k] and B[n,k] read from the stored layouts.  sfa, sfb, c and d as
+ * for fp8_gemm_nt (sfa is [M, K/128], sfb [ceil(N/128), K/128] whatever the
+ * operands' layout).  An MN-major operand is row-major in its stored shape,
+ * with a 16-byte aligned base and a K-row stride (bytes) that is a multiple
+ * of 16 in [rows, 2^28]; its row count (M or N) must be a multiple of 16
+ * (else DG_UNSUPPORTED).  Block scales only (FP32 or packed UE8M0), BF16 d
+ * (one scale per row of B, or an F32 d: DG_UNSUPPORTED).  The fragments of an
+ * MN-major operand are read from LDS with transposing loads; results equal
+ * fp8_gemm_nt's on the same values bit for bit.
+ */
+int fp8_gemm_nn(const dg_tensor* a, const dg_tensor* b, const dg_tensor* sfa, const dg_tensor* sfb,
+                const dg_tensor* c, const dg_tensor* d, hipStream_t stream);
+int fp8_gemm_tn(const dg_tensor* a, const dg_tensor* b, const dg_tensor* sfa, const dg_tensor* sfb,
+                const dg_tensor* c, const dg_tensor* d, hipStream_t stream);
+int fp8_gemm_tt(const dg_tensor* a, const dg_tensor* b, const dg_tensor* sfa, const dg_tensor* sfb,
+                const dg_tensor* c, const dg_tensor* d, hipStream_t stream);
 
 /*
  * fp8_gemm_nt with its output cast to FP8 in the same kernel ("DeepInside
@@ -328,7 +357,8 @@ enum {
   DG_KIND_DENSE = 0, DG_KIND_CONTIGUOUS = 1, DG_KIND_MASKED = 2,            /* FP8 GEMMs */
   DG_KIND_BF16_MASKED = 3, DG_KIND_BF16_DENSE = 4, DG_KIND_BF16_CONTIGUOUS = 5, /* BF16 GEMMs */
   DG_KIND_DENSE_ROWB = 6, DG_KIND_CONTIGUOUS_ROWB = 7, DG_KIND_MASKED_ROWB = 8, /* FP8, one B scale per row */
-  DG_KIND_DENSE_FP8_OUT = 9                                                       /* fp8_gemm_nt_fp8_out */
+  DG_KIND_DENSE_FP8_OUT = 9,                                                      /* fp8_gemm_nt_fp8_out */
+  DG_KIND_DENSE_MN = 10                         /* fp8_gemm_nn / _tn / _tt (an MN-major operand) */
 };
 
 /* Fill *out with the configuration `kind` would launch for these sizes

@@ -14,6 +14,9 @@ from .binding import (  # noqa: F401
     dgmi_init,
     fp8_gemm_nt,
     fp8_gemm_nt_fp8_out,
+    fp8_gemm_nn,
+    fp8_gemm_tn,
+    fp8_gemm_tt,
     m_grouped_fp8_gemm_nt_contiguous,
     m_grouped_fp8_gemm_nt_masked,
     m_grouped_bf16_gemm_nt_masked,

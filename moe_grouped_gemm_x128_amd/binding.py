@@ -19,12 +19,16 @@ DG_KIND_DENSE, DG_KIND_CONTIGUOUS, DG_KIND_MASKED = 0, 1, 2
 DG_KIND_BF16_MASKED, DG_KIND_BF16_DENSE, DG_KIND_BF16_CONTIGUOUS = 3, 4, 5
 DG_KIND_DENSE_ROWB, DG_KIND_CONTIGUOUS_ROWB, DG_KIND_MASKED_ROWB = 6, 7, 8  # FP8, one B scale per row of B
 DG_KIND_DENSE_FP8_OUT = 9  # fp8_gemm_nt_fp8_out
+DG_KIND_DENSE_MN = 10  # fp8_gemm_nn / _tn / _tt
 
 ENTRY_POINTS = (
     "dg_last_error",
     "dgmi_init",
     "fp8_gemm_nt",
     "fp8_gemm_nt_fp8_out",
+    "fp8_gemm_nn",
+    "fp8_gemm_tn",
+    "fp8_gemm_tt",
     "m_grouped_fp8_gemm_nt_contiguous",
     "m_grouped_fp8_gemm_nt_masked",
     "m_grouped_bf16_gemm_nt_masked",
@@ -89,6 +93,9 @@ def load_library(path=None):
         "dgmi_init": ([], ctypes.c_int),
         "fp8_gemm_nt": ([T, T, T, T, T, T, vp], ctypes.c_int),
         "fp8_gemm_nt_fp8_out": ([T, T, T, T, T, T, T, ctypes.c_int, vp], ctypes.c_int),
+        "fp8_gemm_nn": ([T, T, T, T, T, T, vp], ctypes.c_int),
+        "fp8_gemm_tn": ([T, T, T, T, T, T, vp], ctypes.c_int),
+        "fp8_gemm_tt": ([T, T, T, T, T, T, vp], ctypes.c_int),
         "m_grouped_fp8_gemm_nt_contiguous": ([T, T, T, T, T, T, vp], ctypes.c_int),
         "m_grouped_fp8_gemm_nt_masked": ([T, T, T, T, T, T, i64, vp], ctypes.c_int),
         "m_grouped_bf16_gemm_nt_masked": ([T, T, T, T, i64, vp], ctypes.c_int),
@@ -175,6 +182,28 @@ def fp8_gemm_nt(a, b, sfa, sfb, c, d, stream=None):
     _check(lib.fp8_gemm_nt(_ref(describe(a)), _ref(describe(b)), _ref(describe(sfa)), _ref(describe(sfb)),
                            _ref(describe(c)), _ref(describe(d)), _stream(stream)))
     return d
+
+
+def _fp8_gemm_layout(name, a, b, sfa, sfb, c, d, stream):
+    lib = load_library()
+    _check(getattr(lib, name)(_ref(describe(a)), _ref(describe(b)), _ref(describe(sfa)), _ref(describe(sfb)),
+                              _ref(describe(c)), _ref(describe(d)), _stream(stream)))
+    return d
+
+
+def fp8_gemm_nn(a, b, sfa, sfb, c, d, stream=None):
+    """d = c + a . b with a [M, K] (K contiguous) and b [K, N] (N contiguous), FP8."""
+    return _fp8_gemm_layout("fp8_gemm_nn", a, b, sfa, sfb, c, d, stream)
+
+
+def fp8_gemm_tn(a, b, sfa, sfb, c, d, stream=None):
+    """d = c + a^T . b with a [K, M] (M contiguous) and b [K, N], FP8."""
+    return _fp8_gemm_layout("fp8_gemm_tn", a, b, sfa, sfb, c, d, stream)
+
+
+def fp8_gemm_tt(a, b, sfa, sfb, c, d, stream=None):
+    """d = c + a^T . b^T with a [K, M] (M contiguous) and b [N, K] (K contiguous), FP8."""
+    return _fp8_gemm_layout("fp8_gemm_tt", a, b, sfa, sfb, c, d, stream)
 
 
 def fp8_gemm_nt_fp8_out(a, b, sfa, sfb, c, q, sfq, use_ue8m0=False, stream=None):

@@ -192,8 +192,16 @@ int fp8_gemm_common(int mode, const dg_tensor* a, const dg_tensor* b, const dg_t
   const bool fp8_out = q != nullptr;
   if (fp8_out) d = q;  // the output operand, for the shape and alias checks
   const char* dname = fp8_out ? "q" : "d";
-  DG_TRY(check_basic(a, "a", true));
-  DG_TRY(check_basic(b, "b", true));
+  // An MN-major operand (dense only) is the transposed view of a row-major
+  // [K, M] or [K, N] tensor: a 2-D descriptor with unit stride along its rows
+  // and its K-row stride in stride[1].
+  auto mn_major = [](const dg_tensor* t) {
+    return t != nullptr && t->ndim == 2 && t->shape[1] > 1 && t->stride[1] != 1 &&
+           (t->shape[0] <= 1 || t->stride[0] == 1);
+  };
+  const bool a_mn = mode == dgmi::MODE_DENSE && mn_major(a), b_mn = mode == dgmi::MODE_DENSE && mn_major(b);
+  DG_TRY(check_basic(a, "a", !a_mn));
+  DG_TRY(check_basic(b, "b", !b_mn));
   DG_TRY(check_basic(d, dname, true));
   DG_TRY(check_dtype(a, "a", DG_E4M3));
   DG_TRY(check_dtype(b, "b", DG_E4M3));
@@ -247,10 +255,21 @@ int fp8_gemm_common(int mode, const dg_tensor* a, const dg_tensor* b, const dg_t
     return fail(DG_UNSUPPORTED, "%s: one B scale per row is not supported with %s output", fname,
                 fp8_out ? "FP8" : "F32");
 
+  // MN-major operands: K-rows of M (N) bytes, 16-byte aligned, ld bytes apart
+  const int64_t lda = a_mn ? a->stride[1] : va.sr, ldb = b_mn ? b->stride[1] : vb.sr;
+  if (a_mn || b_mn) {
+    if (fp8_out || d_f32 || rowb)
+      return fail(DG_UNSUPPORTED, "%s: MN-major operands take block scales and a BF16 d", fname);
+    if ((a_mn && M % 16) || (b_mn && N % 16))
+      return fail(DG_UNSUPPORTED, "%s: an MN-major operand needs its row count (M or N) to be a multiple of 16",
+                  fname);
+    if ((a_mn && (lda < M || lda > (int64_t(1) << 28))) || (b_mn && (ldb < N || ldb > (int64_t(1) << 28))))
+      return fail(DG_UNSUPPORTED, "%s: the K-row stride of an MN-major operand must lie in [rows, 2^28]", fname);
+  }
   // alignment: 16-B operand rows (the kernels load 16-B chunks), 16-B output rows
-  if (!aligned(a->data, 16) || !aligned(b->data, 16) || va.sr % 16 || vb.sr % 16 || va.sg % 16 || vb.sg % 16)
+  if (!aligned(a->data, 16) || !aligned(b->data, 16) || lda % 16 || ldb % 16 || va.sg % 16 || vb.sg % 16)
     return fail(DG_INVALID_ARG, "%s: a and b need 16-byte aligned bases and row/group strides", fname);
-  DG_TRY(check_row_strides(va.sr, vb.sr, fname));
+  DG_TRY(check_row_strides(a_mn ? 0 : lda, b_mn ? 0 : ldb, fname));
   if (fp8_out) {
     // q rows are written in 4-byte words (16-byte stores when 16-byte aligned)
     if (!aligned(d->data, 4) || (M > 1 && N > 0 && vd.sr % 4))
@@ -328,10 +347,12 @@ int fp8_gemm_common(int mode, const dg_tensor* a, const dg_tensor* b, const dg_t
   p.ldc = ldc;
   p.c_f32 = c_f32 ? 1 : 0;
   p.meta = meta ? static_cast<const int32_t*>(meta->data) : nullptr;
-  p.lda = va.sr;
+  p.lda = lda;
   p.a_gs = va.sg;
-  p.ldb = vb.sr;
+  p.ldb = ldb;
   p.b_gs = vb.sg;
+  p.a_mn = a_mn ? 1 : 0;
+  p.b_mn = b_mn ? 1 : 0;
   p.sfa_sm = vsa.sr;
   p.sfa_sk = sfa->stride[sfa->ndim - 1];
   p.sfa_gs = vsa.sg;
@@ -530,6 +551,46 @@ int dgmi_init(void) {
 int fp8_gemm_nt(const dg_tensor* a, const dg_tensor* b, const dg_tensor* sfa, const dg_tensor* sfb,
                 const dg_tensor* c, const dg_tensor* d, hipStream_t stream) {
   return fp8_gemm_common(dgmi::MODE_DENSE, a, b, sfa, sfb, c, d, nullptr, 0, stream, "fp8_gemm_nt");
+}
+
+// The other three layouts: a descriptor given in its stored shape ([K, M]
+// for A, [K, N] for B, row-major) is viewed as its transpose and handed to
+// the common path, which takes the view as MN-major.
+namespace {
+int transposed(const dg_tensor* t, const char* name, const char* fname, dg_tensor* out) {
+  if (t == nullptr) return fail(DG_INVALID_ARG, "%s: %s descriptor is NULL", fname, name);
+  if (t->ndim != 2) return fail(DG_INVALID_ARG, "%s: %s must be 2-D", fname, name);
+  *out = *t;
+  out->shape[0] = t->shape[1];
+  out->shape[1] = t->shape[0];
+  out->stride[0] = t->stride[1];
+  out->stride[1] = t->stride[0];
+  if (t->shape[1] > 1 && t->stride[1] != 1)
+    return fail(DG_INVALID_ARG, "%s: %s must be row-major (innermost stride 1)", fname, name);
+  return DG_OK;
+}
+}  // namespace
+
+int fp8_gemm_nn(const dg_tensor* a, const dg_tensor* b, const dg_tensor* sfa, const dg_tensor* sfb,
+                const dg_tensor* c, const dg_tensor* d, hipStream_t stream) {
+  dg_tensor bt;
+  DG_TRY(transposed(b, "b", "fp8_gemm_nn", &bt));
+  return fp8_gemm_common(dgmi::MODE_DENSE, a, &bt, sfa, sfb, c, d, nullptr, 0, stream, "fp8_gemm_nn");
+}
+
+int fp8_gemm_tn(const dg_tensor* a, const dg_tensor* b, const dg_tensor* sfa, const dg_tensor* sfb,
+                const dg_tensor* c, const dg_tensor* d, hipStream_t stream) {
+  dg_tensor at, bt;
+  DG_TRY(transposed(a, "a", "fp8_gemm_tn", &at));
+  DG_TRY(transposed(b, "b", "fp8_gemm_tn", &bt));
+  return fp8_gemm_common(dgmi::MODE_DENSE, &at, &bt, sfa, sfb, c, d, nullptr, 0, stream, "fp8_gemm_tn");
+}
+
+int fp8_gemm_tt(const dg_tensor* a, const dg_tensor* b, const dg_tensor* sfa, const dg_tensor* sfb,
+                const dg_tensor* c, const dg_tensor* d, hipStream_t stream) {
+  dg_tensor at;
+  DG_TRY(transposed(a, "a", "fp8_gemm_tt", &at));
+  return fp8_gemm_common(dgmi::MODE_DENSE, &at, b, sfa, sfb, c, d, nullptr, 0, stream, "fp8_gemm_tt");
 }
 
 int fp8_gemm_nt_fp8_out(const dg_tensor* a, const dg_tensor* b, const dg_tensor* sfa, const dg_tensor* sfb,
@@ -860,6 +921,9 @@ int dg_query_config(int32_t kind, int64_t G, int64_t M, int64_t N, int64_t K, dg
   } else if (kind == DG_KIND_DENSE_FP8_OUT) {
     mode = dgmi::MODE_DENSE;
     c = dgmi::fp8_out_gemm_plan(M, N);
+  } else if (kind == DG_KIND_DENSE_MN) {
+    mode = dgmi::MODE_DENSE;
+    c = dgmi::fp8_mn_gemm_plan();
   } else if (kind >= DG_KIND_DENSE_ROWB && kind <= DG_KIND_MASKED_ROWB) {
     mode = kind == DG_KIND_DENSE_ROWB ? dgmi::MODE_DENSE
                                       : (kind == DG_KIND_CONTIGUOUS_ROWB ? dgmi::MODE_CONTIG : dgmi::MODE_MASKED);

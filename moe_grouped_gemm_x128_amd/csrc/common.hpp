@@ -53,6 +53,9 @@ struct GemmParams {
   int64_t ldq, sfq_sm, sfq_sn;
   int32_t q_ue8m0;
   int32_t d_f32;  // dense only: d holds F32 (row stride ldd in F32 elements)
+  // dense FP8 only: A / B stored MN-major ([K, M] / [K, N], rows contiguous);
+  // lda / ldb are then the byte strides between consecutive K-rows
+  int32_t a_mn, b_mn;
 };
 
 // Output of a GEMM: BF16 D, D cast per token to FP8, or the FP32 D itself.

@@ -100,6 +100,17 @@ __device__ __host__ constexpr int swz(int r) { return ((r ^ (r >> 3) ^ (r >> 5))
 // Byte offset in a tile of 16-byte chunk c (0..7) of tile row r.
 __device__ __forceinline__ int lds_off(int r, int c) { return r * 128 + ((c ^ swz(r)) << 4); }
 
+// MN-major operands (the operand stored [K, rows], rows contiguous): a stage
+// holds the slice's 128 K-rows of 256 bytes each (the tile's rows, padded to
+// 256), and the 16-byte chunk c of K-row k is stored at slot c ^ hmn(k),
+//   hmn(k) = (k & 7) | ((k >> 5) & 1) << 3.
+// The transposing fragment reads (ds_read_b64_tr_b8) of one 16-lane group
+// touch K-rows 8 apart in an aligned run of 8 at one chunk: (k & 7) spreads
+// them over 8 slots; the two 16-lane groups served together differ in bit 5
+// of k, and the last term puts them on the other half of the banks.
+constexpr int MN_ROW = 256;
+__device__ __host__ constexpr int hmn(int k) { return (k & 7) | (((k >> 5) & 1) << 3); }
+
 template <int BM_, int BN_, int WM_, int WN_, int STAGES_>
 struct TileShape {
   static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, STAGES = STAGES_;
@@ -370,10 +381,24 @@ __device__ __forceinline__ void epilogue_fp8(const GemmParams& p, f32x4 (&acc)[T
   }
 }
 
-template <class T, int KIND, int SF, int MODE, int OUT = OUT_BF16>
+// LAY: bit 0 -- A is MN-major (stored [K, M], rows contiguous), bit 1 -- B is
+// MN-major (stored [K, N]); dense FP8 with BF16 output on tiles whose B
+// fragments keep MFMA column order ("DeepInside DeepGEMM", section 2: the
+// NN, TN and TT layouts besides NT).
+template <class T, int KIND, int SF, int MODE, int OUT = OUT_BF16, int LAY = 0>
 __global__ __launch_bounds__(T::NT) void gemm_kernel(const GemmParams p) {
   constexpr int S = T::STAGES;
   constexpr bool FP8 = KIND == KIND_FP8;
+  constexpr bool A_MN = (LAY & 1) != 0, B_MN = (LAY & 2) != 0;
+  static_assert(LAY == 0 || (FP8 && MODE == MODE_DENSE && OUT == OUT_BF16 && !T::PERM && T::NW == 8 &&
+                             T::BM <= MN_ROW && T::BN <= MN_ROW),
+                "MN-major operands: dense FP8, BF16 output, MFMA column order, 8 waves");
+  // stage bytes and LDS-DMA instructions per wave per stage of each operand
+  // (an MN-major stage is 128 K-rows of 256 bytes: four K-rows per instruction)
+  constexpr int A_STAGE = A_MN ? BK * MN_ROW : T::A_BYTES, B_STAGE = B_MN ? BK * MN_ROW : T::B_BYTES;
+  constexpr int A_LD = A_MN ? BK * MN_ROW / (1024 * T::NW) : T::A_LOADS;
+  constexpr int B_LD = B_MN ? BK * MN_ROW / (1024 * T::NW) : T::B_LOADS;
+  constexpr int LD_ALL = A_LD + B_LD;
   constexpr bool UE8 = FP8 && (SF & SF_UE8M0) != 0;
   // one B scale per row of B ("DeepInside DeepGEMM", section 4: the per-row
   // b_sf of its dense example): the promote scales each output column by
@@ -389,12 +414,12 @@ __global__ __launch_bounds__(T::NT) void gemm_kernel(const GemmParams p) {
   // one array per stage and operand, so that the compiler can tell the
   // LDS-DMA target of one from the fragment reads of another (it would
   // otherwise drain every load in flight before those reads)
-  __shared__ __attribute__((aligned(16))) uint8_t lds_a0[T::A_BYTES];
-  __shared__ __attribute__((aligned(16))) uint8_t lds_a1[T::A_BYTES];
-  __shared__ __attribute__((aligned(16))) uint8_t lds_a2[S > 2 ? T::A_BYTES : 16];
-  __shared__ __attribute__((aligned(16))) uint8_t lds_b0[T::B_BYTES];
-  __shared__ __attribute__((aligned(16))) uint8_t lds_b1[T::B_BYTES];
-  __shared__ __attribute__((aligned(16))) uint8_t lds_b2[S > 2 ? T::B_BYTES : 16];
+  __shared__ __attribute__((aligned(16))) uint8_t lds_a0[A_STAGE];
+  __shared__ __attribute__((aligned(16))) uint8_t lds_a1[A_STAGE];
+  __shared__ __attribute__((aligned(16))) uint8_t lds_a2[S > 2 ? A_STAGE : 16];
+  __shared__ __attribute__((aligned(16))) uint8_t lds_b0[B_STAGE];
+  __shared__ __attribute__((aligned(16))) uint8_t lds_b1[B_STAGE];
+  __shared__ __attribute__((aligned(16))) uint8_t lds_b2[S > 2 ? B_STAGE : 16];
   // FP8: per stage, A row scales in slots [0, BM), B block scales in
   // [BM, BM + NBT); one slot per thread so the stores need no branch
   __shared__ __attribute__((aligned(16))) float ssc[FP8 ? S : 1][FP8 ? T::NT : 1];
@@ -475,14 +500,39 @@ __global__ __launch_bounds__(T::NT) void gemm_kernel(const GemmParams p) {
   const int lrow = lane >> 3, lslot = lane & 7;
   const int a_rows = __builtin_amdgcn_readfirstlane(max(0, min(min(row_lim - m0, hi), T::BM)));
   const int b_rows = __builtin_amdgcn_readfirstlane(max(0, min(p.N - n0, T::BN)));
-  const uint32_t a_vrow = (uint32_t)((wave * 8 + lrow) * p.lda), b_vrow = (uint32_t)((wave * 8 + lrow) * p.ldb);
+  const uint32_t a_vrow = A_MN ? 0u : (uint32_t)((wave * 8 + lrow) * p.lda);
+  const uint32_t b_vrow = B_MN ? 0u : (uint32_t)((wave * 8 + lrow) * p.ldb);
   const uint32_t vchunk = (uint32_t)(lslot ^ lrow);
-  const int a_jstep = T::NW * 8 * (int)p.lda, b_jstep = T::NW * 8 * (int)p.ldb;
+  const int a_jstep = A_MN ? 0 : T::NW * 8 * (int)p.lda, b_jstep = B_MN ? 0 : T::NW * 8 * (int)p.ldb;
   const uint8_t* const a_tile = A + (int64_t)m0 * p.lda;
   const uint8_t* const b_tile = B + (int64_t)n0 * p.ldb;
-  const int a_bytes = a_rows * (int)p.lda, b_bytes = b_rows * (int)p.ldb;
+  const int a_bytes = A_MN ? 0 : a_rows * (int)p.lda, b_bytes = B_MN ? 0 : b_rows * (int)p.ldb;
 
+  // MN-major operand (stored [K, R] with K-rows ld bytes apart, R = M or N):
+  // instruction j fills K-rows [4(j NW + wave), +4) of the stage, lane l the
+  // 16-byte slot l % 16 of K-row 4(j NW + wave) + l / 16, from the tile's
+  // logical chunk (l % 16) ^ hmn(row).  The buffer resource starts at the
+  // instruction's first K-row of slice kb, column r0, and ends after the
+  // operand's last valid byte: past the matrix's last K-row it reads zeros,
+  // and columns past R in earlier K-rows only feed output rows or columns
+  // that are never stored.
+  const int k_rows = KB * BK;
+  auto issue_mn_one = [&](uint8_t* stage, const uint8_t* base, int64_t ld, int r0, int r_valid, int kb, int j) {
+    const int kr = 4 * (j * T::NW + wave);            // first K-row of the instruction in the slice
+    const int krow = kr + (lane >> 4);
+    const uint32_t voff = (uint32_t)((lane >> 4) * ld + (((lane & 15) ^ hmn(krow)) << 4));
+    const int64_t first = (int64_t)kb * BK + kr;      // K-row of the resource's start
+    const int64_t avail = (int64_t)(k_rows - first - 1) * ld + (r_valid - r0);
+    const uint32_t nrec = (uint32_t)max((int64_t)0, min(avail, (int64_t)0x7fffffff));
+    const __amdgpu_buffer_rsrc_t rsrc =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(base + first * ld + r0), (short)0, (int)nrec, 0x00020000);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)(stage + (j * T::NW + wave) * 1024), 16, voff, 0, 0, 0);
+  };
   auto issue_a_one = [&](uint8_t* stage, int kb, int j) {
+    if constexpr (A_MN) {
+      issue_mn_one(stage, A, p.lda, m0, min(row_lim, m0 + hi), kb, j);
+      return;
+    }
     const uint32_t hu = (uint32_t)swz((j * T::NW + wave) * 8);
     const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
         (void*)(a_tile + (int64_t)j * a_jstep), (short)0, max(0, a_bytes - j * a_jstep), 0x00020000);
@@ -490,6 +540,10 @@ __global__ __launch_bounds__(T::NT) void gemm_kernel(const GemmParams p) {
                                              a_vrow + ((vchunk ^ hu) << 4), kb * BK, 0, 0);
   };
   auto issue_b_one = [&](uint8_t* stage, int kb, int j) {
+    if constexpr (B_MN) {
+      issue_mn_one(stage, B, p.ldb, n0, p.N, kb, j);
+      return;
+    }
     const uint32_t hu = (uint32_t)swz((j * T::NW + wave) * 8);
     const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
         (void*)(b_tile + (int64_t)j * b_jstep), (short)0, max(0, b_bytes - j * b_jstep), 0x00020000);
@@ -498,11 +552,11 @@ __global__ __launch_bounds__(T::NT) void gemm_kernel(const GemmParams p) {
   };
   auto issue_a = [&](uint8_t* stage, int kb) {
 #pragma unroll
-    for (int j = 0; j < T::A_LOADS; ++j) issue_a_one(stage, kb, j);
+    for (int j = 0; j < A_LD; ++j) issue_a_one(stage, kb, j);
   };
   auto issue_b = [&](uint8_t* stage, int kb) {
 #pragma unroll
-    for (int j = 0; j < T::B_LOADS; ++j) issue_b_one(stage, kb, j);
+    for (int j = 0; j < B_LD; ++j) issue_b_one(stage, kb, j);
   };
   auto issue_loads = [&](int st, int kb) {
     issue_a(stage_a(st), kb);
@@ -573,7 +627,7 @@ __global__ __launch_bounds__(T::NT) void gemm_kernel(const GemmParams p) {
     __builtin_amdgcn_sched_barrier(0);
   }
   store_sc(0, rs0, 0);
-  __builtin_amdgcn_s_waitcnt(vmcnt_lgkm0((FP8 ? 1 : 0) + (S - 1) * T::LOADS));
+  __builtin_amdgcn_s_waitcnt(vmcnt_lgkm0((FP8 ? 1 : 0) + (S - 1) * LD_ALL));
   __builtin_amdgcn_s_barrier();
 
   // Early point of K-slice kb (start of its second fragment group): every
@@ -597,7 +651,7 @@ __global__ __launch_bounds__(T::NT) void gemm_kernel(const GemmParams p) {
   // counts in issue order).  Loads issued after the tiles of slice kb+1 that
   // may stay in flight: the B tile of slice kb+2 for two stages; the A tile
   // of slice kb+2 and the B tile of slice kb+3 for three.
-  constexpr int LATE_VM = S == 2 ? T::B_LOADS : (S - 2) * T::LOADS;
+  constexpr int LATE_VM = S == 2 ? B_LD : (S - 2) * LD_ALL;
   auto late_sync = [&](int kb, int slot) {
     store_sc(slot, rs, kb + 1);
     __builtin_amdgcn_s_waitcnt(vmcnt_lgkm0(LATE_VM));
@@ -618,18 +672,40 @@ __global__ __launch_bounds__(T::NT) void gemm_kernel(const GemmParams p) {
   auto spread_loads = [&](int i, int f, uint8_t* cur_a, uint8_t* cur_b, int kb) {
     if (i == 1) {
 #pragma unroll
-      for (int j = 0; j < T::B_LOADS; ++j)
+      for (int j = 0; j < B_LD; ++j)
         if (j % T::FN == f) issue_b_one(cur_b, min(kb + S, KB - 1), j);
     }
     if (i + 1 == T::FM) {
 #pragma unroll
-      for (int j = 0; j < T::A_LOADS; ++j)
+      for (int j = 0; j < A_LD; ++j)
         if (j % T::FN == f) issue_a_one(cur_a, min(kb + S, KB - 1), j);
     }
   };
 
   const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+  // MN-major fragment (16 rows from tile row r0, the lane's 32 K-bytes):
+  // four transposing reads.  Lane s of each 16-lane group reads 8 bytes of
+  // K-row 32q + 8t + s/2 (q = lane / 16, t = 0..3) at tile columns
+  // r0 + 8 (s & 1) .. +7; the group's 16 reads, transposed, hand lane s the
+  // bytes of tile row r0 + s at K 32q + 8t .. +7 -- the K-contiguous order of
+  // the MFMA operand.  hmn of those K-rows is (s / 2) | (q & 1) << 3 for all t.
+  const int mn_s = lane & 15, mn_q = lane >> 4;
+  const int mn_h = (mn_s >> 1) | ((mn_q & 1) << 3);
+  const int mn_k0 = (32 * mn_q + (mn_s >> 1)) * MN_ROW + 8 * (mn_s & 1);
+  auto mn_frag = [&](const uint8_t* stage, int r0) {
+    typedef __attribute__((address_space(3))) i32x2 lds_i32x2;
+    const int off = mn_k0 + ((((r0 >> 4) ^ mn_h)) << 4);
+    i32x8 r;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const i32x2 v = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(stage + off + t * 8 * MN_ROW));
+      r[2 * t] = v[0];
+      r[2 * t + 1] = v[1];
+    }
+    return r;
+  };
   auto b_frag = [&](const uint8_t* stage, int f) {
+    if constexpr (B_MN) return mn_frag(stage, wn * T::TN + 16 * f);
     const int off = T::PERM ? (b_base ^ (swz(f * 4) << 4)) + f * 4 * 128  // rows +4f
                             : b_offs[T::PERM ? 0 : f];
     const i32x4 l = *reinterpret_cast<const i32x4*>(stage + off);
@@ -637,6 +713,7 @@ __global__ __launch_bounds__(T::NT) void gemm_kernel(const GemmParams p) {
     return i32x8{l[0], l[1], l[2], l[3], h[0], h[1], h[2], h[3]};
   };
   auto a_frag = [&](const uint8_t* stage, int i) {
+    if constexpr (A_MN) return mn_frag(stage, wm * T::TM + 16 * i);
     const int off = (a_base ^ (swz(i * 16) << 4)) + i * 16 * 128;  // rows +16i
     const i32x4 l = *reinterpret_cast<const i32x4*>(stage + off);
     const i32x4 h = *reinterpret_cast<const i32x4*>(stage + (off ^ 16));
@@ -1235,7 +1312,44 @@ int64_t plan_grid(const GemmPlan& plan, int part, int mode, int64_t G, int64_t M
   return gemm_grid(plan.cfg[part], mode, G, M, n_len);
 }
 
+// Dense FP8 GEMM with an MN-major A and/or B: one launch of the 256 x 192
+// tile, whose 48-column wave tiles keep the MFMA's column order (the
+// transposing B fragment reads hand each 8-lane run 8 consecutive columns,
+// which the permuted order of the 64-column wave tiles does not keep).
+GemmPlan fp8_mn_gemm_plan() {
+  GemmPlan p;
+  p.parts = 1;
+  p.n_split = 0;
+  p.cfg[0] = make_cfg<TileN, KIND_FP8>(VAR_N);
+  p.cfg[0].lds_bytes = 2 * 2 * BK * MN_ROW + 2 * TileN::NT * 4;  // both operands MN-major (the largest)
+  return p;
+}
+
+hipError_t launch_fp8_gemm_mn(GemmParams p, int sf_fmt, hipStream_t stream) {
+  p.tiles_m = (p.M + TileN::BM - 1) / TileN::BM;
+  p.tiles_n = (p.N + TileN::BN - 1) / TileN::BN;
+  const dim3 g((unsigned)((int64_t)p.tiles_m * p.tiles_n)), b(TileN::NT);
+  const int lay = (p.a_mn ? 1 : 0) | (p.b_mn ? 2 : 0);
+  const bool ue8 = sf_fmt == SF_UE8M0;
+  if (sf_fmt != SF_F32 && sf_fmt != SF_UE8M0) return hipErrorInvalidValue;
+#define DGMI_LAUNCH_MN(LAY_)                                                                                   \
+  do {                                                                                                         \
+    if (ue8) gemm_kernel<TileN, KIND_FP8, SF_UE8M0, MODE_DENSE, OUT_BF16, LAY_><<<g, b, 0, stream>>>(p);     \
+    else gemm_kernel<TileN, KIND_FP8, SF_F32, MODE_DENSE, OUT_BF16, LAY_><<<g, b, 0, stream>>>(p);           \
+  } while (0)
+  if (lay == 1) DGMI_LAUNCH_MN(1);
+  else if (lay == 2) DGMI_LAUNCH_MN(2);
+  else if (lay == 3) DGMI_LAUNCH_MN(3);
+  else return hipErrorInvalidValue;
+#undef DGMI_LAUNCH_MN
+  return hipGetLastError();
+}
+
 hipError_t launch_fp8_gemm(GemmParams p, int mode, int sf_fmt, hipStream_t stream) {
+  if (p.a_mn || p.b_mn) {
+    if (mode != MODE_DENSE || p.d_f32) return hipErrorInvalidValue;
+    return launch_fp8_gemm_mn(p, sf_fmt, stream);
+  }
   return launch_plan<KIND_FP8>(fp8_gemm_plan(mode, p.G, p.M, p.N, p.k_bytes, sf_fmt), p, mode, sf_fmt, stream);
 }
 

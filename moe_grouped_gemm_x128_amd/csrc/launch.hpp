@@ -113,8 +113,11 @@ GemmPlan fp8_gemm_plan(int mode, int64_t G, int64_t M, int64_t N, int64_t K, int
 GemmPlan bf16_gemm_plan(int mode, int64_t G, int64_t M, int64_t N, int64_t K);
 int64_t gemm_grid(const TileCfg& cfg, int mode, int64_t G, int64_t M, int64_t N);
 int64_t plan_grid(const GemmPlan& plan, int part, int mode, int64_t G, int64_t M, int64_t N);
-// sf_fmt: SF_F32 or SF_UE8M0, plus SF_ROWB for one B scale per row of B
+// sf_fmt: SF_F32 or SF_UE8M0, plus SF_ROWB for one B scale per row of B;
+// an MN-major A or B (p.a_mn, p.b_mn: dense, block scales, BF16 d) takes the
+// plan of fp8_mn_gemm_plan
 hipError_t launch_fp8_gemm(GemmParams p, int mode, int sf_fmt, hipStream_t stream);
+GemmPlan fp8_mn_gemm_plan();
 // Dense FP8 GEMM whose output D is cast per token to FP8 (p.q, p.sfq) in the
 // epilogue; block scales only (sf_fmt SF_F32 or SF_UE8M0).
 GemmPlan fp8_out_gemm_plan(int64_t M, int64_t N);

@@ -52,8 +52,11 @@ from .formats import (
 from .quant import per_token_cast_to_fp8, per_block_cast_to_fp8, pack_ue8m0_to_int, AMAX_FLOOR
 from .gemm import (
     bf16_gemm_nt,
+    fp8_gemm_nn,
     fp8_gemm_nt,
     fp8_gemm_nt_fp8_out,
+    fp8_gemm_tn,
+    fp8_gemm_tt,
     m_grouped_bf16_gemm_nt_contiguous,
     m_grouped_fp8_gemm_nt_contiguous,
     m_grouped_fp8_gemm_nt_masked,
@@ -75,8 +78,11 @@ __all__ = [
     "pack_ue8m0_to_int",
     "bf16_gemm_nt",
     "m_grouped_bf16_gemm_nt_contiguous",
+    "fp8_gemm_nn",
     "fp8_gemm_nt",
     "fp8_gemm_nt_fp8_out",
+    "fp8_gemm_tn",
+    "fp8_gemm_tt",
     "m_grouped_fp8_gemm_nt_contiguous",
     "m_grouped_fp8_gemm_nt_masked",
     "m_grouped_bf16_gemm_nt_masked",

@@ -29,8 +29,9 @@ values) is exact in float64.  Only the final multiply and the sum over
 blocks round, at float64 precision.
 
 Pins: tests/test_oracle_gemm.py (pure-Python brute force on tiny shapes,
-the closed form for one-hot B with power-of-two scales, numpy float64
-matmul when every scale is 1, and the masked/contiguous invariants).
+also for the NN / TN / TT storage layouts, the closed form for one-hot B
+with power-of-two scales, numpy float64 matmul when every scale is 1, and
+the masked/contiguous invariants).
 """
 
 import numpy as np
@@ -77,6 +78,24 @@ def fp8_gemm_nt(a, b, sfa, sfb, c=None):
     if c is not None:
         D = D + np.asarray(c, dtype=np.float64)
     return D
+
+
+def fp8_gemm_nn(a, b_kn, sfa, sfb, c=None):
+    """The NN layout ("DeepInside DeepGEMM", section 2: NT, NN, TN and TT):
+    A stored [M, K], B stored [K, N]; D[m, n] = C + sum_k A[m, k] B[k, n] with
+    the same block scales (sfa per row of A and 128-wide K-block, sfb per
+    128 columns of D and K-block)."""
+    return fp8_gemm_nt(a, np.asarray(b_kn).T, sfa, sfb, c)
+
+
+def fp8_gemm_tn(a_km, b_kn, sfa, sfb, c=None):
+    """The TN layout: A stored [K, M], B stored [K, N]."""
+    return fp8_gemm_nt(np.asarray(a_km).T, np.asarray(b_kn).T, sfa, sfb, c)
+
+
+def fp8_gemm_tt(a_km, b, sfa, sfb, c=None):
+    """The TT layout: A stored [K, M], B stored [N, K]."""
+    return fp8_gemm_nt(np.asarray(a_km).T, b, sfa, sfb, c)
 
 
 def fp8_gemm_nt_fp8_out(a, b, sfa, sfb, c=None, use_ue8m0=False):

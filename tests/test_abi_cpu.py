@@ -93,7 +93,7 @@ def test_query_config_is_a_pure_function_of_shapes(lib):
     # 256-row contiguous tiles launch a second grid copy for tiles split between two groups
     assert c["grid"] == (2 * tiles if c["block_m"] == 256 else tiles) and bc["grid"] == c["grid"]
     with pytest.raises(binding.DgmiError):
-        binding.query_config(10, 1, 1, 1, 1)
+        binding.query_config(11, 1, 1, 1, 1)  # no such kind
 
 
 @pytest.mark.parametrize("M,N,tile", [
@@ -223,6 +223,44 @@ def test_dense_validation_errors(lib):
     wide = _t((2, K), torch.uint8, stride=(1 << 23, 1))
     assert _call_dense(lib, wide, b, _t((2, K // 128), torch.float32), sfb, _t((2, N), torch.bfloat16)) == binding.DG_UNSUPPORTED
     assert "row strides" in binding.last_error()
+
+
+def test_mn_major_validation_errors(lib):
+    """fp8_gemm_nn / _tn / _tt: stored operands row-major; an MN-major operand
+    needs rows % 16 == 0, a K-row stride in [rows, 2^28] that is a multiple
+    of 16, block scales and a BF16 d."""
+    D = binding.describe
+    M, N, K = 128, 256, 512
+    a, a_st = _t((M, K), torch.uint8), _t((K, M), torch.uint8)
+    b, b_st = _t((N, K), torch.uint8), _t((K, N), torch.uint8)
+    sfa = _t((M, K // 128), torch.float32)
+    sfb = _t((N // 128, K // 128), torch.float32)
+    d = _t((M, N), torch.bfloat16)
+
+    def call(name, a, b, sfb=sfb, d=d, sfa=sfa):
+        return getattr(lib, name)(ctypes.byref(D(a)), ctypes.byref(D(b)), ctypes.byref(D(sfa)), ctypes.byref(D(sfb)),
+                                  None, ctypes.byref(D(d)), None)
+
+    # stored operands that are not row-major
+    assert call("fp8_gemm_nn", a, b_st.t()) == binding.DG_INVALID_ARG
+    assert call("fp8_gemm_tt", a_st.t(), b) == binding.DG_INVALID_ARG
+    # rows not a multiple of 16
+    a20 = _t((K, 120), torch.uint8)
+    assert call("fp8_gemm_tn", a20, b_st, sfa=_t((120, K // 128), torch.float32),
+                d=_t((120, N), torch.bfloat16)) == binding.DG_UNSUPPORTED
+    assert "multiple of 16" in binding.last_error()
+    # one B scale per row, F32 d: unsupported with an MN-major operand
+    assert call("fp8_gemm_nn", a, b_st, sfb=_t((N, K // 128), torch.float32)) == binding.DG_UNSUPPORTED
+    assert call("fp8_gemm_nn", a, b_st, d=_t((M, N), torch.float32)) == binding.DG_UNSUPPORTED
+    # K-row stride below the row count, and not a multiple of 16
+    short = _t((K, N), torch.uint8, stride=(N - 16, 1))
+    assert call("fp8_gemm_nn", a, short) == binding.DG_UNSUPPORTED
+    odd = _t((K, N + 8), torch.uint8)[:, :N]
+    assert call("fp8_gemm_nn", a, odd) == binding.DG_INVALID_ARG
+    assert "aligned" in binding.last_error()
+    # shape mismatches
+    assert call("fp8_gemm_tn", a_st, _t((K + 128, N), torch.uint8)) == binding.DG_INVALID_ARG
+    assert call("fp8_gemm_tt", _t((K, M + 16), torch.uint8), b) == binding.DG_INVALID_ARG
 
 
 def test_masked_validation_errors(lib):

@@ -88,16 +88,27 @@ def _abs_fp8(codes):
     return np.asarray(codes, dtype=np.uint8) & np.uint8(0x7F)
 
 
-# dense FP8 plans: 128-row tiles (N <= 128 and above), the 256 x 192 tile
-# (one launch below a round of tiles) and a whole round of 256 x 256 tiles
+# dense FP8 plans: 128-row tiles (N <= 128 and above), 192 x 192 tiles (one
+# round of them), one round of 256 x 192 tiles (4096 x 2880) and a whole
+# round of 256 x 256 tiles (4000 x 4000); _expect_tiles checks each
 FP8_SHAPES = [(128, 256, 512), (64, 100, 256), (1, 130, 128), (200, 300, 384), (257, 64, 256), (64, 2112, 1024),
-              (4000, 4000, 256)]
+              (4096, 2880, 256), (4000, 4000, 256)]
+
+
+def _expect_tiles(M, N, K):
+    from moe_grouped_gemm_x128_amd import binding
+
+    c = binding.query_config(binding.DG_KIND_DENSE, 1, M, N, K)
+    want = {(4096, 2880): (256, 192), (4000, 4000): (256, 256)}.get((M, N), (192, 192) if M > 128 else None)
+    if want is not None:
+        assert (c["block_m"], c["block_n"], c["block_n2"]) == want + (0,), c
 
 
 @pytest.mark.parametrize("M,N,K", FP8_SHAPES)
 def test_fp8_dense_f32_out(M, N, K):
     say(f"fp8_gemm_nt F32 d M={M} N={N} K={K}")
     mg = _mg()
+    _expect_tiles(M, N, K)
     xa = synth.normal_f32(701, (M, K))
     xb = synth.normal_f32(702, (N, K))
     a, sfa = q_tok(to_dev(xa))
@@ -118,10 +129,11 @@ def test_fp8_dense_f32_out(M, N, K):
     assert_f32_close(to_host(d), ref, S, K // 128, f"fp8 F32 d {M}x{N}x{K}")
 
 
-@pytest.mark.parametrize("M,N,K", [(192, 384, 1024), (4000, 4000, 512)])
+@pytest.mark.parametrize("M,N,K", [(192, 384, 1024), (4096, 2880, 512), (4000, 4000, 512)])
 def test_fp8_dense_f32_out_packed_ue8m0(M, N, K):
     say(f"fp8_gemm_nt F32 d, packed UE8M0 scales M={M} N={N} K={K}")
     mg = _mg()
+    _expect_tiles(M, N, K)
     xa = synth.normal_f32(711, (M, K))
     xb = synth.normal_f32(712, (N, K))
     a, sfa = q_tok(to_dev(xa), True)
@@ -143,12 +155,13 @@ def test_fp8_dense_f32_out_packed_ue8m0(M, N, K):
     assert_f32_close(to_host(d), ref, S, K // 128, f"fp8 F32 d UE8M0 {M}x{N}x{K}")
 
 
-@pytest.mark.parametrize("M,N,K", [(200, 300, 384), (64, 2112, 512), (4000, 4000, 256)])
+@pytest.mark.parametrize("M,N,K", [(200, 300, 384), (64, 2112, 512), (4096, 2880, 256), (4000, 4000, 256)])
 def test_fp8_dense_f32_accumulate_in_place(M, N, K):
     """d = C first, then d += A . B^T twice with c = d (the in-place
     accumulation of an FP32 output): d = C + 2 A . B^T."""
     say(f"fp8_gemm_nt F32 in-place accumulate M={M} N={N} K={K}")
     mg = _mg()
+    _expect_tiles(M, N, K)
     xa = synth.normal_f32(721, (M, K))
     xb = synth.normal_f32(722, (N, K))
     xc = synth.normal_f32(723, (M, N)) * np.float32(8.0)

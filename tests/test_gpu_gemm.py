@@ -98,7 +98,7 @@ def test_dense_full_compare(M, N, K):
     assert_bf16_close(to_host(d), ref, f"dense {M}x{N}x{K}")
 
 
-@pytest.mark.parametrize("M,N,K", [(192, 384, 1024), (PLAN_L[0], PLAN_L[1], 512)])
+@pytest.mark.parametrize("M,N,K", [(192, 384, 1024), (PLAN_N[0], PLAN_N[1], 512), (PLAN_L[0], PLAN_L[1], 512)])
 def test_dense_ue8m0_packed_scales(M, N, K):
     say(f"fp8_gemm_nt UE8M0 packed scales M={M} N={N} K={K}")
     mg = _mg()
@@ -186,13 +186,15 @@ def test_dense_v3_shapes_sampled(i):
         assert_bf16_close(dh[rows][:, cols], ref, f"dense {M}x{N}x{K} col block {nb}")
 
 
-@pytest.mark.parametrize("M,N,K", [(200, 300, 384), (64, 2112, 1024), (130, 130, 256), PLAN_L])
+@pytest.mark.parametrize("M,N,K", [(200, 300, 384), (64, 2112, 1024), (130, 130, 256), PLAN_N, PLAN_L])
 @pytest.mark.parametrize("c_kind", ["bf16", "f32", "inplace"])
 def test_dense_accumulate_c(M, N, K, c_kind):
     """D = C + A . B^T ("DeepInside DeepGEMM", section 4): C in BF16 or FP32,
-    with a padded row stride, or C being d itself."""
+    with a padded row stride, or C being d itself; on every launch plan
+    (128-row, 192 x 192, 256 x 192 and 256 x 256 tiles)."""
     say(f"fp8_gemm_nt accumulate M={M} N={N} K={K} c={c_kind}")
     mg = _mg()
+    _expect_plan("DG_KIND_DENSE", M, N, K)
     xa = synth.normal_f32(171, (M, K))
     xb = synth.normal_f32(172, (N, K))
     xc = synth.normal_f32(173, (M, N)) * np.float32(8.0)
@@ -223,13 +225,16 @@ def test_dense_accumulate_c(M, N, K, c_kind):
 
 def test_dense_row_stride_at_the_32bit_offset_limit():
     """A and B as row views of buffers whose row stride is the largest the
-    library takes (8 MiB - 16 bytes): a 256-row tile then spans just under
-    2^31 bytes of 32-bit buffer offsets; the next stride up is rejected."""
+    library takes (8 MiB - 16 bytes), on the dense plan's 192 x 192 tiles;
+    the next stride up is rejected.  (The 256-row tiles, which reach just
+    under 2^31 bytes of 32-bit buffer offsets at this stride, are covered by
+    the masked form below.)"""
     say("fp8_gemm_nt row stride 8 MiB - 16")
     mg = _mg()
     from moe_grouped_gemm_x128_amd import binding
 
     M, N, K = 300, 272, 256
+    _expect_plan("DG_KIND_DENSE", M, N, K)
     ld = (1 << 23) - 16
     xa = synth.normal_f32(161, (M, K))
     xb = synth.normal_f32(162, (N, K))
@@ -251,6 +256,41 @@ def test_dense_row_stride_at_the_32bit_offset_limit():
     wide = abuf.as_strided((2, K), (ld + 16, 1))
     with pytest.raises(binding.DgmiError):
         mg.fp8_gemm_nt(wide, b, sfa[:2], sfb, None, d[:2])
+    del abuf, bbuf
+
+
+def test_masked_row_stride_at_the_32bit_offset_limit():
+    """The masked form (one expert, 300 rows, all valid) with A and B rows
+    8 MiB - 16 bytes apart: its 256-row tiles span 256 such rows, just under
+    2^31 bytes of the 32-bit buffer offsets the tile loads use."""
+    say("m_grouped_fp8_gemm_nt_masked row stride 8 MiB - 16, 256-row tiles")
+    mg = _mg()
+    from moe_grouped_gemm_x128_amd import binding
+
+    G, max_m, N, K = 1, 300, 272, 256
+    c = binding.query_config(binding.DG_KIND_MASKED, G, max_m, N, K)
+    assert c["block_m"] == 256, c
+    ld = (1 << 23) - 16
+    xa = synth.normal_f32(163, (max_m, K))
+    xb = synth.normal_f32(164, (N, K))
+    a_c, sfa = q_tok(to_dev(xa))
+    b_c, sfb = q_blk(to_dev(xb))
+    abuf = torch.zeros(max_m * ld, dtype=torch.uint8, device="cuda")
+    bbuf = torch.zeros(N * ld, dtype=torch.uint8, device="cuda")
+    a = abuf.as_strided((G, max_m, K), (max_m * ld, ld, 1))
+    b = bbuf.as_strided((G, N, K), (N * ld, ld, 1))
+    a[0].copy_(a_c)
+    b[0].copy_(b_c)
+    sfa3 = sfa.contiguous().view(G, max_m, K // 128)
+    sfb3 = sfb.view(G, -(-N // 128), K // 128)
+    d = sentinel_like((G, max_m, N))
+    mm = torch.tensor([max_m], dtype=torch.int32, device="cuda")
+    mg.m_grouped_fp8_gemm_nt_masked(a, b, sfa3, sfb3, d, mm, max_m)
+    torch.cuda.synchronize()
+    ra, rsfa = oracle.per_token_cast_to_fp8(xa)
+    rb, rsfb = oracle.per_block_cast_to_fp8(xb)
+    assert np.array_equal(to_host(a_c), ra) and np.array_equal(to_host(b_c), rb)
+    assert_bf16_close(to_host(d)[0], oracle.fp8_gemm_nt(ra, rb, rsfa, rsfb), "masked row stride 8 MiB - 16")
     del abuf, bbuf
 
 

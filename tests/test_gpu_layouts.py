@@ -102,3 +102,115 @@ def test_gemm_layouts_through_the_casts(layout):
     rb, rsfb = oracle.per_block_cast_to_fp8(xb)
     assert np.array_equal(to_host(a), ra) and np.array_equal(to_host(b), rb)
     assert_bf16_close(to_host(d), oracle.fp8_gemm_nt(ra, rb, rsfa, rsfb), f"{layout} GEMM")
+
+
+# ---------------------------------------------------------------------------
+# NN, TN and TT on operands already in FP8 and stored MN-major: the GEMM reads
+# them itself (transposing LDS reads), with results equal to fp8_gemm_nt's on
+# the same values bit for bit
+# ---------------------------------------------------------------------------
+
+def _stored_mn(codes_dev, pad=0):
+    """The K-major codes [R, K] stored MN-major: a row-major [K, R + pad]
+    buffer whose first R columns hold the transpose; returns the [K, R] view."""
+    R, K = codes_dev.shape
+    buf = torch.full((K, R + pad), 0x7F, dtype=torch.uint8, device="cuda")  # NaN codes in the padding
+    buf[:, :R] = codes_dev.t()
+    return buf[:, :R]
+
+
+def _run_layout(mg, layout, a, b, a_st, b_st, sfa, sfb, c, d):
+    if layout == "NN":
+        mg.fp8_gemm_nn(a, b_st, sfa, sfb, c, d)
+    elif layout == "TN":
+        mg.fp8_gemm_tn(a_st, b_st, sfa, sfb, c, d)
+    else:
+        mg.fp8_gemm_tt(a_st, b, sfa, sfb, c, d)
+
+
+@pytest.mark.parametrize("M,N,K", [(128, 256, 512), (272, 208, 384), (64, 96, 256), (16, 16, 128), (528, 400, 1152),
+                                   (1024, 960, 2048)])
+@pytest.mark.parametrize("layout", ["NN", "TN", "TT"])
+def test_fp8_gemm_mn_major_operands(M, N, K, layout):
+    say(f"fp8_gemm_{layout.lower()} MN-major FP8 operands M={M} N={N} K={K}")
+    mg = _mg()
+    from moe_grouped_gemm_x128_amd import binding
+
+    c = binding.query_config(binding.DG_KIND_DENSE_MN, 1, M, N, K)
+    assert (c["block_m"], c["block_n"], c["block_n2"]) == (256, 192, 0)
+    xa = synth.normal_f32(821, (M, K))
+    xb = synth.normal_f32(822, (N, K))
+    a = torch.empty((M, K), dtype=torch.uint8, device="cuda")
+    sfa = torch.empty((K // 128, M), dtype=torch.float32, device="cuda").t()
+    b = torch.empty((N, K), dtype=torch.uint8, device="cuda")
+    sfb = torch.empty((-(-N // 128), K // 128), dtype=torch.float32, device="cuda")
+    mg.per_token_cast_to_fp8(to_dev(xa), a, sfa)
+    mg.per_block_cast_to_fp8(to_dev(xb), b, sfb)
+    a_st = _stored_mn(a, pad=16 if M % 32 else 0)
+    b_st = _stored_mn(b, pad=48)
+    d = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    _run_layout(mg, layout, a, b, a_st, b_st, sfa, sfb, None, d)
+    dref = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    mg.fp8_gemm_nt(a, b, sfa, sfb, None, dref)
+    torch.cuda.synchronize()
+    assert torch.equal(d.view(torch.int16), dref.view(torch.int16)), "differs from fp8_gemm_nt on the same values"
+    ra, rsfa = oracle.per_token_cast_to_fp8(xa)
+    rb, rsfb = oracle.per_block_cast_to_fp8(xb)
+    assert np.array_equal(to_host(a), ra) and np.array_equal(to_host(b), rb)
+    assert_bf16_close(to_host(d), oracle.fp8_gemm_nt(ra, rb, rsfa, rsfb), f"{layout} FP8 {M}x{N}x{K}")
+
+
+@pytest.mark.parametrize("layout", ["NN", "TN", "TT"])
+def test_fp8_gemm_mn_major_ue8m0_and_accumulate(layout):
+    """Packed UE8M0 scales, and D = C + A . B^T with a BF16 C, on MN-major operands."""
+    M, N, K = 400, 336, 1024
+    say(f"fp8_gemm_{layout.lower()} UE8M0 + accumulate M={M} N={N} K={K}")
+    mg = _mg()
+    xa = synth.normal_f32(831, (M, K))
+    xb = synth.normal_f32(832, (N, K))
+    xc = synth.normal_f32(833, (M, N)) * np.float32(4.0)
+    a = torch.empty((M, K), dtype=torch.uint8, device="cuda")
+    sfa = torch.empty((M, K // 128), dtype=torch.float32, device="cuda")
+    b = torch.empty((N, K), dtype=torch.uint8, device="cuda")
+    sfb = torch.empty((-(-N // 128), K // 128), dtype=torch.float32, device="cuda")
+    mg.per_token_cast_to_fp8(to_dev(xa), a, sfa, True)
+    mg.per_block_cast_to_fp8(to_dev(xb), b, sfb, True)
+    pa = torch.empty((M, K // 512), dtype=torch.int32, device="cuda")
+    pb = torch.empty((-(-N // 128), K // 512), dtype=torch.int32, device="cuda")
+    mg.pack_ue8m0_to_int(sfa, pa)
+    mg.pack_ue8m0_to_int(sfb, pb)
+    cbits = synth.bf16_bits_from_f32(xc)
+    c = to_dev(cbits.view(np.int16)).view(torch.bfloat16)
+    a_st, b_st = _stored_mn(a), _stored_mn(b, pad=16)
+    d = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    _run_layout(mg, layout, a, b, a_st, b_st, pa, pb, c, d)
+    dref = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    mg.fp8_gemm_nt(a, b, pa, pb, c, dref)
+    torch.cuda.synchronize()
+    assert torch.equal(d.view(torch.int16), dref.view(torch.int16)), "differs from fp8_gemm_nt on the same values"
+    ra, rsfa = oracle.per_token_cast_to_fp8(xa, True)
+    rb, rsfb = oracle.per_block_cast_to_fp8(xb, True)
+    ref = oracle.fp8_gemm_nt(ra, rb, rsfa, rsfb, c=oracle.bf16_decode(cbits))
+    assert_bf16_close(to_host(d), ref, f"{layout} FP8 UE8M0 + C")
+
+
+def test_fp8_gemm_nt_takes_transposed_views():
+    """fp8_gemm_nt itself takes an MN-major operand given as the transposed
+    view of a row-major [K, R] tensor (both operands here)."""
+    M, N, K = 208, 592, 640
+    say(f"fp8_gemm_nt on transposed views M={M} N={N} K={K}")
+    mg = _mg()
+    xa = synth.normal_f32(841, (M, K))
+    xb = synth.normal_f32(842, (N, K))
+    a = torch.empty((M, K), dtype=torch.uint8, device="cuda")
+    sfa = torch.empty((K // 128, M), dtype=torch.float32, device="cuda").t()
+    b = torch.empty((N, K), dtype=torch.uint8, device="cuda")
+    sfb = torch.empty((-(-N // 128), K // 128), dtype=torch.float32, device="cuda")
+    mg.per_token_cast_to_fp8(to_dev(xa), a, sfa)
+    mg.per_block_cast_to_fp8(to_dev(xb), b, sfb)
+    d = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    mg.fp8_gemm_nt(_stored_mn(a).t(), _stored_mn(b, pad=32).t(), sfa, sfb, None, d)
+    dref = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    mg.fp8_gemm_nt(a, b, sfa, sfb, None, dref)
+    torch.cuda.synchronize()
+    assert torch.equal(d.view(torch.int16), dref.view(torch.int16))

@@ -402,3 +402,20 @@ def test_fp8_out_scale_is_the_block_maximum():
         assert np.all(np.any((q[:, kb * 128:(kb + 1) * 128] & 0x7F) == 0x7E, axis=1))
     s = np.repeat(sf.astype(np.float64), 128, axis=1)[:, :N]
     assert np.all(np.abs(deq - D) <= 2.0 ** -4 * np.abs(D) * (1 + 2.0 ** -7) + 2.0 ** -10 * s + 2.0 ** -8 * np.abs(D))
+
+
+@pytest.mark.parametrize("layout", ["nn", "tn", "tt"])
+def test_storage_layouts_match_brute_force(layout):
+    """NN / TN / TT: the oracle reads A stored [K, M] ('t' first) and B stored
+    [K, N] ('n' second); the brute force indexes the logical A[m, k], B[n, k]
+    of the same codes, element by element."""
+    M, N, K = 5, 7, 256
+    rng = np.random.default_rng(61)
+    a = rng.integers(0, 0x7F, size=(M, K)).astype(np.uint8) | (rng.integers(0, 2, size=(M, K)).astype(np.uint8) << 7)
+    b = rng.integers(0, 0x7F, size=(N, K)).astype(np.uint8) | (rng.integers(0, 2, size=(N, K)).astype(np.uint8) << 7)
+    sfa = rng.uniform(0.5, 2.0, size=(M, 2))
+    sfb = rng.uniform(0.5, 2.0, size=(1, 2))
+    a_st = np.ascontiguousarray(a.T) if layout[0] == "t" else a
+    b_st = np.ascontiguousarray(b.T) if layout[1] == "n" else b
+    got = getattr(oracle, f"fp8_gemm_{layout}")(a_st, b_st, sfa, sfb)
+    assert _close(got, _brute(a, b, sfa, sfb))
