@@ -157,7 +157,8 @@ int fp8_gemm_nt_fp8_out(const dg_tensor* a, const dg_tensor* b, const dg_tensor*
  *   b   E4M3 [G, N, K]
  *   sfa as fp8_gemm_nt with M = Msum;  sfb [G, ceil(N/128), ...] or, one
  *       per row of B, [G, N, ...]
- *   d   BF16 [Msum, N]
+ *   d   BF16 [Msum, N], or F32 [Msum, N] (4-B aligned): the FP32
+ *       accumulator stored without rounding (block scales of B only)
  *   grouped_layout I32 [Msum/128] on the device: group id of each 128-row
  *       block; a negative id marks a block to skip (its rows of d are not
  *       written).  Ids >= G are treated as skipped as well.
@@ -175,7 +176,9 @@ int m_grouped_fp8_gemm_nt_contiguous(const dg_tensor* a, const dg_tensor* b,
  *   sfa F32 [G, max_m, K/128] (or [G*max_m, K/128]) or packed I32
  *   sfb F32 [G, ceil(N/128), K/128] or packed I32 (or one per row of B:
  *       [G, N, ...])
- *   d   BF16 [G, max_m, N] (or [G*max_m, N])
+ *   d   BF16 [G, max_m, N] (or [G*max_m, N]), or F32 of that shape (4-B
+ *       aligned): the FP32 accumulator stored without rounding (block scales
+ *       of B only)
  *   masked_m I32 [G] on the device: group g computes its first
  *       clamp(masked_m[g], 0, max_m) rows; every other row of d is left
  *       untouched.  Read only by the kernels, never by the host.
@@ -185,6 +188,26 @@ int m_grouped_fp8_gemm_nt_masked(const dg_tensor* a, const dg_tensor* b,
                                  const dg_tensor* sfa, const dg_tensor* sfb,
                                  const dg_tensor* d, const dg_tensor* masked_m,
                                  int64_t max_m_per_group, hipStream_t stream);
+
+/*
+ * The two grouped FP8 GEMMs in the accumulate form D = C + A . B^T of
+ * fp8_gemm_nt ("DeepInside DeepGEMM", section 4), the other arguments as
+ * above.  c is BF16 or F32 with d's shape ([Msum, N]; [G, max_m, N] or
+ * [G*max_m, N]), innermost stride 1, element-aligned; each element of C is
+ * added to the FP32 accumulator before d is rounded (BF16) or stored (F32).
+ * c may be d itself (same base, dtype and strides: an in-place D += A . B^T);
+ * any other overlap with d is rejected.  Rows that are not computed (skipped
+ * blocks, rows past masked_m) are neither read from c nor written to d.
+ */
+int m_grouped_fp8_gemm_nt_contiguous_acc(const dg_tensor* a, const dg_tensor* b,
+                                         const dg_tensor* sfa, const dg_tensor* sfb,
+                                         const dg_tensor* c, const dg_tensor* d,
+                                         const dg_tensor* grouped_layout, hipStream_t stream);
+int m_grouped_fp8_gemm_nt_masked_acc(const dg_tensor* a, const dg_tensor* b,
+                                     const dg_tensor* sfa, const dg_tensor* sfb,
+                                     const dg_tensor* c, const dg_tensor* d,
+                                     const dg_tensor* masked_m, int64_t max_m_per_group,
+                                     hipStream_t stream);
 
 /*
  * Masked grouped BF16 GEMM, argument order of the pages' capture example

@@ -206,7 +206,7 @@ int fp8_gemm_common(int mode, const dg_tensor* a, const dg_tensor* b, const dg_t
   DG_TRY(check_dtype(a, "a", DG_E4M3));
   DG_TRY(check_dtype(b, "b", DG_E4M3));
   // d: BF16, or F32 for the dense GEMM (the FP32 accumulator stored as is)
-  const bool d_f32 = !fp8_out && mode == dgmi::MODE_DENSE && d->dtype == DG_F32;
+  const bool d_f32 = !fp8_out && d->dtype == DG_F32;
   DG_TRY(check_dtype(d, dname, fp8_out ? DG_E4M3 : (d_f32 ? DG_F32 : DG_BF16)));
   if (sfa == nullptr || sfb == nullptr) return fail(DG_INVALID_ARG, "%s: scale descriptors must not be NULL", fname);
   if (sfa->dtype != sfb->dtype) return fail(DG_INVALID_ARG, "%s: sfa and sfb must have the same dtype", fname);
@@ -310,21 +310,30 @@ int fp8_gemm_common(int mode, const dg_tensor* a, const dg_tensor* b, const dg_t
     DG_TRY(check_no_alias(sfq, "sfq", q, "q"));
     DG_TRY(check_no_alias(sfq, "sfq", c, "c"));
   }
-  // accumulate input (dense form only): D = C + A . B^T, C BF16 or F32 [M, N];
-  // c may be d itself (same base and strides), any other overlap is rejected
+  // accumulate input: D = C + A . B^T, C BF16 or F32 with d's shape ([M, N],
+  // [Msum, N], or [G, max_m, N] / [G * max_m, N]); c may be d itself (same
+  // base and strides), any other overlap is rejected
   bool c_f32 = false;
-  int64_t ldc = 0;
+  int64_t ldc = 0, c_gs = 0;
   if (c != nullptr) {
-    if (mode != dgmi::MODE_DENSE) return fail(DG_INVALID_ARG, "%s: c is only taken by the dense GEMM", fname);
     DG_TRY(check_basic(c, "c", true));
     if (c->dtype != DG_BF16 && c->dtype != DG_F32) return fail(DG_INVALID_ARG, "%s: c must be BF16 or F32", fname);
-    if (c->ndim != 2 || c->shape[0] != M || c->shape[1] != N)
-      return fail(DG_INVALID_ARG, "%s: c must be [M, N] = [%lld, %lld]", fname, (long long)M, (long long)N);
+    View3 vc;
+    if (mode == dgmi::MODE_MASKED) {
+      DG_TRY(view3(c, "c", G, rows_pg, &vc));
+    } else {
+      if (c->ndim != 2) return fail(DG_INVALID_ARG, "%s: c must be 2-D", fname);
+      DG_TRY(view3(c, "c", 1, 0, &vc));
+    }
+    if ((mode == dgmi::MODE_MASKED && vc.G != G) || vc.R != M || vc.C != N)
+      return fail(DG_INVALID_ARG, "%s: c must have the shape of %s ([..,%lld,%lld])", fname, dname, (long long)M,
+                  (long long)N);
     c_f32 = c->dtype == DG_F32;
     if (!aligned(c->data, c_f32 ? 4 : 2)) return fail(DG_INVALID_ARG, "%s: c must be element-aligned", fname);
-    ldc = c->stride[0];
+    ldc = vc.sr;
+    c_gs = vc.sg;
     // (with FP8 output, c and q differ in dtype and must not overlap)
-    const bool same_as_d = c->data == d->data && c->dtype == d->dtype && ldc == d->stride[0];
+    const bool same_as_d = c->data == d->data && c->dtype == d->dtype && ldc == vd.sr && (G <= 1 || c_gs == vd.sg);
     if (!same_as_d) DG_TRY(check_no_alias(d, dname, c, "c"));
   }
 
@@ -345,6 +354,7 @@ int fp8_gemm_common(int mode, const dg_tensor* a, const dg_tensor* b, const dg_t
   }
   p.c = c != nullptr ? c->data : nullptr;
   p.ldc = ldc;
+  p.c_gs = c_gs;
   p.c_f32 = c_f32 ? 1 : 0;
   p.meta = meta ? static_cast<const int32_t*>(meta->data) : nullptr;
   p.lda = lda;
@@ -360,7 +370,7 @@ int fp8_gemm_common(int mode, const dg_tensor* a, const dg_tensor* b, const dg_t
   p.sfb_sk = sfb->stride[sfb->ndim - 1];
   p.sfb_gs = vsb.sg;
   p.ldd = vd.sr;
-  p.d_gs = vd.sg;
+  p.d_gs = d_f32 ? 2 * vd.sg : vd.sg;  // (the kernels step d in BF16-sized units)
   p.M = (int32_t)M;
   p.N = (int32_t)N;
   p.k_bytes = (int32_t)K;
@@ -615,6 +625,23 @@ int m_grouped_fp8_gemm_nt_masked(const dg_tensor* a, const dg_tensor* b, const d
   if (masked_m == nullptr) return fail(DG_INVALID_ARG, "m_grouped_fp8_gemm_nt_masked: masked_m is NULL");
   return fp8_gemm_common(dgmi::MODE_MASKED, a, b, sfa, sfb, nullptr, d, masked_m, max_m_per_group, stream,
                          "m_grouped_fp8_gemm_nt_masked");
+}
+
+int m_grouped_fp8_gemm_nt_contiguous_acc(const dg_tensor* a, const dg_tensor* b, const dg_tensor* sfa,
+                                         const dg_tensor* sfb, const dg_tensor* c, const dg_tensor* d,
+                                         const dg_tensor* grouped_layout, hipStream_t stream) {
+  if (grouped_layout == nullptr)
+    return fail(DG_INVALID_ARG, "m_grouped_fp8_gemm_nt_contiguous_acc: grouped_layout is NULL");
+  return fp8_gemm_common(dgmi::MODE_CONTIG, a, b, sfa, sfb, c, d, grouped_layout, 0, stream,
+                         "m_grouped_fp8_gemm_nt_contiguous_acc");
+}
+
+int m_grouped_fp8_gemm_nt_masked_acc(const dg_tensor* a, const dg_tensor* b, const dg_tensor* sfa,
+                                     const dg_tensor* sfb, const dg_tensor* c, const dg_tensor* d,
+                                     const dg_tensor* masked_m, int64_t max_m_per_group, hipStream_t stream) {
+  if (masked_m == nullptr) return fail(DG_INVALID_ARG, "m_grouped_fp8_gemm_nt_masked_acc: masked_m is NULL");
+  return fp8_gemm_common(dgmi::MODE_MASKED, a, b, sfa, sfb, c, d, masked_m, max_m_per_group, stream,
+                         "m_grouped_fp8_gemm_nt_masked_acc");
 }
 
 int bf16_gemm_nt(const dg_tensor* a, const dg_tensor* b, const dg_tensor* c, const dg_tensor* d, hipStream_t stream) {

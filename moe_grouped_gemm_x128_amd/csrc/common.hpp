@@ -34,8 +34,9 @@ struct GemmParams {
   const void* sfa;  // FP8 only
   const void* sfb;  // FP8 only
   uint16_t* d;
-  const void* c;        // dense only: optional accumulate input C [M, N] (BF16 or F32), may be d
+  const void* c;        // optional accumulate input C shaped like D (BF16 or F32), may be d
   int64_t ldc;          // row stride of c in elements
+  int64_t c_gs;         // masked: stride of c between groups, in elements
   int32_t c_f32;        // c holds F32 (else BF16)
   const int32_t* meta;  // masked_m [G] or grouped_layout [M/128]; unused for dense
   int64_t lda, a_gs;
@@ -52,7 +53,7 @@ struct GemmParams {
   float* sfq;
   int64_t ldq, sfq_sm, sfq_sn;
   int32_t q_ue8m0;
-  int32_t d_f32;  // dense only: d holds F32 (row stride ldd in F32 elements)
+  int32_t d_f32;  // d holds F32 (row stride ldd in F32 elements; d_gs in BF16-sized units, 2 per element)
   // dense FP8 only: A / B stored MN-major ([K, M] / [K, N], rows contiguous);
   // lda / ldb are then the byte strides between consecutive K-rows
   int32_t a_mn, b_mn;

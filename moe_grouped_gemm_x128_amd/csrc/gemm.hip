@@ -197,11 +197,11 @@ __device__ __forceinline__ bf16x8 hi_bf16(const i32x8& v) { return __builtin_bit
 template <class T, int OUT>
 __device__ __forceinline__ void epilogue_cols4(const GemmParams& p, uint16_t* D, f32x4 (&acc)[T::FM][T::FN], int m0,
                                                int n0, int wm, int wn, int lane, int lo, int hi, int row_lim,
-                                               bool dense) {
+                                               const void* cbase) {
   const int fr = lane & 15;
   const int colq = n0 + wn * T::TN + (lane >> 4) * 4;
   const bool vec_ok = ((p.ldd & 3) == 0) && ((reinterpret_cast<uintptr_t>(D) & 7) == 0);
-  const bool has_c = dense && p.c != nullptr;
+  const bool has_c = cbase != nullptr;
 #pragma unroll
   for (int i = 0; i < T::FM; ++i) {
     const int rl = wm * T::TM + i * 16 + fr;
@@ -214,8 +214,8 @@ __device__ __forceinline__ void epilogue_cols4(const GemmParams& p, uint16_t* D,
       f32x4 v = acc[i][f];
       if (has_c) {
         if (p.c_f32) {
-          const float* crow = static_cast<const float*>(p.c) + (int64_t)row * p.ldc;
-          if (((p.ldc & 3) == 0) && ((reinterpret_cast<uintptr_t>(p.c) & 15) == 0) && c + 4 <= p.N) {
+          const float* crow = static_cast<const float*>(cbase) + (int64_t)row * p.ldc;
+          if (((p.ldc & 3) == 0) && ((reinterpret_cast<uintptr_t>(cbase) & 15) == 0) && c + 4 <= p.N) {
             v += *reinterpret_cast<const f32x4*>(crow + c);
           } else {
 #pragma unroll
@@ -223,8 +223,8 @@ __device__ __forceinline__ void epilogue_cols4(const GemmParams& p, uint16_t* D,
               if (c + e < p.N) v[e] += crow[c + e];
           }
         } else {
-          const uint16_t* crow = static_cast<const uint16_t*>(p.c) + (int64_t)row * p.ldc;
-          if (((p.ldc & 3) == 0) && ((reinterpret_cast<uintptr_t>(p.c) & 7) == 0) && c + 4 <= p.N) {
+          const uint16_t* crow = static_cast<const uint16_t*>(cbase) + (int64_t)row * p.ldc;
+          if (((p.ldc & 3) == 0) && ((reinterpret_cast<uintptr_t>(cbase) & 7) == 0) && c + 4 <= p.N) {
             const i32x2 cv = *reinterpret_cast<const i32x2*>(crow + c);
             v[0] += __uint_as_float((uint32_t)cv[0] << 16);
             v[1] += __uint_as_float((uint32_t)cv[0] & 0xffff0000u);
@@ -486,6 +486,11 @@ __global__ __launch_bounds__(T::NT) void gemm_kernel(const GemmParams p) {
   const uint8_t* A = p.a + (MODE == MODE_MASKED ? (int64_t)g * p.a_gs : 0);
   const uint8_t* B = p.b + (MODE == MODE_DENSE ? 0 : (int64_t)g * p.b_gs);
   uint16_t* D = p.d + (MODE == MODE_MASKED ? (int64_t)g * p.d_gs : 0);
+  // accumulate input C, shaped like D (per group for the masked form)
+  const void* C = p.c == nullptr ? nullptr
+                                 : static_cast<const void*>(static_cast<const uint8_t*>(p.c) +
+                                                            (MODE == MODE_MASKED ? (int64_t)g * p.c_gs * (p.c_f32 ? 4 : 2)
+                                                                                 : 0));
 
   // LDS-DMA sources.  Instruction j of this wave fills tile rows
   // [8(j*NW+wave), +8); lane l writes slot l%8 of row l/8 and so reads chunk
@@ -955,7 +960,7 @@ __global__ __launch_bounds__(T::NT) void gemm_kernel(const GemmParams p) {
   if constexpr (OUT == OUT_FP8) {
     epilogue_fp8<T>(p, acc, lds_b0, m0, n0, wm, wn, lane, row_lim);
   } else if constexpr (!T::PERM) {
-    epilogue_cols4<T, OUT>(p, D, acc, m0, n0, wm, wn, lane, lo, hi, row_lim, MODE == MODE_DENSE);
+    epilogue_cols4<T, OUT>(p, D, acc, m0, n0, wm, wn, lane, lo, hi, row_lim, C);
   } else {
     // ---- epilogue: BF16, row m = lane%16 of each fragment row, 16 consecutive columns per lane
     const int col0 = n0 + wn * T::TN + (lane >> 4) * 16;
@@ -965,14 +970,14 @@ __global__ __launch_bounds__(T::NT) void gemm_kernel(const GemmParams p) {
       const int rl = wm * T::TM + i * 16 + fr;
       const int row = m0 + rl;
       if (rl < lo || rl >= hi || row >= row_lim) continue;
-      if (MODE == MODE_DENSE && p.c != nullptr) {
+      if (C != nullptr) {
         // D = C + A . B^T ("DeepInside DeepGEMM", section 4): C is added to the
         // FP32 accumulator before the BF16 rounding (read before d is written,
         // so c may be d itself)
         const int cc = col0;
         if (p.c_f32) {
-          const float* crow = static_cast<const float*>(p.c) + (int64_t)row * p.ldc;
-          const bool cvec = ((p.ldc & 3) == 0) && ((reinterpret_cast<uintptr_t>(p.c) & 15) == 0) && cc + 16 <= p.N;
+          const float* crow = static_cast<const float*>(C) + (int64_t)row * p.ldc;
+          const bool cvec = ((p.ldc & 3) == 0) && ((reinterpret_cast<uintptr_t>(C) & 15) == 0) && cc + 16 <= p.N;
 #pragma unroll
           for (int f = 0; f < T::FN; ++f) {
             if (cvec) {
@@ -985,8 +990,8 @@ __global__ __launch_bounds__(T::NT) void gemm_kernel(const GemmParams p) {
             }
           }
         } else {
-          const uint16_t* crow = static_cast<const uint16_t*>(p.c) + (int64_t)row * p.ldc;
-          const bool cvec = ((p.ldc & 7) == 0) && ((reinterpret_cast<uintptr_t>(p.c) & 15) == 0) && cc + 16 <= p.N;
+          const uint16_t* crow = static_cast<const uint16_t*>(C) + (int64_t)row * p.ldc;
+          const bool cvec = ((p.ldc & 7) == 0) && ((reinterpret_cast<uintptr_t>(C) & 15) == 0) && cc + 16 <= p.N;
 #pragma unroll
           for (int h = 0; h < 2; ++h) {
             if (cvec) {
@@ -1063,14 +1068,21 @@ template <class T, int KIND, bool ROWB>
 hipError_t launch_tile(const GemmParams& p, int mode, int sf_fmt, int64_t grid, hipStream_t stream) {
   const dim3 g((unsigned)grid), b(T::NT);
   if (p.d_f32) {
-    // FP32 D: dense, block scales
-    if (mode != MODE_DENSE) return hipErrorInvalidValue;
+    // FP32 D: block scales; the BF16 kind dense only
     if constexpr (KIND == KIND_BF16) {
+      if (mode != MODE_DENSE) return hipErrorInvalidValue;
       gemm_kernel<T, KIND_BF16, SF_F32, MODE_DENSE, OUT_F32><<<g, b, 0, stream>>>(p);
     } else {
-      if (sf_fmt == SF_F32) gemm_kernel<T, KIND_FP8, SF_F32, MODE_DENSE, OUT_F32><<<g, b, 0, stream>>>(p);
-      else if (sf_fmt == SF_UE8M0) gemm_kernel<T, KIND_FP8, SF_UE8M0, MODE_DENSE, OUT_F32><<<g, b, 0, stream>>>(p);
+#define DGMI_LAUNCH_F32(SF_)                                                                                 \
+  do {                                                                                                       \
+    if (mode == MODE_DENSE) gemm_kernel<T, KIND_FP8, SF_, MODE_DENSE, OUT_F32><<<g, b, 0, stream>>>(p);     \
+    else if (mode == MODE_CONTIG) gemm_kernel<T, KIND_FP8, SF_, MODE_CONTIG, OUT_F32><<<g, b, 0, stream>>>(p); \
+    else gemm_kernel<T, KIND_FP8, SF_, MODE_MASKED, OUT_F32><<<g, b, 0, stream>>>(p);                       \
+  } while (0)
+      if (sf_fmt == SF_F32) DGMI_LAUNCH_F32(SF_F32);
+      else if (sf_fmt == SF_UE8M0) DGMI_LAUNCH_F32(SF_UE8M0);
       else return hipErrorInvalidValue;
+#undef DGMI_LAUNCH_F32
     }
     return hipGetLastError();
   }

@@ -283,7 +283,20 @@ def test_masked_validation_errors(lib):
     assert call(mm=_t((G,), torch.float32)) == binding.DG_INVALID_ARG
     assert call(max_m=max_m + 1) == binding.DG_INVALID_ARG
     assert call(d=_t((G, max_m, N + 8), torch.bfloat16)) == binding.DG_INVALID_ARG
-    assert call(d=_t((G, max_m, N), torch.float32)) == binding.DG_INVALID_ARG  # F32 d: dense only
+    # F32 d: block scales only (one scale per row of B is unsupported with it)
+    assert call(d=_t((G, max_m, N), torch.float32), sfb=_t((G, N, K // 128), torch.float32)) \
+        == binding.DG_UNSUPPORTED
+    # accumulate form: c with d's shape, BF16 or F32, not overlapping d partly
+    def acc(c, d=d):
+        return lib.m_grouped_fp8_gemm_nt_masked_acc(ctypes.byref(D(a)), ctypes.byref(D(b)), ctypes.byref(D(sfa)),
+                                                    ctypes.byref(D(sfb)), ctypes.byref(D(c)), ctypes.byref(D(d)),
+                                                    ctypes.byref(D(mm)), max_m, None)
+
+    assert acc(_t((G, max_m, N + 1), torch.bfloat16)) == binding.DG_INVALID_ARG
+    assert acc(_t((G, max_m, N), torch.int32)) == binding.DG_INVALID_ARG
+    assert acc(_t((G + 1, max_m, N), torch.bfloat16)) == binding.DG_INVALID_ARG
+    big = _t((G, max_m + 1, N), torch.bfloat16)
+    assert acc(big[:, 1:], d=big[:, :-1]) == binding.DG_INVALID_ARG
     assert call(max_m=-1) == binding.DG_INVALID_ARG
 
 

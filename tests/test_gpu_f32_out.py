@@ -240,3 +240,220 @@ def test_bf16_dense_f32_accumulate_in_place():
     c = xc.astype(np.float64)
     S = oracle.bf16_gemm_nt(ab & np.uint16(0x7FFF), bb & np.uint16(0x7FFF)) + np.abs(c)
     assert_f32_close(to_host(d), oracle.bf16_gemm_nt(ab, bb, c), S, K, "bf16 F32 d = C + AB^T", e_block=0.0)
+
+
+# ---------------------------------------------------------------------------
+# grouped forms: F32 d, and the accumulate form D = C + A . B^T
+# ---------------------------------------------------------------------------
+
+def _grouped_inputs(seed, Mrows, G, N, K, per_group_a=False, ue8m0=False):
+    """Codes and scales for the grouped GEMMs: A [Mrows, K] (or [G, rows, K]),
+    B [G, N, K]; the oracle's and the device's quantization must agree."""
+    mg = _mg()
+    xa = synth.normal_f32(seed, (Mrows, K))
+    xb = synth.normal_f32(seed + 1, (G, N, K))
+    a = torch.empty((Mrows, K), dtype=torch.uint8, device="cuda")
+    sfa = torch.empty((Mrows, K // 128), dtype=torch.float32, device="cuda")
+    mg.per_token_cast_to_fp8(to_dev(xa), a, sfa, ue8m0)
+    b = torch.empty((G, N, K), dtype=torch.uint8, device="cuda")
+    sfb = torch.empty((G, -(-N // 128), K // 128), dtype=torch.float32, device="cuda")
+    mg.per_block_cast_to_fp8(to_dev(xb), b, sfb, ue8m0)
+    ra, rsfa = oracle.per_token_cast_to_fp8(xa, ue8m0)
+    rb, rsfb = oracle.per_block_cast_to_fp8(xb, ue8m0)
+    assert np.array_equal(to_host(a), ra) and np.array_equal(to_host(b), rb)
+    return a, sfa, b, sfb, ra, rsfa, rb, rsfb
+
+
+@pytest.mark.parametrize("c_kind", [None, "bf16", "f32", "inplace"])
+@pytest.mark.parametrize("d_kind", ["bf16", "f32"])
+def test_contiguous_f32_out_and_accumulate(c_kind, d_kind):
+    """Contiguous grouped GEMM with an F32 d and/or C: mixed groups inside
+    256-row tiles and skipped blocks, whose rows stay untouched."""
+    say(f"contiguous d={d_kind} c={c_kind}")
+    mg = _mg()
+    from helpers import SENTINEL_BF16, assert_bf16_close
+
+    G, N, K = 3, 300, 384
+    layout = np.array([2, 2, -1, 0, 1, 0, 2, 7], dtype=np.int32)  # 7 >= G: skipped
+    Msum = layout.size * 128
+    a, sfa, b, sfb, ra, rsfa, rb, rsfb = _grouped_inputs(901, Msum, G, N, K)
+    xc = synth.normal_f32(903, (Msum, N)) * np.float32(4.0)
+    cref = None
+    c = None
+    if d_kind == "f32":
+        dbuf, d = nan_f32(Msum, N, pad=4)
+    else:
+        d = torch.full((Msum, N), SENTINEL_BF16, dtype=torch.int16, device="cuda").view(torch.bfloat16)
+    if c_kind == "bf16":
+        cbits = synth.bf16_bits_from_f32(xc)
+        c, cref = _dev_bf16(cbits), oracle.bf16_decode(cbits)
+    elif c_kind == "f32":
+        c, cref = to_dev(xc), xc.astype(np.float64)
+    elif c_kind == "inplace":
+        if d_kind == "f32":
+            d.copy_(to_dev(xc))
+            cref = xc.astype(np.float64)
+        else:
+            cbits = synth.bf16_bits_from_f32(xc)
+            d.copy_(_dev_bf16(cbits))
+            cref = oracle.bf16_decode(cbits)
+        c = d
+    mg.m_grouped_fp8_gemm_nt_contiguous(a, b, sfa, sfb, d, to_dev(layout), c=c)
+    torch.cuda.synchronize()
+    ref_layout = np.where(layout < G, layout, -1)
+    ref, written = oracle.m_grouped_fp8_gemm_nt_contiguous(ra, rb, rsfa, rsfb, ref_layout)
+    if cref is not None:
+        ref = ref + cref
+    got = to_host(d)
+    if d_kind == "f32":
+        if c_kind == "inplace":
+            assert np.array_equal(got[~written], xc[~written]), "skipped rows changed"
+        else:
+            assert np.isnan(got[~written]).all(), "skipped rows written"
+        S, _ = oracle.m_grouped_fp8_gemm_nt_contiguous(np.asarray(ra) & np.uint8(0x7F), np.asarray(rb) & np.uint8(0x7F),
+                                                       np.abs(rsfa), np.abs(rsfb), ref_layout)
+        if cref is not None:
+            S = S + np.abs(cref)
+        assert_f32_close(got[written], ref[written], S[written], K // 128, f"contiguous F32 d c={c_kind}")
+        assert torch.isnan(dbuf[:, N:]).all(), "row padding written"
+        if c_kind is None:
+            d16 = torch.empty((Msum, N), dtype=torch.bfloat16, device="cuda")
+            mg.m_grouped_fp8_gemm_nt_contiguous(a, b, sfa, sfb, d16, to_dev(layout))
+            torch.cuda.synchronize()
+            rows = torch.from_numpy(written).cuda()
+            assert torch.equal(d[rows].to(torch.bfloat16).view(torch.int16), d16[rows].view(torch.int16))
+    else:
+        if c_kind == "inplace":
+            assert np.array_equal(got[~written], synth.bf16_bits_from_f32(xc)[~written]), "skipped rows changed"
+        else:
+            assert np.all(got[~written] == SENTINEL_BF16), "skipped rows written"
+        assert_bf16_close(got[written], ref[written], f"contiguous BF16 d c={c_kind}")
+
+
+@pytest.mark.parametrize("G,max_m,N,K,mm", [(3, 300, 272, 256, [300, 0, 150]), (4, 96, 200, 384, [96, 17, 0, 64])])
+@pytest.mark.parametrize("c_kind", [None, "bf16", "f32", "inplace"])
+@pytest.mark.parametrize("d_kind", ["bf16", "f32"])
+@pytest.mark.parametrize("ue8m0", [False, True])
+def test_masked_f32_out_and_accumulate(G, max_m, N, K, mm, c_kind, d_kind, ue8m0):
+    """Masked grouped GEMM with an F32 d and/or C (per group, 3-D); rows past
+    masked_m are neither read from c nor written."""
+    say(f"masked G={G} max_m={max_m} N={N} K={K} d={d_kind} c={c_kind} ue8m0={ue8m0}")
+    mg = _mg()
+    from helpers import SENTINEL_BF16, assert_bf16_close
+
+    a, sfa, b, sfb, ra, rsfa, rb, rsfb = _grouped_inputs(911, G * max_m, G, N, K, ue8m0=ue8m0)
+    if ue8m0:
+        pa = torch.empty((G * max_m, -(-(K // 128) // 4)), dtype=torch.int32, device="cuda")
+        pb = torch.empty((G, -(-N // 128), -(-(K // 128) // 4)), dtype=torch.int32, device="cuda")
+        mg.pack_ue8m0_to_int(sfa, pa)
+        mg.pack_ue8m0_to_int(sfb, pb)
+        sfa_d, sfb_d = pa.view(G, max_m, -1), pb
+    else:
+        sfa_d, sfb_d = sfa.view(G, max_m, -1), sfb
+    a3 = a.view(G, max_m, K)
+    xc = synth.normal_f32(913, (G, max_m, N)) * np.float32(4.0)
+    if d_kind == "f32":
+        d = torch.full((G, max_m, N), float("nan"), dtype=torch.float32, device="cuda")
+    else:
+        d = torch.full((G, max_m, N), SENTINEL_BF16, dtype=torch.int16, device="cuda").view(torch.bfloat16)
+    c, cref = None, None
+    if c_kind == "bf16":
+        cbits = synth.bf16_bits_from_f32(xc)
+        c, cref = _dev_bf16(cbits), oracle.bf16_decode(cbits)
+    elif c_kind == "f32":
+        c, cref = to_dev(xc), xc.astype(np.float64)
+    elif c_kind == "inplace":
+        if d_kind == "f32":
+            d.copy_(to_dev(xc))
+            cref = xc.astype(np.float64)
+        else:
+            cbits = synth.bf16_bits_from_f32(xc)
+            d.copy_(_dev_bf16(cbits))
+            cref = oracle.bf16_decode(cbits)
+        c = d
+    masked_m = torch.tensor(mm, dtype=torch.int32, device="cuda")
+    mg.m_grouped_fp8_gemm_nt_masked(a3, b, sfa_d, sfb_d, d, masked_m, max_m, c=c)
+    torch.cuda.synchronize()
+    ref, written = oracle.m_grouped_fp8_gemm_nt_masked(ra.reshape(G, max_m, K), rb, rsfa.reshape(G, max_m, -1), rsfb,
+                                                       np.array(mm), max_m)
+    if cref is not None:
+        ref = ref + cref
+    got = to_host(d)
+    if c_kind == "inplace":
+        keep = xc if d_kind == "f32" else synth.bf16_bits_from_f32(xc)
+        assert np.array_equal(got[~written], keep[~written]), "rows past masked_m changed"
+    elif d_kind == "f32":
+        assert np.isnan(got[~written]).all(), "rows past masked_m written"
+    else:
+        assert np.all(got[~written] == SENTINEL_BF16), "rows past masked_m written"
+    if d_kind == "f32":
+        S, _ = oracle.m_grouped_fp8_gemm_nt_masked((ra & np.uint8(0x7F)).reshape(G, max_m, K), rb & np.uint8(0x7F),
+                                                   np.abs(rsfa).reshape(G, max_m, -1), np.abs(rsfb), np.array(mm),
+                                                   max_m)
+        if cref is not None:
+            S = S + np.abs(cref)
+        assert_f32_close(got[written], ref[written], S[written], K // 128, f"masked F32 d c={c_kind}")
+    else:
+        assert_bf16_close(got[written], ref[written], f"masked BF16 d c={c_kind}")
+
+
+@pytest.mark.parametrize("form", ["contiguous", "masked"])
+@pytest.mark.parametrize("d_kind,c_kind", [("f32", "bf16"), ("bf16", "f32"), ("f32", "inplace")])
+def test_grouped_accumulate_on_256x256_tiles(form, d_kind, c_kind):
+    """The grouped forms' C and F32 d on the 256 x 256 tile (its 64-column
+    wave tiles store 16 consecutive columns per lane)."""
+    from moe_grouped_gemm_x128_amd import binding
+    from helpers import assert_bf16_close
+
+    mg = _mg()
+    N, K = 4096, 256
+    if form == "contiguous":
+        G, Msum = 5, 4096
+        layout = np.array([(j * 7) % 6 - 1 for j in range(Msum // 128)], dtype=np.int32)  # -1 .. 4, mixed
+        plan = binding.query_config(binding.DG_KIND_CONTIGUOUS, G, Msum, N, K)
+        rows = Msum
+    else:
+        G, max_m = 16, 256
+        mm = np.array([256, 0, 1, 255, 128, 129, 200, 17] * 2, dtype=np.int32)
+        plan = binding.query_config(binding.DG_KIND_MASKED, G, max_m, N, K)
+        rows = G * max_m
+    assert (plan["block_m"], plan["block_n"]) == (256, 256), plan
+    say(f"{form} on 256x256 tiles d={d_kind} c={c_kind}")
+    a, sfa, b, sfb, ra, rsfa, rb, rsfb = _grouped_inputs(921, rows, G, N, K)
+    xc = synth.normal_f32(923, (rows, N)) * np.float32(4.0)
+    dt = torch.float32 if d_kind == "f32" else torch.bfloat16
+    d = torch.zeros((rows, N), dtype=dt, device="cuda")
+    if c_kind == "bf16":
+        cbits = synth.bf16_bits_from_f32(xc)
+        c, cref = _dev_bf16(cbits), oracle.bf16_decode(cbits)
+    elif c_kind == "f32":
+        c, cref = to_dev(xc), xc.astype(np.float64)
+    else:
+        d.copy_(to_dev(xc))
+        c, cref = d, xc.astype(np.float64)
+    if form == "contiguous":
+        mg.m_grouped_fp8_gemm_nt_contiguous(a, b, sfa, sfb, d, to_dev(layout), c=c)
+        ref, written = oracle.m_grouped_fp8_gemm_nt_contiguous(ra, rb, rsfa, rsfb, layout)
+        S, _ = oracle.m_grouped_fp8_gemm_nt_contiguous(ra & np.uint8(0x7F), rb & np.uint8(0x7F), rsfa, rsfb, layout)
+    else:
+        d3 = d.view(G, max_m, N)
+        c3 = c.view(G, max_m, N)
+        mg.m_grouped_fp8_gemm_nt_masked(a.view(G, max_m, K), b, sfa.view(G, max_m, -1), sfb, d3, to_dev(mm), max_m,
+                                        c=c3)
+        ref, written = oracle.m_grouped_fp8_gemm_nt_masked(ra.reshape(G, max_m, K), rb, rsfa.reshape(G, max_m, -1),
+                                                           rsfb, mm, max_m)
+        S, _ = oracle.m_grouped_fp8_gemm_nt_masked((ra & np.uint8(0x7F)).reshape(G, max_m, K), rb & np.uint8(0x7F),
+                                                   rsfa.reshape(G, max_m, -1), rsfb, mm, max_m)
+        ref, written, S = ref.reshape(rows, N), written.reshape(rows), S.reshape(rows, N)
+    torch.cuda.synchronize()
+    ref = ref + cref
+    got = to_host(d)
+    if d_kind == "f32":
+        assert_f32_close(got[written], ref[written], (S + np.abs(cref))[written], K // 128, f"{form} F32 d c={c_kind}")
+    else:
+        assert_bf16_close(got[written], ref[written], f"{form} BF16 d c={c_kind}")
+    untouched = xc[~written] if c_kind == "inplace" else np.zeros_like(xc[~written])
+    if d_kind == "f32":
+        assert np.array_equal(got[~written], untouched), "rows that are not computed changed"
+    else:
+        assert np.all(got[~written] == 0), "rows that are not computed were written"
