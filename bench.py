@@ -1,6 +1,6 @@
 """Benchmark of the block-scaled FP8 GEMM path on one MI355X.
 
-    python bench.py [--steps K] [--warmup W] [--settle-seconds S] [--reps R]
+    python bench.py [--steps K] [--warmup W] [--settle-seconds S] [--reps R] [--timing eager|graph]
                     [--workload dense|contiguous|masked|masked_graph|bf16_dense|dense_rowb|dense_fp8_out|
                                 moe_decode|moe_prefill]
                     [--no-masked] [--no-cpu-baseline]
@@ -18,25 +18,29 @@ Prints ONE JSON line.
   whole-step time over the K timed steps (after untimed settle steps for S
   seconds -- the GPU clock dips for the first milliseconds of sustained load
   -- and W warmup steps).
-* `roofline`: the dominant kernel (the FP8 GEMM), timed by the protocol of
-  the pages' test suite ("DeepGEMM CUDA Graph Compatibility for Masked
-  Grouped GEMMs", Verification via Test Suite: graph-mode timing, median):
-  each GEMM call is captured once as a hipGraph, replayed 5 times untimed,
-  then R times with HIP events around the replay on the launch stream; a
-  1 GiB cache flush (a read of a 1 GiB scratch tensor) runs before every
-  timed replay, outside the events, so every replay starts with cold, clean
-  L2s and MALL (a writing flush, whose dirty lines the call would then write
-  back, is reported beside it).  `achieved` = the shapes' FLOPs / the sum of their median replay
+* `roofline`: the dominant kernel (the FP8 GEMM), timed per GEMM call:
+  5 untimed calls, then R calls with HIP events around the call on the
+  launch stream; a 1 GiB cache flush (a read of a 1 GiB scratch tensor) runs
+  before every timed call, outside the events, so every call starts with
+  cold, clean L2s and MALL (a writing flush, whose dirty lines the call
+  would then write back, is reported beside it).  The flush keeps the queue
+  busy while the call is issued, so the events bracket the kernel alone
+  (within 2-4 us of the kernel durations a rocprofv3 kernel trace records).
+  `--timing graph` replays a captured hipGraph instead, the protocol of the
+  pages' test suite ("DeepGEMM CUDA Graph Compatibility for Masked Grouped
+  GEMMs", Verification via Test Suite: graph-mode timing, median); on this
+  runtime each replay adds about 10 us of graph-launch work inside the
+  events.  `achieved` = the shapes' FLOPs / the sum of their median call
   times; the spread (min, p10, p90, max) is listed per shape, next to the
   warm in-step figure (HIP events around the GEMM calls of the timed steps).
 * `masked`: the second half of the metric -- the masked grouped GEMMs
-  against HBM bandwidth, by the same graph-replay protocol: MoE decode
-  (32 experts x 256 rows, masked_m ~ floor(192 U(0.7, 1.3)), (N, K) =
-  (4096, 7168) and (7168, 2048), FP32 scales) and the graph workload (64
-  experts x 128 rows, N 7168, K 2048, a fresh uniform masked_m written before
-  every replay, outside the events; FP8 with packed UE8M0 scales and BF16).
-  GB/s = algorithmic bytes of the draw (B once per active expert, A and D
-  over valid rows, scales) / median replay time.
+  against HBM bandwidth, by the same protocol: MoE decode (32 experts x 256
+  rows, masked_m ~ floor(192 U(0.7, 1.3)), (N, K) = (4096, 7168) and
+  (7168, 2048), FP32 scales) and the graph workload (64 experts x 128 rows,
+  N 7168, K 2048, always as hipGraph replays: a fresh uniform masked_m is
+  written before every replay, outside the events; FP8 with packed UE8M0
+  scales and BF16).  GB/s = algorithmic bytes of the draw (B once per
+  active expert, A and D over valid rows, scales) / median call time.
 * `cpu_baseline`: the CPU oracle timed per configuration on bounded samples
   (about 10-30 s in total), with the host's core count and CPU model.
 
@@ -73,7 +77,7 @@ if ROOT not in sys.path:
 FP8_PEAK_TFLOPS = 5000.0   # MI355X dense FP8 MFMA
 BF16_PEAK_TFLOPS = 2500.0  # MI355X dense BF16 MFMA
 HBM_PEAK_GBS = 8000.0      # MI355X HBM3E
-FLUSH_BYTES = 1 << 30      # cache flush before every timed graph replay (L2 4 MB x 8, MALL 256 MB)
+FLUSH_BYTES = 1 << 30      # cache flush before every timed call (L2 4 MB x 8, MALL 256 MB)
 
 
 def log(msg):
@@ -606,19 +610,19 @@ class MaskedGraphWorkload:
 
 
 # ---------------------------------------------------------------------------
-# timing: one call captured as a hipGraph, replayed with a cold cache
+# timing: one call, eager or as hipGraph replays, with a cold cache
 # ---------------------------------------------------------------------------
 
 def _stats(us):
     a = np.sort(np.asarray(us, dtype=np.float64))
     return {"median_us": float(np.median(a)), "min_us": float(a[0]), "p10_us": float(np.percentile(a, 10)),
-            "p90_us": float(np.percentile(a, 90)), "max_us": float(a[-1]), "replays": int(a.size)}
+            "p90_us": float(np.percentile(a, 90)), "max_us": float(a[-1]), "calls": int(a.size)}
 
 
-class GraphTimer:
-    """Captures a call once (torch.cuda.graph) and times its replays with HIP
-    events on the current stream, a 1 GiB flush before each timed replay
-    (outside the events).
+class CallTimer:
+    """Times a call with HIP events on the current stream, a 1 GiB flush before
+    each timed call (outside the events): eager calls, or replays of the call
+    captured once (torch.cuda.graph).
 
     The flush reads the 1 GiB scratch tensor (a sum): afterwards neither the
     per-XCD L2s nor the 256 MB MALL hold any of the call's operands, and no
@@ -627,9 +631,10 @@ class GraphTimer:
     for out of its own bandwidth; that variant is reported separately
     (write_flush)."""
 
-    def __init__(self, torch, write_flush=False):
+    def __init__(self, torch, write_flush=False, graph=True):
         self.torch = torch
         self.write_flush = write_flush
+        self.graph = graph
         self.flush = torch.ones(FLUSH_BYTES // 4, dtype=torch.float32, device="cuda")
         self.sink = None
 
@@ -650,13 +655,14 @@ class GraphTimer:
         return g
 
     def time(self, fn, reps, warm=5, before=None):
-        """Returns (per-replay microseconds, per-replay results of before())."""
+        """Returns (per-call microseconds, per-call results of before())."""
         torch = self.torch
-        g = self.capture(fn)
+        g = self.capture(fn) if self.graph else None
+        run = g.replay if g is not None else fn
         for _ in range(warm):
             if before is not None:
                 before()
-            g.replay()
+            run()
         torch.cuda.synchronize()
         evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
         tags = []
@@ -665,7 +671,7 @@ class GraphTimer:
                 tags.append(before())
             self._flush()
             e0.record()
-            g.replay()
+            run()
             e1.record()
         torch.cuda.synchronize()
         us = [e0.elapsed_time(e1) * 1e3 for e0, e1 in evs]
@@ -674,7 +680,7 @@ class GraphTimer:
 
 
 def time_gemms(torch, W, timer, reps):
-    """Graph-replay timing of every GEMM call of a workload."""
+    """Cold-cache timing of every GEMM call of a workload."""
     out = []
     for i in range(len(W.flops)):
         us, _ = timer.time(W.gemm_call(i), reps)
@@ -688,7 +694,8 @@ def time_gemms(torch, W, timer, reps):
 
 def masked_block(torch, mg, synth, timer, reps):
     """MoE decode (32 x 256 rows, FP32 scales) and the graph workload (64 x
-    128 rows, FP8 UE8M0 and BF16), each GEMM by the graph-replay protocol."""
+    128 rows, FP8 UE8M0 and BF16), each GEMM call timed after a cache flush
+    (the graph workload always as hipGraph replays)."""
     res = {}
     log("masked block: decode workload (32 experts x 256 rows)")
     Wd = MaskedWorkload(torch, mg, synth)
@@ -720,6 +727,7 @@ def masked_block(torch, mg, synth, timer, reps):
         return mm
 
     graph = {}
+    eager, timer.graph = not timer.graph, True  # this workload is timed as graph replays in either mode
     for i, kind in enumerate(("fp8_ue8m0", "bf16")):
         us, tags = timer.time(Wg.gemm_call(i), reps, before=fresh)
         b = np.array([Wg._bytes(m)[1 + i] for m in tags])
@@ -730,6 +738,7 @@ def masked_block(torch, mg, synth, timer, reps):
                    "mean_sum_masked_m": float(np.mean([m.sum() for m in tags]))})
         st["frac"] = st["gbs_median"] / HBM_PEAK_GBS
         graph[kind] = st
+    timer.graph = not eager
     res["graph"] = {"workload": Wg.name, "experts": Wg.G, "max_m": Wg.max_m, "N": Wg.N, "K": Wg.K,
                     "masked_m": "uniform integers 0..128, a fresh draw before every replay", **graph}
     del Wg
@@ -745,7 +754,7 @@ def masked_block(torch, mg, synth, timer, reps):
 # ---------------------------------------------------------------------------
 
 def recorded_traffic(workload):
-    """Bytes per launch of the dominant GEMM kernel (FETCH + WRITE, calibrated
+    """Bytes per launch of the dominant GEMM kernel (HBM-side reads + writes, calibrated
     against a 1 GiB copy) from profiles/gemm_traffic.txt, or None when the
     record is missing or was taken on a different version of the kernel
     source."""
@@ -922,7 +931,11 @@ def main():
     ap.add_argument("--settle-seconds", type=float, default=1.0,
                     help="untimed steps run for this long before the warmup steps, so that the timed steps see "
                          "the GPU's steady sustained clock rather than the dip of its first milliseconds under load")
-    ap.add_argument("--reps", type=int, default=25, help="timed graph replays per GEMM call (kernel timing)")
+    ap.add_argument("--reps", type=int, default=25, help="timed calls per GEMM call (kernel timing)")
+    ap.add_argument("--timing", choices=("graph", "eager"), default="eager",
+                    help="kernel timing: eager calls (default), or replays of a captured hipGraph (each replay "
+                         "adds about 10 us of graph-launch work inside the events on this runtime); the masked "
+                         "graph workload is always timed as graph replays")
     ap.add_argument("--event-every", type=int, default=10,
                     help="record HIP events around the GEMM calls of one timed step in this many (plus the last)")
     ap.add_argument("--no-masked", action="store_true", help="dense: skip the masked grouped GEMM block")
@@ -1010,9 +1023,9 @@ def main():
     total_flops = float(sum(W.flops))
     value = total_flops / (ms_per_step * 1e-3) / 1e12
 
-    # kernel timing by the graph-replay protocol (cold cache, median)
-    log(f"graph-replay timing of the GEMM calls ({args.reps} replays each, 1 GiB flush before each)")
-    timer = GraphTimer(torch)
+    # kernel timing (cold cache, median)
+    log(f"{args.timing} timing of the GEMM calls ({args.reps} calls each, 1 GiB flush before each)")
+    timer = CallTimer(torch, graph=args.timing == "graph")
     if graph_wl:
         kt = []
         for i in range(nshape):
@@ -1021,7 +1034,7 @@ def main():
             kt.append(_stats(us))
     else:
         kt = time_gemms(torch, W, timer, args.reps)
-        wtimer = GraphTimer(torch, write_flush=True)
+        wtimer = CallTimer(torch, write_flush=True, graph=args.timing == "graph")
         wflush = [k["median_us"] for k in time_gemms(torch, W, wtimer, args.reps)]
         del wtimer
         for k, w in zip(kt, wflush):
@@ -1048,15 +1061,16 @@ def main():
         avg_us = float(np.mean(gemm_us))
         roof = {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s", "frac": achieved / peak}
     roof["traffic"] = recorded_traffic(args.workload)
-    roof["traffic_unit"] = "HBM bytes per GEMM call (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)"
+    roof["traffic_unit"] = ("HBM-side bytes per GEMM call: rocprofv3 TCC_EA0 read requests by size (32/64/128 B) plus "
+                           "write requests, calibrated against a 1 GiB copy")
     roof["algorithmic_bytes_per_launch"] = alg
     roof["kernel"] = "gemm_kernel (BF16 kind)" if args.workload == "bf16_dense" else "gemm_kernel (FP8 kind)"
     roof["avg_launch_us"] = avg_us
-    roof["per_launch"] = ("each GEMM call captured once as a hipGraph, 5 untimed replays, then %d replays with HIP "
-                          "events around the replay on the launch stream and a 1 GiB cache flush (a read of a 1 GiB "
-                          "scratch tensor) before each, outside the events; achieved = the calls' algorithmic work / "
-                          "the sum of their median replay times (a call is one kernel launch, or two in stream order "
-                          "where the launch plan splits the columns)" % args.reps)
+    roof["per_launch"] = ("each GEMM call: 5 untimed calls, then %d calls (%s) with HIP events around the call on the "
+                          "launch stream and a 1 GiB cache flush (a read of a 1 GiB scratch tensor) before each, "
+                          "outside the events; achieved = the calls' algorithmic work / the sum of their median times "
+                          "(a call is one kernel launch, or two in stream order where the launch plan splits the "
+                          "columns)" % (args.reps, "eager" if args.timing == "eager" else "replays of a hipGraph"))
     if not is_masked and not graph_wl:
         wf = total_flops / (sum(k["write_flush_median_us"] for k in kt) * 1e-6) / 1e12
         roof["write_flush"] = {"achieved": wf, "frac": wf / peak,
