@@ -2,7 +2,7 @@
 
     python bench.py [--steps K] [--warmup W] [--settle-seconds S] [--reps R] [--timing eager|graph]
                     [--workload dense|contiguous|masked|masked_graph|bf16_dense|dense_rowb|dense_fp8_out|
-                                moe_decode|moe_prefill]
+                                dense_nn|dense_tn|dense_tt|moe_decode|moe_prefill]
                     [--no-masked] [--no-cpu-baseline]
 
 Default workload ("dense"): the five DeepSeek-V3-shaped dense GEMMs,
@@ -56,6 +56,9 @@ Other workloads (for the measurements in the design notes):
                   token, scales [N, K/128]), as in the pages' dense example
   dense_fp8_out -- the five dense shapes with FP8 output: the GEMM's BF16 result
                   cast per token to E4M3 in its epilogue (fp8_gemm_nt_fp8_out)
+  dense_nn, dense_tn, dense_tt -- the five dense shapes with A stored [K, M] (T) and / or
+                  B stored [K, N] (N), through fp8_gemm_nn / _tn / _tt; one step = the
+                  GEMMs (the operands are cast and transposed once at set-up)
   moe_decode   -- 768 tokens to 8 of 32 experts: moe_dispatch_masked_fp8 (routing +
                   per-token cast), the masked FP8 GEMM (N 4096, K 7168), moe_combine
   moe_prefill  -- 4096 tokens to 8 of 32 experts: moe_dispatch_contiguous_fp8, the
@@ -210,6 +213,49 @@ class DenseFp8OutWorkload(DenseWorkload):
     def config(self):
         return {"workload": self.name, "M": self.M, "shapes_NK": self.shapes,
                 "scales": "fp32 1x128 (A) / 128x128 (B)", "out": "fp8 e4m3, fp32 1x128 scales (per-token cast fused)"}
+
+
+class DenseLayoutWorkload(DenseWorkload):
+    """The five dense shapes with an operand stored MN-major (the NN, TN and
+    TT layouts of the FP8 GEMM): A as [K, M] (TN, TT) and / or B as [K, N]
+    (NN, TN), quantized once at set-up (the K-major casts, then a transposed
+    copy); one step = the GEMM per shape (fp8_gemm_nn / _tn / _tt)."""
+
+    def __init__(self, torch, mg, synth, layout):
+        super().__init__(torch, mg, synth)
+        self.layout = layout
+        self.name = f"dense_fp8_v3_shapes_{layout}"
+        for b in self.bufs:
+            mg.per_token_cast_to_fp8(b["xa"], b["a"], b["sfa"])
+            mg.per_block_cast_to_fp8(b["xb"], b["b"], b["sfb"])
+            if layout[0] == "t":
+                b["a"] = b["a"].t().contiguous()  # [K, M]
+            if layout[1] == "n":
+                b["b"] = b["b"].t().contiguous()  # [K, N]
+            del b["xa"], b["xb"]
+        torch.cuda.synchronize()
+        self.fn = getattr(mg, f"fp8_gemm_{layout}")
+
+    def step(self, events=None):
+        for i, b in enumerate(self.bufs):
+            if events is not None:
+                events[i][0].record()
+            self.fn(b["a"], b["b"], b["sfa"], b["sfb"], None, b["d"])
+            if events is not None:
+                events[i][1].record()
+
+    def gemm_call(self, i):
+        b = self.bufs[i]
+        return lambda: self.fn(b["a"], b["b"], b["sfa"], b["sfb"], None, b["d"])
+
+    def plan_args(self, i):
+        N, K = self.shapes[i]
+        return ("DG_KIND_DENSE_MN", 1, self.M, N, K)
+
+    def config(self):
+        return {"workload": self.name, "M": self.M, "shapes_NK": self.shapes,
+                "layout": {"nn": "A [M, K], B [K, N]", "tn": "A [K, M], B [K, N]", "tt": "A [K, M], B [N, K]"}[self.layout],
+                "scales": "fp32 1x128 (A) / 128x128 (B)", "out": "bf16", "step": "the GEMMs only (operands cast at set-up)"}
 
 
 class Bf16DenseWorkload:
@@ -369,6 +415,7 @@ class MoeDecodeWorkload:
     GEMM and moe_combine on 4096 tokens."""
     name = "moe_decode_dispatch_gemm_combine"
     contig = False
+    align = 128  # contiguous regions: whole 128-row blocks (set by --moe-align)
 
     def __init__(self, torch, mg, synth):
         self.torch, self.mg = torch, mg
@@ -406,7 +453,7 @@ class MoeDecodeWorkload:
         placed = int((self.slot.cpu().numpy() >= 0).sum())
         if self.contig:
             # the GEMM computes every block of every region (padding included)
-            rows = int(sum(-(-int(c_) // 256) * 256 for c_ in mm))
+            rows = int(sum(-(-int(c_) // self.align) * self.align for c_ in mm))
         else:
             rows = int(mm.sum())
         active = int((mm > 0).sum())
@@ -425,9 +472,8 @@ class MoeDecodeWorkload:
             ev = [self.torch.cuda.Event(enable_timing=True) for _ in range(4)]
             ev[0].record()
         if self.contig:
-            # regions in 256-row granules: no 256-row tile of the GEMM holds two experts
             mg.moe_dispatch_contiguous_fp8(self.x, self.topk, self.a[0], self.sfa[0], self.layout, self.masked_m,
-                                           self.slot, align=256)
+                                           self.slot, align=self.align)
         else:
             mg.moe_dispatch_masked_fp8(self.x, self.topk, self.a, self.sfa, self.masked_m, self.slot, self.src)
         if events is not None:
@@ -468,7 +514,7 @@ class MoeDecodeWorkload:
     def config(self):
         if self.contig:
             return {"workload": self.name, "tokens": self.T, "topk": self.k, "experts": self.G, "rows": self.max_m,
-                    "N": self.N, "K": self.K, "routed_pairs": int(self.mm_host.sum()),
+                    "N": self.N, "K": self.K, "routed_pairs": int(self.mm_host.sum()), "region_align": self.align,
                     "step": "moe_dispatch_contiguous_fp8 (count, place, per-token cast), contiguous FP8 GEMM, "
                             "moe_combine"}
         return {"workload": self.name, "tokens": self.T, "topk": self.k, "experts": self.G, "max_m": self.max_m,
@@ -927,7 +973,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="dense",
                     choices=["dense", "contiguous", "masked", "masked_graph", "bf16_dense", "dense_rowb",
-                             "dense_fp8_out", "moe_decode", "moe_prefill"])
+                             "dense_fp8_out", "dense_nn", "dense_tn", "dense_tt", "moe_decode", "moe_prefill"])
     ap.add_argument("--settle-seconds", type=float, default=1.0,
                     help="untimed steps run for this long before the warmup steps, so that the timed steps see "
                          "the GPU's steady sustained clock rather than the dip of its first milliseconds under load")
@@ -938,6 +984,8 @@ def main():
                          "graph workload is always timed as graph replays")
     ap.add_argument("--event-every", type=int, default=10,
                     help="record HIP events around the GEMM calls of one timed step in this many (plus the last)")
+    ap.add_argument("--moe-align", type=int, choices=(128, 256), default=128,
+                    help="moe_prefill: row granule of the experts' regions in the contiguous layout")
     ap.add_argument("--no-masked", action="store_true", help="dense: skip the masked grouped GEMM block")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", action="store_true",
@@ -961,10 +1009,14 @@ def main():
     mg.dgmi_init()
 
     log(f"setting up workload {args.workload}")
-    W = {"dense": DenseWorkload, "contiguous": ContiguousWorkload, "masked": MaskedWorkload,
-         "masked_graph": MaskedGraphWorkload, "bf16_dense": Bf16DenseWorkload,
-         "dense_rowb": DenseRowBWorkload, "dense_fp8_out": DenseFp8OutWorkload,
-         "moe_decode": MoeDecodeWorkload, "moe_prefill": MoePrefillWorkload}[args.workload](torch, mg, synth)
+    MoeDecodeWorkload.align = args.moe_align
+    if args.workload in ("dense_nn", "dense_tn", "dense_tt"):
+        W = DenseLayoutWorkload(torch, mg, synth, args.workload[-2:])
+    else:
+        W = {"dense": DenseWorkload, "contiguous": ContiguousWorkload, "masked": MaskedWorkload,
+             "masked_graph": MaskedGraphWorkload, "bf16_dense": Bf16DenseWorkload,
+             "dense_rowb": DenseRowBWorkload, "dense_fp8_out": DenseFp8OutWorkload,
+             "moe_decode": MoeDecodeWorkload, "moe_prefill": MoePrefillWorkload}[args.workload](torch, mg, synth)
     torch.cuda.synchronize()
 
     # Power-state settle: under sustained GEMM load the clock dips for the first
@@ -1121,6 +1173,9 @@ def main():
         value = float(sum(W.gemm_bytes)) / (ms_per_step * 1e-3) / 1e9
     elif args.workload == "bf16_dense":
         metric = "BF16 GEMM TFLOPS (% BF16 MFMA peak)"
+        unit = "TFLOPS"
+    elif args.workload in ("dense_nn", "dense_tn", "dense_tt"):
+        metric = f"FP8 block-scaled GEMM, {args.workload[-2:].upper()} layout, TFLOPS (% FP8 MFMA peak)"
         unit = "TFLOPS"
     elif args.workload == "dense_fp8_out":
         metric = "FP8 block-scaled GEMM with per-token FP8 output TFLOPS (% FP8 MFMA peak)"

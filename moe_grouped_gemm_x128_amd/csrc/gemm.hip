@@ -26,11 +26,13 @@
 // Arguments"): the grid is a function of the shapes only.
 //   dense      -- tiles of [M, N]
 //   contiguous -- tiles of [Msum, N]; each 128-row block reads its group id
-//                 from grouped_layout on the device, negative = skip.  A
-//                 256-row tile whose two 128-row blocks belong to different
-//                 groups computes its first block; a second copy of the grid
-//                 (blocks total..2*total-1) computes the second block of
-//                 such tiles and exits at once everywhere else.
+//                 from grouped_layout on the device, negative = skip.  With
+//                 256-row tiles each run of blocks of one group is cut into
+//                 tiles from its first block (two blocks a tile, one at the
+//                 run's end), found by scanning back to the run's start; two
+//                 copies of the 256-row tiling start tiles at the even and
+//                 at the odd blocks, and a workgroup whose block starts no
+//                 tile exits at once.
 //   masked     -- G x tiles of [max_m, N]; a tile whose first row is at or
 //                 beyond masked_m[g] exits at once, rows beyond masked_m[g]
 //                 are never stored
@@ -434,10 +436,18 @@ __global__ __launch_bounds__(T::NT) void gemm_kernel(const GemmParams p) {
   // ---- tile decode (device metadata only gates early exits, never the grid)
   const int per_group = p.tiles_m * p.tiles_n;
   const int total = (MODE == MODE_MASKED ? p.G : 1) * per_group;
+  // Contiguous layout with 256-row tiles: a block at an even offset in its
+  // run of equal group ids starts a tile of the run's next two blocks (one
+  // at the run's end), so tiles never straddle groups.  The grid holds two
+  // copies of the 256-row tiling: the first looks at the even blocks, the
+  // second at the odd ones, and a workgroup whose block starts no tile exits
+  // at once -- a layout whose runs all start at even blocks runs its tiles
+  // in the first copy, densely in dispatch order, and exits in the second.
+  constexpr bool RUNS = MODE == MODE_CONTIG && T::BM == 256;
   int bid = blockIdx.x;
-  bool second = false;  // contiguous, 256-row tiles: second copy of the grid
-  if (MODE == MODE_CONTIG && T::BM == 256 && bid >= total) {
-    second = true;
+  int odd = 0;
+  if (RUNS && bid >= total) {
+    odd = 1;
     bid -= total;
   }
   int t = xcd_remap(bid, total);
@@ -448,36 +458,44 @@ __global__ __launch_bounds__(T::NT) void gemm_kernel(const GemmParams p) {
   }
   int tm, tn;
   band_order(t, p.tiles_m, p.tiles_n, MODE == MODE_MASKED ? p.tiles_m : 8, tm, tn);
-  const int m0 = __builtin_amdgcn_readfirstlane(tm * T::BM), n0 = __builtin_amdgcn_readfirstlane(tn * T::BN);
+  const int m0 = __builtin_amdgcn_readfirstlane(tm * T::BM + odd * 128), n0 = __builtin_amdgcn_readfirstlane(tn * T::BN);
 
   int row_lim = p.M;        // rows [0, row_lim) may be read and written
-  int lo = 0, hi = T::BM;   // tile rows this workgroup stores
+  const int lo = 0;         // tile rows [lo, hi) are stored
+  int hi = T::BM;
   if (MODE == MODE_MASKED) {
     int v = __builtin_amdgcn_readfirstlane(p.meta[g]);
     v = v < 0 ? 0 : (v > p.M ? p.M : v);
     if (m0 >= v) return;
     row_lim = v;
   } else if (MODE == MODE_CONTIG) {
-    const int nblk = p.M / 128;
-    const int b0 = m0 / 128;
-    int g0 = __builtin_amdgcn_readfirstlane(p.meta[b0]);
-    if (g0 < 0 || g0 >= p.G) g0 = -1;
-    int g1 = g0;
-    if (T::BM == 256) {
-      g1 = (b0 + 1 < nblk) ? __builtin_amdgcn_readfirstlane(p.meta[b0 + 1]) : -1;
-      if (g1 < 0 || g1 >= p.G) g1 = -1;
+    // group of a 128-row block; ids outside [0, G) skip the block
+    auto group_of = [&](int blk) {
+      const int v = p.meta[blk];
+      return (v < 0 || v >= p.G) ? -1 : v;
+    };
+    const int b = m0 / 128;
+    if (b >= p.M / 128) return;  // odd copy past the last block
+    const int gb = __builtin_amdgcn_readfirstlane(group_of(b));
+    if (gb < 0) return;
+    if constexpr (RUNS) {
+      // first block of the run: lane l compares block base - 1 - l, 64 blocks
+      // a window; the closest differing block (or the matrix start) ends it
+      int base = b, start = -1;
+      while (start < 0) {
+        const int c = base - 1 - lane;
+        const bool differs = c < 0 || group_of(max(c, 0)) != gb;
+        const uint64_t m = __ballot(differs);
+        if (m != 0) start = base - (int)__builtin_ctzll(m);
+        else base -= 64;
+      }
+      start = __builtin_amdgcn_readfirstlane(start);
+      if ((b - start) & 1) return;  // second block of the tile before
+      const int nblk = p.M / 128;
+      const int g1 = b + 1 < nblk ? __builtin_amdgcn_readfirstlane(group_of(b + 1)) : -1;
+      if (g1 != gb) hi = 128;  // the run's last, single block
     }
-    if (second) {
-      if (g0 == g1 || g0 < 0 || g1 < 0) return;  // no second block to do
-      g = g1; lo = 128;
-    } else if (g0 == g1) {
-      if (g0 < 0) return;
-      g = g0;
-    } else if (g0 >= 0) {
-      g = g0; hi = 128;
-    } else {
-      g = g1; lo = 128;
-    }
+    g = gb;
   }
   g = __builtin_amdgcn_readfirstlane(g);
 
@@ -1314,7 +1332,7 @@ GemmPlan fp8_gemm_plan(int mode, int64_t G, int64_t M, int64_t N, int64_t K, int
 int64_t gemm_grid(const TileCfg& cfg, int mode, int64_t G, int64_t M, int64_t N) {
   const int64_t tm = (M + cfg.bm - 1) / cfg.bm, tn = (N + cfg.bn - 1) / cfg.bn;
   const int64_t tiles = (mode == MODE_MASKED ? G : 1) * tm * tn;
-  // contiguous 256-row tiles: a second copy for tiles split between two groups
+  // contiguous 256-row tiles: a copy for the even and one for the odd blocks
   return (mode == MODE_CONTIG && cfg.bm == 256) ? 2 * tiles : tiles;
 }
 

@@ -90,8 +90,11 @@ def test_query_config_is_a_pure_function_of_shapes(lib):
     c = binding.query_config(binding.DG_KIND_CONTIGUOUS, 4, 32768, 4096, 7168)
     bc = binding.query_config(binding.DG_KIND_BF16_CONTIGUOUS, 4, 32768, 4096, 7168)
     tiles = -(-32768 // c["block_m"]) * -(-4096 // c["block_n"])
-    # 256-row contiguous tiles launch a second grid copy for tiles split between two groups
+    # 256-row contiguous tiles: two copies of the tiling, tiles starting at
+    # even and at odd 128-row blocks
     assert c["grid"] == (2 * tiles if c["block_m"] == 256 else tiles) and bc["grid"] == c["grid"]
+    c = binding.query_config(binding.DG_KIND_CONTIGUOUS, 4, 33152, 4096, 7168)  # 259 blocks
+    assert c["block_m"] == 256 and c["grid"] == 2 * 130 * 16
     with pytest.raises(binding.DgmiError):
         binding.query_config(11, 1, 1, 1, 1)  # no such kind
 
@@ -145,7 +148,7 @@ def test_launch_plan_of_the_grouped_shapes(lib):
     assert (m["block_n"], m["n_split"], m["block_n2"], m["grid"]) == (256, 4096, 0, 512)
     m = binding.query_config(binding.DG_KIND_MASKED, 32, 256, 7168, 2048)
     assert (m["block_n"], m["n_split"], m["block_n2"], m["grid"], m["grid2"]) == (256, 7168, 0, 896, 0)
-    # contiguous prefill: whole rounds of 256 x 256 (plus the second grid copy)
+    # contiguous prefill: whole rounds of 256 x 256 (and the odd-block copy)
     for N in (4096, 7168):
         c = binding.query_config(binding.DG_KIND_CONTIGUOUS, 4, 32768, N, 7168)
         assert (c["block_n"], c["n_split"], c["block_n2"], c["grid"]) == (256, N, 0, 2 * 128 * N // 256)

@@ -372,6 +372,35 @@ def test_contiguous_mixed_groups_256x256_tile():
     assert_bf16_close(got[written], ref[written], "contiguous 256 x 256 tile")
 
 
+def test_contiguous_long_runs_at_odd_offsets():
+    """Runs of one group longer than 64 blocks (the run-start scan takes
+    several windows), starting at odd block offsets, with odd lengths (a
+    single-block tile at the run's end), next to skipped blocks."""
+    say("contiguous long runs at odd offsets")
+    mg = _mg()
+    from moe_grouped_gemm_x128_amd import binding
+
+    G, N, K = 3, 320, 256
+    layout = np.array([1] + [0] * 151 + [2] * 3 + [-1] + [1] * 65 + [2] * 2 + [7] + [0] * 130, dtype=np.int32)
+    Msum = layout.size * 128
+    c = binding.query_config(binding.DG_KIND_CONTIGUOUS, G, Msum, N, K)
+    assert c["block_m"] == 256 and c["grid"] == 2 * -(-layout.size // 2) * -(-N // c["block_n"])
+    xa = synth.normal_f32(127, (Msum, K))
+    xb = synth.normal_f32(128, (G, N, K))
+    a, sfa = q_tok(to_dev(xa))
+    b, sfb = q_blk(to_dev(xb))
+    d = sentinel_like((Msum, N))
+    mg.m_grouped_fp8_gemm_nt_contiguous(a, b, sfa, sfb, d, to_dev(layout))
+    torch.cuda.synchronize()
+    ra, rsfa = oracle.per_token_cast_to_fp8(xa)
+    rb, rsfb = oracle.per_block_cast_to_fp8(xb)
+    ref_layout = np.where(layout < G, layout, -1)
+    ref, written = oracle.m_grouped_fp8_gemm_nt_contiguous(ra, rb, rsfa, rsfb, ref_layout)
+    got = to_host(d)
+    assert np.all(got[~written] == SENTINEL_BF16)
+    assert_bf16_close(got[written], ref[written], "contiguous long runs")
+
+
 @pytest.mark.parametrize("si", [0, 1])
 def test_contiguous_prefill_full_size_sampled(si):
     N, K = synth.CONTIG["shapes"][si]
