@@ -1174,6 +1174,12 @@ def main():
     elif args.workload == "bf16_dense":
         metric = "BF16 GEMM TFLOPS (% BF16 MFMA peak)"
         unit = "TFLOPS"
+    elif args.workload == "dense_rowb":
+        metric = "FP8 GEMM with one FP32 B scale per row of B, TFLOPS (% FP8 MFMA peak)"
+        unit = "TFLOPS"
+    elif args.workload == "contiguous":
+        metric = "contiguous grouped FP8 block-scaled GEMM TFLOPS (% FP8 MFMA peak)"
+        unit = "TFLOPS"
     elif args.workload in ("dense_nn", "dense_tn", "dense_tt"):
         metric = f"FP8 block-scaled GEMM, {args.workload[-2:].upper()} layout, TFLOPS (% FP8 MFMA peak)"
         unit = "TFLOPS"
