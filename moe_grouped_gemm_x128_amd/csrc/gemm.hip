@@ -61,7 +61,9 @@
 //     "Technological Innovations of DeepGEMM", item "Support for Arbitrary
 //     Matrix Sizes"): a 256 x 192 tile, alone or (BF16) beside the
 //     256 x 256 one in a second launch over the last columns, when that
-//     fills the last round of workgroups better (plan_large).
+//     fills the last round of workgroups better, and for the dense GEMMs a
+//     192 x 192 tile where a problem fits one round of it (plan_large's
+//     cost model).  MN-major operands take the 256 x 192 tile.
 //   * Tile order is XCD-aware: workgroups are dealt to the 8 XCDs round
 //     robin, so the block index is remapped to give each XCD a contiguous
 //     band of tiles (its L2 then holds the shared A rows / B columns).
@@ -1303,7 +1305,9 @@ hipError_t launch_plan(const GemmPlan& plan, GemmParams p, int mode, int sf_fmt,
 // do not fit in LDS): the 256 x 256 tile, which measured fastest on all the
 // large dense and grouped shapes whose tiles fill whole rounds of the CUs,
 // with the 256 x 192 tile taking all or part of the columns when that fills
-// the last round better (plan_large).
+// the last round better, or (dense only) the 192 x 192 tile where a problem
+// fits one round of it (plan_large, dense_q_wins).  One B scale per row of B
+// takes the 256 x 192 or 192 x 192 tile above 128 rows.
 GemmPlan fp8_gemm_plan(int mode, int64_t G, int64_t M, int64_t N, int64_t K, int sf_fmt) {
   if (M > 128 && (sf_fmt & SF_ROWB)) {
     // row scales: the 256 x 192 tile (the 256 x 256 FP32 kernel has no
