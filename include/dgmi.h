@@ -116,7 +116,9 @@ int fp8_gemm_nt(const dg_tensor* a, const dg_tensor* b, const dg_tensor* sfa,
  * for fp8_gemm_nt (sfa is [M, K/128], sfb [ceil(N/128), K/128] whatever the
  * operands' layout).  An MN-major operand is row-major in its stored shape,
  * with a 16-byte aligned base and a K-row stride (bytes) that is a multiple
- * of 16 in [rows, 2^28]; its row count (M or N) must be a multiple of 16
+ * of 16, at least its row count, and small enough that K x stride < 2^31 - 256
+ * (the operand is addressed with 32-bit offsets); its row count (M or N) must
+ * be a multiple of 16
  * (else DG_UNSUPPORTED).  Block scales only (FP32 or packed UE8M0), BF16 d
  * (one scale per row of B, or an F32 d: DG_UNSUPPORTED).  The fragments of an
  * MN-major operand are read from LDS with transposing loads; results equal

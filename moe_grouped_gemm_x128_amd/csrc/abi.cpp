@@ -263,8 +263,12 @@ int fp8_gemm_common(int mode, const dg_tensor* a, const dg_tensor* b, const dg_t
     if ((a_mn && M % 16) || (b_mn && N % 16))
       return fail(DG_UNSUPPORTED, "%s: an MN-major operand needs its row count (M or N) to be a multiple of 16",
                   fname);
-    if ((a_mn && (lda < M || lda > (int64_t(1) << 28))) || (b_mn && (ldb < N || ldb > (int64_t(1) << 28))))
-      return fail(DG_UNSUPPORTED, "%s: the K-row stride of an MN-major operand must lie in [rows, 2^28]", fname);
+    if ((a_mn && lda < M) || (b_mn && ldb < N))
+      return fail(DG_UNSUPPORTED, "%s: the K-row stride of an MN-major operand must be at least its row count", fname);
+    // the kernels address an MN-major operand with 32-bit offsets from its first K-row
+    const int64_t lim = (int64_t(1) << 31) - 256;
+    if ((a_mn && K * lda > lim) || (b_mn && K * ldb > lim))
+      return fail(DG_UNSUPPORTED, "%s: an MN-major operand must span less than 2^31 bytes (K x K-row stride)", fname);
   }
   // alignment: 16-B operand rows (the kernels load 16-B chunks), 16-B output rows
   if (!aligned(a->data, 16) || !aligned(b->data, 16) || lda % 16 || ldb % 16 || va.sg % 16 || vb.sg % 16)

@@ -536,26 +536,35 @@ __global__ __launch_bounds__(T::NT) void gemm_kernel(const GemmParams p) {
   // MN-major operand (stored [K, R] with K-rows ld bytes apart, R = M or N):
   // instruction j fills K-rows [4(j NW + wave), +4) of the stage, lane l the
   // 16-byte slot l % 16 of K-row 4(j NW + wave) + l / 16, from the tile's
-  // logical chunk (l % 16) ^ hmn(row).  The buffer resource starts at the
-  // instruction's first K-row of slice kb, column r0, and ends after the
-  // operand's last valid byte: past the matrix's last K-row it reads zeros,
-  // and columns past R in earlier K-rows only feed output rows or columns
-  // that are never stored.
+  // logical chunk (l % 16) ^ hmn(row).  One buffer resource per operand
+  // starts at column r0 of K-row 0 and ends after the operand's last valid
+  // byte, so columns past R in the last K-row read zeros (in earlier K-rows
+  // they only feed output rows or columns that are never stored); the lane
+  // offset carries the K-row, slice included (the host keeps K x ld below
+  // 2^31), so a slice's loads need no scalar address work.
   const int k_rows = KB * BK;
-  auto issue_mn_one = [&](uint8_t* stage, const uint8_t* base, int64_t ld, int r0, int r_valid, int kb, int j) {
-    const int kr = 4 * (j * T::NW + wave);            // first K-row of the instruction in the slice
-    const int krow = kr + (lane >> 4);
-    const uint32_t voff = (uint32_t)((lane >> 4) * ld + (((lane & 15) ^ hmn(krow)) << 4));
-    const int64_t first = (int64_t)kb * BK + kr;      // K-row of the resource's start
-    const int64_t avail = (int64_t)(k_rows - first - 1) * ld + (r_valid - r0);
-    const uint32_t nrec = (uint32_t)max((int64_t)0, min(avail, (int64_t)0x7fffffff));
-    const __amdgpu_buffer_rsrc_t rsrc =
-        __builtin_amdgcn_make_buffer_rsrc((void*)(base + first * ld + r0), (short)0, (int)nrec, 0x00020000);
+  auto mn_rsrc = [&](const uint8_t* base, int64_t ld, int r0, int r_valid) {
+    const int64_t avail = (int64_t)(k_rows - 1) * ld + (r_valid - r0);
+    const int nrec = (int)max((int64_t)0, min(avail, (int64_t)0x7fffffff));
+    return __builtin_amdgcn_make_buffer_rsrc((void*)(base + r0), (short)0, nrec, 0x00020000);
+  };
+  const __amdgpu_buffer_rsrc_t a_mn_rsrc = mn_rsrc(A, A_MN ? p.lda : 0, m0, min(row_lim, m0 + hi));
+  const __amdgpu_buffer_rsrc_t b_mn_rsrc = mn_rsrc(B, B_MN ? p.ldb : 0, n0, p.N);
+  // CH: 16-byte chunks of the tile's rows per K-row (16, or 12 on a 192-row
+  // side).  A lane whose logical chunk lies past them gets an offset beyond
+  // the resource (at least 2^31), so the range check turns its load into
+  // zeros with no memory access; no fragment read touches its slot.
+  auto issue_mn_one = [&](auto ch_tag, uint8_t* stage, __amdgpu_buffer_rsrc_t rsrc, int64_t ld, int kb, int j) {
+    constexpr int CH = decltype(ch_tag)::value;
+    const int krow = 4 * (j * T::NW + wave) + (lane >> 4);  // K-row in the slice
+    const int chunk = (lane & 15) ^ hmn(krow);
+    uint32_t voff = (uint32_t)(kb * BK + krow) * (uint32_t)ld + (uint32_t)(chunk << 4);
+    if constexpr (CH < 16) voff = chunk < CH ? voff : 0x80000000u;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)(stage + (j * T::NW + wave) * 1024), 16, voff, 0, 0, 0);
   };
   auto issue_a_one = [&](uint8_t* stage, int kb, int j) {
     if constexpr (A_MN) {
-      issue_mn_one(stage, A, p.lda, m0, min(row_lim, m0 + hi), kb, j);
+      issue_mn_one(std::integral_constant<int, T::BM / 16>{}, stage, a_mn_rsrc, p.lda, kb, j);
       return;
     }
     const uint32_t hu = (uint32_t)swz((j * T::NW + wave) * 8);
@@ -566,7 +575,7 @@ __global__ __launch_bounds__(T::NT) void gemm_kernel(const GemmParams p) {
   };
   auto issue_b_one = [&](uint8_t* stage, int kb, int j) {
     if constexpr (B_MN) {
-      issue_mn_one(stage, B, p.ldb, n0, p.N, kb, j);
+      issue_mn_one(std::integral_constant<int, T::BN / 16>{}, stage, b_mn_rsrc, p.ldb, kb, j);
       return;
     }
     const uint32_t hu = (uint32_t)swz((j * T::NW + wave) * 8);

@@ -230,8 +230,8 @@ def test_dense_validation_errors(lib):
 
 def test_mn_major_validation_errors(lib):
     """fp8_gemm_nn / _tn / _tt: stored operands row-major; an MN-major operand
-    needs rows % 16 == 0, a K-row stride in [rows, 2^28] that is a multiple
-    of 16, block scales and a BF16 d."""
+    needs rows % 16 == 0, a K-row stride of at least its rows that is a
+    multiple of 16 with K x stride below 2^31, block scales and a BF16 d."""
     D = binding.describe
     M, N, K = 128, 256, 512
     a, a_st = _t((M, K), torch.uint8), _t((K, M), torch.uint8)
@@ -258,6 +258,14 @@ def test_mn_major_validation_errors(lib):
     # K-row stride below the row count, and not a multiple of 16
     short = _t((K, N), torch.uint8, stride=(N - 16, 1))
     assert call("fp8_gemm_nn", a, short) == binding.DG_UNSUPPORTED
+    # an operand spanning 2^31 bytes or more (descriptor only: K = 8192 K-rows 2^18 bytes apart)
+    Kb = 8192
+    big = D(b_st)
+    big.shape[0], big.stride[0] = Kb, 1 << 18
+    ab = _t((M, Kb), torch.uint8)
+    rc = lib.fp8_gemm_nn(ctypes.byref(D(ab)), ctypes.byref(big), ctypes.byref(D(_t((M, Kb // 128), torch.float32))),
+                         ctypes.byref(D(_t((N // 128, Kb // 128), torch.float32))), None, ctypes.byref(D(d)), None)
+    assert rc == binding.DG_UNSUPPORTED and "2^31" in binding.last_error()
     odd = _t((K, N + 8), torch.uint8)[:, :N]
     assert call("fp8_gemm_nn", a, odd) == binding.DG_INVALID_ARG
     assert "aligned" in binding.last_error()
