@@ -257,3 +257,112 @@ def test_two_launch_plan_replays_under_capture():
         torch.cuda.synchronize()
         assert np.array_equal(to_host(d), got), f"replay {r} differs from eager"
         assert not np.any(got == SENTINEL_BF16), "elements left unwritten"
+
+
+def test_layouts_and_accumulate_forms_replay_under_capture():
+    """The NN / TN / TT GEMMs on FP8 operands stored MN-major, the masked
+    grouped GEMM with an F32 accumulate input and F32 output, the contiguous
+    grouped GEMM with a BF16 accumulate input and the dense GEMM with FP8
+    output, captured in one graph and replayed three times with new
+    operands written between replays (casts and transposed copies run
+    eagerly, outside the graph): every replay bit-identical to eager calls,
+    the MN-major results equal to the NT GEMM's, and the masked result
+    within the F32 bound of the oracle's C + A . B^T."""
+    mg = _mg()
+    M, N, K, G, max_m = 256, 384, 512, 2, 128
+    layout = torch.tensor([1, 0, 0, -1], dtype=torch.int32, device="cuda")
+    Msum = 4 * 128
+    masked_m = torch.tensor([100, 37], dtype=torch.int32, device="cuda")
+    dev = "cuda"
+    xa, xb = torch.empty((M, K), device=dev), torch.empty((N, K), device=dev)
+    xga, xgb = torch.empty((G * max_m, K), device=dev), torch.empty((G, N, K), device=dev)
+    xc = torch.empty((Msum, K), device=dev)
+    qa, qb = torch.empty((M, K), dtype=torch.uint8, device=dev), torch.empty((N, K), dtype=torch.uint8, device=dev)
+    sfa = torch.empty((K // 128, M), dtype=torch.float32, device=dev).t()
+    sfb = torch.empty((N // 128, K // 128), dtype=torch.float32, device=dev)
+    a_t = torch.empty((K, M), dtype=torch.uint8, device=dev)  # A stored [K, M]
+    b_t = torch.empty((K, N), dtype=torch.uint8, device=dev)  # B stored [K, N]
+    qga = torch.empty((G * max_m, K), dtype=torch.uint8, device=dev)
+    sfga = torch.empty((G * max_m, K // 128), dtype=torch.float32, device=dev)
+    qgb = torch.empty((G, N, K), dtype=torch.uint8, device=dev)
+    sfgb = torch.empty((G, N // 128, K // 128), dtype=torch.float32, device=dev)
+    qc = torch.empty((Msum, K), dtype=torch.uint8, device=dev)
+    sfc = torch.empty((Msum, K // 128), dtype=torch.float32, device=dev)
+    cm = torch.empty((G, max_m, N), dtype=torch.float32, device=dev)
+    cc = torch.empty((Msum, N), dtype=torch.bfloat16, device=dev)
+    outs = {
+        "nn": torch.empty((M, N), dtype=torch.bfloat16, device=dev),
+        "tn": torch.empty((M, N), dtype=torch.bfloat16, device=dev),
+        "tt": torch.empty((M, N), dtype=torch.bfloat16, device=dev),
+        "dm": torch.empty((G, max_m, N), dtype=torch.float32, device=dev),
+        "dc": torch.empty((Msum, N), dtype=torch.bfloat16, device=dev),
+        "q": torch.empty((M, N), dtype=torch.uint8, device=dev),
+        "sfq": torch.empty((M, N // 128), dtype=torch.float32, device=dev),
+    }
+    a3, sfa3 = qga.view(G, max_m, K), sfga.view(G, max_m, K // 128)
+
+    def step():
+        mg.fp8_gemm_nn(qa, b_t, sfa, sfb, None, outs["nn"])
+        mg.fp8_gemm_tn(a_t, b_t, sfa, sfb, None, outs["tn"])
+        mg.fp8_gemm_tt(a_t, qb, sfa, sfb, None, outs["tt"])
+        mg.m_grouped_fp8_gemm_nt_masked(a3, qgb, sfa3, sfgb, outs["dm"], masked_m, max_m, c=cm)
+        mg.m_grouped_fp8_gemm_nt_contiguous(qc, qgb, sfc, sfgb, outs["dc"], layout, c=cc)
+        mg.fp8_gemm_nt_fp8_out(qa, qb, sfa, sfb, None, outs["q"], outs["sfq"])
+
+    def fill(seed):
+        for i, t in enumerate((xa, xb, xga, xgb, xc, cm)):
+            t.copy_(torch.from_numpy(synth.normal_f32(seed + i, tuple(t.shape))))
+        cc.copy_(torch.from_numpy(synth.normal_f32(seed + 9, tuple(cc.shape))))
+        mg.per_token_cast_to_fp8(xa, qa, sfa)
+        mg.per_block_cast_to_fp8(xb, qb, sfb)
+        mg.per_token_cast_to_fp8(xga, qga, sfga)
+        mg.per_block_cast_to_fp8(xgb, qgb, sfgb)
+        mg.per_token_cast_to_fp8(xc, qc, sfc)
+        a_t.copy_(qa.t())
+        b_t.copy_(qb.t())
+        for o in outs.values():
+            o.view(torch.uint8).fill_(0x5A)
+
+    fill(800)
+    step()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        graph.capture_begin()
+        step()
+        graph.capture_end()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    nt = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    for r in range(3):
+        say(f"layouts / accumulate graph replay {r}")
+        fill(810 + 10 * r)
+        graph.replay()
+        torch.cuda.synchronize()
+        got = {k: to_host(v).copy() for k, v in outs.items()}
+        fill(810 + 10 * r)
+        step()
+        torch.cuda.synchronize()
+        for k, v in outs.items():
+            assert np.array_equal(to_host(v), got[k]), f"replay {r}: {k} differs from eager"
+        mg.fp8_gemm_nt(qa, qb, sfa, sfb, None, nt)
+        torch.cuda.synchronize()
+        for k in ("nn", "tn", "tt"):
+            assert np.array_equal(got[k], to_host(nt)), f"replay {r}: {k} differs from the NT GEMM"
+        # rows past masked_m and skipped blocks keep the fill pattern
+        assert np.all(got["dm"][0, 100:].view(np.uint8) == 0x5A) and np.all(got["dm"][1, 37:].view(np.uint8) == 0x5A)
+        assert np.all(got["dc"][384:].view(np.uint8) == 0x5A)
+    # the last replay's masked result against the oracle (F32 output: C + A . B^T)
+    ra, rsfa = oracle.per_token_cast_to_fp8(to_host(xga).reshape(G, max_m, K))
+    rb, rsfb = oracle.per_block_cast_to_fp8(to_host(xgb))
+    cmh = to_host(cm).astype(np.float64)
+    for g, m in enumerate((100, 37)):
+        ref = cmh[g, :m] + oracle.fp8_gemm_nt(ra[g, :m], rb[g], rsfa[g, :m], rsfb[g])
+        # the bound of the F32-output tests: (2^-15 + (K/128 + 2) 2^-24) x the sum of absolute terms
+        S = oracle.fp8_gemm_nt(ra[g, :m] & np.uint8(0x7F), rb[g] & np.uint8(0x7F), np.abs(rsfa[g, :m]),
+                               np.abs(rsfb[g])) + np.abs(cmh[g, :m])
+        bound = (2.0 ** -15 + (K // 128 + 2) * 2.0 ** -24) * S * (1 + 1e-6)
+        err = np.abs(got["dm"][g, :m].astype(np.float64) - ref)
+        assert np.all(err <= bound), f"masked F32 group {g}: max err / bound {(err / bound).max()}"
