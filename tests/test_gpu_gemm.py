@@ -372,6 +372,34 @@ def test_contiguous_mixed_groups_256x256_tile():
     assert_bf16_close(got[written], ref[written], "contiguous 256 x 256 tile")
 
 
+@pytest.mark.parametrize("layout", [[0, 1, 1], [1, 1, 0, 0, 2], [-1, 2, 2]])
+def test_contiguous_odd_block_counts(layout):
+    """256-row tiles on an odd number of 128-row blocks: the odd-block copy
+    of the grid reaches past the last block, and runs end on a single block."""
+    say(f"contiguous odd block count {layout}")
+    mg = _mg()
+    from moe_grouped_gemm_x128_amd import binding
+
+    G, N, K = 3, 200, 256
+    layout = np.array(layout, dtype=np.int32)
+    Msum = layout.size * 128
+    c = binding.query_config(binding.DG_KIND_CONTIGUOUS, G, Msum, N, K)
+    assert c["block_m"] == 256
+    xa = synth.normal_f32(129, (Msum, K))
+    xb = synth.normal_f32(130, (G, N, K))
+    a, sfa = q_tok(to_dev(xa))
+    b, sfb = q_blk(to_dev(xb))
+    d = sentinel_like((Msum, N))
+    mg.m_grouped_fp8_gemm_nt_contiguous(a, b, sfa, sfb, d, to_dev(layout))
+    torch.cuda.synchronize()
+    ra, rsfa = oracle.per_token_cast_to_fp8(xa)
+    rb, rsfb = oracle.per_block_cast_to_fp8(xb)
+    ref, written = oracle.m_grouped_fp8_gemm_nt_contiguous(ra, rb, rsfa, rsfb, layout)
+    got = to_host(d)
+    assert np.all(got[~written] == SENTINEL_BF16)
+    assert_bf16_close(got[written], ref[written], "contiguous odd block count")
+
+
 def test_contiguous_long_runs_at_odd_offsets():
     """Runs of one group longer than 64 blocks (the run-start scan takes
     several windows), starting at odd block offsets, with odd lengths (a
