@@ -73,6 +73,97 @@ def assert_bf16_close(got_bits, ref, what=""):
         raise AssertionError(f"{what}: {int(bad.sum())} elements outside tolerance (rms {rms:.4g}); {details}")
 
 
+# Bound of an FP32 GEMM output against the float64 oracle.
+#
+# S is the sum of the absolute values of every term of the output (C
+# included); u = 2^-24.  FP32 additions that round to nearest, in any order,
+# stay within n u S for n roundings (first order in u).
+#
+# The FP8 matrix core does not sum a 128-term block in FP32.  Measured on
+# gfx950 (one 16x16x128 instruction on crafted operands): it adds the
+# products in groups of 8 consecutive K values; inside a group every product
+# is truncated toward zero to a multiple of 2^(E - 13), E the largest
+# exponent sum e_a + e_b of the group's operand pairs; the truncated
+# products add exactly, and the group sums and the accumulator combine with
+# FP32 round-to-nearest additions.  Only products below the group's largest
+# exponent lose bits, so a group is off by less than 7 * 2^(E - 13) <=
+# 7 * 2^-13 * max|a| * max|b| over the group.  Summed over the groups of all
+# blocks (times the block's scales) that is 7 * 2^-13 * G, G the GEMM of the
+# per-group maxima (fp8_group_max_codes).  This is why the FP8 partial sums
+# are promoted to FP32 every 128 K ("DeepGEMM tested by Novita AI",
+# "Technological Innovations": the tensor core's accumulation keeps only
+# limited precision).  The FP32 roundings of an FP8 GEMM are, per block,
+# 15 additions of group sums and one of the accumulator inside the matrix
+# core, the scale product and the promoting FMA (fp8_rounding_count).
+# The BF16 matrix core also truncates inside groups of 8 products, to a
+# multiple of 2^(E - 24) or finer: less than 7 u of the group's largest
+# product, inside the (K + 2) u S that bound already allows.
+U = 2.0 ** -24
+FP8_GROUP = 8
+FP8_GROUP_ERR = 7 * 2.0 ** -13
+
+
+def fp8_rounding_count(K):
+    return 18 * (K // 128)
+
+
+def fp8_group_max_codes(codes):
+    """E4M3 codes [.., K] (K a multiple of 128) -> codes of the same shape
+    whose 128-wide block kb holds, at positions 0..15, the largest absolute
+    value of each group of 8 consecutive K values of that block, and zeros
+    elsewhere: the oracle's block-scaled GEMM of two such arrays is G."""
+    c = np.asarray(codes, dtype=np.uint8) & np.uint8(0x7F)  # positive codes order as their values
+    lead, K = c.shape[:-1], c.shape[-1]
+    assert K % 128 == 0
+    g = c.reshape(lead + (K // 128, 128 // FP8_GROUP, FP8_GROUP)).max(axis=-1)
+    out = np.zeros(lead + (K // 128, 128), dtype=np.uint8)
+    out[..., :128 // FP8_GROUP] = g
+    return out.reshape(c.shape)
+
+
+def fp8_bound_terms(gemm, ra, rb, rsfa, rsfb, *rest):
+    """S and G of an FP8 GEMM from the oracle's own GEMM `gemm` (dense,
+    masked or contiguous; `rest` its further arguments): S over the absolute
+    codes and scales, G over the group maxima.  Grouped forms return their
+    row mask too, which is dropped."""
+    def run(a, b):
+        r = gemm(a, b, np.abs(rsfa), np.abs(rsfb), *rest)
+        return r[0] if isinstance(r, tuple) else r
+
+    return run(abs_fp8(ra), abs_fp8(rb)), run(fp8_group_max_codes(ra), fp8_group_max_codes(rb))
+
+
+def assert_f32_close(got, ref, S, nround, what, G=None):
+    """got float32 from the device, ref float64 exact, S the sum of absolute
+    terms (C included), G the FP8 group term (None for BF16 GEMMs); bound
+    FP8_GROUP_ERR G + (nround + 2) u S.  Most outputs must also carry bits
+    below BF16 precision (an F32 output rounded to BF16 would pass a loose
+    bound)."""
+    assert got.shape == ref.shape, what
+    assert np.all(np.isfinite(got)), f"{what}: non-finite (unwritten) output"
+    if got.size == 0:
+        return
+    bound = (nround + 2) * U * S * (1 + 1e-6) + np.finfo(np.float32).tiny
+    if G is not None:
+        bound = bound + FP8_GROUP_ERR * G * (1 + 1e-6)
+    err = np.abs(got.astype(np.float64) - ref)
+    say(f"  {what}: largest error / S = 2^{np.log2(max(float((err / np.maximum(S, 1e-300)).max()), 2.0 ** -60)):.1f}, "
+        f"/ bound = {float((err / bound).max()):.3g}")
+    bad = err > bound
+    if bad.any():
+        i = tuple(np.argwhere(bad)[0])
+        raise AssertionError(f"{what}: {int(bad.sum())} outside the bound; first {i}: got {got[i]!r} ref {ref[i]!r} "
+                             f"bound {bound[i]:.3g}")
+    if got.size >= 64:
+        fine = (np.ascontiguousarray(got, dtype=np.float32).view(np.uint32) & np.uint32(0xFFFF)) != 0
+        assert fine.mean() > 0.5, f"{what}: {fine.mean():.2f} of the outputs have bits below BF16 precision"
+
+
+def abs_fp8(codes):
+    """E4M3 codes with the sign bit cleared: the codes of the absolute values."""
+    return np.asarray(codes, dtype=np.uint8) & np.uint8(0x7F)
+
+
 # ---------------------------------------------------------------------------
 # Exact binary32 rounding (host-side pins; no numpy float32 arithmetic)
 # ---------------------------------------------------------------------------

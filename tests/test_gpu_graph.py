@@ -17,7 +17,8 @@ import pytest
 import oracle
 from moe_grouped_gemm_x128_amd import synth
 
-from helpers import SENTINEL_BF16, assert_bf16_close, say, to_dev, to_host
+from helpers import (SENTINEL_BF16, assert_bf16_close, assert_f32_close, fp8_bound_terms, fp8_rounding_count, say,
+                     to_dev, to_host)
 
 pytestmark = pytest.mark.gpu
 
@@ -360,9 +361,6 @@ def test_layouts_and_accumulate_forms_replay_under_capture():
     cmh = to_host(cm).astype(np.float64)
     for g, m in enumerate((100, 37)):
         ref = cmh[g, :m] + oracle.fp8_gemm_nt(ra[g, :m], rb[g], rsfa[g, :m], rsfb[g])
-        # the bound of the F32-output tests: (2^-15 + (K/128 + 2) 2^-24) x the sum of absolute terms
-        S = oracle.fp8_gemm_nt(ra[g, :m] & np.uint8(0x7F), rb[g] & np.uint8(0x7F), np.abs(rsfa[g, :m]),
-                               np.abs(rsfb[g])) + np.abs(cmh[g, :m])
-        bound = (2.0 ** -15 + (K // 128 + 2) * 2.0 ** -24) * S * (1 + 1e-6)
-        err = np.abs(got["dm"][g, :m].astype(np.float64) - ref)
-        assert np.all(err <= bound), f"masked F32 group {g}: max err / bound {(err / bound).max()}"
+        S, Gt = fp8_bound_terms(oracle.fp8_gemm_nt, ra[g, :m], rb[g], rsfa[g, :m], rsfb[g])
+        assert_f32_close(got["dm"][g, :m], ref, S + np.abs(cmh[g, :m]), fp8_rounding_count(K), f"masked F32 group {g}",
+                         G=Gt)
