@@ -90,8 +90,8 @@ int dgmi_init(void);
  *   d   BF16 [M, N], any row stride (innermost stride 1); or F32 [M, N],
  *       4-B aligned: the FP32 accumulator (C added) stored without rounding
  *       (the section's call takes the output dtype as an argument); with
- *       c = d in F32 this is the in-place D += A . B^T.  F32 d takes one
- *       scale per 128x128 block of B only (per-row scales: DG_UNSUPPORTED).
+ *       c = d in F32 this is the in-place D += A . B^T.  Either scale form
+ *       of B goes with either output dtype.
  * D[m,n] = C[m,n] + sum_kb (sum_{k in kb} A[m,k] B[n,k]) * sfa[m,kb] * sfb[n/128,kb]
  * (sfb[n,kb] with one scale per row of B).
  * K must be a multiple of 128; M and N are arbitrary.
@@ -160,7 +160,7 @@ int fp8_gemm_nt_fp8_out(const dg_tensor* a, const dg_tensor* b, const dg_tensor*
  *   sfa as fp8_gemm_nt with M = Msum;  sfb [G, ceil(N/128), ...] or, one
  *       per row of B, [G, N, ...]
  *   d   BF16 [Msum, N], or F32 [Msum, N] (4-B aligned): the FP32
- *       accumulator stored without rounding (block scales of B only)
+ *       accumulator stored without rounding
  *   grouped_layout I32 [Msum/128] on the device: group id of each 128-row
  *       block; a negative id marks a block to skip (its rows of d are not
  *       written).  Ids >= G are treated as skipped as well.
@@ -179,8 +179,7 @@ int m_grouped_fp8_gemm_nt_contiguous(const dg_tensor* a, const dg_tensor* b,
  *   sfb F32 [G, ceil(N/128), K/128] or packed I32 (or one per row of B:
  *       [G, N, ...])
  *   d   BF16 [G, max_m, N] (or [G*max_m, N]), or F32 of that shape (4-B
- *       aligned): the FP32 accumulator stored without rounding (block scales
- *       of B only)
+ *       aligned): the FP32 accumulator stored without rounding
  *   masked_m I32 [G] on the device: group g computes its first
  *       clamp(masked_m[g], 0, max_m) rows; every other row of d is left
  *       untouched.  Read only by the kernels, never by the host.

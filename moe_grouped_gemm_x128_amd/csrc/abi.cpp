@@ -251,9 +251,7 @@ int fp8_gemm_common(int mode, const dg_tensor* a, const dg_tensor* b, const dg_t
   if (mode == dgmi::MODE_DENSE && (sfb->ndim != 2 || sfa->ndim != 2))
     return fail(DG_INVALID_ARG, "%s: sfa and sfb must be 2-D", fname);
   if (mode == dgmi::MODE_CONTIG && sfb->ndim != 3) return fail(DG_INVALID_ARG, "%s: sfb must be [G, ceil(N/128), ..]", fname);
-  if ((fp8_out || d_f32) && rowb)
-    return fail(DG_UNSUPPORTED, "%s: one B scale per row is not supported with %s output", fname,
-                fp8_out ? "FP8" : "F32");
+  if (fp8_out && rowb) return fail(DG_UNSUPPORTED, "%s: one B scale per row is not supported with FP8 output", fname);
 
   // MN-major operands: K-rows of M (N) bytes, 16-byte aligned, ld bytes apart
   const int64_t lda = a_mn ? a->stride[1] : va.sr, ldb = b_mn ? b->stride[1] : vb.sr;

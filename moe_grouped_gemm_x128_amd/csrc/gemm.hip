@@ -1097,7 +1097,7 @@ template <class T, int KIND, bool ROWB>
 hipError_t launch_tile(const GemmParams& p, int mode, int sf_fmt, int64_t grid, hipStream_t stream) {
   const dim3 g((unsigned)grid), b(T::NT);
   if (p.d_f32) {
-    // FP32 D: block scales; the BF16 kind dense only
+    // FP32 D: block or row scales; the BF16 kind dense only
     if constexpr (KIND == KIND_BF16) {
       if (mode != MODE_DENSE) return hipErrorInvalidValue;
       gemm_kernel<T, KIND_BF16, SF_F32, MODE_DENSE, OUT_F32><<<g, b, 0, stream>>>(p);
@@ -1108,9 +1108,16 @@ hipError_t launch_tile(const GemmParams& p, int mode, int sf_fmt, int64_t grid, 
     else if (mode == MODE_CONTIG) gemm_kernel<T, KIND_FP8, SF_, MODE_CONTIG, OUT_F32><<<g, b, 0, stream>>>(p); \
     else gemm_kernel<T, KIND_FP8, SF_, MODE_MASKED, OUT_F32><<<g, b, 0, stream>>>(p);                       \
   } while (0)
-      if (sf_fmt == SF_F32) DGMI_LAUNCH_F32(SF_F32);
-      else if (sf_fmt == SF_UE8M0) DGMI_LAUNCH_F32(SF_UE8M0);
-      else return hipErrorInvalidValue;
+      if (sf_fmt == SF_F32) {
+        DGMI_LAUNCH_F32(SF_F32);
+      } else if (sf_fmt == SF_UE8M0) {
+        DGMI_LAUNCH_F32(SF_UE8M0);
+      } else if constexpr (ROWB) {
+        if (sf_fmt == (SF_F32 | SF_ROWB)) DGMI_LAUNCH_F32(SF_F32 | SF_ROWB);
+        else DGMI_LAUNCH_F32(SF_UE8M0 | SF_ROWB);
+      } else {
+        return hipErrorInvalidValue;  // the launch plan never picks this tile for row scales
+      }
 #undef DGMI_LAUNCH_F32
     }
     return hipGetLastError();
@@ -1153,18 +1160,20 @@ hipError_t launch_tile_fp8_out(const GemmParams& p, int sf_fmt, int64_t grid, hi
   return hipGetLastError();
 }
 
-// Launch the 192 x 192 tile: the dense GEMMs only (FP8 with block scales,
-// FP32 or UE8M0, or BF16; BF16 or FP32 output).  Its 192-row tiles do not
+// Launch the 192 x 192 tile: the dense GEMMs only (FP8 with block or row
+// scales, FP32 or UE8M0, or BF16; BF16 or FP32 output).  Its 192-row tiles do not
 // align with the 128-row blocks of the grouped layouts.
 template <int KIND>
 hipError_t launch_tile_q(const GemmParams& p, int mode, int sf_fmt, int64_t grid, hipStream_t stream) {
   if constexpr (KIND == KIND_FP8) {
     if (mode != MODE_DENSE) return hipErrorInvalidValue;
     const dim3 g((unsigned)grid), b(TileQ::NT);
-    if (sf_fmt == (SF_F32 | SF_ROWB) && !p.d_f32) {
-      gemm_kernel<TileQ, KIND_FP8, SF_F32 | SF_ROWB, MODE_DENSE><<<g, b, 0, stream>>>(p);
-    } else if (sf_fmt == (SF_UE8M0 | SF_ROWB) && !p.d_f32) {
-      gemm_kernel<TileQ, KIND_FP8, SF_UE8M0 | SF_ROWB, MODE_DENSE><<<g, b, 0, stream>>>(p);
+    if (sf_fmt == (SF_F32 | SF_ROWB)) {
+      if (p.d_f32) gemm_kernel<TileQ, KIND_FP8, SF_F32 | SF_ROWB, MODE_DENSE, OUT_F32><<<g, b, 0, stream>>>(p);
+      else gemm_kernel<TileQ, KIND_FP8, SF_F32 | SF_ROWB, MODE_DENSE><<<g, b, 0, stream>>>(p);
+    } else if (sf_fmt == (SF_UE8M0 | SF_ROWB)) {
+      if (p.d_f32) gemm_kernel<TileQ, KIND_FP8, SF_UE8M0 | SF_ROWB, MODE_DENSE, OUT_F32><<<g, b, 0, stream>>>(p);
+      else gemm_kernel<TileQ, KIND_FP8, SF_UE8M0 | SF_ROWB, MODE_DENSE><<<g, b, 0, stream>>>(p);
     } else if (sf_fmt != SF_F32 && sf_fmt != SF_UE8M0) {
       return hipErrorInvalidValue;
     } else if (p.d_f32) {

@@ -180,7 +180,7 @@ def test_dense_validation_errors(lib):
     # wrong dtype of d (BF16 or F32 only)
     assert _call_dense(lib, a, b, sfa, sfb, _t((M, N), torch.int32)) == binding.DG_INVALID_ARG
     assert "dtype" in binding.last_error()
-    # F32 d: 4-byte aligned, block scales only, dense only
+    # F32 d: 4-byte aligned
     D = binding.describe
     f32buf = torch.empty((M, N + 1), dtype=torch.float32)
     dmis = D(f32buf[:, :N])
@@ -188,9 +188,6 @@ def test_dense_validation_errors(lib):
     assert lib.fp8_gemm_nt(ctypes.byref(D(a)), ctypes.byref(D(b)), ctypes.byref(D(sfa)), ctypes.byref(D(sfb)), None,
                            ctypes.byref(dmis), None) == binding.DG_INVALID_ARG
     assert "aligned" in binding.last_error()
-    assert _call_dense(lib, a, b, sfa, _t((N, K // 128), torch.float32), _t((M, N), torch.float32)) \
-        == binding.DG_UNSUPPORTED
-    assert "F32 output" in binding.last_error()
     # K mismatch
     assert _call_dense(lib, a, _t((N, K + 128), torch.uint8), sfa, sfb, d) == binding.DG_INVALID_ARG
     # wrong scale shape (neither one per 128x128 block nor one per row)
@@ -294,9 +291,6 @@ def test_masked_validation_errors(lib):
     assert call(mm=_t((G,), torch.float32)) == binding.DG_INVALID_ARG
     assert call(max_m=max_m + 1) == binding.DG_INVALID_ARG
     assert call(d=_t((G, max_m, N + 8), torch.bfloat16)) == binding.DG_INVALID_ARG
-    # F32 d: block scales only (one scale per row of B is unsupported with it)
-    assert call(d=_t((G, max_m, N), torch.float32), sfb=_t((G, N, K // 128), torch.float32)) \
-        == binding.DG_UNSUPPORTED
     # accumulate form: c with d's shape, BF16 or F32, not overlapping d partly
     def acc(c, d=d):
         return lib.m_grouped_fp8_gemm_nt_masked_acc(ctypes.byref(D(a)), ctypes.byref(D(b)), ctypes.byref(D(sfa)),

@@ -439,3 +439,108 @@ def test_grouped_accumulate_on_256x256_tiles(form, d_kind, c_kind):
         assert np.array_equal(got[~written], untouched), "rows that are not computed changed"
     else:
         assert np.all(got[~written] == 0), "rows that are not computed were written"
+
+
+# one FP32 B scale (or UE8M0 exponent) per row of B with an F32 d: the
+# 128-row tiles, the 192 x 192 and the 256 x 192 tile (dense), and both
+# grouped forms on the 256 x 192 tile, C in place
+@pytest.mark.parametrize("M,N,K", [(64, 100, 384), (100, 300, 256), (1000, 700, 512), (4096, 2880, 256)])
+@pytest.mark.parametrize("ue8m0", [False, True])
+def test_fp8_dense_f32_out_per_row_b_scales(M, N, K, ue8m0):
+    from moe_grouped_gemm_x128_amd import binding
+
+    say(f"fp8_gemm_nt F32 d, per-row B scales M={M} N={N} K={K} ue8m0={ue8m0}")
+    mg = _mg()
+    plan = binding.query_config(binding.DG_KIND_DENSE_ROWB, 1, M, N, K)
+    if M > 128:
+        assert (plan["block_m"], plan["block_n"]) == ((256, 192) if (M, N) == (4096, 2880) else (192, 192)), plan
+    xa = synth.normal_f32(761, (M, K))
+    xb = synth.normal_f32(762, (N, K))
+    xc = synth.normal_f32(763, (M, N)) * np.float32(4.0)
+    a, sfa = q_tok(to_dev(xa), ue8m0)
+    b, sfb = q_tok(to_dev(xb), ue8m0)  # [N, K/128]: one scale per row of B
+    sfb = sfb.contiguous()
+    if ue8m0:
+        pa = torch.empty((M, -(-K // 512)), dtype=torch.int32, device="cuda")
+        pb = torch.empty((N, -(-K // 512)), dtype=torch.int32, device="cuda")
+        mg.pack_ue8m0_to_int(sfa.contiguous(), pa)
+        mg.pack_ue8m0_to_int(sfb, pb)
+        sfa, sfb = pa, pb
+    buf, d = nan_f32(M, N, pad=2)
+    mg.fp8_gemm_nt(a, b, sfa, sfb, None, d)
+    d16 = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    mg.fp8_gemm_nt(a, b, sfa, sfb, None, d16)
+    dc = to_dev(xc)
+    mg.fp8_gemm_nt(a, b, sfa, sfb, dc, dc)  # in place: C + A . B^T
+    torch.cuda.synchronize()
+    assert torch.equal(d.to(torch.bfloat16).view(torch.int16), d16.view(torch.int16))
+    assert torch.isnan(buf[:, N:]).all(), "row padding written"
+    ra, rsfa = oracle.per_token_cast_to_fp8(xa, ue8m0)
+    rb, rsfb = oracle.per_token_cast_to_fp8(xb, ue8m0)
+    assert np.array_equal(to_host(a), ra) and np.array_equal(to_host(b), rb)
+    S, Gt = fp8_bound_terms(oracle.fp8_gemm_nt, ra, rb, rsfa, rsfb)
+    c = xc.astype(np.float64)
+    assert_f32_close(to_host(d), oracle.fp8_gemm_nt(ra, rb, rsfa, rsfb), S, fp8_rounding_count(K),
+                     f"fp8 F32 d per-row B scales {M}x{N}x{K}", G=Gt)
+    assert_f32_close(to_host(dc), oracle.fp8_gemm_nt(ra, rb, rsfa, rsfb, c), S + np.abs(c), fp8_rounding_count(K),
+                     f"fp8 F32 d per-row B scales, C in place {M}x{N}x{K}", G=Gt)
+
+
+@pytest.mark.parametrize("form", ["contiguous", "masked"])
+@pytest.mark.parametrize("ue8m0", [False, True])
+def test_grouped_f32_out_per_row_b_scales(form, ue8m0):
+    say(f"{form} F32 d, per-row B scales ue8m0={ue8m0}")
+    mg = _mg()
+    N, K = 272, 384
+    if form == "contiguous":
+        G = 3
+        layout = np.array([2, 2, -1, 0, 1, 0, 2, 7], dtype=np.int32)
+        rows = layout.size * 128
+    else:
+        G, max_m = 4, 160
+        mm = np.array([0, 17, 160, 999], dtype=np.int32)
+        rows = G * max_m
+    xa = synth.normal_f32(771, (rows, K))
+    xb = synth.normal_f32(772, (G, N, K))
+    xc = synth.normal_f32(773, (rows, N)) * np.float32(4.0)
+    a = torch.empty((rows, K), dtype=torch.uint8, device="cuda")
+    sfa = torch.empty((rows, K // 128), dtype=torch.float32, device="cuda")
+    mg.per_token_cast_to_fp8(to_dev(xa), a, sfa, ue8m0)
+    b = torch.empty((G, N, K), dtype=torch.uint8, device="cuda")
+    sfb = torch.empty((G, N, K // 128), dtype=torch.float32, device="cuda")
+    mg.per_token_cast_to_fp8(to_dev(xb), b, sfb, ue8m0)
+    if ue8m0:
+        pa = torch.empty((rows, 1), dtype=torch.int32, device="cuda")
+        pb = torch.empty((G, N, 1), dtype=torch.int32, device="cuda")
+        mg.pack_ue8m0_to_int(sfa, pa)
+        mg.pack_ue8m0_to_int(sfb, pb)
+        sfa, sfb = pa, pb
+    d = torch.full((rows, N), float("nan"), dtype=torch.float32, device="cuda")
+    dc = to_dev(xc)
+    ra, rsfa = oracle.per_token_cast_to_fp8(xa, ue8m0)
+    rb, rsfb = oracle.per_token_cast_to_fp8(xb, ue8m0)
+    if form == "contiguous":
+        mg.m_grouped_fp8_gemm_nt_contiguous(a, b, sfa, sfb, d, to_dev(layout))
+        mg.m_grouped_fp8_gemm_nt_contiguous(a, b, sfa, sfb, dc, to_dev(layout), c=dc)
+        ref_layout = np.where(layout < G, layout, -1)
+        ref, written = oracle.m_grouped_fp8_gemm_nt_contiguous(ra, rb, rsfa, rsfb, ref_layout)
+        S, Gt = fp8_bound_terms(oracle.m_grouped_fp8_gemm_nt_contiguous, ra, rb, rsfa, rsfb, ref_layout)
+    else:
+        sfa3 = sfa.view(G, max_m, -1)
+        mg.m_grouped_fp8_gemm_nt_masked(a.view(G, max_m, K), b, sfa3, sfb, d.view(G, max_m, N), to_dev(mm), max_m)
+        mg.m_grouped_fp8_gemm_nt_masked(a.view(G, max_m, K), b, sfa3, sfb, dc.view(G, max_m, N), to_dev(mm), max_m,
+                                        c=dc.view(G, max_m, N))
+        args = (ra.reshape(G, max_m, K), rb, rsfa.reshape(G, max_m, -1), rsfb)
+        ref, written = oracle.m_grouped_fp8_gemm_nt_masked(*args, mm, max_m)
+        S, Gt = fp8_bound_terms(oracle.m_grouped_fp8_gemm_nt_masked, *args, mm, max_m)
+        ref, written, S, Gt = ref.reshape(rows, N), written.reshape(rows), S.reshape(rows, N), Gt.reshape(rows, N)
+    torch.cuda.synchronize()
+    assert np.array_equal(to_host(a), ra) and np.array_equal(to_host(b), rb)
+    got, gotc = to_host(d), to_host(dc)
+    assert np.isnan(got[~written]).all(), "rows outside the groups written"
+    assert np.array_equal(gotc[~written], xc[~written]), "rows outside the groups changed"
+    nr = fp8_rounding_count(K)
+    assert_f32_close(got[written], ref[written], S[written], nr, f"{form} F32 d per-row B", G=Gt[written])
+    c = xc.astype(np.float64)
+    assert_f32_close(gotc[written], (ref + c)[written], (S + np.abs(c))[written], nr, f"{form} F32 d per-row B, C",
+                     G=Gt[written])

@@ -176,14 +176,6 @@ def _check(got, ref, S, Gt, written, d_kind, nround, what):
 # case generators (host only)
 # ---------------------------------------------------------------------------
 
-def _bf16_out_with_rowb(case):
-    """One B scale per row is taken with a BF16 output only (the library
-    rejects F32 and FP8 outputs with it)."""
-    if case["rowb"]:
-        case["d_kind"] = "bf16"
-    return case
-
-
 def dense_case(i):
     rng = _rng("dense", i)
     u = rng.random()
@@ -193,10 +185,9 @@ def dense_case(i):
         M, N, K = _loguni(rng, 129, 1300), _loguni(rng, 1, 1500), 128 * int(rng.integers(1, 13))
     else:
         M, N, K = int(rng.integers(1500, 4097)), int(rng.integers(1500, 4097)), 128 * int(rng.integers(1, 3))
-    return _bf16_out_with_rowb(dict(M=M, N=N, K=K, scales=_pick(rng, ["f32", "ue8m0", "packed"]),
-                                    rowb=bool(rng.random() < 0.3), d_kind=_pick(rng, ["bf16", "f32"]),
-                                    c_kind=_pick(rng, [None, "bf16", "f32", "inplace"]), pad=int(rng.integers(0, 9)),
-                                    a_m_major=bool(rng.random() < 0.5)))
+    return dict(M=M, N=N, K=K, scales=_pick(rng, ["f32", "ue8m0", "packed"]), rowb=bool(rng.random() < 0.3),
+                d_kind=_pick(rng, ["bf16", "f32"]), c_kind=_pick(rng, [None, "bf16", "f32", "inplace"]),
+                pad=int(rng.integers(0, 9)), a_m_major=bool(rng.random() < 0.5))
 
 
 def mn_case(i):
@@ -239,7 +230,6 @@ def masked_case(i, bf16=False):
     if not bf16:
         case.update(scales=_pick(rng, ["f32", "ue8m0", "packed"]), rowb=bool(rng.random() < 0.25),
                     d_kind=_pick(rng, ["bf16", "f32"]), c_kind=_pick(rng, [None, "bf16", "f32", "inplace"]))
-        _bf16_out_with_rowb(case)
     return case
 
 
@@ -264,7 +254,6 @@ def contig_case(i, bf16=False):
     if not bf16:
         case.update(scales=_pick(rng, ["f32", "ue8m0", "packed"]), rowb=bool(rng.random() < 0.25),
                     d_kind=_pick(rng, ["bf16", "f32"]), c_kind=_pick(rng, [None, "bf16", "f32", "inplace"]))
-        _bf16_out_with_rowb(case)
     return case
 
 
