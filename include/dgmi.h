@@ -112,15 +112,16 @@ int fp8_gemm_nt(const dg_tensor* a, const dg_tensor* b, const dg_tensor* sfa,
  *   fp8_gemm_tn  a E4M3 [K, M] (M contiguous),  b E4M3 [K, N]
  *   fp8_gemm_tt  a E4M3 [K, M],                 b E4M3 [N, K] (K contiguous)
  * so D[m,n] = C[m,n] + sum_kb (sum_{k in kb} A[m,k] B[n,k]) sfa[m,kb] sfb[n/128,kb]
- * with A[m,k] and B[n,k] read from the stored layouts.  sfa, sfb, c and d as
- * for fp8_gemm_nt (sfa is [M, K/128], sfb [ceil(N/128), K/128] whatever the
- * operands' layout).  An MN-major operand is row-major in its stored shape,
+ * (sfb[n,kb] with one scale per row of B) with A[m,k] and B[n,k] read from
+ * the stored layouts.  sfa, sfb, c and d as for fp8_gemm_nt (sfa is
+ * [M, K/128], sfb [ceil(N/128), K/128] or [N, K/128] whatever the operands'
+ * layout).  An MN-major operand is row-major in its stored shape,
  * with a 16-byte aligned base and a K-row stride (bytes) that is a multiple
  * of 16, at least its row count, and small enough that K x stride < 2^31 - 256
  * (the operand is addressed with 32-bit offsets); its row count (M or N) must
  * be a multiple of 16
- * (else DG_UNSUPPORTED).  Block scales only (FP32 or packed UE8M0), BF16 d
- * (one scale per row of B, or an F32 d: DG_UNSUPPORTED).  The fragments of an
+ * (else DG_UNSUPPORTED).  Either scale form of B (one per 128x128 block or
+ * one per row), FP32 or packed UE8M0; BF16 or F32 d.  The fragments of an
  * MN-major operand are read from LDS with transposing loads; results equal
  * fp8_gemm_nt's on the same values bit for bit.
  */

@@ -256,8 +256,7 @@ int fp8_gemm_common(int mode, const dg_tensor* a, const dg_tensor* b, const dg_t
   // MN-major operands: K-rows of M (N) bytes, 16-byte aligned, ld bytes apart
   const int64_t lda = a_mn ? a->stride[1] : va.sr, ldb = b_mn ? b->stride[1] : vb.sr;
   if (a_mn || b_mn) {
-    if (fp8_out || d_f32 || rowb)
-      return fail(DG_UNSUPPORTED, "%s: MN-major operands take block scales and a BF16 d", fname);
+    if (fp8_out) return fail(DG_UNSUPPORTED, "%s: MN-major operands take a BF16 or F32 d", fname);
     if ((a_mn && M % 16) || (b_mn && N % 16))
       return fail(DG_UNSUPPORTED, "%s: an MN-major operand needs its row count (M or N) to be a multiple of 16",
                   fname);

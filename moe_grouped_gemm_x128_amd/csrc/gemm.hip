@@ -394,9 +394,9 @@ __global__ __launch_bounds__(T::NT) void gemm_kernel(const GemmParams p) {
   constexpr int S = T::STAGES;
   constexpr bool FP8 = KIND == KIND_FP8;
   constexpr bool A_MN = (LAY & 1) != 0, B_MN = (LAY & 2) != 0;
-  static_assert(LAY == 0 || (FP8 && MODE == MODE_DENSE && OUT == OUT_BF16 && !T::PERM && T::NW == 8 &&
+  static_assert(LAY == 0 || (FP8 && MODE == MODE_DENSE && OUT != OUT_FP8 && !T::PERM && T::NW == 8 &&
                              T::BM <= MN_ROW && T::BN <= MN_ROW),
-                "MN-major operands: dense FP8, BF16 output, MFMA column order, 8 waves");
+                "MN-major operands: dense FP8, BF16 or F32 output, MFMA column order, 8 waves");
   // stage bytes and LDS-DMA instructions per wave per stage of each operand
   // (an MN-major stage is 128 K-rows of 256 bytes: four K-rows per instruction)
   constexpr int A_STAGE = A_MN ? BK * MN_ROW : T::A_BYTES, B_STAGE = B_MN ? BK * MN_ROW : T::B_BYTES;
@@ -1382,24 +1382,32 @@ hipError_t launch_fp8_gemm_mn(GemmParams p, int sf_fmt, hipStream_t stream) {
   p.tiles_n = (p.N + TileN::BN - 1) / TileN::BN;
   const dim3 g((unsigned)((int64_t)p.tiles_m * p.tiles_n)), b(TileN::NT);
   const int lay = (p.a_mn ? 1 : 0) | (p.b_mn ? 2 : 0);
-  const bool ue8 = sf_fmt == SF_UE8M0;
-  if (sf_fmt != SF_F32 && sf_fmt != SF_UE8M0) return hipErrorInvalidValue;
-#define DGMI_LAUNCH_MN(LAY_)                                                                                   \
-  do {                                                                                                         \
-    if (ue8) gemm_kernel<TileN, KIND_FP8, SF_UE8M0, MODE_DENSE, OUT_BF16, LAY_><<<g, b, 0, stream>>>(p);     \
-    else gemm_kernel<TileN, KIND_FP8, SF_F32, MODE_DENSE, OUT_BF16, LAY_><<<g, b, 0, stream>>>(p);           \
+  if (sf_fmt != SF_F32 && sf_fmt != SF_UE8M0 && sf_fmt != (SF_F32 | SF_ROWB) && sf_fmt != (SF_UE8M0 | SF_ROWB))
+    return hipErrorInvalidValue;
+#define DGMI_LAUNCH_MN_SF(SF_, LAY_)                                                                            \
+  do {                                                                                                          \
+    if (p.d_f32) gemm_kernel<TileN, KIND_FP8, SF_, MODE_DENSE, OUT_F32, LAY_><<<g, b, 0, stream>>>(p);         \
+    else gemm_kernel<TileN, KIND_FP8, SF_, MODE_DENSE, OUT_BF16, LAY_><<<g, b, 0, stream>>>(p);                \
+  } while (0)
+#define DGMI_LAUNCH_MN(LAY_)                                                                                    \
+  do {                                                                                                          \
+    if (sf_fmt == SF_F32) DGMI_LAUNCH_MN_SF(SF_F32, LAY_);                                                      \
+    else if (sf_fmt == SF_UE8M0) DGMI_LAUNCH_MN_SF(SF_UE8M0, LAY_);                                             \
+    else if (sf_fmt == (SF_F32 | SF_ROWB)) DGMI_LAUNCH_MN_SF(SF_F32 | SF_ROWB, LAY_);                           \
+    else DGMI_LAUNCH_MN_SF(SF_UE8M0 | SF_ROWB, LAY_);                                                           \
   } while (0)
   if (lay == 1) DGMI_LAUNCH_MN(1);
   else if (lay == 2) DGMI_LAUNCH_MN(2);
   else if (lay == 3) DGMI_LAUNCH_MN(3);
   else return hipErrorInvalidValue;
 #undef DGMI_LAUNCH_MN
+#undef DGMI_LAUNCH_MN_SF
   return hipGetLastError();
 }
 
 hipError_t launch_fp8_gemm(GemmParams p, int mode, int sf_fmt, hipStream_t stream) {
   if (p.a_mn || p.b_mn) {
-    if (mode != MODE_DENSE || p.d_f32) return hipErrorInvalidValue;
+    if (mode != MODE_DENSE) return hipErrorInvalidValue;
     return launch_fp8_gemm_mn(p, sf_fmt, stream);
   }
   return launch_plan<KIND_FP8>(fp8_gemm_plan(mode, p.G, p.M, p.N, p.k_bytes, sf_fmt), p, mode, sf_fmt, stream);

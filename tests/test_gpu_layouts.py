@@ -214,3 +214,96 @@ def test_fp8_gemm_nt_takes_transposed_views():
     mg.fp8_gemm_nt(a, b, sfa, sfb, None, dref)
     torch.cuda.synchronize()
     assert torch.equal(d.view(torch.int16), dref.view(torch.int16))
+
+
+@pytest.mark.parametrize("layout", ["NN", "TN", "TT"])
+@pytest.mark.parametrize("M,N,K,ue8m0", [(272, 208, 384, False), (1024, 960, 2048, True)])
+def test_fp8_gemm_mn_major_f32_out(layout, M, N, K, ue8m0):
+    """An F32 d (the accumulator stored without rounding, C added in place)
+    on MN-major operands: bit for bit the F32 output of fp8_gemm_nt on the
+    same values, and within the FP32-output bound of the oracle."""
+    from helpers import assert_f32_close, fp8_bound_terms, fp8_rounding_count
+
+    say(f"fp8_gemm_{layout.lower()} F32 d M={M} N={N} K={K} ue8m0={ue8m0}")
+    mg = _mg()
+    xa = synth.normal_f32(851, (M, K))
+    xb = synth.normal_f32(852, (N, K))
+    xc = synth.normal_f32(853, (M, N)) * np.float32(4.0)
+    a = torch.empty((M, K), dtype=torch.uint8, device="cuda")
+    sfa = torch.empty((M, K // 128), dtype=torch.float32, device="cuda")
+    b = torch.empty((N, K), dtype=torch.uint8, device="cuda")
+    sfb = torch.empty((-(-N // 128), K // 128), dtype=torch.float32, device="cuda")
+    mg.per_token_cast_to_fp8(to_dev(xa), a, sfa, ue8m0)
+    mg.per_block_cast_to_fp8(to_dev(xb), b, sfb, ue8m0)
+    if ue8m0:
+        pa = torch.empty((M, -(-K // 512)), dtype=torch.int32, device="cuda")
+        pb = torch.empty((-(-N // 128), -(-K // 512)), dtype=torch.int32, device="cuda")
+        mg.pack_ue8m0_to_int(sfa, pa)
+        mg.pack_ue8m0_to_int(sfb, pb)
+        sfa, sfb = pa, pb
+    a_st, b_st = _stored_mn(a, pad=16), _stored_mn(b, pad=32)
+    d = torch.full((M, N), float("nan"), dtype=torch.float32, device="cuda")
+    _run_layout(mg, layout, a, b, a_st, b_st, sfa, sfb, None, d)
+    dc = to_dev(xc)
+    _run_layout(mg, layout, a, b, a_st, b_st, sfa, sfb, dc, dc)
+    dref = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    mg.fp8_gemm_nt(a, b, sfa, sfb, None, dref)
+    dcref = to_dev(xc)
+    mg.fp8_gemm_nt(a, b, sfa, sfb, dcref, dcref)
+    torch.cuda.synchronize()
+    assert torch.equal(d.view(torch.int32), dref.view(torch.int32)), "differs from fp8_gemm_nt"
+    assert torch.equal(dc.view(torch.int32), dcref.view(torch.int32)), "differs from fp8_gemm_nt (C in place)"
+    ra, rsfa = oracle.per_token_cast_to_fp8(xa, ue8m0)
+    rb, rsfb = oracle.per_block_cast_to_fp8(xb, ue8m0)
+    assert np.array_equal(to_host(a), ra) and np.array_equal(to_host(b), rb)
+    S, G = fp8_bound_terms(oracle.fp8_gemm_nt, ra, rb, rsfa, rsfb)
+    c = xc.astype(np.float64)
+    assert_f32_close(to_host(d), oracle.fp8_gemm_nt(ra, rb, rsfa, rsfb), S, fp8_rounding_count(K),
+                     f"{layout} F32 d", G=G)
+    assert_f32_close(to_host(dc), oracle.fp8_gemm_nt(ra, rb, rsfa, rsfb, c), S + np.abs(c), fp8_rounding_count(K),
+                     f"{layout} F32 d, C in place", G=G)
+
+
+@pytest.mark.parametrize("layout", ["NN", "TN", "TT"])
+@pytest.mark.parametrize("ue8m0,d_kind", [(False, "bf16"), (True, "bf16"), (False, "f32"), (True, "f32")])
+def test_fp8_gemm_mn_major_per_row_b_scales(layout, ue8m0, d_kind):
+    """One B scale per row of B ([N, K/128], FP32 or packed UE8M0) on
+    MN-major operands: bit for bit fp8_gemm_nt's result on the same values,
+    and the oracle within the tolerance of the output dtype."""
+    from helpers import assert_bf16_close, assert_f32_close, fp8_bound_terms, fp8_rounding_count
+
+    M, N, K = 400, 336, 1024
+    say(f"fp8_gemm_{layout.lower()} per-row B scales ue8m0={ue8m0} d={d_kind}")
+    mg = _mg()
+    xa = synth.normal_f32(861, (M, K))
+    xb = synth.normal_f32(862, (N, K))
+    a = torch.empty((M, K), dtype=torch.uint8, device="cuda")
+    sfa = torch.empty((M, K // 128), dtype=torch.float32, device="cuda")
+    b = torch.empty((N, K), dtype=torch.uint8, device="cuda")
+    sfb = torch.empty((N, K // 128), dtype=torch.float32, device="cuda")
+    mg.per_token_cast_to_fp8(to_dev(xa), a, sfa, ue8m0)
+    mg.per_token_cast_to_fp8(to_dev(xb), b, sfb, ue8m0)  # one scale per row of B
+    if ue8m0:
+        pa = torch.empty((M, K // 512), dtype=torch.int32, device="cuda")
+        pb = torch.empty((N, K // 512), dtype=torch.int32, device="cuda")
+        mg.pack_ue8m0_to_int(sfa, pa)
+        mg.pack_ue8m0_to_int(sfb, pb)
+        sfa, sfb = pa, pb
+    a_st, b_st = _stored_mn(a), _stored_mn(b, pad=16)
+    dt = torch.float32 if d_kind == "f32" else torch.bfloat16
+    d = torch.empty((M, N), dtype=dt, device="cuda")
+    _run_layout(mg, layout, a, b, a_st, b_st, sfa, sfb, None, d)
+    dref = torch.empty((M, N), dtype=dt, device="cuda")
+    mg.fp8_gemm_nt(a, b, sfa, sfb, None, dref)
+    torch.cuda.synchronize()
+    bits = torch.int32 if d_kind == "f32" else torch.int16
+    assert torch.equal(d.view(bits), dref.view(bits)), "differs from fp8_gemm_nt on the same values"
+    ra, rsfa = oracle.per_token_cast_to_fp8(xa, ue8m0)
+    rb, rsfb = oracle.per_token_cast_to_fp8(xb, ue8m0)
+    assert np.array_equal(to_host(a), ra) and np.array_equal(to_host(b), rb)
+    ref = oracle.fp8_gemm_nt(ra, rb, rsfa, rsfb)
+    if d_kind == "f32":
+        S, G = fp8_bound_terms(oracle.fp8_gemm_nt, ra, rb, rsfa, rsfb)
+        assert_f32_close(to_host(d), ref, S, fp8_rounding_count(K), f"{layout} per-row B, F32 d", G=G)
+    else:
+        assert_bf16_close(to_host(d), ref, f"{layout} per-row B scales")

@@ -197,7 +197,8 @@ def mn_case(i):
     return dict(M=16 * int(rng.integers(1, hi + 1)), N=16 * int(rng.integers(1, hi + 1)),
                 K=128 * int(rng.integers(1, 3 if big else 11)), layout=_pick(rng, ["NN", "TN", "TT"]),
                 packed=bool(rng.random() < 0.4), c_bf16=bool(rng.random() < 0.4),
-                pad_a=16 * int(rng.integers(0, 3)), pad_b=16 * int(rng.integers(0, 3)))
+                pad_a=16 * int(rng.integers(0, 3)), pad_b=16 * int(rng.integers(0, 3)),
+                d_kind=_pick(rng, ["bf16", "f32"]), rowb=bool(rng.random() < 0.3))
 
 
 def _masked_m(rng, G, max_m):
@@ -277,7 +278,7 @@ def fp8_out_case(i):
                 sf_m_major=bool(rng.random() < 0.5))
 
 
-N_DENSE, N_MN, N_MASKED, N_CONTIG, N_BF16, N_BF16_GROUPED, N_FP8_OUT = 32, 12, 20, 20, 12, 8, 10
+N_DENSE, N_MN, N_MASKED, N_CONTIG, N_BF16, N_BF16_GROUPED, N_FP8_OUT = 32, 18, 20, 20, 12, 8, 10
 
 
 # ---------------------------------------------------------------------------
@@ -331,9 +332,9 @@ def test_sweep_mn_major(i):
     mg = _mg()
     rng = _rng("mn", 1000 + i)
     xa = _inputs(rng, 61000 + 4 * i, (M, K))
-    xb = _inputs(rng, 61001 + 4 * i, (N, K), 128)
+    xb = _inputs(rng, 61001 + 4 * i, (N, K), 1 if cs["rowb"] else 128)
     a, sfa = _cast_a(xa, cs["packed"], True)
-    b, sfb = _cast_b(xb, cs["packed"], False)
+    b, sfb = _cast_b(xb, cs["packed"], cs["rowb"])
     if cs["packed"]:
         sfa, sfb = _pack(sfa), _pack(sfb)
     a_st, b_st = _stored_mn(a, cs["pad_a"]), _stored_mn(b, cs["pad_b"])
@@ -341,17 +342,24 @@ def test_sweep_mn_major(i):
     if cs["c_bf16"]:
         bits = synth.bf16_bits_from_f32(synth.normal_f32(61002 + 4 * i, (M, N)) * np.float32(4.0))
         c, cref = to_dev(bits.view(np.int16)).view(torch.bfloat16), oracle.bf16_decode(bits)
-    d = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    dt = torch.float32 if cs["d_kind"] == "f32" else torch.bfloat16
+    d = torch.empty((M, N), dtype=dt, device="cuda")
     fn = {"NN": lambda: mg.fp8_gemm_nn(a, b_st, sfa, sfb, c, d),
           "TN": lambda: mg.fp8_gemm_tn(a_st, b_st, sfa, sfb, c, d),
           "TT": lambda: mg.fp8_gemm_tt(a_st, b, sfa, sfb, c, d)}[cs["layout"]]
     fn()
-    dref = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    dref = torch.empty((M, N), dtype=dt, device="cuda")
     mg.fp8_gemm_nt(a, b, sfa, sfb, c, dref)
     torch.cuda.synchronize()
-    assert torch.equal(d.view(torch.int16), dref.view(torch.int16)), f"{what}: differs from fp8_gemm_nt"
-    ra, rsfa, rb, rsfb = _oracle_operands(xa, xb, cs["packed"], False, a, b, what)
-    assert_bf16_close(to_host(d), oracle.fp8_gemm_nt(ra, rb, rsfa, rsfb, cref), what)
+    bits_view = torch.int32 if dt == torch.float32 else torch.int16
+    assert torch.equal(d.view(bits_view), dref.view(bits_view)), f"{what}: differs from fp8_gemm_nt"
+    ra, rsfa, rb, rsfb = _oracle_operands(xa, xb, cs["packed"], cs["rowb"], a, b, what)
+    ref = oracle.fp8_gemm_nt(ra, rb, rsfa, rsfb, cref)
+    S = Gt = None
+    if cs["d_kind"] == "f32":
+        S, Gt = fp8_bound_terms(oracle.fp8_gemm_nt, ra, rb, rsfa, rsfb)
+        S = S if cref is None else S + np.abs(cref)
+    _check(to_host(d), ref, S, Gt, None, cs["d_kind"], fp8_rounding_count(K), what)
 
 
 @pytest.mark.parametrize("i", range(N_MASKED))
