@@ -140,8 +140,8 @@ int fp8_gemm_tt(const dg_tensor* a, const dg_tensor* b, const dg_tensor* sfa, co
  * per token exactly as per_token_cast_to_fp8 casts that BF16 tensor, so q
  * and sfq are bit-identical to fp8_gemm_nt followed by per_token_cast_to_fp8
  * with the same use_ue8m0.  The BF16 D is never written to memory.
- *   a, b, sfa, c  as fp8_gemm_nt; sfb one scale per 128x128 block of B only
- *       (one scale per row of B returns DG_UNSUPPORTED)
+ *   a, b, sfa, sfb, c  as fp8_gemm_nt (sfb one scale per 128x128 block of B
+ *       or one per row of B)
  *   q   E4M3 [M, N], any row stride that is a multiple of 4 (innermost
  *       stride 1), 4-B aligned base; must not overlap any input
  *   sfq F32 [M, ceil(N/128)], any strides, 4-B aligned: the scale of each
@@ -383,7 +383,8 @@ enum {
   DG_KIND_BF16_MASKED = 3, DG_KIND_BF16_DENSE = 4, DG_KIND_BF16_CONTIGUOUS = 5, /* BF16 GEMMs */
   DG_KIND_DENSE_ROWB = 6, DG_KIND_CONTIGUOUS_ROWB = 7, DG_KIND_MASKED_ROWB = 8, /* FP8, one B scale per row */
   DG_KIND_DENSE_FP8_OUT = 9,                                                      /* fp8_gemm_nt_fp8_out */
-  DG_KIND_DENSE_MN = 10                         /* fp8_gemm_nn / _tn / _tt (an MN-major operand) */
+  DG_KIND_DENSE_MN = 10,                        /* fp8_gemm_nn / _tn / _tt (an MN-major operand) */
+  DG_KIND_DENSE_FP8_OUT_ROWB = 11               /* fp8_gemm_nt_fp8_out, one B scale per row */
 };
 
 /* Fill *out with the configuration `kind` would launch for these sizes

@@ -20,6 +20,7 @@ DG_KIND_BF16_MASKED, DG_KIND_BF16_DENSE, DG_KIND_BF16_CONTIGUOUS = 3, 4, 5
 DG_KIND_DENSE_ROWB, DG_KIND_CONTIGUOUS_ROWB, DG_KIND_MASKED_ROWB = 6, 7, 8  # FP8, one B scale per row of B
 DG_KIND_DENSE_FP8_OUT = 9  # fp8_gemm_nt_fp8_out
 DG_KIND_DENSE_MN = 10  # fp8_gemm_nn / _tn / _tt
+DG_KIND_DENSE_FP8_OUT_ROWB = 11  # fp8_gemm_nt_fp8_out, one B scale per row
 
 ENTRY_POINTS = (
     "dg_last_error",

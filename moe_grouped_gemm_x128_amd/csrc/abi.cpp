@@ -251,7 +251,6 @@ int fp8_gemm_common(int mode, const dg_tensor* a, const dg_tensor* b, const dg_t
   if (mode == dgmi::MODE_DENSE && (sfb->ndim != 2 || sfa->ndim != 2))
     return fail(DG_INVALID_ARG, "%s: sfa and sfb must be 2-D", fname);
   if (mode == dgmi::MODE_CONTIG && sfb->ndim != 3) return fail(DG_INVALID_ARG, "%s: sfb must be [G, ceil(N/128), ..]", fname);
-  if (fp8_out && rowb) return fail(DG_UNSUPPORTED, "%s: one B scale per row is not supported with FP8 output", fname);
 
   // MN-major operands: K-rows of M (N) bytes, 16-byte aligned, ld bytes apart
   const int64_t lda = a_mn ? a->stride[1] : va.sr, ldb = b_mn ? b->stride[1] : vb.sr;
@@ -378,7 +377,8 @@ int fp8_gemm_common(int mode, const dg_tensor* a, const dg_tensor* b, const dg_t
   p.G = (int32_t)G;
   if (M == 0 || N == 0 || G == 0) return ok();
   if (K == 0) return fail(DG_UNSUPPORTED, "%s: K = 0 is not supported", fname);
-  if (fp8_out) return check_launch(dgmi::launch_fp8_gemm_fp8_out(p, sf_fmt, stream), fname);
+  if (fp8_out)
+    return check_launch(dgmi::launch_fp8_gemm_fp8_out(p, sf_fmt | (rowb ? dgmi::SF_ROWB : 0), stream), fname);
   return check_launch(dgmi::launch_fp8_gemm(p, mode, sf_fmt | (rowb ? dgmi::SF_ROWB : 0), stream), fname);
 }
 
@@ -946,9 +946,9 @@ int dg_query_config(int32_t kind, int64_t G, int64_t M, int64_t N, int64_t K, dg
   } else if (kind >= DG_KIND_DENSE && kind <= DG_KIND_MASKED) {
     mode = kind == DG_KIND_DENSE ? dgmi::MODE_DENSE : (kind == DG_KIND_CONTIGUOUS ? dgmi::MODE_CONTIG : dgmi::MODE_MASKED);
     c = dgmi::fp8_gemm_plan(mode, G, M, N, K, dgmi::SF_F32);
-  } else if (kind == DG_KIND_DENSE_FP8_OUT) {
+  } else if (kind == DG_KIND_DENSE_FP8_OUT || kind == DG_KIND_DENSE_FP8_OUT_ROWB) {
     mode = dgmi::MODE_DENSE;
-    c = dgmi::fp8_out_gemm_plan(M, N);
+    c = dgmi::fp8_out_gemm_plan(M, N, dgmi::SF_F32 | (kind == DG_KIND_DENSE_FP8_OUT_ROWB ? dgmi::SF_ROWB : 0));
   } else if (kind == DG_KIND_DENSE_MN) {
     mode = dgmi::MODE_DENSE;
     c = dgmi::fp8_mn_gemm_plan();

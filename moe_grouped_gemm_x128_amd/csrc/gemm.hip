@@ -1149,14 +1149,23 @@ hipError_t launch_tile(const GemmParams& p, int mode, int sf_fmt, int64_t grid, 
   }
 }
 
-// Launch one tile configuration of the dense FP8 GEMM with FP8 output
-// (block scales only).
-template <class T>
+// Launch one tile configuration of the dense FP8 GEMM with FP8 output.
+// ROWB: whether the tile also takes one B scale per row (not the 256 x 256
+// tile, which has no registers for the per-lane column scales).
+template <class T, bool ROWB>
 hipError_t launch_tile_fp8_out(const GemmParams& p, int sf_fmt, int64_t grid, hipStream_t stream) {
   const dim3 g((unsigned)grid), b(T::NT);
-  if (sf_fmt == SF_F32) gemm_kernel<T, KIND_FP8, SF_F32, MODE_DENSE, OUT_FP8><<<g, b, 0, stream>>>(p);
-  else if (sf_fmt == SF_UE8M0) gemm_kernel<T, KIND_FP8, SF_UE8M0, MODE_DENSE, OUT_FP8><<<g, b, 0, stream>>>(p);
-  else return hipErrorInvalidValue;
+  if (sf_fmt == SF_F32) {
+    gemm_kernel<T, KIND_FP8, SF_F32, MODE_DENSE, OUT_FP8><<<g, b, 0, stream>>>(p);
+  } else if (sf_fmt == SF_UE8M0) {
+    gemm_kernel<T, KIND_FP8, SF_UE8M0, MODE_DENSE, OUT_FP8><<<g, b, 0, stream>>>(p);
+  } else if constexpr (ROWB) {
+    if (sf_fmt == (SF_F32 | SF_ROWB)) gemm_kernel<T, KIND_FP8, SF_F32 | SF_ROWB, MODE_DENSE, OUT_FP8><<<g, b, 0, stream>>>(p);
+    else if (sf_fmt == (SF_UE8M0 | SF_ROWB)) gemm_kernel<T, KIND_FP8, SF_UE8M0 | SF_ROWB, MODE_DENSE, OUT_FP8><<<g, b, 0, stream>>>(p);
+    else return hipErrorInvalidValue;
+  } else {
+    return hipErrorInvalidValue;  // the launch plan never picks this tile for row scales
+  }
   return hipGetLastError();
 }
 
@@ -1416,25 +1425,31 @@ hipError_t launch_fp8_gemm(GemmParams p, int mode, int sf_fmt, hipStream_t strea
 // Dense FP8 GEMM with FP8 output: the tiles whose waves cover 64 columns
 // (a 128-column block is two neighbouring waves), one launch: 256 x 256
 // above 128 rows, the 128-row tiles below.
-GemmPlan fp8_out_gemm_plan(int64_t M, int64_t N) {
+GemmPlan fp8_out_gemm_plan(int64_t M, int64_t N, int sf_fmt) {
   GemmPlan p;
   p.parts = 1;
   p.n_split = N;
-  if (M > 128) p.cfg[0] = make_cfg<TileL, KIND_FP8>(VAR_L);
-  else p.cfg[0] = N <= 128 ? make_cfg<TileS, KIND_FP8>(VAR_S) : make_cfg<TileW, KIND_FP8>(VAR_W);
+  if (M > 128) {
+    // one B scale per row: the 256 x 128 tile (wave tile 64 x 64, 64 columns
+    // per wave as the FP8 epilogue needs, registers to spare)
+    p.cfg[0] = (sf_fmt & SF_ROWB) ? make_cfg<TileT, KIND_FP8>(VAR_T) : make_cfg<TileL, KIND_FP8>(VAR_L);
+  } else {
+    p.cfg[0] = N <= 128 ? make_cfg<TileS, KIND_FP8>(VAR_S) : make_cfg<TileW, KIND_FP8>(VAR_W);
+  }
   return p;
 }
 
 hipError_t launch_fp8_gemm_fp8_out(GemmParams p, int sf_fmt, hipStream_t stream) {
-  const TileCfg cfg = fp8_out_gemm_plan(p.M, p.N).cfg[0];
+  const TileCfg cfg = fp8_out_gemm_plan(p.M, p.N, sf_fmt).cfg[0];
   p.tiles_m = (p.M + cfg.bm - 1) / cfg.bm;
   p.tiles_n = (p.N + cfg.bn - 1) / cfg.bn;
   const int64_t grid = gemm_grid(cfg, MODE_DENSE, 1, p.M, p.N);
   if (grid == 0) return hipSuccess;
   switch (cfg.variant) {
-    case VAR_L: return launch_tile_fp8_out<TileL>(p, sf_fmt, grid, stream);
-    case VAR_W: return launch_tile_fp8_out<TileW>(p, sf_fmt, grid, stream);
-    default: return launch_tile_fp8_out<TileS>(p, sf_fmt, grid, stream);
+    case VAR_L: return launch_tile_fp8_out<TileL, false>(p, sf_fmt, grid, stream);
+    case VAR_T: return launch_tile_fp8_out<TileT, true>(p, sf_fmt, grid, stream);
+    case VAR_W: return launch_tile_fp8_out<TileW, true>(p, sf_fmt, grid, stream);
+    default: return launch_tile_fp8_out<TileS, true>(p, sf_fmt, grid, stream);
   }
 }
 

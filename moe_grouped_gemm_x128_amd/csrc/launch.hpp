@@ -119,8 +119,8 @@ int64_t plan_grid(const GemmPlan& plan, int part, int mode, int64_t G, int64_t M
 hipError_t launch_fp8_gemm(GemmParams p, int mode, int sf_fmt, hipStream_t stream);
 GemmPlan fp8_mn_gemm_plan();
 // Dense FP8 GEMM whose output D is cast per token to FP8 (p.q, p.sfq) in the
-// epilogue; block scales only (sf_fmt SF_F32 or SF_UE8M0).
-GemmPlan fp8_out_gemm_plan(int64_t M, int64_t N);
+// epilogue; sf_fmt SF_F32 or SF_UE8M0, plus SF_ROWB for one B scale per row.
+GemmPlan fp8_out_gemm_plan(int64_t M, int64_t N, int sf_fmt);
 hipError_t launch_fp8_gemm_fp8_out(GemmParams p, int sf_fmt, hipStream_t stream);
 // BF16 GEMMs: same kernel body; byte strides in p, no scales
 hipError_t launch_bf16_gemm(GemmParams p, int mode, hipStream_t stream);

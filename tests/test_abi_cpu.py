@@ -96,7 +96,7 @@ def test_query_config_is_a_pure_function_of_shapes(lib):
     c = binding.query_config(binding.DG_KIND_CONTIGUOUS, 4, 33152, 4096, 7168)  # 259 blocks
     assert c["block_m"] == 256 and c["grid"] == 2 * 130 * 16
     with pytest.raises(binding.DgmiError):
-        binding.query_config(11, 1, 1, 1, 1)  # no such kind
+        binding.query_config(12, 1, 1, 1, 1)  # no such kind
 
 
 @pytest.mark.parametrize("M,N,tile", [
@@ -113,6 +113,12 @@ def test_fp8_out_plan(lib, M, N, tile):
     assert (c["block_m"], c["block_n"], c["threads"]) == tile
     assert c["n_split"] == N and c["block_n2"] == 0 and c["grid2"] == 0
     assert c["grid"] == -(-M // tile[0]) * -(-N // tile[1])
+    # one B scale per row: the 256 x 128 tile above 128 rows (the 256 x 256
+    # tile has no registers for the per-lane column scales)
+    r = binding.query_config(binding.DG_KIND_DENSE_FP8_OUT_ROWB, 1, M, N, 7168)
+    want = (256, 128, 512) if M > 128 else tile
+    assert (r["block_m"], r["block_n"], r["threads"]) == want
+    assert r["grid"] == -(-M // want[0]) * -(-N // want[1])
 
 
 @pytest.mark.parametrize("N,K,fp8_plan,bf16_plan", [
@@ -416,8 +422,9 @@ def test_fp8_out_validation_errors(lib):
     assert _call_fp8_out(lib, a, b, sfa, sfb, q, _t((M, N // 128 + 1), f32)) == binding.DG_INVALID_ARG
     assert _call_fp8_out(lib, a, b, sfa, sfb, q, _t((M, N // 128), bf)) == binding.DG_INVALID_ARG
     assert _call_fp8_out(lib, a, b, sfa, sfb, q, _t((M + 1, N // 128), f32)) == binding.DG_INVALID_ARG
-    # one B scale per row: not supported with FP8 output
-    assert _call_fp8_out(lib, a, b, sfa, _t((N, K // 128), f32), q, sfq) == binding.DG_UNSUPPORTED
+    # one B scale per row is taken (past validation the CPU build's launch fails: no GPU here)
+    assert _call_fp8_out(lib, a, b, sfa, _t((N, K // 128), f32), q, sfq) not in (binding.DG_UNSUPPORTED,
+                                                                              binding.DG_INVALID_ARG)
     # sfq overlapping q, c overlapping q
     buf = torch.empty(M * N + 64, dtype=u8)
     q2 = buf[: M * N].view(M, N)

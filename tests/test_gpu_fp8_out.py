@@ -117,12 +117,17 @@ def assert_fp8_out_close(q, sf, D, ue8m0, what):
             assert np.all((p >= lo) & (p / 2 < hi)), f"{what}: block {kb} UE8M0 scale"
 
 
-def run_case(M, N, K, c_kind=None, ue8m0=False, in_ue8m0=False, q_pad=0, sf_m_major=False, seed=0):
+def run_case(M, N, K, c_kind=None, ue8m0=False, in_ue8m0=False, q_pad=0, sf_m_major=False, seed=0, rowb=False):
+    """rowb: one B scale per row of B ([N, K/128]) instead of 128 x 128 blocks."""
     mg = _mg()
     xa = synth.normal_f32(900 + seed, (M, K))
     xb = synth.normal_f32(901 + seed, (N, K))
     a, sfa = q_tok(to_dev(xa), in_ue8m0)
-    b, sfb = q_blk(to_dev(xb), in_ue8m0)
+    if rowb:
+        b, sfb = q_tok(to_dev(xb), in_ue8m0)
+        sfb = sfb.contiguous()
+    else:
+        b, sfb = q_blk(to_dev(xb), in_ue8m0)
     c, cref = None, None
     if c_kind is not None:
         xc = synth.normal_f32(902 + seed, (M, N)) * np.float32(4.0)
@@ -147,7 +152,7 @@ def run_case(M, N, K, c_kind=None, ue8m0=False, in_ue8m0=False, q_pad=0, sf_m_ma
         assert np.all(to_host(qbuf[:, N:]) == 0x55), "row padding of q written"
     # the oracle, on its own quantized operands
     ra, rsfa = oracle.per_token_cast_to_fp8(xa, in_ue8m0)
-    rb, rsfb = oracle.per_block_cast_to_fp8(xb, in_ue8m0)
+    rb, rsfb = (oracle.per_token_cast_to_fp8 if rowb else oracle.per_block_cast_to_fp8)(xb, in_ue8m0)
     assert np.array_equal(to_host(a), ra) and np.array_equal(to_host(b), rb)
     D = oracle.fp8_gemm_nt(ra, rb, rsfa, rsfb, cref)
     assert_fp8_out_close(qh, sfh, D, ue8m0, f"fp8 out {M}x{N}x{K} c={c_kind} ue8m0={ue8m0}")
@@ -274,3 +279,18 @@ def test_fp8_out_graph_replay():
         mg.fp8_gemm_nt_fp8_out(a, b, sfa, sfb, None, qe, sfe, True)
         torch.cuda.synchronize()
         assert np.array_equal(to_host(q), to_host(qe)) and np.array_equal(to_host(sfq), to_host(sfe)), f"replay {r}"
+
+
+# one B scale per row of B: the 256 x 128 tile above 128 rows, the 128-row
+# tiles below; FP32 and UE8M0 input scales, C, both output scale formats
+@pytest.mark.parametrize("M,N,K", [(300, 520, 512), (4096, 2048, 256), (200, 130, 384), (64, 300, 384),
+                                   (100, 100, 256)])
+@pytest.mark.parametrize("in_ue8m0,ue8m0,c_kind", [(False, False, None), (True, True, "bf16"), (False, True, "f32")])
+def test_fp8_out_per_row_b_scales(M, N, K, in_ue8m0, ue8m0, c_kind):
+    from moe_grouped_gemm_x128_amd import binding
+
+    say(f"fp8_gemm_nt_fp8_out per-row B scales M={M} N={N} K={K} in_ue8m0={in_ue8m0} ue8m0={ue8m0} c={c_kind}")
+    plan = binding.query_config(binding.DG_KIND_DENSE_FP8_OUT_ROWB, 1, M, N, K)
+    if M > 128:
+        assert (plan["block_m"], plan["block_n"]) == (256, 128), plan
+    run_case(M, N, K, c_kind=c_kind, ue8m0=ue8m0, in_ue8m0=in_ue8m0, seed=40, rowb=True)

@@ -275,10 +275,10 @@ def fp8_out_case(i):
     K = 128 * int(rng.integers(1, 3 if M >= 1500 else 9))
     return dict(M=M, N=N, K=K, c_kind=_pick(rng, [None, "bf16", "f32"]), ue8m0=bool(rng.random() < 0.5),
                 in_ue8m0=bool(rng.random() < 0.5), q_pad=4 * int(rng.integers(0, 3)),
-                sf_m_major=bool(rng.random() < 0.5))
+                sf_m_major=bool(rng.random() < 0.5), rowb=bool(rng.random() < 0.3))
 
 
-N_DENSE, N_MN, N_MASKED, N_CONTIG, N_BF16, N_BF16_GROUPED, N_FP8_OUT = 32, 18, 20, 20, 12, 8, 10
+N_DENSE, N_MN, N_MASKED, N_CONTIG, N_BF16, N_BF16_GROUPED, N_FP8_OUT = 32, 18, 20, 20, 12, 8, 14
 
 
 # ---------------------------------------------------------------------------
@@ -439,7 +439,7 @@ def test_sweep_fp8_out(i):
     cs = fp8_out_case(i)
     say(f"sweep fp8 out {i} {cs}")
     run_case(cs["M"], cs["N"], cs["K"], c_kind=cs["c_kind"], ue8m0=cs["ue8m0"], in_ue8m0=cs["in_ue8m0"],
-             q_pad=cs["q_pad"], sf_m_major=cs["sf_m_major"], seed=64000 + 4 * i)
+             q_pad=cs["q_pad"], sf_m_major=cs["sf_m_major"], seed=64000 + 4 * i, rowb=cs["rowb"])
 
 
 # ---------------------------------------------------------------------------
