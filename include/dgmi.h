@@ -215,8 +215,9 @@ int m_grouped_fp8_gemm_nt_masked_acc(const dg_tensor* a, const dg_tensor* b,
  * Masked grouped BF16 GEMM, argument order of the pages' capture example
  * (a, b, d, masked_m, max_m_per_group): D[g,m,:] = A[g,m,:] . B[g]^T for
  * m < clamp(masked_m[g], 0, max_m), FP32 accumulation, BF16 out.
- *   a BF16 [G, max_m, K] or [G*max_m, K]; b BF16 [G, N, K]; d like a with N.
- *   K must be a multiple of 64.
+ *   a BF16 [G, max_m, K] or [G*max_m, K]; b BF16 [G, N, K]; d like a with N,
+ *   BF16, or F32 (4-B aligned: the FP32 accumulator stored without rounding).
+ *   Rows past masked_m are not written.  K must be a multiple of 64.
  */
 int m_grouped_bf16_gemm_nt_masked(const dg_tensor* a, const dg_tensor* b,
                                   const dg_tensor* d, const dg_tensor* masked_m,
@@ -238,6 +239,7 @@ int bf16_gemm_nt(const dg_tensor* a, const dg_tensor* b, const dg_tensor* c, con
  * Contiguous grouped BF16 GEMM: the layout of m_grouped_fp8_gemm_nt_contiguous
  * without scales.
  *   a BF16 [Msum, K] (Msum % 128 == 0), b BF16 [G, N, K], d BF16 [Msum, N]
+ *   or F32 [Msum, N] (4-B aligned: the FP32 accumulator stored without rounding)
  *   grouped_layout I32 [Msum/128]: group id per 128-row block; negative ids
  *   (and ids >= G) skip the block, its rows of d are not written.
  *   K must be a multiple of 64.

@@ -457,8 +457,8 @@ int bf16_gemm_common(int mode, const dg_tensor* a, const dg_tensor* b, const dg_
   DG_TRY(check_basic(d, "d", true));
   DG_TRY(check_dtype(a, "a", DG_BF16));
   DG_TRY(check_dtype(b, "b", DG_BF16));
-  // d: BF16, or F32 for the dense GEMM (the FP32 accumulator stored as is)
-  const bool d_f32 = mode == dgmi::MODE_DENSE && d->dtype == DG_F32;
+  // d: BF16, or F32 (the FP32 accumulator stored as is)
+  const bool d_f32 = d->dtype == DG_F32;
   DG_TRY(check_dtype(d, "d", d_f32 ? DG_F32 : DG_BF16));
   View3 va, vb, vd;
   int64_t G = 1;
@@ -531,7 +531,7 @@ int bf16_gemm_common(int mode, const dg_tensor* a, const dg_tensor* b, const dg_
   p.ldb = 2 * vb.sr;
   p.b_gs = 2 * vb.sg;
   p.ldd = vd.sr;
-  p.d_gs = vd.sg;
+  p.d_gs = d_f32 ? 2 * vd.sg : vd.sg;  // (the kernels step d in BF16-sized units)
   p.M = (int32_t)M;
   p.N = (int32_t)N;
   p.k_bytes = (int32_t)(2 * K);

@@ -1097,10 +1097,11 @@ template <class T, int KIND, bool ROWB>
 hipError_t launch_tile(const GemmParams& p, int mode, int sf_fmt, int64_t grid, hipStream_t stream) {
   const dim3 g((unsigned)grid), b(T::NT);
   if (p.d_f32) {
-    // FP32 D: block or row scales; the BF16 kind dense only
+    // FP32 D: every kind, form and scale format
     if constexpr (KIND == KIND_BF16) {
-      if (mode != MODE_DENSE) return hipErrorInvalidValue;
-      gemm_kernel<T, KIND_BF16, SF_F32, MODE_DENSE, OUT_F32><<<g, b, 0, stream>>>(p);
+      if (mode == MODE_DENSE) gemm_kernel<T, KIND_BF16, SF_F32, MODE_DENSE, OUT_F32><<<g, b, 0, stream>>>(p);
+      else if (mode == MODE_CONTIG) gemm_kernel<T, KIND_BF16, SF_F32, MODE_CONTIG, OUT_F32><<<g, b, 0, stream>>>(p);
+      else gemm_kernel<T, KIND_BF16, SF_F32, MODE_MASKED, OUT_F32><<<g, b, 0, stream>>>(p);
     } else {
 #define DGMI_LAUNCH_F32(SF_)                                                                                 \
   do {                                                                                                       \

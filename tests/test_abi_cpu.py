@@ -74,6 +74,9 @@ def test_bf16_gemm_validation_errors(lib):
     assert contig(_t((200, K), torch.bfloat16), bg, _t((200, N), torch.bfloat16), lay) == binding.DG_INVALID_ARG  # Msum % 128
     assert contig(_t((256, K), torch.bfloat16), bg, dg, _t((3,), torch.int32)) == binding.DG_INVALID_ARG  # layout length
     assert contig(_t((256, K), torch.bfloat16), _t((N, K), torch.bfloat16), dg, lay) == binding.DG_INVALID_ARG  # b rank
+    # an F32 d is taken (past validation the CPU build's launch fails: no GPU here)
+    assert contig(_t((256, K), torch.bfloat16), bg, _t((256, N), torch.float32), lay) not in (binding.DG_UNSUPPORTED,
+                                                                                           binding.DG_INVALID_ARG)
 
 
 def test_query_config_is_a_pure_function_of_shapes(lib):

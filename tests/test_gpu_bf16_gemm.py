@@ -156,3 +156,34 @@ def test_bf16_contiguous_skips_and_mixed_tiles(layout, N):
     got = to_host(d)
     assert np.all(got[~written] == SENTINEL_BF16)
     assert_bf16_close(got[written], ref[written], "bf16 contiguous")
+
+
+@pytest.mark.parametrize("layout,N", [([2, -1, 0, 2, 1, -1, 5], 300), ([0, 0, 1, 1, 2, 2, 0, 0] * 4, 4096)])
+def test_bf16_contiguous_f32_out(layout, N):
+    """An F32 d on the contiguous BF16 GEMM: the FP32 accumulator within the
+    (K + 2) u S bound, rounding to the BF16 output bit for bit; skipped
+    blocks keep their NaN fill."""
+    from helpers import assert_f32_close
+
+    say(f"m_grouped_bf16_gemm_nt_contiguous F32 d N={N}")
+    mg = _mg()
+    layout = np.array(layout, dtype=np.int32)
+    G, K = 3, 192 if N < 4096 else 64
+    Msum = layout.size * 128
+    ab = synth.bf16_bits_from_f32(synth.normal_f32(191, (Msum, K)))
+    bb = synth.bf16_bits_from_f32(synth.normal_f32(192, (G, N, K)))
+    buf = torch.full((Msum, N + 2), float("nan"), dtype=torch.float32, device="cuda")
+    d = buf[:, :N]
+    mg.m_grouped_bf16_gemm_nt_contiguous(_dev_bf16(ab), _dev_bf16(bb), d, to_dev(layout))
+    d16 = _sentinel((Msum, N))
+    mg.m_grouped_bf16_gemm_nt_contiguous(_dev_bf16(ab), _dev_bf16(bb), d16, to_dev(layout))
+    torch.cuda.synchronize()
+    ref_layout = np.where(layout < G, layout, -1)
+    ref, written = oracle.m_grouped_bf16_gemm_nt_contiguous(ab, bb, ref_layout)
+    S, _ = oracle.m_grouped_bf16_gemm_nt_contiguous(ab & np.uint16(0x7FFF), bb & np.uint16(0x7FFF), ref_layout)
+    got = to_host(d)
+    assert np.isnan(got[~written]).all(), "skipped blocks written"
+    assert torch.isnan(buf[:, N:]).all(), "row padding written"
+    rows = torch.from_numpy(written).cuda()
+    assert torch.equal(d[rows].to(torch.bfloat16).view(torch.int16), d16[rows].view(torch.int16))
+    assert_f32_close(got[written], ref[written], S[written], K, "bf16 contiguous F32 d")

@@ -65,3 +65,35 @@ def test_bf16_masked_2d_operands():
     got = to_host(d).reshape(G, max_m, N)
     assert np.all(got[~written] == SENTINEL_BF16)
     assert_bf16_close(got[written], ref[written], "bf16 masked 2-D")
+
+
+@pytest.mark.parametrize("G,max_m,N,K,mm", [
+    (4, 128, 300, 256, [0, 5, 128, 77]),
+    (2, 256, 384, 320, [256, 130]),
+    (16, 256, 4096, 64, [0, 17, 256, 999, -3, 129, 128, 200, 1, 255, 64, 130, 250, 16, 0, 192]),
+])
+def test_bf16_masked_f32_out(G, max_m, N, K, mm):
+    """An F32 d: the FP32 accumulator stored without rounding (within the
+    (K + 2) u S bound of FP32 summation, and rounding to the BF16 output bit
+    for bit); rows past masked_m keep their NaN fill."""
+    from helpers import assert_f32_close
+
+    say(f"bf16 masked F32 d G={G} max_m={max_m} N={N} K={K}")
+    mg = _mg()
+    mm = np.array(mm, dtype=np.int32)
+    ab = synth.bf16_bits_from_f32(synth.normal_f32(155, (G, max_m, K)))
+    bb = synth.bf16_bits_from_f32(synth.normal_f32(156, (G, N, K)))
+    buf = torch.full((G, max_m, N + 4), float("nan"), dtype=torch.float32, device="cuda")
+    d = buf[..., :N]
+    mg.m_grouped_bf16_gemm_nt_masked(_dev_bf16(ab), _dev_bf16(bb), d, to_dev(mm), max_m)
+    d16 = torch.full((G, max_m, N), SENTINEL_BF16, dtype=torch.int16, device="cuda").view(torch.bfloat16)
+    mg.m_grouped_bf16_gemm_nt_masked(_dev_bf16(ab), _dev_bf16(bb), d16, to_dev(mm), max_m)
+    torch.cuda.synchronize()
+    ref, written = oracle.m_grouped_bf16_gemm_nt_masked(ab, bb, mm, max_m)
+    S, _ = oracle.m_grouped_bf16_gemm_nt_masked(ab & np.uint16(0x7FFF), bb & np.uint16(0x7FFF), mm, max_m)
+    got = to_host(d)
+    assert np.isnan(got[~written]).all(), "rows past masked_m written"
+    assert torch.isnan(buf[..., N:]).all(), "row padding written"
+    rows = torch.from_numpy(written).cuda()
+    assert torch.equal(d[rows].to(torch.bfloat16).view(torch.int16), d16[rows].view(torch.int16))
+    assert_f32_close(got[written], ref[written], S[written], K, "bf16 masked F32 d")

@@ -228,7 +228,9 @@ def masked_case(i, bf16=False):
         G, max_m = int(rng.integers(1, 9)), _loguni(rng, 1, 400)
         N, K = _loguni(rng, 16, 2200), kunit * int(rng.integers(1, 9))
     case = dict(G=G, max_m=max_m, N=N, K=K, mm=_masked_m(rng, G, max_m), pad=int(rng.integers(0, 5)))
-    if not bf16:
+    if bf16:
+        case.update(d_kind=_pick(rng, ["bf16", "f32"]))
+    else:
         case.update(scales=_pick(rng, ["f32", "ue8m0", "packed"]), rowb=bool(rng.random() < 0.25),
                     d_kind=_pick(rng, ["bf16", "f32"]), c_kind=_pick(rng, [None, "bf16", "f32", "inplace"]))
     return case
@@ -252,7 +254,9 @@ def contig_case(i, bf16=False):
         G, nblocks = int(rng.integers(1, 9)), _loguni(rng, 1, 48)
         N, K = _loguni(rng, 16, 2200), kunit * int(rng.integers(1, 9))
     case = dict(G=G, N=N, K=K, layout=_layout(rng, G, nblocks), pad=int(rng.integers(0, 5)))
-    if not bf16:
+    if bf16:
+        case.update(d_kind=_pick(rng, ["bf16", "f32"]))
+    else:
         case.update(scales=_pick(rng, ["f32", "ue8m0", "packed"]), rowb=bool(rng.random() < 0.25),
                     d_kind=_pick(rng, ["bf16", "f32"]), c_kind=_pick(rng, [None, "bf16", "f32", "inplace"]))
     return case
@@ -278,7 +282,7 @@ def fp8_out_case(i):
                 sf_m_major=bool(rng.random() < 0.5), rowb=bool(rng.random() < 0.3))
 
 
-N_DENSE, N_MN, N_MASKED, N_CONTIG, N_BF16, N_BF16_GROUPED, N_FP8_OUT = 32, 18, 20, 20, 12, 8, 14
+N_DENSE, N_MN, N_MASKED, N_CONTIG, N_BF16, N_BF16_GROUPED, N_FP8_OUT = 32, 18, 20, 20, 12, 12, 14
 
 
 # ---------------------------------------------------------------------------
@@ -491,15 +495,18 @@ def test_sweep_bf16_masked(i):
     rng = _rng("bf16_masked", 1000 + i)
     ab = _bf16_inputs(rng, 66000 + 4 * i, (G, max_m, K))
     bb = _bf16_inputs(rng, 66001 + 4 * i, (G, N, K))
-    buf, d = _out((G, max_m, N), "bf16", cs["pad"])
+    buf, d = _out((G, max_m, N), cs["d_kind"], cs["pad"])
     mm = np.array(cs["mm"], dtype=np.int32)
     mg.m_grouped_bf16_gemm_nt_masked(_dev_bf16(ab), _dev_bf16(bb), d, to_dev(mm), max_m)
     torch.cuda.synchronize()
     ref, written = oracle.m_grouped_bf16_gemm_nt_masked(ab, bb, mm, max_m)
+    S = None
+    if cs["d_kind"] == "f32":
+        S, _ = oracle.m_grouped_bf16_gemm_nt_masked(_abs_bf16(ab), _abs_bf16(bb), mm, max_m)
     got = to_host(d)
-    _untouched(got, written, "bf16", None, None, what)
+    _untouched(got, written, cs["d_kind"], None, None, what)
     _pad_untouched(buf, N, what)
-    _check(got, ref, None, None, written, "bf16", K, what)
+    _check(got, ref, S, None, written, cs["d_kind"], K, what)
 
 
 @pytest.mark.parametrize("i", range(N_BF16_GROUPED))
@@ -514,11 +521,15 @@ def test_sweep_bf16_contiguous(i):
     rng = _rng("bf16_contig", 1000 + i)
     ab = _bf16_inputs(rng, 67000 + 4 * i, (Msum, K))
     bb = _bf16_inputs(rng, 67001 + 4 * i, (G, N, K))
-    buf, d = _out((Msum, N), "bf16", cs["pad"])
+    buf, d = _out((Msum, N), cs["d_kind"], cs["pad"])
     mg.m_grouped_bf16_gemm_nt_contiguous(_dev_bf16(ab), _dev_bf16(bb), d, to_dev(layout))
     torch.cuda.synchronize()
-    ref, written = oracle.m_grouped_bf16_gemm_nt_contiguous(ab, bb, np.where(layout < G, layout, -1))
+    ref_layout = np.where(layout < G, layout, -1)
+    ref, written = oracle.m_grouped_bf16_gemm_nt_contiguous(ab, bb, ref_layout)
+    S = None
+    if cs["d_kind"] == "f32":
+        S, _ = oracle.m_grouped_bf16_gemm_nt_contiguous(_abs_bf16(ab), _abs_bf16(bb), ref_layout)
     got = to_host(d)
-    _untouched(got, written, "bf16", None, None, what)
+    _untouched(got, written, cs["d_kind"], None, None, what)
     _pad_untouched(buf, N, what)
-    _check(got, ref, None, None, written, "bf16", K, what)
+    _check(got, ref, S, None, written, cs["d_kind"], K, what)
