@@ -248,6 +248,23 @@ int m_grouped_bf16_gemm_nt_contiguous(const dg_tensor* a, const dg_tensor* b, co
                                       const dg_tensor* grouped_layout, hipStream_t stream);
 
 /*
+ * The two grouped BF16 GEMMs in the accumulate form D = C + A . B^T of
+ * bf16_gemm_nt (the accumulate form of fp8_gemm_nt, "DeepInside DeepGEMM",
+ * section 4), the other arguments as above.  c is BF16 or F32 with d's
+ * shape ([Msum, N]; [G, max_m, N] or [G*max_m, N]), innermost stride 1,
+ * element-aligned; each element of C is added to the FP32 accumulator before
+ * d is rounded (BF16) or stored (F32).  c may be d itself (same base, dtype
+ * and strides: an in-place D += A . B^T); any other overlap with d is
+ * rejected.  Rows that are not computed (skipped blocks, rows past masked_m)
+ * are neither read from c nor written to d.
+ */
+int m_grouped_bf16_gemm_nt_contiguous_acc(const dg_tensor* a, const dg_tensor* b, const dg_tensor* c,
+                                          const dg_tensor* d, const dg_tensor* grouped_layout, hipStream_t stream);
+int m_grouped_bf16_gemm_nt_masked_acc(const dg_tensor* a, const dg_tensor* b, const dg_tensor* c,
+                                      const dg_tensor* d, const dg_tensor* masked_m, int64_t max_m_per_group,
+                                      hipStream_t stream);
+
+/*
  * Per-token FP8 cast: each row of x cut into 1x128 blocks along K; block
  * scale s = amax/448 (amax floored at 1e-4; with use_ue8m0 rounded up to a
  * power of two), q = e4m3(x/s) rounded to nearest even after clamping to

@@ -37,6 +37,8 @@ ENTRY_POINTS = (
     "m_grouped_bf16_gemm_nt_masked",
     "bf16_gemm_nt",
     "m_grouped_bf16_gemm_nt_contiguous",
+    "m_grouped_bf16_gemm_nt_contiguous_acc",
+    "m_grouped_bf16_gemm_nt_masked_acc",
     "per_token_cast_to_fp8",
     "per_block_cast_to_fp8",
     "pack_ue8m0_to_int",
@@ -103,6 +105,8 @@ def load_library(path=None):
         "m_grouped_fp8_gemm_nt_masked": ([T, T, T, T, T, T, i64, vp], ctypes.c_int),
         "m_grouped_fp8_gemm_nt_contiguous_acc": ([T, T, T, T, T, T, T, vp], ctypes.c_int),
         "m_grouped_fp8_gemm_nt_masked_acc": ([T, T, T, T, T, T, T, i64, vp], ctypes.c_int),
+        "m_grouped_bf16_gemm_nt_contiguous_acc": ([T, T, T, T, T, vp], ctypes.c_int),
+        "m_grouped_bf16_gemm_nt_masked_acc": ([T, T, T, T, T, i64, vp], ctypes.c_int),
         "m_grouped_bf16_gemm_nt_masked": ([T, T, T, T, i64, vp], ctypes.c_int),
         "bf16_gemm_nt": ([T, T, T, T, vp], ctypes.c_int),
         "m_grouped_bf16_gemm_nt_contiguous": ([T, T, T, T, vp], ctypes.c_int),
@@ -250,8 +254,15 @@ def m_grouped_fp8_gemm_nt_masked(a, b, sfa, sfb, d, masked_m, max_m_per_group, s
     return d
 
 
-def m_grouped_bf16_gemm_nt_masked(a, b, d, masked_m, max_m_per_group, stream=None):
+def m_grouped_bf16_gemm_nt_masked(a, b, d, masked_m, max_m_per_group, stream=None, c=None):
+    """Masked grouped BF16 GEMM; with c (BF16/F32, d's shape, may be d) the
+    accumulate form d = c + a . b^T (m_grouped_bf16_gemm_nt_masked_acc)."""
     lib = load_library()
+    if c is not None:
+        _check(lib.m_grouped_bf16_gemm_nt_masked_acc(_ref(describe(a)), _ref(describe(b)), _ref(describe(c)),
+                                                     _ref(describe(d)), _ref(describe(masked_m)), int(max_m_per_group),
+                                                     _stream(stream)))
+        return d
     _check(lib.m_grouped_bf16_gemm_nt_masked(_ref(describe(a)), _ref(describe(b)), _ref(describe(d)),
                                              _ref(describe(masked_m)), int(max_m_per_group), _stream(stream)))
     return d
@@ -265,8 +276,15 @@ def bf16_gemm_nt(a, b, c, d, stream=None):
     return d
 
 
-def m_grouped_bf16_gemm_nt_contiguous(a, b, d, grouped_layout, stream=None):
+def m_grouped_bf16_gemm_nt_contiguous(a, b, d, grouped_layout, stream=None, c=None):
+    """Contiguous grouped BF16 GEMM; with c (BF16/F32, d's shape, may be d)
+    the accumulate form d = c + a . b^T (m_grouped_bf16_gemm_nt_contiguous_acc)."""
     lib = load_library()
+    if c is not None:
+        _check(lib.m_grouped_bf16_gemm_nt_contiguous_acc(_ref(describe(a)), _ref(describe(b)), _ref(describe(c)),
+                                                         _ref(describe(d)), _ref(describe(grouped_layout)),
+                                                         _stream(stream)))
+        return d
     _check(lib.m_grouped_bf16_gemm_nt_contiguous(_ref(describe(a)), _ref(describe(b)), _ref(describe(d)),
                                                  _ref(describe(grouped_layout)), _stream(stream)))
     return d

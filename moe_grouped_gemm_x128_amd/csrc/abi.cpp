@@ -504,16 +504,27 @@ int bf16_gemm_common(int mode, const dg_tensor* a, const dg_tensor* b, const dg_
   DG_TRY(check_no_alias(d, "d", b, "b"));
   if (meta != nullptr) DG_TRY(check_no_alias(d, "d", meta, "metadata"));
   bool c_f32 = false;
-  int64_t ldc = 0;
+  int64_t ldc = 0, c_gs = 0;
   if (c != nullptr) {
+    // C shaped like d: [M, N] (dense), [Msum, N] (contiguous), [G, max_m, N]
+    // or [G*max_m, N] (masked, its own group stride)
     DG_TRY(check_basic(c, "c", true));
     if (c->dtype != DG_BF16 && c->dtype != DG_F32) return fail(DG_INVALID_ARG, "%s: c must be BF16 or F32", fname);
-    if (c->ndim != 2 || c->shape[0] != M || c->shape[1] != N)
-      return fail(DG_INVALID_ARG, "%s: c must be [M, N] = [%lld, %lld]", fname, (long long)M, (long long)N);
+    View3 vc;
+    if (mode == dgmi::MODE_MASKED) {
+      DG_TRY(view3(c, "c", G, max_m, &vc));
+    } else {
+      if (c->ndim != 2) return fail(DG_INVALID_ARG, "%s: c must be 2-D", fname);
+      DG_TRY(view3(c, "c", 1, 0, &vc));
+    }
+    if ((mode == dgmi::MODE_MASKED && vc.G != G) || vc.R != M || vc.C != N)
+      return fail(DG_INVALID_ARG, "%s: c must have the shape of d ([..,%lld,%lld])", fname, (long long)M,
+                  (long long)N);
     c_f32 = c->dtype == DG_F32;
     if (!aligned(c->data, c_f32 ? 4 : 2)) return fail(DG_INVALID_ARG, "%s: c must be element-aligned", fname);
-    ldc = c->stride[0];
-    const bool same_as_d = c->data == d->data && c->dtype == d->dtype && ldc == d->stride[0];
+    ldc = vc.sr;
+    c_gs = vc.sg;
+    const bool same_as_d = c->data == d->data && c->dtype == d->dtype && ldc == vd.sr && (G <= 1 || c_gs == vd.sg);
     if (!same_as_d) DG_TRY(check_no_alias(d, "d", c, "c"));
   }
   // the kernel addresses A and B in bytes
@@ -524,6 +535,7 @@ int bf16_gemm_common(int mode, const dg_tensor* a, const dg_tensor* b, const dg_
   p.d_f32 = d_f32 ? 1 : 0;
   p.c = c != nullptr ? c->data : nullptr;
   p.ldc = ldc;
+  p.c_gs = c_gs;
   p.c_f32 = c_f32 ? 1 : 0;
   p.meta = meta ? static_cast<const int32_t*>(meta->data) : nullptr;
   p.lda = 2 * va.sr;
@@ -661,6 +673,21 @@ int m_grouped_bf16_gemm_nt_masked(const dg_tensor* a, const dg_tensor* b, const 
   if (masked_m == nullptr) return fail(DG_INVALID_ARG, "m_grouped_bf16_gemm_nt_masked: masked_m is NULL");
   return bf16_gemm_common(dgmi::MODE_MASKED, a, b, nullptr, d, masked_m, max_m_per_group, stream,
                           "m_grouped_bf16_gemm_nt_masked");
+}
+
+int m_grouped_bf16_gemm_nt_contiguous_acc(const dg_tensor* a, const dg_tensor* b, const dg_tensor* c,
+                                          const dg_tensor* d, const dg_tensor* grouped_layout, hipStream_t stream) {
+  if (grouped_layout == nullptr)
+    return fail(DG_INVALID_ARG, "m_grouped_bf16_gemm_nt_contiguous_acc: grouped_layout is NULL");
+  return bf16_gemm_common(dgmi::MODE_CONTIG, a, b, c, d, grouped_layout, 0, stream,
+                          "m_grouped_bf16_gemm_nt_contiguous_acc");
+}
+
+int m_grouped_bf16_gemm_nt_masked_acc(const dg_tensor* a, const dg_tensor* b, const dg_tensor* c, const dg_tensor* d,
+                                      const dg_tensor* masked_m, int64_t max_m_per_group, hipStream_t stream) {
+  if (masked_m == nullptr) return fail(DG_INVALID_ARG, "m_grouped_bf16_gemm_nt_masked_acc: masked_m is NULL");
+  return bf16_gemm_common(dgmi::MODE_MASKED, a, b, c, d, masked_m, max_m_per_group, stream,
+                          "m_grouped_bf16_gemm_nt_masked_acc");
 }
 
 int per_token_cast_to_fp8(const dg_tensor* x, const dg_tensor* q, const dg_tensor* sf, int use_ue8m0,

@@ -77,6 +77,31 @@ def test_bf16_gemm_validation_errors(lib):
     # an F32 d is taken (past validation the CPU build's launch fails: no GPU here)
     assert contig(_t((256, K), torch.bfloat16), bg, _t((256, N), torch.float32), lay) not in (binding.DG_UNSUPPORTED,
                                                                                            binding.DG_INVALID_ARG)
+    # accumulate forms: c with d's shape (masked: per group), BF16 or F32, not overlapping d partly
+    ag = _t((256, K), torch.bfloat16)
+
+    def contig_acc(c, d=dg):
+        return lib.m_grouped_bf16_gemm_nt_contiguous_acc(ctypes.byref(D(ag)), ctypes.byref(D(bg)), ctypes.byref(D(c)),
+                                                         ctypes.byref(D(d)), ctypes.byref(D(lay)), None)
+
+    assert contig_acc(_t((256, N + 1), torch.bfloat16)) == binding.DG_INVALID_ARG  # c shape
+    assert contig_acc(_t((256, N), torch.int32)) == binding.DG_INVALID_ARG  # c dtype
+    big = _t((257, N), torch.bfloat16)
+    assert contig_acc(big[1:], d=big[:256]) == binding.DG_INVALID_ARG  # partial overlap of c and d
+    assert "overlaps" in binding.last_error()
+    assert contig_acc(dg) not in (binding.DG_UNSUPPORTED, binding.DG_INVALID_ARG)  # in place: taken
+    max_m = 64
+    am, dm, mm = _t((3, max_m, K), torch.bfloat16), _t((3, max_m, N), torch.float32), _t((3,), torch.int32)
+
+    def masked_acc(c):
+        return lib.m_grouped_bf16_gemm_nt_masked_acc(ctypes.byref(D(am)), ctypes.byref(D(bg)), ctypes.byref(D(c)),
+                                                     ctypes.byref(D(dm)), ctypes.byref(D(mm)), max_m, None)
+
+    assert masked_acc(_t((2, max_m, N), torch.float32)) == binding.DG_INVALID_ARG  # groups
+    assert masked_acc(_t((3, max_m, N + 8), torch.float32)[..., :N]) not in (binding.DG_UNSUPPORTED,
+                                                                           binding.DG_INVALID_ARG)  # own strides
+    assert lib.m_grouped_bf16_gemm_nt_masked_acc(ctypes.byref(D(am)), ctypes.byref(D(bg)), ctypes.byref(D(dm)),
+                                                 ctypes.byref(D(dm)), None, max_m, None) == binding.DG_INVALID_ARG
 
 
 def test_query_config_is_a_pure_function_of_shapes(lib):

@@ -187,3 +187,57 @@ def test_bf16_contiguous_f32_out(layout, N):
     rows = torch.from_numpy(written).cuda()
     assert torch.equal(d[rows].to(torch.bfloat16).view(torch.int16), d16[rows].view(torch.int16))
     assert_f32_close(got[written], ref[written], S[written], K, "bf16 contiguous F32 d")
+
+
+@pytest.mark.parametrize("c_kind", ["bf16", "f32", "inplace"])
+@pytest.mark.parametrize("d_kind", ["bf16", "f32"])
+@pytest.mark.parametrize("layout,N", [([2, -1, 0, 2, 1, -1, 5], 300), ([0, 0, 1, 1, 2, 2, 0, 0] * 4, 4096)])
+def test_bf16_contiguous_accumulate(layout, N, c_kind, d_kind):
+    """D = C + A . B^T (m_grouped_bf16_gemm_nt_contiguous_acc): C BF16 or
+    F32 shaped like d, or d itself; skipped blocks are neither read from C
+    nor written."""
+    from helpers import assert_f32_close
+
+    say(f"m_grouped_bf16_gemm_nt_contiguous accumulate N={N} c={c_kind} d={d_kind}")
+    mg = _mg()
+    layout = np.array(layout, dtype=np.int32)
+    G, K = 3, 192 if N < 4096 else 64
+    Msum = layout.size * 128
+    ab = synth.bf16_bits_from_f32(synth.normal_f32(193, (Msum, K)))
+    bb = synth.bf16_bits_from_f32(synth.normal_f32(194, (G, N, K)))
+    xc = synth.normal_f32(195, (Msum, N)) * np.float32(4.0)
+    cbits = synth.bf16_bits_from_f32(xc)
+    if d_kind == "f32":
+        d = torch.full((Msum, N), float("nan"), dtype=torch.float32, device="cuda")
+    else:
+        d = _sentinel((Msum, N))
+    if c_kind == "bf16":
+        c, cref = _dev_bf16(cbits), oracle.bf16_decode(cbits)
+    elif c_kind == "f32":
+        c, cref = to_dev(xc), xc.astype(np.float64)
+    else:
+        if d_kind == "f32":
+            d.copy_(to_dev(xc))
+            cref = xc.astype(np.float64)
+        else:
+            d.copy_(_dev_bf16(cbits))
+            cref = oracle.bf16_decode(cbits)
+        c = d
+    mg.m_grouped_bf16_gemm_nt_contiguous(_dev_bf16(ab), _dev_bf16(bb), d, to_dev(layout), c=c)
+    torch.cuda.synchronize()
+    ref_layout = np.where(layout < G, layout, -1)
+    ref, written = oracle.m_grouped_bf16_gemm_nt_contiguous(ab, bb, ref_layout)
+    ref = ref + cref
+    got = to_host(d)
+    if c_kind == "inplace":
+        keep = xc if d_kind == "f32" else cbits
+        assert np.array_equal(got[~written], keep[~written]), "skipped blocks changed"
+    elif d_kind == "f32":
+        assert np.isnan(got[~written]).all(), "skipped blocks written"
+    else:
+        assert np.all(got[~written] == SENTINEL_BF16), "skipped blocks written"
+    if d_kind == "f32":
+        S, _ = oracle.m_grouped_bf16_gemm_nt_contiguous(ab & np.uint16(0x7FFF), bb & np.uint16(0x7FFF), ref_layout)
+        assert_f32_close(got[written], ref[written], (S + np.abs(cref))[written], K, f"bf16 contiguous C={c_kind}")
+    else:
+        assert_bf16_close(got[written], ref[written], f"bf16 contiguous C={c_kind}")

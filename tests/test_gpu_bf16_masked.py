@@ -97,3 +97,55 @@ def test_bf16_masked_f32_out(G, max_m, N, K, mm):
     rows = torch.from_numpy(written).cuda()
     assert torch.equal(d[rows].to(torch.bfloat16).view(torch.int16), d16[rows].view(torch.int16))
     assert_f32_close(got[written], ref[written], S[written], K, "bf16 masked F32 d")
+
+
+@pytest.mark.parametrize("c_kind", ["bf16", "f32", "inplace"])
+@pytest.mark.parametrize("d_kind", ["bf16", "f32"])
+@pytest.mark.parametrize("G,max_m,N,K,mm", [(3, 200, 300, 192, [200, 0, 77]),
+                                            (16, 256, 4096, 64, [256, 0, 1, 255, 128, 129, 200, 17] * 2)])
+def test_bf16_masked_accumulate(G, max_m, N, K, mm, c_kind, d_kind):
+    """D = C + A . B^T per group (m_grouped_bf16_gemm_nt_masked_acc): C BF16
+    or F32 with d's shape, or d itself; rows past masked_m are neither read
+    from C nor written."""
+    from helpers import assert_f32_close
+
+    say(f"bf16 masked accumulate G={G} max_m={max_m} N={N} K={K} c={c_kind} d={d_kind}")
+    mg = _mg()
+    mm = np.array(mm, dtype=np.int32)
+    ab = synth.bf16_bits_from_f32(synth.normal_f32(157, (G, max_m, K)))
+    bb = synth.bf16_bits_from_f32(synth.normal_f32(158, (G, N, K)))
+    xc = synth.normal_f32(159, (G, max_m, N)) * np.float32(4.0)
+    if d_kind == "f32":
+        d = torch.full((G, max_m, N), float("nan"), dtype=torch.float32, device="cuda")
+    else:
+        d = torch.full((G, max_m, N), SENTINEL_BF16, dtype=torch.int16, device="cuda").view(torch.bfloat16)
+    cbits = synth.bf16_bits_from_f32(xc)
+    if c_kind == "bf16":
+        c, cref = _dev_bf16(cbits), oracle.bf16_decode(cbits)
+    elif c_kind == "f32":
+        c, cref = to_dev(xc), xc.astype(np.float64)
+    else:
+        if d_kind == "f32":
+            d.copy_(to_dev(xc))
+            cref = xc.astype(np.float64)
+        else:
+            d.copy_(_dev_bf16(cbits))
+            cref = oracle.bf16_decode(cbits)
+        c = d
+    mg.m_grouped_bf16_gemm_nt_masked(_dev_bf16(ab), _dev_bf16(bb), d, to_dev(mm), max_m, c=c)
+    torch.cuda.synchronize()
+    ref, written = oracle.m_grouped_bf16_gemm_nt_masked(ab, bb, mm, max_m)
+    ref = ref + cref
+    got = to_host(d)
+    if c_kind == "inplace":
+        keep = xc if d_kind == "f32" else cbits
+        assert np.array_equal(got[~written], keep[~written]), "rows past masked_m changed"
+    elif d_kind == "f32":
+        assert np.isnan(got[~written]).all(), "rows past masked_m written"
+    else:
+        assert np.all(got[~written] == SENTINEL_BF16), "rows past masked_m written"
+    if d_kind == "f32":
+        S, _ = oracle.m_grouped_bf16_gemm_nt_masked(ab & np.uint16(0x7FFF), bb & np.uint16(0x7FFF), mm, max_m)
+        assert_f32_close(got[written], ref[written], (S + np.abs(cref))[written], K, f"bf16 masked C={c_kind}")
+    else:
+        assert_bf16_close(got[written], ref[written], f"bf16 masked C={c_kind}")

@@ -229,7 +229,7 @@ def masked_case(i, bf16=False):
         N, K = _loguni(rng, 16, 2200), kunit * int(rng.integers(1, 9))
     case = dict(G=G, max_m=max_m, N=N, K=K, mm=_masked_m(rng, G, max_m), pad=int(rng.integers(0, 5)))
     if bf16:
-        case.update(d_kind=_pick(rng, ["bf16", "f32"]))
+        case.update(d_kind=_pick(rng, ["bf16", "f32"]), c_kind=_pick(rng, [None, "bf16", "f32", "inplace"]))
     else:
         case.update(scales=_pick(rng, ["f32", "ue8m0", "packed"]), rowb=bool(rng.random() < 0.25),
                     d_kind=_pick(rng, ["bf16", "f32"]), c_kind=_pick(rng, [None, "bf16", "f32", "inplace"]))
@@ -255,7 +255,7 @@ def contig_case(i, bf16=False):
         N, K = _loguni(rng, 16, 2200), kunit * int(rng.integers(1, 9))
     case = dict(G=G, N=N, K=K, layout=_layout(rng, G, nblocks), pad=int(rng.integers(0, 5)))
     if bf16:
-        case.update(d_kind=_pick(rng, ["bf16", "f32"]))
+        case.update(d_kind=_pick(rng, ["bf16", "f32"]), c_kind=_pick(rng, [None, "bf16", "f32", "inplace"]))
     else:
         case.update(scales=_pick(rng, ["f32", "ue8m0", "packed"]), rowb=bool(rng.random() < 0.25),
                     d_kind=_pick(rng, ["bf16", "f32"]), c_kind=_pick(rng, [None, "bf16", "f32", "inplace"]))
@@ -496,15 +496,19 @@ def test_sweep_bf16_masked(i):
     ab = _bf16_inputs(rng, 66000 + 4 * i, (G, max_m, K))
     bb = _bf16_inputs(rng, 66001 + 4 * i, (G, N, K))
     buf, d = _out((G, max_m, N), cs["d_kind"], cs["pad"])
+    c, cref, stored = _accumulate_input(rng, 66002 + 4 * i, (G, max_m, N), cs["c_kind"], d)
     mm = np.array(cs["mm"], dtype=np.int32)
-    mg.m_grouped_bf16_gemm_nt_masked(_dev_bf16(ab), _dev_bf16(bb), d, to_dev(mm), max_m)
+    mg.m_grouped_bf16_gemm_nt_masked(_dev_bf16(ab), _dev_bf16(bb), d, to_dev(mm), max_m, c=c)
     torch.cuda.synchronize()
     ref, written = oracle.m_grouped_bf16_gemm_nt_masked(ab, bb, mm, max_m)
     S = None
     if cs["d_kind"] == "f32":
         S, _ = oracle.m_grouped_bf16_gemm_nt_masked(_abs_bf16(ab), _abs_bf16(bb), mm, max_m)
+    if cref is not None:
+        ref = ref + cref
+        S = S + np.abs(cref) if S is not None else None
     got = to_host(d)
-    _untouched(got, written, cs["d_kind"], None, None, what)
+    _untouched(got, written, cs["d_kind"], cs["c_kind"], stored, what)
     _pad_untouched(buf, N, what)
     _check(got, ref, S, None, written, cs["d_kind"], K, what)
 
@@ -522,14 +526,18 @@ def test_sweep_bf16_contiguous(i):
     ab = _bf16_inputs(rng, 67000 + 4 * i, (Msum, K))
     bb = _bf16_inputs(rng, 67001 + 4 * i, (G, N, K))
     buf, d = _out((Msum, N), cs["d_kind"], cs["pad"])
-    mg.m_grouped_bf16_gemm_nt_contiguous(_dev_bf16(ab), _dev_bf16(bb), d, to_dev(layout))
+    c, cref, stored = _accumulate_input(rng, 67002 + 4 * i, (Msum, N), cs["c_kind"], d)
+    mg.m_grouped_bf16_gemm_nt_contiguous(_dev_bf16(ab), _dev_bf16(bb), d, to_dev(layout), c=c)
     torch.cuda.synchronize()
     ref_layout = np.where(layout < G, layout, -1)
     ref, written = oracle.m_grouped_bf16_gemm_nt_contiguous(ab, bb, ref_layout)
     S = None
     if cs["d_kind"] == "f32":
         S, _ = oracle.m_grouped_bf16_gemm_nt_contiguous(_abs_bf16(ab), _abs_bf16(bb), ref_layout)
+    if cref is not None:
+        ref = ref + cref
+        S = S + np.abs(cref) if S is not None else None
     got = to_host(d)
-    _untouched(got, written, cs["d_kind"], None, None, what)
+    _untouched(got, written, cs["d_kind"], cs["c_kind"], stored, what)
     _pad_untouched(buf, N, what)
     _check(got, ref, S, None, written, cs["d_kind"], K, what)
