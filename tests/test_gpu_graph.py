@@ -364,3 +364,79 @@ def test_layouts_and_accumulate_forms_replay_under_capture():
         S, Gt = fp8_bound_terms(oracle.fp8_gemm_nt, ra[g, :m], rb[g], rsfa[g, :m], rsfb[g])
         assert_f32_close(got["dm"][g, :m], ref, S + np.abs(cmh[g, :m]), fp8_rounding_count(K), f"masked F32 group {g}",
                          G=Gt)
+
+
+def test_row_scale_and_output_forms_replay_under_capture():
+    """One graph with the forms that take one B scale per row and the F32
+    and FP8 outputs: the dense FP8 GEMM (row scales, F32 d), the FP8-output
+    GEMM (row scales, the 256 x 128 tile), the TT layout (row scales, F32 d)
+    and the masked BF16 GEMM's accumulate form (BF16 C, F32 d); replayed
+    three times with new inputs, each replay bit-identical to an eager run."""
+    mg = _mg()
+    M, N, K = 256, 384, 512
+    G, max_m, Kb = 2, 128, 256
+    xa = torch.empty((M, K), device="cuda")
+    xb = torch.empty((N, K), device="cuda")
+    xm = torch.empty((G, max_m, Kb), device="cuda")
+    xmb = torch.empty((G, N, Kb), device="cuda")
+    xc = torch.empty((G, max_m, N), device="cuda")
+    masked_m = torch.tensor([100, 37], dtype=torch.int32, device="cuda")
+    qa = torch.empty((M, K), dtype=torch.uint8, device="cuda")
+    sfa = torch.empty((K // 128, M), dtype=torch.float32, device="cuda").t()
+    qb = torch.empty((N, K), dtype=torch.uint8, device="cuda")
+    sfb = torch.empty((N, K // 128), dtype=torch.float32, device="cuda")  # one scale per row of B
+    a_st = torch.empty((K, M), dtype=torch.uint8, device="cuda")  # A stored MN-major
+    outs = {"d32": torch.empty((M, N), dtype=torch.float32, device="cuda"),
+            "q8": torch.empty((M, N), dtype=torch.uint8, device="cuda"),
+            "sfq": torch.empty((M, N // 128), dtype=torch.float32, device="cuda"),
+            "tt32": torch.empty((M, N), dtype=torch.float32, device="cuda"),
+            "m32": torch.empty((G, max_m, N), dtype=torch.float32, device="cuda")}
+
+    def step():
+        mg.per_token_cast_to_fp8(xa, qa, sfa)
+        mg.per_token_cast_to_fp8(xb, qb, sfb)
+        mg.fp8_gemm_nt(qa, qb, sfa, sfb, None, outs["d32"])
+        mg.fp8_gemm_nt_fp8_out(qa, qb, sfa, sfb, None, outs["q8"], outs["sfq"])
+        a_st.copy_(qa.t())
+        mg.fp8_gemm_tt(a_st, qb, sfa, sfb, None, outs["tt32"])
+        mg.m_grouped_bf16_gemm_nt_masked(xm.to(torch.bfloat16), xmb.to(torch.bfloat16), outs["m32"], masked_m, max_m,
+                                         c=xc.to(torch.bfloat16))
+
+    def fill(seed):
+        for i, t in enumerate((xa, xb, xm, xmb, xc)):
+            t.copy_(torch.from_numpy(synth.normal_f32(seed + i, tuple(t.shape))))
+        for o in outs.values():
+            o.view(torch.uint8).fill_(0x5A)
+
+    fill(900)
+    step()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        graph.capture_begin()
+        step()
+        graph.capture_end()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    for r in range(3):
+        say(f"row-scale / output-form graph replay {r}")
+        fill(910 + 10 * r)
+        graph.replay()
+        torch.cuda.synchronize()
+        got = {k: to_host(v).copy() for k, v in outs.items()}
+        fill(910 + 10 * r)
+        step()
+        torch.cuda.synchronize()
+        for k, v in outs.items():
+            assert np.array_equal(to_host(v).view(np.uint8), got[k].view(np.uint8)), f"replay {r}: {k} differs from eager"
+        # the TT layout equals the NT GEMM; rows past masked_m keep the fill
+        assert np.array_equal(got["tt32"].view(np.uint32), got["d32"].view(np.uint32))
+        assert np.all(got["m32"][0, 100:].view(np.uint8) == 0x5A) and np.all(got["m32"][1, 37:].view(np.uint8) == 0x5A)
+    # the last replay's F32 dense result against the oracle
+    ra, rsfa = oracle.per_token_cast_to_fp8(to_host(xa))
+    rb, rsfb = oracle.per_token_cast_to_fp8(to_host(xb))
+    S, Gt = fp8_bound_terms(oracle.fp8_gemm_nt, ra, rb, rsfa, rsfb)
+    assert_f32_close(got["d32"], oracle.fp8_gemm_nt(ra, rb, rsfa, rsfb), S, fp8_rounding_count(K),
+                     "replayed dense FP8, row scales, F32 d", G=Gt)
