@@ -6,6 +6,7 @@
 // "DeepGEMM tested by Novita AI", section "Technological Innovations"):
 //   D[m, n] = sum_kb P_kb[m, n] * sfa[m, kb] * sfb[n / 128, kb],
 //   P_kb    = A[m, kb*128 : kb*128+128] . B[n, same]^T
+// (or sfb[n, kb] with one scale per row of B, section 4's example call)
 // Each 128-wide K-block is exactly one v_mfma_f32_16x16x128_f8f6f4 per
 // 16x16 output fragment, computed into a fresh FP32 partial; the partial is
 // then promoted into the FP32 accumulator with one FMA per element using the
@@ -13,7 +14,9 @@
 // UE8M0 scales the promote is the MFMA's own: v_mfma_scale_f32_16x16x128_
 // f8f6f4 multiplies by 2^(e-127) per A row and per B row and accumulates in
 // place (the SM100 recipe of "DeepInside DeepGEMM", section 2, on CDNA4).
-// Output is BF16 (round to nearest even).
+// Output is BF16 (round to nearest even), the FP32 accumulator itself, or
+// (dense) FP8 cast per token in the epilogue; an accumulate input C is added
+// to the FP32 accumulator first.
 //
 // The BF16 kind ("DeepGEMM CUDA Graph Compatibility for Masked Grouped
 // GEMMs", the masked BF16 call of its capture example) computes
