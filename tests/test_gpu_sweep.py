@@ -9,7 +9,9 @@ index, so a failing case names everything needed to rerun it alone:
   * BF16 or F32 outputs with or without an accumulate input C (also in
     place), padded output rows;
   * random masked_m (clamped and negative values included) and random
-    contiguous layouts (runs of one group, skipped blocks, ids past G).
+    contiguous layouts (runs of one group, skipped blocks, ids past G);
+  * the per-token and per-block casts and the MoE dispatch and combine on
+    random shapes and routings.
 Inputs carry a power-of-two magnitude per row (per 128-row block for
 block-scaled B) and per 128-column block, so a scale read from the wrong
 row or block shows.  The GEMMs are those of "DeepGEMM: clean and efficient
@@ -32,7 +34,7 @@ torch = pytest.importorskip("torch")
 
 SWEEP_SEED = 20261203
 FORMS = {"dense": 1, "mn": 2, "masked": 3, "contig": 4, "bf16_dense": 5, "bf16_masked": 6, "bf16_contig": 7,
-         "fp8_out": 8}
+         "fp8_out": 8, "cast": 9, "moe": 10}
 
 
 def _mg():
@@ -541,3 +543,122 @@ def test_sweep_bf16_contiguous(i):
     _untouched(got, written, cs["d_kind"], cs["c_kind"], stored, what)
     _pad_untouched(buf, N, what)
     _check(got, ref, S, None, written, cs["d_kind"], K, what)
+
+
+# ---------------------------------------------------------------------------
+# the casts and the MoE steps either side of the grouped GEMMs
+# ---------------------------------------------------------------------------
+
+def cast_case(i):
+    rng = _rng("cast", i)
+    G = int(rng.integers(2, 5)) if rng.random() < 0.25 else 0  # 0: a 2-D tensor
+    return dict(block=bool(rng.random() < 0.4), G=G, R=_loguni(rng, 1, 600 if G else 3000),
+                K=8 * _loguni(rng, 1, 1024), bf16=bool(rng.random() < 0.4), mn=bool(rng.random() < 0.3),
+                ue8m0=bool(rng.random() < 0.4), sf_mn=bool(rng.random() < 0.5), zero_rows=bool(rng.random() < 0.3))
+
+
+def moe_case(i):
+    rng = _rng("moe", i)
+    G = int(rng.integers(1, 41))
+    return dict(T=_loguni(rng, 1, 2000), k=int(rng.integers(1, min(8, G) + 1)), G=G, max_m=_loguni(rng, 1, 300),
+                K=8 * _loguni(rng, 1, 900), N=_loguni(rng, 1, 3000), p_none=float(rng.choice([0.0, 0.05, 0.2])),
+                x_bf16=bool(rng.random() < 0.4), ue8m0=bool(rng.random() < 0.4), align=_pick(rng, [128, 256]),
+                cap=float(rng.uniform(0.5, 1.5)))
+
+
+N_CAST, N_MOE = 24, 12
+
+
+@pytest.mark.parametrize("i", range(N_CAST))
+def test_sweep_cast(i):
+    """Per-token and per-block casts against the oracle, codes and scales bit
+    for bit: F32 or BF16 sources, K-major or MN-major, 2-D or 3-D, ragged K,
+    scales K-major or M-major, magnitudes over 2^-20 .. 2^11 with all-zero
+    rows (the amax floor)."""
+    cs = cast_case(i)
+    what = f"sweep cast {i} {cs}"
+    say(what)
+    mg = _mg()
+    rng = _rng("cast", 1000 + i)
+    lead = (cs["G"],) if cs["G"] else ()
+    R, K = cs["R"], cs["K"]
+    x = synth.normal_f32(68000 + 4 * i, lead + (R, K))
+    e = rng.integers(-20, 12, size=lead + (R, -(-K // 128)))
+    x = (x * np.exp2(np.repeat(e, 128, axis=-1)[..., :K])).astype(np.float32)
+    if cs["zero_rows"]:
+        x[..., rng.integers(0, R, size=max(1, R // 8)), :] = 0.0
+    if cs["bf16"]:
+        bits = synth.bf16_bits_from_f32(x)
+        x = oracle.bf16_decode(bits).astype(np.float32)
+        stored = np.ascontiguousarray(np.swapaxes(bits, -1, -2)) if cs["mn"] else bits
+        src = to_dev(stored.view(np.int16)).view(torch.bfloat16)
+    else:
+        src = to_dev(np.ascontiguousarray(np.swapaxes(x, -1, -2)) if cs["mn"] else x)
+    if cs["mn"]:
+        src = src.transpose(-1, -2)  # the logical [.., R, K] view of a tensor stored [.., K, R]
+    q = torch.full(lead + (R, K), 0x55, dtype=torch.uint8, device="cuda")
+    if cs["block"]:
+        sf = torch.full(lead + (-(-R // 128), -(-K // 128)), float("nan"), dtype=torch.float32, device="cuda")
+        mg.per_block_cast_to_fp8(src, q, sf, cs["ue8m0"])
+        rq, rsf = oracle.per_block_cast_to_fp8(x, cs["ue8m0"])
+    else:
+        if cs["sf_mn"] and not lead:
+            sf = torch.full((-(-K // 128), R), float("nan"), dtype=torch.float32, device="cuda").t()
+        else:
+            sf = torch.full(lead + (R, -(-K // 128)), float("nan"), dtype=torch.float32, device="cuda")
+        mg.per_token_cast_to_fp8(src, q, sf, cs["ue8m0"])
+        rq, rsf = oracle.per_token_cast_to_fp8(x, cs["ue8m0"])
+    torch.cuda.synchronize()
+    assert np.array_equal(to_host(q), rq), f"{what}: codes"
+    assert np.array_equal(to_host(sf).view(np.uint32), rsf.view(np.uint32)), f"{what}: scales"
+
+
+@pytest.mark.parametrize("i", range(N_MOE))
+def test_sweep_moe_dispatch_and_combine(i):
+    """MoE dispatch into the masked and the contiguous layouts (routing
+    tables, codes and scales bit for bit, untouched rows) and the combine
+    (within its FP32-sum bound), against the oracle."""
+    from test_gpu_moe import _check_dispatch, _combine_bound, _contig_buffers, _dispatch_buffers
+
+    cs = moe_case(i)
+    T, k, G, max_m, K, N = cs["T"], cs["k"], cs["G"], cs["max_m"], cs["K"], cs["N"]
+    what = f"sweep moe {i} {cs}"
+    say(what)
+    mg = _mg()
+    x = synth.normal_f32(69000 + 4 * i, (T, K))
+    topk, w = synth.moe_routing(69001 + 4 * i, T, G, k, cs["p_none"])
+    if cs["x_bf16"]:
+        xb = synth.bf16_bits_from_f32(x)
+        xd = to_dev(xb.view(np.int16)).view(torch.bfloat16)
+        x = oracle.bf16_decode(xb).astype(np.float32)
+    else:
+        xd = to_dev(x)
+    # masked layout
+    outs = _dispatch_buffers(T, K, k, G, max_m)
+    mg.moe_dispatch_masked_fp8(xd, to_dev(topk), *outs, use_ue8m0=cs["ue8m0"])
+    torch.cuda.synchronize()
+    _, rslot = _check_dispatch(x, topk, G, max_m, cs["ue8m0"], outs, what)
+    # contiguous layout: a capacity around the routed rows, in whole 128-row blocks
+    align = cs["align"]
+    Mcap = 128 * max(1, int(cs["cap"] * (T * k + (align - 1) * G) / 128))
+    couts = _contig_buffers(T, K, k, G, Mcap)
+    mg.moe_dispatch_contiguous_fp8(xd, to_dev(topk), *couts, align=align, use_ue8m0=cs["ue8m0"])
+    torch.cuda.synchronize()
+    a, sfa, layout, counts, slot = (to_host(t) for t in couts)
+    ra, rsfa, owned, rlayout, rcounts, rcslot = oracle.moe_dispatch_contiguous_fp8(x, topk, G, Mcap, cs["ue8m0"],
+                                                                                   align=align)
+    assert np.array_equal(counts, rcounts) and np.array_equal(layout, rlayout), f"{what}: contiguous tables"
+    assert np.array_equal(slot, rcslot), f"{what}: contiguous slots"
+    assert np.array_equal(a[owned], ra[owned]), f"{what}: contiguous codes"
+    assert np.array_equal(sfa[owned].view(np.uint32), rsfa[owned].view(np.uint32)), f"{what}: contiguous scales"
+    assert np.all(a[~owned] == 0x55) and np.all(np.isnan(sfa[~owned])), f"{what}: contiguous padding rows written"
+    # combine over the masked slots
+    d_bits = synth.bf16_bits_from_f32(synth.normal_f32(69002 + 4 * i, (G, max_m, N)))
+    y = torch.full((T, N), float("nan"), dtype=torch.bfloat16, device="cuda")
+    mg.moe_combine(to_dev(d_bits.view(np.int16)).view(torch.bfloat16), to_dev(rslot), to_dev(w), y)
+    torch.cuda.synchronize()
+    got = oracle.bf16_decode(to_host(y))
+    y_ref = oracle.moe_combine(d_bits, rslot, w)
+    assert np.all(np.isfinite(got)), f"{what}: combine output not written"
+    bound = _combine_bound(d_bits, rslot, w, y_ref)
+    assert np.all(np.abs(got - y_ref) <= bound * (1 + 1e-6)), f"{what}: combine outside the bound"
