@@ -44,7 +44,7 @@ Prints ONE JSON line.
 * `cpu_baseline`: the CPU oracle timed per configuration on bounded samples
   (about 10-30 s in total), with the host's core count and CPU model.
 
-Other workloads (for the measurements in the design notes):
+Other workloads (each run on its own with --workload):
   contiguous   -- MoE prefill: 4 groups x 8192 rows, (N, K) = (4096, 7168) and (7168, 2048)
   masked       -- MoE decode: 32 experts, max_m 256, masked_m ~ floor(192 U(0.7, 1.3)),
                   (N, K) = (4096, 7168) and (7168, 2048); metric GB/s

@@ -8,7 +8,7 @@ padded buffer of max_m rows of which masked_m[e] are valid; "DeepGEMM CUDA
 Graph Compatibility for Masked Grouped GEMMs", last section: the fused MoE
 path chains the input casting and the masked GEMM calls under the same
 stateless launch model).  The pages name the steps, not their definition;
-the reading taken (listed in the design notes):
+the reading taken:
 
   * Route: topk_idx [T, k] holds the expert of each (token, choice); a
     value outside [0, G) routes nowhere.  Pairs routed to expert e take its

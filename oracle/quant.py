@@ -19,7 +19,7 @@ What is computed:
     pack_ue8m0_to_int is not CUDA Graph capture safe", section "Expected
     behavior": shift the int32 view right by 23 and keep the low byte).
 
-Readings where the pages are silent (each listed in the design notes):
+Readings where the pages are silent:
   * amax is floored at AMAX_FLOOR = 1e-4 so an all-zero block has a finite
     scale and encodes to zeros.
   * s is the correctly rounded FP32 quotient amax/448, and the quantized
