@@ -6,7 +6,8 @@
   by FP32 FMAs, and a scaled instruction would apply E8M0 scale bytes of 0
   (2^-127) to every product.  The UE8M0 kinds must use the scaled instruction
   (the power-of-two scales are applied inside the matrix core).
-* No GEMM kernel may spill to scratch (private segment size 0).
+* No kernel of the library (GEMMs, casts, pack, MoE routing and combine)
+  may spill to scratch (private segment size 0).
 
 Skipped when the library has not been built here or the LLVM tools of the
 ROCm install are missing."""
@@ -19,7 +20,8 @@ import subprocess
 import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-OBJ = os.path.join(ROOT, "moe_grouped_gemm_x128_amd", "_build", "gemm.hip.o")
+BUILD = os.path.join(ROOT, "moe_grouped_gemm_x128_amd", "_build")
+OBJ = os.path.join(BUILD, "gemm.hip.o")
 LLVM = "/opt/rocm/lib/llvm/bin"
 TOOLS = ["llvm-objcopy", "clang-offload-bundler", "llvm-objdump", "llvm-readelf"]
 
@@ -27,21 +29,26 @@ TOOLS = ["llvm-objcopy", "clang-offload-bundler", "llvm-objdump", "llvm-readelf"
 KERNEL_RE = re.compile(r"gemm_kernelINS0_9TileShapeI((?:Li\d+E){5})EELi(\d+)ELi(\d+)ELi(\d+)ELi(\d+)E")
 
 
-@pytest.fixture(scope="module")
-def code_object(tmp_path_factory):
-    if not os.path.exists(OBJ):
+def _extract(obj, d):
+    """The gfx950 code object bundled in a hipcc object file."""
+    if not os.path.exists(obj):
         pytest.skip("library not built in-tree")
     if not all(os.path.exists(os.path.join(LLVM, t)) for t in TOOLS):
         pytest.skip("ROCm LLVM tools not found")
-    d = tmp_path_factory.mktemp("isa")
-    fat = str(d / "gemm.fatbin")
-    co = str(d / "gemm_gfx950.co")
-    subprocess.run([os.path.join(LLVM, "llvm-objcopy"), f"--dump-section=.hip_fatbin={fat}", OBJ, str(d / "x.o")],
+    base = os.path.basename(obj)
+    fat = str(d / (base + ".fatbin"))
+    co = str(d / (base + "_gfx950.co"))
+    subprocess.run([os.path.join(LLVM, "llvm-objcopy"), f"--dump-section=.hip_fatbin={fat}", obj, str(d / "x.o")],
                    check=True, capture_output=True)
     subprocess.run([os.path.join(LLVM, "clang-offload-bundler"), "--unbundle", "--type=o",
                     "--targets=hipv4-amdgcn-amd-amdhsa--gfx950", f"--input={fat}", f"--output={co}"],
                    check=True, capture_output=True)
     return co
+
+
+@pytest.fixture(scope="module")
+def code_object(tmp_path_factory):
+    return _extract(OBJ, tmp_path_factory.mktemp("isa"))
 
 
 def _functions(co):
@@ -90,3 +97,19 @@ def test_no_gemm_kernel_spills(code_object):
             assert int(s.split(":", 1)[1]) == 0, f"{name} uses scratch"
             seen += 1
     assert seen >= 20
+
+
+@pytest.mark.parametrize("src", ["quant.hip", "moe.hip"])
+def test_no_other_kernel_spills(src, tmp_path):
+    co = _extract(os.path.join(BUILD, src + ".o"), tmp_path)
+    notes = subprocess.run([os.path.join(LLVM, "llvm-readelf"), "--notes", co], check=True, capture_output=True,
+                           text=True).stdout
+    name, seen = None, 0
+    for line in notes.splitlines():
+        s = line.strip()
+        if s.startswith(".name:"):
+            name = s.split(":", 1)[1].strip()
+        elif s.startswith(".private_segment_fixed_size:") and name:
+            assert int(s.split(":", 1)[1]) == 0, f"{name} uses scratch"
+            seen += 1
+    assert seen >= 3
