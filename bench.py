@@ -415,7 +415,7 @@ class MoeDecodeWorkload:
     GEMM and moe_combine on 4096 tokens."""
     name = "moe_decode_dispatch_gemm_combine"
     contig = False
-    align = 256  # contiguous regions: row granule (set by --moe-align)
+    align = 128  # contiguous regions: row granule (set by --moe-align)
 
     def __init__(self, torch, mg, synth):
         self.torch, self.mg = torch, mg
@@ -984,7 +984,7 @@ def main():
                          "graph workload is always timed as graph replays")
     ap.add_argument("--event-every", type=int, default=10,
                     help="record HIP events around the GEMM calls of one timed step in this many (plus the last)")
-    ap.add_argument("--moe-align", type=int, choices=(128, 256), default=256,
+    ap.add_argument("--moe-align", type=int, choices=(128, 256), default=128,
                     help="moe_prefill: row granule of the experts' regions in the contiguous layout")
     ap.add_argument("--no-masked", action="store_true", help="dense: skip the masked grouped GEMM block")
     ap.add_argument("--no-cpu-baseline", action="store_true")

@@ -32,10 +32,10 @@
 //                 from grouped_layout on the device, negative = skip.  With
 //                 256-row tiles each run of blocks of one group is cut into
 //                 tiles from its first block (two blocks a tile, one at the
-//                 run's end), found by scanning back to the run's start; two
-//                 copies of the 256-row tiling start tiles at the even and
-//                 at the odd blocks, and a workgroup whose block starts no
-//                 tile exits at once.
+//                 run's end); each workgroup lists the tile starts with a
+//                 block-wide scan of grouped_layout, the grid holds one
+//                 workgroup per block and column tile, and those past the
+//                 listed tiles exit at once.
 //   masked     -- G x tiles of [max_m, N]; a tile whose first row is at or
 //                 beyond masked_m[g] exits at once, rows beyond masked_m[g]
 //                 are never stored
@@ -158,6 +158,70 @@ __device__ __forceinline__ uint32_t load_scale_raw(const void* base, int64_t idx
 template <int SF>
 __device__ __forceinline__ float scale_value(uint32_t raw, int kb) {
   return (SF & SF_UE8M0) == 0 ? __uint_as_float(raw) : ue8m0_to_f32((raw >> ((kb & 3) * 8)) & 0xffu);
+}
+
+// Tile starts of a contiguous layout with 256-row tiles.  A run is a
+// maximal sequence of blocks of one group; the blocks at even offsets in it
+// start tiles.  Every thread takes one block a pass (NW*64 blocks a pass);
+// per wave, ballots give the run starts and tile starts among its lanes, and
+// the waves' masks, shared in LDS, give each lane its run's start (the
+// latest one at or before it, or the carry from earlier passes) and each
+// tile start its place in the list.  Entry j of the list: first block x 2 +
+// (the next block belongs to the tile), and grp[j] its group.  Returns the
+// number of tiles; every thread calls it, the lists are complete on return.
+template <int NW>
+__device__ __forceinline__ int contig_tile_list(int nblk, const int* layout, int G, int* list, int* grp,
+                                                uint64_t* ws_rs, int* ws_cnt) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const uint64_t below = (1ull << lane) - 1;  // lanes before this one
+  int count = 0, carry = -1;                  // tiles so far; latest run start so far
+  for (int base = 0; base < nblk; base += NW * 64) {
+    // the block's group and its neighbours' (ids outside [0, G) skip a
+    // block); the loads are clamped into the layout, so all three issue at
+    // once, and the selects put -1 where a neighbour does not exist
+    const int b = base + tid, bc = min(b, nblk - 1);
+    const int v = layout[bc], vp = layout[max(bc - 1, 0)], vn = layout[min(bc + 1, nblk - 1)];
+    auto valid = [G](int x) { return x >= 0 && x < G ? x : -1; };
+    const int gb = b < nblk ? valid(v) : -1;
+    const int gp = b > 0 && b < nblk ? valid(vp) : -1;
+    const int gn = b + 1 < nblk ? valid(vn) : -1;
+    const uint64_t m_rs = __ballot(gb >= 0 && gb != gp);  // run starts
+    if (lane == 0) ws_rs[wave] = m_rs;
+    __syncthreads();
+    // this lane's run start: the latest in its own wave at or before it,
+    // else the latest in the earlier waves, else the carry (run starts grow
+    // with the block index)
+    int before = carry, last = carry;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      const uint64_t x = ws_rs[w];
+      const int h = x != 0 ? base + w * 64 + 63 - __clzll(x) : -1;
+      last = max(last, h);
+      before = w < wave ? max(before, h) : before;
+    }
+    const uint64_t mine = m_rs & (below | (1ull << lane));
+    const int rs = mine != 0 ? b - lane + 63 - __clzll(mine) : before;
+    const bool starts = gb >= 0 && ((b - rs) & 1) == 0;
+    const uint64_t m_st = __ballot(starts);
+    if (lane == 0) ws_cnt[wave] = __popcll(m_st);
+    __syncthreads();
+    int off = count, tot = 0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      const int c = ws_cnt[w];
+      off += w < wave ? c : 0;
+      tot += c;
+    }
+    if (starts) {
+      const int j = off + __popcll(m_st & below);
+      list[j] = 2 * b + (gn == gb ? 1 : 0);
+      grp[j] = gb;
+    }
+    count += tot;
+    carry = last;
+  }
+  __syncthreads();
+  return count;
 }
 
 // Tile index of this workgroup after the XCD remap: the hardware deals
@@ -441,65 +505,59 @@ __global__ __launch_bounds__(T::NT) void gemm_kernel(const GemmParams p) {
   // ---- tile decode (device metadata only gates early exits, never the grid)
   const int per_group = p.tiles_m * p.tiles_n;
   const int total = (MODE == MODE_MASKED ? p.G : 1) * per_group;
+  // group of a 128-row block of the contiguous layout; ids outside [0, G)
+  // skip the block
+  auto group_of = [&](int blk) {
+    const int v = p.meta[blk];
+    return (v < 0 || v >= p.G) ? -1 : v;
+  };
   // Contiguous layout with 256-row tiles: a block at an even offset in its
   // run of equal group ids starts a tile of the run's next two blocks (one
-  // at the run's end), so tiles never straddle groups.  The grid holds two
-  // copies of the 256-row tiling: the first looks at the even blocks, the
-  // second at the odd ones, and a workgroup whose block starts no tile exits
-  // at once -- a layout whose runs all start at even blocks runs its tiles
-  // in the first copy, densely in dispatch order, and exits in the second.
+  // at the run's end), so tiles never straddle groups.  Every workgroup
+  // scans grouped_layout and builds the list of those tile starts, in block
+  // order, in the first two A stages (free until the prologue).  The grid holds
+  // one workgroup per 128-row block and column tile: the first
+  // (list length) x tiles_n take the listed tiles in the usual XCD-banded
+  // order, the rest -- all after them in dispatch order -- exit at once.
   constexpr bool RUNS = MODE == MODE_CONTIG && T::BM == 256;
-  int bid = blockIdx.x;
-  int odd = 0;
-  if (RUNS && bid >= total) {
-    odd = 1;
-    bid -= total;
+  int tm, tn, g = 0, hi = T::BM;
+  if constexpr (RUNS) {
+    static_assert(A_STAGE >= 4 * RUNS_MAX_BLOCKS, "the tile lists fit the first two A stages");
+    __shared__ uint64_t ws_rs[T::NW];
+    __shared__ int ws_cnt[T::NW];
+    int* list = reinterpret_cast<int*>(lds_a0);
+    int* grp = reinterpret_cast<int*>(lds_a1);
+    const int count = contig_tile_list<T::NW>(p.M / 128, p.meta, p.G, list, grp, ws_rs, ws_cnt);
+    const int total_c = count * p.tiles_n;
+    if ((int)blockIdx.x >= total_c) return;
+    int j;
+    band_order(xcd_remap(blockIdx.x, total_c), count, p.tiles_n, 8, j, tn);
+    const int e = __builtin_amdgcn_readfirstlane(list[j]);
+    tm = e >> 1;  // the tile's first 128-row block
+    g = __builtin_amdgcn_readfirstlane(grp[j]);
+    if ((e & 1) == 0) hi = 128;  // one block: the run's last
+    __syncthreads();  // every wave has read the lists before the prologue loads into these stages
+  } else {
+    int t = xcd_remap(blockIdx.x, total);
+    if (MODE == MODE_MASKED) {
+      g = t / per_group;
+      t -= g * per_group;
+    }
+    band_order(t, p.tiles_m, p.tiles_n, MODE == MODE_MASKED ? p.tiles_m : 8, tm, tn);
   }
-  int t = xcd_remap(bid, total);
-  int g = 0;
-  if (MODE == MODE_MASKED) {
-    g = t / per_group;
-    t -= g * per_group;
-  }
-  int tm, tn;
-  band_order(t, p.tiles_m, p.tiles_n, MODE == MODE_MASKED ? p.tiles_m : 8, tm, tn);
-  const int m0 = __builtin_amdgcn_readfirstlane(tm * T::BM + odd * 128), n0 = __builtin_amdgcn_readfirstlane(tn * T::BN);
+  const int m0 = __builtin_amdgcn_readfirstlane(RUNS ? tm * 128 : tm * T::BM);
+  const int n0 = __builtin_amdgcn_readfirstlane(tn * T::BN);
 
-  int row_lim = p.M;        // rows [0, row_lim) may be read and written
-  const int lo = 0;         // tile rows [lo, hi) are stored
-  int hi = T::BM;
+  int row_lim = p.M;  // rows [0, row_lim) may be read and written
+  const int lo = 0;   // tile rows [lo, hi) are stored
   if (MODE == MODE_MASKED) {
     int v = __builtin_amdgcn_readfirstlane(p.meta[g]);
     v = v < 0 ? 0 : (v > p.M ? p.M : v);
     if (m0 >= v) return;
     row_lim = v;
-  } else if (MODE == MODE_CONTIG) {
-    // group of a 128-row block; ids outside [0, G) skip the block
-    auto group_of = [&](int blk) {
-      const int v = p.meta[blk];
-      return (v < 0 || v >= p.G) ? -1 : v;
-    };
-    const int b = m0 / 128;
-    if (b >= p.M / 128) return;  // odd copy past the last block
-    const int gb = __builtin_amdgcn_readfirstlane(group_of(b));
+  } else if (MODE == MODE_CONTIG && !RUNS) {
+    const int gb = __builtin_amdgcn_readfirstlane(group_of(m0 / 128));
     if (gb < 0) return;
-    if constexpr (RUNS) {
-      // first block of the run: lane l compares block base - 1 - l, 64 blocks
-      // a window; the closest differing block (or the matrix start) ends it
-      int base = b, start = -1;
-      while (start < 0) {
-        const int c = base - 1 - lane;
-        const bool differs = c < 0 || group_of(max(c, 0)) != gb;
-        const uint64_t m = __ballot(differs);
-        if (m != 0) start = base - (int)__builtin_ctzll(m);
-        else base -= 64;
-      }
-      start = __builtin_amdgcn_readfirstlane(start);
-      if ((b - start) & 1) return;  // second block of the tile before
-      const int nblk = p.M / 128;
-      const int g1 = b + 1 < nblk ? __builtin_amdgcn_readfirstlane(group_of(b + 1)) : -1;
-      if (g1 != gb) hi = 128;  // the run's last, single block
-    }
     g = gb;
   }
   g = __builtin_amdgcn_readfirstlane(g);
@@ -1340,7 +1398,9 @@ hipError_t launch_plan(const GemmPlan& plan, GemmParams p, int mode, int sf_fmt,
 // fits one round of it (plan_large, dense_q_wins).  One B scale per row of B
 // takes the 256 x 192 or 192 x 192 tile above 128 rows.
 GemmPlan fp8_gemm_plan(int mode, int64_t G, int64_t M, int64_t N, int64_t K, int sf_fmt) {
-  if (M > 128 && (sf_fmt & SF_ROWB)) {
+  // rows <= 128, or a contiguous layout too long for the 256-row tiles' list
+  const bool rows128 = M <= 128 || (mode == MODE_CONTIG && M / 128 > RUNS_MAX_BLOCKS);
+  if (!rows128 && (sf_fmt & SF_ROWB)) {
     // row scales: the 256 x 192 tile (the 256 x 256 FP32 kernel has no
     // registers left for per-lane column scales)
     GemmPlan p;
@@ -1354,7 +1414,7 @@ GemmPlan fp8_gemm_plan(int mode, int64_t G, int64_t M, int64_t N, int64_t K, int
     }
     return p;
   }
-  if (M <= 128) {
+  if (rows128) {
     GemmPlan p;
     p.parts = 1;
     p.n_split = N;
@@ -1366,9 +1426,10 @@ GemmPlan fp8_gemm_plan(int mode, int64_t G, int64_t M, int64_t N, int64_t K, int
 
 int64_t gemm_grid(const TileCfg& cfg, int mode, int64_t G, int64_t M, int64_t N) {
   const int64_t tm = (M + cfg.bm - 1) / cfg.bm, tn = (N + cfg.bn - 1) / cfg.bn;
-  const int64_t tiles = (mode == MODE_MASKED ? G : 1) * tm * tn;
-  // contiguous 256-row tiles: a copy for the even and one for the odd blocks
-  return (mode == MODE_CONTIG && cfg.bm == 256) ? 2 * tiles : tiles;
+  // contiguous 256-row tiles: one workgroup per 128-row block (at most one
+  // tile starts there) and column tile; those past the listed tiles exit
+  if (mode == MODE_CONTIG && cfg.bm == 256) return (M / 128) * tn;
+  return (mode == MODE_MASKED ? G : 1) * tm * tn;
 }
 
 int64_t plan_grid(const GemmPlan& plan, int part, int mode, int64_t G, int64_t M, int64_t N) {
@@ -1460,7 +1521,7 @@ hipError_t launch_fp8_gemm_fp8_out(GemmParams p, int sf_fmt, hipStream_t stream)
 // BF16 GEMMs: the same tile choice as the FP8 GEMM (a K-slice is 64 BF16
 // elements instead of 128 FP8 ones, the bytes per tile are the same).
 GemmPlan bf16_gemm_plan(int mode, int64_t G, int64_t M, int64_t N, int64_t K) {
-  if (M <= 128) {
+  if (M <= 128 || (mode == MODE_CONTIG && M / 128 > RUNS_MAX_BLOCKS)) {
     GemmPlan p;
     p.parts = 1;
     p.n_split = N;

@@ -107,6 +107,10 @@ struct GemmPlan {
   int parts;
 };
 
+// Contiguous layouts of more 128-row blocks than this take 128-row tiles: the
+// 256-row tiles list their tile starts in LDS (4 bytes a block).
+constexpr int64_t RUNS_MAX_BLOCKS = 8192;
+
 // GEMMs: the plan for (mode, G, M, N, K) and the grid of each launch (pure
 // functions of the shapes), and the launchers.
 GemmPlan fp8_gemm_plan(int mode, int64_t G, int64_t M, int64_t N, int64_t K, int sf_fmt);

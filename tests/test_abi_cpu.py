@@ -118,11 +118,16 @@ def test_query_config_is_a_pure_function_of_shapes(lib):
     c = binding.query_config(binding.DG_KIND_CONTIGUOUS, 4, 32768, 4096, 7168)
     bc = binding.query_config(binding.DG_KIND_BF16_CONTIGUOUS, 4, 32768, 4096, 7168)
     tiles = -(-32768 // c["block_m"]) * -(-4096 // c["block_n"])
-    # 256-row contiguous tiles: two copies of the tiling, tiles starting at
-    # even and at odd 128-row blocks
-    assert c["grid"] == (2 * tiles if c["block_m"] == 256 else tiles) and bc["grid"] == c["grid"]
+    # 256-row contiguous tiles: one workgroup per 128-row block and column
+    # tile (at most one tile starts at each block)
+    assert c["grid"] == ((32768 // 128) * 16 if c["block_m"] == 256 else tiles) and bc["grid"] == c["grid"]
     c = binding.query_config(binding.DG_KIND_CONTIGUOUS, 4, 33152, 4096, 7168)  # 259 blocks
-    assert c["block_m"] == 256 and c["grid"] == 2 * 130 * 16
+    assert c["block_m"] == 256 and c["grid"] == 259 * 16
+    # past 8192 blocks the tile list would not fit: 128-row tiles
+    for kind in (binding.DG_KIND_CONTIGUOUS, binding.DG_KIND_BF16_CONTIGUOUS):
+        assert binding.query_config(kind, 4, 8192 * 128, 4096, 7168)["block_m"] == 256
+        big = binding.query_config(kind, 4, 8193 * 128, 4096, 7168)
+        assert big["block_m"] == 128 and big["grid"] == 8193 * -(-4096 // big["block_n"])
     with pytest.raises(binding.DgmiError):
         binding.query_config(12, 1, 1, 1, 1)  # no such kind
 
@@ -182,10 +187,11 @@ def test_launch_plan_of_the_grouped_shapes(lib):
     assert (m["block_n"], m["n_split"], m["block_n2"], m["grid"]) == (256, 4096, 0, 512)
     m = binding.query_config(binding.DG_KIND_MASKED, 32, 256, 7168, 2048)
     assert (m["block_n"], m["n_split"], m["block_n2"], m["grid"], m["grid2"]) == (256, 7168, 0, 896, 0)
-    # contiguous prefill: whole rounds of 256 x 256 (and the odd-block copy)
+    # contiguous prefill: whole rounds of 256 x 256 (a workgroup per 128-row
+    # block and column tile, those past the listed tiles exit)
     for N in (4096, 7168):
         c = binding.query_config(binding.DG_KIND_CONTIGUOUS, 4, 32768, N, 7168)
-        assert (c["block_n"], c["n_split"], c["block_n2"], c["grid"]) == (256, N, 0, 2 * 128 * N // 256)
+        assert (c["block_n"], c["n_split"], c["block_n2"], c["grid"]) == (256, N, 0, 256 * N // 256)
     # rows <= 128: one launch of a 128-row tile
     s = binding.query_config(binding.DG_KIND_MASKED, 64, 128, 7168, 2048)
     assert (s["block_m"], s["n_split"], s["block_n2"], s["grid2"]) == (128, 7168, 0, 0)

@@ -374,8 +374,8 @@ def test_contiguous_mixed_groups_256x256_tile():
 
 @pytest.mark.parametrize("layout", [[0, 1, 1], [1, 1, 0, 0, 2], [-1, 2, 2]])
 def test_contiguous_odd_block_counts(layout):
-    """256-row tiles on an odd number of 128-row blocks: the odd-block copy
-    of the grid reaches past the last block, and runs end on a single block."""
+    """256-row tiles on an odd number of 128-row blocks: runs end on a
+    single block, one of them the layout's last."""
     say(f"contiguous odd block count {layout}")
     mg = _mg()
     from moe_grouped_gemm_x128_amd import binding
@@ -401,8 +401,8 @@ def test_contiguous_odd_block_counts(layout):
 
 
 def test_contiguous_long_runs_at_odd_offsets():
-    """Runs of one group longer than 64 blocks (the run-start scan takes
-    several windows), starting at odd block offsets, with odd lengths (a
+    """Runs of one group longer than 64 blocks (longer than a wave's part of
+    the run-start scan), starting at odd block offsets, with odd lengths (a
     single-block tile at the run's end), next to skipped blocks."""
     say("contiguous long runs at odd offsets")
     mg = _mg()
@@ -412,7 +412,7 @@ def test_contiguous_long_runs_at_odd_offsets():
     layout = np.array([1] + [0] * 151 + [2] * 3 + [-1] + [1] * 65 + [2] * 2 + [7] + [0] * 130, dtype=np.int32)
     Msum = layout.size * 128
     c = binding.query_config(binding.DG_KIND_CONTIGUOUS, G, Msum, N, K)
-    assert c["block_m"] == 256 and c["grid"] == 2 * -(-layout.size // 2) * -(-N // c["block_n"])
+    assert c["block_m"] == 256 and c["grid"] == layout.size * -(-N // c["block_n"])
     xa = synth.normal_f32(127, (Msum, K))
     xb = synth.normal_f32(128, (G, N, K))
     a, sfa = q_tok(to_dev(xa))
@@ -427,6 +427,45 @@ def test_contiguous_long_runs_at_odd_offsets():
     got = to_host(d)
     assert np.all(got[~written] == SENTINEL_BF16)
     assert_bf16_close(got[written], ref[written], "contiguous long runs")
+
+
+@pytest.mark.parametrize("dtype", ["fp8", "bf16"])
+def test_contiguous_layout_longer_than_a_workgroup(dtype):
+    """1100 blocks: the tile-start scan takes three passes over the layout
+    (512 threads a pass), with runs crossing the pass boundaries at even and
+    at odd offsets, a run covering a whole pass, and skipped blocks."""
+    say(f"contiguous 1100-block layout {dtype}")
+    mg = _mg()
+    from moe_grouped_gemm_x128_amd import binding
+
+    rng = np.random.default_rng(1100)
+    runs = [(0, 3), (1, 508), (2, 2), (0, 1), (-1, 1), (1, 600), (2, 5)]  # 1120 blocks, cut to 1100
+    layout = np.concatenate([np.full(n, g, dtype=np.int32) for g, n in runs])[:1100]
+    layout[rng.choice(1100, 40, replace=False)] = -1
+    G, N, K = 3, 136, 128
+    Msum = layout.size * 128
+    kind = binding.DG_KIND_CONTIGUOUS if dtype == "fp8" else binding.DG_KIND_BF16_CONTIGUOUS
+    c = binding.query_config(kind, G, Msum, N, K)
+    assert c["block_m"] == 256 and c["grid"] == 1100 * -(-N // c["block_n"])
+    xa = synth.normal_f32(131, (Msum, K))
+    xb = synth.normal_f32(132, (G, N, K))
+    d = sentinel_like((Msum, N))
+    if dtype == "fp8":
+        a, sfa = q_tok(to_dev(xa))
+        b, sfb = q_blk(to_dev(xb))
+        mg.m_grouped_fp8_gemm_nt_contiguous(a, b, sfa, sfb, d, to_dev(layout))
+        ra, rsfa = oracle.per_token_cast_to_fp8(xa)
+        rb, rsfb = oracle.per_block_cast_to_fp8(xb)
+        ref, written = oracle.m_grouped_fp8_gemm_nt_contiguous(ra, rb, rsfa, rsfb, layout)
+    else:
+        ab, bb = synth.bf16_bits_from_f32(xa), synth.bf16_bits_from_f32(xb)
+        mg.m_grouped_bf16_gemm_nt_contiguous(to_dev(ab.view(np.int16)).view(torch.bfloat16),
+                                             to_dev(bb.view(np.int16)).view(torch.bfloat16), d, to_dev(layout))
+        ref, written = oracle.m_grouped_bf16_gemm_nt_contiguous(ab, bb, layout)
+    torch.cuda.synchronize()
+    got = to_host(d)
+    assert np.all(got[~written] == SENTINEL_BF16)
+    assert_bf16_close(got[written], ref[written], f"contiguous 1100-block layout {dtype}")
 
 
 @pytest.mark.parametrize("si", [0, 1])
