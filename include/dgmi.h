@@ -354,9 +354,9 @@ int moe_dispatch_masked_fp8(const dg_tensor* x, const dg_tensor* topk_idx, const
  *   counts          I32 [G] out: pairs routed to each expert
  *   slot            I32 [T, k] out, contiguous: the row of a where (t, j)
  *                   landed, -1 if routed nowhere or past the capacity Mcap
- *   align           128 (whole blocks), or 256: no 256-row tile of the
- *                   contiguous GEMM then holds two experts, which it would
- *                   compute twice (one pass per expert)
+ *   align           128 (whole blocks), or 256 (whole 256-row tiles of the
+ *                   contiguous GEMM: no region then ends in a one-block
+ *                   tile, at the cost of more padding rows)
  * Mcap >= T * k + (align - 1) * G holds every routing.  The outputs feed
  * m_grouped_fp8_gemm_nt_contiguous (a, sfa, grouped_layout) and moe_combine
  * (slot, with the GEMM's [Mcap, N] output viewed as [1, Mcap, N]).

@@ -22,7 +22,7 @@ the reading taken:
   * Contiguous layout (prefill, "DeepGEMM tested by Novita AI", contiguous
     layout: groups concatenated along M in 128-row blocks, a group id per
     block): expert e's pairs fill a region of ceil(count_e / align) * align
-    rows (align 128, or 256 so that no 256-row tile holds two experts) that
+    rows (align 128 or 256: whole blocks, or whole 256-row tiles) that
     starts where expert e - 1's region ends; rows past the capacity Mcap are
     dropped; blocks past the last region get id -1.  slot[t, j] is
     the row in the concatenated buffer (or -1); rows of a region past its
