@@ -468,6 +468,44 @@ def test_contiguous_layout_longer_than_a_workgroup(dtype):
     assert_bf16_close(got[written], ref[written], f"contiguous 1100-block layout {dtype}")
 
 
+@pytest.mark.parametrize("nblk,block_m,run", [(8192, 256, 40), (8192, 256, 3), (8193, 128, 40)])
+def test_contiguous_largest_tile_list(nblk, block_m, run):
+    """The longest layout the 256-row tiles' LDS list holds (8192 blocks,
+    16 scan passes; runs of 1..40 blocks, or of 1..3 so that the list holds
+    about 5500 tiles), and one block more, which takes 128-row tiles: 5
+    groups with skipped (-1) and out-of-range (>= G) ids; FP8 codes and
+    scales drawn directly (every finite E4M3 magnitude), the whole output
+    against the oracle."""
+    say(f"contiguous largest tile list: {nblk} blocks, runs of 1..{run}")
+    mg = _mg()
+    from moe_grouped_gemm_x128_amd import binding
+
+    G, N, K = 5, 64, 128
+    rng = np.random.default_rng(8192 + nblk + run)
+    ids, lens = rng.integers(-1, G + 1, size=nblk), rng.integers(1, run + 1, size=nblk)
+    layout = np.repeat(ids, lens)[:nblk].astype(np.int32)
+    M = nblk * 128
+    c = binding.query_config(binding.DG_KIND_CONTIGUOUS, G, M, N, K)
+    assert c["block_m"] == block_m
+    if block_m == 256:
+        assert c["grid"] == nblk * -(-N // c["block_n"])
+
+    def codes(shape):
+        v = rng.integers(0, 0x7F, size=shape, dtype=np.uint8)
+        return v | (rng.integers(0, 2, size=shape, dtype=np.uint8) << np.uint8(7))
+
+    ra, rb = codes((M, K)), codes((G, N, K))
+    rsfa = rng.uniform(2.0 ** -10, 2.0 ** -6, size=(M, K // 128)).astype(np.float32)
+    rsfb = rng.uniform(2.0 ** -10, 2.0 ** -6, size=(G, 1, K // 128)).astype(np.float32)
+    d = sentinel_like((M, N))
+    mg.m_grouped_fp8_gemm_nt_contiguous(to_dev(ra), to_dev(rb), to_dev(rsfa), to_dev(rsfb), d, to_dev(layout))
+    torch.cuda.synchronize()
+    ref, written = oracle.m_grouped_fp8_gemm_nt_contiguous(ra, rb, rsfa, rsfb, np.where(layout < G, layout, -1))
+    got = to_host(d)
+    assert np.all(got[~written] == SENTINEL_BF16)
+    assert_bf16_close(got[written], ref[written], f"contiguous {nblk} blocks")
+
+
 @pytest.mark.parametrize("si", [0, 1])
 def test_contiguous_prefill_full_size_sampled(si):
     N, K = synth.CONTIG["shapes"][si]
