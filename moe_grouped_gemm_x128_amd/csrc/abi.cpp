@@ -990,11 +990,11 @@ int dg_query_config(int32_t kind, int64_t G, int64_t M, int64_t N, int64_t K, dg
   out->block_n = c.cfg[0].bn;
   out->threads = c.cfg[0].threads;
   out->grid = dgmi::plan_grid(c, 0, mode, G, M, N);
-  out->lds_bytes = c.cfg[0].lds_bytes;
+  out->lds_bytes = dgmi::plan_lds(c, 0, mode);
   out->n_split = c.parts == 2 ? c.n_split : N;
   out->block_n2 = c.parts == 2 ? c.cfg[1].bn : 0;
   out->grid2 = dgmi::plan_grid(c, 1, mode, G, M, N);
-  out->lds_bytes2 = c.parts == 2 ? c.cfg[1].lds_bytes : 0;
+  out->lds_bytes2 = dgmi::plan_lds(c, 1, mode);
   return ok();
 }
 

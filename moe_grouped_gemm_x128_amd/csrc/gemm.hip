@@ -1438,6 +1438,14 @@ int64_t plan_grid(const GemmPlan& plan, int part, int mode, int64_t G, int64_t M
   return gemm_grid(plan.cfg[part], mode, G, M, n_len);
 }
 
+int plan_lds(const GemmPlan& plan, int part, int mode) {
+  if (part >= plan.parts) return 0;
+  const TileCfg& c = plan.cfg[part];
+  // contiguous 256-row tiles: the run scan's wave masks (8 bytes) and tile
+  // counts (4 bytes) per wave, beside the stages
+  return c.lds_bytes + ((mode == MODE_CONTIG && c.bm == 256) ? (c.threads / 64) * 12 : 0);
+}
+
 // Dense FP8 GEMM with an MN-major A and/or B: one launch of the 256 x 192
 // tile, whose 48-column wave tiles keep the MFMA's column order (the
 // transposing B fragment reads hand each 8-lane run 8 consecutive columns,

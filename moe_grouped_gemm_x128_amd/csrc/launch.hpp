@@ -117,6 +117,8 @@ GemmPlan fp8_gemm_plan(int mode, int64_t G, int64_t M, int64_t N, int64_t K, int
 GemmPlan bf16_gemm_plan(int mode, int64_t G, int64_t M, int64_t N, int64_t K);
 int64_t gemm_grid(const TileCfg& cfg, int mode, int64_t G, int64_t M, int64_t N);
 int64_t plan_grid(const GemmPlan& plan, int part, int mode, int64_t G, int64_t M, int64_t N);
+// static LDS of one workgroup of launch `part` (0 past the plan's launches)
+int plan_lds(const GemmPlan& plan, int part, int mode);
 // sf_fmt: SF_F32 or SF_UE8M0, plus SF_ROWB for one B scale per row of B;
 // an MN-major A or B (p.a_mn, p.b_mn: dense, block scales, BF16 d) takes the
 // plan of fp8_mn_gemm_plan

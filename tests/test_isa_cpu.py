@@ -113,3 +113,47 @@ def test_no_other_kernel_spills(src, tmp_path):
             assert int(s.split(":", 1)[1]) == 0, f"{name} uses scratch"
             seen += 1
     assert seen >= 3
+
+
+def _lds_sizes(co):
+    """{(BM, BN, KIND, MODE): static LDS sizes} of the GEMM kernels in the code
+    object (each kernel's metadata map opens with .agpr_count)."""
+    notes = subprocess.run([os.path.join(LLVM, "llvm-readelf"), "--notes", co], check=True, capture_output=True,
+                           text=True).stdout
+    out = {}
+    for entry in re.split(r"\n\s*- \.agpr_count:", notes)[1:]:
+        name = re.search(r"\.name:\s+(\S+)", entry)
+        m = KERNEL_RE.search(name.group(1)) if name else None
+        if not m:
+            continue
+        bm, bn = (int(x) for x in re.findall(r"\d+", m.group(1))[:2])
+        size = int(re.search(r"\.group_segment_fixed_size:\s+(\d+)", entry).group(1))
+        out.setdefault((bm, bn, int(m.group(2)), int(m.group(4))), set()).add(size)
+    return out
+
+
+def test_query_config_reports_the_kernels_static_lds(code_object):
+    """lds_bytes of query_config is the static LDS of a kernel that launch
+    runs (the code object's group segment size), the contiguous 256-row
+    tiles' run-scan words included."""
+    from moe_grouped_gemm_x128_amd import binding
+
+    sizes = _lds_sizes(code_object)
+    assert len(sizes) >= 20
+    b = binding
+    kinds = [(b.DG_KIND_DENSE, 0, 0), (b.DG_KIND_CONTIGUOUS, 0, 1), (b.DG_KIND_MASKED, 0, 2),
+             (b.DG_KIND_BF16_DENSE, 1, 0), (b.DG_KIND_BF16_CONTIGUOUS, 1, 1), (b.DG_KIND_BF16_MASKED, 1, 2),
+             (b.DG_KIND_DENSE_ROWB, 0, 0), (b.DG_KIND_CONTIGUOUS_ROWB, 0, 1), (b.DG_KIND_MASKED_ROWB, 0, 2)]
+    shapes = [(4, 128, 7168, 2048), (4, 4096, 7168, 2048), (4, 4096, 2112, 7168), (4, 4096, 7168, 16384),
+              (4, 4096, 100, 512), (4, 8193 * 128, 4096, 7168)]
+    checked = 0
+    for kind, k_id, mode in kinds:
+        for G, M, N, K in shapes:
+            c = binding.query_config(kind, G, M, N, K)
+            key = (c["block_m"], c["block_n"], k_id, mode)
+            assert c["lds_bytes"] in sizes.get(key, ()), (kind, (G, M, N, K), key, c["lds_bytes"], sizes.get(key))
+            if c["block_n2"]:
+                key2 = (c["block_m"], c["block_n2"], k_id, mode)
+                assert c["lds_bytes2"] in sizes.get(key2, ()), (kind, (G, M, N, K), key2, c["lds_bytes2"])
+            checked += 1
+    assert checked == len(kinds) * len(shapes)
