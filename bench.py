@@ -351,6 +351,7 @@ class ContiguousWorkload:
 
 class MaskedWorkload:
     name = "masked_fp8_moe_decode"
+    uniform_m = None  # every expert's masked_m set to this value instead of the seeded draw
 
     def __init__(self, torch, mg, synth):
         self.torch, self.mg = torch, mg
@@ -358,7 +359,10 @@ class MaskedWorkload:
         c = synth.MASKED
         self.G, self.max_m = c["G"], c["max_m"]
         self.shapes = list(c["shapes"])
-        mm = synth.masked_m_decode(c["seed_m"], self.G)
+        if self.uniform_m is None:
+            mm = synth.masked_m_decode(c["seed_m"], self.G)
+        else:
+            mm = np.full(self.G, self.uniform_m, dtype=np.int32)
         self.mm_host = mm
         self.masked_m = torch.from_numpy(mm).to(dev)
         self.bufs = []
@@ -402,8 +406,11 @@ class MaskedWorkload:
         return ("DG_KIND_MASKED", self.G, self.max_m, N, K)
 
     def config(self):
-        return {"workload": self.name, "experts": self.G, "max_m": self.max_m,
-                "sum_masked_m": int(self.mm_host.sum()), "shapes_NK": self.shapes}
+        cfg = {"workload": self.name, "experts": self.G, "max_m": self.max_m,
+               "sum_masked_m": int(self.mm_host.sum()), "shapes_NK": self.shapes}
+        if self.uniform_m is not None:
+            cfg["masked_m"] = f"every expert {self.uniform_m}"
+        return cfg
 
 
 class MoeDecodeWorkload:
@@ -986,6 +993,9 @@ def main():
                     help="record HIP events around the GEMM calls of one timed step in this many (plus the last)")
     ap.add_argument("--moe-align", type=int, choices=(128, 256), default=128,
                     help="moe_prefill: row granule of the experts' regions in the contiguous layout")
+    ap.add_argument("--masked-m", type=int, default=None,
+                    help="masked: set every expert's masked_m to this many rows (1..256) instead of the seeded "
+                         "draw, to time the decode GEMM against the number of valid rows")
     ap.add_argument("--no-masked", action="store_true", help="dense: skip the masked grouped GEMM block")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", action="store_true",
@@ -1010,6 +1020,11 @@ def main():
 
     log(f"setting up workload {args.workload}")
     MoeDecodeWorkload.align = args.moe_align
+    if args.masked_m is not None:
+        if args.workload != "masked" or not 1 <= args.masked_m <= 256:
+            print("--masked-m takes 1..256 rows, with --workload masked", file=sys.stderr)
+            sys.exit(2)
+        MaskedWorkload.uniform_m = args.masked_m
     if args.workload in ("dense_nn", "dense_tn", "dense_tt"):
         W = DenseLayoutWorkload(torch, mg, synth, args.workload[-2:])
     else:
