@@ -378,7 +378,9 @@ class MaskedWorkload:
             self.bufs.append(dict(
                 xa=xa, b=b, sfb=sfb,
                 a=torch.empty((self.G, self.max_m, K), dtype=torch.uint8, device=dev),
-                sfa=torch.empty((self.G, self.max_m, K // 128), dtype=torch.float32, device=dev),
+                # M-major per expert (the 256 row scales of a K-block contiguous: eight cache lines
+                # per slice of a tile instead of one per row)
+                sfa=torch.empty((self.G, K // 128, self.max_m), dtype=torch.float32, device=dev).transpose(1, 2),
                 d=torch.empty((self.G, self.max_m, N), dtype=torch.bfloat16, device=dev)))
         rows = int(mm.sum())
         active = int((mm > 0).sum())
@@ -446,7 +448,8 @@ class MoeDecodeWorkload:
         del xb
         ga = 1 if self.contig else G
         self.a = torch.empty((ga, max_m, K), dtype=torch.uint8, device=dev)
-        self.sfa = torch.empty((ga, max_m, K // 128), dtype=torch.float32, device=dev)
+        # M-major per expert, as for the masked decode workload
+        self.sfa = torch.empty((ga, K // 128, max_m), dtype=torch.float32, device=dev).transpose(1, 2)
         self.masked_m = torch.empty((G,), dtype=torch.int32, device=dev)  # contiguous: the counts
         self.layout = torch.empty((max_m // 128,), dtype=torch.int32, device=dev)
         self.slot = torch.empty((T, k), dtype=torch.int32, device=dev)
