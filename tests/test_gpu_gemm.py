@@ -803,3 +803,42 @@ def test_grouped_per_row_b_scales(ue8m0):
     gotc = to_host(dg)
     assert np.all(gotc[~wc] == SENTINEL_BF16)
     assert_bf16_close(gotc[wc], refc[wc], "contiguous per-row B scales")
+
+
+@pytest.mark.gpu
+def test_masked_scales_m_major_per_expert():
+    """A's scales stored M-major per expert ([G, K/128, max_m] seen through a
+    transposed view, the layout of the masked decode benchmark), written by
+    the per-token cast: the same codes and scales as the K-major layout, and
+    the masked GEMM's output bit-identical to the K-major run and within the
+    oracle's tolerance; rows past masked_m untouched."""
+    say("masked, A scales M-major per expert")
+    mg = _mg()
+    G, max_m, N, K = 4, 256, 512, 512
+    KB = K // 128
+    mm = np.array([200, 256, 1, 129], dtype=np.int32)
+    xa = synth.normal_f32(811, (G, max_m, K))
+    xb = synth.normal_f32(812, (G, N, K))
+    xa_d = to_dev(xa)
+    a1 = torch.empty((G, max_m, K), dtype=torch.uint8, device="cuda")
+    s1 = torch.empty((G, max_m, KB), dtype=torch.float32, device="cuda")
+    a2 = torch.empty_like(a1)
+    s2 = torch.empty((G, KB, max_m), dtype=torch.float32, device="cuda").transpose(1, 2)
+    assert s2.stride() == (KB * max_m, 1, max_m)
+    mg.per_token_cast_to_fp8(xa_d, a1, s1)
+    mg.per_token_cast_to_fp8(xa_d, a2, s2)
+    b, sfb = q_blk(to_dev(xb), False)
+    d1 = sentinel_like((G, max_m, N))
+    d2 = sentinel_like((G, max_m, N))
+    mmd = to_dev(mm)
+    mg.m_grouped_fp8_gemm_nt_masked(a1, b, s1, sfb, d1, mmd, max_m)
+    mg.m_grouped_fp8_gemm_nt_masked(a2, b, s2, sfb, d2, mmd, max_m)
+    torch.cuda.synchronize()
+    assert torch.equal(a1, a2) and torch.equal(s1, s2)
+    assert torch.equal(d1.view(torch.int16), d2.view(torch.int16))  # bit patterns (the sentinel is a NaN)
+    ra, rsfa = oracle.per_token_cast_to_fp8(xa)
+    rb, rsfb = oracle.per_block_cast_to_fp8(xb)
+    ref, written = oracle.m_grouped_fp8_gemm_nt_masked(ra, rb, rsfa, rsfb, mm, max_m)
+    got = to_host(d2)
+    assert np.all(got[~written] == SENTINEL_BF16)
+    assert_bf16_close(got[written], ref[written], "masked, M-major A scales")

@@ -325,3 +325,21 @@ def test_moe_decode_chain_graph_replay():
         # and the routing against the oracle
         rmm, rslot, _, _ = oracle.moe_route(tr, G, max_m)
         assert np.array_equal(to_host(gbufs[2]), rmm) and np.array_equal(to_host(gbufs[3]), rslot), f"replay {r}"
+
+
+def test_dispatch_scales_m_major_per_expert():
+    """The dispatch writing A's scales M-major per expert ([G, K/128, max_m]
+    seen through a transposed view, the layout of the MoE decode benchmark):
+    the same codes, scales and routing as the oracle."""
+    say("moe_dispatch_masked_fp8, scales M-major per expert")
+    mg = _mg()
+    T, k, G, max_m, K = 96, 4, 8, 64, 1024
+    x = synth.normal_f32(651, (T, K))
+    topk, _ = synth.moe_routing(652, T, G, k, 0.05)
+    a, _, masked_m, slot, src = _dispatch_buffers(T, K, k, G, max_m)
+    sfa = torch.full((G, K // 128, max_m), float("nan"), dtype=torch.float32, device="cuda").transpose(1, 2)
+    assert sfa.stride() == (K // 128 * max_m, 1, max_m)
+    outs = (a, sfa, masked_m, slot, src)
+    mg.moe_dispatch_masked_fp8(to_dev(x), to_dev(topk), *outs)
+    torch.cuda.synchronize()
+    _check_dispatch(x, topk, G, max_m, False, outs, "dispatch, M-major scales")
